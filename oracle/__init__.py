@@ -1,0 +1,28 @@
+"""fp64 CPU oracle for LoRA over a frozen GGUF block-quantised base.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or execute this package; only the tests,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+
+It is a plain, slow, obviously-correct restatement of what the method
+computes, written from the pages (page 2, "Show HN: LoRA over GGUF - Train
+Qwen3.8-Flash-Next in 40G VRAM", section "Things involved in the training":
+MMQ and grouped MMQ like llama.cpp; the fast LoRA backward formula like
+Unsloth for linear and MoE layers; MoE routing like OpenAI triton-kernels;
+chunked cross entropy like Liger Kernel, which works with MMQ; load-balancing
+loss disabled).  Everything is computed in float64 from the exact bytes and
+bf16 values the GPU receives.  It shares no code with the HIP path: the only
+module both sides import is ``synth`` (seeded inputs, no method arithmetic).
+
+Modules:
+  blocks   - block decode (Q8_0, Q4_0, 2-bit scale/min)
+  linear   - fused linear forward and the fast LoRA backward
+  routing  - softmax top-k, stable expert sort, offsets, positions; backward
+  moe      - grouped expert FFN forward/backward and a per-token brute force
+  lmhead   - LM head with chunked online log-sum-exp cross entropy
+
+Every function is pinned by tests under tests/ (marked "not gpu") to values
+fixed independently of the oracle: hand-built blocks, closed forms, brute
+force and finite differences.
+"""
+from . import blocks, linear, routing, moe, lmhead  # noqa: F401
