@@ -1,0 +1,292 @@
+/*
+ * gq.h -- C ABI of libgq: LoRA over a frozen GGUF block-quantised base on
+ * AMD MI355X (gfx950).
+ *
+ * The method (page 2, "Show HN: LoRA over GGUF - Train Qwen3.8-Flash-Next in
+ * 40G VRAM", section "Things involved in the training"): the base weights
+ * stay in GGUF blocks and are multiplied without being expanded ("MMQ and
+ * grouped MMQ like llama.cpp"); a LoRA adapter is folded into the same layer
+ * and trained with the fast backward formula ("Fast LoRA bwd formula like
+ * Unsloth for linear layer and MoE layer"); MoE routing is softmax top-k
+ * ("MoE routing like OpenAI triton-kernels"); the LM head feeds a chunked
+ * cross entropy ("Chunked cross entropy loss like Liger Kernel, which works
+ * with MMQ"); no load-balancing loss.
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers are DEVICE pointers to contiguous row-major data
+ *    unless a parameter says "host".  bf16 arrays are passed as uint16_t bit
+ *    patterns.  The caller owns all memory; the library never allocates.
+ *    Temporary storage comes from a caller-provided workspace sized by the
+ *    matching *_workspace_size() query (bytes, 256-byte aligned pointer).
+ *  - `stream` is a hipStream_t (0 = the default stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises, nothing copies
+ *    between host and device.  Results are stream-ordered.
+ *  - Return value: GQ_OK (0) or a negative GQ_E* code.  Argument errors are
+ *    found on the host before any HIP call; gq_last_error() then returns a
+ *    thread-local message.  A failed launch returns GQ_EHIP.
+ *  - Results are bitwise deterministic from run to run (no float atomics;
+ *    every reduction has a fixed order).
+ *  - No full-precision copy of a quantised weight is ever written: the
+ *    blocks are decoded into registers / LDS inside the kernels.
+ *  - Calls are reentrant; there is no global mutable state besides the
+ *    thread-local error text.
+ *
+ * Block formats (32 weights per block, little-endian fields, the blocks of
+ * one row contiguous, rows contiguous):
+ *   GQ_Q8_0  34 B: fp16 d, int8 q[32]                 w_i = d*q_i
+ *   GQ_Q4_0  18 B: fp16 d, u8 qs[16]; byte j holds element j (low nibble)
+ *            and element j+16 (high nibble)            w_i = d*(q_i - 8)
+ *   GQ_Q2_DM 12 B: fp16 d, fp16 m, u8 qs[8]; byte j holds element j+8p in
+ *            bits [2p, 2p+2)                           w_i = d*q_i + m
+ * (Q8_0 / Q4_0 are GGUF's formats; the 2-bit scale/min format stands in for
+ * the pages' 2-bit bases, page 2 sections "DeepSeek-specific" and
+ * "Qwen4-Exp-specific".)
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define GQ_OK 0
+#define GQ_EINVAL (-1)     /* bad argument (null pointer, size, alignment) */
+#define GQ_ENOTSUP (-2)    /* valid but unsupported shape or type */
+#define GQ_EWORKSPACE (-3) /* workspace missing or smaller than required */
+#define GQ_EHIP (-4)       /* a HIP launch or runtime call failed */
+#define GQ_EDEVICE (-5)    /* reserved: device-detected data error */
+
+/* quant types */
+#define GQ_Q8_0 0
+#define GQ_Q4_0 1
+#define GQ_Q2_DM 2
+
+/* output dtypes of gq_dequant */
+#define GQ_F32 0
+#define GQ_BF16 1
+
+/* grouped forward epilogues */
+#define GQ_EPI_NONE 0   /* out = o = in deq(W)^T + s (in A^T) B^T           */
+#define GQ_EPI_SWIGLU 1 /* two projections (gate, up): out = silu(g) * u    */
+
+/* grouped backward modes */
+#define GQ_BWD_DOWN_SWIGLU 0
+#define GQ_BWD_GATEUP 1
+
+/* Library version: major*10000 + minor*100 + patch. */
+int gq_version(void);
+
+/* Thread-local text of the last error returned on this thread ("" if none). */
+const char* gq_last_error(void);
+
+/* Bytes per 32-weight block of `qtype`, or -1 for an unknown type. */
+int64_t gq_block_bytes(int qtype);
+
+/*
+ * Block decode (the primitive inside every MMQ; a test/debug export).
+ * blocks: [rows][cols/32] blocks of `qtype`.  out: [rows][cols] float32
+ * (out_dtype GQ_F32) or bf16 (GQ_BF16).  The float32 result is the weight's
+ * exact value rounded once to nearest-even (exact for Q8_0 / Q4_0); bf16 is
+ * that float32 rounded to nearest-even.  fp16 subnormal scales are honoured.
+ * cols % 32 == 0.  rows == 0 is a no-op.
+ */
+int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype,
+               void* out, void* stream);
+
+/*
+ * A quantised projection with its LoRA adapter (one layer, or E stacked
+ * experts when n_experts > 1):
+ *   w_blocks  [E][n_out][n_in/32] blocks of `qtype`
+ *   A         [E][rank][n_in]  float32
+ *   B         [E][n_out][rank] float32
+ *   scale     s = alpha / rank
+ * Constraints: n_in % 64 == 0 (whole pairs of blocks per row, so every row
+ * starts dword-aligned), n_out % 8 == 0 (16-byte activation rows in the
+ * backward), 1 <= rank <= 16, 1 <= n_experts <= 1024.  Grouped backward also
+ * needs the expert intermediate size (gate/up n_out) % 64 == 0.
+ */
+typedef struct gq_lora_linear {
+    int32_t qtype;
+    int32_t rank;
+    int64_t n_out;
+    int64_t n_in;
+    const void* w_blocks;
+    const float* A;
+    const float* B;
+    float scale;
+    int32_t n_experts;
+} gq_lora_linear;
+
+/*
+ * Fused linear forward (one layer; n_experts must be 1):
+ *   xa = x A^T                 [T][rank] float32 (saved for the backward)
+ *   y  = x deq(W)^T + s xa B^T [T][n_out] bf16
+ * x [T][n_in] bf16.  T == 0 is a no-op.
+ */
+size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear* L, int64_t T);
+int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
+                       float* xa, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fast LoRA backward (the frozen W gets no gradient):
+ *   dX = dY deq(W) + s (dY B) A     [T][n_in] bf16  (dx may be NULL: skipped)
+ *   dB = s dY^T xa                  [n_out][rank] float32 (overwritten)
+ *   dA = s (dY B)^T x               [rank][n_in]  float32 (overwritten)
+ * x [T][n_in] bf16, xa [T][rank] float32 from the forward, dy [T][n_out] bf16.
+ */
+size_t gq_linear_lora_bwd_workspace_size(const gq_lora_linear* L, int64_t T);
+int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                       const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MoE routing, softmax top-k.  For each token t over logits [T][E] (fp32):
+ *   ids[t][0..k)  the k largest logits, ties to the lower expert index, in
+ *                 that order;
+ *   w[t][0..k)    softmax over the k selected logits (fp32);
+ *   sorted[T*k]   assignment indices a = t*k + j sorted stably by expert;
+ *   offsets[E+1]  offsets[e] = number of assignments with expert < e;
+ *   pos[T*k]      pos[sorted[p]] = p.
+ * 1 <= k <= min(E, 16), E <= 1024.  NaN logits give an unspecified order.
+ */
+size_t gq_moe_route_workspace_size(int64_t T, int32_t E, int32_t k);
+int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                 int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Router backward (no load-balancing term): dlogits [T][E] fp32 (overwritten),
+ * dlogits[t][ids[t][j]] = w[t][j] (dw[t][j] - sum_i w[t][i] dw[t][i]), else 0.
+ * dw [T][k] fp32. */
+int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
+                     int32_t k, float* dlogits, void* stream);
+
+/* Combine: y[t] = sum_{j<k} w[t][j] o[pos[t*k+j]]  (fp32 sum in slot order).
+ * o [T*k][H] bf16 rows in sorted order; y [T][H] bf16.  H % 8 == 0. */
+int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, int64_t T,
+                       int32_t k, int64_t H, uint16_t* y, void* stream);
+
+/* Combine backward for the activations: dx[t] = sum_j dxrows[pos[t*k+j]]
+ * (fp32 sum in slot order).  dxrows [T*k][H] bf16; dx [T][H] bf16. */
+int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k,
+                       int64_t H, uint16_t* dx, void* stream);
+
+/*
+ * Grouped MMQ + LoRA forward over routed rows.  P[0..nproj) are stacked
+ * expert projections with identical shapes (n_experts = E).  Row p
+ * (0 <= p < M) belongs to expert e with offsets[e] <= p < offsets[e+1]
+ * (offsets [E+1], device) and reads activation row
+ *   in[gather[p] / gather_div]   (gather may be NULL: row p reads in[p]).
+ *   GQ_EPI_NONE   (nproj 1): out[p] = in_p deq(W_e)^T + s (in_p A_e^T) B_e^T
+ *                            xa[p]  = in_p A_e^T
+ *   GQ_EPI_SWIGLU (nproj 2, P[0] = gate, P[1] = up):
+ *                 g, u as above; out[p] = silu(g) * u;
+ *                 save_g[p] = g, save_u[p] = u (bf16); xa = [2][M][rank].
+ * Only experts that own rows read their blocks.
+ */
+typedef struct gq_grouped_fwd_args {
+    const uint16_t* in;      /* activations [*][n_in] bf16 */
+    const int32_t* gather;   /* [M] or NULL */
+    int32_t gather_div;      /* >= 1 */
+    const int32_t* offsets;  /* [E+1] */
+    int64_t M;               /* total rows */
+    uint16_t* out;           /* [M][n_out] bf16 */
+    uint16_t* save_g;        /* SWIGLU only */
+    uint16_t* save_u;        /* SWIGLU only */
+    float* xa;               /* [nproj][M][rank] */
+} gq_grouped_fwd_args;
+
+size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t nproj,
+                                              int64_t M);
+int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epilogue,
+                            const gq_grouped_fwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * Grouped fast-LoRA backward of a routed SwiGLU expert FFN, in two calls.
+ *
+ * GQ_BWD_DOWN_SWIGLU, nproj 3: P[0] = down, P[1] = gate, P[2] = up.
+ *   For row p of expert e with token t = gather[p] / gather_div and gate
+ *   weight wp = w_flat[sorted[p]]:
+ *     e_p   = dy[t] deq(Wd_e) + s (dy[t] Bd_e) Ad_e          (unweighted)
+ *     dh    = wp e_p;  sg = sigmoid(g);  dg = dh u sg (1 + g (1 - sg));
+ *     du    = dh g sg                       -> dg, du [M][I] bf16
+ *     dw_flat[sorted[p]] = <e_p, silu(g) u>  (= <dy[t], o_p>)   fp32
+ *     dgB[p] = dg Bg_e, duB[p] = du Bu_e     [M][rank] fp32
+ *     dA_d[e] = s sum_p (wp dy[t] Bd_e)^T h_p,  dB_d[e] = s sum_p (wp dy[t])^T xa_d[p]
+ *   Inputs: dy [T][H], g, u, h [M][I] bf16 (saved), xa_d [M][rank].
+ * GQ_BWD_GATEUP, nproj 2: P[0] = gate, P[1] = up.
+ *   dxrows[p] = dg deq(Wg_e) + du deq(Wu_e) + s (dgB[p] Ag_e + duB[p] Au_e)  bf16
+ *   dA_g[e] = s sum_p dgB[p]^T x_p,  dB_g[e] = s sum_p dg[p]^T xa_g[p]; same for up.
+ *   Inputs: x (activation rows via gather), dg, du, dgB, duB, xa (= [2][M][rank]).
+ * Adapter gradients of experts without rows are written as exact zeros.
+ */
+typedef struct gq_grouped_bwd_args {
+    const int32_t* offsets;  /* [E+1] */
+    int64_t M;
+    const int32_t* gather;   /* [M] row -> activation row * gather_div, or NULL */
+    int32_t gather_div;
+    /* DOWN_SWIGLU */
+    const uint16_t* dy;      /* [*][H] bf16, read through gather */
+    const float* w_flat;     /* [M] gate weights by assignment */
+    const int32_t* sorted;   /* [M] */
+    const uint16_t* g;       /* [M][I] */
+    const uint16_t* u;
+    const uint16_t* h;
+    const float* xa_d;       /* [M][rank] */
+    float* dw_flat;          /* [M] by assignment */
+    float* dA_d;             /* [E][rank][I] */
+    float* dB_d;             /* [E][H][rank] */
+    /* shared between the two modes */
+    uint16_t* dg;            /* [M][I] (written by DOWN_SWIGLU, read by GATEUP) */
+    uint16_t* du;
+    float* dgB;              /* [M][rank] */
+    float* duB;
+    /* GATEUP */
+    const uint16_t* x;       /* [*][H] bf16, read through gather */
+    const float* xa;         /* [2][M][rank] (xa_g, xa_u) */
+    uint16_t* dxrows;        /* [M][H] bf16 */
+    float* dA_g;             /* [E][rank][H] */
+    float* dB_g;             /* [E][I][rank] */
+    float* dA_u;
+    float* dB_u;
+} gq_grouped_bwd_args;
+
+size_t gq_grouped_mmq_lora_bwd_workspace_size(const gq_lora_linear* P, int32_t nproj,
+                                              int32_t mode, int64_t M);
+int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode,
+                            const gq_grouped_bwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * LM head + chunked cross entropy (head->n_experts must be 1; n_out = V
+ * vocabulary rows, n_in = H):
+ *   z     = h deq(W)^T + s (h A^T) B^T   (never stored whole)
+ *   lse   [T] fp32 log-sum-exp of each row of z (online over the vocabulary)
+ *   loss  (device scalar) = (1/N_valid) sum_{valid t} (lse_t - z[t][label_t])
+ * If dh != NULL also (the vocabulary walked in chunks of chunk_rows rows;
+ * G = grad_scale/N_valid (softmax(z) - onehot(label)), zero rows for ignored
+ * tokens):
+ *   dh [T][H] bf16 = G deq(W) + s (G B) A;  dA [rank][H] = s (G B)^T h;
+ *   dB [V][rank] = s G^T (h A^T)            (fp32, overwritten)
+ * labels [T] int64, each in [0, V) or == ignore_index.  With no valid label
+ * the loss and gradients are zero.  A label outside [0, V) that is not
+ * ignore_index is treated as ignored and sets the workspace's first 32-bit
+ * word to nonzero (GQ_EDEVICE condition, readable after synchronising).
+ * chunk_rows >= 1.
+ */
+size_t gq_lmhead_chunked_ce_workspace_size(const gq_lora_linear* head, int64_t T,
+                                           int64_t chunk_rows);
+int gq_lmhead_chunked_ce(const gq_lora_linear* head, const uint16_t* h, const int64_t* labels,
+                         int64_t T, int64_t chunk_rows, int64_t ignore_index, float grad_scale,
+                         float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

@@ -1,0 +1,353 @@
+"""Python binding of libgq (LoRA over a frozen GGUF block-quantised base, MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgq.so (C ABI declared in include/gq.h).  PyTorch provides device
+memory and the current HIP stream.  The library must be built
+(`python -m quantized_base_lora_amd.build`); importing the binding without it
+raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgq.so")
+
+GQ_OK, GQ_EINVAL, GQ_ENOTSUP, GQ_EWORKSPACE, GQ_EHIP, GQ_EDEVICE = 0, -1, -2, -3, -4, -5
+Q8_0, Q4_0, Q2_DM = 0, 1, 2
+F32, BF16 = 0, 1
+EPI_NONE, EPI_SWIGLU = 0, 1
+BWD_DOWN_SWIGLU, BWD_GATEUP = 0, 1
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q2_DM: 12}
+
+EXPORTS = (
+    "gq_version", "gq_last_error", "gq_block_bytes", "gq_dequant",
+    "gq_linear_lora_fwd_workspace_size", "gq_linear_lora_fwd",
+    "gq_linear_lora_bwd_workspace_size", "gq_linear_lora_bwd",
+    "gq_moe_route_workspace_size", "gq_moe_route", "gq_moe_route_bwd",
+    "gq_moe_combine_fwd", "gq_moe_combine_bwd",
+    "gq_grouped_mmq_lora_fwd_workspace_size", "gq_grouped_mmq_lora_fwd",
+    "gq_grouped_mmq_lora_bwd_workspace_size", "gq_grouped_mmq_lora_bwd",
+    "gq_lmhead_chunked_ce_workspace_size", "gq_lmhead_chunked_ce",
+)
+
+
+class GQError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gq error {code}: {msg}")
+        self.code = code
+
+
+class LoraLinear(C.Structure):
+    _fields_ = [("qtype", C.c_int32), ("rank", C.c_int32), ("n_out", C.c_int64),
+                ("n_in", C.c_int64), ("w_blocks", C.c_void_p), ("A", C.c_void_p),
+                ("B", C.c_void_p), ("scale", C.c_float), ("n_experts", C.c_int32)]
+
+
+class GroupedFwdArgs(C.Structure):
+    _fields_ = [("inp", C.c_void_p), ("gather", C.c_void_p), ("gather_div", C.c_int32),
+                ("offsets", C.c_void_p), ("M", C.c_int64), ("out", C.c_void_p),
+                ("save_g", C.c_void_p), ("save_u", C.c_void_p), ("xa", C.c_void_p)]
+
+
+class GroupedBwdArgs(C.Structure):
+    _fields_ = [("offsets", C.c_void_p), ("M", C.c_int64), ("gather", C.c_void_p),
+                ("gather_div", C.c_int32),
+                ("dy", C.c_void_p), ("w_flat", C.c_void_p), ("sorted", C.c_void_p),
+                ("g", C.c_void_p), ("u", C.c_void_p), ("h", C.c_void_p), ("xa_d", C.c_void_p),
+                ("dw_flat", C.c_void_p), ("dA_d", C.c_void_p), ("dB_d", C.c_void_p),
+                ("dg", C.c_void_p), ("du", C.c_void_p), ("dgB", C.c_void_p), ("duB", C.c_void_p),
+                ("x", C.c_void_p), ("xa", C.c_void_p), ("dxrows", C.c_void_p),
+                ("dA_g", C.c_void_p), ("dB_g", C.c_void_p), ("dA_u", C.c_void_p),
+                ("dB_u", C.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgq.so and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libgq.so not built at {path}; run python -m quantized_base_lora_amd.build")
+    lib = C.CDLL(path)
+    vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    P = C.POINTER
+    sig = {
+        "gq_version": (C.c_int, []),
+        "gq_last_error": (C.c_char_p, []),
+        "gq_block_bytes": (i64, [C.c_int]),
+        "gq_dequant": (C.c_int, [C.c_int, vp, i64, i64, C.c_int, vp, vp]),
+        "gq_linear_lora_fwd_workspace_size": (sz, [P(LoraLinear), i64]),
+        "gq_linear_lora_fwd": (C.c_int, [P(LoraLinear), vp, i64, vp, vp, vp, sz, vp]),
+        "gq_linear_lora_bwd_workspace_size": (sz, [P(LoraLinear), i64]),
+        "gq_linear_lora_bwd": (C.c_int, [P(LoraLinear), vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "gq_moe_route_workspace_size": (sz, [i64, i32, i32]),
+        "gq_moe_route": (C.c_int, [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gq_moe_route_bwd": (C.c_int, [vp, vp, vp, i64, i32, i32, vp, vp]),
+        "gq_moe_combine_fwd": (C.c_int, [vp, vp, vp, i64, i32, i64, vp, vp]),
+        "gq_moe_combine_bwd": (C.c_int, [vp, vp, i64, i32, i64, vp, vp]),
+        "gq_grouped_mmq_lora_fwd_workspace_size": (sz, [P(LoraLinear), i32, i64]),
+        "gq_grouped_mmq_lora_fwd": (C.c_int, [P(LoraLinear), i32, i32, P(GroupedFwdArgs), vp, sz, vp]),
+        "gq_grouped_mmq_lora_bwd_workspace_size": (sz, [P(LoraLinear), i32, i32, i64]),
+        "gq_grouped_mmq_lora_bwd": (C.c_int, [P(LoraLinear), i32, i32, P(GroupedBwdArgs), vp, sz, vp]),
+        "gq_lmhead_chunked_ce_workspace_size": (sz, [P(LoraLinear), i64, i64]),
+        "gq_lmhead_chunked_ce": (C.c_int, [P(LoraLinear), vp, vp, i64, i64, i64, f32, vp, vp, vp,
+                                           vp, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def lib():
+    return load_library()
+
+
+def last_error() -> str:
+    return lib().gq_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != GQ_OK:
+        raise GQError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Proj:
+    """A quantised projection (or E stacked experts) with its LoRA adapter.
+    blocks: uint8 [E?, n_out, n_in/32*bs]; A: fp32 [E?, r, n_in]; B: fp32 [E?, n_out, r]."""
+    qtype: int
+    n_out: int
+    n_in: int
+    blocks: torch.Tensor
+    A: torch.Tensor
+    B: torch.Tensor
+    scale: float
+    n_experts: int = 1
+
+    @property
+    def rank(self) -> int:
+        return self.A.shape[-2]
+
+    def c(self) -> LoraLinear:
+        return LoraLinear(self.qtype, self.rank, self.n_out, self.n_in, _ptr(self.blocks),
+                          _ptr(self.A), _ptr(self.B), float(self.scale), self.n_experts)
+
+
+# ------------------------------------------------------------------ entry points
+def dequant(qtype: int, blocks: torch.Tensor, rows: int, cols: int, out_dtype=torch.float32):
+    out = torch.empty((rows, cols), dtype=out_dtype, device=blocks.device)
+    code = F32 if out_dtype == torch.float32 else BF16
+    _check(lib().gq_dequant(qtype, _ptr(blocks), rows, cols, code, _ptr(out), _stream()))
+    return out
+
+
+def linear_lora_fwd(p: Proj, x: torch.Tensor):
+    T = x.shape[0]
+    y = torch.empty((T, p.n_out), dtype=torch.bfloat16, device=x.device)
+    xa = torch.empty((T, p.rank), dtype=torch.float32, device=x.device)
+    L = p.c()
+    nbytes = lib().gq_linear_lora_fwd_workspace_size(C.byref(L), T)
+    ws = _workspace(nbytes, x.device)
+    _check(lib().gq_linear_lora_fwd(C.byref(L), _ptr(x), T, _ptr(y), _ptr(xa), _ptr(ws), nbytes,
+                                    _stream()))
+    return y, xa
+
+
+def linear_lora_bwd(p: Proj, x, xa, dy, need_dx: bool = True, ws: torch.Tensor | None = None):
+    T = x.shape[0]
+    dx = torch.empty((T, p.n_in), dtype=torch.bfloat16, device=x.device) if need_dx else None
+    dA = torch.empty((p.rank, p.n_in), dtype=torch.float32, device=x.device)
+    dB = torch.empty((p.n_out, p.rank), dtype=torch.float32, device=x.device)
+    L = p.c()
+    nbytes = lib().gq_linear_lora_bwd_workspace_size(C.byref(L), T)
+    if ws is None or ws.numel() < nbytes:
+        ws = _workspace(nbytes, x.device)
+    _check(lib().gq_linear_lora_bwd(C.byref(L), _ptr(x), _ptr(xa), _ptr(dy), T, _ptr(dx), _ptr(dA),
+                                    _ptr(dB), _ptr(ws), nbytes, _stream()))
+    return dx, dA, dB
+
+
+def moe_route(logits: torch.Tensor, k: int):
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sorted_ = torch.empty(T * k, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nbytes = lib().gq_moe_route_workspace_size(T, E, k)
+    ws = _workspace(nbytes, dev)
+    _check(lib().gq_moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(sorted_),
+                              _ptr(offsets), _ptr(pos), _ptr(ws), nbytes, _stream()))
+    return ids, w, sorted_, offsets, pos
+
+
+def moe_route_bwd(ids, w, dw, E: int):
+    T, k = ids.shape
+    dl = torch.empty((T, E), dtype=torch.float32, device=ids.device)
+    _check(lib().gq_moe_route_bwd(_ptr(ids), _ptr(w), _ptr(dw), T, E, k, _ptr(dl), _stream()))
+    return dl
+
+
+def moe_combine_fwd(o, w, pos, T: int, k: int):
+    H = o.shape[1]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=o.device)
+    _check(lib().gq_moe_combine_fwd(_ptr(o), _ptr(w), _ptr(pos), T, k, H, _ptr(y), _stream()))
+    return y
+
+
+def moe_combine_bwd(dxrows, pos, T: int, k: int):
+    H = dxrows.shape[1]
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dxrows.device)
+    _check(lib().gq_moe_combine_bwd(_ptr(dxrows), _ptr(pos), T, k, H, _ptr(dx), _stream()))
+    return dx
+
+
+def _projs(ps):
+    arr = (LoraLinear * len(ps))(*[p.c() for p in ps])
+    return arr
+
+
+def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, offsets, M: int):
+    dev = inp.device
+    N = projs[0].n_out
+    r = projs[0].rank
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    g = u = None
+    if epilogue == EPI_SWIGLU:
+        g = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        u = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xa = torch.empty((len(projs), M, r), dtype=torch.float32, device=dev)
+    arr = _projs(projs)
+    nbytes = lib().gq_grouped_mmq_lora_fwd_workspace_size(arr, len(projs), M)
+    ws = _workspace(nbytes, dev)
+    a = GroupedFwdArgs(_ptr(inp), _ptr(gather), gather_div, _ptr(offsets), M, _ptr(out), _ptr(g),
+                       _ptr(u), _ptr(xa))
+    _check(lib().gq_grouped_mmq_lora_fwd(arr, len(projs), epilogue, C.byref(a), _ptr(ws), nbytes,
+                                         _stream()))
+    return out, g, u, xa
+
+
+def grouped_mmq_lora_bwd(projs, mode: int, **t):
+    """Thin wrapper: `t` maps gq_grouped_bwd_args field names to tensors/ints."""
+    arr = _projs(projs)
+    M = int(t["M"])
+    dev = t["offsets"].device
+    nbytes = lib().gq_grouped_mmq_lora_bwd_workspace_size(arr, len(projs), mode, M)
+    ws = t.pop("ws", None)
+    if ws is None or ws.numel() < nbytes:
+        ws = _workspace(nbytes, dev)
+    a = GroupedBwdArgs()
+    for name, _ in GroupedBwdArgs._fields_:
+        v = t.get(name)
+        if v is None:
+            continue
+        setattr(a, name, v if isinstance(v, int) else _ptr(v))
+    if not t.get("gather_div"):
+        a.gather_div = 1
+    _check(lib().gq_grouped_mmq_lora_bwd(arr, len(projs), mode, C.byref(a), _ptr(ws), nbytes,
+                                         _stream()))
+
+
+def lmhead_chunked_ce(head: Proj, h, labels, chunk_rows: int = 4096, ignore_index: int = -100,
+                      grad_scale: float = 1.0, want_grad: bool = True, ws=None):
+    T = h.shape[0]
+    dev = h.device
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dh = dA = dB = None
+    if want_grad:
+        dh = torch.empty((T, head.n_in), dtype=torch.bfloat16, device=dev)
+        dA = torch.empty((head.rank, head.n_in), dtype=torch.float32, device=dev)
+        dB = torch.empty((head.n_out, head.rank), dtype=torch.float32, device=dev)
+    L = head.c()
+    nbytes = lib().gq_lmhead_chunked_ce_workspace_size(C.byref(L), T, chunk_rows)
+    if ws is None or ws.numel() < nbytes:
+        ws = _workspace(nbytes, dev)
+    _check(lib().gq_lmhead_chunked_ce(C.byref(L), _ptr(h), _ptr(labels), T, chunk_rows,
+                                      ignore_index, grad_scale, _ptr(loss), _ptr(lse), _ptr(dh),
+                                      _ptr(dA), _ptr(dB), _ptr(ws), nbytes, _stream()))
+    return dict(loss=loss, lse=lse, dh=dh, dA=dA, dB=dB, ws=ws)
+
+
+# ------------------------------------------------------------ MoE layer helpers
+@dataclass
+class MoEWeights:
+    gate: Proj
+    up: Proj
+    down: Proj
+
+
+def moe_ffn_fwd(wts: MoEWeights, x, logits, k: int):
+    """Routed SwiGLU expert FFN forward: routing, grouped gate/up MMQ with the
+    SwiGLU epilogue, grouped down MMQ, combine.  Returns y and the saved state."""
+    T = x.shape[0]
+    ids, w, sorted_, offsets, pos = moe_route(logits, k)
+    M = T * k
+    h, g, u, xa_gu = grouped_mmq_lora_fwd([wts.gate, wts.up], EPI_SWIGLU, x, sorted_, k, offsets, M)
+    o, _, _, xa_d = grouped_mmq_lora_fwd([wts.down], EPI_NONE, h, None, 1, offsets, M)
+    y = moe_combine_fwd(o, w, pos, T, k)
+    saved = dict(ids=ids, w=w, sorted=sorted_, offsets=offsets, pos=pos, g=g, u=u, h=h,
+                 xa_gu=xa_gu, xa_d=xa_d[0], o=o)
+    return y, saved
+
+
+def moe_ffn_bwd(wts: MoEWeights, x, dy, saved, k: int, E: int):
+    """Backward of moe_ffn_fwd: returns dx, dlogits and the adapter gradients."""
+    T, H = x.shape
+    M = T * k
+    I = wts.gate.n_out
+    r = wts.gate.rank
+    dev = x.device
+    f32, bf = torch.float32, torch.bfloat16
+    dg = torch.empty((M, I), dtype=bf, device=dev)
+    du = torch.empty((M, I), dtype=bf, device=dev)
+    dgB = torch.empty((M, r), dtype=f32, device=dev)
+    duB = torch.empty((M, r), dtype=f32, device=dev)
+    dw_flat = torch.empty(M, dtype=f32, device=dev)
+    grads = dict(dA_d=torch.empty((E, r, I), dtype=f32, device=dev),
+                 dB_d=torch.empty((E, H, r), dtype=f32, device=dev),
+                 dA_g=torch.empty((E, r, H), dtype=f32, device=dev),
+                 dB_g=torch.empty((E, I, r), dtype=f32, device=dev),
+                 dA_u=torch.empty((E, r, H), dtype=f32, device=dev),
+                 dB_u=torch.empty((E, I, r), dtype=f32, device=dev))
+    grouped_mmq_lora_bwd([wts.down, wts.gate, wts.up], BWD_DOWN_SWIGLU, offsets=saved["offsets"],
+                         M=M, gather=saved["sorted"], gather_div=k, dy=dy, w_flat=saved["w"],
+                         sorted=saved["sorted"], g=saved["g"], u=saved["u"], h=saved["h"],
+                         xa_d=saved["xa_d"], dw_flat=dw_flat, dA_d=grads["dA_d"],
+                         dB_d=grads["dB_d"], dg=dg, du=du, dgB=dgB, duB=duB)
+    dxrows = torch.empty((M, H), dtype=bf, device=dev)
+    grouped_mmq_lora_bwd([wts.gate, wts.up], BWD_GATEUP, offsets=saved["offsets"], M=M,
+                         gather=saved["sorted"], gather_div=k, x=x, xa=saved["xa_gu"], dg=dg,
+                         du=du, dgB=dgB, duB=duB, dxrows=dxrows, dA_g=grads["dA_g"],
+                         dB_g=grads["dB_g"], dA_u=grads["dA_u"], dB_u=grads["dB_u"])
+    dx = moe_combine_bwd(dxrows, saved["pos"], T, k)
+    dlogits = moe_route_bwd(saved["ids"], saved["w"], dw_flat.view(T, k), E)
+    return dict(dx=dx, dlogits=dlogits, dw=dw_flat.view(T, k), **grads)

@@ -1,0 +1,766 @@
+// C ABI of libgq: argument validation (before any HIP call), workspace
+// planning and launch sequencing.  Every step of the computation runs in the
+// HIP kernels of gq_gemm.hip / gq_small.hip on the caller's stream.
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/gq.h"
+#include "gq_internal.h"
+
+using namespace gq;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                  \
+  do {                                       \
+    hipError_t _e = (expr);                  \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+int64_t block_bytes(int qtype) {
+  switch (qtype) {
+    case GQ_Q8_0: return 34;
+    case GQ_Q4_0: return 18;
+    case GQ_Q2_DM: return 12;
+    default: return -1;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+// With base == nullptr it only measures.
+struct Ws {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Ws(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <class T>
+  T* take(int64_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += (size_t)count * sizeof(T);
+    return p;
+  }
+  size_t size() const { return (off + 255) & ~(size_t)255; }
+};
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return GQ_OK;
+  if (!ws) return fail(GQ_EWORKSPACE, "workspace is NULL but %zu bytes are required", need);
+  if (!aligned(ws, 256)) return fail(GQ_EINVAL, "workspace must be 256-byte aligned");
+  if (have < need)
+    return fail(GQ_EWORKSPACE, "workspace too small: %zu bytes given, %zu required", have, need);
+  return GQ_OK;
+}
+
+int check_proj(const gq_lora_linear* L, const char* name, bool grouped) {
+  if (!L) return fail(GQ_EINVAL, "%s: NULL projection", name);
+  if (block_bytes(L->qtype) < 0) return fail(GQ_EINVAL, "%s: unknown qtype %d", name, L->qtype);
+  if (L->rank < 1 || L->rank > 16) return fail(GQ_EINVAL, "%s: rank %d not in [1, 16]", name, L->rank);
+  if (L->n_in < 64 || L->n_in % 64)
+    return fail(GQ_ENOTSUP, "%s: n_in %lld must be a positive multiple of 64", name,
+                (long long)L->n_in);
+  if (L->n_out < 8 || L->n_out % 8)
+    return fail(GQ_ENOTSUP, "%s: n_out %lld must be a positive multiple of 8", name,
+                (long long)L->n_out);
+  if (L->n_in > INT_MAX / 2 || L->n_out > INT_MAX / 2)
+    return fail(GQ_ENOTSUP, "%s: dimension too large", name);
+  if (!grouped && L->n_experts != 1)
+    return fail(GQ_EINVAL, "%s: n_experts must be 1 here (got %d)", name, L->n_experts);
+  if (L->n_experts < 1 || L->n_experts > 1024)
+    return fail(GQ_EINVAL, "%s: n_experts %d not in [1, 1024]", name, L->n_experts);
+  if (!L->w_blocks || !L->A || !L->B) return fail(GQ_EINVAL, "%s: NULL weight or adapter", name);
+  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 4) || !aligned(L->B, 4))
+    return fail(GQ_EINVAL, "%s: weight/adapter pointers must be 4-byte aligned", name);
+  return GQ_OK;
+}
+
+int64_t rowbytes(const gq_lora_linear* L) { return (L->n_in / 32) * block_bytes(L->qtype); }
+int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// tile configuration: 128-row tiles unless that leaves the chip underfilled
+int pick_tile(int64_t rows_est, int64_t ntiles) {
+  const int64_t t128 = (int64_t)cdiv(rows_est, 128) * ntiles;
+  return t128 < 512 ? TILE_64x128 : TILE_128x128;
+}
+
+GemmArgs gemm_defaults() {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.asplit = INT_MAX;
+  a.wsplit = INT_MAX;
+  a.gdiv = 1;
+  a.E = 1;
+  return a;
+}
+
+constexpr int RC = 256;  // rows per partial-reduction chunk
+
+hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
+
+}  // namespace
+
+extern "C" {
+
+int gq_version(void) { return 100; }
+
+const char* gq_last_error(void) { return g_err.c_str(); }
+
+int64_t gq_block_bytes(int qtype) { return block_bytes(qtype); }
+
+// ------------------------------------------------------------------ dequant
+int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype, void* out,
+               void* stream) {
+  g_err.clear();
+  if (block_bytes(qtype) < 0) return fail(GQ_EINVAL, "gq_dequant: unknown qtype %d", qtype);
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return fail(GQ_EINVAL, "gq_dequant: rows >= 0 and cols a positive multiple of 32 required");
+  if (out_dtype != GQ_F32 && out_dtype != GQ_BF16)
+    return fail(GQ_EINVAL, "gq_dequant: unknown out_dtype %d", out_dtype);
+  if (rows == 0) return GQ_OK;
+  if (!blocks || !out) return fail(GQ_EINVAL, "gq_dequant: NULL pointer");
+  if (!aligned(blocks, 2) || !aligned(out, 16))
+    return fail(GQ_EINVAL, "gq_dequant: blocks must be 2-byte and out 16-byte aligned");
+  HIP_TRY(launch_dequant(qtype, blocks, rows, cols, out_dtype == GQ_BF16, out, S(stream)),
+          "gq_dequant");
+  return GQ_OK;
+}
+
+// ------------------------------------------------------------------- linear
+size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear*, int64_t) { return 0; }
+
+int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
+                       float* xa, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_proj(L, "gq_linear_lora_fwd", false);
+  if (rc) return rc;
+  if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_linear_lora_fwd: bad T %lld", (long long)T);
+  if (T == 0) return GQ_OK;
+  if (!x || !y || !xa) return fail(GQ_EINVAL, "gq_linear_lora_fwd: NULL x, y or xa");
+  if (!aligned(x, 16) || !aligned(y, 2) || !aligned(xa, 4))
+    return fail(GQ_EINVAL, "gq_linear_lora_fwd: x must be 16-byte aligned");
+  const hipStream_t st = S(stream);
+  const int r = L->rank, K = (int)L->n_in, N = (int)L->n_out;
+
+  RowDotArgs rd;
+  memset(&rd, 0, sizeof rd);
+  rd.M = T; rd.C = K; rd.r = r; rd.act = x; rd.lda = K; rd.gdiv = 1; rd.E = 1;
+  rd.W[0] = L->A; rd.w_jstride = K; rd.w_cstride = 1; rd.out[0] = xa; rd.nout = 1;
+  HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_fwd: x A^T");
+
+  GemmArgs g = gemm_defaults();
+  g.M = T; g.N = N; g.K = K;
+  g.a0 = x; g.lda = K;
+  g.w0 = static_cast<const uint8_t*>(L->w_blocks);
+  g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
+  g.ntiles = cdiv(N, TILE_BN);
+  const int tc = pick_tile(T, g.ntiles);
+  g.mtiles = cdiv(T, tile_bm(tc));
+  g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
+  g.o0 = y; g.ldo = N;
+  HIP_TRY(launch_gemm(L->qtype, EPI_LIN, tc, g, st), "gq_linear_lora_fwd: MMQ");
+  return GQ_OK;
+}
+
+namespace {
+struct LinBwdWs {
+  float* dyB;
+  float* part;
+};
+LinBwdWs plan_lin_bwd(Ws& w, const gq_lora_linear* L, int64_t T) {
+  LinBwdWs p;
+  const int64_t slots = cdiv(T, RC);
+  const int64_t cmax = L->n_in > L->n_out ? L->n_in : L->n_out;
+  p.dyB = w.take<float>(T * L->rank);
+  p.part = w.take<float>(slots * cmax * L->rank);
+  return p;
+}
+}  // namespace
+
+size_t gq_linear_lora_bwd_workspace_size(const gq_lora_linear* L, int64_t T) {
+  if (!L || T <= 0 || L->rank < 1 || L->rank > 16) return 0;
+  Ws w(nullptr);
+  plan_lin_bwd(w, L, T);
+  return w.size();
+}
+
+int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                       const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_proj(L, "gq_linear_lora_bwd", false);
+  if (rc) return rc;
+  if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_linear_lora_bwd: bad T %lld", (long long)T);
+  if (!dA || !dB) return fail(GQ_EINVAL, "gq_linear_lora_bwd: NULL dA or dB");
+  const hipStream_t st = S(stream);
+  const int r = L->rank, K = (int)L->n_in, N = (int)L->n_out;
+  if (T == 0) {
+    HIP_TRY(launch_fill_f32(dA, (int64_t)r * K, 0.f, st), "gq_linear_lora_bwd: zero dA");
+    HIP_TRY(launch_fill_f32(dB, (int64_t)N * r, 0.f, st), "gq_linear_lora_bwd: zero dB");
+    return GQ_OK;
+  }
+  if (!x || !xa || !dy) return fail(GQ_EINVAL, "gq_linear_lora_bwd: NULL x, xa or dy");
+  if (!aligned(x, 16) || !aligned(dy, 16) || (dx && !aligned(dx, 2)))
+    return fail(GQ_EINVAL, "gq_linear_lora_bwd: x and dy must be 16-byte aligned");
+  Ws meas(nullptr);
+  plan_lin_bwd(meas, L, T);
+  if ((rc = check_ws(ws, ws_bytes, meas.size()))) return rc;
+  Ws w(ws);
+  const LinBwdWs P = plan_lin_bwd(w, L, T);
+  const int slots = cdiv(T, RC);
+
+  RowDotArgs rd;
+  memset(&rd, 0, sizeof rd);
+  rd.M = T; rd.C = N; rd.r = r; rd.act = dy; rd.lda = N; rd.gdiv = 1; rd.E = 1;
+  rd.W[0] = L->B; rd.w_jstride = 1; rd.w_cstride = r; rd.out[0] = P.dyB; rd.nout = 1;
+  HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_bwd: dY B");
+
+  ColRedArgs cr;
+  memset(&cr, 0, sizeof cr);
+  cr.M = T; cr.C = N; cr.r = r; cr.U = dy; cr.ldu = N; cr.gdiv = 1; cr.Vv = xa;
+  cr.E = 1; cr.rc = RC; cr.slots = slots; cr.part = P.part;
+  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB partials");
+  HIP_TRY(launch_colred_finish(P.part, nullptr, 1, slots, N, r, L->scale, 0, dB, st),
+          "gq_linear_lora_bwd: dB");
+
+  if (dx) {
+    GemmArgs g = gemm_defaults();
+    g.M = T; g.N = K; g.K = N;
+    g.a0 = dy; g.lda = N;
+    g.w0 = static_cast<const uint8_t*>(L->w_blocks);
+    g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
+    g.ntiles = cdiv(K, TILE_BN);
+    const int tc = pick_tile(T, g.ntiles);
+    g.mtiles = cdiv(T, tile_bm(tc));
+    g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
+    g.o0 = dx; g.ldo = K;
+    HIP_TRY(launch_gemm(L->qtype, EPI_LIN_BWD, tc, g, st), "gq_linear_lora_bwd: dX MMQ");
+  }
+
+  cr.C = K; cr.U = x; cr.ldu = K; cr.Vv = P.dyB;
+  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dA partials");
+  HIP_TRY(launch_colred_finish(P.part, nullptr, 1, slots, K, r, L->scale, 1, dA, st),
+          "gq_linear_lora_bwd: dA");
+  return GQ_OK;
+}
+
+// ------------------------------------------------------------------ routing
+size_t gq_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T <= 0 || E < 1 || k < 1) return 0;
+  return (route_ws_bytes(T, E, k) + 255) & ~(size_t)255;
+}
+
+int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                 int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                 void* stream) {
+  g_err.clear();
+  if (E < 1 || E > 1024) return fail(GQ_EINVAL, "gq_moe_route: E %d not in [1, 1024]", E);
+  if (k < 1 || k > 16 || k > E) return fail(GQ_EINVAL, "gq_moe_route: k %d not in [1, min(E, 16)]", k);
+  if (T < 0 || T * k > INT_MAX) return fail(GQ_EINVAL, "gq_moe_route: bad T %lld", (long long)T);
+  if (!offsets) return fail(GQ_EINVAL, "gq_moe_route: NULL offsets");
+  const hipStream_t st = S(stream);
+  if (T == 0) {
+    HIP_TRY(launch_fill_f32(reinterpret_cast<float*>(offsets), E + 1, 0.f, st), "gq_moe_route");
+    return GQ_OK;
+  }
+  if (!logits || !ids || !w || !sorted || !pos) return fail(GQ_EINVAL, "gq_moe_route: NULL pointer");
+  int rc = check_ws(ws, ws_bytes, gq_moe_route_workspace_size(T, E, k));
+  if (rc) return rc;
+  HIP_TRY(launch_route(logits, T, E, k, ids, w, sorted, offsets, pos, ws, st), "gq_moe_route");
+  return GQ_OK;
+}
+
+int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
+                     int32_t k, float* dlogits, void* stream) {
+  g_err.clear();
+  if (E < 1 || E > 1024 || k < 1 || k > 16 || k > E)
+    return fail(GQ_EINVAL, "gq_moe_route_bwd: bad E %d / k %d", E, k);
+  if (T < 0) return fail(GQ_EINVAL, "gq_moe_route_bwd: bad T");
+  if (T == 0) return GQ_OK;
+  if (!ids || !w || !dw || !dlogits) return fail(GQ_EINVAL, "gq_moe_route_bwd: NULL pointer");
+  HIP_TRY(launch_route_bwd(ids, w, dw, T, E, k, dlogits, S(stream)), "gq_moe_route_bwd");
+  return GQ_OK;
+}
+
+int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, int64_t T, int32_t k,
+                       int64_t H, uint16_t* y, void* stream) {
+  g_err.clear();
+  if (T < 0 || k < 1 || k > 16 || H < 8 || H % 8 || T * ((H + 2047) / 2048) > INT_MAX)
+    return fail(GQ_EINVAL, "gq_moe_combine_fwd: bad T/k/H (H must be a multiple of 8)");
+  if (T == 0) return GQ_OK;
+  if (!o || !w || !pos || !y) return fail(GQ_EINVAL, "gq_moe_combine_fwd: NULL pointer");
+  if (!aligned(o, 16) || !aligned(y, 16))
+    return fail(GQ_EINVAL, "gq_moe_combine_fwd: o and y must be 16-byte aligned");
+  HIP_TRY(launch_combine(o, w, pos, T, k, H, y, S(stream)), "gq_moe_combine_fwd");
+  return GQ_OK;
+}
+
+int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k, int64_t H,
+                       uint16_t* dx, void* stream) {
+  g_err.clear();
+  if (T < 0 || k < 1 || k > 16 || H < 8 || H % 8)
+    return fail(GQ_EINVAL, "gq_moe_combine_bwd: bad T/k/H (H must be a multiple of 8)");
+  if (T == 0) return GQ_OK;
+  if (!dxrows || !pos || !dx) return fail(GQ_EINVAL, "gq_moe_combine_bwd: NULL pointer");
+  if (!aligned(dxrows, 16) || !aligned(dx, 16))
+    return fail(GQ_EINVAL, "gq_moe_combine_bwd: dxrows and dx must be 16-byte aligned");
+  HIP_TRY(launch_combine(dxrows, nullptr, pos, T, k, H, dx, S(stream)), "gq_moe_combine_bwd");
+  return GQ_OK;
+}
+
+// ------------------------------------------------------------ grouped MMQ
+namespace {
+int check_group(const gq_lora_linear* P, int nproj, const char* name) {
+  for (int i = 0; i < nproj; ++i) {
+    int rc = check_proj(&P[i], name, true);
+    if (rc) return rc;
+  }
+  return GQ_OK;
+}
+bool same_shape(const gq_lora_linear& a, const gq_lora_linear& b) {
+  return a.qtype == b.qtype && a.rank == b.rank && a.n_out == b.n_out && a.n_in == b.n_in &&
+         a.n_experts == b.n_experts && a.scale == b.scale;
+}
+int64_t grouped_mtiles(int64_t M, int E, int bm) { return cdiv(M, bm) + E; }
+}  // namespace
+
+size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t, int64_t) {
+  if (!P) return 0;
+  Ws w(nullptr);
+  w.take<int32_t>(P->n_experts + 1);
+  return w.size();
+}
+
+int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epilogue,
+                            const gq_grouped_fwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_err.clear();
+  if (!P || !a) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: NULL argument");
+  if (!((epilogue == GQ_EPI_NONE && nproj == 1) || (epilogue == GQ_EPI_SWIGLU && nproj == 2)))
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: epilogue %d needs nproj %d", epilogue,
+                epilogue == GQ_EPI_SWIGLU ? 2 : 1);
+  int rc = check_group(P, nproj, "gq_grouped_mmq_lora_fwd");
+  if (rc) return rc;
+  if (nproj == 2 && !same_shape(P[0], P[1]))
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: gate and up projections differ in shape");
+  const int64_t M = a->M;
+  if (M < 0 || M > INT_MAX) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: bad M");
+  if (!a->offsets) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: NULL offsets");
+  if (M == 0) return GQ_OK;
+  if (!a->in || !a->out || !a->xa) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: NULL in/out/xa");
+  if (epilogue == GQ_EPI_SWIGLU && (!a->save_g || !a->save_u))
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: SWIGLU needs save_g and save_u");
+  if (a->gather_div < 1) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: gather_div < 1");
+  if (!aligned(a->in, 16)) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: in must be 16-byte aligned");
+  if ((rc = check_ws(ws, ws_bytes, gq_grouped_mmq_lora_fwd_workspace_size(P, nproj, M)))) return rc;
+  const hipStream_t st = S(stream);
+  const int E = P->n_experts, r = P->rank, K = (int)P->n_in, N = (int)P->n_out;
+  Ws w(ws);
+  int32_t* ts = w.take<int32_t>(E + 1);
+
+  RowDotArgs rd;
+  memset(&rd, 0, sizeof rd);
+  rd.M = M; rd.C = K; rd.r = r; rd.act = a->in; rd.lda = K; rd.gather = a->gather;
+  rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E;
+  rd.w_estride = (int64_t)r * K; rd.w_jstride = K; rd.w_cstride = 1; rd.nout = nproj;
+  for (int i = 0; i < nproj; ++i) {
+    rd.W[i] = P[i].A;
+    rd.out[i] = a->xa + (int64_t)i * M * r;
+  }
+  HIP_TRY(launch_rowdot(rd, st), "gq_grouped_mmq_lora_fwd: in A^T");
+
+  GemmArgs g = gemm_defaults();
+  g.M = M; g.K = K;
+  g.a0 = a->in; g.lda = K; g.gather = a->gather; g.gdiv = a->gather_div;
+  g.w0 = static_cast<const uint8_t*>(P[0].w_blocks);
+  g.w1 = nproj == 2 ? static_cast<const uint8_t*>(P[1].w_blocks) : nullptr;
+  g.w_rowbytes = rowbytes(P); g.w_estride = (int64_t)N * g.w_rowbytes; g.w_nb = K / 32;
+  g.w_rows = N;
+  g.E = E; g.offsets = a->offsets; g.tile_start = ts;
+  g.s = P->scale; g.r = r;
+  g.lB0 = P[0].B; g.lB1 = nproj == 2 ? P[1].B : nullptr; g.lB_estride = (int64_t)N * r;
+  g.rv0 = a->xa; g.rv1 = nproj == 2 ? a->xa + M * r : nullptr;
+  g.o0 = a->out; g.o1 = a->save_g; g.o2 = a->save_u; g.ldo = N;
+  int epi;
+  if (epilogue == GQ_EPI_SWIGLU) {
+    g.N = 2 * N;
+    g.ntiles = cdiv(N, TILE_BN / 2);
+    epi = EPI_SWIGLU;
+  } else {
+    g.N = N;
+    g.ntiles = cdiv(N, TILE_BN);
+    epi = EPI_LIN;
+  }
+  const int tc = pick_tile(M, g.ntiles);
+  g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
+  HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), ts, st), "gq_grouped_mmq_lora_fwd: tiles");
+  HIP_TRY(launch_gemm(P->qtype, epi, tc, g, st), "gq_grouped_mmq_lora_fwd: grouped MMQ");
+  return GQ_OK;
+}
+
+namespace {
+struct GrpBwdWs {
+  int32_t* ts;
+  int32_t* cs;
+  float* dyB;
+  float* wdyB;
+  float* wxa;
+  float* part_down;
+  float* part;
+};
+GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
+  GrpBwdWs p;
+  memset(&p, 0, sizeof p);
+  const int E = P->n_experts, r = P->rank;
+  p.ts = w.take<int32_t>(E + 1);
+  p.cs = w.take<int32_t>(E + 1);
+  const int64_t slots = grouped_mtiles(M, E, RC);
+  if (mode == GQ_BWD_DOWN_SWIGLU) {
+    const int64_t H = P[0].n_out, I = P[0].n_in;
+    p.dyB = w.take<float>(M * r);
+    p.wdyB = w.take<float>(M * r);
+    p.wxa = w.take<float>(M * r);
+    p.part_down = w.take<float>((int64_t)cdiv(I, TILE_BN) * M * (1 + 2 * r));
+    p.part = w.take<float>(slots * (H > I ? H : I) * r);
+  } else {
+    const int64_t H = P[0].n_in, I = P[0].n_out;
+    p.part = w.take<float>(slots * (H > I ? H : I) * r);
+  }
+  return p;
+}
+}  // namespace
+
+size_t gq_grouped_mmq_lora_bwd_workspace_size(const gq_lora_linear* P, int32_t nproj,
+                                              int32_t mode, int64_t M) {
+  if (!P || M <= 0 || nproj < 1) return 0;
+  Ws w(nullptr);
+  plan_grp_bwd(w, P, mode, M);
+  return w.size();
+}
+
+int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode,
+                            const gq_grouped_bwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_err.clear();
+  if (!P || !a) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL argument");
+  const hipStream_t st = S(stream);
+  const int64_t M = a->M;
+  if (M < 0 || M > INT_MAX) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: bad M");
+  if (!a->offsets) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL offsets");
+  if (a->gather_div < 1) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: gather_div < 1");
+  int rc;
+  if (mode == GQ_BWD_DOWN_SWIGLU) {
+    if (nproj != 3) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: DOWN_SWIGLU needs nproj 3");
+    if ((rc = check_group(P, 3, "gq_grouped_mmq_lora_bwd"))) return rc;
+    if (!same_shape(P[1], P[2]) || P[0].n_in != P[1].n_out || P[0].n_out != P[1].n_in ||
+        P[0].rank != P[1].rank || P[0].n_experts != P[1].n_experts || P[0].scale != P[1].scale)
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: down/gate/up shapes do not form an FFN");
+  } else if (mode == GQ_BWD_GATEUP) {
+    if (nproj != 2) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: GATEUP needs nproj 2");
+    if ((rc = check_group(P, 2, "gq_grouped_mmq_lora_bwd"))) return rc;
+    if (!same_shape(P[0], P[1]))
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: gate and up projections differ in shape");
+  } else {
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: unknown mode %d", mode);
+  }
+  const int E = P->n_experts, r = P->rank;
+  const float s = P->scale;
+  if (M == 0) {
+    // no rows: every adapter gradient is exactly zero
+    if (mode == GQ_BWD_DOWN_SWIGLU) {
+      const int64_t H = P[0].n_out, I = P[0].n_in;
+      if (!a->dA_d || !a->dB_d) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL dA_d/dB_d");
+      HIP_TRY(launch_fill_f32(a->dA_d, (int64_t)E * r * I, 0.f, st), "zero dA_d");
+      HIP_TRY(launch_fill_f32(a->dB_d, (int64_t)E * H * r, 0.f, st), "zero dB_d");
+    } else {
+      const int64_t H = P[0].n_in, I = P[0].n_out;
+      if (!a->dA_g || !a->dB_g || !a->dA_u || !a->dB_u)
+        return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL adapter gradient");
+      HIP_TRY(launch_fill_f32(a->dA_g, (int64_t)E * r * H, 0.f, st), "zero dA_g");
+      HIP_TRY(launch_fill_f32(a->dA_u, (int64_t)E * r * H, 0.f, st), "zero dA_u");
+      HIP_TRY(launch_fill_f32(a->dB_g, (int64_t)E * I * r, 0.f, st), "zero dB_g");
+      HIP_TRY(launch_fill_f32(a->dB_u, (int64_t)E * I * r, 0.f, st), "zero dB_u");
+    }
+    return GQ_OK;
+  }
+  if ((rc = check_ws(ws, ws_bytes, gq_grouped_mmq_lora_bwd_workspace_size(P, nproj, mode, M))))
+    return rc;
+  Ws w(ws);
+  const GrpBwdWs W = plan_grp_bwd(w, P, mode, M);
+  const int slots = (int)grouped_mtiles(M, E, RC);
+  HIP_TRY(launch_tile_start(a->offsets, E, RC, W.cs, st), "gq_grouped_mmq_lora_bwd: chunks");
+
+  ColRedArgs cr;
+  memset(&cr, 0, sizeof cr);
+  cr.M = M; cr.r = r; cr.offsets = a->offsets; cr.chunk_start = W.cs; cr.E = E; cr.rc = RC;
+  cr.slots = slots; cr.part = W.part; cr.gdiv = 1;
+
+  if (mode == GQ_BWD_DOWN_SWIGLU) {
+    const int H = (int)P[0].n_out, I = (int)P[0].n_in;
+    if (!a->dy || !a->w_flat || !a->sorted || !a->g || !a->u || !a->h || !a->xa_d || !a->dw_flat ||
+        !a->dA_d || !a->dB_d || !a->dg || !a->du || !a->dgB || !a->duB)
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for DOWN_SWIGLU");
+    if (!aligned(a->dy, 16) || !aligned(a->h, 4) || !aligned(a->dg, 4) || !aligned(a->du, 4))
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: dy must be 16-byte aligned");
+    // dY Bd (unweighted) and its gate-weighted copy
+    RowDotArgs rd;
+    memset(&rd, 0, sizeof rd);
+    rd.M = M; rd.C = H; rd.r = r; rd.act = a->dy; rd.lda = H; rd.gather = a->gather;
+    rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E;
+    rd.W[0] = P[0].B; rd.w_estride = (int64_t)H * r; rd.w_jstride = 1; rd.w_cstride = r;
+    rd.out[0] = W.dyB; rd.nout = 1; rd.out2 = W.wdyB; rd.wflat = a->w_flat; rd.sorted = a->sorted;
+    HIP_TRY(launch_rowdot(rd, st), "gq_grouped_mmq_lora_bwd: dY Bd");
+    HIP_TRY(launch_scale_rows(a->xa_d, a->w_flat, a->sorted, M, r, W.wxa, st),
+            "gq_grouped_mmq_lora_bwd: w xa_d");
+
+    GemmArgs g = gemm_defaults();
+    g.M = M; g.N = I; g.K = H;
+    g.a0 = a->dy; g.lda = H; g.gather = a->gather; g.gdiv = a->gather_div;
+    g.w0 = static_cast<const uint8_t*>(P[0].w_blocks);
+    g.w_rowbytes = rowbytes(&P[0]); g.w_estride = (int64_t)H * g.w_rowbytes; g.w_nb = I / 32;
+    g.w_rows = H;
+    g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
+    g.ntiles = cdiv(I, TILE_BN);
+    const int tc = pick_tile(M, g.ntiles);
+    g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
+    g.s = s; g.r = r;
+    g.lA0 = P[0].A; g.lA_estride = (int64_t)r * I;
+    g.lB1 = P[1].B; g.lB2 = P[2].B; g.lB_estride = (int64_t)I * r;
+    g.rv0 = W.dyB; g.s0 = a->g; g.s1 = a->u; g.wflat = a->w_flat; g.sorted = a->sorted;
+    g.o0 = a->dg; g.o1 = a->du; g.ldo = I; g.f0 = W.part_down;
+    HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), W.ts, st), "gq_grouped_mmq_lora_bwd: tiles");
+    HIP_TRY(launch_gemm(P[0].qtype, EPI_DOWN_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: down MMQ");
+    HIP_TRY(launch_down_finish(W.part_down, g.ntiles, M, r, a->sorted, a->dw_flat, a->dgB, a->duB, st),
+            "gq_grouped_mmq_lora_bwd: dw, dgB, duB");
+
+    // dA_d[e] = s sum_p (w dY Bd)^T h ;  dB_d[e] = s sum_p dY^T (w xa_d)
+    cr.C = I; cr.U = a->h; cr.ldu = I; cr.Vv = W.wdyB;
+    HIP_TRY(launch_colred(cr, st), "dA_d partials");
+    HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 1, a->dA_d, st), "dA_d");
+    cr.C = H; cr.U = a->dy; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;
+    cr.Vv = W.wxa;
+    HIP_TRY(launch_colred(cr, st), "dB_d partials");
+    HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 0, a->dB_d, st), "dB_d");
+    return GQ_OK;
+  }
+
+  // GATEUP
+  const int H = (int)P[0].n_in, I = (int)P[0].n_out;
+  if (!a->x || !a->xa || !a->dg || !a->du || !a->dgB || !a->duB || !a->dxrows || !a->dA_g ||
+      !a->dB_g || !a->dA_u || !a->dB_u)
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for GATEUP");
+  if (!aligned(a->x, 16) || !aligned(a->dg, 16) || !aligned(a->du, 16))
+    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: x, dg, du must be 16-byte aligned");
+  GemmArgs g = gemm_defaults();
+  g.M = M; g.N = H; g.K = 2 * I;
+  g.a0 = a->dg; g.a1 = a->du; g.lda = I; g.asplit = I;
+  g.w0 = static_cast<const uint8_t*>(P[0].w_blocks);
+  g.w1 = static_cast<const uint8_t*>(P[1].w_blocks);
+  g.w_rowbytes = rowbytes(&P[0]); g.w_estride = (int64_t)I * g.w_rowbytes; g.w_nb = H / 32;
+  g.w_rows = I; g.wsplit = I;
+  g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
+  g.ntiles = cdiv(H, TILE_BN);
+  const int tc = pick_tile(M, g.ntiles);
+  g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
+  g.s = s; g.r = r;
+  g.lA0 = P[0].A; g.lA1 = P[1].A; g.lA_estride = (int64_t)r * H;
+  g.rv0 = a->dgB; g.rv1 = a->duB;
+  g.o0 = a->dxrows; g.ldo = H;
+  if (I % GEMM_BK)
+    return fail(GQ_ENOTSUP, "gq_grouped_mmq_lora_bwd: intermediate size must be a multiple of 64");
+  HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), W.ts, st), "gq_grouped_mmq_lora_bwd: tiles");
+  HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: gate/up MMQ");
+
+  cr.C = H; cr.U = a->x; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;
+  cr.Vv = a->dgB;
+  HIP_TRY(launch_colred(cr, st), "dA_g partials");
+  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 1, a->dA_g, st), "dA_g");
+  cr.Vv = a->duB;
+  HIP_TRY(launch_colred(cr, st), "dA_u partials");
+  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 1, a->dA_u, st), "dA_u");
+  cr.C = I; cr.U = a->dg; cr.ldu = I; cr.gather = nullptr; cr.gdiv = 1; cr.Vv = a->xa;
+  HIP_TRY(launch_colred(cr, st), "dB_g partials");
+  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 0, a->dB_g, st), "dB_g");
+  cr.U = a->du; cr.Vv = a->xa + M * r;
+  HIP_TRY(launch_colred(cr, st), "dB_u partials");
+  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 0, a->dB_u, st), "dB_u");
+  return GQ_OK;
+}
+
+// ---------------------------------------------------------------- LM head
+namespace {
+struct CeWs {
+  int32_t* err;
+  float* nvalid;
+  float* xa;
+  float* part_ml;
+  float* zlab;
+  float* term;
+  uint16_t* G;
+  float* dh_acc;
+  float* part_GB;
+  float* part_dB;
+  float* GB;
+  float* part;
+  int64_t ldG;
+  int mt;
+  int ntiles_bwd;
+  int tc_fwd, tc_bwd, tc_dh;
+};
+CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad) {
+  CeWs p;
+  memset(&p, 0, sizeof p);
+  const int64_t V = L->n_out, H = L->n_in, r = L->rank;
+  p.err = w.take<int32_t>(64);
+  p.nvalid = w.take<float>(64);
+  p.xa = w.take<float>(T * r);
+  const int nt_v = cdiv(V, TILE_BN);
+  p.tc_fwd = pick_tile(T, nt_v);
+  p.part_ml = w.take<float>((int64_t)nt_v * T * 2);
+  p.zlab = w.take<float>(T);
+  p.term = w.take<float>(T);
+  if (grad) {
+    const int64_t C = chunk < V ? chunk : V;
+    p.ldG = (C + 63) / 64 * 64;
+    p.G = w.take<uint16_t>(T * p.ldG);
+    p.dh_acc = w.take<float>(T * H);
+    int64_t ntb = 0;
+    for (int64_t c0 = 0; c0 < V; c0 += chunk) ntb += cdiv((V - c0) < chunk ? V - c0 : chunk, TILE_BN);
+    p.ntiles_bwd = (int)ntb;
+    p.part_GB = w.take<float>(ntb * T * r);
+    p.tc_bwd = pick_tile(T, cdiv(C, TILE_BN));
+    p.mt = cdiv(T, tile_bm(p.tc_bwd));
+    p.part_dB = w.take<float>((int64_t)p.mt * V * r);
+    p.GB = w.take<float>(T * r);
+    p.part = w.take<float>((int64_t)cdiv(T, RC) * H * r);
+    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN));
+  }
+  return p;
+}
+}  // namespace
+
+size_t gq_lmhead_chunked_ce_workspace_size(const gq_lora_linear* L, int64_t T, int64_t chunk) {
+  if (!L || T <= 0 || chunk < 1 || L->rank < 1 || L->n_out < 1) return 0;
+  Ws w(nullptr);
+  plan_ce(w, L, T, chunk, true);
+  return w.size();
+}
+
+int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64_t* labels,
+                         int64_t T, int64_t chunk, int64_t ignore_index, float grad_scale,
+                         float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_proj(L, "gq_lmhead_chunked_ce", false);
+  if (rc) return rc;
+  if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: bad T");
+  if (chunk < 1) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: chunk_rows must be >= 1");
+  if (!loss) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: NULL loss");
+  const bool grad = dh != nullptr;
+  if (grad && (!dA || !dB)) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: dh needs dA and dB");
+  const hipStream_t st = S(stream);
+  const int64_t V = L->n_out;
+  const int H = (int)L->n_in, r = L->rank;
+  if (T == 0) {
+    HIP_TRY(launch_fill_f32(loss, 1, 0.f, st), "gq_lmhead_chunked_ce");
+    if (grad) {
+      HIP_TRY(launch_fill_f32(dA, (int64_t)r * H, 0.f, st), "gq_lmhead_chunked_ce");
+      HIP_TRY(launch_fill_f32(dB, V * r, 0.f, st), "gq_lmhead_chunked_ce");
+    }
+    return GQ_OK;
+  }
+  if (!h || !labels || !lse) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: NULL h, labels or lse");
+  if (!aligned(h, 16) || (grad && !aligned(dh, 2)))
+    return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: h must be 16-byte aligned");
+  if (chunk > V) chunk = V;
+  if (chunk > INT_MAX / 2) return fail(GQ_ENOTSUP, "gq_lmhead_chunked_ce: chunk too large");
+  Ws meas(nullptr);
+  plan_ce(meas, L, T, chunk, grad);
+  if ((rc = check_ws(ws, ws_bytes, meas.size()))) return rc;
+  Ws w(ws);
+  const CeWs P = plan_ce(w, L, T, chunk, grad);
+
+  HIP_TRY(launch_ce_prep(labels, T, V, ignore_index, P.err, P.nvalid, st), "ce: labels");
+  RowDotArgs rd;
+  memset(&rd, 0, sizeof rd);
+  rd.M = T; rd.C = H; rd.r = r; rd.act = h; rd.lda = H; rd.gdiv = 1; rd.E = 1;
+  rd.W[0] = L->A; rd.w_jstride = H; rd.w_cstride = 1; rd.out[0] = P.xa; rd.nout = 1;
+  HIP_TRY(launch_rowdot(rd, st), "ce: h A^T");
+
+  const uint8_t* wb = static_cast<const uint8_t*>(L->w_blocks);
+  GemmArgs g = gemm_defaults();
+  g.M = T; g.N = (int)V; g.K = H;
+  g.a0 = h; g.lda = H;
+  g.w0 = wb; g.w_rowbytes = rowbytes(L); g.w_nb = H / 32; g.w_rows = (int)V; g.w_row0 = 0;
+  g.ntiles = cdiv(V, TILE_BN);
+  g.mtiles = cdiv(T, tile_bm(P.tc_fwd));
+  g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = P.xa;
+  g.f0 = P.part_ml; g.f1 = P.zlab; g.labels = labels; g.ignore_index = ignore_index;
+  g.V = (int)V; g.ntile_base = 0;
+  HIP_TRY(launch_gemm(L->qtype, EPI_CE_FWD, P.tc_fwd, g, st), "ce: logits pass");
+  HIP_TRY(launch_ce_merge(P.part_ml, g.ntiles, T, P.zlab, labels, V, ignore_index, P.nvalid, lse,
+                          loss, P.term, st),
+          "ce: log-sum-exp merge");
+  if (!grad) return GQ_OK;
+
+  int ntile_base = 0;
+  for (int64_t c0 = 0; c0 < V; c0 += chunk) {
+    const int C = (int)((V - c0) < chunk ? V - c0 : chunk);
+    GemmArgs b = gemm_defaults();
+    b.M = T; b.N = C; b.K = H;
+    b.a0 = h; b.lda = H;
+    b.w0 = wb; b.w_rowbytes = rowbytes(L); b.w_nb = H / 32; b.w_rows = C; b.w_row0 = (int)c0;
+    b.ntiles = cdiv(C, TILE_BN);
+    b.mtiles = cdiv(T, tile_bm(P.tc_bwd));
+    b.s = L->scale; b.r = r; b.lB0 = L->B; b.rv0 = P.xa;
+    b.o0 = P.G; b.ldo = P.ldG;
+    b.f1 = P.part_GB; b.f2 = P.part_dB;
+    b.labels = labels; b.ignore_index = ignore_index; b.lse = lse; b.coef = grad_scale;
+    b.nvalid = P.nvalid; b.V = (int)V; b.ntile_base = ntile_base;
+    HIP_TRY(launch_gemm(L->qtype, EPI_CE_BWD, P.tc_bwd, b, st), "ce: gradient tile pass");
+    ntile_base += b.ntiles;
+
+    GemmArgs d = gemm_defaults();
+    d.M = T; d.N = H; d.K = C;
+    d.a0 = P.G; d.lda = P.ldG;
+    d.w0 = wb; d.w_rowbytes = rowbytes(L); d.w_nb = H / 32; d.w_rows = C; d.w_row0 = (int)c0;
+    d.ntiles = cdiv(H, TILE_BN);
+    d.mtiles = cdiv(T, tile_bm(P.tc_dh));
+    d.f0 = P.dh_acc; d.ldf = H; d.accum = c0 > 0;
+    HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, d, st), "ce: dh pass");
+  }
+  HIP_TRY(launch_sum_parts(P.part_GB, P.ntiles_bwd, T, r, 1.f, P.GB, st), "ce: G B");
+  HIP_TRY(launch_sum_parts(P.part_dB, P.mt, V, r, L->scale, dB, st), "ce: dB");
+  HIP_TRY(launch_ce_final_dh(P.dh_acc, P.GB, L->A, T, H, r, L->scale, dh, st), "ce: dh");
+  ColRedArgs cr;
+  memset(&cr, 0, sizeof cr);
+  cr.M = T; cr.C = H; cr.r = r; cr.U = h; cr.ldu = H; cr.gdiv = 1; cr.Vv = P.GB; cr.E = 1;
+  cr.rc = RC; cr.slots = cdiv(T, RC); cr.part = P.part;
+  HIP_TRY(launch_colred(cr, st), "ce: dA partials");
+  HIP_TRY(launch_colred_finish(P.part, nullptr, 1, cr.slots, H, r, L->scale, 1, dA, st), "ce: dA");
+  return GQ_OK;
+}
+
+}  // extern "C"

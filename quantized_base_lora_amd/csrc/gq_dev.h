@@ -1,0 +1,124 @@
+// Device-side helpers shared by the gq kernels (gfx950 / CDNA4).
+//
+// Block decode follows the block definitions of GGUF Q8_0 / Q4_0 and the
+// 2-bit scale/min format (page 2 "Show HN: LoRA over GGUF", section "Things
+// involved in the training": MMQ over GGUF weights).  Blocks are read with
+// dword loads from the 4-byte-aligned address at or below the block (blocks
+// are only 2-byte aligned: 34 and 18 bytes) and realigned in registers, then
+// decoded straight to bf16 pairs -- no full-precision weight is ever stored.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum { QT_Q8_0 = 0, QT_Q4_0 = 1, QT_Q2_DM = 2 };
+
+template <int QT> struct QTraits;
+template <> struct QTraits<QT_Q8_0> { static constexpr int BS = 34, NDW = 9; };
+template <> struct QTraits<QT_Q4_0> { static constexpr int BS = 18, NDW = 5; };
+template <> struct QTraits<QT_Q2_DM> { static constexpr int BS = 12, NDW = 3; };
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return (float)h;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// round-to-nearest-even float -> bf16 bits (hardware v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Raw bytes of one block, realigned: hdr = first 4 bytes of the block
+// (d, and m for Q2_DM), q[] = the payload as dwords.
+template <int QT> struct RawBlock {
+  static constexpr int NQ = QT == QT_Q8_0 ? 8 : (QT == QT_Q4_0 ? 4 : 2);
+  uint32_t hdr;
+  uint32_t q[NQ];
+};
+
+// Load the block at byte address `blk` (2-byte aligned).  The dword window
+// [blk & ~3, (blk & ~3) + 4*NDW) stays inside the block for a block that
+// starts 2 bytes past a dword boundary, and runs at most 2 bytes past its end
+// otherwise; callers only issue the latter kind when another block follows
+// in the same row (rows of an even number of blocks start dword-aligned).
+template <int QT>
+__device__ __forceinline__ void load_block(const uint8_t* blk, RawBlock<QT>& rb) {
+  constexpr int NDW = QTraits<QT>::NDW;
+  const uintptr_t a = (uintptr_t)blk;
+  const uint32_t* p = (const uint32_t*)(a & ~(uintptr_t)3);
+  uint32_t dw[NDW];
+#pragma unroll
+  for (int i = 0; i < NDW; ++i) dw[i] = p[i];
+  if constexpr (QT == QT_Q2_DM) {
+    // 12-byte blocks in dword-aligned rows are always dword-aligned
+    rb.hdr = dw[0];
+    rb.q[0] = dw[1];
+    rb.q[1] = dw[2];
+  } else {
+    const bool sh = (a & 2) != 0;  // block starts at byte 2 of dw[0]
+    rb.hdr = sh ? (dw[0] >> 16) : (dw[0] & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < RawBlock<QT>::NQ; ++i)
+      rb.q[i] = sh ? dw[i + 1] : __builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2);
+  }
+}
+
+// Decode to 32 floats in element order (exact value rounded once to fp32).
+template <int QT>
+__device__ __forceinline__ void decode_block(const RawBlock<QT>& rb, float (&w)[32]) {
+  const float d = h2f(rb.hdr & 0xffffu);
+  if constexpr (QT == QT_Q8_0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = (int)(int8_t)(uint8_t)(rb.q[i] >> (8 * b));
+        w[4 * i + b] = d * (float)q;
+      }
+    }
+  } else if constexpr (QT == QT_Q4_0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (rb.q[i] >> (8 * b)) & 0xffu;
+        w[4 * i + b] = d * (float)((int)(byte & 15u) - 8);
+        w[16 + 4 * i + b] = d * (float)((int)(byte >> 4) - 8);
+      }
+    }
+  } else {
+    const float m = h2f(rb.hdr >> 16);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t byte = (rb.q[j >> 2] >> (8 * (j & 3))) & 0xffu;
+        const float q = (float)((byte >> (2 * p)) & 3u);
+        w[8 * p + j] = __builtin_fmaf(d, q, m);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace gq

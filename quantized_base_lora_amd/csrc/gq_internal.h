@@ -1,0 +1,195 @@
+// Internal launch interface between the C ABI (gq_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gq {
+
+// GEMM epilogues of the one MFMA kernel template (gq_gemm.hip).
+//   NT = the reduction runs along the weight's block dimension (forward):
+//        C[p][n] = sum_k act[p][k] * deq(W)[n][k]
+//   NN = the reduction runs along the weight's rows (backward):
+//        C[p][c] = sum_n act[p][n] * deq(W)[n][c]
+enum Epi {
+  EPI_LIN = 0,      // NT: out = C + s * rv0[p] . lB0[n]            -> bf16
+  EPI_SWIGLU,       // NT: gate/up pair, h = silu(g) u               -> bf16 g,u,h
+  EPI_CE_FWD,       // NT: per-row (max, sumexp) partials + label logit
+  EPI_CE_BWD,       // NT: G tile -> bf16, partial G.B and G^T.xa
+  EPI_LIN_BWD,      // NN: out = C + s * rv0[p] . lA0[:, c]          -> bf16
+  EPI_DOWN_BWD,     // NN: MoE down backward + SwiGLU backward
+  EPI_GATEUP_BWD,   // NN: dxrows = C + s (rv0 . lA0 + rv1 . lA1)    -> bf16
+  EPI_DH_ACC,       // NN: f0 (+)= C                                  fp32
+  EPI_COUNT
+};
+
+struct GemmArgs {
+  // geometry: M rows, N output columns, K reduction length
+  int64_t M;
+  int32_t N;
+  int32_t K;
+  // activation operand (bf16 rows); a1 serves reduction indices >= asplit
+  const uint16_t* a0;
+  const uint16_t* a1;
+  int64_t lda;
+  int32_t asplit;
+  const int32_t* gather;  // row p reads a[gather[p] / gdiv]
+  int32_t gdiv;
+  // weights: raw blocks, w1 = second projection (gate/up pairs)
+  const uint8_t* w0;
+  const uint8_t* w1;
+  int64_t w_estride;   // bytes between experts
+  int64_t w_rowbytes;  // bytes per weight row
+  int32_t w_nb;        // blocks per weight row
+  int32_t w_rows;      // rows per weight source (NN: bound on the reduction rows)
+  int32_t wsplit;      // NN: reduction index where w1 starts
+  int32_t w_row0;      // first weight row (chunk offset)
+  // grouping (offsets == nullptr: dense)
+  int32_t E;
+  const int32_t* offsets;
+  const int32_t* tile_start;
+  int32_t mtiles;      // m-tile slots in the grid
+  int32_t ntiles;
+  // epilogue
+  float s;
+  int32_t r;
+  const float* lA0;
+  const float* lA1;
+  const float* lB0;
+  const float* lB1;
+  const float* lB2;
+  int64_t lA_estride;  // floats between experts
+  int64_t lB_estride;
+  const float* rv0;    // per-row rank vectors [M][r]
+  const float* rv1;
+  uint16_t* o0;
+  uint16_t* o1;
+  uint16_t* o2;
+  int64_t ldo;
+  float* f0;
+  float* f1;
+  float* f2;
+  int64_t ldf;
+  const uint16_t* s0;  // saved g
+  const uint16_t* s1;  // saved u
+  const float* wflat;
+  const int32_t* sorted;
+  const int64_t* labels;
+  const float* lse;
+  float coef;
+  int64_t ignore_index;
+  int32_t V;
+  int32_t ntile_base;  // global n-tile index of this launch's first n-tile
+  int32_t accum;       // EPI_DH_ACC: add into f0
+  const float* nvalid; // EPI_CE_BWD: device count of valid labels
+};
+
+enum TileCfg { TILE_128x128 = 0, TILE_64x128 = 1 };
+
+// tile rows (BM) of a tile configuration
+inline int tile_bm(int cfg) { return cfg == TILE_128x128 ? 128 : 64; }
+constexpr int TILE_BN = 128;
+constexpr int GEMM_BK = 64;
+
+hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
+
+// ---- small kernels (gq_small.hip) ----
+hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols,
+                          int out_bf16, void* out, hipStream_t st);
+
+// tile_start[e] = sum_{e' < e} ceil(cnt(e') / bm); E + 1 entries
+hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tile_start,
+                             hipStream_t st);
+
+// out[p][j] = sum_c act(p)[c] * W(e)[j][c]   (W [r][C] if w_jstride == C, or
+// [C][r] if w_jstride == 1, w_cstride == r); act rows via gather; e via offsets.
+// out2 (optional): out2[p][j] = wflat[sorted[p]] * out[p][j]
+struct RowDotArgs {
+  int64_t M;
+  int32_t C;
+  int32_t r;
+  const uint16_t* act;
+  int64_t lda;
+  const int32_t* gather;
+  int32_t gdiv;
+  const int32_t* offsets;
+  int32_t E;
+  const float* W[2];
+  int64_t w_estride;
+  int64_t w_jstride;
+  int64_t w_cstride;
+  float* out[2];
+  int32_t nout;
+  float* out2;  // weighted copy of out[0]
+  const float* wflat;
+  const int32_t* sorted;
+};
+hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st);
+
+// Partial outer-product reductions over row chunks:
+//   part[slot][c][j] = sum_{rows p of slot} U(p)[c] * Vv[p][j]
+// slots: chunks of `rc` rows within each expert (chunk_start from
+// launch_tile_start with bm = rc).  U rows via gather.
+struct ColRedArgs {
+  int64_t M;
+  int32_t C;
+  int32_t r;
+  const uint16_t* U;
+  int64_t ldu;
+  const int32_t* gather;
+  int32_t gdiv;
+  const float* Vv;
+  const int32_t* offsets;   // nullptr = dense
+  const int32_t* chunk_start;
+  int32_t E;
+  int32_t rc;
+  int32_t slots;
+  float* part;              // [slots][C][r]
+};
+hipError_t launch_colred(const ColRedArgs& a, hipStream_t st);
+
+// out = s * sum over an expert's slots (in order) of part; experts with no
+// rows get zeros.  transpose: out[e][j][c] instead of out[e][c][j].
+// chunk_start == nullptr: one dense group of nslots_dense slots.
+hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
+                                int32_t nslots_dense, int32_t C, int32_t r, float s,
+                                int transpose, float* out, hipStream_t st);
+
+// out[i][j] = sum_{t < nparts} part[t][i][j] (fixed order); i < rows, j < width
+hipError_t launch_sum_parts(const float* part, int32_t nparts, int64_t rows, int32_t width,
+                            float scale, float* out, hipStream_t st);
+
+// routing
+hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                        float* w, int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws,
+                        hipStream_t st);
+size_t route_ws_bytes(int64_t T, int32_t E, int32_t k);
+hipError_t launch_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T,
+                            int32_t E, int32_t k, float* dlogits, hipStream_t st);
+hipError_t launch_combine(const uint16_t* rows, const float* w, const int32_t* pos, int64_t T,
+                          int32_t k, int64_t H, uint16_t* out, hipStream_t st);
+
+// MoE down-backward partial finish: from part [ntiles][M][1 + 2r]
+//   dw_flat[sorted[p]] = sum part[.][p][0]; dgB[p][j] = sum part[.][p][1+j];
+//   duB[p][j] = sum part[.][p][1+r+j]
+hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int32_t r,
+                              const int32_t* sorted, float* dw_flat, float* dgB, float* duB,
+                              hipStream_t st);
+
+// LM head helpers
+hipError_t launch_ce_prep(const int64_t* labels, int64_t T, int64_t V, int64_t ignore_index,
+                          int32_t* err, float* nvalid, hipStream_t st);
+// term: [T] scratch for the per-token loss terms
+hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, const float* zlab,
+                           const int64_t* labels, int64_t V, int64_t ignore_index,
+                           const float* nvalid, float* lse, float* loss, float* term,
+                           hipStream_t st);
+hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
+                              int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st);
+// out[p][j] = wflat[sorted[p]] * in[p][j]
+hipError_t launch_scale_rows(const float* in, const float* wflat, const int32_t* sorted, int64_t M,
+                             int32_t r, float* out, hipStream_t st);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st);
+
+}  // namespace gq

@@ -1,0 +1,664 @@
+// Small (HBM- or latency-bound) kernels around the MFMA GEMMs.
+//
+//  * block decode export (gq_dequant)
+//  * rank-r adapter passes: row dots (x A^T, dY B) one wave per row with a
+//    shuffle reduction; column outer-product reductions (dA, dB) over fixed
+//    row chunks with partials summed in chunk order (deterministic, no float
+//    atomics)
+//  * MoE routing "like OpenAI triton-kernels" (page 2 "Show HN: LoRA over
+//    GGUF", section "Things involved in the training"): wave-per-token top-k,
+//    a stable counting sort by expert (per-chunk histograms, a scan, and
+//    in-chunk ranks from an LDS key scan) -- positions never come from atomics
+//  * the sparse combine of the experts' outputs and its backward
+//  * the online log-sum-exp merge of the chunked cross entropy
+#include <math.h>
+
+#include "gq_dev.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+// ---------------------------------------------------------------- dequant
+template <int QT>
+__global__ void dequant_kernel(const uint8_t* __restrict__ blocks, int64_t nblocks,
+                               int out_bf16, void* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  constexpr int BS = QTraits<QT>::BS;
+  // 2-byte loads only: blocks are 2-byte aligned and may end the buffer
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + b * BS);
+  RawBlock<QT> rb;
+  if constexpr (QT == QT_Q2_DM) {
+    rb.hdr = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+#pragma unroll
+    for (int i = 0; i < RawBlock<QT>::NQ; ++i)
+      rb.q[i] = (uint32_t)h[2 + 2 * i] | ((uint32_t)h[3 + 2 * i] << 16);
+  } else {
+    rb.hdr = h[0];
+#pragma unroll
+    for (int i = 0; i < RawBlock<QT>::NQ; ++i)
+      rb.q[i] = (uint32_t)h[1 + 2 * i] | ((uint32_t)h[2 + 2 * i] << 16);
+  }
+  float w[32];
+  decode_block<QT>(rb, w);
+  if (out_bf16) {
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + b * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = make_uint4(pack_bf2(w[8 * i], w[8 * i + 1]), pack_bf2(w[8 * i + 2], w[8 * i + 3]),
+                        pack_bf2(w[8 * i + 4], w[8 * i + 5]), pack_bf2(w[8 * i + 6], w[8 * i + 7]));
+  } else {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + b * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  }
+}
+
+// ------------------------------------------------------ tile prefix (E <= 1024)
+__global__ void tile_start_kernel(const int32_t* __restrict__ offsets, int32_t E, int32_t bm,
+                                  int32_t* __restrict__ ts) {
+  __shared__ int32_t sh[1024];
+  const int t = threadIdx.x;
+  int v = 0;
+  if (t < E) {
+    const int cnt = offsets[t + 1] - offsets[t];
+    v = (cnt + bm - 1) / bm;
+  }
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = t >= o ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  if (t < E) ts[t + 1] = sh[t];
+  if (t == 0) ts[0] = 0;
+}
+
+__device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_t p) {
+  int lo = 0, hi = E;  // offsets[lo] <= p < offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------- row dots
+template <int NOUT>
+__global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= a.M) return;
+  const int r = a.r;
+  int e = 0;
+  if (a.offsets) e = find_expert(a.offsets, a.E, p);
+  const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
+  const uint16_t* x = a.act + src * a.lda;
+  float acc[NOUT][16];
+#pragma unroll
+  for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[o][j] = 0.f;
+  for (int c = lane * 8; c < a.C; c += 512) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + c);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    float xv[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      xv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
+      xv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
+    }
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+      const float* W = a.W[o] + (int64_t)e * a.w_estride;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j < r) {
+          const float* wj = W + (int64_t)j * a.w_jstride + (int64_t)c * a.w_cstride;
+          float t = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) t += xv[q] * wj[q * a.w_cstride];
+          acc[o][j] += t;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < r) acc[o][j] = warp_sum(acc[o][j]);
+  if (lane == 0) {
+    float wp = 0.f;
+    if (a.out2) wp = a.wflat[a.sorted[p]];
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < r) {
+          a.out[o][p * r + j] = acc[o][j];
+          if (o == 0 && a.out2) a.out2[p * r + j] = wp * acc[o][j];
+        }
+  }
+}
+
+// ---------------------------------------------------- column reductions
+// Each thread owns 2 adjacent columns; a block covers 512 columns of one slot.
+__global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
+  const int slot = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 2;
+  int64_t r0, r1;
+  if (a.offsets) {
+    const int32_t* cs = a.chunk_start;
+    if (slot >= cs[a.E]) return;
+    const int e = find_expert(cs, a.E, slot);
+    r0 = (int64_t)a.offsets[e] + (int64_t)(slot - cs[e]) * a.rc;
+    r1 = min((int64_t)a.offsets[e + 1], r0 + a.rc);
+  } else {
+    r0 = (int64_t)slot * a.rc;
+    r1 = min(a.M, r0 + a.rc);
+  }
+  if (c >= a.C) return;
+  const int r = a.r;
+  float acc0[16], acc1[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc0[j] = acc1[j] = 0.f;
+  for (int64_t p = r0; p < r1; ++p) {
+    const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
+    const uint32_t u2 = *reinterpret_cast<const uint32_t*>(a.U + src * a.ldu + c);
+    const float u0 = bf2f((uint16_t)(u2 & 0xffffu)), u1 = bf2f((uint16_t)(u2 >> 16));
+    const float* v = a.Vv + p * r;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < r) {
+        const float vj = v[j];
+        acc0[j] += u0 * vj;
+        acc1[j] += u1 * vj;
+      }
+  }
+  float* dst = a.part + ((int64_t)slot * a.C + c) * r;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < r) {
+      dst[j] = acc0[j];
+      dst[r + j] = acc1[j];
+    }
+}
+
+// out[e] = s * sum_{slots of e} part[slot]; thread per (c, j) of one expert
+__global__ void colred_finish_kernel(const float* __restrict__ part,
+                                     const int32_t* __restrict__ cs, int32_t nslots_dense,
+                                     int32_t C, int32_t r, float s, int transpose,
+                                     float* __restrict__ out) {
+  const int e = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)C * r;
+  if (i >= n) return;
+  const int s0 = cs ? cs[e] : 0;
+  const int s1 = cs ? cs[e + 1] : nslots_dense;
+  float acc = 0.f;
+  for (int sl = s0; sl < s1; ++sl) acc += part[(int64_t)sl * n + i];
+  const int64_t c = i / r, j = i % r;
+  float* o = out + (int64_t)e * n;
+  if (transpose)
+    o[j * C + c] = s * acc;
+  else
+    o[i] = s * acc;
+}
+
+__global__ void sum_parts_kernel(const float* __restrict__ part, int32_t nparts, int64_t n,
+                                 float scale, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int t = 0; t < nparts; ++t) acc += part[(int64_t)t * n + i];
+  out[i] = scale * acc;
+}
+
+// ----------------------------------------------------------------- routing
+constexpr int ROUTE_CHUNK = 256;
+
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// one wave per token; up to 16 logits per lane (E <= 1024)
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
+                                                   int32_t E, int32_t k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float val[16];
+  const float* row = logits + t * E;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int ex = lane + 64 * q;
+    val[q] = ex < E ? row[ex] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float sel_v[16];
+  int sel_i[16];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int ex = lane + 64 * q;
+      if (ex < E && !((taken >> q) & 1u) && (bi == 0x7fffffff || better(val[q], ex, bv, bi))) {
+        bv = val[q];
+        bi = ex;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    sel_v[j & 15] = bv;
+    sel_i[j & 15] = bi;
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+  if (lane == 0) {
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __expf(sel_v[j] - sel_v[0]);
+    for (int j = 0; j < k; ++j) {
+      ids[t * k + j] = sel_i[j];
+      w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / sum;
+    }
+  }
+}
+
+__global__ void route_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int32_t E,
+                                  int32_t* __restrict__ counts) {
+  __shared__ int32_t hist[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t a = (int64_t)blockIdx.x * ROUTE_CHUNK + threadIdx.x;
+  if (a < n) atomicAdd(&hist[ids[a]], 1);  // integer counts: order-independent
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// one block of 1024 threads: per-expert running bases over chunks, then the
+// exclusive scan over experts
+__global__ void route_scan_kernel(int32_t* __restrict__ counts, int32_t nchunks, int32_t E,
+                                  int32_t* __restrict__ offsets) {
+  __shared__ int32_t sh[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = counts[(int64_t)c * E + e];
+      counts[(int64_t)c * E + e] = tot;
+      tot += v;
+    }
+  }
+  sh[e] = tot;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = e >= o ? sh[e - o] : 0;
+    __syncthreads();
+    sh[e] += add;
+    __syncthreads();
+  }
+  const int excl = sh[e] - tot;
+  if (e < E) {
+    offsets[e] = excl;
+    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += excl;
+  }
+  if (e == 0) offsets[E] = sh[1023];
+}
+
+__global__ void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n, int32_t E,
+                                     const int32_t* __restrict__ base, int32_t* __restrict__ sorted,
+                                     int32_t* __restrict__ pos) {
+  __shared__ int32_t keys[ROUTE_CHUNK];
+  const int t = threadIdx.x;
+  const int64_t a = (int64_t)blockIdx.x * ROUTE_CHUNK + t;
+  const int key = a < n ? ids[a] : -1;
+  keys[t] = key;
+  __syncthreads();
+  if (a >= n) return;
+  int rank = 0;
+  for (int j = 0; j < t; ++j) rank += keys[j] == key;
+  const int p = base[(int64_t)blockIdx.x * E + key] + rank;
+  sorted[p] = (int32_t)a;
+  pos[a] = p;
+}
+
+__global__ __launch_bounds__(256) void route_bwd_kernel(const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ dw, int64_t T,
+                                                        int32_t E, int32_t k,
+                                                        float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float inner = 0.f;
+  for (int j = 0; j < k; ++j) inner += w[t * k + j] * dw[t * k + j];
+  for (int ex = lane; ex < E; ex += 64) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (ids[t * k + j] == ex) v = w[t * k + j] * (dw[t * k + j] - inner);
+    dl[t * E + ex] = v;
+  }
+}
+
+// y[t][c..c+8) = sum_j w[t][j] rows[pos[t*k+j]][c..c+8)   (w == nullptr: weight 1)
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ rows,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ pos, int64_t T,
+                                                      int32_t k, int64_t H,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t nxb = (H + 2047) / 2048;  // column blocks per token
+  const int64_t t = blockIdx.x / nxb;
+  const int64_t c = ((blockIdx.x % nxb) * 256 + threadIdx.x) * 8;
+  if (t >= T || c >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t pr = pos[t * k + j];
+    const float wj = w ? w[t * k + j] : 1.f;
+    const uint4 raw = *reinterpret_cast<const uint4*>(rows + pr * H + c);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += wj * bf2f((uint16_t)(rw[q] & 0xffffu));
+      acc[2 * q + 1] += wj * bf2f((uint16_t)(rw[q] >> 16));
+    }
+  }
+  *reinterpret_cast<uint4*>(out + t * H + c) =
+      make_uint4(pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
+                 pack_bf2(acc[6], acc[7]));
+}
+
+__global__ void down_finish_kernel(const float* __restrict__ part, int32_t ntiles, int64_t M,
+                                   int32_t r, const int32_t* __restrict__ sorted,
+                                   float* __restrict__ dw_flat, float* __restrict__ dgB,
+                                   float* __restrict__ duB) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= M) return;
+  const int width = 1 + 2 * r;
+  float dw = 0.f, g[16], u[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) g[j] = u[j] = 0.f;
+  for (int nt = 0; nt < ntiles; ++nt) {
+    const float* src = part + ((int64_t)nt * M + p) * width;
+    dw += src[0];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < r) {
+        g[j] += src[1 + j];
+        u[j] += src[1 + r + j];
+      }
+  }
+  dw_flat[sorted[p]] = dw;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < r) {
+      dgB[p * r + j] = g[j];
+      duB[p * r + j] = u[j];
+    }
+}
+
+// --------------------------------------------------------- cross entropy
+__global__ void ce_prep_kernel(const int64_t* __restrict__ labels, int64_t T, int64_t V,
+                               int64_t ignore_index, int32_t* __restrict__ err,
+                               float* __restrict__ nvalid) {
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t bad[256];
+  int c = 0, b = 0;
+  for (int64_t t = threadIdx.x; t < T; t += blockDim.x) {
+    const int64_t l = labels[t];
+    if (l == ignore_index) continue;
+    if (l >= 0 && l < V) ++c; else ++b;
+  }
+  cnt[threadIdx.x] = c;
+  bad[threadIdx.x] = b;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      cnt[threadIdx.x] += cnt[threadIdx.x + o];
+      bad[threadIdx.x] += bad[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *nvalid = (float)cnt[0];
+    *err = bad[0] ? 1 : 0;
+  }
+}
+
+// per token: ordered online merge of the (max, sumexp) partials
+__global__ void ce_merge_kernel(const float* __restrict__ part, int32_t ntiles, int64_t T,
+                                const float* __restrict__ zlab, const int64_t* __restrict__ labels,
+                                int64_t V, int64_t ignore_index, float* __restrict__ lse,
+                                float* __restrict__ term) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float m = -INFINITY, l = 0.f;
+  for (int nt = 0; nt < ntiles; ++nt) {
+    const float m2 = part[((int64_t)nt * T + t) * 2], l2 = part[((int64_t)nt * T + t) * 2 + 1];
+    if (m2 == -INFINITY) continue;
+    if (m2 > m) {
+      l = (m == -INFINITY ? 0.f : l * __expf(m - m2)) + l2;
+      m = m2;
+    } else {
+      l += l2 * __expf(m2 - m);
+    }
+  }
+  const float v = m + __logf(l);
+  lse[t] = v;
+  const int64_t lab = labels[t];
+  term[t] = (lab != ignore_index && lab >= 0 && lab < V) ? v - zlab[t] : 0.f;
+}
+
+// loss = sum(term) / nvalid, fixed-order tree in one block
+__global__ void ce_loss_kernel(const float* __restrict__ term, int64_t T,
+                               const float* __restrict__ nvalid, float* __restrict__ loss) {
+  __shared__ float sh[1024];
+  float acc = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += blockDim.x) acc += term[t];
+  sh[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float nv = *nvalid;
+    *loss = nv > 0.f ? sh[0] / nv : 0.f;
+  }
+}
+
+__global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, const float* __restrict__ GB,
+                                   const float* __restrict__ A, int64_t T, int32_t H, int32_t r,
+                                   float s, uint16_t* __restrict__ dh) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * H) return;
+  const int64_t t = i / H, c = i % H;
+  float v = 0.f;
+  for (int j = 0; j < r; ++j) v += GB[t * r + j] * A[(int64_t)j * H + c];
+  dh[i] = f2bf(dh_acc[i] + s * v);
+}
+
+// out[p][j] = wflat[sorted[p]] * in[p][j]
+__global__ void scale_rows_kernel(const float* __restrict__ in, const float* __restrict__ wflat,
+                                  const int32_t* __restrict__ sorted, int64_t M, int32_t r,
+                                  float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * r) return;
+  out[i] = wflat[sorted[i / r]] * in[i];
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+// ================================================================ launchers
+hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_bf16,
+                          void* out, hipStream_t st) {
+  const int64_t nb = rows * (cols / 32);
+  if (nb == 0) return hipSuccess;
+  const dim3 g(blocks_for(nb, 256)), b(256);
+  const uint8_t* bl = static_cast<const uint8_t*>(blocks);
+  switch (qtype) {
+    case QT_Q8_0: hipLaunchKernelGGL(dequant_kernel<QT_Q8_0>, g, b, 0, st, bl, nb, out_bf16, out); break;
+    case QT_Q4_0: hipLaunchKernelGGL(dequant_kernel<QT_Q4_0>, g, b, 0, st, bl, nb, out_bf16, out); break;
+    case QT_Q2_DM: hipLaunchKernelGGL(dequant_kernel<QT_Q2_DM>, g, b, 0, st, bl, nb, out_bf16, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* ts,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, ts);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const dim3 g(blocks_for(a.M, 4)), b(256);
+  if (a.nout == 2)
+    hipLaunchKernelGGL(rowdot_kernel<2>, g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<1>, g, b, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
+  if (a.slots == 0) return hipSuccess;
+  const dim3 g((unsigned)a.slots, blocks_for(a.C, 512)), b(256);
+  hipLaunchKernelGGL(colred_kernel, g, b, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
+                                int32_t nslots_dense, int32_t C, int32_t r, float s, int transpose,
+                                float* out, hipStream_t st) {
+  const dim3 g(blocks_for((int64_t)C * r, 256), (unsigned)E), b(256);
+  hipLaunchKernelGGL(colred_finish_kernel, g, b, 0, st, part, chunk_start, nslots_dense, C, r, s,
+                     transpose, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* part, int32_t nparts, int64_t rows, int32_t width,
+                            float scale, float* out, hipStream_t st) {
+  const int64_t n = rows * width;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, part, nparts, n,
+                     scale, out);
+  return hipGetLastError();
+}
+
+size_t route_ws_bytes(int64_t T, int32_t E, int32_t k) {
+  const int64_t n = T * k;
+  const int64_t nch = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  return (size_t)(nch * E * sizeof(int32_t));
+}
+
+hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                        float* w, int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws,
+                        hipStream_t st) {
+  const int64_t n = T * k;
+  const int nch = (int)((n + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
+  int32_t* counts = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(topk_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, logits, T, E, k, ids, w);
+  hipLaunchKernelGGL(route_hist_kernel, dim3(nch), dim3(ROUTE_CHUNK), 0, st, ids, n, E, counts);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nch, E, offsets);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nch), dim3(ROUTE_CHUNK), 0, st, ids, n, E, counts,
+                     sorted, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T,
+                            int32_t E, int32_t k, float* dlogits, hipStream_t st) {
+  hipLaunchKernelGGL(route_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, ids, w, dw, T, E,
+                     k, dlogits);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t* rows, const float* w, const int32_t* pos, int64_t T,
+                          int32_t k, int64_t H, uint16_t* out, hipStream_t st) {
+  const dim3 g((unsigned)(blocks_for(H, 2048) * T)), b(256);
+  hipLaunchKernelGGL(combine_kernel, g, b, 0, st, rows, w, pos, T, k, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int32_t r,
+                              const int32_t* sorted, float* dw_flat, float* dgB, float* duB,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(down_finish_kernel, dim3(blocks_for(M, 256)), dim3(256), 0, st, part, ntiles,
+                     M, r, sorted, dw_flat, dgB, duB);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_prep(const int64_t* labels, int64_t T, int64_t V, int64_t ignore_index,
+                          int32_t* err, float* nvalid, hipStream_t st) {
+  hipLaunchKernelGGL(ce_prep_kernel, dim3(1), dim3(256), 0, st, labels, T, V, ignore_index, err,
+                     nvalid);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, const float* zlab,
+                           const int64_t* labels, int64_t V, int64_t ignore_index,
+                           const float* nvalid, float* lse, float* loss, float* term,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(ce_merge_kernel, dim3(blocks_for(T, 256)), dim3(256), 0, st, part_ml, ntiles, T,
+                     zlab, labels, V, ignore_index, lse, term);
+  hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, term, T, nvalid, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
+                              int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st) {
+  const int64_t n = T * H;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_final_dh_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, dh_acc, GB, A,
+                     T, H, r, s, dh);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_rows(const float* in, const float* wflat, const int32_t* sorted, int64_t M,
+                             int32_t r, float* out, hipStream_t st) {
+  const int64_t n = M * r;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_rows_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, in, wflat,
+                     sorted, M, r, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u16_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace gq
