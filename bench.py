@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantised-base LoRA hot path on one MI355X.
+
+A step is the fused dequant-GEMM + LoRA forward and fast backward of the
+dense Q4_0 linear layer (T 2048 tokens, 2048 -> 6144, rank 4, alpha 8):
+gq_linear_lora_fwd + gq_linear_lora_bwd on inputs already resident in HBM.
+`value` is its algorithmic TFLOP/s.  The same JSON line also carries the
+routed MoE layer (Q4_0, 2048 tokens, hidden 2048, 128 experts top-8,
+intermediate 768, rank 4) train tokens/s, the roofline of the dominant MMQ
+kernel (timed with HIP events around each launch inside the timed region) and
+the fp64 oracle timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def linear_flops(T, K, N, r):
+    # fwd: 2TNK + 2TKr + 2TNr ; bwd: dX 2TNK + 2TNr + 2TKr, dB 2TNr, dA 2TKr
+    return 4 * T * N * K + 6 * T * r * (N + K)
+
+
+def moe_flops(T, H, I, k, r):
+    return T * k * (12 * H * I + 18 * r * (H + I))
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("gq_gemm_impl.h", "gq_dev.h"):
+        with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    the counters were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "mmq_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != gemm_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_base_lora_amd as gq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    lib = gq.lib()
+
+    # ------------------------------------------------------------ linear step
+    cfg = synth.CFG2
+    t0 = time.time()
+    inp = synth.make_linear(cfg)
+    log(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s")
+    p = gq.Proj(cfg.qtype, cfg.N, cfg.K, u8(inp["blocks"]), f32(inp["A"]), f32(inp["B"]),
+                float(inp["scale"]))
+    x, dy = bf(inp["x"]), bf(inp["dy"])
+    ws = torch.empty(lib.gq_linear_lora_bwd_workspace_size(gq.C.byref(p.c()), cfg.T),
+                     dtype=torch.uint8, device=dev)
+
+    def step(prof=None):
+        if prof:
+            lib.gq_profile_mmq_events(prof[0].cuda_event, prof[1].cuda_event)
+        y, xa = gq.linear_lora_fwd(p, x)
+        if prof:
+            lib.gq_profile_mmq_events(prof[2].cuda_event, prof[3].cuda_event)
+        out = gq.linear_lora_bwd(p, x, xa, dy, ws=ws)
+        if prof:
+            lib.gq_profile_mmq_events(None, None)
+        return y, out
+
+    for _ in range(args.warmup):
+        step()
+    K = args.steps
+    prof = [[ev() for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    start, stop = ev(), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        step(prof[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    fwd_ms = sum(pp[0].elapsed_time(pp[1]) for pp in prof) / K
+    bwd_ms = sum(pp[2].elapsed_time(pp[3]) for pp in prof) / K
+    flops = linear_flops(cfg.T, cfg.K, cfg.N, cfg.rank)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] linear step {ms:.3f} ms  ({tflops:.1f} TFLOP/s); MMQ fwd {fwd_ms*1e3:.1f} us, "
+        f"MMQ dX {bwd_ms*1e3:.1f} us")
+
+    # dominant kernel: the slower of the two MMQ launches of the step
+    gemm_flops = 2 * cfg.T * cfg.N * cfg.K + 2 * cfg.T * cfg.N * cfg.rank
+    if bwd_ms >= fwd_ms:
+        kname, kms, kkey = "mmq_nn_dx_q4_0_t2048_2048x6144", bwd_ms, "mmq_nn_lin_bwd_q4_0_cfg2"
+    else:
+        kname, kms, kkey = "mmq_nt_fwd_q4_0_t2048_2048x6144", fwd_ms, "mmq_nt_lin_q4_0_cfg2"
+    achieved = gemm_flops / (kms * 1e-3) / 1e12
+    roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(kkey), "launch_us": round(kms * 1e3, 2),
+                "other_mmq_us": round((fwd_ms if kms == bwd_ms else bwd_ms) * 1e3, 2)}
+
+    result = {
+        "metric": "fused dequant-GEMM+LoRA fwd+bwd TFLOP/s & MoE-layer train tokens/s, % roofline",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "n_in": cfg.K, "n_out": cfg.N,
+                   "qtype": "q4_0", "rank": cfg.rank, "alpha": cfg.alpha, "seed": cfg.seed,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+    }
+
+    # --------------------------------------------------------------- MoE layer
+    if not args.no_moe:
+        mc = synth.CFG3
+        t0 = time.time()
+        minp = synth.make_moe(mc)
+        log(f"[bench] inputs {mc.name} generated in {time.time() - t0:.1f}s")
+        E, H, I, s = mc.E, mc.H, mc.I, float(minp["scale"])
+        mk = lambda w, a, b, no, ni: gq.Proj(mc.qtype, no, ni, u8(w), f32(a), f32(b), s, E)
+        wts = gq.MoEWeights(mk(minp["wg"], minp["ag"], minp["bg"], I, H),
+                            mk(minp["wu"], minp["au"], minp["bu"], I, H),
+                            mk(minp["wd"], minp["ad"], minp["bd"], H, I))
+        mx, mdy, mlg = bf(minp["x"]), bf(minp["dy"]), f32(minp["logits"])
+        del minp
+
+        def mstep():
+            yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
+            return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
+
+        for _ in range(max(2, args.warmup)):
+            mstep()
+        torch.cuda.synchronize()
+        a, b = ev(), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            mstep()
+        b.record()
+        torch.cuda.synchronize()
+        mms = a.elapsed_time(b) / K
+        mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
+        result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
+                               "ms_per_step": round(mms, 4),
+                               "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
+                               "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+
+        from oracle import linear as ol
+
+        reps, spent = 0, 0.0
+        while spent < args.cpu_seconds and reps < 50:
+            t0 = time.perf_counter()
+            ol.run(inp)
+            spent += time.perf_counter() - t0
+            reps += 1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        result["cpu_baseline"] = {"value": round(flops * reps / spent / 1e12, 5), "unit": "TFLOP/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"{reps} full fwd+bwd passes of {cfg.name} in fp64 "
+                                            f"numpy/OpenBLAS, {spent:.1f}s"}
+        log(f"[bench] cpu oracle {reps} reps in {spent:.1f}s on {threads} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -87,6 +87,16 @@ const char* gq_last_error(void);
 int64_t gq_block_bytes(int qtype);
 
 /*
+ * Timing hook for profilers and benchmarks (not part of the method): while
+ * `start` / `stop` are non-NULL hipEvent_t handles, every fused MMQ kernel
+ * this thread launches records `start` on its stream just before the kernel
+ * and `stop` just after it, so hipEventElapsedTime(start, stop) is that
+ * kernel's duration.  Pass NULL, NULL to switch it off.  The events belong
+ * to the caller; they are recorded again by each later MMQ launch.
+ */
+void gq_profile_mmq_events(void* start, void* stop);
+
+/*
  * Block decode (the primitive inside every MMQ; a test/debug export).
  * blocks: [rows][cols/32] blocks of `qtype`.  out: [rows][cols] float32
  * (out_dtype GQ_F32) or bf16 (GQ_BF16).  The float32 result is the weight's

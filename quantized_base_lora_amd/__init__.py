@@ -25,7 +25,7 @@ BWD_DOWN_SWIGLU, BWD_GATEUP = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q2_DM: 12}
 
 EXPORTS = (
-    "gq_version", "gq_last_error", "gq_block_bytes", "gq_dequant",
+    "gq_version", "gq_last_error", "gq_block_bytes", "gq_profile_mmq_events", "gq_dequant",
     "gq_linear_lora_fwd_workspace_size", "gq_linear_lora_fwd",
     "gq_linear_lora_bwd_workspace_size", "gq_linear_lora_bwd",
     "gq_moe_route_workspace_size", "gq_moe_route", "gq_moe_route_bwd",
@@ -83,6 +83,7 @@ def load_library(path: str = LIB_PATH):
         "gq_version": (C.c_int, []),
         "gq_last_error": (C.c_char_p, []),
         "gq_block_bytes": (i64, [C.c_int]),
+        "gq_profile_mmq_events": (None, [vp, vp]),
         "gq_dequant": (C.c_int, [C.c_int, vp, i64, i64, C.c_int, vp, vp]),
         "gq_linear_lora_fwd_workspace_size": (sz, [P(LoraLinear), i64]),
         "gq_linear_lora_fwd": (C.c_int, [P(LoraLinear), vp, i64, vp, vp, vp, sz, vp]),

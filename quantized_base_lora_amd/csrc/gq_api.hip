@@ -128,6 +128,10 @@ const char* gq_last_error(void) { return g_err.c_str(); }
 
 int64_t gq_block_bytes(int qtype) { return block_bytes(qtype); }
 
+void gq_profile_mmq_events(void* start, void* stop) {
+  set_profile_events(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+}
+
 // ------------------------------------------------------------------ dequant
 int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype, void* out,
                void* stream) {

@@ -12,8 +12,11 @@ hipError_t launch_gemm_q4_0_nn(int epi, int tilecfg, const GemmArgs& a, hipStrea
 hipError_t launch_gemm_q2_dm_nt(int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_q2_dm_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
 
-hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {
-  if ((int64_t)a.mtiles * a.ntiles == 0) return hipSuccess;
+namespace {
+// optional timing events recorded around every MMQ launch of this thread
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+hipError_t dispatch(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {
   const bool nn = epi >= EPI_LIN_BWD;
   switch (qtype) {
     case QT_Q8_0: return nn ? launch_gemm_q8_0_nn(epi, tilecfg, a, st) : launch_gemm_q8_0_nt(epi, tilecfg, a, st);
@@ -21,5 +24,22 @@ hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipSt
     case QT_Q2_DM: return nn ? launch_gemm_q2_dm_nn(epi, tilecfg, a, st) : launch_gemm_q2_dm_nt(epi, tilecfg, a, st);
     default: return hipErrorInvalidValue;
   }
+}
+}  // namespace
+
+void set_profile_events(hipEvent_t start, hipEvent_t stop) {
+  g_prof_start = start;
+  g_prof_stop = stop;
+}
+
+hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {
+  if ((int64_t)a.mtiles * a.ntiles == 0) return hipSuccess;
+  if (g_prof_start) {
+    const hipError_t e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = dispatch(qtype, epi, tilecfg, a, st);
+  if (e == hipSuccess && g_prof_stop) return hipEventRecord(g_prof_stop, st);
+  return e;
 }
 }  // namespace gq

@@ -92,6 +92,8 @@ constexpr int TILE_BN = 128;
 constexpr int GEMM_BK = 64;
 
 hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
+// thread-local timing events recorded around each launch_gemm (nullptr: off)
+void set_profile_events(hipEvent_t start, hipEvent_t stop);
 
 // ---- small kernels (gq_small.hip) ----
 hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols,
