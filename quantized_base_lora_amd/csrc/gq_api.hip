@@ -90,8 +90,8 @@ int check_proj(const gq_lora_linear* L, const char* name, bool grouped) {
   if (L->n_experts < 1 || L->n_experts > 1024)
     return fail(GQ_EINVAL, "%s: n_experts %d not in [1, 1024]", name, L->n_experts);
   if (!L->w_blocks || !L->A || !L->B) return fail(GQ_EINVAL, "%s: NULL weight or adapter", name);
-  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 4) || !aligned(L->B, 4))
-    return fail(GQ_EINVAL, "%s: weight/adapter pointers must be 4-byte aligned", name);
+  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 16) || !aligned(L->B, 4))
+    return fail(GQ_EINVAL, "%s: w_blocks and B must be 4-byte and A 16-byte aligned", name);
   return GQ_OK;
 }
 
@@ -114,7 +114,17 @@ GemmArgs gemm_defaults() {
   return a;
 }
 
-constexpr int RC = 256;  // rows per partial-reduction chunk
+// Rows per chunk of the adapter-gradient column reductions: the largest
+// power of two (16..512) that still gives >= 512 workgroups, so that the
+// reduction fills the chip without multiplying the partial-sum traffic.
+int pick_rc(int64_t M, int64_t C, int r, int E) {
+  const int64_t cb = cdiv(C, 256 * colred_cols_per_thread(r));
+  const int extra = E > 1 ? E : 0;
+  int rc = 16;
+  while (rc < 512 && (cdiv(M, rc * 2) + extra) * cb >= 512) rc *= 2;
+  return rc;
+}
+int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
 hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
 
@@ -193,9 +203,12 @@ struct LinBwdWs {
   float* dyB;
   float* part;
 };
+int lin_rc(const gq_lora_linear* L, int64_t T) {
+  return pick_rc(T, L->n_in > L->n_out ? L->n_in : L->n_out, L->rank, 1);
+}
 LinBwdWs plan_lin_bwd(Ws& w, const gq_lora_linear* L, int64_t T) {
   LinBwdWs p;
-  const int64_t slots = cdiv(T, RC);
+  const int64_t slots = colred_slots(T, lin_rc(L, T), 1);
   const int64_t cmax = L->n_in > L->n_out ? L->n_in : L->n_out;
   p.dyB = w.take<float>(T * L->rank);
   p.part = w.take<float>(slots * cmax * L->rank);
@@ -233,7 +246,8 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
   if ((rc = check_ws(ws, ws_bytes, meas.size()))) return rc;
   Ws w(ws);
   const LinBwdWs P = plan_lin_bwd(w, L, T);
-  const int slots = cdiv(T, RC);
+  const int rcl = lin_rc(L, T);
+  const int slots = (int)colred_slots(T, rcl, 1);
 
   RowDotArgs rd;
   memset(&rd, 0, sizeof rd);
@@ -244,7 +258,7 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
   cr.M = T; cr.C = N; cr.r = r; cr.U = dy; cr.ldu = N; cr.gdiv = 1; cr.Vv = xa;
-  cr.E = 1; cr.rc = RC; cr.slots = slots; cr.part = P.part;
+  cr.E = 1; cr.rc = rcl; cr.slots = slots; cr.part = P.part;
   HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB partials");
   HIP_TRY(launch_colred_finish(P.part, nullptr, 1, slots, N, r, L->scale, 0, dB, st),
           "gq_linear_lora_bwd: dB");
@@ -434,13 +448,17 @@ struct GrpBwdWs {
   float* part_down;
   float* part;
 };
+int grp_rc(const gq_lora_linear* P, int64_t M) {
+  const int64_t H = P[0].n_in > P[0].n_out ? P[0].n_in : P[0].n_out;
+  return pick_rc(M, H, P[0].rank, P[0].n_experts);
+}
 GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
   GrpBwdWs p;
   memset(&p, 0, sizeof p);
   const int E = P->n_experts, r = P->rank;
   p.ts = w.take<int32_t>(E + 1);
   p.cs = w.take<int32_t>(E + 1);
-  const int64_t slots = grouped_mtiles(M, E, RC);
+  const int64_t slots = colred_slots(M, grp_rc(P, M), E);
   if (mode == GQ_BWD_DOWN_SWIGLU) {
     const int64_t H = P[0].n_out, I = P[0].n_in;
     p.dyB = w.take<float>(M * r);
@@ -513,12 +531,13 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     return rc;
   Ws w(ws);
   const GrpBwdWs W = plan_grp_bwd(w, P, mode, M);
-  const int slots = (int)grouped_mtiles(M, E, RC);
-  HIP_TRY(launch_tile_start(a->offsets, E, RC, W.cs, st), "gq_grouped_mmq_lora_bwd: chunks");
+  const int rcg = grp_rc(P, M);
+  const int slots = (int)colred_slots(M, rcg, E);
+  HIP_TRY(launch_tile_start(a->offsets, E, rcg, W.cs, st), "gq_grouped_mmq_lora_bwd: chunks");
 
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
-  cr.M = M; cr.r = r; cr.offsets = a->offsets; cr.chunk_start = W.cs; cr.E = E; cr.rc = RC;
+  cr.M = M; cr.r = r; cr.offsets = a->offsets; cr.chunk_start = W.cs; cr.E = E; cr.rc = rcg;
   cr.slots = slots; cr.part = W.part; cr.gdiv = 1;
 
   if (mode == GQ_BWD_DOWN_SWIGLU) {
@@ -658,7 +677,7 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     p.mt = cdiv(T, tile_bm(p.tc_bwd));
     p.part_dB = w.take<float>((int64_t)p.mt * V * r);
     p.GB = w.take<float>(T * r);
-    p.part = w.take<float>((int64_t)cdiv(T, RC) * H * r);
+    p.part = w.take<float>(colred_slots(T, pick_rc(T, H, (int)r, 1), 1) * H * r);
     p.tc_dh = pick_tile(T, cdiv(H, TILE_BN));
   }
   return p;
@@ -761,7 +780,7 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
   cr.M = T; cr.C = H; cr.r = r; cr.U = h; cr.ldu = H; cr.gdiv = 1; cr.Vv = P.GB; cr.E = 1;
-  cr.rc = RC; cr.slots = cdiv(T, RC); cr.part = P.part;
+  cr.rc = pick_rc(T, H, r, 1); cr.slots = (int)colred_slots(T, cr.rc, 1); cr.part = P.part;
   HIP_TRY(launch_colred(cr, st), "ce: dA partials");
   HIP_TRY(launch_colred_finish(P.part, nullptr, 1, cr.slots, H, r, L->scale, 1, dA, st), "ce: dA");
   return GQ_OK;

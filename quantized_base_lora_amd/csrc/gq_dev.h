@@ -115,6 +115,66 @@ __device__ __forceinline__ void decode_block(const RawBlock<QT>& rb, float (&w)[
   }
 }
 
+// Decode for the MMQ kernels: the same values as decode_block for every
+// finite scale, with fewer VALU ops.  Bytes are converted with the
+// byte-select conversions (v_cvt_f32_ubyte0..3) and the offset folded into
+// one FMA:
+//   Q8_0: u = q + 128 (xor 0x80 per byte)  w = u*d - 128*d
+//   Q4_0: u = nibble                        w = u*d - 8*d
+//   Q2:   u = bit pair                      w = u*d + m
+// Every product and sum is exact (fp16 d times an 8-bit integer), so the
+// result is bit-identical to d*q.  With an infinite scale the biased form
+// yields NaN where d*q would be +-inf.
+// byte b of x as float: one v_cvt_f32_ubyte{b} (register-only asm; the
+// optimiser would otherwise split it into a bit-field extract plus convert)
+__device__ __forceinline__ float ubyte(uint32_t x, int b) {
+  float r;
+  switch (b) {
+    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); break;
+    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); break;
+    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); break;
+    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); break;
+  }
+  return r;
+}
+
+template <int QT>
+__device__ __forceinline__ void decode_block_fast(const RawBlock<QT>& rb, float (&w)[32]) {
+  const float d = h2f(rb.hdr & 0xffffu);
+  if constexpr (QT == QT_Q8_0) {
+    const float off = -128.f * d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = rb.q[i] ^ 0x80808080u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[4 * i + b] = __builtin_fmaf(ubyte(u, b), d, off);
+    }
+  } else if constexpr (QT == QT_Q4_0) {
+    const float off = -8.f * d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = rb.q[i] & 0x0f0f0f0fu;
+      const uint32_t hi = (rb.q[i] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        w[4 * i + b] = __builtin_fmaf(ubyte(lo, b), d, off);
+        w[16 + 4 * i + b] = __builtin_fmaf(ubyte(hi, b), d, off);
+      }
+    }
+  } else {
+    const float m = h2f(rb.hdr >> 16);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t u = (rb.q[h] >> (2 * pp)) & 0x03030303u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[8 * pp + 4 * h + b] = __builtin_fmaf(ubyte(u, b), d, m);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -41,16 +41,21 @@ constexpr int BK = GEMM_BK;  // 64 = two quant blocks along k
 constexpr int LDK = BK + 8;  // padded LDS row (bf16): 144 B keeps ds_read_b128 conflict-free
 constexpr int NTHR = 256;
 
-template <int BM, int BN>
+template <int BM, int BN, bool STAGE>
 struct Geom {
   static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int A_CHUNKS = BM * BK / 8 / NTHR;  // 16-byte chunks per thread
   static constexpr int SMEM_MAIN = 2 * (BM + BN) * LDK * 2;
   static constexpr int ZP = BN + 1;  // pitch (floats) of the staged epilogue tile
-  static constexpr int SMEM_Z = BM * ZP * 4;
+  static constexpr int SMEM_Z = STAGE ? BM * ZP * 4 : 0;
   static constexpr int SMEM = SMEM_MAIN > SMEM_Z ? SMEM_MAIN : SMEM_Z;
 };
+
+// epilogues that stage the output tile through LDS
+constexpr bool epi_stages(int epi) {
+  return epi == EPI_CE_FWD || epi == EPI_CE_BWD || epi == EPI_DOWN_BWD;
+}
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
@@ -136,14 +141,77 @@ __device__ __forceinline__ void z_col_reduce(float* Z, const float* X, int r, in
   __syncthreads();
 }
 
+// Row dots of the staged (dg, du) bf16 pairs with the columns' Bg / Bu rank
+// vectors: part[row][1 + j] = sum_c dg[row][c] Bg[n0+c][j],
+//          part[row][1 + r + j] = sum_c du[row][c] Bu[n0+c][j].
+// Segments of columns are combined in order through LDS (deterministic).
+template <int BM, int BN, int R>
+__device__ __forceinline__ void down_pair_reduce(uint32_t* Zu, const float* Bg, const float* Bu,
+                                                 int r, int n0, int ncols, int64_t r0, int64_t r1,
+                                                 float* part, int width) {
+  constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG, ZP = BN + 1;
+  const int tid = threadIdx.x;
+  const int row = tid % BM, seg = tid / BM;
+  float ag[R], au[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
+  const int cend = min((seg + 1) * SEGC, ncols - n0);
+  for (int c = seg * SEGC; c < cend; ++c) {
+    const uint32_t pv = Zu[row * ZP + c];
+    const float dg = __builtin_bit_cast(float, pv << 16);
+    const float du = __builtin_bit_cast(float, pv & 0xffff0000u);
+    const float* bg = Bg + (int64_t)(n0 + c) * r;
+    const float* bu = Bu + (int64_t)(n0 + c) * r;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j < r) {
+        ag[j] += dg * bg[j];
+        au[j] += du * bu[j];
+      }
+    }
+  }
+  __syncthreads();
+  float* X = reinterpret_cast<float*>(Zu);  // [NSEG][BM][2R + 1]
+  constexpr int XP = 2 * R + 1;
+  if (seg > 0) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      X[(seg * BM + row) * XP + j] = ag[j];
+      X[(seg * BM + row) * XP + R + j] = au[j];
+    }
+  }
+  __syncthreads();
+  if (seg == 0) {
+    for (int sg = 1; sg < NSEG; ++sg) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        ag[j] += X[(sg * BM + row) * XP + j];
+        au[j] += X[(sg * BM + row) * XP + R + j];
+      }
+    }
+    const int64_t pr = r0 + row;
+    if (pr < r1) {
+      float* dst = part + pr * width;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (j < r) {
+          dst[1 + j] = ag[j];
+          dst[1 + r + j] = au[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 template <int QT, int EPI, int BM, int BN>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
-  using G = Geom<BM, BN>;
+__global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(const GemmArgs p) {
+  using G = Geom<BM, BN, epi_stages(EPI)>;
   constexpr bool NN = EPI >= EPI_LIN_BWD;
   constexpr int BS = QTraits<QT>::BS;
   constexpr int TM = G::TM, TN = G::TN, WTM = G::WTM, WTN = G::WTN, ZP = G::ZP;
-  static_assert(BN == 128, "weight item mapping assumes 256 blocks per k-step");
-  static_assert(EPI != EPI_SWIGLU || TN == 2, "SwiGLU pairs gate/up n-subtiles");
+  static_assert(BN == 128 || BN == 256, "weight items: 2*BN blocks per k-step");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate/up n-subtiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -182,6 +250,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
     r1 = min(p.M, r0 + BM);
   }
   const int n0 = ntile * BN;
+  auto LCb = [&](int b) { return wn * WTN + b * 32 + (lane & 31); };
 
   // ---- activation operand: fixed rows per thread
   int64_t aoff[G::A_CHUNKS];
@@ -195,8 +264,8 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
     if (aval[i] && p.gather) src = p.gather[pr] / p.gdiv;
     aoff[i] = aval[i] ? src * p.lda + (c & 7) * 8 : 0;
   }
-  uint4 areg[G::A_CHUNKS];
-  auto load_a = [&](int kt) {
+  uint4 areg0[G::A_CHUNKS], areg1[G::A_CHUNKS];
+  auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS]) {
     int k0 = kt * BK;
     const uint16_t* base = p.a0;
     if (k0 >= p.asplit) { base = p.a1; k0 -= p.asplit; }
@@ -209,7 +278,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
         areg[i] = make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, const uint4 (&areg)[G::A_CHUNKS]) {
     uint16_t* A = As + buf * BM * LDK;
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
@@ -218,66 +287,80 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
     }
   };
 
-  // ---- weight operand: one block per thread per k-step
-  // NT: item (row = tid >> 1, kb = tid & 1): blocks 2kt + kb of weight row `wrow_n`
-  // NN: item (kb = tid >> 6, row = tid & 63): block n0/32 + kb of reduction row kt*64 + row
-  const int w_it_row = NN ? (tid & 63) : (tid >> 1);
-  const int w_it_kb = NN ? (tid >> 6) : (tid & 1);
-  const uint8_t* wptr = nullptr;  // NT: row base + kb*BS
-  bool wrow_ok = false;
-  if constexpr (!NN) {
-    const uint8_t* src = p.w0;
-    int nrow;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int proj = (w_it_row >> 5) & 1;
-      nrow = (n0 >> 1) + (w_it_row >> 6) * 32 + (w_it_row & 31);
-      src = proj ? p.w1 : p.w0;
-    } else {
-      nrow = n0 + w_it_row;
-    }
-    wrow_ok = nrow < p.w_rows;
-    wptr = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + nrow) * p.w_rowbytes +
-           w_it_kb * BS;
-  } else {
-    wrow_ok = ((n0 >> 5) + w_it_kb) < p.w_nb;
-  }
-  RawBlock<QT> wr;
-  auto load_w = [&](int kt) {
-    const uint8_t* blk = nullptr;
+  // ---- weight operand: WPT = 2*BN/256 blocks per thread per k-step.
+  // Item it = tid + 256*i:
+  // NT: (row = it >> 1, kb = it & 1): block 2kt + kb of weight row `row`
+  // NN: (kb = it >> 6, row = it & 63): block n0/32 + kb of reduction row kt*64 + row
+  constexpr int WPT = 2 * BN / NTHR;
+  int w_it_row[WPT], w_it_kb[WPT];
+  const uint8_t* wptr[WPT];  // NT: row base + kb*BS
+  bool wrow_ok[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int it = tid + NTHR * i;
+    w_it_row[i] = NN ? (it & 63) : (it >> 1);
+    w_it_kb[i] = NN ? (it >> 6) : (it & 1);
+    wptr[i] = nullptr;
     if constexpr (!NN) {
-      if (wrow_ok) blk = wptr + (int64_t)kt * 2 * BS;
+      const uint8_t* src = p.w0;
+      int nrow;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int proj = (w_it_row[i] >> 5) & 1;
+        nrow = (n0 >> 1) + (w_it_row[i] >> 6) * 32 + (w_it_row[i] & 31);
+        src = proj ? p.w1 : p.w0;
+      } else {
+        nrow = n0 + w_it_row[i];
+      }
+      wrow_ok[i] = nrow < p.w_rows;
+      wptr[i] = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + nrow) * p.w_rowbytes +
+                w_it_kb[i] * BS;
     } else {
-      const int rg = kt * BK + w_it_row;
-      if (wrow_ok && rg < p.K) {
-        const bool second = rg >= p.wsplit;
-        const uint8_t* src = second ? p.w1 : p.w0;
-        const int rr = second ? rg - p.wsplit : rg;
-        blk = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + rr) * p.w_rowbytes +
-              (int64_t)((n0 >> 5) + w_it_kb) * BS;
+      wrow_ok[i] = ((n0 >> 5) + w_it_kb[i]) < p.w_nb;
+    }
+  }
+  RawBlock<QT> wr0[WPT], wr1[WPT];
+  auto load_w = [&](int kt, RawBlock<QT> (&wr)[WPT]) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const uint8_t* blk = nullptr;
+      if constexpr (!NN) {
+        if (wrow_ok[i]) blk = wptr[i] + (int64_t)kt * 2 * BS;
+      } else {
+        const int rg = kt * BK + w_it_row[i];
+        if (wrow_ok[i] && rg < p.K) {
+          const bool second = rg >= p.wsplit;
+          const uint8_t* src = second ? p.w1 : p.w0;
+          const int rr = second ? rg - p.wsplit : rg;
+          blk = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + rr) * p.w_rowbytes +
+                (int64_t)((n0 >> 5) + w_it_kb[i]) * BS;
+        }
+      }
+      if (blk) {
+        load_block<QT>(blk, wr[i]);
+      } else {
+        wr[i].hdr = 0;
+#pragma unroll
+        for (int q = 0; q < RawBlock<QT>::NQ; ++q) wr[i].q[q] = 0;
       }
     }
-    if (blk) {
-      load_block<QT>(blk, wr);
-    } else {
-      wr.hdr = 0;
-#pragma unroll
-      for (int i = 0; i < RawBlock<QT>::NQ; ++i) wr.q[i] = 0;
-    }
   };
-  auto store_w = [&](int buf) {
-    float w[32];
-    decode_block<QT>(wr, w);
+  auto store_w = [&](int buf, const RawBlock<QT> (&wr)[WPT]) {
     uint16_t* B = Bs + buf * BN * LDK;
-    if constexpr (!NN) {
-      uint4* dst = reinterpret_cast<uint4*>(B + w_it_row * LDK + w_it_kb * 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[i] = make_uint4(pack_bf2(w[8 * i + 0], w[8 * i + 1]), pack_bf2(w[8 * i + 2], w[8 * i + 3]),
-                            pack_bf2(w[8 * i + 4], w[8 * i + 5]), pack_bf2(w[8 * i + 6], w[8 * i + 7]));
-    } else {
-      uint16_t* dst = B + (w_it_kb * 32) * LDK + w_it_row;
+    for (int i = 0; i < WPT; ++i) {
+      float w[32];
+      decode_block_fast<QT>(wr[i], w);
+      if constexpr (!NN) {
+        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * LDK + w_it_kb[i] * 32);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) dst[i * LDK] = f2bf(w[i]);
+        for (int q = 0; q < 4; ++q)
+          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
+                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
+      } else {
+        uint16_t* dst = B + (w_it_kb[i] * 32) * LDK + w_it_row[i];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) dst[q * LDK] = f2bf(w[q]);
+      }
     }
   };
 
@@ -291,18 +374,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
   const int nk = (p.K + BK - 1) / BK;
-  load_a(0);
-  load_w(0);
-  store_a(0);
-  store_w(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_a(kt + 1);
-      load_w(kt + 1);
-    }
+  // Software pipeline, prefetch depth 2: tile kt+2 is loaded into the
+  // register set that tile kt was stored from, while the MFMAs of tile kt run
+  // and tile kt+1 (loaded one step earlier) waits in the other set.
+  auto compute = [&](int cur) {
     const uint16_t* A = As + cur * BM * LDK;
     const uint16_t* B = Bs + cur * BN * LDK;
 #pragma unroll
@@ -322,66 +397,199 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
         for (int b = 0; b < TN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
-    if (more) {
-      store_a(cur ^ 1);
-      store_w(cur ^ 1);
+  };
+  constexpr bool DEEP = BM * BN < 256 * 256;  // small tiles: prefetch depth 2
+  if constexpr (DEEP) {
+    load_a(0, areg0);
+    load_w(0, wr0);
+    if (nk > 1) {
+      load_a(1, areg1);
+      load_w(1, wr1);
     }
+    store_a(0, areg0);
+    store_w(0, wr0);
     __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      // even step: compute buffer 0, refill set 0 with tile kt+2, store set 1 (tile kt+1)
+      if (kt + 2 < nk) {
+        load_a(kt + 2, areg0);
+        load_w(kt + 2, wr0);
+      }
+      compute(0);
+      if (kt + 1 < nk) {
+        store_a(1, areg1);
+        store_w(1, wr1);
+      }
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      // odd step: compute buffer 1, refill set 1 with tile kt+3, store set 0 (tile kt+2)
+      if (kt + 3 < nk) {
+        load_a(kt + 3, areg1);
+        load_w(kt + 3, wr1);
+      }
+      compute(1);
+      if (kt + 2 < nk) {
+        store_a(0, areg0);
+        store_w(0, wr0);
+      }
+      __syncthreads();
+    }
+  } else {
+    // large tiles: one k-step of MFMAs (~2k cycles per wave) covers the
+    // latency of the next tile's loads; one register set
+    load_a(0, areg0);
+    load_w(0, wr0);
+    store_a(0, areg0);
+    store_w(0, wr0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        load_a(kt + 1, areg0);
+        load_w(kt + 1, wr0);
+      }
+      compute(cur);
+      if (more) {
+        store_a(cur ^ 1, areg0);
+        store_w(cur ^ 1, wr0);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- rank-r adapter term, folded into the accumulators on the MFMA:
+  //   acc[row][col] += sum_j X(row, j) * s * Y(col, j)
+  // over one k16 slice per 16 adapter ranks.  X and s*Y are split into bf16
+  // hi + lo parts and accumulated as hi*hi + hi*lo + lo*hi (about 16
+  // significant bits, far inside the bf16 output precision).  Row / column
+  // operands follow the MFMA layout: lane l holds row (col) l%32 and ranks
+  // 8*(l/32) .. +8 of the slice.
+  const int r = p.r;
+  const float s = p.s;
+  constexpr int NSET = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr bool FOLD = EPI != EPI_DH_ACC;
+  if constexpr (FOLD) {
+    const int rtot = EPI == EPI_GATEUP_BWD ? 2 * r : r;
+    const float* Y0;
+    const float* Y1 = nullptr;
+    if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD || EPI == EPI_GATEUP_BWD) {
+      Y0 = p.lA0 + (int64_t)e * p.lA_estride;  // A [r][N]: Y(c, j) = A[j*N + c]
+      if constexpr (EPI == EPI_GATEUP_BWD) Y1 = p.lA1 + (int64_t)e * p.lA_estride;
+    } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+      Y0 = p.lB0 + (int64_t)p.w_row0 * r;      // B [V][r], columns from w_row0
+    } else {
+      Y0 = p.lB0 + (int64_t)e * p.lB_estride;  // B [N][r]
+      if constexpr (EPI == EPI_SWIGLU) Y1 = p.lB1 + (int64_t)e * p.lB_estride;
+    }
+    auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)v[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(v[i] - (float)h);
+      }
+    };
+    for (int q = 0; q * 16 < rtot; ++q) {
+      const int j0 = q * 16 + (lane >> 5) * 8;
+      bf16x8 ah[TM][NSET], al[TM][NSET];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int64_t row = r0 + wm * WTM + a * 32 + (lane & 31);
+        const bool ok = row < r1;
+#pragma unroll
+        for (int st = 0; st < NSET; ++st) {
+          const float* X = st == 0 ? p.rv0 : p.rv1;
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i;
+            float x = 0.f;
+            if (ok && j < rtot) {
+              if constexpr (EPI == EPI_GATEUP_BWD)
+                x = j < r ? p.rv0[row * r + j] : p.rv1[row * r + j - r];
+              else
+                x = X[row * r + j];
+            }
+            v[i] = x;
+          }
+          split8(v, ah[a][st], al[a][st]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int st = EPI == EPI_SWIGLU ? (b & 1) : 0;
+        int col;
+        bool ok;
+        if constexpr (EPI == EPI_SWIGLU) {
+          col = (n0 >> 1) + (wn * (TN / 2) + (b >> 1)) * 32 + (lane & 31);
+          ok = col < p.w_rows;
+        } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+          col = n0 + LCb(b);
+          ok = col < p.w_rows;
+        } else {
+          col = n0 + LCb(b);
+          ok = col < p.N;
+        }
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = j0 + i;
+          float y = 0.f;
+          if (ok && j < rtot) {
+            if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD)
+              y = Y0[(int64_t)j * p.N + col];
+            else if constexpr (EPI == EPI_GATEUP_BWD)
+              y = j < r ? Y0[(int64_t)j * p.N + col] : Y1[(int64_t)(j - r) * p.N + col];
+            else
+              y = (st == 0 ? Y0 : Y1)[(int64_t)col * r + j];
+          }
+          v[i] = s * y;
+        }
+        bf16x8 bh, bl;
+        split8(v, bh, bl);
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bh, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bl, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a][st], bh, acc[a][b], 0, 0, 0);
+        }
+      }
+    }
   }
 
   // ---- epilogues.  acc[a][b][v] sits at local row
   //   lr = wm*WTM + a*32 + (v>>2)*8 + (lane>>5)*4 + (v&3), local col lc = wn*WTN + b*32 + (lane&31)
-  const int r = p.r;
-  const float s = p.s;
   auto LR = [&](int a, int v) { return wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); };
-  auto LC = [&](int b) { return wn * WTN + b * 32 + (lane & 31); };
-  auto dotr = [&](const float* x, const float* y) {
-    float t = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) t += x[j] * y[j];
-    return t;
-  };
+  auto LC = [&](int b) { return LCb(b); };
 
-  if constexpr (EPI == EPI_LIN) {
-    const float* Bm = p.lB0 + (int64_t)e * p.lB_estride;
+  if constexpr (EPI == EPI_LIN || EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
       const int n = n0 + LC(b);
       if (n >= p.N) continue;
-      float bv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) bv[j] = j < r ? Bm[(int64_t)n * r + j] : 0.f;
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t pr = r0 + LR(a, v);
-          if (pr < r1) {
-            const float val = acc[a][b][v] + s * dotr(p.rv0 + pr * r, bv);
-            p.o0[pr * p.ldo + n] = f2bf(val);
-          }
+          if (pr < r1) p.o0[pr * p.ldo + n] = f2bf(acc[a][b][v]);
         }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    const int i = (n0 >> 1) + wn * 32 + (lane & 31);
-    if (i < p.w_rows) {
-      const float* Bg = p.lB0 + (int64_t)e * p.lB_estride + (int64_t)i * r;
-      const float* Bu = p.lB1 + (int64_t)e * p.lB_estride + (int64_t)i * r;
-      float bg[16], bu[16];
+    // n-subtiles come in (gate, up) pairs over the same 32 intermediate rows
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        bg[j] = j < r ? Bg[j] : 0.f;
-        bu[j] = j < r ? Bu[j] : 0.f;
-      }
+    for (int b2 = 0; b2 < TN / 2; ++b2) {
+      const int i = (n0 >> 1) + (wn * (TN / 2) + b2) * 32 + (lane & 31);
+      if (i >= p.w_rows) continue;
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t pr = r0 + LR(a, v);
           if (pr < r1) {
-            const float g = acc[a][0][v] + s * dotr(p.rv0 + pr * r, bg);
-            const float u = acc[a][1][v] + s * dotr(p.rv1 + pr * r, bu);
+            const float g = acc[a][2 * b2][v];
+            const float u = acc[a][2 * b2 + 1][v];
             const float h = g * sigmoidf_(g) * u;
             const int64_t o = pr * p.ldo + i;
             p.o0[o] = f2bf(h);
@@ -390,45 +598,6 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
           }
         }
     }
-  } else if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
-    constexpr bool DUAL = EPI == EPI_GATEUP_BWD;
-    const float* A0 = p.lA0 + (int64_t)e * p.lA_estride;
-    const float* A1 = DUAL ? p.lA1 + (int64_t)e * p.lA_estride : nullptr;
-    float av0[TN][16], av1[TN][16];
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int c = n0 + LC(b);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        av0[b][j] = (c < p.N && j < r) ? A0[(int64_t)j * p.N + c] : 0.f;
-        av1[b][j] = (DUAL && c < p.N && j < r) ? A1[(int64_t)j * p.N + c] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t pr = r0 + LR(a, v);
-        if (pr >= r1) continue;
-        float x0[16], x1[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          x0[j] = j < r ? p.rv0[pr * r + j] : 0.f;
-          x1[j] = (DUAL && j < r) ? p.rv1[pr * r + j] : 0.f;
-        }
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int c = n0 + LC(b);
-          if (c >= p.N) continue;
-          float t = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            t += x0[j] * av0[b][j];
-            if (DUAL) t += x1[j] * av1[b][j];
-          }
-          p.o0[pr * p.ldo + c] = f2bf(acc[a][b][v] + s * t);
-        }
-      }
   } else if constexpr (EPI == EPI_DH_ACC) {
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
@@ -446,108 +615,87 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
         }
     }
   } else if constexpr (EPI == EPI_DOWN_BWD) {
-    // columns are the expert's intermediate index i (< N = I).  Pass 0 writes
-    // dg, du (bf16) and stages e*h for the dw row sums; passes 1 and 2 read
-    // back this thread's own dg / du and stage them for the row dots with
-    // Bg / Bu (the same rounded values the gate/up backward consumes).
+    // columns are the expert's intermediate index i (< N = I); acc holds
+    // e = dY deq(Wd) + s (dY Bd) Ad.  One compute pass writes dg, du (bf16),
+    // stages e*h and keeps (dg, du) packed in registers; two LDS row
+    // reductions give the dw and (dg Bg, du Bu) partials of this column tile.
     float* Z = reinterpret_cast<float*>(smem);
-    const float* Ad = p.lA0 + (int64_t)e * p.lA_estride;
+    uint32_t* Zu = reinterpret_cast<uint32_t*>(smem);
     const int width = 1 + 2 * r;
-    {
-      float av[TN][16];
+    uint32_t pk[TM][TN][16];
 #pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int c = n0 + LC(b);
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) av[b][j] = (c < p.N && j < r) ? Ad[(int64_t)j * p.N + c] : 0.f;
-      }
+      for (int v = 0; v < 16; ++v) {
+        const int lr = LR(a, v);
+        const int64_t pr = r0 + lr;
+        const bool rok = pr < r1;
+        const float wp = rok ? p.wflat[p.sorted[pr]] : 0.f;
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lr = LR(a, v);
-          const int64_t pr = r0 + lr;
-          const bool rok = pr < r1;
-          float x[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) x[j] = (rok && j < r) ? p.rv0[pr * r + j] : 0.f;
-          const float wp = rok ? p.wflat[p.sorted[pr]] : 0.f;
-#pragma unroll
-          for (int b = 0; b < TN; ++b) {
-            const int lc = LC(b);
-            const int c = n0 + lc;
-            float zv = 0.f;
-            if (rok && c < p.N) {
-              float t = 0.f;
-#pragma unroll
-              for (int j = 0; j < 16; ++j) t += x[j] * av[b][j];
-              const float ev = acc[a][b][v] + s * t;
-              const int64_t o = pr * p.ldo + c;
-              const float gg = bf2f(p.s0[o]), uu = bf2f(p.s1[o]);
-              const float sg = sigmoidf_(gg);
-              const float silu = gg * sg;
-              const float dh = wp * ev;
-              p.o0[o] = f2bf(dh * uu * sg * (1.f + gg * (1.f - sg)));
-              p.o1[o] = f2bf(dh * silu);
-              zv = ev * silu * uu;
-            }
-            Z[lr * ZP + lc] = zv;
+        for (int b = 0; b < TN; ++b) {
+          const int lc = LC(b);
+          const int c = n0 + lc;
+          float zv = 0.f;
+          uint32_t packed = 0;
+          if (rok && c < p.N) {
+            const float ev = acc[a][b][v];
+            const int64_t o = pr * p.ldo + c;
+            const float gg = bf2f(p.s0[o]), uu = bf2f(p.s1[o]);
+            const float sg = sigmoidf_(gg);
+            const float silu = gg * sg;
+            const float dh = wp * ev;
+            packed = pack_bf2(dh * uu * sg * (1.f + gg * (1.f - sg)), dh * silu);
+            p.o0[o] = (uint16_t)(packed & 0xffffu);
+            p.o1[o] = (uint16_t)(packed >> 16);
+            zv = ev * silu * uu;
           }
+          pk[a][b][v] = packed;
+          Z[lr * ZP + lc] = zv;
         }
-    }
+      }
     __syncthreads();
     z_row_reduce<BM, BN>(Z, nullptr, r, 1, n0, p.N, [&](int row, float(&out)[16]) {
       const int64_t pr = r0 + row;
       if (pr < r1) p.f0[((int64_t)ntile * p.M + pr) * width] = out[0];
     });
-#pragma unroll 1
-    for (int pass = 1; pass < 3; ++pass) {
-      const uint16_t* src = pass == 1 ? p.o0 : p.o1;
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lr = LR(a, v);
-          const int64_t pr = r0 + lr;
+      for (int b = 0; b < TN; ++b)
 #pragma unroll
-          for (int b = 0; b < TN; ++b) {
-            const int lc = LC(b);
-            const int c = n0 + lc;
-            Z[lr * ZP + lc] = (pr < r1 && c < p.N) ? bf2f(src[pr * p.ldo + c]) : 0.f;
-          }
-        }
-      __syncthreads();
-      const float* Wc = (pass == 1 ? p.lB1 : p.lB2) + (int64_t)e * p.lB_estride;
-      const int off = pass == 1 ? 1 : 1 + r;
-      z_row_reduce<BM, BN>(Z, Wc, r, r, n0, p.N, [&](int row, float(&out)[16]) {
-        const int64_t pr = r0 + row;
-        if (pr < r1) {
-          float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width + off;
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (j < r) dst[j] = out[j];
-        }
-      });
-    }
+        for (int v = 0; v < 16; ++v) Zu[LR(a, v) * ZP + LC(b)] = pk[a][b][v];
+    __syncthreads();
+    const float* Bg = p.lB1 + (int64_t)e * p.lB_estride;
+    const float* Bu = p.lB2 + (int64_t)e * p.lB_estride;
+    float* part = p.f0 + (int64_t)ntile * p.M * width;
+    if (r <= 4)
+      down_pair_reduce<BM, BN, 4>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
+    else if (r <= 8)
+      down_pair_reduce<BM, BN, 8>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
+    else
+      down_pair_reduce<BM, BN, 16>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
   } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+    // acc holds the logits z of this tile (adapter term included)
     float* Z = reinterpret_cast<float*>(smem);
     const int64_t V = p.V;
     const int64_t c0 = p.w_row0;  // vocab offset of this launch's columns
-    const float* Bm = p.lB0;
     float coef = 0.f;
     if constexpr (EPI == EPI_CE_BWD) {
       const float nv = *p.nvalid;
       coef = nv > 0.f ? p.coef / nv : 0.f;
     }
+    // the gradient tile G (bwd) or the logits (fwd), staged in Z
+    auto gval = [&](int a, int b, int v, int64_t pr, int n) {
+      const int64_t vv = c0 + n;
+      const int64_t lab = p.labels[pr];
+      const bool valid = lab != p.ignore_index && lab >= 0 && lab < V;
+      if (!valid || n >= p.w_rows) return 0.f;
+      return coef * (__expf(acc[a][b][v] - p.lse[pr]) - (vv == lab ? 1.f : 0.f));
+    };
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
       const int lc = LC(b);
       const int n = n0 + lc;
-      const int64_t vv = c0 + n;
-      const bool vok = n < p.w_rows;  // inside this launch's vocab range
-      float bv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) bv[j] = (vok && j < r) ? Bm[vv * r + j] : 0.f;
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -556,17 +704,11 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
           const int64_t pr = r0 + lr;
           float zv;
           if constexpr (EPI == EPI_CE_FWD) {
-            zv = -INFINITY;
-            if (pr < r1 && vok) zv = acc[a][b][v] + s * dotr(p.rv0 + pr * r, bv);
+            zv = (pr < r1 && n < p.w_rows) ? acc[a][b][v] : -INFINITY;
           } else {
             zv = 0.f;
             if (pr < r1) {
-              const int64_t lab = p.labels[pr];
-              const bool valid = lab != p.ignore_index && lab >= 0 && lab < V;
-              if (valid && vok) {
-                const float z = acc[a][b][v] + s * dotr(p.rv0 + pr * r, bv);
-                zv = coef * (__expf(z - p.lse[pr]) - (vv == lab ? 1.f : 0.f));
-              }
+              zv = gval(a, b, v, pr, n);
               if (n < p.ldo) p.o0[pr * p.ldo + n] = f2bf(zv);
             }
           }
@@ -619,7 +761,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
       if (have_lab) p.f1[pr] = zl;
     } else {
       // G . B over this tile's vocab columns -> part_GB[ntile][T][r]
-      z_row_reduce<BM, BN>(Z, Bm + c0 * r, r, r, n0, p.w_rows, [&](int row, float(&out)[16]) {
+      z_row_reduce<BM, BN>(Z, p.lB0 + c0 * r, r, r, n0, p.w_rows, [&](int row, float(&out)[16]) {
         const int64_t pr = r0 + row;
         if (pr < r1) {
           float* dst = p.f1 + ((int64_t)(p.ntile_base + ntile) * p.M + pr) * r;
@@ -628,7 +770,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
             if (j < r) dst[j] = out[j];
         }
       });
-      // G^T . xa over this tile's rows -> part_dB[mtile][V][r]  (rewrite Z first)
+      // G^T . xa over this tile's rows -> part_dB[mtile][V][r]  (restage G)
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const int lc = LC(b);
@@ -639,17 +781,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
           for (int v = 0; v < 16; ++v) {
             const int lr = LR(a, v);
             const int64_t pr = r0 + lr;
-            float zv = 0.f;
-            if (pr < r1 && n < p.w_rows) {
-              const int64_t lab = p.labels[pr];
-              const bool valid = lab != p.ignore_index && lab >= 0 && lab < V;
-              if (valid) {
-                const int64_t vv = c0 + n;
-                const float z = acc[a][b][v] + s * dotr(p.rv0 + pr * r, Bm + vv * r);
-                zv = coef * (__expf(z - p.lse[pr]) - (vv == lab ? 1.f : 0.f));
-              }
-            }
-            Z[lr * ZP + lc] = zv;
+            Z[lr * ZP + lc] = pr < r1 ? gval(a, b, v, pr, n) : 0.f;
           }
       }
       __syncthreads();
@@ -669,6 +801,12 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs p) {
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(NTHR);
+  if constexpr (!epi_stages(EPI)) {
+    if (tilecfg == TILE_256x256) {
+      hipLaunchKernelGGL((gemm_kernel<QT, EPI, 256, 256>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (tilecfg == TILE_128x128)
     hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128>), grid, block, 0, st, a);
   else

@@ -84,10 +84,12 @@ struct GemmArgs {
   const float* nvalid; // EPI_CE_BWD: device count of valid labels
 };
 
-enum TileCfg { TILE_128x128 = 0, TILE_64x128 = 1 };
+enum TileCfg { TILE_128x128 = 0, TILE_64x128 = 1, TILE_256x256 = 2 };
 
-// tile rows (BM) of a tile configuration
-inline int tile_bm(int cfg) { return cfg == TILE_128x128 ? 128 : 64; }
+// tile rows (BM) and columns (BN) of a tile configuration.  TILE_256x256 is
+// available for the epilogues that do not stage through LDS.
+inline int tile_bm(int cfg) { return cfg == TILE_256x256 ? 256 : (cfg == TILE_128x128 ? 128 : 64); }
+inline int tile_bn(int cfg) { return cfg == TILE_256x256 ? 256 : 128; }
 constexpr int TILE_BN = 128;
 constexpr int GEMM_BK = 64;
 
@@ -149,6 +151,8 @@ struct ColRedArgs {
   float* part;              // [slots][C][r]
 };
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st);
+// columns per thread of launch_colred (the grid covers 256 * this per block)
+int colred_cols_per_thread(int r);
 
 // out = s * sum over an expert's slots (in order) of part; experts with no
 // rows get zeros.  transpose: out[e][j][c] instead of out[e][c][j].

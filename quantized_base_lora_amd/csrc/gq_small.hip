@@ -88,41 +88,87 @@ __device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_
 }
 
 // ------------------------------------------------------------- row dots
-template <int NOUT>
+// out[o][p][j] = sum_c act(p)[c] * W_o(e_p)[j][c], j < r <= R.
+// One wave owns RB consecutive rows; lanes split the columns 8 at a time
+// (16-byte activation loads), so each loaded chunk of W serves RB rows.
+// WT: W stored [C][r] (a LoRA B matrix) instead of [r][C] (an A matrix).
+// The per-lane partials are reduced across the wave with a fixed shuffle
+// tree (deterministic).
+template <int R, int NOUT, bool WT>
 __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
+  constexpr int RB = R <= 4 ? 4 : (R <= 8 ? 2 : 1);
   const int lane = threadIdx.x & 63;
-  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= a.M) return;
+  const int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RB;
+  if (p0 >= a.M) return;
   const int r = a.r;
-  int e = 0;
-  if (a.offsets) e = find_expert(a.offsets, a.E, p);
-  const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
-  const uint16_t* x = a.act + src * a.lda;
-  float acc[NOUT][16];
+  int eq[RB];
+  const uint16_t* xq[RB];
+  bool vq[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    const int64_t p = p0 + q;
+    vq[q] = p < a.M;
+    eq[q] = (vq[q] && a.offsets) ? find_expert(a.offsets, a.E, p) : 0;
+    const int64_t src = !vq[q] ? 0 : (a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p);
+    xq[q] = a.act + src * a.lda;
+  }
+  float acc[NOUT][RB][R];
 #pragma unroll
   for (int o = 0; o < NOUT; ++o)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[o][j] = 0.f;
-  for (int c = lane * 8; c < a.C; c += 512) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + c);
-    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-    float xv[8];
+    for (int q = 0; q < RB; ++q)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      xv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
-      xv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
+      for (int j = 0; j < R; ++j) acc[o][q][j] = 0.f;
+  for (int c = lane * 8; c < a.C; c += 512) {
+    float xv[RB][8];
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (vq[q]) raw = *reinterpret_cast<const uint4*>(xq[q] + c);
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        xv[q][2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
+        xv[q][2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
+      }
     }
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) {
-      const float* W = a.W[o] + (int64_t)e * a.w_estride;
+      float w[R][8];
+      int ecur = -1;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < r) {
-          const float* wj = W + (int64_t)j * a.w_jstride + (int64_t)c * a.w_cstride;
-          float t = 0.f;
+      for (int q = 0; q < RB; ++q) {
+        if (!vq[q]) continue;
+        if (eq[q] != ecur) {
+          ecur = eq[q];
+          const float* W = a.W[o] + (int64_t)ecur * a.w_estride;
+          if constexpr (WT) {
+            // [C][r]: the 8 columns' rank vectors are contiguous
 #pragma unroll
-          for (int q = 0; q < 8; ++q) t += xv[q] * wj[q * a.w_cstride];
-          acc[o][j] += t;
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+              for (int j = 0; j < R; ++j) w[j][t] = j < r ? W[(int64_t)(c + t) * r + j] : 0.f;
+          } else {
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+              if (j < r) {
+                const float4 lo = *reinterpret_cast<const float4*>(W + (int64_t)j * a.C + c);
+                const float4 hi = *reinterpret_cast<const float4*>(W + (int64_t)j * a.C + c + 4);
+                w[j][0] = lo.x; w[j][1] = lo.y; w[j][2] = lo.z; w[j][3] = lo.w;
+                w[j][4] = hi.x; w[j][5] = hi.y; w[j][6] = hi.z; w[j][7] = hi.w;
+              } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) w[j][t] = 0.f;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          float t0 = 0.f;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) t0 += xv[q][t] * w[j][t];
+          acc[o][q][j] += t0;
         }
       }
     }
@@ -130,27 +176,36 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
 #pragma unroll
   for (int o = 0; o < NOUT; ++o)
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) acc[o][j] = warp_sum(acc[o][j]);
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (j < r) acc[o][q][j] = warp_sum(acc[o][q][j]);
   if (lane == 0) {
-    float wp = 0.f;
-    if (a.out2) wp = a.wflat[a.sorted[p]];
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o)
+    for (int q = 0; q < RB; ++q) {
+      if (!vq[q]) continue;
+      const int64_t p = p0 + q;
+      const float wp = a.out2 ? a.wflat[a.sorted[p]] : 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < r) {
-          a.out[o][p * r + j] = acc[o][j];
-          if (o == 0 && a.out2) a.out2[p * r + j] = wp * acc[o][j];
-        }
+      for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (j < r) {
+            a.out[o][p * r + j] = acc[o][q][j];
+            if (o == 0 && a.out2) a.out2[p * r + j] = wp * acc[o][q][j];
+          }
+    }
   }
 }
 
 // ---------------------------------------------------- column reductions
-// Each thread owns 2 adjacent columns; a block covers 512 columns of one slot.
+// part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j].  Each thread
+// owns CPT adjacent columns (one 16- or 8-byte load per row); the row index,
+// gather and V[p] are uniform across the block (scalar loads).
+template <int R, int CPT>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   const int slot = blockIdx.x;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 2;
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * CPT;
   int64_t r0, r1;
   if (a.offsets) {
     const int32_t* cs = a.chunk_start;
@@ -164,29 +219,46 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   }
   if (c >= a.C) return;
   const int r = a.r;
-  float acc0[16], acc1[16];
+  float acc[CPT][R];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc0[j] = acc1[j] = 0.f;
+  for (int t = 0; t < CPT; ++t)
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
+#pragma unroll 4
   for (int64_t p = r0; p < r1; ++p) {
     const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
-    const uint32_t u2 = *reinterpret_cast<const uint32_t*>(a.U + src * a.ldu + c);
-    const float u0 = bf2f((uint16_t)(u2 & 0xffffu)), u1 = bf2f((uint16_t)(u2 >> 16));
-    const float* v = a.Vv + p * r;
+    const uint16_t* u = a.U + src * a.ldu + c;
+    float uv[CPT];
+    if constexpr (CPT == 8) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(u);
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) {
-        const float vj = v[j];
-        acc0[j] += u0 * vj;
-        acc1[j] += u1 * vj;
+      for (int t = 0; t < 4; ++t) {
+        uv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
+        uv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
       }
+    } else {
+      const uint2 raw = *reinterpret_cast<const uint2*>(u);
+      uv[0] = bf2f((uint16_t)(raw.x & 0xffffu));
+      uv[1] = bf2f((uint16_t)(raw.x >> 16));
+      uv[2] = bf2f((uint16_t)(raw.y & 0xffffu));
+      uv[3] = bf2f((uint16_t)(raw.y >> 16));
+    }
+    const float* v = a.Vv + p * r;
+    float vv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) vv[j] = j < r ? v[j] : 0.f;
+#pragma unroll
+    for (int t = 0; t < CPT; ++t)
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[j];
   }
   float* dst = a.part + ((int64_t)slot * a.C + c) * r;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < r) {
-      dst[j] = acc0[j];
-      dst[r + j] = acc1[j];
-    }
+  for (int t = 0; t < CPT; ++t)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < r) dst[t * r + j] = acc[t][j];
 }
 
 // out[e] = s * sum_{slots of e} part[slot]; thread per (c, j) of one expert
@@ -537,20 +609,37 @@ hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int3
   return hipGetLastError();
 }
 
-hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
-  if (a.M == 0) return hipSuccess;
-  const dim3 g(blocks_for(a.M, 4)), b(256);
-  if (a.nout == 2)
-    hipLaunchKernelGGL(rowdot_kernel<2>, g, b, 0, st, a);
-  else
-    hipLaunchKernelGGL(rowdot_kernel<1>, g, b, 0, st, a);
+template <int R>
+hipError_t rowdot_r(const RowDotArgs& a, hipStream_t st) {
+  constexpr int RB = R <= 4 ? 4 : (R <= 8 ? 2 : 1);
+  const dim3 g(blocks_for(a.M, 4 * RB)), b(256);
+  const bool wt = a.w_jstride == 1;
+  if (a.nout == 2) {
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<R, 2, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<R, 2, false>), g, b, 0, st, a);
+  } else {
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<R, 1, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<R, 1, false>), g, b, 0, st, a);
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  if (a.r <= 4) return rowdot_r<4>(a, st);
+  if (a.r <= 8) return rowdot_r<8>(a, st);
+  return rowdot_r<16>(a, st);
+}
+
+int colred_cols_per_thread(int r) { return r <= 8 ? 8 : 4; }
+
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   if (a.slots == 0) return hipSuccess;
-  const dim3 g((unsigned)a.slots, blocks_for(a.C, 512)), b(256);
-  hipLaunchKernelGGL(colred_kernel, g, b, 0, st, a);
+  const int cpt = colred_cols_per_thread(a.r);
+  const dim3 g((unsigned)a.slots, blocks_for(a.C, 256 * cpt)), b(256);
+  if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8>), g, b, 0, st, a);
+  else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((colred_kernel<16, 4>), g, b, 0, st, a);
   return hipGetLastError();
 }
 
