@@ -213,6 +213,82 @@ def main():
                                "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
 
+    # ------------------------------------------------------- other workloads
+    if args.all:
+        extra = {}
+
+        def timed(fn, steps):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, b = ev(), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        c1 = synth.CFG1
+        i1 = synth.make_linear(c1)
+        p1 = gq.Proj(c1.qtype, c1.N, c1.K, u8(i1["blocks"]), f32(i1["A"]), f32(i1["B"]),
+                     float(i1["scale"]))
+        x1, dy1 = bf(i1["x"]), bf(i1["dy"])
+
+        def s1():
+            yy, xa1 = gq.linear_lora_fwd(p1, x1)
+            return gq.linear_lora_bwd(p1, x1, xa1, dy1)
+
+        m1 = timed(s1, K)
+        f1 = linear_flops(c1.T, c1.K, c1.N, c1.rank)
+        extra[c1.name] = {"ms_per_step": round(m1, 4), "tflops": round(f1 / (m1 * 1e-3) / 1e12, 2)}
+        log(f"[bench] {c1.name}: {m1 * 1e3:.1f} us/step")
+
+        c4 = synth.CFG4
+        t0 = time.time()
+        i4 = synth.make_moe(c4)
+        log(f"[bench] inputs {c4.name} generated in {time.time() - t0:.1f}s")
+        s4 = float(i4["scale"])
+        mk4 = lambda w, a, b, no, ni: gq.Proj(c4.qtype, no, ni, u8(w), f32(a), f32(b), s4, c4.E)
+        w4 = gq.MoEWeights(mk4(i4["wg"], i4["ag"], i4["bg"], c4.I, c4.H),
+                           mk4(i4["wu"], i4["au"], i4["bu"], c4.I, c4.H),
+                           mk4(i4["wd"], i4["ad"], i4["bd"], c4.H, c4.I))
+        x4, dy4, lg4 = bf(i4["x"]), bf(i4["dy"]), f32(i4["logits"])
+        del i4
+
+        def st4():
+            yy, sv = gq.moe_ffn_fwd(w4, x4, lg4, c4.k)
+            return gq.moe_ffn_bwd(w4, x4, dy4, sv, c4.k, c4.E)
+
+        m4 = timed(st4, max(3, K // 4))
+        f4 = moe_flops(c4.T, c4.H, c4.I, c4.k, c4.rank)
+        extra[c4.name] = {"ms_per_step": round(m4, 4), "tokens_per_s": round(c4.T / (m4 * 1e-3), 1),
+                          "tflops": round(f4 / (m4 * 1e-3) / 1e12, 2)}
+        log(f"[bench] {c4.name}: {m4:.3f} ms/step")
+        del w4, x4, dy4, lg4
+
+        c5 = synth.CFG5
+        t0 = time.time()
+        i5 = synth.make_head(c5)
+        log(f"[bench] inputs {c5.name} generated in {time.time() - t0:.1f}s")
+        hd = gq.Proj(c5.qtype, c5.V, c5.H, u8(i5["blocks"]), f32(i5["A"]), f32(i5["B"]),
+                     float(i5["scale"]))
+        h5 = bf(i5["h"])
+        lab5 = torch.from_numpy(i5["labels"]).to(dev)
+        ws5 = [None]
+
+        def st5():
+            out = gq.lmhead_chunked_ce(hd, h5, lab5, chunk_rows=c5.chunk, ws=ws5[0])
+            ws5[0] = out["ws"]
+            return out
+
+        m5 = timed(st5, max(3, K // 4))
+        f5 = 6 * c5.T * c5.V * c5.H + 8 * c5.T * c5.V * c5.rank + 6 * c5.T * c5.rank * c5.H
+        extra[c5.name] = {"ms_per_step": round(m5, 4), "tokens_per_s": round(c5.T / (m5 * 1e-3), 1),
+                          "tflops": round(f5 / (m5 * 1e-3) / 1e12, 2)}
+        log(f"[bench] {c5.name}: {m5:.3f} ms/step")
+        result["other_workloads"] = extra
+
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu:
         from threadpoolctl import threadpool_info
