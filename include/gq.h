@@ -114,6 +114,7 @@ int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int ou
  *   A         [E][rank][n_in]  float32
  *   B         [E][n_out][rank] float32
  *   scale     s = alpha / rank
+ * Pointers: w_blocks 4-byte aligned, A and B 16-byte aligned.
  * Constraints: n_in % 64 == 0 (whole pairs of blocks per row, so every row
  * starts dword-aligned), n_out % 8 == 0 (16-byte activation rows in the
  * backward), 1 <= rank <= 16, 1 <= n_experts <= 1024.  Grouped backward also

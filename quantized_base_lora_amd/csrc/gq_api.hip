@@ -90,8 +90,8 @@ int check_proj(const gq_lora_linear* L, const char* name, bool grouped) {
   if (L->n_experts < 1 || L->n_experts > 1024)
     return fail(GQ_EINVAL, "%s: n_experts %d not in [1, 1024]", name, L->n_experts);
   if (!L->w_blocks || !L->A || !L->B) return fail(GQ_EINVAL, "%s: NULL weight or adapter", name);
-  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 16) || !aligned(L->B, 4))
-    return fail(GQ_EINVAL, "%s: w_blocks and B must be 4-byte and A 16-byte aligned", name);
+  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 16) || !aligned(L->B, 16))
+    return fail(GQ_EINVAL, "%s: w_blocks must be 4-byte and A, B 16-byte aligned", name);
   return GQ_OK;
 }
 
@@ -118,10 +118,10 @@ GemmArgs gemm_defaults() {
 // power of two (16..512) that still gives >= 512 workgroups, so that the
 // reduction fills the chip without multiplying the partial-sum traffic.
 int pick_rc(int64_t M, int64_t C, int r, int E) {
-  const int64_t cb = cdiv(C, 256 * colred_cols_per_thread(r));
+  const int64_t cb = cdiv(C, colred_cols_per_block(r));
   const int extra = E > 1 ? E : 0;
-  int rc = 16;
-  while (rc < 512 && (cdiv(M, rc * 2) + extra) * cb >= 512) rc *= 2;
+  int rc = 32;
+  while (rc < 1024 && (cdiv(M, rc * 2) + extra) * cb >= 512) rc *= 2;
   return rc;
 }
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }

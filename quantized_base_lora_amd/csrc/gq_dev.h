@@ -56,26 +56,47 @@ template <int QT> struct RawBlock {
 // starts 2 bytes past a dword boundary, and runs at most 2 bytes past its end
 // otherwise; callers only issue the latter kind when another block follows
 // in the same row (rows of an even number of blocks start dword-aligned).
+template <int QT> struct BlockWindow {
+  uint32_t dw[QTraits<QT>::NDW];
+  uint32_t sh;  // nonzero: the block starts at byte 2 of dw[0]
+};
+
+// Issue the dword loads of one block and nothing else, so that a prefetch
+// does not pull the realignment (which waits for the data) up to the load.
 template <int QT>
-__device__ __forceinline__ void load_block(const uint8_t* blk, RawBlock<QT>& rb) {
-  constexpr int NDW = QTraits<QT>::NDW;
+__device__ __forceinline__ void load_window(const uint8_t* blk, BlockWindow<QT>& w) {
   const uintptr_t a = (uintptr_t)blk;
-  const uint32_t* p = (const uint32_t*)(a & ~(uintptr_t)3);
-  uint32_t dw[NDW];
+  // global address space explicitly: a generic (flat) load would also count
+  // against the LDS wait counter and serialise with the LDS reads
+  const __attribute__((address_space(1))) uint32_t* p =
+      (const __attribute__((address_space(1))) uint32_t*)(a & ~(uintptr_t)3);
 #pragma unroll
-  for (int i = 0; i < NDW; ++i) dw[i] = p[i];
+  for (int i = 0; i < QTraits<QT>::NDW; ++i) w.dw[i] = p[i];
+  w.sh = (uint32_t)(a & 2);
+}
+
+// Realign a loaded window to hdr + payload dwords, ANDed with `mask`.
+template <int QT>
+__device__ __forceinline__ void realign(const BlockWindow<QT>& w, uint32_t mask, RawBlock<QT>& rb) {
   if constexpr (QT == QT_Q2_DM) {
     // 12-byte blocks in dword-aligned rows are always dword-aligned
-    rb.hdr = dw[0];
-    rb.q[0] = dw[1];
-    rb.q[1] = dw[2];
+    rb.hdr = w.dw[0] & mask;
+    rb.q[0] = w.dw[1] & mask;
+    rb.q[1] = w.dw[2] & mask;
   } else {
-    const bool sh = (a & 2) != 0;  // block starts at byte 2 of dw[0]
-    rb.hdr = sh ? (dw[0] >> 16) : (dw[0] & 0xffffu);
+    const bool sh = w.sh != 0;
+    rb.hdr = (sh ? (w.dw[0] >> 16) : (w.dw[0] & 0xffffu)) & mask;
 #pragma unroll
     for (int i = 0; i < RawBlock<QT>::NQ; ++i)
-      rb.q[i] = sh ? dw[i + 1] : __builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2);
+      rb.q[i] = (sh ? w.dw[i + 1] : __builtin_amdgcn_alignbyte(w.dw[i + 1], w.dw[i], 2)) & mask;
   }
+}
+
+template <int QT>
+__device__ __forceinline__ void load_block(const uint8_t* blk, RawBlock<QT>& rb) {
+  BlockWindow<QT> w;
+  load_window<QT>(blk, w);
+  realign<QT>(w, 0xffffffffu, rb);
 }
 
 // Decode to 32 floats in element order (exact value rounded once to fp32).

@@ -41,12 +41,16 @@ constexpr int BK = GEMM_BK;  // 64 = two quant blocks along k
 constexpr int LDK = BK + 8;  // padded LDS row (bf16): 144 B keeps ds_read_b128 conflict-free
 constexpr int NTHR = 256;
 
-template <int BM, int BN, bool STAGE>
+template <int BM, int BN, bool STAGE, bool NN>
 struct Geom {
   static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int A_CHUNKS = BM * BK / 8 / NTHR;  // 16-byte chunks per thread
-  static constexpr int SMEM_MAIN = 2 * (BM + BN) * LDK * 2;
+  // weight tile in LDS (bf16 elements): NT [BN][LDK] (k contiguous);
+  // NN [64][PN] row-major (columns contiguous), read with transposing loads
+  static constexpr int PN = BN + 16;
+  static constexpr int B_TILE = NN ? BK * PN : BN * LDK;
+  static constexpr int SMEM_MAIN = 2 * (BM * LDK + B_TILE) * 2;
   static constexpr int ZP = BN + 1;  // pitch (floats) of the staged epilogue tile
   static constexpr int SMEM_Z = STAGE ? BM * ZP * 4 : 0;
   static constexpr int SMEM = SMEM_MAIN > SMEM_Z ? SMEM_MAIN : SMEM_Z;
@@ -58,6 +62,15 @@ constexpr bool epi_stages(int epi) {
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// all-ones / all-zeros mask the optimiser cannot see through (an empty
+// register-only asm), so a load whose result is masked is never turned back
+// into a branch around the load
+__device__ __forceinline__ uint32_t opaque_mask(bool keep) {
+  uint32_t m = keep ? 0xffffffffu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
 
 // Row reduction of the staged tile Z [BM][ZP]:
 //   out[j] = sum_{c : n0 + c < ncols} Z[row][c] * (W ? W[(n0 + c) * r + j] : 1),  j < nv
@@ -206,8 +219,8 @@ __device__ __forceinline__ void down_pair_reduce(uint32_t* Zu, const float* Bg, 
 
 template <int QT, int EPI, int BM, int BN>
 __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(const GemmArgs p) {
-  using G = Geom<BM, BN, epi_stages(EPI)>;
   constexpr bool NN = EPI >= EPI_LIN_BWD;
+  using G = Geom<BM, BN, epi_stages(EPI), NN>;
   constexpr int BS = QTraits<QT>::BS;
   constexpr int TM = G::TM, TN = G::TN, WTM = G::WTM, WTN = G::WTN, ZP = G::ZP;
   static_assert(BN == 128 || BN == 256, "weight items: 2*BN blocks per k-step");
@@ -216,6 +229,7 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Bs = As + 2 * BM * LDK;
+  constexpr int B_TILE = G::B_TILE, PN = G::PN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,41 +279,49 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
     aoff[i] = aval[i] ? src * p.lda + (c & 7) * 8 : 0;
   }
   uint4 areg0[G::A_CHUNKS], areg1[G::A_CHUNKS];
-  auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS]) {
+  uint32_t amsk0[G::A_CHUNKS], amsk1[G::A_CHUNKS];
+  auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS], uint32_t (&amsk)[G::A_CHUNKS]) {
     int k0 = kt * BK;
     const uint16_t* base = p.a0;
     if (k0 >= p.asplit) { base = p.a1; k0 -= p.asplit; }
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
+      // unconditional load from a clamped address, zeroed by select, so the
+      // steady-state loop stays one basic block
       const int kc = kt * BK + ((tid + NTHR * i) & 7) * 8;
-      if (aval[i] && kc < p.K)
-        areg[i] = *reinterpret_cast<const uint4*>(base + aoff[i] + k0);
-      else
-        areg[i] = make_uint4(0, 0, 0, 0);
+      const bool ok = aval[i] && kc < p.K;
+      // the mask is applied at the LDS store, so waiting for this load is
+      // deferred to the store that consumes it
+      areg[i] = *reinterpret_cast<const uint4*>(ok ? base + aoff[i] + k0 : p.a0);
+      amsk[i] = opaque_mask(ok);
     }
   };
-  auto store_a = [&](int buf, const uint4 (&areg)[G::A_CHUNKS]) {
+  auto store_a = [&](int buf, const uint4 (&areg)[G::A_CHUNKS], const uint32_t (&amsk)[G::A_CHUNKS]) {
     uint16_t* A = As + buf * BM * LDK;
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
       const int c = tid + NTHR * i;
-      *reinterpret_cast<uint4*>(A + (c >> 3) * LDK + (c & 7) * 8) = areg[i];
+      const uint32_t m = amsk[i];
+      *reinterpret_cast<uint4*>(A + (c >> 3) * LDK + (c & 7) * 8) =
+          make_uint4(areg[i].x & m, areg[i].y & m, areg[i].z & m, areg[i].w & m);
     }
   };
 
   // ---- weight operand: WPT = 2*BN/256 blocks per thread per k-step.
-  // Item it = tid + 256*i:
+  // Item it = tid + 256*i; consecutive lanes read consecutive blocks of a row:
   // NT: (row = it >> 1, kb = it & 1): block 2kt + kb of weight row `row`
-  // NN: (kb = it >> 6, row = it & 63): block n0/32 + kb of reduction row kt*64 + row
+  // NN: (row = it / NB, kb = it % NB), NB = BN/32 blocks per row: block
+  //     n0/32 + kb of reduction row kt*64 + row
   constexpr int WPT = 2 * BN / NTHR;
+  constexpr int NB = BN / 32;
   int w_it_row[WPT], w_it_kb[WPT];
   const uint8_t* wptr[WPT];  // NT: row base + kb*BS
   bool wrow_ok[WPT];
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     const int it = tid + NTHR * i;
-    w_it_row[i] = NN ? (it & 63) : (it >> 1);
-    w_it_kb[i] = NN ? (it >> 6) : (it & 1);
+    w_it_row[i] = NN ? (it / NB) : (it >> 1);
+    w_it_kb[i] = NN ? (it % NB) : (it & 1);
     wptr[i] = nullptr;
     if constexpr (!NN) {
       const uint8_t* src = p.w0;
@@ -318,38 +340,42 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
       wrow_ok[i] = ((n0 >> 5) + w_it_kb[i]) < p.w_nb;
     }
   }
-  RawBlock<QT> wr0[WPT], wr1[WPT];
-  auto load_w = [&](int kt, RawBlock<QT> (&wr)[WPT]) {
+  BlockWindow<QT> wr0[WPT], wr1[WPT];
+  uint32_t wmsk0[WPT], wmsk1[WPT];
+  auto load_w = [&](int kt, BlockWindow<QT> (&wr)[WPT], uint32_t (&wmsk)[WPT]) {
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const uint8_t* blk = nullptr;
       if constexpr (!NN) {
         if (wrow_ok[i]) blk = wptr[i] + (int64_t)kt * 2 * BS;
       } else {
+        // address arithmetic without a branch (a conditional block here
+        // splits the pipelined loop); invalid items read block 0 of w0
         const int rg = kt * BK + w_it_row[i];
-        if (wrow_ok[i] && rg < p.K) {
-          const bool second = rg >= p.wsplit;
-          const uint8_t* src = second ? p.w1 : p.w0;
-          const int rr = second ? rg - p.wsplit : rg;
-          blk = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + rr) * p.w_rowbytes +
-                (int64_t)((n0 >> 5) + w_it_kb[i]) * BS;
-        }
+        const bool ok = wrow_ok[i] && rg < p.K;
+        const int rv = ok ? rg : 0;
+        const bool second = rv >= p.wsplit;
+        const uint8_t* src = second ? p.w1 : p.w0;
+        const int rr = second ? rv - p.wsplit : rv;
+        const uint8_t* a = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + rr) * p.w_rowbytes +
+                           (int64_t)((n0 >> 5) + w_it_kb[i]) * BS;
+        blk = ok ? a : nullptr;
       }
-      if (blk) {
-        load_block<QT>(blk, wr[i]);
-      } else {
-        wr[i].hdr = 0;
-#pragma unroll
-        for (int q = 0; q < RawBlock<QT>::NQ; ++q) wr[i].q[q] = 0;
-      }
+      // unconditional load (the first block of w0 when out of range; rows
+      // hold at least two blocks, so the dword window stays in bounds),
+      // zeroed by select
+      load_window<QT>(blk ? blk : p.w0, wr[i]);
+      wmsk[i] = opaque_mask(blk != nullptr);
     }
   };
-  auto store_w = [&](int buf, const RawBlock<QT> (&wr)[WPT]) {
-    uint16_t* B = Bs + buf * BN * LDK;
+  auto store_w = [&](int buf, const BlockWindow<QT> (&wraw)[WPT], const uint32_t (&wmsk)[WPT]) {
+    uint16_t* B = Bs + buf * B_TILE;
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
+      RawBlock<QT> wr;
+      realign<QT>(wraw[i], wmsk[i], wr);
       float w[32];
-      decode_block_fast<QT>(wr[i], w);
+      decode_block_fast<QT>(wr, w);
       if constexpr (!NN) {
         uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * LDK + w_it_kb[i] * 32);
 #pragma unroll
@@ -357,9 +383,12 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
           dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
                               pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
       } else {
-        uint16_t* dst = B + (w_it_kb[i] * 32) * LDK + w_it_row[i];
+        // row-major store: reduction row w_it_row, columns kb*32 .. +32
+        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * PN + w_it_kb[i] * 32);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) dst[q * LDK] = f2bf(w[q]);
+        for (int q = 0; q < 4; ++q)
+          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
+                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
       }
     }
   };
@@ -377,9 +406,17 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
   // Software pipeline, prefetch depth 2: tile kt+2 is loaded into the
   // register set that tile kt was stored from, while the MFMAs of tile kt run
   // and tile kt+1 (loaded one step earlier) waits in the other set.
+  // NN operand B from the row-major tile with ds_read_b64_tr_b16: within
+  // each 16-lane group g, output lane 16g + j slot t receives element j % 4
+  // of the 4-element chunk addressed by lane 16g + 4t + j / 4.  Lane
+  // 16g + 4t + q therefore addresses reduction row 8*(g/2) + t (+4 for the
+  // second half) at column 16*(g%2) + 4q of its 32-column subtile, and lane
+  // L ends up with rows 8*(L/32) .. +8 of column L % 32 -- the MFMA B layout.
+  const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   auto compute = [&](int cur) {
     const uint16_t* A = As + cur * BM * LDK;
-    const uint16_t* B = Bs + cur * BN * LDK;
+    const uint16_t* B = Bs + cur * B_TILE;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[TM], bfr[TN];
@@ -388,9 +425,23 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
         af[a] = *reinterpret_cast<const bf16x8*>(A + (wm * WTM + a * 32 + (lane & 31)) * LDK +
                                                  kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-      for (int b = 0; b < TN; ++b)
-        bfr[b] = *reinterpret_cast<const bf16x8*>(B + (wn * WTN + b * 32 + (lane & 31)) * LDK +
-                                                  kk * 16 + (lane >> 5) * 8);
+      for (int b = 0; b < TN; ++b) {
+        if constexpr (NN) {
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+          const uint16_t* base = B + (kk * 16 + tr_row) * PN + wn * WTN + b * 32 + tr_col;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(__attribute__((address_space(3))) void*)(base));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(__attribute__((address_space(3))) void*)(base + 4 * PN));
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          bfr[b] = __builtin_bit_cast(bf16x8, both);
+        } else {
+          bfr[b] = *reinterpret_cast<const bf16x8*>(B + (wn * WTN + b * 32 + (lane & 31)) * LDK +
+                                                    kk * 16 + (lane >> 5) * 8);
+        }
+      }
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -400,62 +451,75 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
   };
   constexpr bool DEEP = BM * BN < 256 * 256;  // small tiles: prefetch depth 2
   if constexpr (DEEP) {
-    load_a(0, areg0);
-    load_w(0, wr0);
+    load_a(0, areg0, amsk0);
+    load_w(0, wr0, wmsk0);
     if (nk > 1) {
-      load_a(1, areg1);
-      load_w(1, wr1);
+      load_a(1, areg1, amsk1);
+      load_w(1, wr1, wmsk1);
     }
-    store_a(0, areg0);
-    store_w(0, wr0);
+    store_a(0, areg0, amsk0);
+    store_w(0, wr0, wmsk0);
     __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      // even step: compute buffer 0, refill set 0 with tile kt+2, store set 1 (tile kt+1)
+    int kt = 0;
+    // steady state without branches, so the decode of the next tile can be
+    // scheduled among the MFMAs of the current one
+    // (the scheduling fence keeps the loads ahead of the decode of the
+    // other set, which would otherwise wait for them)
+    for (; kt + 3 < nk; kt += 2) {
+      load_a(kt + 2, areg0, amsk0);
+      load_w(kt + 2, wr0, wmsk0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0);
+      store_a(1, areg1, amsk1);
+      store_w(1, wr1, wmsk1);
+      __syncthreads();
+      load_a(kt + 3, areg1, amsk1);
+      load_w(kt + 3, wr1, wmsk1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1);
+      store_a(0, areg0, amsk0);
+      store_w(0, wr0, wmsk0);
+      __syncthreads();
+    }
+    // tail: tiles kt .. nk-1 (at most three)
+    for (; kt < nk; kt += 2) {
       if (kt + 2 < nk) {
-        load_a(kt + 2, areg0);
-        load_w(kt + 2, wr0);
+        load_a(kt + 2, areg0, amsk0);
+        load_w(kt + 2, wr0, wmsk0);
       }
       compute(0);
       if (kt + 1 < nk) {
-        store_a(1, areg1);
-        store_w(1, wr1);
+        store_a(1, areg1, amsk1);
+        store_w(1, wr1, wmsk1);
       }
       __syncthreads();
       if (kt + 1 >= nk) break;
-      // odd step: compute buffer 1, refill set 1 with tile kt+3, store set 0 (tile kt+2)
-      if (kt + 3 < nk) {
-        load_a(kt + 3, areg1);
-        load_w(kt + 3, wr1);
-      }
       compute(1);
       if (kt + 2 < nk) {
-        store_a(0, areg0);
-        store_w(0, wr0);
+        store_a(0, areg0, amsk0);
+        store_w(0, wr0, wmsk0);
       }
       __syncthreads();
     }
   } else {
     // large tiles: one k-step of MFMAs (~2k cycles per wave) covers the
     // latency of the next tile's loads; one register set
-    load_a(0, areg0);
-    load_w(0, wr0);
-    store_a(0, areg0);
-    store_w(0, wr0);
+    load_a(0, areg0, amsk0);
+    load_w(0, wr0, wmsk0);
+    store_a(0, areg0, amsk0);
+    store_w(0, wr0, wmsk0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
+    int kt = 0;
+    for (; kt + 1 < nk; ++kt) {
       const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_a(kt + 1, areg0);
-        load_w(kt + 1, wr0);
-      }
+      load_a(kt + 1, areg0, amsk0);
+      load_w(kt + 1, wr0, wmsk0);
       compute(cur);
-      if (more) {
-        store_a(cur ^ 1, areg0);
-        store_w(cur ^ 1, wr0);
-      }
+      store_a(cur ^ 1, areg0, amsk0);
+      store_w(cur ^ 1, wr0, wmsk0);
       __syncthreads();
     }
+    compute(kt & 1);
   }
 
   // ---- rank-r adapter term, folded into the accumulators on the MFMA:

@@ -151,8 +151,8 @@ struct ColRedArgs {
   float* part;              // [slots][C][r]
 };
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st);
-// columns per thread of launch_colred (the grid covers 256 * this per block)
-int colred_cols_per_thread(int r);
+// columns covered by one launch_colred workgroup
+int colred_cols_per_block(int r);
 
 // out = s * sum over an expert's slots (in order) of part; experts with no
 // rows get zeros.  transpose: out[e][j][c] instead of out[e][c][j].

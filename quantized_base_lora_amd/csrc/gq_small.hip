@@ -89,17 +89,18 @@ __device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_
 
 // ------------------------------------------------------------- row dots
 // out[o][p][j] = sum_c act(p)[c] * W_o(e_p)[j][c], j < r <= R.
-// One wave owns RB consecutive rows; lanes split the columns 8 at a time
-// (16-byte activation loads), so each loaded chunk of W serves RB rows.
+// A block owns RB consecutive rows; its four waves split the columns
+// (16-byte activation loads, 8 columns per lane, 2048 columns per pass), so
+// each loaded chunk of W serves RB rows.  Lane partials are reduced with a
+// fixed shuffle tree, the four waves' sums are added in wave order through
+// LDS (deterministic).
 // WT: W stored [C][r] (a LoRA B matrix) instead of [r][C] (an A matrix).
-// The per-lane partials are reduced across the wave with a fixed shuffle
-// tree (deterministic).
 template <int R, int NOUT, bool WT>
 __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
-  constexpr int RB = R <= 4 ? 4 : (R <= 8 ? 2 : 1);
-  const int lane = threadIdx.x & 63;
-  const int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RB;
-  if (p0 >= a.M) return;
+  constexpr int RB = R <= 4 ? 8 : (R <= 8 ? 4 : 2);
+  __shared__ float red[4][NOUT][RB][R];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t p0 = (int64_t)blockIdx.x * RB;
   const int r = a.r;
   int eq[RB];
   const uint16_t* xq[RB];
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
     for (int q = 0; q < RB; ++q)
 #pragma unroll
       for (int j = 0; j < R; ++j) acc[o][q][j] = 0.f;
-  for (int c = lane * 8; c < a.C; c += 512) {
+  for (int c = wave * 512 + lane * 8; c < a.C; c += 2048) {
     float xv[RB][8];
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
@@ -143,11 +144,22 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
           ecur = eq[q];
           const float* W = a.W[o] + (int64_t)ecur * a.w_estride;
           if constexpr (WT) {
-            // [C][r]: the 8 columns' rank vectors are contiguous
+            // [C][r]: the 8 columns' rank vectors are 8*r contiguous floats
+            const float* base = W + (int64_t)c * r;
+            if (r == R) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+              for (int u = 0; u < 2 * R; ++u) {
+                const float4 f = reinterpret_cast<const float4*>(base)[u];
+                const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-              for (int j = 0; j < R; ++j) w[j][t] = j < r ? W[(int64_t)(c + t) * r + j] : 0.f;
+                for (int h = 0; h < 4; ++h) w[(4 * u + h) % R][(4 * u + h) / R] = fv[h];
+              }
+            } else {
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int j = 0; j < R; ++j) w[j][t] = j < r ? base[t * r + j] : 0.f;
+            }
           } else {
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -178,34 +190,35 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
 #pragma unroll
     for (int q = 0; q < RB; ++q)
 #pragma unroll
-      for (int j = 0; j < R; ++j)
-        if (j < r) acc[o][q][j] = warp_sum(acc[o][q][j]);
-  if (lane == 0) {
-#pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      if (!vq[q]) continue;
-      const int64_t p = p0 + q;
-      const float wp = a.out2 ? a.wflat[a.sorted[p]] : 0.f;
-#pragma unroll
-      for (int o = 0; o < NOUT; ++o)
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (j < r) {
-            a.out[o][p * r + j] = acc[o][q][j];
-            if (o == 0 && a.out2) a.out2[p * r + j] = wp * acc[o][q][j];
-          }
+      for (int j = 0; j < R; ++j) {
+        const float v = warp_sum(acc[o][q][j]);
+        if (lane == 0) red[wave][o][q][j] = v;
+      }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NOUT * RB * R) {
+    const int o = t / (RB * R), q = (t / R) % RB, j = t % R;
+    const int64_t p = p0 + q;
+    if (p < a.M && j < r) {
+      const float v = red[0][o][q][j] + red[1][o][q][j] + red[2][o][q][j] + red[3][o][q][j];
+      a.out[o][p * r + j] = v;
+      if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v;
     }
   }
 }
 
 // ---------------------------------------------------- column reductions
-// part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j].  Each thread
-// owns CPT adjacent columns (one 16- or 8-byte load per row); the row index,
-// gather and V[p] are uniform across the block (scalar loads).
+// part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j].  A block owns
+// one slot and 64*CPT columns: every lane owns CPT adjacent columns (one 16-
+// or 8-byte load per row, a wave reads a contiguous row segment), the four
+// waves take every fourth row, and the wave partials are added in wave
+// order through LDS.
 template <int R, int CPT>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
+  __shared__ float red[3][64][CPT][R];
   const int slot = blockIdx.x;
-  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * CPT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = ((int64_t)blockIdx.y * 64 + lane) * CPT;
   int64_t r0, r1;
   if (a.offsets) {
     const int32_t* cs = a.chunk_start;
@@ -217,48 +230,60 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     r0 = (int64_t)slot * a.rc;
     r1 = min(a.M, r0 + a.rc);
   }
-  if (c >= a.C) return;
+  const bool cok = c < a.C;
   const int r = a.r;
   float acc[CPT][R];
 #pragma unroll
   for (int t = 0; t < CPT; ++t)
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
+  if (cok) {
 #pragma unroll 4
-  for (int64_t p = r0; p < r1; ++p) {
-    const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
-    const uint16_t* u = a.U + src * a.ldu + c;
-    float uv[CPT];
-    if constexpr (CPT == 8) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(u);
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int64_t p = r0 + wave; p < r1; p += 4) {
+      const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
+      const uint16_t* u = a.U + src * a.ldu + c;
+      float uv[CPT];
+      if constexpr (CPT == 8) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(u);
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
-        uv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
+        for (int t = 0; t < 4; ++t) {
+          uv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
+          uv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
+        }
+      } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(u);
+        uv[0] = bf2f((uint16_t)(raw.x & 0xffffu));
+        uv[1] = bf2f((uint16_t)(raw.x >> 16));
+        uv[2] = bf2f((uint16_t)(raw.y & 0xffffu));
+        uv[3] = bf2f((uint16_t)(raw.y >> 16));
       }
-    } else {
-      const uint2 raw = *reinterpret_cast<const uint2*>(u);
-      uv[0] = bf2f((uint16_t)(raw.x & 0xffffu));
-      uv[1] = bf2f((uint16_t)(raw.x >> 16));
-      uv[2] = bf2f((uint16_t)(raw.y & 0xffffu));
-      uv[3] = bf2f((uint16_t)(raw.y >> 16));
-    }
-    const float* v = a.Vv + p * r;
-    float vv[R];
+      const float* v = a.Vv + p * r;
+      float vv[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) vv[j] = j < r ? v[j] : 0.f;
+      for (int j = 0; j < R; ++j) vv[j] = j < r ? v[j] : 0.f;
+#pragma unroll
+      for (int t = 0; t < CPT; ++t)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[j];
+    }
+  }
+  if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < CPT; ++t)
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[j];
+      for (int j = 0; j < R; ++j) red[wave - 1][lane][t][j] = acc[t][j];
   }
-  float* dst = a.part + ((int64_t)slot * a.C + c) * r;
+  __syncthreads();
+  if (wave == 0 && cok) {
+    float* dst = a.part + ((int64_t)slot * a.C + c) * r;
 #pragma unroll
-  for (int t = 0; t < CPT; ++t)
+    for (int t = 0; t < CPT; ++t)
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < r) dst[t * r + j] = acc[t][j];
+      for (int j = 0; j < R; ++j)
+        if (j < r)
+          dst[t * r + j] = acc[t][j] + red[0][lane][t][j] + red[1][lane][t][j] + red[2][lane][t][j];
+  }
 }
 
 // out[e] = s * sum_{slots of e} part[slot]; thread per (c, j) of one expert
@@ -611,8 +636,8 @@ hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int3
 
 template <int R>
 hipError_t rowdot_r(const RowDotArgs& a, hipStream_t st) {
-  constexpr int RB = R <= 4 ? 4 : (R <= 8 ? 2 : 1);
-  const dim3 g(blocks_for(a.M, 4 * RB)), b(256);
+  constexpr int RB = R <= 4 ? 8 : (R <= 8 ? 4 : 2);
+  const dim3 g(blocks_for(a.M, RB)), b(256);
   const bool wt = a.w_jstride == 1;
   if (a.nout == 2) {
     if (wt) hipLaunchKernelGGL((rowdot_kernel<R, 2, true>), g, b, 0, st, a);
@@ -631,12 +656,11 @@ hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   return rowdot_r<16>(a, st);
 }
 
-int colred_cols_per_thread(int r) { return r <= 8 ? 8 : 4; }
+int colred_cols_per_block(int r) { return r <= 8 ? 512 : 256; }
 
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   if (a.slots == 0) return hipSuccess;
-  const int cpt = colred_cols_per_thread(a.r);
-  const dim3 g((unsigned)a.slots, blocks_for(a.C, 256 * cpt)), b(256);
+  const dim3 g((unsigned)a.slots, blocks_for(a.C, colred_cols_per_block(a.r))), b(256);
   if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8>), g, b, 0, st, a);
   else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8>), g, b, 0, st, a);
   else hipLaunchKernelGGL((colred_kernel<16, 4>), g, b, 0, st, a);
