@@ -99,9 +99,16 @@ int64_t rowbytes(const gq_lora_linear* L) { return (L->n_in / 32) * block_bytes(
 int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // tile configuration: 128-row tiles unless that leaves the chip underfilled
-int pick_tile(int64_t rows_est, int64_t ntiles) {
+// 128x128 tiles decode each weight tile for twice the rows of 64x128 ones
+// and run faster per flop even at one workgroup per CU; halve the rows only
+// when 128-row tiles would leave most of the 256 CUs idle.
+// A launch of at most one 128x128 tile per CU with a long reduction runs each
+// tile on eight waves (two k-groups), which keeps two waves per SIMD busy;
+// `k2ok` marks the epilogues that allow it.
+int pick_tile(int64_t rows_est, int64_t ntiles, int64_t K = 0, bool k2ok = false) {
   const int64_t t128 = (int64_t)cdiv(rows_est, 128) * ntiles;
-  return t128 < 512 ? TILE_64x128 : TILE_128x128;
+  if (k2ok && t128 <= 256 && K >= 1024) return TILE_128x128_K2;
+  return t128 < 192 ? TILE_64x128 : TILE_128x128;
 }
 
 GemmArgs gemm_defaults() {
@@ -121,7 +128,7 @@ int pick_rc(int64_t M, int64_t C, int r, int E) {
   const int64_t cb = cdiv(C, colred_cols_per_block(r));
   const int extra = E > 1 ? E : 0;
   int rc = 32;
-  while (rc < 1024 && (cdiv(M, rc * 2) + extra) * cb >= 512) rc *= 2;
+  while (rc < 1024 && (cdiv(M, rc * 2) + extra) * cb >= 256) rc *= 2;
   return rc;
 }
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
@@ -190,7 +197,7 @@ int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, ui
   g.w0 = static_cast<const uint8_t*>(L->w_blocks);
   g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
   g.ntiles = cdiv(N, TILE_BN);
-  const int tc = pick_tile(T, g.ntiles);
+  const int tc = pick_tile(T, g.ntiles, K, true);
   g.mtiles = cdiv(T, tile_bm(tc));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
   g.o0 = y; g.ldo = N;
@@ -270,7 +277,7 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
     g.w0 = static_cast<const uint8_t*>(L->w_blocks);
     g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
     g.ntiles = cdiv(K, TILE_BN);
-    const int tc = pick_tile(T, g.ntiles);
+    const int tc = pick_tile(T, g.ntiles, N, true);
     g.mtiles = cdiv(T, tile_bm(tc));
     g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
     g.o0 = dx; g.ldo = K;
@@ -678,7 +685,7 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     p.part_dB = w.take<float>((int64_t)p.mt * V * r);
     p.GB = w.take<float>(T * r);
     p.part = w.take<float>(colred_slots(T, pick_rc(T, H, (int)r, 1), 1) * H * r);
-    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN));
+    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), C, true);
   }
   return p;
 }

@@ -41,7 +41,7 @@ constexpr int BK = GEMM_BK;  // 64 = two quant blocks along k
 constexpr int LDK = BK + 8;  // padded LDS row (bf16): 144 B keeps ds_read_b128 conflict-free
 constexpr int NTHR = 256;
 
-template <int BM, int BN, bool STAGE, bool NN>
+template <int BM, int BN, bool STAGE, bool NN, int KS>
 struct Geom {
   static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -53,7 +53,12 @@ struct Geom {
   static constexpr int SMEM_MAIN = 2 * (BM * LDK + B_TILE) * 2;
   static constexpr int ZP = BN + 1;  // pitch (floats) of the staged epilogue tile
   static constexpr int SMEM_Z = STAGE ? BM * ZP * 4 : 0;
-  static constexpr int SMEM = SMEM_MAIN > SMEM_Z ? SMEM_MAIN : SMEM_Z;
+  // KS groups of four waves, each with its own double-buffered stages; the
+  // cross-group reduction of the accumulators reuses the same memory
+  static constexpr int SMEM_K = KS * SMEM_MAIN;
+  static constexpr int SMEM_RED = KS > 1 ? BM * BN * 4 : 0;
+  static constexpr int SMEM_KR = SMEM_K > SMEM_RED ? SMEM_K : SMEM_RED;
+  static constexpr int SMEM = SMEM_KR > SMEM_Z ? SMEM_KR : SMEM_Z;
 };
 
 // epilogues that stage the output tile through LDS
@@ -217,21 +222,26 @@ __device__ __forceinline__ void down_pair_reduce(uint32_t* Zu, const float* Bg, 
   __syncthreads();
 }
 
-template <int QT, int EPI, int BM, int BN>
-__global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(const GemmArgs p) {
+template <int QT, int EPI, int BM, int BN, int KS>
+__global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
+    const GemmArgs p) {
   constexpr bool NN = EPI >= EPI_LIN_BWD;
-  using G = Geom<BM, BN, epi_stages(EPI), NN>;
+  using G = Geom<BM, BN, epi_stages(EPI), NN, KS>;
   constexpr int BS = QTraits<QT>::BS;
   constexpr int TM = G::TM, TN = G::TN, WTM = G::WTM, WTN = G::WTN, ZP = G::ZP;
   static_assert(BN == 128 || BN == 256, "weight items: 2*BN blocks per k-step");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate/up n-subtiles");
+  static_assert(KS == 1 || (KS == 2 && !epi_stages(EPI)),
+                "split-K groups: the reduction leaves one group for a barrier-free epilogue");
 
+  // group `grp` of four waves takes k-steps grp, grp + KS, grp + 2KS, ...
+  const int grp = KS > 1 ? (int)(threadIdx.x / NTHR) : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem + grp * G::SMEM_MAIN);
   uint16_t* Bs = As + 2 * BM * LDK;
   constexpr int B_TILE = G::B_TILE, PN = G::PN;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x % NTHR;  // thread within the group
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -264,6 +274,9 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
     r1 = min(p.M, r0 + BM);
   }
   const int n0 = ntile * BN;
+  const int nk = (p.K + BK - 1) / BK;  // k-steps of the whole reduction
+  const int nkl = (nk + KS - 1) / KS;   // k-steps of each group
+  auto KT = [&](int ls) { return ls * KS + grp; };
   auto LCb = [&](int b) { return wn * WTN + b * 32 + (lane & 31); };
 
   // ---- activation operand: fixed rows per thread
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
     for (int i = 0; i < WPT; ++i) {
       const uint8_t* blk = nullptr;
       if constexpr (!NN) {
-        if (wrow_ok[i]) blk = wptr[i] + (int64_t)kt * 2 * BS;
+        if (wrow_ok[i] && kt < nk) blk = wptr[i] + (int64_t)kt * 2 * BS;
       } else {
         // address arithmetic without a branch (a conditional block here
         // splits the pipelined loop); invalid items read block 0 of w0
@@ -402,7 +415,6 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  const int nk = (p.K + BK - 1) / BK;
   // Software pipeline, prefetch depth 2: tile kt+2 is loaded into the
   // register set that tile kt was stored from, while the MFMAs of tile kt run
   // and tile kt+1 (loaded one step earlier) waits in the other set.
@@ -451,11 +463,11 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
   };
   constexpr bool DEEP = BM * BN < 256 * 256;  // small tiles: prefetch depth 2
   if constexpr (DEEP) {
-    load_a(0, areg0, amsk0);
-    load_w(0, wr0, wmsk0);
-    if (nk > 1) {
-      load_a(1, areg1, amsk1);
-      load_w(1, wr1, wmsk1);
+    load_a(KT(0), areg0, amsk0);
+    load_w(KT(0), wr0, wmsk0);
+    if (nkl > 1) {
+      load_a(KT(1), areg1, amsk1);
+      load_w(KT(1), wr1, wmsk1);
     }
     store_a(0, areg0, amsk0);
     store_w(0, wr0, wmsk0);
@@ -465,37 +477,37 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
     // scheduled among the MFMAs of the current one
     // (the scheduling fence keeps the loads ahead of the decode of the
     // other set, which would otherwise wait for them)
-    for (; kt + 3 < nk; kt += 2) {
-      load_a(kt + 2, areg0, amsk0);
-      load_w(kt + 2, wr0, wmsk0);
+    for (; kt + 3 < nkl; kt += 2) {
+      load_a(KT(kt + 2), areg0, amsk0);
+      load_w(KT(kt + 2), wr0, wmsk0);
       __builtin_amdgcn_sched_barrier(0);
       compute(0);
       store_a(1, areg1, amsk1);
       store_w(1, wr1, wmsk1);
       __syncthreads();
-      load_a(kt + 3, areg1, amsk1);
-      load_w(kt + 3, wr1, wmsk1);
+      load_a(KT(kt + 3), areg1, amsk1);
+      load_w(KT(kt + 3), wr1, wmsk1);
       __builtin_amdgcn_sched_barrier(0);
       compute(1);
       store_a(0, areg0, amsk0);
       store_w(0, wr0, wmsk0);
       __syncthreads();
     }
-    // tail: tiles kt .. nk-1 (at most three)
-    for (; kt < nk; kt += 2) {
-      if (kt + 2 < nk) {
-        load_a(kt + 2, areg0, amsk0);
-        load_w(kt + 2, wr0, wmsk0);
+    // tail: tiles kt .. nkl-1 (at most three)
+    for (; kt < nkl; kt += 2) {
+      if (kt + 2 < nkl) {
+        load_a(KT(kt + 2), areg0, amsk0);
+        load_w(KT(kt + 2), wr0, wmsk0);
       }
       compute(0);
-      if (kt + 1 < nk) {
+      if (kt + 1 < nkl) {
         store_a(1, areg1, amsk1);
         store_w(1, wr1, wmsk1);
       }
       __syncthreads();
-      if (kt + 1 >= nk) break;
+      if (kt + 1 >= nkl) break;
       compute(1);
-      if (kt + 2 < nk) {
+      if (kt + 2 < nkl) {
         store_a(0, areg0, amsk0);
         store_w(0, wr0, wmsk0);
       }
@@ -504,22 +516,56 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
   } else {
     // large tiles: one k-step of MFMAs (~2k cycles per wave) covers the
     // latency of the next tile's loads; one register set
-    load_a(0, areg0, amsk0);
-    load_w(0, wr0, wmsk0);
+    load_a(KT(0), areg0, amsk0);
+    load_w(KT(0), wr0, wmsk0);
     store_a(0, areg0, amsk0);
     store_w(0, wr0, wmsk0);
     __syncthreads();
     int kt = 0;
-    for (; kt + 1 < nk; ++kt) {
+    for (; kt + 1 < nkl; ++kt) {
       const int cur = kt & 1;
-      load_a(kt + 1, areg0, amsk0);
-      load_w(kt + 1, wr0, wmsk0);
+      load_a(KT(kt + 1), areg0, amsk0);
+      load_w(KT(kt + 1), wr0, wmsk0);
       compute(cur);
       store_a(cur ^ 1, areg0, amsk0);
       store_w(cur ^ 1, wr0, wmsk0);
       __syncthreads();
     }
     compute(kt & 1);
+  }
+
+  if constexpr (KS > 1) {
+    // fold the second group's partial sums into the first group's
+    // accumulators (fixed order: deterministic), then retire the second
+    // group; everything below is barrier-free
+    __syncthreads();
+    float4* red = reinterpret_cast<float4*>(smem);
+    const int slot0 = wave * TM * TN;
+    if (grp == 1) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            red[((slot0 + a * TN + b) * 4 + v4) * 64 + lane] =
+                make_float4(acc[a][b][4 * v4], acc[a][b][4 * v4 + 1], acc[a][b][4 * v4 + 2],
+                            acc[a][b][4 * v4 + 3]);
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 q = red[((slot0 + a * TN + b) * 4 + v4) * 64 + lane];
+          acc[a][b][4 * v4] += q.x;
+          acc[a][b][4 * v4 + 1] += q.y;
+          acc[a][b][4 * v4 + 2] += q.z;
+          acc[a][b][4 * v4 + 3] += q.w;
+        }
   }
 
   // ---- rank-r adapter term, folded into the accumulators on the MFMA:
@@ -864,17 +910,17 @@ __global__ __launch_bounds__(NTHR, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ker
 
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(NTHR);
+  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
   if constexpr (!epi_stages(EPI)) {
-    if (tilecfg == TILE_256x256) {
-      hipLaunchKernelGGL((gemm_kernel<QT, EPI, 256, 256>), grid, block, 0, st, a);
+    if (tilecfg == TILE_128x128_K2) {
+      hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128, 2>), grid, dim3(2 * NTHR), 0, st, a);
       return hipGetLastError();
     }
   }
   if (tilecfg == TILE_128x128)
-    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128, 1>), grid, dim3(NTHR), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 64, 128>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 64, 128, 1>), grid, dim3(NTHR), 0, st, a);
   return hipGetLastError();
 }
 

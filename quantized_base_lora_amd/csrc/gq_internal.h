@@ -84,12 +84,13 @@ struct GemmArgs {
   const float* nvalid; // EPI_CE_BWD: device count of valid labels
 };
 
-enum TileCfg { TILE_128x128 = 0, TILE_64x128 = 1, TILE_256x256 = 2 };
+// TILE_128x128_K2: 128x128 tiles computed by 512 threads, two groups of four
+// waves taking alternate k-steps (split-K inside the workgroup), reduced in
+// LDS; only for the epilogues that do not stage through LDS.
+enum TileCfg { TILE_128x128 = 0, TILE_64x128 = 1, TILE_128x128_K2 = 2 };
 
-// tile rows (BM) and columns (BN) of a tile configuration.  TILE_256x256 is
-// available for the epilogues that do not stage through LDS.
-inline int tile_bm(int cfg) { return cfg == TILE_256x256 ? 256 : (cfg == TILE_128x128 ? 128 : 64); }
-inline int tile_bn(int cfg) { return cfg == TILE_256x256 ? 256 : 128; }
+inline int tile_bm(int cfg) { return cfg == TILE_64x128 ? 64 : 128; }
+inline int tile_bn(int) { return 128; }
 constexpr int TILE_BN = 128;
 constexpr int GEMM_BK = 64;
 

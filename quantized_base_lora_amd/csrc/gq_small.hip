@@ -88,121 +88,111 @@ __device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_
 }
 
 // ------------------------------------------------------------- row dots
-// out[o][p][j] = sum_c act(p)[c] * W_o(e_p)[j][c], j < r <= R.
-// A block owns RB consecutive rows; its four waves split the columns
-// (16-byte activation loads, 8 columns per lane, 2048 columns per pass), so
-// each loaded chunk of W serves RB rows.  Lane partials are reduced with a
-// fixed shuffle tree, the four waves' sums are added in wave order through
-// LDS (deterministic).
+// out[o][p][j] = sum_c act(p)[c] * W_o(e_p)[j][c], j < r <= 16, on the
+// 16x16x32 bf16 MFMA: rows p are the MFMA rows, ranks j its columns, the
+// activation columns c its reduction.  A block owns 16 consecutive rows and
+// its eight waves take every eighth 32-column step; the fp32 rank vectors
+// enter as bf16 hi + lo parts (about 16 significant bits).  Rows of a block
+// that belong to different experts (sorted grouped rows) are covered by one
+// pass per expert with the other rows masked.  The eight wave partials are
+// added in wave order through LDS (deterministic).
 // WT: W stored [C][r] (a LoRA B matrix) instead of [r][C] (an A matrix).
-template <int R, int NOUT, bool WT>
-__global__ __launch_bounds__(256) void rowdot_kernel(const RowDotArgs a) {
-  constexpr int RB = R <= 4 ? 8 : (R <= 8 ? 4 : 2);
-  __shared__ float red[4][NOUT][RB][R];
+constexpr int RD_WAVES = 8;
+
+template <int NOUT, bool WT>
+__global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs a) {
+  __shared__ f32x4 red[RD_WAVES - 1][NOUT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * RB;
+  const int64_t p0 = (int64_t)blockIdx.x * 16;
   const int r = a.r;
-  int eq[RB];
-  const uint16_t* xq[RB];
-  bool vq[RB];
-#pragma unroll
-  for (int q = 0; q < RB; ++q) {
-    const int64_t p = p0 + q;
-    vq[q] = p < a.M;
-    eq[q] = (vq[q] && a.offsets) ? find_expert(a.offsets, a.E, p) : 0;
-    const int64_t src = !vq[q] ? 0 : (a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p);
-    xq[q] = a.act + src * a.lda;
+  // the activation row this lane feeds into the MFMA (row lane % 16)
+  const int64_t pa = p0 + (lane & 15);
+  const bool pav = pa < a.M;
+  const int64_t src = !pav ? 0 : (a.gather ? (int64_t)(a.gather[pa] / a.gdiv) : pa);
+  const uint16_t* arow = a.act + src * a.lda + 8 * (lane >> 4);
+  int ea = 0, elo = 0, ehi = 0;
+  if (a.offsets) {
+    ea = pav ? find_expert(a.offsets, a.E, pa) : -1;
+    elo = find_expert(a.offsets, a.E, p0);
+    ehi = find_expert(a.offsets, a.E, (p0 + 16 < a.M ? p0 + 16 : a.M) - 1);
   }
-  float acc[NOUT][RB][R];
+  const int j = lane & 15;  // rank column this lane feeds (B operand)
+  const bool jok = j < r;
+  const int jc = jok ? j : 0;  // clamped: every load below stays in bounds
+  f32x4 acc[NOUT];
 #pragma unroll
-  for (int o = 0; o < NOUT; ++o)
+  for (int o = 0; o < NOUT; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int UNR = 4;  // 32-column steps whose loads are issued together
+  for (int e = elo; e <= ehi; ++e) {
+    const bool rowok = pav && ea == e;
+    const float* Wb[NOUT];
 #pragma unroll
-    for (int q = 0; q < RB; ++q)
+    for (int o = 0; o < NOUT; ++o) Wb[o] = a.W[o] + (int64_t)e * a.w_estride + (int64_t)jc * a.w_jstride;
+    for (int cb = wave * 32; cb < a.C; cb += 32 * RD_WAVES * UNR) {
+      uint4 raw[UNR];
+      float w8[UNR][NOUT][8];
+      bool aok[UNR], wok[UNR];
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[o][q][j] = 0.f;
-  for (int c = wave * 512 + lane * 8; c < a.C; c += 2048) {
-    float xv[RB][8];
+      for (int u = 0; u < UNR; ++u) {
+        const int c = cb + u * 32 * RD_WAVES + 8 * (lane >> 4);
+        const bool cok = c < a.C;  // C % 8 == 0: whole 8-column chunks
+        const int cc = cok ? c : 0;
+        aok[u] = rowok && cok;
+        wok[u] = jok && cok;
+        raw[u] = *reinterpret_cast<const uint4*>(aok[u] ? arow + (c - 8 * (lane >> 4)) : a.act);
 #pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (vq[q]) raw = *reinterpret_cast<const uint4*>(xq[q] + c);
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        xv[q][2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
-        xv[q][2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
-      }
-    }
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) {
-      float w[R][8];
-      int ecur = -1;
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        if (!vq[q]) continue;
-        if (eq[q] != ecur) {
-          ecur = eq[q];
-          const float* W = a.W[o] + (int64_t)ecur * a.w_estride;
+        for (int o = 0; o < NOUT; ++o) {
           if constexpr (WT) {
-            // [C][r]: the 8 columns' rank vectors are 8*r contiguous floats
-            const float* base = W + (int64_t)c * r;
-            if (r == R) {
 #pragma unroll
-              for (int u = 0; u < 2 * R; ++u) {
-                const float4 f = reinterpret_cast<const float4*>(base)[u];
-                const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) w[(4 * u + h) % R][(4 * u + h) / R] = fv[h];
-              }
-            } else {
-#pragma unroll
-              for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int j = 0; j < R; ++j) w[j][t] = j < r ? base[t * r + j] : 0.f;
-            }
+            for (int t = 0; t < 8; ++t) w8[u][o][t] = Wb[o][(int64_t)(cc + t) * a.w_cstride];
           } else {
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-              if (j < r) {
-                const float4 lo = *reinterpret_cast<const float4*>(W + (int64_t)j * a.C + c);
-                const float4 hi = *reinterpret_cast<const float4*>(W + (int64_t)j * a.C + c + 4);
-                w[j][0] = lo.x; w[j][1] = lo.y; w[j][2] = lo.z; w[j][3] = lo.w;
-                w[j][4] = hi.x; w[j][5] = hi.y; w[j][6] = hi.z; w[j][7] = hi.w;
-              } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) w[j][t] = 0.f;
-              }
-            }
+            const float4 lo = *reinterpret_cast<const float4*>(Wb[o] + cc);
+            const float4 hi = *reinterpret_cast<const float4*>(Wb[o] + cc + 4);
+            w8[u][o][0] = lo.x; w8[u][o][1] = lo.y; w8[u][o][2] = lo.z; w8[u][o][3] = lo.w;
+            w8[u][o][4] = hi.x; w8[u][o][5] = hi.y; w8[u][o][6] = hi.z; w8[u][o][7] = hi.w;
           }
         }
+      }
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          float t0 = 0.f;
+      for (int u = 0; u < UNR; ++u) {
+        const uint4 rv = aok[u] ? raw[u] : make_uint4(0u, 0u, 0u, 0u);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, rv);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) t0 += xv[q][t] * w[j][t];
-          acc[o][q][j] += t0;
+        for (int o = 0; o < NOUT; ++o) {
+          bf16x8 wh, wl;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float w = wok[u] ? w8[u][o][t] : 0.f;
+            const __bf16 h = (__bf16)w;
+            wh[t] = h;
+            wl[t] = (__bf16)(w - (float)h);
+          }
+          acc[o] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wh, acc[o], 0, 0, 0);
+          acc[o] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wl, acc[o], 0, 0, 0);
         }
       }
     }
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int o = 0; o < NOUT; ++o)
-#pragma unroll
-    for (int q = 0; q < RB; ++q)
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const float v = warp_sum(acc[o][q][j]);
-        if (lane == 0) red[wave][o][q][j] = v;
-      }
+    for (int o = 0; o < NOUT; ++o) red[wave - 1][o][lane] = acc[o];
+  }
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < NOUT * RB * R) {
-    const int o = t / (RB * R), q = (t / R) % RB, j = t % R;
-    const int64_t p = p0 + q;
-    if (p < a.M && j < r) {
-      const float v = red[0][o][q][j] + red[1][o][q][j] + red[2][o][q][j] + red[3][o][q][j];
-      a.out[o][p * r + j] = v;
-      if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v;
+  if (wave == 0 && jok) {
+    // D layout: lane holds rank column lane % 16 of rows 4*(lane/16) .. +4
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+      f32x4 v = acc[o];
+#pragma unroll
+      for (int w = 0; w < RD_WAVES - 1; ++w) v += red[w][o][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t p = p0 + 4 * (lane >> 4) + q;
+        if (p < a.M) {
+          a.out[o][p * r + j] = v[q];
+          if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v[q];
+        }
+      }
     }
   }
 }
@@ -217,7 +207,8 @@ template <int R, int CPT>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   __shared__ float red[3][64][CPT][R];
   const int slot = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = ((int64_t)blockIdx.y * 64 + lane) * CPT;
   int64_t r0, r1;
   if (a.offsets) {
@@ -231,41 +222,51 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     r1 = min(a.M, r0 + a.rc);
   }
   const bool cok = c < a.C;
+  const int64_t cc = cok ? c : 0;  // clamped: loads stay in bounds
   const int r = a.r;
   float acc[CPT][R];
 #pragma unroll
   for (int t = 0; t < CPT; ++t)
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
-  if (cok) {
-#pragma unroll 4
-    for (int64_t p = r0 + wave; p < r1; p += 4) {
-      const int64_t src = a.gather ? (int64_t)(a.gather[p] / a.gdiv) : p;
-      const uint16_t* u = a.U + src * a.ldu + c;
-      float uv[CPT];
+  // rows r0 + wave + 4i; UNR rows' loads are issued together
+  constexpr int UNR = 8;
+  for (int64_t pb = r0 + wave; pb < r1; pb += 4 * UNR) {
+    uint32_t rw[UNR][CPT / 2];
+    float vv[UNR][R];
+    bool ok[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t p = pb + 4 * u;
+      const bool pok = p < r1;  // wave-uniform
+      ok[u] = pok && cok;
+      const int64_t pc = pok ? p : r0;
+      const int64_t src = a.gather ? (int64_t)(a.gather[pc] / a.gdiv) : pc;
+      const uint16_t* up = a.U + src * a.ldu + cc;
       if constexpr (CPT == 8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(u);
-        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uv[2 * t] = bf2f((uint16_t)(rw[t] & 0xffffu));
-          uv[2 * t + 1] = bf2f((uint16_t)(rw[t] >> 16));
-        }
+        const uint4 raw = *reinterpret_cast<const uint4*>(up);
+        rw[u][0] = raw.x; rw[u][1] = raw.y; rw[u][2] = raw.z; rw[u][3] = raw.w;
       } else {
-        const uint2 raw = *reinterpret_cast<const uint2*>(u);
-        uv[0] = bf2f((uint16_t)(raw.x & 0xffffu));
-        uv[1] = bf2f((uint16_t)(raw.x >> 16));
-        uv[2] = bf2f((uint16_t)(raw.y & 0xffffu));
-        uv[3] = bf2f((uint16_t)(raw.y >> 16));
+        const uint2 raw = *reinterpret_cast<const uint2*>(up);
+        rw[u][0] = raw.x; rw[u][1] = raw.y;
       }
-      const float* v = a.Vv + p * r;
-      float vv[R];
+      const float* v = a.Vv + pc * r;
 #pragma unroll
-      for (int j = 0; j < R; ++j) vv[j] = j < r ? v[j] : 0.f;
+      for (int j = 0; j < R; ++j) vv[u][j] = (pok && j < r) ? v[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float uv[CPT];
+#pragma unroll
+      for (int t = 0; t < CPT / 2; ++t) {
+        const uint32_t w = ok[u] ? rw[u][t] : 0u;
+        uv[2 * t] = bf2f((uint16_t)(w & 0xffffu));
+        uv[2 * t + 1] = bf2f((uint16_t)(w >> 16));
+      }
 #pragma unroll
       for (int t = 0; t < CPT; ++t)
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[j];
+        for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[u][j];
     }
   }
   if (wave > 0) {
@@ -286,25 +287,40 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   }
 }
 
-// out[e] = s * sum_{slots of e} part[slot]; thread per (c, j) of one expert
-__global__ void colred_finish_kernel(const float* __restrict__ part,
-                                     const int32_t* __restrict__ cs, int32_t nslots_dense,
-                                     int32_t C, int32_t r, float s, int transpose,
-                                     float* __restrict__ out) {
+// out[e] = s * sum_{slots of e} part[slot].  A block covers 32 outputs (c, j)
+// of one expert with eight slot lanes each: lane g adds slots g, g+8, ... in
+// order, and the eight lane sums are added in lane order through LDS
+// (deterministic), so many slots are read with eight loads in flight.
+__global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restrict__ part,
+                                                            const int32_t* __restrict__ cs,
+                                                            int32_t nslots_dense, int32_t C,
+                                                            int32_t r, float s, int transpose,
+                                                            float* __restrict__ out) {
+  __shared__ float red[8][32];
   const int e = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int oi = threadIdx.x & 31, g = threadIdx.x >> 5;
   const int64_t n = (int64_t)C * r;
-  if (i >= n) return;
+  const int64_t i = (int64_t)blockIdx.x * 32 + oi;
   const int s0 = cs ? cs[e] : 0;
   const int s1 = cs ? cs[e + 1] : nslots_dense;
   float acc = 0.f;
-  for (int sl = s0; sl < s1; ++sl) acc += part[(int64_t)sl * n + i];
-  const int64_t c = i / r, j = i % r;
-  float* o = out + (int64_t)e * n;
-  if (transpose)
-    o[j * C + c] = s * acc;
-  else
-    o[i] = s * acc;
+  if (i < n) {
+#pragma unroll 4
+    for (int sl = s0 + g; sl < s1; sl += 8) acc += part[(int64_t)sl * n + i];
+  }
+  red[g][oi] = acc;
+  __syncthreads();
+  if (g == 0 && i < n) {
+    float t = red[0][oi];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) t += red[k][oi];
+    const int64_t c = i / r, jj = i % r;
+    float* o = out + (int64_t)e * n;
+    if (transpose)
+      o[jj * C + c] = s * t;
+    else
+      o[i] = s * t;
+  }
 }
 
 __global__ void sum_parts_kernel(const float* __restrict__ part, int32_t nparts, int64_t n,
@@ -634,26 +650,18 @@ hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int3
   return hipGetLastError();
 }
 
-template <int R>
-hipError_t rowdot_r(const RowDotArgs& a, hipStream_t st) {
-  constexpr int RB = R <= 4 ? 8 : (R <= 8 ? 4 : 2);
-  const dim3 g(blocks_for(a.M, RB)), b(256);
-  const bool wt = a.w_jstride == 1;
-  if (a.nout == 2) {
-    if (wt) hipLaunchKernelGGL((rowdot_kernel<R, 2, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((rowdot_kernel<R, 2, false>), g, b, 0, st, a);
-  } else {
-    if (wt) hipLaunchKernelGGL((rowdot_kernel<R, 1, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((rowdot_kernel<R, 1, false>), g, b, 0, st, a);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (a.r <= 4) return rowdot_r<4>(a, st);
-  if (a.r <= 8) return rowdot_r<8>(a, st);
-  return rowdot_r<16>(a, st);
+  const dim3 g(blocks_for(a.M, 16)), b(64 * RD_WAVES);
+  const bool wt = a.w_jstride == 1;
+  if (a.nout == 2) {
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<2, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<2, false>), g, b, 0, st, a);
+  } else {
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<1, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<1, false>), g, b, 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 int colred_cols_per_block(int r) { return r <= 8 ? 512 : 256; }
@@ -670,7 +678,7 @@ hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
 hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
                                 int32_t nslots_dense, int32_t C, int32_t r, float s, int transpose,
                                 float* out, hipStream_t st) {
-  const dim3 g(blocks_for((int64_t)C * r, 256), (unsigned)E), b(256);
+  const dim3 g(blocks_for((int64_t)C * r, 32), (unsigned)E), b(256);
   hipLaunchKernelGGL(colred_finish_kernel, g, b, 0, st, part, chunk_start, nslots_dense, C, r, s,
                      transpose, out);
   return hipGetLastError();
