@@ -106,6 +106,39 @@ def main():
 
     lib = gq.lib()
 
+    def time_steps(fn, steps, warmup):
+        """(eager ms, graph ms) per step: `steps` Python-driven calls, then the
+        same step captured once in a HIP graph and replayed `steps` times (no
+        host launch overhead between kernels; every kernel still runs)."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        eager = a.elapsed_time(b) / steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        replayed = a.elapsed_time(b) / steps
+        del graph
+        return eager, replayed
+
     # ------------------------------------------------------------ linear step
     cfg = synth.CFG2
     t0 = time.time()
@@ -128,18 +161,9 @@ def main():
             lib.gq_profile_mmq_events(None, None)
         return y, out
 
-    for _ in range(args.warmup):
-        step()
     K = args.steps
     # timed steps: nothing but the step itself on the stream
-    torch.cuda.synchronize()
-    start, stop = ev(), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(K):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / K
+    ms_eager, ms = time_steps(step, K, args.warmup)
     # a second pass of K steps with events around the two MMQ launches (on
     # the stream they are launched on) gives the per-launch durations; the
     # event markers add queue latency, so they stay out of the timed steps
@@ -152,8 +176,8 @@ def main():
     bwd_ms = sum(pp[2].elapsed_time(pp[3]) for pp in prof) / K
     flops = linear_flops(cfg.T, cfg.K, cfg.N, cfg.rank)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] linear step {ms:.3f} ms  ({tflops:.1f} TFLOP/s); MMQ fwd {fwd_ms*1e3:.1f} us, "
-        f"MMQ dX {bwd_ms*1e3:.1f} us")
+    log(f"[bench] linear step {ms:.3f} ms graph-replayed ({tflops:.1f} TFLOP/s), {ms_eager:.3f} ms "
+        f"eager; MMQ fwd {fwd_ms*1e3:.1f} us, MMQ dX {bwd_ms*1e3:.1f} us")
 
     # dominant kernel: the slower of the two MMQ launches of the step
     gemm_flops = 2 * cfg.T * cfg.N * cfg.K + 2 * cfg.T * cfg.N * cfg.rank
@@ -175,6 +199,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "launch": "hip_graph_replay",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -204,19 +230,10 @@ def main():
             yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
             return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
 
-        for _ in range(max(2, args.warmup)):
-            mstep()
-        torch.cuda.synchronize()
-        a, b = ev(), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(K):
-            mstep()
-        b.record()
-        torch.cuda.synchronize()
-        mms = a.elapsed_time(b) / K
+        mms_eager, mms = time_steps(mstep, K, max(2, args.warmup))
         mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
         result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
-                               "ms_per_step": round(mms, 4),
+                               "ms_per_step": round(mms, 4), "ms_per_step_eager": round(mms_eager, 4),
                                "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
                                "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
@@ -226,16 +243,7 @@ def main():
         extra = {}
 
         def timed(fn, steps):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            a, b = ev(), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(steps):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / steps
+            return time_steps(fn, steps, 2)[1]
 
         c1 = synth.CFG1
         i1 = synth.make_linear(c1)

@@ -51,52 +51,30 @@ template <int QT> struct RawBlock {
   uint32_t q[NQ];
 };
 
-// Load the block at byte address `blk` (2-byte aligned).  The dword window
-// [blk & ~3, (blk & ~3) + 4*NDW) stays inside the block for a block that
-// starts 2 bytes past a dword boundary, and runs at most 2 bytes past its end
-// otherwise; callers only issue the latter kind when another block follows
-// in the same row (rows of an even number of blocks start dword-aligned).
-template <int QT> struct BlockWindow {
-  uint32_t dw[QTraits<QT>::NDW];
-  uint32_t sh;  // nonzero: the block starts at byte 2 of dw[0]
-};
-
-// Issue the dword loads of one block and nothing else, so that a prefetch
-// does not pull the realignment (which waits for the data) up to the load.
-template <int QT>
-__device__ __forceinline__ void load_window(const uint8_t* blk, BlockWindow<QT>& w) {
-  const uintptr_t a = (uintptr_t)blk;
-  // global address space explicitly: a generic (flat) load would also count
-  // against the LDS wait counter and serialise with the LDS reads
-  const __attribute__((address_space(1))) uint32_t* p =
-      (const __attribute__((address_space(1))) uint32_t*)(a & ~(uintptr_t)3);
-#pragma unroll
-  for (int i = 0; i < QTraits<QT>::NDW; ++i) w.dw[i] = p[i];
-  w.sh = (uint32_t)(a & 2);
-}
-
-// Realign a loaded window to hdr + payload dwords, ANDed with `mask`.
-template <int QT>
-__device__ __forceinline__ void realign(const BlockWindow<QT>& w, uint32_t mask, RawBlock<QT>& rb) {
-  if constexpr (QT == QT_Q2_DM) {
-    // 12-byte blocks in dword-aligned rows are always dword-aligned
-    rb.hdr = w.dw[0] & mask;
-    rb.q[0] = w.dw[1] & mask;
-    rb.q[1] = w.dw[2] & mask;
-  } else {
-    const bool sh = w.sh != 0;
-    rb.hdr = (sh ? (w.dw[0] >> 16) : (w.dw[0] & 0xffffu)) & mask;
-#pragma unroll
-    for (int i = 0; i < RawBlock<QT>::NQ; ++i)
-      rb.q[i] = (sh ? w.dw[i + 1] : __builtin_amdgcn_alignbyte(w.dw[i + 1], w.dw[i], 2)) & mask;
-  }
-}
-
+// Issue the loads of the block at byte address `blk` (2-byte aligned): the
+// fp16 scale and the payload.  The payload of a 2-byte aligned block is read
+// with unaligned dword loads straight into place (global memory accepts
+// them on this target), so nothing waits for the data before its use.
+// Global address space explicitly: a generic (flat) load would also count
+// against the LDS wait counter and serialise with the LDS reads.
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 template <int QT>
 __device__ __forceinline__ void load_block(const uint8_t* blk, RawBlock<QT>& rb) {
-  BlockWindow<QT> w;
-  load_window<QT>(blk, w);
-  realign<QT>(w, 0xffffffffu, rb);
+  typedef const __attribute__((address_space(1))) uint16_t g_u16;
+  typedef const __attribute__((address_space(1))) uint32_t g_u32;
+  typedef const __attribute__((address_space(1))) u32_a2 g_u32a2;
+  if constexpr (QT == QT_Q2_DM) {
+    // 12-byte blocks in dword-aligned rows are always dword-aligned
+    const g_u32* p = (const g_u32*)blk;
+    rb.hdr = p[0];
+    rb.q[0] = p[1];
+    rb.q[1] = p[2];
+  } else {
+    rb.hdr = *(const g_u16*)blk;
+    const g_u32a2* q = (const g_u32a2*)(blk + 2);
+#pragma unroll
+    for (int i = 0; i < RawBlock<QT>::NQ; ++i) rb.q[i] = q[i];
+  }
 }
 
 // Decode to 32 floats in element order (exact value rounded once to fp32).

@@ -77,6 +77,8 @@ __device__ __forceinline__ uint32_t opaque_mask(bool keep) {
   return m;
 }
 
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 // Row reduction of the staged tile Z [BM][ZP]:
 //   out[j] = sum_{c : n0 + c < ncols} Z[row][c] * (W ? W[(n0 + c) * r + j] : 1),  j < nv
 // Thread (row = tid % BM, seg = tid / BM) sums one column segment; segments
@@ -279,133 +281,6 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   auto KT = [&](int ls) { return ls * KS + grp; };
   auto LCb = [&](int b) { return wn * WTN + b * 32 + (lane & 31); };
 
-  // ---- activation operand: fixed rows per thread
-  int64_t aoff[G::A_CHUNKS];
-  bool aval[G::A_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < G::A_CHUNKS; ++i) {
-    const int c = tid + NTHR * i;
-    const int64_t pr = r0 + (c >> 3);
-    aval[i] = pr < r1;
-    int64_t src = pr;
-    if (aval[i] && p.gather) src = p.gather[pr] / p.gdiv;
-    aoff[i] = aval[i] ? src * p.lda + (c & 7) * 8 : 0;
-  }
-  uint4 areg0[G::A_CHUNKS], areg1[G::A_CHUNKS];
-  uint32_t amsk0[G::A_CHUNKS], amsk1[G::A_CHUNKS];
-  auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS], uint32_t (&amsk)[G::A_CHUNKS]) {
-    int k0 = kt * BK;
-    const uint16_t* base = p.a0;
-    if (k0 >= p.asplit) { base = p.a1; k0 -= p.asplit; }
-#pragma unroll
-    for (int i = 0; i < G::A_CHUNKS; ++i) {
-      // unconditional load from a clamped address, zeroed by select, so the
-      // steady-state loop stays one basic block
-      const int kc = kt * BK + ((tid + NTHR * i) & 7) * 8;
-      const bool ok = aval[i] && kc < p.K;
-      // the mask is applied at the LDS store, so waiting for this load is
-      // deferred to the store that consumes it
-      areg[i] = *reinterpret_cast<const uint4*>(ok ? base + aoff[i] + k0 : p.a0);
-      amsk[i] = opaque_mask(ok);
-    }
-  };
-  auto store_a = [&](int buf, const uint4 (&areg)[G::A_CHUNKS], const uint32_t (&amsk)[G::A_CHUNKS]) {
-    uint16_t* A = As + buf * BM * LDK;
-#pragma unroll
-    for (int i = 0; i < G::A_CHUNKS; ++i) {
-      const int c = tid + NTHR * i;
-      const uint32_t m = amsk[i];
-      *reinterpret_cast<uint4*>(A + (c >> 3) * LDK + (c & 7) * 8) =
-          make_uint4(areg[i].x & m, areg[i].y & m, areg[i].z & m, areg[i].w & m);
-    }
-  };
-
-  // ---- weight operand: WPT = 2*BN/256 blocks per thread per k-step.
-  // Item it = tid + 256*i; consecutive lanes read consecutive blocks of a row:
-  // NT: (row = it >> 1, kb = it & 1): block 2kt + kb of weight row `row`
-  // NN: (row = it / NB, kb = it % NB), NB = BN/32 blocks per row: block
-  //     n0/32 + kb of reduction row kt*64 + row
-  constexpr int WPT = 2 * BN / NTHR;
-  constexpr int NB = BN / 32;
-  int w_it_row[WPT], w_it_kb[WPT];
-  const uint8_t* wptr[WPT];  // NT: row base + kb*BS
-  bool wrow_ok[WPT];
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int it = tid + NTHR * i;
-    w_it_row[i] = NN ? (it / NB) : (it >> 1);
-    w_it_kb[i] = NN ? (it % NB) : (it & 1);
-    wptr[i] = nullptr;
-    if constexpr (!NN) {
-      const uint8_t* src = p.w0;
-      int nrow;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const int proj = (w_it_row[i] >> 5) & 1;
-        nrow = (n0 >> 1) + (w_it_row[i] >> 6) * 32 + (w_it_row[i] & 31);
-        src = proj ? p.w1 : p.w0;
-      } else {
-        nrow = n0 + w_it_row[i];
-      }
-      wrow_ok[i] = nrow < p.w_rows;
-      wptr[i] = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + nrow) * p.w_rowbytes +
-                w_it_kb[i] * BS;
-    } else {
-      wrow_ok[i] = ((n0 >> 5) + w_it_kb[i]) < p.w_nb;
-    }
-  }
-  BlockWindow<QT> wr0[WPT], wr1[WPT];
-  uint32_t wmsk0[WPT], wmsk1[WPT];
-  auto load_w = [&](int kt, BlockWindow<QT> (&wr)[WPT], uint32_t (&wmsk)[WPT]) {
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const uint8_t* blk = nullptr;
-      if constexpr (!NN) {
-        if (wrow_ok[i] && kt < nk) blk = wptr[i] + (int64_t)kt * 2 * BS;
-      } else {
-        // address arithmetic without a branch (a conditional block here
-        // splits the pipelined loop); invalid items read block 0 of w0
-        const int rg = kt * BK + w_it_row[i];
-        const bool ok = wrow_ok[i] && rg < p.K;
-        const int rv = ok ? rg : 0;
-        const bool second = rv >= p.wsplit;
-        const uint8_t* src = second ? p.w1 : p.w0;
-        const int rr = second ? rv - p.wsplit : rv;
-        const uint8_t* a = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + rr) * p.w_rowbytes +
-                           (int64_t)((n0 >> 5) + w_it_kb[i]) * BS;
-        blk = ok ? a : nullptr;
-      }
-      // unconditional load (the first block of w0 when out of range; rows
-      // hold at least two blocks, so the dword window stays in bounds),
-      // zeroed by select
-      load_window<QT>(blk ? blk : p.w0, wr[i]);
-      wmsk[i] = opaque_mask(blk != nullptr);
-    }
-  };
-  auto store_w = [&](int buf, const BlockWindow<QT> (&wraw)[WPT], const uint32_t (&wmsk)[WPT]) {
-    uint16_t* B = Bs + buf * B_TILE;
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      RawBlock<QT> wr;
-      realign<QT>(wraw[i], wmsk[i], wr);
-      float w[32];
-      decode_block_fast<QT>(wr, w);
-      if constexpr (!NN) {
-        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * LDK + w_it_kb[i] * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
-                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
-      } else {
-        // row-major store: reduction row w_it_row, columns kb*32 .. +32
-        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * PN + w_it_kb[i] * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
-                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
-      }
-    }
-  };
-
   // ---- main loop
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -415,9 +290,6 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  // Software pipeline, prefetch depth 2: tile kt+2 is loaded into the
-  // register set that tile kt was stored from, while the MFMAs of tile kt run
-  // and tile kt+1 (loaded one step earlier) waits in the other set.
   // NN operand B from the row-major tile with ds_read_b64_tr_b16: within
   // each 16-lane group g, output lane 16g + j slot t receives element j % 4
   // of the 4-element chunk addressed by lane 16g + 4t + j / 4.  Lane
@@ -461,8 +333,152 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
   };
-  constexpr bool DEEP = BM * BN < 256 * 256;  // small tiles: prefetch depth 2
-  if constexpr (DEEP) {
+
+  // ---- activation operand: fixed rows per thread
+  int64_t aoff[G::A_CHUNKS];
+  bool aval[G::A_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < G::A_CHUNKS; ++i) {
+    const int c = tid + NTHR * i;
+    const int64_t pr = r0 + (c >> 3);
+    aval[i] = pr < r1;
+    int64_t src = pr;
+    if (aval[i] && p.gather) src = p.gather[pr] / p.gdiv;
+    aoff[i] = aval[i] ? src * p.lda + (c & 7) * 8 : 0;
+  }
+
+  // ---- weight operand: WPT = 2*BN/256 blocks per thread per k-step.
+  // Item it = tid + 256*i; consecutive lanes read consecutive blocks of a row:
+  // NT: (row = it >> 1, kb = it & 1): block 2kt + kb of weight row `row`
+  // NN: (row = it / NB, kb = it % NB), NB = BN/32 blocks per row: block
+  //     n0/32 + kb of reduction row kt*64 + row
+  constexpr int WPT = 2 * BN / NTHR;
+  constexpr int NB = BN / 32;
+  int w_it_row[WPT], w_it_kb[WPT];
+  const uint8_t* wptr[WPT];  // NT: row base + kb*BS;  NN: block of k-step 0 in w0
+  bool wrow_ok[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int it = tid + NTHR * i;
+    w_it_row[i] = NN ? (it / NB) : (it >> 1);
+    w_it_kb[i] = NN ? (it % NB) : (it & 1);
+    if constexpr (!NN) {
+      const uint8_t* src = p.w0;
+      int nrow;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int proj = (w_it_row[i] >> 5) & 1;
+        nrow = (n0 >> 1) + (w_it_row[i] >> 6) * 32 + (w_it_row[i] & 31);
+        src = proj ? p.w1 : p.w0;
+      } else {
+        nrow = n0 + w_it_row[i];
+      }
+      wrow_ok[i] = nrow < p.w_rows;
+      wptr[i] = src + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + nrow) * p.w_rowbytes +
+                w_it_kb[i] * BS;
+    } else {
+      wrow_ok[i] = ((n0 >> 5) + w_it_kb[i]) < p.w_nb;
+      wptr[i] = p.w0 + (int64_t)e * p.w_estride + (int64_t)(p.w_row0 + w_it_row[i]) * p.w_rowbytes +
+                (int64_t)((n0 >> 5) + w_it_kb[i]) * BS;
+    }
+  }
+  // NN: byte offset of k-step kt from wptr -- uniform across the workgroup.
+  // Rows at or past wsplit (a multiple of 64) come from w1.
+  auto nn_koff = [&](int kt) {
+    const int k0 = kt * BK;
+    const int64_t delta = (int64_t)((uintptr_t)p.w1 - (uintptr_t)p.w0) - (int64_t)p.wsplit * p.w_rowbytes;
+    // select by mask: a branch here would split the pipelined loop
+    return (int64_t)k0 * p.w_rowbytes + (delta & -(int64_t)(k0 >= p.wsplit));
+  };
+
+  // A workgroup whose tile has every row, every weight column and only whole
+  // k-steps runs the pipeline without masks or clamped addresses.
+  bool full = (r1 - r0 == BM) && (p.K % (BK * KS) == 0);
+  if constexpr (NN) {
+    full = full && ((n0 >> 5) + NB <= p.w_nb);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    full = full && ((n0 >> 1) + BN / 2 <= p.w_rows);
+  } else {
+    full = full && (n0 + BN <= p.w_rows);
+  }
+
+  auto pipeline = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    uint4 areg0[G::A_CHUNKS], areg1[G::A_CHUNKS];
+    uint32_t amsk0[G::A_CHUNKS], amsk1[G::A_CHUNKS];
+    auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS], uint32_t (&amsk)[G::A_CHUNKS]) {
+      int k0 = kt * BK;
+      const uint16_t* base = p.a0;
+      if (k0 >= p.asplit) { base = p.a1; k0 -= p.asplit; }
+#pragma unroll
+      for (int i = 0; i < G::A_CHUNKS; ++i) {
+        if constexpr (FULL) {
+          areg[i] = *reinterpret_cast<const uint4*>(base + aoff[i] + k0);
+        } else {
+          // unconditional load from a clamped address, zeroed at the LDS
+          // store (so nothing waits for it here), so the steady-state loop
+          // stays one basic block
+          const int kc = kt * BK + ((tid + NTHR * i) & 7) * 8;
+          const bool ok = aval[i] && kc < p.K;
+          areg[i] = *reinterpret_cast<const uint4*>(ok ? base + aoff[i] + k0 : p.a0);
+          amsk[i] = opaque_mask(ok);
+        }
+      }
+    };
+    auto store_a = [&](int buf, const uint4 (&areg)[G::A_CHUNKS], const uint32_t (&amsk)[G::A_CHUNKS]) {
+      uint16_t* A = As + buf * BM * LDK;
+#pragma unroll
+      for (int i = 0; i < G::A_CHUNKS; ++i) {
+        const int c = tid + NTHR * i;
+        uint4 v = areg[i];
+        if constexpr (!FULL) {
+          const uint32_t m = amsk[i];
+          v = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        }
+        *reinterpret_cast<uint4*>(A + (c >> 3) * LDK + (c & 7) * 8) = v;
+      }
+    };
+    RawBlock<QT> wr0[WPT], wr1[WPT];
+    uint32_t wmsk0[WPT], wmsk1[WPT];
+    auto load_w = [&](int kt, RawBlock<QT> (&wr)[WPT], uint32_t (&wmsk)[WPT]) {
+      const int64_t koff = NN ? nn_koff(kt) : (int64_t)kt * 2 * BS;
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        if constexpr (FULL) {
+          load_block<QT>(wptr[i] + koff, wr[i]);
+        } else {
+          // unconditional load (block 0 of w0 when out of range), zeroed at
+          // the store; branch-free address selection keeps the loop one block
+          const bool ok = wrow_ok[i] && (NN ? kt * BK + w_it_row[i] < p.K : kt < nk);
+          load_block<QT>(ok ? wptr[i] + koff : p.w0, wr[i]);
+          wmsk[i] = opaque_mask(ok);
+        }
+      }
+    };
+    auto store_w = [&](int buf, const RawBlock<QT> (&wraw)[WPT], const uint32_t (&wmsk)[WPT]) {
+      uint16_t* B = Bs + buf * B_TILE;
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        RawBlock<QT> wr = wraw[i];
+        if constexpr (!FULL) {
+          wr.hdr &= wmsk[i];
+#pragma unroll
+          for (int q = 0; q < RawBlock<QT>::NQ; ++q) wr.q[q] &= wmsk[i];
+        }
+        float w[32];
+        decode_block_fast<QT>(wr, w);
+        // NT: row w_it_row of the [n][k] tile, k = kb*32 .. +32
+        // NN: reduction row w_it_row of the row-major tile, columns kb*32 .. +32
+        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * (NN ? PN : LDK) + w_it_kb[i] * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
+                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
+      }
+    };
+
+    // Software pipeline, prefetch depth 2: tile kt+2 is loaded into the
+    // register set that tile kt was stored from, while the MFMAs of tile kt
+    // run and tile kt+1 (loaded one step earlier) waits in the other set.
     load_a(KT(0), areg0, amsk0);
     load_w(KT(0), wr0, wmsk0);
     if (nkl > 1) {
@@ -474,9 +490,9 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     __syncthreads();
     int kt = 0;
     // steady state without branches, so the decode of the next tile can be
-    // scheduled among the MFMAs of the current one
-    // (the scheduling fence keeps the loads ahead of the decode of the
-    // other set, which would otherwise wait for them)
+    // scheduled among the MFMAs of the current one (the scheduling fence
+    // keeps the loads ahead of the decode of the other set, which would
+    // otherwise wait for them)
     for (; kt + 3 < nkl; kt += 2) {
       load_a(KT(kt + 2), areg0, amsk0);
       load_w(KT(kt + 2), wr0, wmsk0);
@@ -513,26 +529,11 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       }
       __syncthreads();
     }
-  } else {
-    // large tiles: one k-step of MFMAs (~2k cycles per wave) covers the
-    // latency of the next tile's loads; one register set
-    load_a(KT(0), areg0, amsk0);
-    load_w(KT(0), wr0, wmsk0);
-    store_a(0, areg0, amsk0);
-    store_w(0, wr0, wmsk0);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 1 < nkl; ++kt) {
-      const int cur = kt & 1;
-      load_a(KT(kt + 1), areg0, amsk0);
-      load_w(KT(kt + 1), wr0, wmsk0);
-      compute(cur);
-      store_a(cur ^ 1, areg0, amsk0);
-      store_w(cur ^ 1, wr0, wmsk0);
-      __syncthreads();
-    }
-    compute(kt & 1);
-  }
+  };
+  if (full)
+    pipeline(BoolC<true>{});
+  else
+    pipeline(BoolC<false>{});
 
   if constexpr (KS > 1) {
     // fold the second group's partial sums into the first group's
