@@ -11,6 +11,17 @@ kernel (timed with HIP events around each launch inside the timed region) and
 the fp64 oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+HBM traffic of the two MMQ launches: run the step under two rocprofv3
+counter passes with a plain device copy of known size in the same process,
+
+    rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- \\
+        python3 bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1
+    rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- (same)
+
+then `python bench.py --traffic-from F/run_counter_collection.csv
+W/run_counter_collection.csv` (no GPU needed) scales each counter by what it
+reads for the copy and writes profiles/mmq_traffic.json and its summary.
 """
 from __future__ import annotations
 
@@ -65,6 +76,75 @@ def load_traffic(kernel_key):
     return ent.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+# the two MMQ launches of the linear step: kernel name fragment, threads per
+# launch (tiles x workgroup size), key in mmq_traffic.json
+MMQ_LAUNCHES = (
+    ("gemm_kernel<1, 0, 128, 128, 1>", 768 * 256, "mmq_nt_lin_q4_0_cfg2"),
+    ("gemm_kernel<1, 4, 128, 128, 2>", 256 * 512, "mmq_nn_lin_bwd_q4_0_cfg2"),
+)
+
+
+def write_traffic(fetch_csv, write_csv, cmdline):
+    """Bytes per launch of the MMQ kernels from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled so that the reference copy reads and writes
+    exactly its size."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            rows.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return rows
+
+    out, lines = {}, []
+    scale = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = per_kernel(path, counter)
+        copy = [v for (n, g), vs in rows.items() if "copy" in n.lower() for v in vs
+                if v * 1024 > 0.5 * COPY_BYTES]
+        if not copy:
+            raise SystemExit(f"no reference copy of {COPY_BYTES} bytes found in {path}")
+        scale[counter] = statistics.median(copy) * 1024 / COPY_BYTES
+        lines.append(f"| reference copy ({COPY_BYTES >> 20} MiB) | {counter} | "
+                     f"{statistics.median(copy):.0f} KiB | factor {scale[counter]:.4f} |")
+        for frag, grid, key in MMQ_LAUNCHES:
+            vals = [v for (n, g), vs in rows.items() if frag in n and g == grid for v in vs]
+            if not vals:
+                raise SystemExit(f"no dispatch of {frag} (grid {grid}) in {path}")
+            med = statistics.median(vals)
+            bytes_ = med * 1024 / scale[counter]
+            e = out.setdefault(key, {"source_hash": gemm_source_hash(), "kernel": frag})
+            e["fetch_bytes" if counter == "FETCH_SIZE" else "write_bytes"] = round(bytes_)
+            lines.append(f"| {frag} (grid {grid}) | {counter} | {med:.0f} KiB x {len(vals)} | "
+                         f"{bytes_ / 1e6:.2f} MB per launch |")
+    for e in out.values():
+        e["hbm_bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "mmq_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "mmq_traffic_linear_q4_0_t2048_2048x6144.md"), "w") as fh:
+        fh.write("# HBM traffic of the two MMQ launches of the dense Q4_0 linear step "
+                 "(T 2048, 2048 -> 6144, rank 4)\n\n")
+        fh.write("Counter passes (repo root on the GPU box, TMPDIR=/tmp, run from /tmp):\n\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch -o run -- "
+                 "python3 <repo>/bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1\n")
+        fh.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write -o run -- "
+                 "python3 <repo>/bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1\n\n")
+        fh.write(f"Summary written by: `{cmdline}`\n\n")
+        fh.write("Each counter (KiB per dispatch, median over dispatches) is divided by what the same "
+                 "counter reads for a plain device copy of known size in the same process.\n\n")
+        fh.write("| kernel | counter | raw | scaled |\n|---|---|---|---|\n")
+        fh.write("\n".join(lines) + "\n\n")
+        for key, e in out.items():
+            fh.write(f"- {key}: fetch {e['fetch_bytes'] / 1e6:.2f} MB + write {e['write_bytes'] / 1e6:.2f} MB"
+                     f" = {e['hbm_bytes_per_launch'] / 1e6:.2f} MB per launch (source hash {e['source_hash']})\n")
+    log(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -74,7 +154,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="no HIP-graph replay (counter runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a %d MiB device copy (counter scale reference)" % (COPY_BYTES >> 20))
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/mmq_traffic.json from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, " ".join(sys.argv))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
@@ -105,11 +193,18 @@ def main():
         return e
 
     lib = gq.lib()
+    if args.copy_probe:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def time_steps(fn, steps, warmup):
-        """(eager ms, graph ms) per step: `steps` Python-driven calls, then the
-        same step captured once in a HIP graph and replayed `steps` times (no
-        host launch overhead between kernels; every kernel still runs)."""
+        """(eager ms, graph ms) per step: `steps` calls issued from Python, then
+        the same step captured once in a HIP graph and replayed `steps` times
+        (no host launch work between kernels; every kernel still runs)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -120,6 +215,8 @@ def main():
         b.record()
         torch.cuda.synchronize()
         eager = a.elapsed_time(b) / steps
+        if args.eager:
+            return eager, eager
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -163,7 +260,7 @@ def main():
 
     K = args.steps
     # timed steps: nothing but the step itself on the stream
-    ms_eager, ms = time_steps(step, K, args.warmup)
+    ms, ms_graph = time_steps(step, K, args.warmup)
     # a second pass of K steps with events around the two MMQ launches (on
     # the stream they are launched on) gives the per-launch durations; the
     # event markers add queue latency, so they stay out of the timed steps
@@ -176,8 +273,8 @@ def main():
     bwd_ms = sum(pp[2].elapsed_time(pp[3]) for pp in prof) / K
     flops = linear_flops(cfg.T, cfg.K, cfg.N, cfg.rank)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] linear step {ms:.3f} ms graph-replayed ({tflops:.1f} TFLOP/s), {ms_eager:.3f} ms "
-        f"eager; MMQ fwd {fwd_ms*1e3:.1f} us, MMQ dX {bwd_ms*1e3:.1f} us")
+    log(f"[bench] linear step {ms:.3f} ms ({tflops:.1f} TFLOP/s), {ms_graph:.3f} ms replayed from a "
+        f"HIP graph; MMQ fwd {fwd_ms*1e3:.1f} us, MMQ dX {bwd_ms*1e3:.1f} us")
 
     # dominant kernel: the slower of the two MMQ launches of the step
     gemm_flops = 2 * cfg.T * cfg.N * cfg.K + 2 * cfg.T * cfg.N * cfg.rank
@@ -199,8 +296,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "ms_per_step_eager": round(ms_eager, 4),
-        "launch": "hip_graph_replay",
+        "ms_per_step_hip_graph": round(ms_graph, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -230,10 +326,10 @@ def main():
             yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
             return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
 
-        mms_eager, mms = time_steps(mstep, K, max(2, args.warmup))
+        mms, mms_graph = time_steps(mstep, K, max(2, args.warmup))
         mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
         result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
-                               "ms_per_step": round(mms, 4), "ms_per_step_eager": round(mms_eager, 4),
+                               "ms_per_step": round(mms, 4), "ms_per_step_hip_graph": round(mms_graph, 4),
                                "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
                                "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
@@ -243,7 +339,7 @@ def main():
         extra = {}
 
         def timed(fn, steps):
-            return time_steps(fn, steps, 2)[1]
+            return time_steps(fn, steps, 2)[0]
 
         c1 = synth.CFG1
         i1 = synth.make_linear(c1)
@@ -312,7 +408,7 @@ def main():
         from oracle import linear as ol
 
         reps, spent = 0, 0.0
-        while spent < args.cpu_seconds and reps < 50:
+        while spent < args.cpu_seconds and reps < 500:
             t0 = time.perf_counter()
             ol.run(inp)
             spent += time.perf_counter() - t0

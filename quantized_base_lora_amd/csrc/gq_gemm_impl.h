@@ -78,46 +78,62 @@ __device__ __forceinline__ uint32_t opaque_mask(bool keep) {
 }
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
+template <int I> struct IntC { static constexpr int value = I; };
+
+// r (<= R) rank values at p: R/4 vector loads when r == R (rank vectors of
+// r = R floats are 16-byte aligned), else guarded scalar loads.
+template <int R>
+__device__ __forceinline__ void load_rank(const float* p, int r, float (&v)[R]) {
+  if (r == R) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = j < r ? p[j] : 0.f;
+  }
+}
 
 // Row reduction of the staged tile Z [BM][ZP]:
-//   out[j] = sum_{c : n0 + c < ncols} Z[row][c] * (W ? W[(n0 + c) * r + j] : 1),  j < nv
-// Thread (row = tid % BM, seg = tid / BM) sums one column segment; segments
-// are combined in order through LDS.  sink(row, out) runs on segment 0.
-// Caller has synchronised after writing Z; returns synchronised.
-template <int BM, int BN, class Sink>
-__device__ __forceinline__ void z_row_reduce(float* Z, const float* W, int r, int nv, int n0,
-                                             int ncols, Sink sink) {
-  constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG, ZP = BN + 1;
+//   out[j] = sum_{c : n0 + c < ncols} Z[row][c] * W[(n0 + c) * r + j],  j < r <= R
+// (W == nullptr: out[0] = the plain row sum).  Thread (row = tid % BM,
+// seg = tid / BM) sums one column segment; segments are combined in order
+// through LDS.  sink(row, out) runs on segment 0.  Caller has synchronised
+// after writing Z; returns synchronised.
+template <int BM, int BN, int R, class Sink>
+__device__ __forceinline__ void z_row_reduce(float* Z, const float* W, int r, int n0, int ncols,
+                                             Sink sink) {
+  constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG, ZP = BN + 1, XP = R + 1;
   const int tid = threadIdx.x;
   const int row = tid % BM, seg = tid / BM;
-  float acc[16];
+  float acc[R];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int j = 0; j < R; ++j) acc[j] = 0.f;
   const int cend = min((seg + 1) * SEGC, ncols - n0);
-  for (int c = seg * SEGC; c < cend; ++c) {
-    const float z = Z[row * ZP + c];
-    if (W) {
-      const float* w = W + (int64_t)(n0 + c) * r;
+  if (W) {
+    for (int c = seg * SEGC; c < cend; ++c) {
+      const float z = Z[row * ZP + c];
+      float w[R];
+      load_rank<R>(W + (int64_t)(n0 + c) * r, r, w);
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < nv) acc[j] += z * w[j];
-    } else {
-      acc[0] += z;
+      for (int j = 0; j < R; ++j) acc[j] += z * w[j];
     }
+  } else {
+    for (int c = seg * SEGC; c < cend; ++c) acc[0] += Z[row * ZP + c];
   }
   __syncthreads();
-  float* X = Z;  // reuse: [NSEG][BM][17]
+  float* X = Z;  // reuse: [NSEG][BM][R + 1]
   if (seg > 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < nv) X[(seg * BM + row) * 17 + j] = acc[j];
+    for (int j = 0; j < R; ++j) X[(seg * BM + row) * XP + j] = acc[j];
   }
   __syncthreads();
   if (seg == 0) {
     for (int sg = 1; sg < NSEG; ++sg) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < nv) acc[j] += X[(sg * BM + row) * 17 + j];
+      for (int j = 0; j < R; ++j) acc[j] += X[(sg * BM + row) * XP + j];
     }
     sink(row, acc);
   }
@@ -125,36 +141,34 @@ __device__ __forceinline__ void z_row_reduce(float* Z, const float* W, int r, in
 }
 
 // Column reduction of Z: out[j] = sum_{row : r0 + row < r1} Z[row][col] * X[(r0+row)*r + j]
-template <int BM, int BN, class Sink>
+template <int BM, int BN, int R, class Sink>
 __device__ __forceinline__ void z_col_reduce(float* Z, const float* X, int r, int64_t r0,
                                              int64_t r1, Sink sink) {
-  constexpr int NSEG = NTHR / BN, SEGR = BM / NSEG, ZP = BN + 1;
+  constexpr int NSEG = NTHR / BN, SEGR = BM / NSEG, ZP = BN + 1, XP = R + 1;
   const int tid = threadIdx.x;
   const int col = tid % BN, seg = tid / BN;
-  float acc[16];
+  float acc[R];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int j = 0; j < R; ++j) acc[j] = 0.f;
   const int rend = (int)min((int64_t)(seg + 1) * SEGR, r1 - r0);
   for (int rr = seg * SEGR; rr < rend; ++rr) {
     const float z = Z[rr * ZP + col];
-    const float* x = X + (r0 + rr) * r;
+    float x[R];
+    load_rank<R>(X + (r0 + rr) * r, r, x);
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) acc[j] += z * x[j];
+    for (int j = 0; j < R; ++j) acc[j] += z * x[j];
   }
   __syncthreads();
   float* Xs = Z;
   if (seg > 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) Xs[(seg * BN + col) * 17 + j] = acc[j];
+    for (int j = 0; j < R; ++j) Xs[(seg * BN + col) * XP + j] = acc[j];
   }
   __syncthreads();
   if (seg == 0) {
     for (int sg = 1; sg < NSEG; ++sg) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < r) acc[j] += Xs[(sg * BN + col) * 17 + j];
+      for (int j = 0; j < R; ++j) acc[j] += Xs[(sg * BN + col) * XP + j];
     }
     sink(col, acc);
   }
@@ -180,14 +194,13 @@ __device__ __forceinline__ void down_pair_reduce(uint32_t* Zu, const float* Bg, 
     const uint32_t pv = Zu[row * ZP + c];
     const float dg = __builtin_bit_cast(float, pv << 16);
     const float du = __builtin_bit_cast(float, pv & 0xffff0000u);
-    const float* bg = Bg + (int64_t)(n0 + c) * r;
-    const float* bu = Bu + (int64_t)(n0 + c) * r;
+    float bg[R], bu[R];
+    load_rank<R>(Bg + (int64_t)(n0 + c) * r, r, bg);
+    load_rank<R>(Bu + (int64_t)(n0 + c) * r, r, bu);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (j < r) {
-        ag[j] += dg * bg[j];
-        au[j] += du * bu[j];
-      }
+      ag[j] += dg * bg[j];
+      au[j] += du * bu[j];
     }
   }
   __syncthreads();
@@ -255,8 +268,25 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
     bid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
   }
-  const int mslot = bid % p.mtiles;
-  const int ntile = bid / p.mtiles;
+  // Dense launches: each XCD's run of tiles covers GM m-tiles by a band of
+  // n-tiles (grouped ordering), so its L2 holds the activation rows of GM
+  // m-tiles and the weight columns of the band instead of every m-tile.
+  // Grouped launches keep m-slots fastest: their unused trailing slots are
+  // then spread evenly over the XCDs.
+  int mslot, ntile;
+  if (p.offsets) {
+    mslot = bid % p.mtiles;
+    ntile = bid / p.mtiles;
+  } else {
+    constexpr int GM = 4;
+    const int gsize = GM * p.ntiles;
+    const int g = bid / gsize;
+    const int m_first = g * GM;
+    const int gm = min(p.mtiles - m_first, GM);
+    const int idx = bid - g * gsize;
+    mslot = m_first + idx % gm;
+    ntile = idx / gm;
+  }
   int e = 0;
   int64_t r0, r1;
   if (p.offsets) {
@@ -765,7 +795,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         }
       }
     __syncthreads();
-    z_row_reduce<BM, BN>(Z, nullptr, r, 1, n0, p.N, [&](int row, float(&out)[16]) {
+    z_row_reduce<BM, BN, 4>(Z, nullptr, r, n0, p.N, [&](int row, float(&out)[4]) {
       const int64_t pr = r0 + row;
       if (pr < r1) p.f0[((int64_t)ntile * p.M + pr) * width] = out[0];
     });
@@ -822,6 +852,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
               zv = gval(a, b, v, pr, n);
               if (n < p.ldo) p.o0[pr * p.ldo + n] = f2bf(zv);
             }
+            acc[a][b][v] = zv;  // G, restaged below without recomputing
           }
           Z[lr * ZP + lc] = zv;
         }
@@ -871,40 +902,43 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       }
       if (have_lab) p.f1[pr] = zl;
     } else {
-      // G . B over this tile's vocab columns -> part_GB[ntile][T][r]
-      z_row_reduce<BM, BN>(Z, p.lB0 + c0 * r, r, r, n0, p.w_rows, [&](int row, float(&out)[16]) {
-        const int64_t pr = r0 + row;
-        if (pr < r1) {
-          float* dst = p.f1 + ((int64_t)(p.ntile_base + ntile) * p.M + pr) * r;
+      // G . B over this tile's vocab columns -> part_GB[ntile][T][r], then
+      // G^T . xa over this tile's rows -> part_dB[mtile][V][r] (G restaged
+      // from the accumulators)
+      auto reductions = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        z_row_reduce<BM, BN, R>(Z, p.lB0 + c0 * r, r, n0, p.w_rows, [&](int row, float(&out)[R]) {
+          const int64_t pr = r0 + row;
+          if (pr < r1) {
+            float* dst = p.f1 + ((int64_t)(p.ntile_base + ntile) * p.M + pr) * r;
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (j < r) dst[j] = out[j];
-        }
-      });
-      // G^T . xa over this tile's rows -> part_dB[mtile][V][r]  (restage G)
-#pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int lc = LC(b);
-        const int n = n0 + lc;
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int lr = LR(a, v);
-            const int64_t pr = r0 + lr;
-            Z[lr * ZP + lc] = pr < r1 ? gval(a, b, v, pr, n) : 0.f;
+            for (int j = 0; j < R; ++j)
+              if (j < r) dst[j] = out[j];
           }
-      }
-      __syncthreads();
-      z_col_reduce<BM, BN>(Z, p.rv0, r, r0, r1, [&](int col, float(&out)[16]) {
-        const int n = n0 + col;
-        if (n < p.w_rows) {
-          float* dst = p.f2 + ((int64_t)mslot * V + c0 + n) * r;
+        });
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (j < r) dst[j] = out[j];
-        }
-      });
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) Z[LR(a, v) * ZP + LC(b)] = acc[a][b][v];
+        __syncthreads();
+        z_col_reduce<BM, BN, R>(Z, p.rv0, r, r0, r1, [&](int col, float(&out)[R]) {
+          const int n = n0 + col;
+          if (n < p.w_rows) {
+            float* dst = p.f2 + ((int64_t)mslot * V + c0 + n) * r;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+              if (j < r) dst[j] = out[j];
+          }
+        });
+      };
+      if (r <= 4)
+        reductions(IntC<4>{});
+      else if (r <= 8)
+        reductions(IntC<8>{});
+      else
+        reductions(IntC<16>{});
     }
   }
 }

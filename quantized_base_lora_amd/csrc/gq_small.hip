@@ -287,33 +287,35 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   }
 }
 
-// out[e] = s * sum_{slots of e} part[slot].  A block covers 32 outputs (c, j)
-// of one expert with eight slot lanes each: lane g adds slots g, g+8, ... in
-// order, and the eight lane sums are added in lane order through LDS
-// (deterministic), so many slots are read with eight loads in flight.
+// out[e] = s * sum_{slots of e} part[slot].  A block covers 256/SL outputs
+// (c, j) of one expert with SL slot lanes each: lane g adds slots g, g+SL,
+// ... in order, and the SL lane sums are added in lane order through LDS
+// (deterministic), so many slots are read with many loads in flight.
+template <int SL>
 __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restrict__ part,
                                                             const int32_t* __restrict__ cs,
                                                             int32_t nslots_dense, int32_t C,
                                                             int32_t r, float s, int transpose,
                                                             float* __restrict__ out) {
-  __shared__ float red[8][32];
+  constexpr int NO = 256 / SL;
+  __shared__ float red[SL][NO];
   const int e = blockIdx.y;
-  const int oi = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int oi = threadIdx.x % NO, g = threadIdx.x / NO;
   const int64_t n = (int64_t)C * r;
-  const int64_t i = (int64_t)blockIdx.x * 32 + oi;
+  const int64_t i = (int64_t)blockIdx.x * NO + oi;
   const int s0 = cs ? cs[e] : 0;
   const int s1 = cs ? cs[e + 1] : nslots_dense;
   float acc = 0.f;
   if (i < n) {
 #pragma unroll 4
-    for (int sl = s0 + g; sl < s1; sl += 8) acc += part[(int64_t)sl * n + i];
+    for (int sl = s0 + g; sl < s1; sl += SL) acc += part[(int64_t)sl * n + i];
   }
   red[g][oi] = acc;
   __syncthreads();
   if (g == 0 && i < n) {
     float t = red[0][oi];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) t += red[k][oi];
+    for (int k = 1; k < SL; ++k) t += red[k][oi];
     const int64_t c = i / r, jj = i % r;
     float* o = out + (int64_t)e * n;
     if (transpose)
@@ -321,15 +323,6 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
     else
       o[i] = s * t;
   }
-}
-
-__global__ void sum_parts_kernel(const float* __restrict__ part, int32_t nparts, int64_t n,
-                                 float scale, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float acc = 0.f;
-  for (int t = 0; t < nparts; ++t) acc += part[(int64_t)t * n + i];
-  out[i] = scale * acc;
 }
 
 // ----------------------------------------------------------------- routing
@@ -554,30 +547,48 @@ __global__ void ce_prep_kernel(const int64_t* __restrict__ labels, int64_t T, in
 }
 
 // per token: ordered online merge of the (max, sumexp) partials
-__global__ void ce_merge_kernel(const float* __restrict__ part, int32_t ntiles, int64_t T,
-                                const float* __restrict__ zlab, const int64_t* __restrict__ labels,
-                                int64_t V, int64_t ignore_index, float* __restrict__ lse,
-                                float* __restrict__ term) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float m = -INFINITY, l = 0.f;
-  for (int nt = 0; nt < ntiles; ++nt) {
-    const float m2 = part[((int64_t)nt * T + t) * 2], l2 = part[((int64_t)nt * T + t) * 2 + 1];
-    if (m2 == -INFINITY) continue;
-    if (m2 > m) {
-      l = (m == -INFINITY ? 0.f : l * __expf(m - m2)) + l2;
-      m = m2;
-    } else {
-      l += l2 * __expf(m2 - m);
-    }
+// Merge the per-tile (max, sum exp) partials [ntiles][T][2] of each token
+// into lse.  A block takes 8 tokens with 32 tile lanes each; lane g merges
+// tiles g, g+32, ... online and the 32 lane results are merged in lane order
+// through LDS (deterministic).
+__device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2) {
+  if (m2 == -INFINITY) return;
+  if (m2 > m) {
+    l = (m == -INFINITY ? 0.f : l * __expf(m - m2)) + l2;
+    m = m2;
+  } else {
+    l += l2 * __expf(m2 - m);
   }
-  const float v = m + __logf(l);
-  lse[t] = v;
-  const int64_t lab = labels[t];
-  term[t] = (lab != ignore_index && lab >= 0 && lab < V) ? v - zlab[t] : 0.f;
 }
 
-// loss = sum(term) / nvalid, fixed-order tree in one block
+__global__ __launch_bounds__(256) void ce_merge_kernel(const float* __restrict__ part,
+                                                       int32_t ntiles, int64_t T,
+                                                       const float* __restrict__ zlab,
+                                                       const int64_t* __restrict__ labels, int64_t V,
+                                                       int64_t ignore_index, float* __restrict__ lse,
+                                                       float* __restrict__ term) {
+  __shared__ float2 red[32][8];
+  const int ti = threadIdx.x & 7, g = threadIdx.x >> 3;
+  const int64_t t = (int64_t)blockIdx.x * 8 + ti;
+  float m = -INFINITY, l = 0.f;
+  if (t < T) {
+#pragma unroll 4
+    for (int nt = g; nt < ntiles; nt += 32) {
+      const float2 v = *reinterpret_cast<const float2*>(part + ((int64_t)nt * T + t) * 2);
+      lse_merge(m, l, v.x, v.y);
+    }
+  }
+  red[g][ti] = make_float2(m, l);
+  __syncthreads();
+  if (g == 0 && t < T) {
+    for (int k = 1; k < 32; ++k) lse_merge(m, l, red[k][ti].x, red[k][ti].y);
+    const float v = m + __logf(l);
+    lse[t] = v;
+    const int64_t lab = labels[t];
+    term[t] = (lab != ignore_index && lab >= 0 && lab < V) ? v - zlab[t] : 0.f;
+  }
+}
+
 __global__ void ce_loss_kernel(const float* __restrict__ term, int64_t T,
                                const float* __restrict__ nvalid, float* __restrict__ loss) {
   __shared__ float sh[1024];
@@ -678,19 +689,23 @@ hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
 hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
                                 int32_t nslots_dense, int32_t C, int32_t r, float s, int transpose,
                                 float* out, hipStream_t st) {
-  const dim3 g(blocks_for((int64_t)C * r, 32), (unsigned)E), b(256);
-  hipLaunchKernelGGL(colred_finish_kernel, g, b, 0, st, part, chunk_start, nslots_dense, C, r, s,
-                     transpose, out);
+  // many slots per output (dense, long reductions): 32 slot lanes
+  if (!chunk_start && nslots_dense > 64) {
+    const dim3 g(blocks_for((int64_t)C * r, 8), (unsigned)E), b(256);
+    hipLaunchKernelGGL(colred_finish_kernel<32>, g, b, 0, st, part, chunk_start, nslots_dense, C, r,
+                       s, transpose, out);
+  } else {
+    const dim3 g(blocks_for((int64_t)C * r, 32), (unsigned)E), b(256);
+    hipLaunchKernelGGL(colred_finish_kernel<8>, g, b, 0, st, part, chunk_start, nslots_dense, C, r,
+                       s, transpose, out);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_sum_parts(const float* part, int32_t nparts, int64_t rows, int32_t width,
                             float scale, float* out, hipStream_t st) {
-  const int64_t n = rows * width;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, part, nparts, n,
-                     scale, out);
-  return hipGetLastError();
+  if (rows * width == 0) return hipSuccess;
+  return launch_colred_finish(part, nullptr, 1, nparts, (int32_t)rows, width, scale, 0, out, st);
 }
 
 size_t route_ws_bytes(int64_t T, int32_t E, int32_t k) {
@@ -746,7 +761,7 @@ hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, cons
                            const int64_t* labels, int64_t V, int64_t ignore_index,
                            const float* nvalid, float* lse, float* loss, float* term,
                            hipStream_t st) {
-  hipLaunchKernelGGL(ce_merge_kernel, dim3(blocks_for(T, 256)), dim3(256), 0, st, part_ml, ntiles, T,
+  hipLaunchKernelGGL(ce_merge_kernel, dim3(blocks_for(T, 8)), dim3(256), 0, st, part_ml, ntiles, T,
                      zlab, labels, V, ignore_index, lse, term);
   hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, term, T, nvalid, loss);
   return hipGetLastError();
