@@ -125,10 +125,12 @@ GemmArgs gemm_defaults() {
 // power of two (16..512) that still gives >= 512 workgroups, so that the
 // reduction fills the chip without multiplying the partial-sum traffic.
 int pick_rc(int64_t M, int64_t C, int r, int E) {
+  // grouped: short per-expert slots (32 rows per wave) keep the Zipf head
+  // experts from serialising the launch
+  if (E > 1) return 128;
   const int64_t cb = cdiv(C, colred_cols_per_block(r));
-  const int extra = E > 1 ? E : 0;
   int rc = 32;
-  while (rc < 1024 && (cdiv(M, rc * 2) + extra) * cb >= 256) rc *= 2;
+  while (rc < 1024 && cdiv(M, rc * 2) * cb >= 256) rc *= 2;
   return rc;
 }
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
@@ -374,7 +376,8 @@ int64_t grouped_mtiles(int64_t M, int E, int bm) { return cdiv(M, bm) + E; }
 size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t, int64_t) {
   if (!P) return 0;
   Ws w(nullptr);
-  w.take<int32_t>(P->n_experts + 1);
+  w.take<int32_t>(P->n_experts + 1);  // GEMM tiles
+  w.take<int32_t>(P->n_experts + 1);  // 16-row tiles of the row dots
   return w.size();
 }
 
@@ -404,11 +407,16 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
   const int E = P->n_experts, r = P->rank, K = (int)P->n_in, N = (int)P->n_out;
   Ws w(ws);
   int32_t* ts = w.take<int32_t>(E + 1);
+  int32_t* ts16 = w.take<int32_t>(E + 1);
+  const int ntiles_fwd = epilogue == GQ_EPI_SWIGLU ? cdiv(N, TILE_BN / 2) : cdiv(N, TILE_BN);
+  const int tc = pick_tile(M, ntiles_fwd);
+  HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), ts, 16, ts16, 1, nullptr, st),
+          "gq_grouped_mmq_lora_fwd: tiles");
 
   RowDotArgs rd;
   memset(&rd, 0, sizeof rd);
   rd.M = M; rd.C = K; rd.r = r; rd.act = a->in; rd.lda = K; rd.gather = a->gather;
-  rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E;
+  rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E; rd.tile16 = ts16;
   rd.w_estride = (int64_t)r * K; rd.w_jstride = K; rd.w_cstride = 1; rd.nout = nproj;
   for (int i = 0; i < nproj; ++i) {
     rd.W[i] = P[i].A;
@@ -438,9 +446,7 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
     g.ntiles = cdiv(N, TILE_BN);
     epi = EPI_LIN;
   }
-  const int tc = pick_tile(M, g.ntiles);
   g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
-  HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), ts, st), "gq_grouped_mmq_lora_fwd: tiles");
   HIP_TRY(launch_gemm(P->qtype, epi, tc, g, st), "gq_grouped_mmq_lora_fwd: grouped MMQ");
   return GQ_OK;
 }
@@ -449,6 +455,7 @@ namespace {
 struct GrpBwdWs {
   int32_t* ts;
   int32_t* cs;
+  int32_t* ts16;
   float* dyB;
   float* wdyB;
   float* wxa;
@@ -465,6 +472,7 @@ GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
   const int E = P->n_experts, r = P->rank;
   p.ts = w.take<int32_t>(E + 1);
   p.cs = w.take<int32_t>(E + 1);
+  p.ts16 = w.take<int32_t>(E + 1);
   const int64_t slots = colred_slots(M, grp_rc(P, M), E);
   if (mode == GQ_BWD_DOWN_SWIGLU) {
     const int64_t H = P[0].n_out, I = P[0].n_in;
@@ -540,7 +548,13 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   const GrpBwdWs W = plan_grp_bwd(w, P, mode, M);
   const int rcg = grp_rc(P, M);
   const int slots = (int)colred_slots(M, rcg, E);
-  HIP_TRY(launch_tile_start(a->offsets, E, rcg, W.cs, st), "gq_grouped_mmq_lora_bwd: chunks");
+  // GEMM tiles (the backward MMQ's tile height), column-reduction chunks and
+  // 16-row row-dot tiles of every expert, in one launch
+  const int ntiles_bwd = cdiv(P[0].n_in, TILE_BN);  // N of both backward MMQs
+  const int tc = pick_tile(M, ntiles_bwd);
+  HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), W.ts, rcg, W.cs, 16,
+                             mode == GQ_BWD_DOWN_SWIGLU ? W.ts16 : nullptr, st),
+          "gq_grouped_mmq_lora_bwd: tiles");
 
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
@@ -558,7 +572,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     RowDotArgs rd;
     memset(&rd, 0, sizeof rd);
     rd.M = M; rd.C = H; rd.r = r; rd.act = a->dy; rd.lda = H; rd.gather = a->gather;
-    rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E;
+    rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E; rd.tile16 = W.ts16;
     rd.W[0] = P[0].B; rd.w_estride = (int64_t)H * r; rd.w_jstride = 1; rd.w_cstride = r;
     rd.out[0] = W.dyB; rd.nout = 1; rd.out2 = W.wdyB; rd.wflat = a->w_flat; rd.sorted = a->sorted;
     HIP_TRY(launch_rowdot(rd, st), "gq_grouped_mmq_lora_bwd: dY Bd");
@@ -573,14 +587,12 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     g.w_rows = H;
     g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
     g.ntiles = cdiv(I, TILE_BN);
-    const int tc = pick_tile(M, g.ntiles);
     g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
     g.s = s; g.r = r;
     g.lA0 = P[0].A; g.lA_estride = (int64_t)r * I;
     g.lB1 = P[1].B; g.lB2 = P[2].B; g.lB_estride = (int64_t)I * r;
     g.rv0 = W.dyB; g.s0 = a->g; g.s1 = a->u; g.wflat = a->w_flat; g.sorted = a->sorted;
     g.o0 = a->dg; g.o1 = a->du; g.ldo = I; g.f0 = W.part_down;
-    HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), W.ts, st), "gq_grouped_mmq_lora_bwd: tiles");
     HIP_TRY(launch_gemm(P[0].qtype, EPI_DOWN_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: down MMQ");
     HIP_TRY(launch_down_finish(W.part_down, g.ntiles, M, r, a->sorted, a->dw_flat, a->dgB, a->duB, st),
             "gq_grouped_mmq_lora_bwd: dw, dgB, duB");
@@ -612,7 +624,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   g.w_rows = I; g.wsplit = I;
   g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
   g.ntiles = cdiv(H, TILE_BN);
-  const int tc = pick_tile(M, g.ntiles);
   g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
   g.s = s; g.r = r;
   g.lA0 = P[0].A; g.lA1 = P[1].A; g.lA_estride = (int64_t)r * H;
@@ -620,7 +631,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   g.o0 = a->dxrows; g.ldo = H;
   if (I % GEMM_BK)
     return fail(GQ_ENOTSUP, "gq_grouped_mmq_lora_bwd: intermediate size must be a multiple of 64");
-  HIP_TRY(launch_tile_start(a->offsets, E, tile_bm(tc), W.ts, st), "gq_grouped_mmq_lora_bwd: tiles");
   HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: gate/up MMQ");
 
   cr.C = H; cr.U = a->x; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;

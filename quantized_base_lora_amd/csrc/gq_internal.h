@@ -105,6 +105,10 @@ hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t c
 // tile_start[e] = sum_{e' < e} ceil(cnt(e') / bm); E + 1 entries
 hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tile_start,
                              hipStream_t st);
+// up to three prefixes in one launch (ts1 / ts2 nullable)
+hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int32_t bm0, int32_t* ts0,
+                              int32_t bm1, int32_t* ts1, int32_t bm2, int32_t* ts2,
+                              hipStream_t st);
 
 // out[p][j] = sum_c act(p)[c] * W(e)[j][c]   (W [r][C] if w_jstride == C, or
 // [C][r] if w_jstride == 1, w_cstride == r); act rows via gather; e via offsets.
@@ -119,6 +123,7 @@ struct RowDotArgs {
   int32_t gdiv;
   const int32_t* offsets;
   int32_t E;
+  const int32_t* tile16;  // grouped: prefix of 16-row tiles per expert (launch_tile_starts)
   const float* W[2];
   int64_t w_estride;
   int64_t w_jstride;

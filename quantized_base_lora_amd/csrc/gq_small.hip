@@ -57,25 +57,35 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ blocks, int64_t nbloc
 }
 
 // ------------------------------------------------------ tile prefix (E <= 1024)
-__global__ void tile_start_kernel(const int32_t* __restrict__ offsets, int32_t E, int32_t bm,
-                                  int32_t* __restrict__ ts) {
-  __shared__ int32_t sh[1024];
+// Exclusive prefix over experts of ceil(rows_e / bm[q]) for up to three tile
+// or chunk heights at once (one launch instead of one per height):
+// ts_q[e] = first tile of expert e, ts_q[E] = number of tiles.
+__global__ __launch_bounds__(1024) void tile_start_kernel(const int32_t* __restrict__ offsets,
+                                                          int32_t E, int3 bm, int32_t* ts0,
+                                                          int32_t* ts1, int32_t* ts2) {
+  __shared__ int32_t sh[3][1024];
   const int t = threadIdx.x;
-  int v = 0;
-  if (t < E) {
-    const int cnt = offsets[t + 1] - offsets[t];
-    v = (cnt + bm - 1) / bm;
-  }
-  sh[t] = v;
+  const int bms[3] = {bm.x, bm.y, bm.z};
+  int32_t* outs[3] = {ts0, ts1, ts2};
+  const int cnt = t < E ? offsets[t + 1] - offsets[t] : 0;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) sh[q][t] = (t < E && outs[q]) ? (cnt + bms[q] - 1) / bms[q] : 0;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    const int add = t >= o ? sh[t - o] : 0;
+    int add[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) add[q] = t >= o ? sh[q][t - o] : 0;
     __syncthreads();
-    sh[t] += add;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) sh[q][t] += add[q];
     __syncthreads();
   }
-  if (t < E) ts[t + 1] = sh[t];
-  if (t == 0) ts[0] = 0;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    if (!outs[q]) continue;
+    if (t < E) outs[q][t + 1] = sh[q][t];
+    if (t == 0) outs[q][0] = 0;
+  }
 }
 
 __device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_t p) {
@@ -103,19 +113,27 @@ template <int NOUT, bool WT>
 __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs a) {
   __shared__ f32x4 red[RD_WAVES - 1][NOUT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * 16;
   const int r = a.r;
+  // rows p0 .. p1-1 of one expert: grouped rows come in expert-aligned
+  // 16-row tiles (prefix tile16), so every block makes one pass with one
+  // expert's rank vectors
+  int64_t p0, p1;
+  int e = 0;
+  if (a.tile16) {
+    const int tile = blockIdx.x;
+    if (tile >= a.tile16[a.E]) return;
+    e = find_expert(a.tile16, a.E, tile);
+    p0 = (int64_t)a.offsets[e] + (int64_t)(tile - a.tile16[e]) * 16;
+    p1 = min((int64_t)a.offsets[e + 1], p0 + 16);
+  } else {
+    p0 = (int64_t)blockIdx.x * 16;
+    p1 = min(a.M, p0 + 16);
+  }
   // the activation row this lane feeds into the MFMA (row lane % 16)
   const int64_t pa = p0 + (lane & 15);
-  const bool pav = pa < a.M;
+  const bool pav = pa < p1;
   const int64_t src = !pav ? 0 : (a.gather ? (int64_t)(a.gather[pa] / a.gdiv) : pa);
   const uint16_t* arow = a.act + src * a.lda + 8 * (lane >> 4);
-  int ea = 0, elo = 0, ehi = 0;
-  if (a.offsets) {
-    ea = pav ? find_expert(a.offsets, a.E, pa) : -1;
-    elo = find_expert(a.offsets, a.E, p0);
-    ehi = find_expert(a.offsets, a.E, (p0 + 16 < a.M ? p0 + 16 : a.M) - 1);
-  }
   const int j = lane & 15;  // rank column this lane feeds (B operand)
   const bool jok = j < r;
   const int jc = jok ? j : 0;  // clamped: every load below stays in bounds
@@ -123,8 +141,8 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
 #pragma unroll
   for (int o = 0; o < NOUT; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int UNR = 4;  // 32-column steps whose loads are issued together
-  for (int e = elo; e <= ehi; ++e) {
-    const bool rowok = pav && ea == e;
+  {
+    const bool rowok = pav;
     const float* Wb[NOUT];
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) Wb[o] = a.W[o] + (int64_t)e * a.w_estride + (int64_t)jc * a.w_jstride;
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t p = p0 + 4 * (lane >> 4) + q;
-        if (p < a.M) {
+        if (p < p1) {
           a.out[o][p * r + j] = v[q];
           if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v[q];
         }
@@ -657,13 +675,21 @@ hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t c
 
 hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* ts,
                              hipStream_t st) {
-  hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, ts);
+  return launch_tile_starts(offsets, E, bm, ts, 1, nullptr, 1, nullptr, st);
+}
+
+hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int32_t bm0, int32_t* ts0,
+                              int32_t bm1, int32_t* ts1, int32_t bm2, int32_t* ts2,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E,
+                     make_int3(bm0, bm1, bm2), ts0, ts1, ts2);
   return hipGetLastError();
 }
 
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  const dim3 g(blocks_for(a.M, 16)), b(64 * RD_WAVES);
+  // grouped: at most M/16 + E expert-aligned tiles
+  const dim3 g(blocks_for(a.M, 16) + (a.tile16 ? (unsigned)a.E : 0u)), b(64 * RD_WAVES);
   const bool wt = a.w_jstride == 1;
   if (a.nout == 2) {
     if (wt) hipLaunchKernelGGL((rowdot_kernel<2, true>), g, b, 0, st, a);
@@ -686,11 +712,49 @@ hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Grouped finish: out[e] = s * sum of expert e's slots, in slot order.  A
+// thread owns four consecutive outputs (one 16-byte load per slot); experts
+// with no slots get zeros.
+__global__ __launch_bounds__(256) void colred_finish_grp_kernel(const float* __restrict__ part,
+                                                                const int32_t* __restrict__ cs,
+                                                                int32_t C, int32_t r, float s,
+                                                                int transpose,
+                                                                float* __restrict__ out) {
+  const int e = blockIdx.y;
+  const int64_t n = (int64_t)C * r;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const int s0 = cs[e], s1 = cs[e + 1];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int sl = s0; sl < s1; ++sl) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)sl * n + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+  float* o = out + (int64_t)e * n;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t ii = i + q;
+    if (transpose)
+      o[(ii % r) * C + ii / r] = s * a4[q];
+    else
+      o[ii] = s * a4[q];
+  }
+}
+
 hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
                                 int32_t nslots_dense, int32_t C, int32_t r, float s, int transpose,
                                 float* out, hipStream_t st) {
+  if (chunk_start) {
+    const int64_t n = (int64_t)C * r;  // a multiple of 4: C % 8 == 0
+    const dim3 g(blocks_for(n, 1024), (unsigned)E), b(256);
+    hipLaunchKernelGGL(colred_finish_grp_kernel, g, b, 0, st, part, chunk_start, C, r, s, transpose,
+                       out);
+    return hipGetLastError();
+  }
   // many slots per output (dense, long reductions): 32 slot lanes
-  if (!chunk_start && nslots_dense > 64) {
+  if (nslots_dense > 64) {
     const dim3 g(blocks_for((int64_t)C * r, 8), (unsigned)E), b(256);
     hipLaunchKernelGGL(colred_finish_kernel<32>, g, b, 0, st, part, chunk_start, nslots_dense, C, r,
                        s, transpose, out);
