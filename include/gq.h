@@ -234,6 +234,8 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
  *   dA_g[e] = s sum_p dgB[p]^T x_p,  dB_g[e] = s sum_p dg[p]^T xa_g[p]; same for up.
  *   Inputs: x (activation rows via gather), dg, du, dgB, duB, xa (= [2][M][rank]).
  * Adapter gradients of experts without rows are written as exact zeros.
+ * All bf16 row arrays (dy, x, g, u, h, dg, du, dxrows) must be 16-byte
+ * aligned (GQ_EINVAL otherwise).
  */
 typedef struct gq_grouped_bwd_args {
     const int32_t* offsets;  /* [E+1] */

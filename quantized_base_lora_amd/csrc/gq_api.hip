@@ -566,8 +566,9 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     if (!a->dy || !a->w_flat || !a->sorted || !a->g || !a->u || !a->h || !a->xa_d || !a->dw_flat ||
         !a->dA_d || !a->dB_d || !a->dg || !a->du || !a->dgB || !a->duB)
       return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for DOWN_SWIGLU");
-    if (!aligned(a->dy, 16) || !aligned(a->h, 4) || !aligned(a->dg, 4) || !aligned(a->du, 4))
-      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: dy must be 16-byte aligned");
+    if (!aligned(a->dy, 16) || !aligned(a->h, 16) || !aligned(a->g, 16) || !aligned(a->u, 16) ||
+        !aligned(a->dg, 16) || !aligned(a->du, 16))
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: dy, g, u, h, dg, du must be 16-byte aligned");
     // dY Bd (unweighted) and its gate-weighted copy
     RowDotArgs rd;
     memset(&rd, 0, sizeof rd);

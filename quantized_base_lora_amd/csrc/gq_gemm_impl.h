@@ -52,7 +52,9 @@ struct Geom {
   static constexpr int B_TILE = NN ? BK * PN : BN * LDK;
   static constexpr int SMEM_MAIN = 2 * (BM * LDK + B_TILE) * 2;
   static constexpr int ZP = BN + 1;  // pitch (floats) of the staged epilogue tile
-  static constexpr int SMEM_Z = STAGE ? BM * ZP * 4 : 0;
+  // staged tile with 16-byte aligned rows (BN + 4 floats) plus two [BN][8]
+  // rank-vector slices (the SwiGLU-backward epilogue); covers the ZP layout
+  static constexpr int SMEM_Z = STAGE ? BM * (BN + 4) * 4 + 2 * BN * 8 * 4 : 0;
   // KS groups of four waves, each with its own double-buffered stages; the
   // cross-group reduction of the accumulators reuses the same memory
   static constexpr int SMEM_K = KS * SMEM_MAIN;
@@ -171,68 +173,6 @@ __device__ __forceinline__ void z_col_reduce(float* Z, const float* X, int r, in
       for (int j = 0; j < R; ++j) acc[j] += Xs[(sg * BN + col) * XP + j];
     }
     sink(col, acc);
-  }
-  __syncthreads();
-}
-
-// Row dots of the staged (dg, du) bf16 pairs with the columns' Bg / Bu rank
-// vectors: part[row][1 + j] = sum_c dg[row][c] Bg[n0+c][j],
-//          part[row][1 + r + j] = sum_c du[row][c] Bu[n0+c][j].
-// Segments of columns are combined in order through LDS (deterministic).
-template <int BM, int BN, int R>
-__device__ __forceinline__ void down_pair_reduce(uint32_t* Zu, const float* Bg, const float* Bu,
-                                                 int r, int n0, int ncols, int64_t r0, int64_t r1,
-                                                 float* part, int width) {
-  constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG, ZP = BN + 1;
-  const int tid = threadIdx.x;
-  const int row = tid % BM, seg = tid / BM;
-  float ag[R], au[R];
-#pragma unroll
-  for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
-  const int cend = min((seg + 1) * SEGC, ncols - n0);
-  for (int c = seg * SEGC; c < cend; ++c) {
-    const uint32_t pv = Zu[row * ZP + c];
-    const float dg = __builtin_bit_cast(float, pv << 16);
-    const float du = __builtin_bit_cast(float, pv & 0xffff0000u);
-    float bg[R], bu[R];
-    load_rank<R>(Bg + (int64_t)(n0 + c) * r, r, bg);
-    load_rank<R>(Bu + (int64_t)(n0 + c) * r, r, bu);
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      ag[j] += dg * bg[j];
-      au[j] += du * bu[j];
-    }
-  }
-  __syncthreads();
-  float* X = reinterpret_cast<float*>(Zu);  // [NSEG][BM][2R + 1]
-  constexpr int XP = 2 * R + 1;
-  if (seg > 0) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      X[(seg * BM + row) * XP + j] = ag[j];
-      X[(seg * BM + row) * XP + R + j] = au[j];
-    }
-  }
-  __syncthreads();
-  if (seg == 0) {
-    for (int sg = 1; sg < NSEG; ++sg) {
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        ag[j] += X[(sg * BM + row) * XP + j];
-        au[j] += X[(sg * BM + row) * XP + R + j];
-      }
-    }
-    const int64_t pr = r0 + row;
-    if (pr < r1) {
-      float* dst = part + pr * width;
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if (j < r) {
-          dst[1 + j] = ag[j];
-          dst[1 + r + j] = au[j];
-        }
-      }
-    }
   }
   __syncthreads();
 }
@@ -756,65 +696,147 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         }
     }
   } else if constexpr (EPI == EPI_DOWN_BWD) {
-    // columns are the expert's intermediate index i (< N = I); acc holds
-    // e = dY deq(Wd) + s (dY Bd) Ad.  One compute pass writes dg, du (bf16),
-    // stages e*h and keeps (dg, du) packed in registers; two LDS row
-    // reductions give the dw and (dg Bg, du Bu) partials of this column tile.
+    // Columns are the expert's intermediate index i (< N = I); acc holds
+    // e = dY deq(Wd) + s (dY Bd) Ad.  e is staged row-major in LDS; each
+    // thread then owns a segment of one row: 16-byte loads of the saved g, u,
+    // the SwiGLU backward, 16-byte stores of dg, du (bf16), and the row
+    // partials of this column tile: dw = sum e*silu(g)*u, dgB = sum dg*Bg,
+    // duB = sum du*Bu (with the stored bf16 dg, du), combined in segment
+    // order through LDS.  Bg, Bu of the tile's columns sit in LDS for r <= 8.
+    constexpr int ZD = BN + 4;
+    constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG;
     float* Z = reinterpret_cast<float*>(smem);
-    uint32_t* Zu = reinterpret_cast<uint32_t*>(smem);
+    float* Bst = Z + BM * ZD;  // [2][BN][8]
     const int width = 1 + 2 * r;
-    uint32_t pk[TM][TN][16];
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = LR(a, v);
-        const int64_t pr = r0 + lr;
-        const bool rok = pr < r1;
-        const float wp = rok ? p.wflat[p.sorted[pr]] : 0.f;
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int lc = LC(b);
-          const int c = n0 + lc;
-          float zv = 0.f;
-          uint32_t packed = 0;
-          if (rok && c < p.N) {
-            const float ev = acc[a][b][v];
-            const int64_t o = pr * p.ldo + c;
-            const float gg = bf2f(p.s0[o]), uu = bf2f(p.s1[o]);
-            const float sg = sigmoidf_(gg);
-            const float silu = gg * sg;
-            const float dh = wp * ev;
-            packed = pack_bf2(dh * uu * sg * (1.f + gg * (1.f - sg)), dh * silu);
-            p.o0[o] = (uint16_t)(packed & 0xffffu);
-            p.o1[o] = (uint16_t)(packed >> 16);
-            zv = ev * silu * uu;
-          }
-          pk[a][b][v] = packed;
-          Z[lr * ZP + lc] = zv;
-        }
-      }
-    __syncthreads();
-    z_row_reduce<BM, BN, 4>(Z, nullptr, r, n0, p.N, [&](int row, float(&out)[4]) {
-      const int64_t pr = r0 + row;
-      if (pr < r1) p.f0[((int64_t)ntile * p.M + pr) * width] = out[0];
-    });
+    const float* Bg = p.lB1 + (int64_t)e * p.lB_estride;
+    const float* Bu = p.lB2 + (int64_t)e * p.lB_estride;
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Zu[LR(a, v) * ZP + LC(b)] = pk[a][b][v];
+        for (int v = 0; v < 16; ++v) Z[LR(a, v) * ZD + LC(b)] = acc[a][b][v];
+    if (r <= 8) {
+      for (int idx = tid; idx < 2 * BN * 8; idx += NTHR) {
+        const int mat = idx / (BN * 8), c = (idx >> 3) % BN, j = idx & 7;
+        const int col = n0 + c;
+        Bst[idx] = (j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + j] : 0.f;
+      }
+    }
     __syncthreads();
-    const float* Bg = p.lB1 + (int64_t)e * p.lB_estride;
-    const float* Bu = p.lB2 + (int64_t)e * p.lB_estride;
-    float* part = p.f0 + (int64_t)ntile * p.M * width;
+    const int row = tid % BM, seg = tid / BM;
+    const int64_t pr = r0 + row;
+    const bool rok = pr < r1;
+    auto segment = [&](auto rc) {
+      constexpr int R = decltype(rc)::value;
+      float dw = 0.f, ag[R], au[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
+      if (rok) {
+        const float wp = p.wflat[p.sorted[pr]];
+#pragma unroll 1
+        for (int q = 0; q < SEGC / 8; ++q) {
+          const int lc = seg * SEGC + 8 * q;
+          const int c = n0 + lc;
+          if (c >= p.N) break;  // N % 8 == 0: whole 8-column chunks
+          const int64_t o = pr * p.ldo + c;
+          const uint4 g8 = *reinterpret_cast<const uint4*>(p.s0 + o);
+          const uint4 u8 = *reinterpret_cast<const uint4*>(p.s1 + o);
+          const float4 e0 = *reinterpret_cast<const float4*>(Z + row * ZD + lc);
+          const float4 e1 = *reinterpret_cast<const float4*>(Z + row * ZD + lc + 4);
+          const uint32_t gw[4] = {g8.x, g8.y, g8.z, g8.w}, uw[4] = {u8.x, u8.y, u8.z, u8.w};
+          const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+          uint32_t dgp[4], dup[4];
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            float dgv[2], duv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float gg = bf2f((uint16_t)(gw[t2] >> (16 * h)));
+              const float uu = bf2f((uint16_t)(uw[t2] >> (16 * h)));
+              const float eh = ev[2 * t2 + h];
+              const float sg = sigmoidf_(gg);
+              const float silu = gg * sg;
+              const float dh = wp * eh;
+              dgv[h] = dh * uu * sg * (1.f + gg * (1.f - sg));
+              duv[h] = dh * silu;
+              dw += eh * silu * uu;
+            }
+            dgp[t2] = pack_bf2(dgv[0], dgv[1]);
+            dup[t2] = pack_bf2(duv[0], duv[1]);
+          }
+          *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
+          *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
+          // rank partials of the eight columns: R <= 8 from the LDS slices
+          // (unrolled); R = 16 from global memory, one column at a time so the
+          // loads of all eight columns are not hoisted at once
+          auto col_terms = [&](int t) {
+            const float dq = __builtin_bit_cast(float, (dgp[t >> 1] >> (16 * (t & 1))) << 16);
+            const float uq = __builtin_bit_cast(float, (dup[t >> 1] >> (16 * (t & 1))) << 16);
+            float bg[R], bu[R];
+            if constexpr (R <= 8) {
+#pragma unroll
+              for (int j = 0; j < R; ++j) {
+                bg[j] = Bst[(lc + t) * 8 + j];
+                bu[j] = Bst[(BN + lc + t) * 8 + j];
+              }
+            } else {
+              load_rank<R>(Bg + (int64_t)(c + t) * r, r, bg);
+              load_rank<R>(Bu + (int64_t)(c + t) * r, r, bu);
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+              ag[j] += dq * bg[j];
+              au[j] += uq * bu[j];
+            }
+          };
+          if constexpr (R <= 8) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) col_terms(t);
+          } else {
+#pragma unroll 1
+            for (int t = 0; t < 8; ++t) col_terms(t);
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int XP = 2 * R + 1;
+      float* X = Z;  // [NSEG][BM][XP]
+      if (seg > 0) {
+        X[(seg * BM + row) * XP] = dw;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          X[(seg * BM + row) * XP + 1 + j] = ag[j];
+          X[(seg * BM + row) * XP + 1 + R + j] = au[j];
+        }
+      }
+      __syncthreads();
+      if (seg == 0 && rok) {
+        for (int sg = 1; sg < NSEG; ++sg) {
+          dw += X[(sg * BM + row) * XP];
+#pragma unroll
+          for (int j = 0; j < R; ++j) {
+            ag[j] += X[(sg * BM + row) * XP + 1 + j];
+            au[j] += X[(sg * BM + row) * XP + 1 + R + j];
+          }
+        }
+        float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width;
+        dst[0] = dw;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          if (j < r) {
+            dst[1 + j] = ag[j];
+            dst[1 + r + j] = au[j];
+          }
+        }
+      }
+    };
     if (r <= 4)
-      down_pair_reduce<BM, BN, 4>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
+      segment(IntC<4>{});
     else if (r <= 8)
-      down_pair_reduce<BM, BN, 8>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
+      segment(IntC<8>{});
     else
-      down_pair_reduce<BM, BN, 16>(Zu, Bg, Bu, r, n0, p.N, r0, r1, part, width);
+      segment(IntC<16>{});
   } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
     // acc holds the logits z of this tile (adapter term included)
     float* Z = reinterpret_cast<float*>(smem);
