@@ -85,6 +85,18 @@ MMQ_LAUNCHES = (
 )
 
 
+def moe_layer_bytes(T, H, I, E, k, r, qtype_bytes, active):
+    """Algorithmic HBM bytes of one routed-MoE layer fwd+bwd: the blocks of
+    the active experts read once per pass (gate, up, down; forward and
+    backward), token activations in and out (x, dY read; y, dx written), all
+    experts' adapters read and their gradients written."""
+    per_expert = (2 * I * (H // 32) + H * (I // 32)) * qtype_bytes
+    weights = 2 * active * per_expert
+    acts = 4 * T * H * 2
+    adapters = 2 * E * 4 * r * (2 * H + I + 2 * I + H)
+    return weights + acts + adapters
+
+
 def write_traffic(fetch_csv, write_csv, cmdline):
     """Bytes per launch of the MMQ kernels from FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), each scaled so that the reference copy reads and writes
@@ -153,6 +165,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="small-token sweep (HBM-bound shapes); included in --all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="no HIP-graph replay (counter runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -400,6 +414,70 @@ def main():
                           "tflops": round(f5 / (m5 * 1e-3) / 1e12, 2)}
         log(f"[bench] {c5.name}: {m5:.3f} ms/step")
         result["other_workloads"] = extra
+
+    # ------------------------------------------------- small-token sweep
+    if args.sweep or args.all:
+        sweep = []
+        sc = synth.CFG3
+        t0 = time.time()
+        winp = synth.make_moe(sc)  # expert weights are per-expert streams: shared by every T
+        log(f"[bench] sweep weights {sc.name} generated in {time.time() - t0:.1f}s")
+        mk = lambda w, a, b, no, ni: gq.Proj(sc.qtype, no, ni, u8(w), f32(a), f32(b),
+                                             float(winp["scale"]), sc.E)
+        swts = gq.MoEWeights(mk(winp["wg"], winp["ag"], winp["bg"], sc.I, sc.H),
+                             mk(winp["wu"], winp["au"], winp["bu"], sc.I, sc.H),
+                             mk(winp["wd"], winp["ad"], winp["bd"], sc.H, sc.I))
+        del winp
+        bs = {0: 34, 1: 18, 2: 12}[sc.qtype]
+        for T in (16, 64, 128, 256, 512):
+            tc = synth.MoECfg(f"moe_q4_0_t{T}_h2048_e128k8_i768_r4", T=T, H=sc.H, I=sc.I, E=sc.E,
+                              k=sc.k, qtype=sc.qtype, rank=sc.rank, alpha=sc.alpha, seed=sc.seed)
+            tinp = synth.make_moe(tc, experts=[])  # token draws only
+            tx, tdy, tlg = bf(tinp["x"]), bf(tinp["dy"]), f32(tinp["logits"])
+
+            def tstep():
+                yy, sv = gq.moe_ffn_fwd(swts, tx, tlg, tc.k)
+                return gq.moe_ffn_bwd(swts, tx, tdy, sv, tc.k, tc.E)
+
+            tms = time_steps(tstep, max(10, K), 3)[0]
+            _, sv = gq.moe_ffn_fwd(swts, tx, tlg, tc.k)
+            active = int((sv["offsets"][1:] - sv["offsets"][:-1] > 0).sum().item())
+            nbytes = moe_layer_bytes(T, sc.H, sc.I, sc.E, sc.k, sc.rank, bs, active)
+            gbs = nbytes / (tms * 1e-3) / 1e9
+            sweep.append({"workload": tc.name, "op": "moe layer fwd+bwd", "ms": round(tms, 4),
+                          "active_experts": active, "algorithmic_bytes": nbytes,
+                          "GB_per_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                          "tokens_per_s": round(T / (tms * 1e-3), 1)})
+            log(f"[bench] sweep {tc.name}: {tms:.3f} ms, {active} experts, {gbs:.0f} GB/s "
+                f"({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
+        del swts
+        hc = synth.CFG5
+        for T in (16, 64, 128):
+            cfgT = synth.HeadCfg(f"lmhead_fwd_q8_0_t{T}_h2048_v151936_r4", T=T, H=hc.H, V=hc.V,
+                                 qtype=hc.qtype, rank=hc.rank, alpha=hc.alpha, chunk=hc.chunk,
+                                 seed=hc.seed)
+            hinp = synth.make_head(cfgT)
+            hd = gq.Proj(cfgT.qtype, cfgT.V, cfgT.H, u8(hinp["blocks"]), f32(hinp["A"]),
+                         f32(hinp["B"]), float(hinp["scale"]))
+            hh = bf(hinp["h"])
+            hl = torch.from_numpy(hinp["labels"]).to(dev)
+            del hinp
+            hws = [None]
+
+            def hstep():
+                out = gq.lmhead_chunked_ce(hd, hh, hl, chunk_rows=cfgT.chunk, want_grad=False, ws=hws[0])
+                hws[0] = out["ws"]
+                return out
+
+            hms = time_steps(hstep, max(10, K), 3)[0]
+            nbytes = cfgT.V * (cfgT.H // 32) * 34 + T * cfgT.H * 2 + cfgT.V * cfgT.rank * 4 + cfgT.rank * cfgT.H * 4
+            gbs = nbytes / (hms * 1e-3) / 1e9
+            sweep.append({"workload": cfgT.name, "op": "LM head forward (loss, lse)", "ms": round(hms, 4),
+                          "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+            log(f"[bench] sweep {cfgT.name}: {hms:.3f} ms, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
+            del hd
+        result["small_token_sweep"] = sweep
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu:
