@@ -53,10 +53,15 @@ def moe_flops(T, H, I, k, r):
 
 
 def gemm_source_hash():
+    """Hash of the MMQ kernel source with comments and blank lines dropped,
+    so that counters stay attributed to the kernel until its code changes."""
     h = hashlib.sha256()
     for f in ("gq_gemm_impl.h", "gq_dev.h"):
-        with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -95,6 +100,45 @@ def moe_layer_bytes(T, H, I, E, k, r, qtype_bytes, active):
     acts = 4 * T * H * 2
     adapters = 2 * E * 4 * r * (2 * H + I + 2 * I + H)
     return weights + acts + adapters
+
+
+def write_kernel_summary(csv_dir, out_md, title):
+    """rocprofv3's own --stats table, plus the same trace broken out by launch
+    size (kernels of one name run at several grid sizes)."""
+    import csv
+    import re
+    import statistics
+
+    def short(n):
+        n = n.replace("void ", "").replace("gq::(anonymous namespace)::", "").replace("gq::", "")
+        return re.sub(r"\(.*", "", n)
+
+    stats = list(csv.DictReader(open(os.path.join(csv_dir, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(csv_dir, "run_kernel_trace.csv"))))
+    by = {}
+    for r in trace:
+        key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in by.values())
+    with open(out_md, "w") as fh:
+        fh.write(f"# rocprofv3 kernel summary: {title}\n\n")
+        fh.write("Command (repo root on the GPU box, TMPDIR=/tmp, run from /tmp):\n\n")
+        fh.write("    rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/<dir> -o run -- "
+                 f"python3 <repo>/bench.py {title}\n\n")
+        fh.write("gemm_kernel<qtype, epilogue, BM, BN, k-groups>: qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, "
+                 "1 SwiGLU, 2 CE logits, 3 CE gradient, 4 linear backward (dX), 5 SwiGLU backward, "
+                 "6 gate/up backward, 7 dh accumulate.\n\n")
+        fh.write("## rocprofv3 --stats (run_kernel_stats.csv)\n\n| kernel | calls | avg us | min us | max us | % |\n"
+                 "|---|---|---|---|---|---|\n")
+        for r in stats[:30]:
+            fh.write(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |\n")
+        fh.write("\n## Same trace by launch size (run_kernel_trace.csv)\n\n| kernel | threads per launch | calls | "
+                 "avg us | median us | % of GPU time |\n|---|---|---|---|---|---|\n")
+        for (name, grid), v in sorted(by.items(), key=lambda kv: -sum(kv[1]))[:40]:
+            fh.write(f"| {name} | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {statistics.median(v):.1f} | "
+                     f"{100 * sum(v) / total:.1f} |\n")
+    log(f"wrote {out_md}")
 
 
 def write_traffic(fetch_csv, write_csv, cmdline):
@@ -171,11 +215,17 @@ def main():
     ap.add_argument("--eager", action="store_true", help="no HIP-graph replay (counter runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a %d MiB device copy (counter scale reference)" % (COPY_BYTES >> 20))
+    ap.add_argument("--kernel-summary", nargs=3, metavar=("CSV_DIR", "OUT_MD", "TITLE"),
+                    help="write a kernel-time summary from a rocprofv3 --kernel-trace --stats "
+                         "--output-format csv run (files run_kernel_stats.csv, run_kernel_trace.csv)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/mmq_traffic.json from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from, " ".join(sys.argv))
+        return
+    if args.kernel_summary:
+        write_kernel_summary(*args.kernel_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "

@@ -2,10 +2,10 @@
 //
 // Block decode follows the block definitions of GGUF Q8_0 / Q4_0 and the
 // 2-bit scale/min format (page 2 "Show HN: LoRA over GGUF", section "Things
-// involved in the training": MMQ over GGUF weights).  Blocks are read with
-// dword loads from the 4-byte-aligned address at or below the block (blocks
-// are only 2-byte aligned: 34 and 18 bytes) and realigned in registers, then
-// decoded straight to bf16 pairs -- no full-precision weight is ever stored.
+// involved in the training": MMQ over GGUF weights).  A block (only 2-byte
+// aligned: 34 and 18 bytes) is read as its fp16 scale plus the payload with
+// unaligned dword loads, then decoded straight to bf16 pairs -- no
+// full-precision weight is ever stored.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,8 +43,8 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Raw bytes of one block, realigned: hdr = first 4 bytes of the block
-// (d, and m for Q2_DM), q[] = the payload as dwords.
+// Raw bytes of one block: hdr = the scale (low 16 bits; d and m for Q2_DM),
+// q[] = the payload as dwords.
 template <int QT> struct RawBlock {
   static constexpr int NQ = QT == QT_Q8_0 ? 8 : (QT == QT_Q4_0 ? 4 : 2);
   uint32_t hdr;

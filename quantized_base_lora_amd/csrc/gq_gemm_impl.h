@@ -6,24 +6,28 @@
 // decoding the compressed weights in registers and multiplying at once, with
 // no fp16 copy of W) is built here for CDNA4:
 //
-//  * 256 threads = 4 wave64s in a 2x2 grid; block tile BM x 128, k-step 64.
+//  * 256 threads = 4 wave64s in a 2x2 grid (block tile BM x 128, k-step 64),
+//    or 512 threads in two k-groups of four waves that take alternate
+//    k-steps and add their accumulators through LDS (split-K inside the
+//    workgroup, for launches of at most one tile per CU).
 //  * Activations (bf16) are staged global -> registers -> LDS; weight blocks
-//    are loaded raw (dword loads + byte realignment), decoded to bf16 in
+//    are loaded raw (scale + unaligned payload loads), decoded to bf16 in
 //    registers and written to LDS -- the only full-precision copy of W is the
 //    64-deep LDS slice of the current tile.
 //  * NT (forward): the reduction runs along the weight's block dimension, the
 //    decoded tile is stored [n][k].  NN (backward, dX = dY deq(W)): the
-//    reduction runs along the weight's rows; the decode writes the tile
-//    transposed, so both modes feed v_mfma_f32_32x32x16_bf16 from identical
-//    [col][k] LDS layouts (fp32 accumulation).
-//  * Double-buffered LDS, one barrier per k-step; the next tile's global
-//    loads are in flight while the MFMAs of the current one run.
+//    reduction runs along the weight's rows; the decoded rows are stored
+//    row-major and read back transposed (ds_read_b64_tr_b16) into the same
+//    MFMA operand layout (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//  * Double-buffered LDS, one barrier per k-step, prefetch depth 2; the
+//    steady-state loop is one basic block, and full tiles run a copy of it
+//    without masks.
 //  * Grouped (MoE) launches map m-tile slots to experts through a device
 //    prefix of per-expert tile counts: no host sync, idle experts' blocks are
 //    never read.
 //  * Workgroups are renumbered so that each XCD (8 per MI355X, dispatched
-//    round-robin) works on a contiguous run of tiles that share weight tiles
-//    in its own L2.
+//    round-robin) works on a contiguous run of tiles; dense launches order
+//    that run as 4 m-tiles by a band of n-tiles (L2 reuse of both operands).
 //  * Epilogues fold in the rank-r adapter term and the fused consumers
 //    (SwiGLU, the cross-entropy partials, the SwiGLU backward), with row and
 //    column reductions staged through LDS in a fixed order (deterministic).
