@@ -133,6 +133,20 @@ int pick_rc(int64_t M, int64_t C, int r, int E) {
   while (rc < 1024 && cdiv(M, rc * 2) * cb >= 256) rc *= 2;
   return rc;
 }
+// Forward launches with few rows per weight row run the skinny MMQ (each
+// block streamed once per 16/32-row tile with coalesced loads), when its
+// layout conditions hold: K a multiple of 256 (whole 8-block segments) and
+// 16-byte aligned weights.  rows_per_w = rows sharing one weight (tokens, or
+// routed rows per expert on average).
+int pick_fwd_tile(int64_t rows_per_w, int64_t rows_est, int64_t ntiles128, int64_t K,
+                  bool w_aligned) {
+  if (K % 256 == 0 && w_aligned) {
+    if (rows_per_w <= 16) return TILE_SKINNY16;
+    if (rows_per_w <= 32) return TILE_SKINNY32;
+  }
+  return pick_tile(rows_est, ntiles128);
+}
+
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
 hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
@@ -408,8 +422,9 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
   Ws w(ws);
   int32_t* ts = w.take<int32_t>(E + 1);
   int32_t* ts16 = w.take<int32_t>(E + 1);
-  const int ntiles_fwd = epilogue == GQ_EPI_SWIGLU ? cdiv(N, TILE_BN / 2) : cdiv(N, TILE_BN);
-  const int tc = pick_tile(M, ntiles_fwd);
+  const int ncols = epilogue == GQ_EPI_SWIGLU ? 2 * N : N;  // GEMM columns
+  const bool w_al = aligned(P[0].w_blocks, 16) && (nproj < 2 || aligned(P[1].w_blocks, 16));
+  const int tc = pick_fwd_tile(cdiv(M, E), M, cdiv(ncols, TILE_BN), K, w_al);
   HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), ts, 16, ts16, 1, nullptr, st),
           "gq_grouped_mmq_lora_fwd: tiles");
 
@@ -439,11 +454,11 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
   int epi;
   if (epilogue == GQ_EPI_SWIGLU) {
     g.N = 2 * N;
-    g.ntiles = cdiv(N, TILE_BN / 2);
+    g.ntiles = cdiv(2 * N, tile_bn(tc));
     epi = EPI_SWIGLU;
   } else {
     g.N = N;
-    g.ntiles = cdiv(N, TILE_BN);
+    g.ntiles = cdiv(N, tile_bn(tc));
     epi = EPI_LIN;
   }
   g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
@@ -678,7 +693,7 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
   p.nvalid = w.take<float>(64);
   p.xa = w.take<float>(T * r);
   const int nt_v = cdiv(V, TILE_BN);
-  p.tc_fwd = pick_tile(T, nt_v);
+  p.tc_fwd = pick_fwd_tile(T, T, nt_v, H, aligned(L->w_blocks, 16));
   p.part_ml = w.take<float>((int64_t)nt_v * T * 2);
   p.zlab = w.take<float>(T);
   p.term = w.take<float>(T);
@@ -755,7 +770,7 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   g.M = T; g.N = (int)V; g.K = H;
   g.a0 = h; g.lda = H;
   g.w0 = wb; g.w_rowbytes = rowbytes(L); g.w_nb = H / 32; g.w_rows = (int)V; g.w_row0 = 0;
-  g.ntiles = cdiv(V, TILE_BN);
+  g.ntiles = cdiv(V, tile_bn(P.tc_fwd));
   g.mtiles = cdiv(T, tile_bm(P.tc_fwd));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = P.xa;
   g.f0 = P.part_ml; g.f1 = P.zlab; g.labels = labels; g.ignore_index = ignore_index;

@@ -970,8 +970,14 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
 }
 
 template <int QT, int EPI>
+hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st);
+
+template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
+  if constexpr (EPI == EPI_LIN || EPI == EPI_SWIGLU || EPI == EPI_CE_FWD) {
+    if (tile_skinny(tilecfg)) return launch_skinny<QT, EPI>(tile_bm(tilecfg) / 16, a, st);
+  }
   if constexpr (!epi_stages(EPI)) {
     if (tilecfg == TILE_128x128_K2) {
       hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128, 2>), grid, dim3(2 * NTHR), 0, st, a);

@@ -5,13 +5,15 @@ bench.py times.
   output against the full fp64 oracle, both adapter readings.
 * MoE Q4_0 (T 2048, H 2048, 128 experts top-8, I 768): every output against
   the full grouped oracle.
-* MoE 2-bit, Zipf-skewed (T 4096, H 4096, 256 experts top-8, I 1024, r 8):
+* MoE 2-bit, Zipf-skewed (T 4096, H 4096, 256 experts top-8, I 1024, r 8),
+  and the Q4_0 MoE weights at T 16 and T 512 (the small-token sweep):
   routing bit-exact in full; y, dX, dlogits on sampled tokens and the
   adapter gradients of sampled experts (heaviest, median, lightest active,
   idle) from the per-expert oracle, one expert decoded at a time.
-* LM head Q8_0 (T 2048, H 2048, V 151936, 4096-row chunks): loss, lse, dh,
-  dA, dB against the full chunked oracle.
+* LM head Q8_0 (T 2048, H 2048, V 151936, 4096-row chunks), also at T 16
+  and T 32: loss, lse, dh, dA, dB against the full chunked oracle.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -84,8 +86,18 @@ def test_moe_q4_0_full():
         say(f"  {n}: {check(n, host(g[n]), b[n.replace('_', '')]):.2e}")
 
 
-def test_moe_2bit_zipf_sampled():
-    cfg = synth.CFG4
+# the 2-bit workload, and the small-token sweep of the Q4_0 MoE workload at
+# its smallest and largest token counts (skinny forward MMQ, 16- and 32-row
+# tiles)
+SAMPLED_MOE = [
+    synth.CFG4,
+    dataclasses.replace(synth.CFG3, name="moe_q4_0_t16_h2048_e128k8_i768_r4", T=16),
+    dataclasses.replace(synth.CFG3, name="moe_q4_0_t512_h2048_e128k8_i768_r4", T=512),
+]
+
+
+@pytest.mark.parametrize("cfg", SAMPLED_MOE, ids=lambda c: c.name)
+def test_moe_sampled(cfg):
     say("fullsize moe", cfg.name)
     inp = synth.make_moe(cfg)
     T, k, E = cfg.T, cfg.k, cfg.E
@@ -139,8 +151,15 @@ def test_moe_2bit_zipf_sampled():
         assert np.all(host(g[n][idle]) == 0.0), n
 
 
-def test_lmhead_full():
-    cfg = synth.CFG5
+HEAD_FULL = [
+    synth.CFG5,
+    dataclasses.replace(synth.CFG5, name="lmhead_q8_0_t16_h2048_v151936_r4", T=16),
+    dataclasses.replace(synth.CFG5, name="lmhead_q8_0_t32_h2048_v151936_r4", T=32),
+]
+
+
+@pytest.mark.parametrize("cfg", HEAD_FULL, ids=lambda c: c.name)
+def test_lmhead_full(cfg):
     say("fullsize lmhead", cfg.name)
     inp = synth.make_head(cfg)
     head = gq.Proj(cfg.qtype, cfg.V, cfg.H, u8_dev(inp["blocks"]), f32_dev(inp["A"]),

@@ -187,6 +187,13 @@ MOE_CASES = [
     (100, 128, 128, 8, 2, 0, 4, 0.0),
     (257, 256, 192, 16, 4, 2, 8, 1.0),
     (64, 128, 64, 32, 8, 1, 4, 1.0),  # many idle experts
+    # few rows per expert, K % 256 == 0: the skinny forward MMQ (16-row tiles,
+    # 32-row tiles in the last case); in the first only the down projection
+    # (K = I = 256) runs skinny, on a ragged last column tile (H = 320)
+    (40, 320, 256, 8, 2, 0, 4, 1.0),
+    (48, 512, 256, 8, 2, 1, 4, 1.0),
+    (30, 256, 256, 4, 2, 2, 8, 0.0),
+    (64, 256, 256, 4, 2, 1, 4, 0.5),
 ]
 
 
@@ -229,6 +236,10 @@ HEAD_CASES = [
     (130, 128, 1000, 384, 1, 0.2),
     (64, 256, 4096, 4096, 2, 0.0),
     (200, 192, 3000, 1024, 0, 0.1),
+    # T <= 32 with H % 256 == 0: the skinny logits pass; ragged vocabulary tile
+    (16, 256, 1000, 1000, 0, 0.1),
+    (30, 512, 3000, 1024, 1, 0.0),
+    (7, 256, 712, 712, 2, 0.2),
 ]
 
 
