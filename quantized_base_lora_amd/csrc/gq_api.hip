@@ -134,17 +134,18 @@ int pick_rc(int64_t M, int64_t C, int r, int E) {
   return rc;
 }
 // Forward launches with few rows per weight row run the skinny MMQ (each
-// block streamed once per 16/32-row tile with coalesced loads), when its
+// block streamed once per 16/32/64-row tile with coalesced loads), when its
 // layout conditions hold: K a multiple of 256 (whole 8-block segments) and
 // 16-byte aligned weights.  rows_per_w = rows sharing one weight (tokens, or
 // routed rows per expert on average).
 int pick_fwd_tile(int64_t rows_per_w, int64_t rows_est, int64_t ntiles128, int64_t K,
-                  bool w_aligned) {
+                  bool w_aligned, bool k2ok = false) {
   if (K % 256 == 0 && w_aligned) {
     if (rows_per_w <= 16) return TILE_SKINNY16;
     if (rows_per_w <= 32) return TILE_SKINNY32;
+    if (rows_per_w <= 64) return TILE_SKINNY64;
   }
-  return pick_tile(rows_est, ntiles128);
+  return pick_tile(rows_est, ntiles128, K, k2ok);
 }
 
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
@@ -213,7 +214,7 @@ int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, ui
   g.w0 = static_cast<const uint8_t*>(L->w_blocks);
   g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
   g.ntiles = cdiv(N, TILE_BN);
-  const int tc = pick_tile(T, g.ntiles, K, true);
+  const int tc = pick_fwd_tile(T, T, g.ntiles, K, aligned(L->w_blocks, 16), true);
   g.mtiles = cdiv(T, tile_bm(tc));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
   g.o0 = y; g.ldo = N;

@@ -87,14 +87,16 @@ struct GemmArgs {
 // TILE_128x128_K2: 128x128 tiles computed by 512 threads, two groups of four
 // waves taking alternate k-steps (split-K inside the workgroup), reduced in
 // LDS; only for the epilogues that do not stage through LDS.
-// TILE_SKINNY{16,32}: the forward-only skinny MMQ for few rows per weight
-// (16 or 32 rows per tile, 128 weight rows per workgroup; K % 256 == 0).
+// TILE_SKINNY{16,32,64}: the forward-only skinny MMQ for few rows per
+// weight (16, 32 or 64 rows per tile, 128 weight rows per workgroup;
+// K % 256 == 0).
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,
   TILE_128x128_K2 = 2,
   TILE_SKINNY16 = 3,
-  TILE_SKINNY32 = 4
+  TILE_SKINNY32 = 4,
+  TILE_SKINNY64 = 5
 };
 
 inline bool tile_skinny(int cfg) { return cfg >= TILE_SKINNY16; }
@@ -103,6 +105,7 @@ inline int tile_bm(int cfg) {
     case TILE_64x128: return 64;
     case TILE_SKINNY16: return 16;
     case TILE_SKINNY32: return 32;
+    case TILE_SKINNY64: return 64;
     default: return 128;
   }
 }

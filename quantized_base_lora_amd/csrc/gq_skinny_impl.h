@@ -299,9 +299,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
       }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // up waves hand their values to the gate waves of the same indices
-    __syncthreads();  // every wave is done with its LDS weight region
-    float* xch = reinterpret_cast<float*>(&lds_w[0][0]);
-    static_assert(4 * 64 * 4 * RG * sizeof(float) <= sizeof(lds_w), "exchange fits");
+    __syncthreads();  // every wave is done with the activation tiles
+    float* xch = reinterpret_cast<float*>(&lds_x[0][0]);
+    static_assert(4 * 64 * 4 * RG * sizeof(float) <= XBUF, "exchange fits");
     if (wave >= 4) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -380,8 +380,10 @@ hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(64 * SK_WAVES);
   if (rg == 1)
     hipLaunchKernelGGL((skinny_kernel<QT, EPI, 1>), grid, block, 0, st, a);
-  else
+  else if (rg == 2)
     hipLaunchKernelGGL((skinny_kernel<QT, EPI, 2>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<QT, EPI, 4>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,9 @@ def lin_proj(inp):
 LIN_CASES = [
     (1, 64, 8, 0, 1), (5, 128, 96, 1, 2), (129, 256, 200, 2, 4), (128, 1024, 1024, 0, 4),
     (300, 512, 520, 1, 8), (77, 192, 136, 2, 16),
+    # T <= 64, K % 256 == 0: the skinny forward MMQ with 16-, 32- and 64-row
+    # tiles, ragged last column tile
+    (9, 256, 200, 0, 4), (20, 512, 264, 1, 8), (33, 256, 136, 2, 4), (64, 512, 128, 1, 16),
 ]
 
 
