@@ -225,7 +225,8 @@ int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, ui
 namespace {
 struct LinBwdWs {
   float* dyB;
-  float* part;
+  float* part_dB;
+  float* part_dA;
 };
 int lin_rc(const gq_lora_linear* L, int64_t T) {
   return pick_rc(T, L->n_in > L->n_out ? L->n_in : L->n_out, L->rank, 1);
@@ -233,9 +234,9 @@ int lin_rc(const gq_lora_linear* L, int64_t T) {
 LinBwdWs plan_lin_bwd(Ws& w, const gq_lora_linear* L, int64_t T) {
   LinBwdWs p;
   const int64_t slots = colred_slots(T, lin_rc(L, T), 1);
-  const int64_t cmax = L->n_in > L->n_out ? L->n_in : L->n_out;
   p.dyB = w.take<float>(T * L->rank);
-  p.part = w.take<float>(slots * cmax * L->rank);
+  p.part_dB = w.take<float>(slots * L->n_out * L->rank);
+  p.part_dA = w.take<float>(slots * L->n_in * L->rank);
   return p;
 }
 }  // namespace
@@ -279,13 +280,21 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
   rd.W[0] = L->B; rd.w_jstride = 1; rd.w_cstride = r; rd.out[0] = P.dyB; rd.nout = 1;
   HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_bwd: dY B");
 
+  // dB = s dY^T xa and dA = s (dY B)^T x: both reductions in one launch,
+  // both finishes in one launch
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
   cr.M = T; cr.C = N; cr.r = r; cr.U = dy; cr.ldu = N; cr.gdiv = 1; cr.Vv = xa;
-  cr.E = 1; cr.rc = rcl; cr.slots = slots; cr.part = P.part;
-  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB partials");
-  HIP_TRY(launch_colred_finish(P.part, nullptr, 1, slots, N, r, L->scale, 0, dB, st),
-          "gq_linear_lora_bwd: dB");
+  cr.E = 1; cr.rc = rcl; cr.slots = slots; cr.part = P.part_dB;
+  cr.njobs = 2;
+  cr.C_1 = K; cr.U_1 = x; cr.ldu_1 = K; cr.gdiv_1 = 1; cr.Vv_1 = P.dyB; cr.part_1 = P.part_dA;
+  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB, dA partials");
+  ColFinJobs fj;
+  memset(&fj, 0, sizeof fj);
+  fj.n = 2;
+  fj.part[0] = P.part_dB; fj.out[0] = dB; fj.C[0] = N; fj.transpose[0] = 0;
+  fj.part[1] = P.part_dA; fj.out[1] = dA; fj.C[1] = K; fj.transpose[1] = 1;
+  HIP_TRY(launch_colred_finish_dense(fj, slots, r, L->scale, st), "gq_linear_lora_bwd: dB, dA");
 
   if (dx) {
     GemmArgs g = gemm_defaults();
@@ -300,11 +309,6 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
     g.o0 = dx; g.ldo = K;
     HIP_TRY(launch_gemm(L->qtype, EPI_LIN_BWD, tc, g, st), "gq_linear_lora_bwd: dX MMQ");
   }
-
-  cr.C = K; cr.U = x; cr.ldu = K; cr.Vv = P.dyB;
-  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dA partials");
-  HIP_TRY(launch_colred_finish(P.part, nullptr, 1, slots, K, r, L->scale, 1, dA, st),
-          "gq_linear_lora_bwd: dA");
   return GQ_OK;
 }
 
@@ -476,7 +480,7 @@ struct GrpBwdWs {
   float* wdyB;
   float* wxa;
   float* part_down;
-  float* part;
+  float* part[4];  // colred partials, one set per adapter gradient
 };
 int grp_rc(const gq_lora_linear* P, int64_t M) {
   const int64_t H = P[0].n_in > P[0].n_out ? P[0].n_in : P[0].n_out;
@@ -496,10 +500,14 @@ GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
     p.wdyB = w.take<float>(M * r);
     p.wxa = w.take<float>(M * r);
     p.part_down = w.take<float>((int64_t)cdiv(I, TILE_BN) * M * (1 + 2 * r));
-    p.part = w.take<float>(slots * (H > I ? H : I) * r);
+    p.part[0] = w.take<float>(slots * I * r);  // dA_d
+    p.part[1] = w.take<float>(slots * H * r);  // dB_d
   } else {
     const int64_t H = P[0].n_in, I = P[0].n_out;
-    p.part = w.take<float>(slots * (H > I ? H : I) * r);
+    p.part[0] = w.take<float>(slots * H * r);  // dA_g
+    p.part[1] = w.take<float>(slots * H * r);  // dA_u
+    p.part[2] = w.take<float>(slots * I * r);  // dB_g
+    p.part[3] = w.take<float>(slots * I * r);  // dB_u
   }
   return p;
 }
@@ -575,7 +583,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
   cr.M = M; cr.r = r; cr.offsets = a->offsets; cr.chunk_start = W.cs; cr.E = E; cr.rc = rcg;
-  cr.slots = slots; cr.part = W.part; cr.gdiv = 1;
+  cr.slots = slots; cr.gdiv = 1;
 
   if (mode == GQ_BWD_DOWN_SWIGLU) {
     const int H = (int)P[0].n_out, I = (int)P[0].n_in;
@@ -614,14 +622,19 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     HIP_TRY(launch_down_finish(W.part_down, g.ntiles, M, r, a->sorted, a->dw_flat, a->dgB, a->duB, st),
             "gq_grouped_mmq_lora_bwd: dw, dgB, duB");
 
-    // dA_d[e] = s sum_p (w dY Bd)^T h ;  dB_d[e] = s sum_p dY^T (w xa_d)
-    cr.C = I; cr.U = a->h; cr.ldu = I; cr.Vv = W.wdyB;
-    HIP_TRY(launch_colred(cr, st), "dA_d partials");
-    HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 1, a->dA_d, st), "dA_d");
-    cr.C = H; cr.U = a->dy; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;
-    cr.Vv = W.wxa;
-    HIP_TRY(launch_colred(cr, st), "dB_d partials");
-    HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 0, a->dB_d, st), "dB_d");
+    // dA_d[e] = s sum_p (w dY Bd)^T h ;  dB_d[e] = s sum_p dY^T (w xa_d):
+    // both reductions in one launch, both finishes in one launch
+    cr.C = I; cr.U = a->h; cr.ldu = I; cr.Vv = W.wdyB; cr.part = W.part[0];
+    cr.njobs = 2;
+    cr.C_1 = H; cr.U_1 = a->dy; cr.ldu_1 = H; cr.gather_1 = a->gather; cr.gdiv_1 = a->gather_div;
+    cr.Vv_1 = W.wxa; cr.part_1 = W.part[1];
+    HIP_TRY(launch_colred(cr, st), "dA_d, dB_d partials");
+    ColFinJobs fj;
+    memset(&fj, 0, sizeof fj);
+    fj.n = 2;
+    fj.part[0] = W.part[0]; fj.out[0] = a->dA_d; fj.C[0] = I; fj.transpose[0] = 1;
+    fj.part[1] = W.part[1]; fj.out[1] = a->dB_d; fj.C[1] = H; fj.transpose[1] = 0;
+    HIP_TRY(launch_colred_finish_grp(fj, W.cs, E, r, s, st), "dA_d, dB_d");
     return GQ_OK;
   }
 
@@ -650,19 +663,27 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     return fail(GQ_ENOTSUP, "gq_grouped_mmq_lora_bwd: intermediate size must be a multiple of 64");
   HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: gate/up MMQ");
 
+  // dA_g and dA_u in one pass over the gathered x rows
   cr.C = H; cr.U = a->x; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;
-  cr.Vv = a->dgB;
-  HIP_TRY(launch_colred(cr, st), "dA_g partials");
-  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 1, a->dA_g, st), "dA_g");
-  cr.Vv = a->duB;
-  HIP_TRY(launch_colred(cr, st), "dA_u partials");
-  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, H, r, s, 1, a->dA_u, st), "dA_u");
+  cr.Vv = a->dgB; cr.part = W.part[0];
+  cr.Vv2 = a->duB; cr.part2 = W.part[1];
+  HIP_TRY(launch_colred(cr, st), "dA_g, dA_u partials");
+  // dB_g and dB_u in one launch
+  cr.Vv2 = nullptr; cr.part2 = nullptr;
   cr.C = I; cr.U = a->dg; cr.ldu = I; cr.gather = nullptr; cr.gdiv = 1; cr.Vv = a->xa;
-  HIP_TRY(launch_colred(cr, st), "dB_g partials");
-  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 0, a->dB_g, st), "dB_g");
-  cr.U = a->du; cr.Vv = a->xa + M * r;
-  HIP_TRY(launch_colred(cr, st), "dB_u partials");
-  HIP_TRY(launch_colred_finish(W.part, W.cs, E, 0, I, r, s, 0, a->dB_u, st), "dB_u");
+  cr.part = W.part[2];
+  cr.njobs = 2;
+  cr.C_1 = I; cr.U_1 = a->du; cr.ldu_1 = I; cr.gather_1 = nullptr; cr.gdiv_1 = 1;
+  cr.Vv_1 = a->xa + M * r; cr.part_1 = W.part[3];
+  HIP_TRY(launch_colred(cr, st), "dB_g, dB_u partials");
+  ColFinJobs fj;
+  memset(&fj, 0, sizeof fj);
+  fj.n = 4;
+  fj.part[0] = W.part[0]; fj.out[0] = a->dA_g; fj.C[0] = H; fj.transpose[0] = 1;
+  fj.part[1] = W.part[1]; fj.out[1] = a->dA_u; fj.C[1] = H; fj.transpose[1] = 1;
+  fj.part[2] = W.part[2]; fj.out[2] = a->dB_g; fj.C[2] = I; fj.transpose[2] = 0;
+  fj.part[3] = W.part[3]; fj.out[3] = a->dB_u; fj.C[3] = I; fj.transpose[3] = 0;
+  HIP_TRY(launch_colred_finish_grp(fj, W.cs, E, r, s, st), "dA_g, dA_u, dB_g, dB_u");
   return GQ_OK;
 }
 

@@ -174,10 +174,40 @@ struct ColRedArgs {
   int32_t rc;
   int32_t slots;
   float* part;              // [slots][C][r]
+  // optional second rank-vector array over the same U (one pass, two
+  // partial sets); only with njobs <= 1
+  const float* Vv2;
+  float* part2;
+  // optional second independent reduction in the same launch (blockIdx.z
+  // == 1) over the same rows and slots: its own U, C, gather and V
+  int32_t njobs;            // 0 or 1: one job
+  int32_t C_1;
+  const uint16_t* U_1;
+  int64_t ldu_1;
+  const int32_t* gather_1;
+  int32_t gdiv_1;
+  const float* Vv_1;
+  float* part_1;
 };
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st);
 // columns covered by one launch_colred workgroup
 int colred_cols_per_block(int r);
+
+// Up to four grouped finishes in one launch (blockIdx.z = job): out[j] =
+// s * sum over an expert's slots (in order) of part[j], as
+// launch_colred_finish with chunk_start.
+struct ColFinJobs {
+  int32_t n;
+  const float* part[4];
+  float* out[4];
+  int32_t C[4];
+  int32_t transpose[4];
+};
+hipError_t launch_colred_finish_grp(const ColFinJobs& j, const int32_t* chunk_start, int32_t E,
+                                    int32_t r, float s, hipStream_t st);
+// Up to four dense finishes (one group of nslots slots) in one launch.
+hipError_t launch_colred_finish_dense(const ColFinJobs& j, int32_t nslots, int32_t r, float s,
+                                      hipStream_t st);
 
 // out = s * sum over an expert's slots (in order) of part; experts with no
 // rows get zeros.  transpose: out[e][j][c] instead of out[e][c][j].

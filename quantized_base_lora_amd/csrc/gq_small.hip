@@ -12,6 +12,7 @@
 //  * the sparse combine of the experts' outputs and its backward
 //  * the online log-sum-exp merge of the chunked cross entropy
 #include <math.h>
+#include <string.h>
 
 #include "gq_dev.h"
 #include "gq_internal.h"
@@ -220,14 +221,25 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
 // one slot and 64*CPT columns: every lane owns CPT adjacent columns (one 16-
 // or 8-byte load per row, a wave reads a contiguous row segment), the four
 // waves take every fourth row, and the wave partials are added in wave
-// order through LDS.
-template <int R, int CPT>
+// order through LDS.  NV = 2: a second rank-vector array V2 over the same U
+// rows (one pass over U for two reductions).  blockIdx.z picks one of two
+// independent jobs sharing the launch (same rows and slots).
+template <int R, int CPT, int NV>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   __shared__ float red[3][64][CPT][R];
+  const bool z1 = blockIdx.z == 1;
+  const int32_t C = z1 ? a.C_1 : a.C;
+  const uint16_t* const U = z1 ? a.U_1 : a.U;
+  const int64_t ldu = z1 ? a.ldu_1 : a.ldu;
+  const int32_t* const gather = z1 ? a.gather_1 : a.gather;
+  const int32_t gdiv = z1 ? a.gdiv_1 : a.gdiv;
+  const float* const Vv = z1 ? a.Vv_1 : a.Vv;
+  float* const part = z1 ? a.part_1 : a.part;
   const int slot = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = ((int64_t)blockIdx.y * 64 + lane) * CPT;
+  if ((int64_t)blockIdx.y * 64 * CPT >= C) return;  // this job has fewer columns
   int64_t r0, r1;
   if (a.offsets) {
     const int32_t* cs = a.chunk_start;
@@ -239,19 +251,21 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     r0 = (int64_t)slot * a.rc;
     r1 = min(a.M, r0 + a.rc);
   }
-  const bool cok = c < a.C;
+  const bool cok = c < C;
   const int64_t cc = cok ? c : 0;  // clamped: loads stay in bounds
   const int r = a.r;
-  float acc[CPT][R];
+  float acc[NV][CPT][R];
 #pragma unroll
-  for (int t = 0; t < CPT; ++t)
+  for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
+    for (int t = 0; t < CPT; ++t)
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[v][t][j] = 0.f;
   // rows r0 + wave + 4i; UNR rows' loads are issued together
   constexpr int UNR = 8;
   for (int64_t pb = r0 + wave; pb < r1; pb += 4 * UNR) {
     uint32_t rw[UNR][CPT / 2];
-    float vv[UNR][R];
+    float vv[UNR][NV][R];
     bool ok[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -259,8 +273,8 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
       const bool pok = p < r1;  // wave-uniform
       ok[u] = pok && cok;
       const int64_t pc = pok ? p : r0;
-      const int64_t src = a.gather ? (int64_t)(a.gather[pc] / a.gdiv) : pc;
-      const uint16_t* up = a.U + src * a.ldu + cc;
+      const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
+      const uint16_t* up = U + src * ldu + cc;
       if constexpr (CPT == 8) {
         const uint4 raw = *reinterpret_cast<const uint4*>(up);
         rw[u][0] = raw.x; rw[u][1] = raw.y; rw[u][2] = raw.z; rw[u][3] = raw.w;
@@ -268,9 +282,12 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
         const uint2 raw = *reinterpret_cast<const uint2*>(up);
         rw[u][0] = raw.x; rw[u][1] = raw.y;
       }
-      const float* v = a.Vv + pc * r;
 #pragma unroll
-      for (int j = 0; j < R; ++j) vv[u][j] = (pok && j < r) ? v[j] : 0.f;
+      for (int v = 0; v < NV; ++v) {
+        const float* vp = (v == 0 ? Vv : a.Vv2) + pc * r;
+#pragma unroll
+        for (int j = 0; j < R; ++j) vv[u][v][j] = (pok && j < r) ? vp[j] : 0.f;
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -282,26 +299,33 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
         uv[2 * t + 1] = bf2f((uint16_t)(w >> 16));
       }
 #pragma unroll
-      for (int t = 0; t < CPT; ++t)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[t][j] += uv[t] * vv[u][j];
+        for (int t = 0; t < CPT; ++t)
+#pragma unroll
+          for (int j = 0; j < R; ++j) acc[v][t][j] += uv[t] * vv[u][v][j];
     }
   }
-  if (wave > 0) {
+  // wave partials added in wave order, one rank-vector set at a time
 #pragma unroll
-    for (int t = 0; t < CPT; ++t)
+  for (int v = 0; v < NV; ++v) {
+    if (v > 0) __syncthreads();  // wave 0 is done reading the previous set
+    if (wave > 0) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) red[wave - 1][lane][t][j] = acc[t][j];
-  }
-  __syncthreads();
-  if (wave == 0 && cok) {
-    float* dst = a.part + ((int64_t)slot * a.C + c) * r;
+      for (int t = 0; t < CPT; ++t)
 #pragma unroll
-    for (int t = 0; t < CPT; ++t)
+        for (int j = 0; j < R; ++j) red[wave - 1][lane][t][j] = acc[v][t][j];
+    }
+    __syncthreads();
+    if (wave == 0 && cok) {
+      float* dst = (v == 0 ? part : a.part2) + ((int64_t)slot * C + c) * r;
 #pragma unroll
-      for (int j = 0; j < R; ++j)
-        if (j < r)
-          dst[t * r + j] = acc[t][j] + red[0][lane][t][j] + red[1][lane][t][j] + red[2][lane][t][j];
+      for (int t = 0; t < CPT; ++t)
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (j < r)
+            dst[t * r + j] = acc[v][t][j] + red[0][lane][t][j] + red[1][lane][t][j] + red[2][lane][t][j];
+    }
   }
 }
 
@@ -310,23 +334,21 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
 // ... in order, and the SL lane sums are added in lane order through LDS
 // (deterministic), so many slots are read with many loads in flight.
 template <int SL>
-__global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restrict__ part,
-                                                            const int32_t* __restrict__ cs,
-                                                            int32_t nslots_dense, int32_t C,
-                                                            int32_t r, float s, int transpose,
-                                                            float* __restrict__ out) {
+__global__ __launch_bounds__(256) void colred_finish_kernel(const ColFinJobs jb,
+                                                            int32_t nslots, int32_t r, float s) {
   constexpr int NO = 256 / SL;
   __shared__ float red[SL][NO];
-  const int e = blockIdx.y;
+  const int z = blockIdx.z;
+  const int32_t C = jb.C[z];
+  const float* __restrict__ part = jb.part[z];
   const int oi = threadIdx.x % NO, g = threadIdx.x / NO;
   const int64_t n = (int64_t)C * r;
   const int64_t i = (int64_t)blockIdx.x * NO + oi;
-  const int s0 = cs ? cs[e] : 0;
-  const int s1 = cs ? cs[e + 1] : nslots_dense;
+  if ((int64_t)blockIdx.x * NO >= n) return;  // this job has fewer outputs
   float acc = 0.f;
   if (i < n) {
 #pragma unroll 4
-    for (int sl = s0 + g; sl < s1; sl += SL) acc += part[(int64_t)sl * n + i];
+    for (int sl = g; sl < nslots; sl += SL) acc += part[(int64_t)sl * n + i];
   }
   red[g][oi] = acc;
   __syncthreads();
@@ -335,11 +357,10 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
 #pragma unroll
     for (int k = 1; k < SL; ++k) t += red[k][oi];
     const int64_t c = i / r, jj = i % r;
-    float* o = out + (int64_t)e * n;
-    if (transpose)
-      o[jj * C + c] = s * t;
+    if (jb.transpose[z])
+      jb.out[z][jj * C + c] = s * t;
     else
-      o[i] = s * t;
+      jb.out[z][i] = s * t;
   }
 }
 
@@ -414,17 +435,21 @@ __global__ void route_hist_kernel(const int32_t* __restrict__ ids, int64_t n, in
 }
 
 // one block of 1024 threads: per-expert running bases over chunks, then the
-// exclusive scan over experts
+// exclusive scan over experts.  The chunk counts of an expert are read 8 at a
+// time (independent loads in flight) in both passes.
 __global__ void route_scan_kernel(int32_t* __restrict__ counts, int32_t nchunks, int32_t E,
                                   int32_t* __restrict__ offsets) {
   __shared__ int32_t sh[1024];
+  constexpr int G = 8;
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = counts[(int64_t)c * E + e];
-      counts[(int64_t)c * E + e] = tot;
-      tot += v;
+    for (int c0 = 0; c0 < nchunks; c0 += G) {
+      int v[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[i] = c0 + i < nchunks ? counts[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < G; ++i) tot += v[i];
     }
   }
   sh[e] = tot;
@@ -438,7 +463,17 @@ __global__ void route_scan_kernel(int32_t* __restrict__ counts, int32_t nchunks,
   const int excl = sh[e] - tot;
   if (e < E) {
     offsets[e] = excl;
-    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += excl;
+    int run = excl;
+    for (int c0 = 0; c0 < nchunks; c0 += G) {
+      int v[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[i] = c0 + i < nchunks ? counts[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (c0 + i < nchunks) counts[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
   }
   if (e == 0) offsets[E] = sh[1023];
 }
@@ -705,22 +740,34 @@ int colred_cols_per_block(int r) { return r <= 8 ? 512 : 256; }
 
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   if (a.slots == 0) return hipSuccess;
-  const dim3 g((unsigned)a.slots, blocks_for(a.C, colred_cols_per_block(a.r))), b(256);
-  if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8>), g, b, 0, st, a);
-  else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8>), g, b, 0, st, a);
-  else hipLaunchKernelGGL((colred_kernel<16, 4>), g, b, 0, st, a);
+  const bool two = a.njobs == 2;
+  const int32_t cmax = two && a.C_1 > a.C ? a.C_1 : a.C;
+  const dim3 g((unsigned)a.slots, blocks_for(cmax, colred_cols_per_block(a.r)), two ? 2 : 1),
+      b(256);
+  if (a.Vv2) {
+    if (two) return hipErrorInvalidValue;
+    if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8, 2>), g, b, 0, st, a);
+    else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8, 2>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((colred_kernel<16, 4, 2>), g, b, 0, st, a);
+  } else {
+    if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8, 1>), g, b, 0, st, a);
+    else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8, 1>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((colred_kernel<16, 4, 1>), g, b, 0, st, a);
+  }
   return hipGetLastError();
 }
 
 // Grouped finish: out[e] = s * sum of expert e's slots, in slot order.  A
 // thread owns four consecutive outputs (one 16-byte load per slot); experts
-// with no slots get zeros.
-__global__ __launch_bounds__(256) void colred_finish_grp_kernel(const float* __restrict__ part,
+// with no slots get zeros.  blockIdx.z = job.
+__global__ __launch_bounds__(256) void colred_finish_grp_kernel(const ColFinJobs jb,
                                                                 const int32_t* __restrict__ cs,
-                                                                int32_t C, int32_t r, float s,
-                                                                int transpose,
-                                                                float* __restrict__ out) {
+                                                                int32_t r, float s) {
+  const int z = blockIdx.z;
   const int e = blockIdx.y;
+  const int32_t C = jb.C[z];
+  const float* __restrict__ part = jb.part[z];
+  const int transpose = jb.transpose[z];
   const int64_t n = (int64_t)C * r;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
@@ -732,7 +779,7 @@ __global__ __launch_bounds__(256) void colred_finish_grp_kernel(const float* __r
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
   const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
-  float* o = out + (int64_t)e * n;
+  float* o = jb.out[z] + (int64_t)e * n;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t ii = i + q;
@@ -743,25 +790,49 @@ __global__ __launch_bounds__(256) void colred_finish_grp_kernel(const float* __r
   }
 }
 
+hipError_t launch_colred_finish_grp(const ColFinJobs& j, const int32_t* chunk_start, int32_t E,
+                                    int32_t r, float s, hipStream_t st) {
+  if (j.n < 1 || j.n > 4) return hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int z = 0; z < j.n; ++z) {
+    const int64_t n = (int64_t)j.C[z] * r;  // a multiple of 4: C % 8 == 0
+    if (n > nmax) nmax = n;
+  }
+  const dim3 g(blocks_for(nmax, 1024), (unsigned)E, (unsigned)j.n), b(256);
+  hipLaunchKernelGGL(colred_finish_grp_kernel, g, b, 0, st, j, chunk_start, r, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_colred_finish(const float* part, const int32_t* chunk_start, int32_t E,
                                 int32_t nslots_dense, int32_t C, int32_t r, float s, int transpose,
                                 float* out, hipStream_t st) {
   if (chunk_start) {
-    const int64_t n = (int64_t)C * r;  // a multiple of 4: C % 8 == 0
-    const dim3 g(blocks_for(n, 1024), (unsigned)E), b(256);
-    hipLaunchKernelGGL(colred_finish_grp_kernel, g, b, 0, st, part, chunk_start, C, r, s, transpose,
-                       out);
-    return hipGetLastError();
+    ColFinJobs j;
+    memset(&j, 0, sizeof j);
+    j.n = 1; j.part[0] = part; j.out[0] = out; j.C[0] = C; j.transpose[0] = transpose;
+    return launch_colred_finish_grp(j, chunk_start, E, r, s, st);
   }
-  // many slots per output (dense, long reductions): 32 slot lanes
-  if (nslots_dense > 64) {
-    const dim3 g(blocks_for((int64_t)C * r, 8), (unsigned)E), b(256);
-    hipLaunchKernelGGL(colred_finish_kernel<32>, g, b, 0, st, part, chunk_start, nslots_dense, C, r,
-                       s, transpose, out);
+  ColFinJobs j;
+  memset(&j, 0, sizeof j);
+  j.n = 1; j.part[0] = part; j.out[0] = out; j.C[0] = C; j.transpose[0] = transpose;
+  return launch_colred_finish_dense(j, nslots_dense, r, s, st);
+}
+
+hipError_t launch_colred_finish_dense(const ColFinJobs& j, int32_t nslots, int32_t r, float s,
+                                      hipStream_t st) {
+  if (j.n < 1 || j.n > 4) return hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int z = 0; z < j.n; ++z) {
+    const int64_t n = (int64_t)j.C[z] * r;
+    if (n > nmax) nmax = n;
+  }
+  // many slots per output (long reductions): 32 slot lanes
+  if (nslots > 64) {
+    const dim3 g(blocks_for(nmax, 8), 1, (unsigned)j.n), b(256);
+    hipLaunchKernelGGL(colred_finish_kernel<32>, g, b, 0, st, j, nslots, r, s);
   } else {
-    const dim3 g(blocks_for((int64_t)C * r, 32), (unsigned)E), b(256);
-    hipLaunchKernelGGL(colred_finish_kernel<8>, g, b, 0, st, part, chunk_start, nslots_dense, C, r,
-                       s, transpose, out);
+    const dim3 g(blocks_for(nmax, 32), 1, (unsigned)j.n), b(256);
+    hipLaunchKernelGGL(colred_finish_kernel<8>, g, b, 0, st, j, nslots, r, s);
   }
   return hipGetLastError();
 }
