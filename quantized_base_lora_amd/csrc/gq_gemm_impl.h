@@ -181,6 +181,21 @@ __device__ __forceinline__ void z_col_reduce(float* Z, const float* X, int r, in
   __syncthreads();
 }
 
+// Instruction interleave for the steady-state k-step: LEAD LDS reads first
+// (the first MFMA operands), then per MFMA NV VALU ops (the decode of the
+// next tile) and ND LDS ops, so the decode issues in the shadow of the
+// matrix cores instead of in clusters (measured ~10% on the dense forward).
+template <int NM, int NV, int ND, int LEAD>
+__device__ __forceinline__ void mfma_interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    __builtin_amdgcn_sched_group_barrier(0x080, ND, 0);
+  }
+}
+
 template <int QT, int EPI, int BM, int BN, int KS>
 __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
     const GemmArgs p) {
@@ -474,6 +489,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       compute(0);
       store_a(1, areg1, amsk1);
       store_w(1, wr1, wmsk1);
+      mfma_interleave<TM * TN * (BK / 16), 6, 2, 8>();
       __syncthreads();
       load_a(KT(kt + 3), areg1, amsk1);
       load_w(KT(kt + 3), wr1, wmsk1);
@@ -481,6 +497,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       compute(1);
       store_a(0, areg0, amsk0);
       store_w(0, wr0, wmsk0);
+      mfma_interleave<TM * TN * (BK / 16), 6, 2, 8>();
       __syncthreads();
     }
     // tail: tiles kt .. nkl-1 (at most three)

@@ -217,6 +217,7 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
 }
 
 // ---------------------------------------------------- column reductions
+template <bool B> struct BoolC2 { static constexpr bool value = B; };
 // part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j].  A block owns
 // one slot and 64*CPT columns: every lane owns CPT adjacent columns (one 16-
 // or 8-byte load per row, a wave reads a contiguous row segment), the four
@@ -261,51 +262,78 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     for (int t = 0; t < CPT; ++t)
 #pragma unroll
       for (int j = 0; j < R; ++j) acc[v][t][j] = 0.f;
-  // rows r0 + wave + 4i; UNR rows' loads are issued together
-  constexpr int UNR = 8;
-  for (int64_t pb = r0 + wave; pb < r1; pb += 4 * UNR) {
-    uint32_t rw[UNR][CPT / 2];
-    float vv[UNR][NV][R];
-    bool ok[UNR];
+  // rows r0 + wave + 4i; UNR rows' loads are issued together.  Two copies
+  // of the loop: r == R (rank vectors read with whole 16-byte loads, no
+  // per-element branches) and r < R.
+  int vzero = 0;
+  asm volatile("" : "+v"(vzero));  // a VGPR zero: vector address below
+  auto rows = [&](auto fullr) {
+    // rows r0 + wave + 4i; UNR rows' loads are issued together
+    constexpr int UNR = NV * R >= 16 ? 4 : 8;
+    for (int64_t pb = r0 + wave; pb < r1; pb += 4 * UNR) {
+      uint32_t rw[UNR][CPT / 2];
+      float vv[UNR][NV][R];
+      bool ok[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t p = pb + 4 * u;
-      const bool pok = p < r1;  // wave-uniform
-      ok[u] = pok && cok;
-      const int64_t pc = pok ? p : r0;
-      const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
-      const uint16_t* up = U + src * ldu + cc;
-      if constexpr (CPT == 8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(up);
-        rw[u][0] = raw.x; rw[u][1] = raw.y; rw[u][2] = raw.z; rw[u][3] = raw.w;
-      } else {
-        const uint2 raw = *reinterpret_cast<const uint2*>(up);
-        rw[u][0] = raw.x; rw[u][1] = raw.y;
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t p = pb + 4 * u;
+        const bool pok = p < r1;  // wave-uniform
+        ok[u] = pok && cok;
+        const int64_t pc = pok ? p : r0;
+        const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
+        const uint16_t* up = U + src * ldu + cc;
+        if constexpr (CPT == 8) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(up);
+          rw[u][0] = raw.x; rw[u][1] = raw.y; rw[u][2] = raw.z; rw[u][3] = raw.w;
+        } else {
+          const uint2 raw = *reinterpret_cast<const uint2*>(up);
+          rw[u][0] = raw.x; rw[u][1] = raw.y;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          // the row's rank vector (wave-uniform): whole 16-byte loads when
+          // r == R, no per-element branches
+          const float* vp = (v == 0 ? Vv : a.Vv2) + pc * r;
+          if constexpr (decltype(fullr)::value) {
+            // vector loads (every lane the same address) keep the values in
+            // VGPRs: as scalar loads they overflow the SGPRs
+            const float4* vp4 = reinterpret_cast<const float4*>(vp) + vzero;
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q) {
+              const float4 f = vp4[q];
+              vv[u][v][4 * q] = pok ? f.x : 0.f;
+              vv[u][v][4 * q + 1] = pok ? f.y : 0.f;
+              vv[u][v][4 * q + 2] = pok ? f.z : 0.f;
+              vv[u][v][4 * q + 3] = pok ? f.w : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < R; ++j) vv[u][v][j] = (pok && j < r) ? vp[j] : 0.f;
+          }
+        }
       }
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const float* vp = (v == 0 ? Vv : a.Vv2) + pc * r;
+      for (int u = 0; u < UNR; ++u) {
+        float uv[CPT];
 #pragma unroll
-        for (int j = 0; j < R; ++j) vv[u][v][j] = (pok && j < r) ? vp[j] : 0.f;
+        for (int t = 0; t < CPT / 2; ++t) {
+          const uint32_t w = ok[u] ? rw[u][t] : 0u;
+          uv[2 * t] = bf2f((uint16_t)(w & 0xffffu));
+          uv[2 * t + 1] = bf2f((uint16_t)(w >> 16));
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int t = 0; t < CPT; ++t)
+#pragma unroll
+            for (int j = 0; j < R; ++j) acc[v][t][j] += uv[t] * vv[u][v][j];
       }
     }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      float uv[CPT];
-#pragma unroll
-      for (int t = 0; t < CPT / 2; ++t) {
-        const uint32_t w = ok[u] ? rw[u][t] : 0u;
-        uv[2 * t] = bf2f((uint16_t)(w & 0xffffu));
-        uv[2 * t + 1] = bf2f((uint16_t)(w >> 16));
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int t = 0; t < CPT; ++t)
-#pragma unroll
-          for (int j = 0; j < R; ++j) acc[v][t][j] += uv[t] * vv[u][v][j];
-    }
-  }
+  };
+  if (r == R)
+    rows(BoolC2<true>{});
+  else
+    rows(BoolC2<false>{});
   // wave partials added in wave order, one rank-vector set at a time
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
