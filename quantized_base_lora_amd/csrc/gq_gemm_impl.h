@@ -287,14 +287,18 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   // L ends up with rows 8*(L/32) .. +8 of column L % 32 -- the MFMA B layout.
   const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto compute = [&](int cur) {
+  // NA = the wave's 32-row sub-tiles that hold rows of the tile (a partly
+  // filled MoE tile leaves whole sub-tiles empty: no MFMAs for them)
+  auto compute = [&](int cur, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
     const uint16_t* A = As + cur * BM * LDK;
     const uint16_t* B = Bs + cur * B_TILE;
+    if constexpr (NA == 0) return;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < NA; ++a)
         af[a] = *reinterpret_cast<const bf16x8*>(A + (wm * WTM + a * 32 + (lane & 31)) * LDK +
                                                  kk * 16 + (lane >> 5) * 8);
 #pragma unroll
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         }
       }
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
@@ -390,8 +394,9 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     full = full && (n0 + BN <= p.w_rows);
   }
 
-  auto pipeline = [&](auto full_c) {
+  auto pipeline = [&](auto full_c, auto na_c) {
     constexpr bool FULL = decltype(full_c)::value;
+    constexpr int NA = decltype(na_c)::value;
     uint4 areg0[G::A_CHUNKS], areg1[G::A_CHUNKS];
     uint32_t amsk0[G::A_CHUNKS], amsk1[G::A_CHUNKS];
     auto load_a = [&](int kt, uint4 (&areg)[G::A_CHUNKS], uint32_t (&amsk)[G::A_CHUNKS]) {
@@ -486,18 +491,18 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       load_a(KT(kt + 2), areg0, amsk0);
       load_w(KT(kt + 2), wr0, wmsk0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0);
+      compute(0, na_c);
       store_a(1, areg1, amsk1);
       store_w(1, wr1, wmsk1);
-      mfma_interleave<TM * TN * (BK / 16), 6, 2, 8>();
+      mfma_interleave<NA * TN * (BK / 16), 6, 2, 8>();
       __syncthreads();
       load_a(KT(kt + 3), areg1, amsk1);
       load_w(KT(kt + 3), wr1, wmsk1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(1);
+      compute(1, na_c);
       store_a(0, areg0, amsk0);
       store_w(0, wr0, wmsk0);
-      mfma_interleave<TM * TN * (BK / 16), 6, 2, 8>();
+      mfma_interleave<NA * TN * (BK / 16), 6, 2, 8>();
       __syncthreads();
     }
     // tail: tiles kt .. nkl-1 (at most three)
@@ -506,14 +511,14 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         load_a(KT(kt + 2), areg0, amsk0);
         load_w(KT(kt + 2), wr0, wmsk0);
       }
-      compute(0);
+      compute(0, na_c);
       if (kt + 1 < nkl) {
         store_a(1, areg1, amsk1);
         store_w(1, wr1, wmsk1);
       }
       __syncthreads();
       if (kt + 1 >= nkl) break;
-      compute(1);
+      compute(1, na_c);
       if (kt + 2 < nkl) {
         store_a(0, areg0, amsk0);
         store_w(0, wr0, wmsk0);
@@ -521,10 +526,19 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       __syncthreads();
     }
   };
-  if (full)
-    pipeline(BoolC<true>{});
-  else
-    pipeline(BoolC<false>{});
+  if (full) {
+    pipeline(BoolC<true>{}, IntC<TM>{});
+  } else {
+    // this wave's rows wm*WTM .. +WTM of the tile, in 32-row sub-tiles
+    const int64_t left = r1 - r0 - (int64_t)wm * WTM;
+    const int nact = left <= 0 ? 0 : (left >= WTM ? TM : (int)((left + 31) / 32));
+    if (nact >= TM)
+      pipeline(BoolC<false>{}, IntC<TM>{});
+    else if (TM == 2 && nact == 1)
+      pipeline(BoolC<false>{}, IntC<(TM > 1 ? 1 : TM)>{});
+    else
+      pipeline(BoolC<false>{}, IntC<0>{});
+  }
 
   if constexpr (KS > 1) {
     // fold the second group's partial sums into the first group's
