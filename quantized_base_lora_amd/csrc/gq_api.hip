@@ -122,12 +122,13 @@ GemmArgs gemm_defaults() {
 }
 
 // Rows per chunk of the adapter-gradient column reductions: the largest
-// power of two (16..512) that still gives >= 512 workgroups, so that the
-// reduction fills the chip without multiplying the partial-sum traffic.
+// power of two (32..1024) that still gives >= 256 workgroups, so that the
+// reduction fills the chip without multiplying the partial-sum traffic
+// (C x r floats per chunk, written and read once more by the finish).
 int pick_rc(int64_t M, int64_t C, int r, int E) {
-  // grouped: short per-expert slots (32 rows per wave) keep the Zipf head
-  // experts from serialising the launch
-  if (E > 1) return 128;
+  // grouped: per-expert chunks of 256 rows -- most experts are one chunk
+  // (one partial set each), the Zipf head experts are still split
+  if (E > 1) return 256;
   const int64_t cb = cdiv(C, colred_cols_per_block(r));
   int rc = 32;
   while (rc < 1024 && cdiv(M, rc * 2) * cb >= 256) rc *= 2;

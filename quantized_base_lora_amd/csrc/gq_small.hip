@@ -217,30 +217,35 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
 }
 
 // ---------------------------------------------------- column reductions
-template <bool B> struct BoolC2 { static constexpr bool value = B; };
-// part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j].  A block owns
-// one slot and 64*CPT columns: every lane owns CPT adjacent columns (one 16-
-// or 8-byte load per row, a wave reads a contiguous row segment), the four
-// waves take every fourth row, and the wave partials are added in wave
-// order through LDS.  NV = 2: a second rank-vector array V2 over the same U
-// rows (one pass over U for two reductions).  blockIdx.z picks one of two
-// independent jobs sharing the launch (same rows and slots).
-template <int R, int CPT, int NV>
+// part[slot][c][j] = sum_{rows p of slot} U(p)[c] * V[p][j]  (j < r <= 16),
+// as D[j][c] = V^T U on v_mfma_f32_16x16x32_bf16: the reduction over rows is
+// the MFMA k dimension.  A workgroup (4 waves) owns one slot and CR_COLS
+// columns; rows go in steps of 32: the U rows (bf16, exact) are loaded with
+// 16-byte coalesced loads into an LDS tile and read back transposed
+// (ds_read_b64_tr_b16) as the B operand; the rank vectors enter as A in
+// bf16 hi + lo parts (about 16 significant bits), two MFMAs per product.
+// Each wave owns 64 columns (four 16-column MFMA tiles).  The next step's
+// U loads are in flight while the current step is multiplied.  NV = 2: a
+// second rank-vector array V2 over the same U rows (one pass over U for two
+// reductions).  blockIdx.z picks one of two independent jobs sharing the
+// launch (same rows and slots).
+constexpr int CR_COLS = 256;
+constexpr int CR_PITCH = CR_COLS + 8;  // bf16 elements per LDS tile row
+
+template <int NV>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
-  __shared__ float red[3][64][CPT][R];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][32 * CR_PITCH];
   const bool z1 = blockIdx.z == 1;
   const int32_t C = z1 ? a.C_1 : a.C;
   const uint16_t* const U = z1 ? a.U_1 : a.U;
   const int64_t ldu = z1 ? a.ldu_1 : a.ldu;
   const int32_t* const gather = z1 ? a.gather_1 : a.gather;
   const int32_t gdiv = z1 ? a.gdiv_1 : a.gdiv;
-  const float* const Vv = z1 ? a.Vv_1 : a.Vv;
-  float* const part = z1 ? a.part_1 : a.part;
+  const float* const V0 = z1 ? a.Vv_1 : a.Vv;
+  float* const part0 = z1 ? a.part_1 : a.part;
   const int slot = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t c = ((int64_t)blockIdx.y * 64 + lane) * CPT;
-  if ((int64_t)blockIdx.y * 64 * CPT >= C) return;  // this job has fewer columns
+  const int64_t c0 = (int64_t)blockIdx.y * CR_COLS;
+  if (c0 >= C) return;  // this job has fewer columns
   int64_t r0, r1;
   if (a.offsets) {
     const int32_t* cs = a.chunk_start;
@@ -252,107 +257,109 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     r0 = (int64_t)slot * a.rc;
     r1 = min(a.M, r0 + a.rc);
   }
-  const bool cok = c < C;
-  const int64_t cc = cok ? c : 0;  // clamped: loads stay in bounds
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = a.r;
-  float acc[NV][CPT][R];
+
+  // U tile loads: 32 rows x 256 columns = 1024 16-byte chunks, 4 per thread
+  // (chunk t: row t / 32, columns 8 (t % 32) .. +8); zero past r1 or C
+  constexpr int UCH = 4;
+  int64_t uoff[UCH];
+  int urow[UCH], ucol[UCH];
+  bool ucok[UCH];
+#pragma unroll
+  for (int i = 0; i < UCH; ++i) {
+    const int t = i * 256 + tid;
+    urow[i] = t >> 5;
+    ucol[i] = (t & 31) * 8;
+    ucok[i] = c0 + ucol[i] < C;
+    uoff[i] = c0 + (ucok[i] ? ucol[i] : 0);
+  }
+  uint4 ur[UCH];
+  auto load_u = [&](int64_t p0) {
+#pragma unroll
+    for (int i = 0; i < UCH; ++i) {
+      const int64_t p = p0 + urow[i];
+      const bool ok = p < r1 && ucok[i];
+      const int64_t pc = p < r1 ? p : r0;
+      const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
+      ur[i] = *reinterpret_cast<const uint4*>(U + src * ldu + uoff[i]);
+      if (!ok) ur[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_u = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < UCH; ++i)
+      *reinterpret_cast<uint4*>(&tile[buf][urow[i] * CR_PITCH + ucol[i]]) = ur[i];
+  };
+
+  // A operand: lane (j = lane % 16, q = lane / 16) holds V[p0 + 8q + i][j],
+  // i < 8, as bf16 hi and lo
+  const int aj = lane & 15, aq = lane >> 4;
+  auto load_a = [&](const float* V, int64_t p0, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t p = p0 + 8 * aq + i;
+      const float v = (p < r1 && aj < r) ? V[p * r + aj] : 0.f;
+      const __bf16 h = (__bf16)v;
+      hi[i] = h;
+      lo[i] = (__bf16)(v - (float)h);
+    }
+  };
+
+  // B operand (transposing reads): lane L = 16g + 4t + m addresses row
+  // 8g + t (+4 for the second read) at column 4m of its 16-column tile;
+  // lane 16g + c then holds rows 8g .. 8g+7 of column c
+  const int tr_row = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_col = 4 * (lane & 3);
+
+  f32x4 acc[NV][4];
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int t = 0; t < CPT; ++t)
+    for (int g = 0; g < 4; ++g) acc[v][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  int buf = 0;
+  load_u(r0);
+  for (int64_t p0 = r0; p0 < r1; p0 += 32) {
+    store_u(buf);
+    if (p0 + 32 < r1) load_u(p0 + 32);
+    bf16x8 ahi[NV], alo[NV];
+    load_a(V0, p0, ahi[0], alo[0]);
+    if constexpr (NV == 2) load_a(a.Vv2, p0, ahi[1], alo[1]);
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[v][t][j] = 0.f;
-  // rows r0 + wave + 4i; UNR rows' loads are issued together.  Two copies
-  // of the loop: r == R (rank vectors read with whole 16-byte loads, no
-  // per-element branches) and r < R.
-  int vzero = 0;
-  asm volatile("" : "+v"(vzero));  // a VGPR zero: vector address below
-  auto rows = [&](auto fullr) {
-    // rows r0 + wave + 4i; UNR rows' loads are issued together
-    constexpr int UNR = NV * R >= 16 ? 4 : 8;
-    for (int64_t pb = r0 + wave; pb < r1; pb += 4 * UNR) {
-      uint32_t rw[UNR][CPT / 2];
-      float vv[UNR][NV][R];
-      bool ok[UNR];
+    for (int g = 0; g < 4; ++g) {
+      const uint16_t* base = &tile[buf][tr_row * CR_PITCH + wave * 64 + g * 16 + tr_col];
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(__attribute__((address_space(3))) void*)(base));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(__attribute__((address_space(3))) void*)(base + 4 * CR_PITCH));
+      typedef short v8i16 __attribute__((ext_vector_type(8)));
+      const v8i16 both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const bf16x8 b = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int64_t p = pb + 4 * u;
-        const bool pok = p < r1;  // wave-uniform
-        ok[u] = pok && cok;
-        const int64_t pc = pok ? p : r0;
-        const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
-        const uint16_t* up = U + src * ldu + cc;
-        if constexpr (CPT == 8) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(up);
-          rw[u][0] = raw.x; rw[u][1] = raw.y; rw[u][2] = raw.z; rw[u][3] = raw.w;
-        } else {
-          const uint2 raw = *reinterpret_cast<const uint2*>(up);
-          rw[u][0] = raw.x; rw[u][1] = raw.y;
-        }
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          // the row's rank vector (wave-uniform): whole 16-byte loads when
-          // r == R, no per-element branches
-          const float* vp = (v == 0 ? Vv : a.Vv2) + pc * r;
-          if constexpr (decltype(fullr)::value) {
-            // vector loads (every lane the same address) keep the values in
-            // VGPRs: as scalar loads they overflow the SGPRs
-            const float4* vp4 = reinterpret_cast<const float4*>(vp) + vzero;
-#pragma unroll
-            for (int q = 0; q < R / 4; ++q) {
-              const float4 f = vp4[q];
-              vv[u][v][4 * q] = pok ? f.x : 0.f;
-              vv[u][v][4 * q + 1] = pok ? f.y : 0.f;
-              vv[u][v][4 * q + 2] = pok ? f.z : 0.f;
-              vv[u][v][4 * q + 3] = pok ? f.w : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < R; ++j) vv[u][v][j] = (pok && j < r) ? vp[j] : 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        float uv[CPT];
-#pragma unroll
-        for (int t = 0; t < CPT / 2; ++t) {
-          const uint32_t w = ok[u] ? rw[u][t] : 0u;
-          uv[2 * t] = bf2f((uint16_t)(w & 0xffffu));
-          uv[2 * t + 1] = bf2f((uint16_t)(w >> 16));
-        }
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-          for (int t = 0; t < CPT; ++t)
-#pragma unroll
-            for (int j = 0; j < R; ++j) acc[v][t][j] += uv[t] * vv[u][v][j];
+      for (int v = 0; v < NV; ++v) {
+        acc[v][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[v], b, acc[v][g], 0, 0, 0);
+        acc[v][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[v], b, acc[v][g], 0, 0, 0);
       }
     }
-  };
-  if (r == R)
-    rows(BoolC2<true>{});
-  else
-    rows(BoolC2<false>{});
-  // wave partials added in wave order, one rank-vector set at a time
+    buf ^= 1;
+  }
+  // D layout: lane holds column lane % 16 of its tile, ranks 4 (lane / 16) .. +4
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    if (v > 0) __syncthreads();  // wave 0 is done reading the previous set
-    if (wave > 0) {
+    float* dst = v == 0 ? part0 : a.part2;
 #pragma unroll
-      for (int t = 0; t < CPT; ++t)
+    for (int g = 0; g < 4; ++g) {
+      const int64_t c = c0 + wave * 64 + g * 16 + (lane & 15);
+      if (c >= C) continue;
 #pragma unroll
-        for (int j = 0; j < R; ++j) red[wave - 1][lane][t][j] = acc[v][t][j];
-    }
-    __syncthreads();
-    if (wave == 0 && cok) {
-      float* dst = (v == 0 ? part : a.part2) + ((int64_t)slot * C + c) * r;
-#pragma unroll
-      for (int t = 0; t < CPT; ++t)
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (j < r)
-            dst[t * r + j] = acc[v][t][j] + red[0][lane][t][j] + red[1][lane][t][j] + red[2][lane][t][j];
+      for (int q = 0; q < 4; ++q) {
+        const int j = 4 * (lane >> 4) + q;
+        if (j < r) dst[((int64_t)slot * C + c) * r + j] = acc[v][g][q];
+      }
     }
   }
 }
@@ -764,23 +771,19 @@ hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-int colred_cols_per_block(int r) { return r <= 8 ? 512 : 256; }
+int colred_cols_per_block(int) { return CR_COLS; }
 
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   if (a.slots == 0) return hipSuccess;
+  if (a.r > 16) return hipErrorInvalidValue;
   const bool two = a.njobs == 2;
   const int32_t cmax = two && a.C_1 > a.C ? a.C_1 : a.C;
-  const dim3 g((unsigned)a.slots, blocks_for(cmax, colred_cols_per_block(a.r)), two ? 2 : 1),
-      b(256);
+  const dim3 g((unsigned)a.slots, blocks_for(cmax, CR_COLS), two ? 2 : 1), b(256);
   if (a.Vv2) {
     if (two) return hipErrorInvalidValue;
-    if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8, 2>), g, b, 0, st, a);
-    else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8, 2>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((colred_kernel<16, 4, 2>), g, b, 0, st, a);
+    hipLaunchKernelGGL(colred_kernel<2>, g, b, 0, st, a);
   } else {
-    if (a.r <= 4) hipLaunchKernelGGL((colred_kernel<4, 8, 1>), g, b, 0, st, a);
-    else if (a.r <= 8) hipLaunchKernelGGL((colred_kernel<8, 8, 1>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((colred_kernel<16, 4, 1>), g, b, 0, st, a);
+    hipLaunchKernelGGL(colred_kernel<1>, g, b, 0, st, a);
   }
   return hipGetLastError();
 }
