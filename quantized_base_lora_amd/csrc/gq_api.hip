@@ -157,6 +157,20 @@ int pick_grp_tile(int64_t M, int E, int64_t ntiles) {
   return pick_tile(M, ntiles);
 }
 
+// Backward (NN) launches with few rows per weight run the skinny NN MMQ
+// (16 or 32 rows per tile, 256 output columns per workgroup) when the
+// output row length is a multiple of 256 (whole 8-block segments) and the
+// weights are 16-byte aligned.
+int pick_nn_tile(int64_t rows_per_w, int64_t rows_est, int64_t ntiles128, int64_t Nout,
+                 bool w_aligned, int64_t Kred, bool k2ok = false) {
+  if (Nout % 256 == 0 && w_aligned) {
+    if (rows_per_w <= 16) return TILE_SKINNY16;
+    if (rows_per_w <= 32) return TILE_SKINNY32;
+  }
+  return pick_tile(rows_est, ntiles128, Kred, k2ok);
+}
+int nn_tile_bn(int tc) { return tile_skinny(tc) ? 256 : TILE_BN; }
+
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
 hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
@@ -311,8 +325,8 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
     g.a0 = dy; g.lda = N;
     g.w0 = static_cast<const uint8_t*>(L->w_blocks);
     g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
-    g.ntiles = cdiv(K, TILE_BN);
-    const int tc = pick_tile(T, g.ntiles, N, true);
+    const int tc = pick_nn_tile(T, T, cdiv(K, TILE_BN), K, aligned(L->w_blocks, 16), N, true);
+    g.ntiles = cdiv(K, nn_tile_bn(tc));
     g.mtiles = cdiv(T, tile_bm(tc));
     g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
     g.o0 = dx; g.ldo = K;
@@ -585,7 +599,15 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   // GEMM tiles (the backward MMQ's tile height), column-reduction chunks and
   // 16-row row-dot tiles of every expert, in one launch
   const int ntiles_bwd = cdiv(P[0].n_in, TILE_BN);  // N of both backward MMQs
-  const int tc = pick_grp_tile(M, E, ntiles_bwd);
+  int tc = pick_grp_tile(M, E, ntiles_bwd);
+  // gate/up backward with at most 8 rows per expert on average: the skinny
+  // NN MMQ (with more, experts spill into second 16-row tiles that re-read
+  // the weights, and the 64-row tile measured faster)
+  if (mode == GQ_BWD_GATEUP && nproj == 2 && cdiv(M, E) <= 8 && aligned(P[0].w_blocks, 16) &&
+      aligned(P[1].w_blocks, 16)) {
+    const int tn = pick_nn_tile(cdiv(M, E), M, ntiles_bwd, P[0].n_in, true, 0);
+    if (tile_skinny(tn)) tc = tn;
+  }
   HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), W.ts, rcg, W.cs, 16,
                              mode == GQ_BWD_DOWN_SWIGLU ? W.ts16 : nullptr, st),
           "gq_grouped_mmq_lora_bwd: tiles");
@@ -663,7 +685,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   g.w_rowbytes = rowbytes(&P[0]); g.w_estride = (int64_t)I * g.w_rowbytes; g.w_nb = H / 32;
   g.w_rows = I; g.wsplit = I;
   g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
-  g.ntiles = cdiv(H, TILE_BN);
+  g.ntiles = cdiv(H, nn_tile_bn(tc));
   g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
   g.s = s; g.r = r;
   g.lA0 = P[0].A; g.lA1 = P[1].A; g.lA_estride = (int64_t)r * H;

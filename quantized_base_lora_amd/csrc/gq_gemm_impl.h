@@ -1002,12 +1002,20 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
 
 template <int QT, int EPI>
 hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st);
+template <int QT, int EPI>
+hipError_t launch_skinny_nn(int rg, const GemmArgs& a, hipStream_t st);
 
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
   if constexpr (EPI == EPI_LIN || EPI == EPI_SWIGLU || EPI == EPI_CE_FWD) {
     if (tile_skinny(tilecfg)) return launch_skinny<QT, EPI>(tile_bm(tilecfg) / 16, a, st);
+  }
+  if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
+    if (tile_skinny(tilecfg)) {
+      if (tile_bm(tilecfg) > 32) return hipErrorInvalidValue;
+      return launch_skinny_nn<QT, EPI>(tile_bm(tilecfg) / 16, a, st);
+    }
   }
   if constexpr (!epi_stages(EPI)) {
     if (tilecfg == TILE_128x128_K2) {

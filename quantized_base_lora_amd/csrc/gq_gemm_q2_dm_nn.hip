@@ -1,5 +1,6 @@
 // MFMA GEMM instantiations: Q2_DM blocks, backward (NN) epilogues.
 #include "gq_gemm_impl.h"
+#include "gq_skinny_impl.h"
 
 namespace gq {
 hipError_t launch_gemm_q2_dm_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {

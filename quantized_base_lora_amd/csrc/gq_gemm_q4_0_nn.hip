@@ -1,5 +1,6 @@
 // MFMA GEMM instantiations: Q4_0 blocks, backward (NN) epilogues.
 #include "gq_gemm_impl.h"
+#include "gq_skinny_impl.h"
 
 namespace gq {
 hipError_t launch_gemm_q4_0_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {

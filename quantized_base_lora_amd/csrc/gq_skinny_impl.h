@@ -387,5 +387,237 @@ hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+// Skinny NN MMQ (backward dX = dY deq(W) for few rows per weight): the
+// reduction runs over weight rows, the outputs over a row's elements.  A
+// workgroup (8 waves) owns 16 * RG output rows by 256 output columns (8
+// blocks of every weight row, one 16-byte aligned segment); wave w owns the
+// 32 columns of block w.  Per step of 64 weight rows:
+//  * the 64 row segments are read with coalesced 16-byte loads into a shared
+//    LDS tile (double-buffered, one barrier per step; the next step's loads
+//    are in flight meanwhile);
+//  * lane l of wave w decodes block w of step row l and writes its 32 bf16
+//    values row-major into the wave's own LDS region, read back transposed
+//    (ds_read_b64_tr_b16) as the B operand of v_mfma_f32_16x16x32_bf16;
+//  * the A operand (activation rows x 32 reduction rows) is read straight
+//    from global memory; rows past the tile or the reduction are zero.
+// The adapter term s * (X . A[:, col]) is added in fp32 in the epilogue.
+// Epilogues: EPI_LIN_BWD (bf16 dX) and EPI_GATEUP_BWD (reduction over the
+// gate rows with dg, then the up rows with du; bf16 dX rows).
+constexpr int SKN_COLS = 256;  // output columns per workgroup
+
+template <int QT, int EPI, int RG>
+__global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs p) {
+  static_assert(EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD, "NN epilogues");
+  constexpr int BS = QTraits<QT>::BS;
+  constexpr int SEGB = 8 * BS;             // bytes of a row's 8-block segment
+  constexpr int SEGQ = SEGB / 16;
+  constexpr int NCH = 64 * SEGQ;           // 16-byte chunks per step
+  constexpr int NTHR = 64 * SK_WAVES;
+  constexpr int CI = (NCH + NTHR - 1) / NTHR;
+  constexpr int RAWB = 64 * SEGB + 16;     // raw tile bytes (tail read slack)
+  constexpr int DP = 40;                   // decoded row pitch (bf16): 32 + 8
+  constexpr int NQ = RawBlock<QT>::NQ;
+  constexpr int RT = 16 * RG;
+  __shared__ __attribute__((aligned(16))) uint8_t raw[2][RAWB];
+  __shared__ __attribute__((aligned(16))) uint16_t dec[SK_WAVES][64 * DP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+
+  int bid;
+  {
+    const int nblk = gridDim.x, qq = nblk >> 3, rem = nblk & 7;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    bid = (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + loc;
+  }
+  const int mslot = bid % p.mtiles;
+  const int ntile = bid / p.mtiles;
+  int e = 0;
+  int64_t r0, r1;
+  if (p.offsets) {
+    const int32_t* ts = p.tile_start;
+    if (mslot >= ts[p.E]) return;
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ts[mid] <= mslot) lo = mid; else hi = mid;
+    }
+    e = lo;
+    r0 = (int64_t)p.offsets[e] + (int64_t)(mslot - ts[e]) * RT;
+    r1 = min((int64_t)p.offsets[e + 1], r0 + RT);
+  } else {
+    r0 = (int64_t)mslot * RT;
+    if (r0 >= p.M) return;
+    r1 = min(p.M, r0 + RT);
+  }
+  const int c0 = ntile * SKN_COLS;  // first output column (weight row element)
+  const int Kr = p.K;               // reduction length (weight rows)
+  const int nsteps = (Kr + 63) / 64;
+
+  // raw chunk loads: chunk t = row t / SEGQ of the step, bytes 16 (t % SEGQ)
+  // of the row's segment; rows past the reduction re-read row 0
+  const uint8_t* wbase0 = p.w0 + (int64_t)e * p.w_estride + (int64_t)ntile * SEGB;
+  const uint8_t* wbase1 = p.w1 ? p.w1 + (int64_t)e * p.w_estride + (int64_t)ntile * SEGB : wbase0;
+  int crow[CI], coff[CI];
+  bool cval[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int t = i * NTHR + tid;
+    cval[i] = t < NCH;
+    const int tt = cval[i] ? t : 0;
+    crow[i] = tt / SEGQ;
+    coff[i] = (tt % SEGQ) * 16;
+  }
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
+  u32x4 wr[CI];
+  auto load_w = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < CI; ++i) {
+      int n = st * 64 + crow[i];
+      if (n >= Kr) n = 0;
+      const uint8_t* b = n >= p.wsplit ? wbase1 + (int64_t)(n - p.wsplit) * p.w_rowbytes
+                                       : wbase0 + (int64_t)n * p.w_rowbytes;
+      wr[i] = *(g_u32x4*)(b + coff[i]);
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CI; ++i)
+      if (cval[i]) *reinterpret_cast<u32x4*>(&raw[buf][crow[i] * SEGB + coff[i]]) = wr[i];
+  };
+
+  // A fragments: lane (m, q) holds A[row 16 rg + m][n0 + 32 ks + 8q .. +8]
+  const uint16_t* arow[RG];
+  bool aok[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int64_t pr = r0 + rg * 16 + nl;
+    aok[rg] = pr < r1;
+    int64_t src = aok[rg] ? pr : r0;
+    if (p.gather) src = p.gather[src] / p.gdiv;
+    arow[rg] = p.a0 + src * p.lda;
+  }
+  const uint16_t* arow1[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) arow1[rg] = p.a1 ? arow[rg] - p.a0 + p.a1 : arow[rg];
+  auto load_a = [&](int st, int ks, int rg) -> bf16x8 {
+    const int n = st * 64 + ks * 32 + 8 * q;  // 8 reduction rows n .. n+7
+    const bool ok = aok[rg] && n < Kr;
+    const uint16_t* src = n >= p.asplit ? arow1[rg] + (n - p.asplit) : arow[rg] + n;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = *reinterpret_cast<const uint4*>(src);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  // transposed reads: lane 16g + 4t + m addresses decoded row 8g + t (+4),
+  // columns 4m .. +4 of a 16-column group; lane 16g + c then holds rows
+  // 8g .. 8g+7 of column c
+  const int tr_row = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_col = 4 * (lane & 3);
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  uint16_t* D = dec[wave];
+
+  f32x4 acc[RG][2];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[rg][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_w(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    store_w(buf);
+    if (st + 1 < nsteps) load_w(st + 1);
+    bf16x8 af[2][RG];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) af[ks][rg] = load_a(st, ks, rg);
+    __syncthreads();
+    // decode block `wave` of step row `lane` into the wave's region
+    {
+      const int off = lane * SEGB + wave * BS;
+      RawBlock<QT> rb;
+      if constexpr (QT == QT_Q2_DM) {
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(&raw[buf][off]);
+        rb.hdr = d[0]; rb.q[0] = d[1]; rb.q[1] = d[2];
+      } else {
+        rb.hdr = *reinterpret_cast<const uint16_t*>(&raw[buf][off]);
+        const int sh = (off + 2) & 3;
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(&raw[buf][off + 2 - sh]);
+        uint32_t Dw[NQ + 1];
+#pragma unroll
+        for (int t = 0; t <= NQ; ++t) Dw[t] = d[t];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) rb.q[t] = __builtin_amdgcn_alignbyte(Dw[t + 1], Dw[t], sh);
+      }
+      float w[32];
+      decode_block_fast<QT>(rb, w);
+      uint4* dst = reinterpret_cast<uint4*>(D + lane * DP);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        dst[q4] = make_uint4(pack_bf2(w[8 * q4 + 0], w[8 * q4 + 1]), pack_bf2(w[8 * q4 + 2], w[8 * q4 + 3]),
+                             pack_bf2(w[8 * q4 + 4], w[8 * q4 + 5]), pack_bf2(w[8 * q4 + 6], w[8 * q4 + 7]));
+    }
+    // (the wave's own region: the LDS writes above complete before the
+    // reads below in this wave's program order)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint16_t* base = D + (ks * 32 + tr_row) * DP + g * 16 + tr_col;
+        const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(__attribute__((address_space(3))) void*)(base));
+        const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(__attribute__((address_space(3))) void*)(base + 4 * DP));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        const bf16x8 b = __builtin_bit_cast(bf16x8, both);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          acc[rg][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][rg], b, acc[rg][g], 0, 0, 0);
+      }
+  }
+
+  // ---- epilogue: acc[rg][g][v] at row r0 + 16 rg + 4q + v, column
+  // c0 + 32 wave + 16 g + nl.  Adapter term in fp32:
+  //   + s * sum_j X(row, j) * A[j][col]   (GATEUP: both projections)
+  const int r = p.r;
+  const float s_ = p.s;
+  const float* Y0 = p.lA0 + (int64_t)e * p.lA_estride;
+  const float* Y1 = EPI == EPI_GATEUP_BWD ? p.lA1 + (int64_t)e * p.lA_estride : nullptr;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int col = c0 + 32 * wave + 16 * g + nl;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll 1
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pr = r0 + rg * 16 + 4 * q + v;
+        if (pr >= r1) continue;
+        float t = 0.f;
+        for (int j = 0; j < r; ++j) t += p.rv0[pr * r + j] * Y0[(int64_t)j * p.N + col];
+        if constexpr (EPI == EPI_GATEUP_BWD)
+          for (int j = 0; j < r; ++j) t += p.rv1[pr * r + j] * Y1[(int64_t)j * p.N + col];
+        p.o0[pr * p.ldo + col] = f2bf(acc[rg][g][v] + s_ * t);
+      }
+  }
+}
+
+template <int QT, int EPI>
+hipError_t launch_skinny_nn(int rg, const GemmArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(64 * SK_WAVES);
+  if (rg == 1)
+    hipLaunchKernelGGL((skinny_nn_kernel<QT, EPI, 1>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((skinny_nn_kernel<QT, EPI, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace gq
