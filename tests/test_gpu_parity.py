@@ -197,6 +197,9 @@ MOE_CASES = [
     (48, 512, 256, 8, 2, 1, 4, 1.0),
     (30, 256, 256, 4, 2, 2, 8, 0.0),
     (64, 256, 256, 4, 2, 1, 4, 0.5),
+    # at most 8 rows per expert: the gate/up backward on the skinny NN MMQ
+    (24, 256, 128, 8, 2, 2, 4, 1.0),
+    (16, 512, 192, 16, 2, 0, 8, 0.0),
 ]
 
 
