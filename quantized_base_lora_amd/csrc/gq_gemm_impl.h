@@ -104,30 +104,30 @@ __device__ __forceinline__ void load_rank(const float* p, int r, float (&v)[R]) 
 
 // Row reduction of the staged tile Z [BM][ZP]:
 //   out[j] = sum_{c : n0 + c < ncols} Z[row][c] * W[(n0 + c) * r + j],  j < r <= R
-// (W == nullptr: out[0] = the plain row sum).  Thread (row = tid % BM,
+// The tile's rank vectors are first staged in LDS (S: BN x R floats) by all
+// threads, so the reduction loop reads only LDS.  Thread (row = tid % BM,
 // seg = tid / BM) sums one column segment; segments are combined in order
 // through LDS.  sink(row, out) runs on segment 0.  Caller has synchronised
 // after writing Z; returns synchronised.
 template <int BM, int BN, int R, class Sink>
-__device__ __forceinline__ void z_row_reduce(float* Z, const float* W, int r, int n0, int ncols,
-                                             Sink sink) {
+__device__ __forceinline__ void z_row_reduce(float* Z, float* S, const float* W, int r, int n0,
+                                             int ncols, Sink sink) {
   constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG, ZP = BN + 1, XP = R + 1;
   const int tid = threadIdx.x;
   const int row = tid % BM, seg = tid / BM;
+  for (int i = tid; i < BN * R; i += NTHR) {
+    const int c = i / R, j = i % R;
+    S[i] = (j < r && n0 + c < ncols) ? W[(int64_t)(n0 + c) * r + j] : 0.f;
+  }
+  __syncthreads();
   float acc[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) acc[j] = 0.f;
-  const int cend = min((seg + 1) * SEGC, ncols - n0);
-  if (W) {
-    for (int c = seg * SEGC; c < cend; ++c) {
-      const float z = Z[row * ZP + c];
-      float w[R];
-      load_rank<R>(W + (int64_t)(n0 + c) * r, r, w);
+#pragma unroll 4
+  for (int c = seg * SEGC; c < (seg + 1) * SEGC; ++c) {
+    const float z = Z[row * ZP + c];
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[j] += z * w[j];
-    }
-  } else {
-    for (int c = seg * SEGC; c < cend; ++c) acc[0] += Z[row * ZP + c];
+    for (int j = 0; j < R; ++j) acc[j] += z * S[c * R + j];
   }
   __syncthreads();
   float* X = Z;  // reuse: [NSEG][BM][R + 1]
@@ -146,23 +146,27 @@ __device__ __forceinline__ void z_row_reduce(float* Z, const float* W, int r, in
   __syncthreads();
 }
 
-// Column reduction of Z: out[j] = sum_{row : r0 + row < r1} Z[row][col] * X[(r0+row)*r + j]
+// Column reduction of Z: out[j] = sum_{row : r0 + row < r1} Z[row][col] * X[(r0+row)*r + j],
+// the tile's rank vectors staged in LDS (S: BM x R floats) first.
 template <int BM, int BN, int R, class Sink>
-__device__ __forceinline__ void z_col_reduce(float* Z, const float* X, int r, int64_t r0,
+__device__ __forceinline__ void z_col_reduce(float* Z, float* S, const float* X, int r, int64_t r0,
                                              int64_t r1, Sink sink) {
   constexpr int NSEG = NTHR / BN, SEGR = BM / NSEG, ZP = BN + 1, XP = R + 1;
   const int tid = threadIdx.x;
   const int col = tid % BN, seg = tid / BN;
+  for (int i = tid; i < BM * R; i += NTHR) {
+    const int rr = i / R, j = i % R;
+    S[i] = (j < r && r0 + rr < r1) ? X[(r0 + rr) * r + j] : 0.f;
+  }
+  __syncthreads();
   float acc[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) acc[j] = 0.f;
-  const int rend = (int)min((int64_t)(seg + 1) * SEGR, r1 - r0);
-  for (int rr = seg * SEGR; rr < rend; ++rr) {
+#pragma unroll 4
+  for (int rr = seg * SEGR; rr < (seg + 1) * SEGR; ++rr) {
     const float z = Z[rr * ZP + col];
-    float x[R];
-    load_rank<R>(X + (r0 + rr) * r, r, x);
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[j] += z * x[j];
+    for (int j = 0; j < R; ++j) acc[j] += z * S[rr * R + j];
   }
   __syncthreads();
   float* Xs = Z;
@@ -904,11 +908,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
           if constexpr (EPI == EPI_CE_FWD) {
             zv = (pr < r1 && n < p.w_rows) ? acc[a][b][v] : -INFINITY;
           } else {
-            zv = 0.f;
-            if (pr < r1) {
-              zv = gval(a, b, v, pr, n);
-              if (n < p.ldo) p.o0[pr * p.ldo + n] = f2bf(zv);
-            }
+            zv = pr < r1 ? gval(a, b, v, pr, n) : 0.f;
             acc[a][b][v] = zv;  // G, restaged below without recomputing
           }
           Z[lr * ZP + lc] = zv;
@@ -959,12 +959,33 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       }
       if (have_lab) p.f1[pr] = zl;
     } else {
+      // the G tile to bf16, rows stored with 16-byte stores from the staged
+      // copy (two threads per row, 8 columns per store)
+      {
+        const int row = tid >> 1, half = tid & 1;
+        const int64_t pr = r0 + row;
+        if (pr < r1) {
+#pragma unroll
+          for (int q8 = 0; q8 < BN / 16; ++q8) {
+            const int c = half * (BN / 2) + q8 * 8;
+            if (n0 + c < p.ldo) {
+              const float* z = Z + row * ZP + c;
+              *reinterpret_cast<uint4*>(p.o0 + pr * p.ldo + n0 + c) =
+                  make_uint4(pack_bf2(z[0], z[1]), pack_bf2(z[2], z[3]), pack_bf2(z[4], z[5]),
+                             pack_bf2(z[6], z[7]));
+            }
+          }
+        }
+      }
       // G . B over this tile's vocab columns -> part_GB[ntile][T][r], then
       // G^T . xa over this tile's rows -> part_dB[mtile][V][r] (G restaged
-      // from the accumulators)
+      // from the accumulators); the rank vectors go through the LDS area
+      // behind the staged tile
+      float* S = reinterpret_cast<float*>(smem + BM * (BN + 4) * 4);
       auto reductions = [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        z_row_reduce<BM, BN, R>(Z, p.lB0 + c0 * r, r, n0, p.w_rows, [&](int row, float(&out)[R]) {
+        static_assert(BN * R * 4 <= 2 * BN * 8 * 4 && BM * R * 4 <= 2 * BN * 8 * 4, "staging fits");
+        z_row_reduce<BM, BN, R>(Z, S, p.lB0 + c0 * r, r, n0, p.w_rows, [&](int row, float(&out)[R]) {
           const int64_t pr = r0 + row;
           if (pr < r1) {
             float* dst = p.f1 + ((int64_t)(p.ntile_base + ntile) * p.M + pr) * r;
@@ -980,7 +1001,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
 #pragma unroll
             for (int v = 0; v < 16; ++v) Z[LR(a, v) * ZP + LC(b)] = acc[a][b][v];
         __syncthreads();
-        z_col_reduce<BM, BN, R>(Z, p.rv0, r, r0, r1, [&](int col, float(&out)[R]) {
+        z_col_reduce<BM, BN, R>(Z, S, p.rv0, r, r0, r1, [&](int col, float(&out)[R]) {
           const int n = n0 + col;
           if (n < p.w_rows) {
             float* dst = p.f2 + ((int64_t)mslot * V + c0 + n) * r;
