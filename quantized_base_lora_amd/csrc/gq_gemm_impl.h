@@ -188,7 +188,9 @@ __device__ __forceinline__ void z_col_reduce(float* Z, float* S, const float* X,
 // Instruction interleave for the steady-state k-step: LEAD LDS reads first
 // (the first MFMA operands), then per MFMA NV VALU ops (the decode of the
 // next tile) and ND LDS ops, so the decode issues in the shadow of the
-// matrix cores instead of in clusters (measured ~10% on the dense forward).
+// matrix cores instead of in clusters (measured ~10% on the dense forward;
+// the NN path, with two transposing reads per B fragment, takes 4 LDS ops
+// per MFMA: ~5% on the dX launch).
 template <int NM, int NV, int ND, int LEAD>
 __device__ __forceinline__ void mfma_interleave() {
   __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       compute(0, na_c);
       store_a(1, areg1, amsk1);
       store_w(1, wr1, wmsk1);
-      mfma_interleave<NA * TN * (BK / 16), 6, 2, 8>();
+      mfma_interleave<NA * TN * (BK / 16), 6, NN ? 4 : 2, 8>();
       __syncthreads();
       load_a(KT(kt + 3), areg1, amsk1);
       load_w(KT(kt + 3), wr1, wmsk1);
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       compute(1, na_c);
       store_a(0, areg0, amsk0);
       store_w(0, wr0, wmsk0);
-      mfma_interleave<NA * TN * (BK / 16), 6, 2, 8>();
+      mfma_interleave<NA * TN * (BK / 16), 6, NN ? 4 : 2, 8>();
       __syncthreads();
     }
     // tail: tiles kt .. nkl-1 (at most three)
