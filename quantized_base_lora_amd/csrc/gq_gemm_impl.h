@@ -738,14 +738,13 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     }
   } else if constexpr (EPI == EPI_DOWN_BWD) {
     // Columns are the expert's intermediate index i (< N = I); acc holds
-    // e = dY deq(Wd) + s (dY Bd) Ad.  e is staged row-major in LDS; each
-    // thread then owns a segment of one row: 16-byte loads of the saved g, u,
-    // the SwiGLU backward, 16-byte stores of dg, du (bf16), and the row
+    // e = dY deq(Wd) + s (dY Bd) Ad.  e is staged row-major in LDS; 16
+    // threads then share a row, 8 columns each: 16-byte loads of the saved
+    // g, u, the SwiGLU backward, 16-byte stores of dg, du (bf16), and the row
     // partials of this column tile: dw = sum e*silu(g)*u, dgB = sum dg*Bg,
-    // duB = sum du*Bu (with the stored bf16 dg, du), combined in segment
-    // order through LDS.  Bg, Bu of the tile's columns sit in LDS for r <= 8.
+    // duB = sum du*Bu (with the stored bf16 dg, du).  Bg, Bu of the tile's
+    // columns sit in LDS for r <= 8.
     constexpr int ZD = BN + 4;
-    constexpr int NSEG = NTHR / BM, SEGC = BN / NSEG;
     float* Z = reinterpret_cast<float*>(smem);
     float* Bst = Z + BM * ZD;  // [2][BN][8]
     const int width = 1 + 2 * r;
@@ -765,109 +764,100 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       }
     }
     __syncthreads();
-    const int row = tid % BM, seg = tid / BM;
-    const int64_t pr = r0 + row;
-    const bool rok = pr < r1;
+    // 4 threads per tile row, 4 chunks of 8 columns each (a wave's g, u
+    // loads and dg, du stores cover 16 rows x 64 contiguous bytes per
+    // chunk), 64 rows per pass; the row partials are summed over the row's
+    // 4 threads with xor shuffles (fixed order) and written by its first
+    // thread
+    constexpr int TPR = 4, RPP = NTHR / TPR, CPT = BN / TPR / 8;
+    const int cq = tid % TPR, rsub = tid / TPR;
     auto segment = [&](auto rc) {
       constexpr int R = decltype(rc)::value;
-      float dw = 0.f, ag[R], au[R];
+      for (int pass = 0; pass < BM / RPP; ++pass) {
+        if (r0 + pass * RPP >= r1) break;  // workgroup-uniform: no rows left
+        const int row = pass * RPP + rsub;
+        const int64_t pr = r0 + row;
+        float dw = 0.f, ag[R], au[R];
 #pragma unroll
-      for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
-      if (rok) {
-        const float wp = p.wflat[p.sorted[pr]];
-#pragma unroll 1
-        for (int q = 0; q < SEGC / 8; ++q) {
-          const int lc = seg * SEGC + 8 * q;
+        for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
+        const float wp = pr < r1 ? p.wflat[p.sorted[pr]] : 0.f;
+#pragma unroll
+        for (int ch = 0; ch < CPT; ++ch) {
+          const int lc = (ch * TPR + cq) * 8;
           const int c = n0 + lc;
-          if (c >= p.N) break;  // N % 8 == 0: whole 8-column chunks
-          const int64_t o = pr * p.ldo + c;
-          const uint4 g8 = *reinterpret_cast<const uint4*>(p.s0 + o);
-          const uint4 u8 = *reinterpret_cast<const uint4*>(p.s1 + o);
-          const float4 e0 = *reinterpret_cast<const float4*>(Z + row * ZD + lc);
-          const float4 e1 = *reinterpret_cast<const float4*>(Z + row * ZD + lc + 4);
-          const uint32_t gw[4] = {g8.x, g8.y, g8.z, g8.w}, uw[4] = {u8.x, u8.y, u8.z, u8.w};
-          const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-          uint32_t dgp[4], dup[4];
+          const bool ok = pr < r1 && c < p.N;  // N % 8 == 0: whole 8-column chunks
+          if (ok) {
+            const int64_t o = pr * p.ldo + c;
+            const uint4 g8 = *reinterpret_cast<const uint4*>(p.s0 + o);
+            const uint4 u8 = *reinterpret_cast<const uint4*>(p.s1 + o);
+            const float4 e0 = *reinterpret_cast<const float4*>(Z + row * ZD + lc);
+            const float4 e1 = *reinterpret_cast<const float4*>(Z + row * ZD + lc + 4);
+            const uint32_t gw[4] = {g8.x, g8.y, g8.z, g8.w}, uw[4] = {u8.x, u8.y, u8.z, u8.w};
+            const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+            uint32_t dgp[4], dup[4];
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            float dgv[2], duv[2];
+            for (int t2 = 0; t2 < 4; ++t2) {
+              float dgv[2], duv[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float gg = bf2f((uint16_t)(gw[t2] >> (16 * h)));
-              const float uu = bf2f((uint16_t)(uw[t2] >> (16 * h)));
-              const float eh = ev[2 * t2 + h];
-              const float sg = sigmoidf_(gg);
-              const float silu = gg * sg;
-              const float dh = wp * eh;
-              dgv[h] = dh * uu * sg * (1.f + gg * (1.f - sg));
-              duv[h] = dh * silu;
-              dw += eh * silu * uu;
+              for (int h = 0; h < 2; ++h) {
+                const float gg = bf2f((uint16_t)(gw[t2] >> (16 * h)));
+                const float uu = bf2f((uint16_t)(uw[t2] >> (16 * h)));
+                const float eh = ev[2 * t2 + h];
+                const float sg = sigmoidf_(gg);
+                const float silu = gg * sg;
+                const float dh = wp * eh;
+                dgv[h] = dh * uu * sg * (1.f + gg * (1.f - sg));
+                duv[h] = dh * silu;
+                dw += eh * silu * uu;
+              }
+              dgp[t2] = pack_bf2(dgv[0], dgv[1]);
+              dup[t2] = pack_bf2(duv[0], duv[1]);
             }
-            dgp[t2] = pack_bf2(dgv[0], dgv[1]);
-            dup[t2] = pack_bf2(duv[0], duv[1]);
-          }
-          *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
-          *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
-          // rank partials of the eight columns: R <= 8 from the LDS slices
-          // (unrolled); R = 16 from global memory, one column at a time so the
-          // loads of all eight columns are not hoisted at once
-          auto col_terms = [&](int t) {
-            const float dq = __builtin_bit_cast(float, (dgp[t >> 1] >> (16 * (t & 1))) << 16);
-            const float uq = __builtin_bit_cast(float, (dup[t >> 1] >> (16 * (t & 1))) << 16);
-            float bg[R], bu[R];
-            if constexpr (R <= 8) {
+            *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
+            *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
+            // rank partials of the eight columns (with the stored bf16 dg, du):
+            // R <= 8 from the LDS slices, R = 16 from global memory
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float dq = __builtin_bit_cast(float, (dgp[t >> 1] >> (16 * (t & 1))) << 16);
+              const float uq = __builtin_bit_cast(float, (dup[t >> 1] >> (16 * (t & 1))) << 16);
+              float bg[R], bu[R];
+              if constexpr (R <= 8) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                  bg[j] = Bst[(lc + t) * 8 + j];
+                  bu[j] = Bst[(BN + lc + t) * 8 + j];
+                }
+              } else {
+                load_rank<R>(Bg + (int64_t)(c + t) * r, r, bg);
+                load_rank<R>(Bu + (int64_t)(c + t) * r, r, bu);
+              }
 #pragma unroll
               for (int j = 0; j < R; ++j) {
-                bg[j] = Bst[(lc + t) * 8 + j];
-                bu[j] = Bst[(BN + lc + t) * 8 + j];
+                ag[j] += dq * bg[j];
+                au[j] += uq * bu[j];
               }
-            } else {
-              load_rank<R>(Bg + (int64_t)(c + t) * r, r, bg);
-              load_rank<R>(Bu + (int64_t)(c + t) * r, r, bu);
             }
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-              ag[j] += dq * bg[j];
-              au[j] += uq * bu[j];
-            }
-          };
-          if constexpr (R <= 8) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) col_terms(t);
-          } else {
-#pragma unroll 1
-            for (int t = 0; t < 8; ++t) col_terms(t);
           }
         }
-      }
-      __syncthreads();
-      constexpr int XP = 2 * R + 1;
-      float* X = Z;  // [NSEG][BM][XP]
-      if (seg > 0) {
-        X[(seg * BM + row) * XP] = dw;
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          X[(seg * BM + row) * XP + 1 + j] = ag[j];
-          X[(seg * BM + row) * XP + 1 + R + j] = au[j];
-        }
-      }
-      __syncthreads();
-      if (seg == 0 && rok) {
-        for (int sg = 1; sg < NSEG; ++sg) {
-          dw += X[(sg * BM + row) * XP];
+        for (int o2 = 1; o2 < TPR; o2 <<= 1) {
+          dw += __shfl_xor(dw, o2, TPR);
 #pragma unroll
           for (int j = 0; j < R; ++j) {
-            ag[j] += X[(sg * BM + row) * XP + 1 + j];
-            au[j] += X[(sg * BM + row) * XP + 1 + R + j];
+            ag[j] += __shfl_xor(ag[j], o2, TPR);
+            au[j] += __shfl_xor(au[j], o2, TPR);
           }
         }
-        float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width;
-        dst[0] = dw;
+        if (cq == 0 && pr < r1) {
+          float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width;
+          dst[0] = dw;
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          if (j < r) {
-            dst[1 + j] = ag[j];
-            dst[1 + r + j] = au[j];
+          for (int j = 0; j < R; ++j) {
+            if (j < r) {
+              dst[1 + j] = ag[j];
+              dst[1 + r + j] = au[j];
+            }
           }
         }
       }
