@@ -686,17 +686,49 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   auto LC = [&](int b) { return LCb(b); };
 
   if constexpr (EPI == EPI_LIN || EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int n = n0 + LC(b);
-      if (n >= p.N) continue;
+    // the wave's WTM x WTN output tile goes through a wave-private LDS
+    // region (rows of WTN + 8 bf16) and leaves as 16-byte row stores (8
+    // lanes per 128-byte row segment) -- when the output rows allow 16-byte
+    // stores; else one 2-byte store per value.  The region lies past the
+    // split-K reduction buffer, which other waves may still be reading.
+    const bool vec = ((uintptr_t)p.o0 % 16 == 0) && (p.ldo % 8 == 0) && (p.N % 8 == 0);
+    if (vec) {
+      constexpr int SP = WTN + 8;
+      uint16_t* Ws = reinterpret_cast<uint16_t*>(smem + (KS > 1 ? BM * BN * 4 : 0)) + wave * WTM * SP;
+      static_assert((KS > 1 ? BM * BN * 4 : 0) + 4 * WTM * SP * 2 <= G::SMEM, "staging fits");
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t pr = r0 + LR(a, v);
-          if (pr < r1) p.o0[pr * p.ldo + n] = f2bf(acc[a][b][v]);
-        }
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            Ws[(a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * SP + b * 32 + (lane & 31)] =
+                f2bf(acc[a][b][v]);
+      // (the wave's own region: its LDS writes complete before these reads)
+      constexpr int CH = WTN / 8;
+      const int64_t rbase = r0 + wm * WTM;
+      const int cbase = n0 + wn * WTN;
+#pragma unroll
+      for (int i = lane; i < WTM * CH; i += 64) {
+        const int rr = i / CH, cc = (i % CH) * 8;
+        const int64_t pr = rbase + rr;
+        const int n = cbase + cc;
+        if (pr < r1 && n < p.N)
+          *reinterpret_cast<uint4*>(p.o0 + pr * p.ldo + n) = *reinterpret_cast<const uint4*>(Ws + rr * SP + cc);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int n = n0 + LC(b);
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t pr = r0 + LR(a, v);
+            if (pr < r1) p.o0[pr * p.ldo + n] = f2bf(acc[a][b][v]);
+          }
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // n-subtiles come in (gate, up) pairs over the same 32 intermediate rows
