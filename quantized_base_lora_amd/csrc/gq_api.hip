@@ -158,18 +158,18 @@ int pick_grp_tile(int64_t M, int E, int64_t ntiles) {
 }
 
 // Backward (NN) launches with few rows per weight run the skinny NN MMQ
-// (16 or 32 rows per tile, 256 output columns per workgroup) when the
-// output row length is a multiple of 256 (whole 8-block segments) and the
+// (16 or 32 rows per tile, 128 output columns per workgroup) when the
+// output row length is a multiple of 128 (whole 4-block segments) and the
 // weights are 16-byte aligned.
 int pick_nn_tile(int64_t rows_per_w, int64_t rows_est, int64_t ntiles128, int64_t Nout,
                  bool w_aligned, int64_t Kred, bool k2ok = false) {
-  if (Nout % 256 == 0 && w_aligned) {
+  if (Nout % 128 == 0 && w_aligned) {
     if (rows_per_w <= 16) return TILE_SKINNY16;
     if (rows_per_w <= 32) return TILE_SKINNY32;
   }
   return pick_tile(rows_est, ntiles128, Kred, k2ok);
 }
-int nn_tile_bn(int tc) { return tile_skinny(tc) ? 256 : TILE_BN; }
+int nn_tile_bn(int tc) { (void)tc; return TILE_BN; }  // 128 for the tile and the skinny NN MMQ
 
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
@@ -600,11 +600,11 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   // 16-row row-dot tiles of every expert, in one launch
   const int ntiles_bwd = cdiv(P[0].n_in, TILE_BN);  // N of both backward MMQs
   int tc = pick_grp_tile(M, E, ntiles_bwd);
-  // gate/up backward with at most 8 rows per expert on average: the skinny
-  // NN MMQ (with more, experts spill into second 16-row tiles that re-read
-  // the weights, and the 64-row tile measured faster)
-  if (mode == GQ_BWD_GATEUP && nproj == 2 && cdiv(M, E) <= 8 && aligned(P[0].w_blocks, 16) &&
-      aligned(P[1].w_blocks, 16)) {
+  // backward MMQ with at most 8 rows per expert on average: the skinny NN
+  // MMQ (with more, experts spill into second 16-row tiles that re-read the
+  // weights, and the 64-row tile measured faster)
+  const bool w_al = aligned(P[0].w_blocks, 16) && (mode != GQ_BWD_GATEUP || aligned(P[1].w_blocks, 16));
+  if (cdiv(M, E) <= 8 && w_al) {
     const int tn = pick_nn_tile(cdiv(M, E), M, ntiles_bwd, P[0].n_in, true, 0);
     if (tile_skinny(tn)) tc = tn;
   }
@@ -643,7 +643,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     g.w_rowbytes = rowbytes(&P[0]); g.w_estride = (int64_t)H * g.w_rowbytes; g.w_nb = I / 32;
     g.w_rows = H;
     g.E = E; g.offsets = a->offsets; g.tile_start = W.ts;
-    g.ntiles = cdiv(I, TILE_BN);
+    g.ntiles = cdiv(I, nn_tile_bn(tc));
     g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
     g.s = s; g.r = r;
     g.lA0 = P[0].A; g.lA_estride = (int64_t)r * I;
@@ -812,7 +812,6 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   Ws w(ws);
   const CeWs P = plan_ce(w, L, T, chunk, grad);
 
-  HIP_TRY(launch_ce_prep(labels, T, V, ignore_index, P.err, P.nvalid, st), "ce: labels");
   RowDotArgs rd;
   memset(&rd, 0, sizeof rd);
   rd.M = T; rd.C = H; rd.r = r; rd.act = h; rd.lda = H; rd.gdiv = 1; rd.E = 1;
@@ -830,9 +829,9 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   g.f0 = P.part_ml; g.f1 = P.zlab; g.labels = labels; g.ignore_index = ignore_index;
   g.V = (int)V; g.ntile_base = 0;
   HIP_TRY(launch_gemm(L->qtype, EPI_CE_FWD, P.tc_fwd, g, st), "ce: logits pass");
-  HIP_TRY(launch_ce_merge(P.part_ml, g.ntiles, T, P.zlab, labels, V, ignore_index, P.nvalid, lse,
-                          loss, P.term, st),
-          "ce: log-sum-exp merge");
+  HIP_TRY(launch_ce_merge(P.part_ml, g.ntiles, T, P.zlab, labels, V, ignore_index, lse, P.term,
+                          P.err, P.nvalid, loss, st),
+          "ce: log-sum-exp merge, loss");
   if (!grad) return GQ_OK;
 
   int ntile_base = 0;

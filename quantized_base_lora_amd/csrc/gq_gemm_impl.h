@@ -770,12 +770,14 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     }
   } else if constexpr (EPI == EPI_DOWN_BWD) {
     // Columns are the expert's intermediate index i (< N = I); acc holds
-    // e = dY deq(Wd) + s (dY Bd) Ad.  e is staged row-major in LDS; 16
-    // threads then share a row, 8 columns each: 16-byte loads of the saved
-    // g, u, the SwiGLU backward, 16-byte stores of dg, du (bf16), and the row
-    // partials of this column tile: dw = sum e*silu(g)*u, dgB = sum dg*Bg,
-    // duB = sum du*Bu (with the stored bf16 dg, du).  Bg, Bu of the tile's
-    // columns sit in LDS for r <= 8.
+    // e = dY deq(Wd) + s (dY Bd) Ad.  e is staged row-major in LDS; 4
+    // threads then share a row, 8 columns at a time: 16-byte loads of the
+    // saved g, u, the SwiGLU backward, 16-byte stores of dg, du (bf16), and
+    // the row partials of this column tile: dw = sum e*silu(g)*u, dgB =
+    // sum dg*Bg, duB = sum du*Bu (with the stored bf16 dg, du).  Bg, Bu of
+    // the tile's columns sit in LDS, 8 ranks at a time: rank 16 takes a
+    // second pass over the rows for ranks 8..15 (recomputing dg, du, no
+    // stores).
     constexpr int ZD = BN + 4;
     float* Z = reinterpret_cast<float*>(smem);
     float* Bst = Z + BM * ZD;  // [2][BN][8]
@@ -788,14 +790,6 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
       for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) Z[LR(a, v) * ZD + LC(b)] = acc[a][b][v];
-    if (r <= 8) {
-      for (int idx = tid; idx < 2 * BN * 8; idx += NTHR) {
-        const int mat = idx / (BN * 8), c = (idx >> 3) % BN, j = idx & 7;
-        const int col = n0 + c;
-        Bst[idx] = (j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + j] : 0.f;
-      }
-    }
-    __syncthreads();
     // 4 threads per tile row, 4 chunks of 8 columns each (a wave's g, u
     // loads and dg, du stores cover 16 rows x 64 contiguous bytes per
     // chunk), 64 rows per pass; the row partials are summed over the row's
@@ -803,8 +797,9 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
     // thread
     constexpr int TPR = 4, RPP = NTHR / TPR, CPT = BN / TPR / 8;
     const int cq = tid % TPR, rsub = tid / TPR;
-    auto segment = [&](auto rc) {
+    auto segment = [&](auto rc, const int jb) {
       constexpr int R = decltype(rc)::value;
+      const bool first = jb == 0;
       for (int pass = 0; pass < BM / RPP; ++pass) {
         if (r0 + pass * RPP >= r1) break;  // workgroup-uniform: no rows left
         const int row = pass * RPP + rsub;
@@ -845,29 +840,19 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
               dgp[t2] = pack_bf2(dgv[0], dgv[1]);
               dup[t2] = pack_bf2(duv[0], duv[1]);
             }
-            *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
-            *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
-            // rank partials of the eight columns (with the stored bf16 dg, du):
-            // R <= 8 from the LDS slices, R = 16 from global memory
+            if (first) {
+              *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
+              *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
+            }
+            // rank partials of the eight columns (with the stored bf16 dg, du)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               const float dq = __builtin_bit_cast(float, (dgp[t >> 1] >> (16 * (t & 1))) << 16);
               const float uq = __builtin_bit_cast(float, (dup[t >> 1] >> (16 * (t & 1))) << 16);
-              float bg[R], bu[R];
-              if constexpr (R <= 8) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                  bg[j] = Bst[(lc + t) * 8 + j];
-                  bu[j] = Bst[(BN + lc + t) * 8 + j];
-                }
-              } else {
-                load_rank<R>(Bg + (int64_t)(c + t) * r, r, bg);
-                load_rank<R>(Bu + (int64_t)(c + t) * r, r, bu);
-              }
 #pragma unroll
               for (int j = 0; j < R; ++j) {
-                ag[j] += dq * bg[j];
-                au[j] += uq * bu[j];
+                ag[j] += dq * Bst[(lc + t) * 8 + j];
+                au[j] += uq * Bst[(BN + lc + t) * 8 + j];
               }
             }
           }
@@ -883,23 +868,30 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         }
         if (cq == 0 && pr < r1) {
           float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width;
-          dst[0] = dw;
+          if (first) dst[0] = dw;
 #pragma unroll
           for (int j = 0; j < R; ++j) {
-            if (j < r) {
-              dst[1 + j] = ag[j];
-              dst[1 + r + j] = au[j];
+            if (jb + j < r) {
+              dst[1 + jb + j] = ag[j];
+              dst[1 + r + jb + j] = au[j];
             }
           }
         }
       }
     };
-    if (r <= 4)
-      segment(IntC<4>{});
-    else if (r <= 8)
-      segment(IntC<8>{});
-    else
-      segment(IntC<16>{});
+    for (int jb = 0; jb < r; jb += 8) {
+      if (jb) __syncthreads();  // the previous pass is done with Bst
+      for (int idx = tid; idx < 2 * BN * 8; idx += NTHR) {
+        const int mat = idx / (BN * 8), c = (idx >> 3) % BN, j = idx & 7;
+        const int col = n0 + c;
+        Bst[idx] = (jb + j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + jb + j] : 0.f;
+      }
+      __syncthreads();
+      if (r - jb <= 4)
+        segment(IntC<4>{}, jb);
+      else
+        segment(IntC<8>{}, jb);
+    }
   } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
     // acc holds the logits z of this tile (adapter term included)
     float* Z = reinterpret_cast<float*>(smem);
@@ -1056,7 +1048,7 @@ hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI == EPI_LIN || EPI == EPI_SWIGLU || EPI == EPI_CE_FWD) {
     if (tile_skinny(tilecfg)) return launch_skinny<QT, EPI>(tile_bm(tilecfg) / 16, a, st);
   }
-  if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
+  if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD || EPI == EPI_DOWN_BWD) {
     if (tile_skinny(tilecfg)) {
       if (tile_bm(tilecfg) > 32) return hipErrorInvalidValue;
       return launch_skinny_nn<QT, EPI>(tile_bm(tilecfg) / 16, a, st);

@@ -238,12 +238,12 @@ hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int3
                               hipStream_t st);
 
 // LM head helpers
-hipError_t launch_ce_prep(const int64_t* labels, int64_t T, int64_t V, int64_t ignore_index,
-                          int32_t* err, float* nvalid, hipStream_t st);
-// term: [T] scratch for the per-token loss terms
+// term: [T] scratch for the per-token loss terms.  Also writes nvalid (the
+// number of labels in [0, V)), err (1 if a label is neither valid nor the
+// ignore index) and the loss; lse and the gradient passes read nothing else.
 hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, const float* zlab,
-                           const int64_t* labels, int64_t V, int64_t ignore_index,
-                           const float* nvalid, float* lse, float* loss, float* term,
+                           const int64_t* labels, int64_t V, int64_t ignore_index, float* lse,
+                           float* term, int32_t* err, float* nvalid, float* loss,
                            hipStream_t st);
 hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
                               int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st);

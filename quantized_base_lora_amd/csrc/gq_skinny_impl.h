@@ -38,6 +38,9 @@
 //    sum-exp partials of the workgroup's 128 vocabulary rows, label logit).
 //  Requires K % 256 == 0 and 16-byte aligned weight and activation rows;
 //  the host falls back to the tile GEMM otherwise.
+//
+// The second kernel in this file, skinny_nn_kernel, is the transposed (NN)
+// counterpart for the backward data gradient; its own comment describes it.
 #pragma once
 #include "gq_gemm_impl.h"
 
@@ -250,9 +253,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
   // wrow.  Adapter term in fp32.
   const int r = p.r;
   const float s_ = p.s;
-  auto fold = [&](auto rc) {
-    constexpr int R = decltype(rc)::value;
-    if (!wok) return;
+  // four ranks at a time; every row's loads of a chunk are issued together
+  // (rows past the tile read the first row and add nothing)
+  if (wok) {
     const float* Bm;
     const float* X;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -265,28 +268,33 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
       Bm = p.lB0 + (int64_t)e * p.lB_estride;
       X = p.rv0;
     }
-    float bv[R];
-    load_rank<R>(Bm + (int64_t)wrow * r, r, bv);
+    Bm += (int64_t)wrow * r;
+    float t[RG][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
-#pragma unroll 1
-      for (int v = 0; v < 4; ++v) {
-        const int64_t pr = r0 + rg * 16 + 4 * q + v;
-        if (pr >= r1) continue;
-        float xv[R];
-        load_rank<R>(X + pr * r, r, xv);
-        float t = 0.f;
 #pragma unroll
-        for (int j = 0; j < R; ++j) t += xv[j] * bv[j];
-        acc[rg][v] += s_ * t;
-      }
-  };
-  if (r <= 4)
-    fold(IntC<4>{});
-  else if (r <= 8)
-    fold(IntC<8>{});
-  else
-    fold(IntC<16>{});
+      for (int v = 0; v < 4; ++v) t[rg][v] = 0.f;
+#pragma unroll 1
+    for (int jc = 0; jc < r; jc += 4) {
+      float bv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) bv[jj] = jc + jj < r ? Bm[jc + jj] : 0.f;
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t pr = r0 + rg * 16 + 4 * q + v;
+          const float* xr = X + (pr < r1 ? pr : r0) * r + jc;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) t[rg][v] += (jc + jj < r ? xr[jj] : 0.f) * bv[jj];
+        }
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (r0 + rg * 16 + 4 * q + v < r1) acc[rg][v] += s_ * t[rg][v];
+  }
 
   if constexpr (EPI == EPI_LIN) {
     if (!wok) return;
@@ -390,40 +398,242 @@ hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st) {
 
 // Skinny NN MMQ (backward dX = dY deq(W) for few rows per weight): the
 // reduction runs over weight rows, the outputs over a row's elements.  A
-// workgroup (8 waves) owns 16 * RG output rows by 256 output columns (8
-// blocks of every weight row, one 16-byte aligned segment); wave w owns the
-// 32 columns of block w.  Per step of 64 weight rows:
-//  * the 64 row segments are read with coalesced 16-byte loads into a shared
-//    LDS tile (double-buffered, one barrier per step; the next step's loads
-//    are in flight meanwhile);
-//  * lane l of wave w decodes block w of step row l and writes its 32 bf16
-//    values row-major into the wave's own LDS region, read back transposed
-//    (ds_read_b64_tr_b16) as the B operand of v_mfma_f32_16x16x32_bf16;
+// workgroup (8 waves) owns 16 * RG output rows by 128 output columns (4
+// blocks of every weight row); wave w owns the 32 columns of block w % 4 in
+// reduction group w / 4.  Per step of 128 weight rows:
+//  * the 128 row segments are read with coalesced 8-byte loads into a
+//    shared LDS tile (double-buffered, one barrier per step; the next
+//    step's loads are in flight meanwhile);
+//  * lane l of wave w decodes block w % 4 of step row 64 (w / 4) + l and
+//    writes its 32 bf16 values row-major into the wave's own LDS region,
+//    read back transposed (ds_read_b64_tr_b16) as the B operand of
+//    v_mfma_f32_16x16x32_bf16: reduction group g takes rows 64g .. 64g+63
+//    of every step;
 //  * the A operand (activation rows x 32 reduction rows) is read straight
 //    from global memory; rows past the tile or the reduction are zero.
+// The two groups' partial sums meet in LDS (group 0 + group 1, a fixed
+// order).  A launch has twice the workgroups and half the sequential steps
+// of one with 256 columns and 64-row steps: these launches are short grids
+// whose time is the latency of each workgroup's chain of steps.
 // The adapter term s * (X . A[:, col]) is added in fp32 in the epilogue.
-// Epilogues: EPI_LIN_BWD (bf16 dX) and EPI_GATEUP_BWD (reduction over the
-// gate rows with dg, then the up rows with du; bf16 dX rows).
-constexpr int SKN_COLS = 256;  // output columns per workgroup
+// Epilogues: EPI_LIN_BWD (bf16 dX), EPI_GATEUP_BWD (reduction over the
+// gate rows with dg, then the up rows with du; bf16 dX rows) and
+// EPI_DOWN_BWD (the SwiGLU backward on the tile's e = dY deq(Wd) + adapter:
+// e staged in LDS, one thread per 8 columns of a row with 16-byte g/u loads
+// and dg/du stores, row partials dw, dg.Bg, du.Bu of the 128 columns summed
+// over the row's 16 threads by xor shuffles in a fixed order).
+constexpr int SKN_COLS = 128;  // output columns per workgroup
+constexpr int SKN_ROWS = 128;  // reduction rows per step (two groups of 64)
+
+// Adapter term of a skinny NN tile, s * sum_j X[row][j] * Y[j][col] (TWO:
+// plus the second projection's X1, Y1), at the accumulator positions of a
+// group-0 lane (row r0 + 16 rg + 4q + v, column c0 + 32 wave + 16 g + nl);
+// zero outside the tile.
+template <int RG, bool TWO>
+__device__ __forceinline__ void nn_adapter(const GemmArgs& p, const float* Y0, const float* Y1,
+                                           int64_t r0, int64_t r1, int c0, float (&ad)[RG][2][4]) {
+  const int lane = threadIdx.x & 63, cg = (threadIdx.x >> 6) & 3;
+  const int nl = lane & 15, q = lane >> 4;
+  const int r = p.r;
+  float t[RG][2][4];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[rg][g][v] = 0.f;
+  // four ranks at a time, every load of a chunk issued together
+#pragma unroll 1
+  for (int jc = 0; jc < r; jc += 4) {
+    float y0[2][4], y1[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int col = c0 + 32 * cg + 16 * g + nl;
+      const bool okc = col < p.N;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bool ok = okc && jc + jj < r;
+        y0[g][jj] = ok ? Y0[(int64_t)(jc + jj) * p.N + col] : 0.f;
+        if constexpr (TWO) y1[g][jj] = ok ? Y1[(int64_t)(jc + jj) * p.N + col] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pr = r0 + rg * 16 + 4 * q + v;
+        const bool okr = pr < r1;
+        float x0[4], x1[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const bool ok = okr && jc + jj < r;
+          x0[jj] = ok ? p.rv0[pr * r + jc + jj] : 0.f;
+          if constexpr (TWO) x1[jj] = ok ? p.rv1[pr * r + jc + jj] : 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            t[rg][g][v] += x0[jj] * y0[g][jj];
+            if constexpr (TWO) t[rg][g][v] += x1[jj] * y1[g][jj];
+          }
+      }
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ad[rg][g][v] = p.s * t[rg][g][v];
+}
+
+// SwiGLU backward on a skinny NN tile (RT = 16 RG rows x 128 columns of the
+// intermediate index).  acc (valid in the group-0 waves) holds dY deq(Wd);
+// Z (LDS, [RT][128 + 4] floats) and Bst (LDS, [2][128][8]) are free when
+// this runs; every thread of the workgroup calls it.
+template <int RG>
+__device__ __forceinline__ void skinny_down_epilogue(const GemmArgs& p, const f32x4 (&acc)[RG][2],
+                                                     int e, int64_t r0, int64_t r1, int c0,
+                                                     int ntile, float* Z, float* Bst) {
+  constexpr int RT = 16 * RG, ZD = SKN_COLS + 4, NT = 64 * SK_WAVES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+  const int r = p.r;
+  const float* Ad = p.lA0 + (int64_t)e * p.lA_estride;
+  const float* Bg = p.lB1 + (int64_t)e * p.lB_estride;
+  const float* Bu = p.lB2 + (int64_t)e * p.lB_estride;
+  // e = acc + s (dY Bd)[row] . Ad[:, col], staged by the group-0 waves
+  if (wave < 4) {
+    float ad[RG][2][4];
+    nn_adapter<RG, false>(p, Ad, nullptr, r0, r1, c0, ad);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int lc = 32 * wave + 16 * g + nl;
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Z[(rg * 16 + 4 * q + v) * ZD + lc] = acc[rg][g][v] + ad[rg][g][v];
+    }
+  }
+  // 16 threads per row (8 columns each), NT / 16 rows per pass
+  constexpr int TPR = SKN_COLS / 8, RPP = NT / TPR;
+  static_assert(RT <= RPP, "one pass covers the tile's rows");
+  const int cq = tid % TPR, row = tid / TPR;
+  const int width = 1 + 2 * r;
+  auto rows = [&](auto rc, const int jb) {
+    constexpr int R = decltype(rc)::value;
+    const bool first = jb == 0;
+    const int64_t pr = r0 + row;
+    float dw = 0.f, ag[R], au[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) ag[j] = au[j] = 0.f;
+    const int lc = cq * 8;
+    const int c = c0 + lc;
+    if (row < RT && pr < r1 && c < p.N) {  // N % 8 == 0: whole 8-column chunks
+      const float wp = p.wflat[p.sorted[pr]];
+      const int64_t o = pr * p.ldo + c;
+      const uint4 g8 = *reinterpret_cast<const uint4*>(p.s0 + o);
+      const uint4 u8 = *reinterpret_cast<const uint4*>(p.s1 + o);
+      const float4 e0 = *reinterpret_cast<const float4*>(Z + row * ZD + lc);
+      const float4 e1 = *reinterpret_cast<const float4*>(Z + row * ZD + lc + 4);
+      const uint32_t gw[4] = {g8.x, g8.y, g8.z, g8.w}, uw[4] = {u8.x, u8.y, u8.z, u8.w};
+      const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+      uint32_t dgp[4], dup[4];
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        float dgv[2], duv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float gg = bf2f((uint16_t)(gw[t2] >> (16 * h)));
+          const float uu = bf2f((uint16_t)(uw[t2] >> (16 * h)));
+          const float eh = ev[2 * t2 + h];
+          const float sg = sigmoidf_(gg);
+          const float silu = gg * sg;
+          const float dh = wp * eh;
+          dgv[h] = dh * uu * sg * (1.f + gg * (1.f - sg));
+          duv[h] = dh * silu;
+          dw += eh * silu * uu;
+        }
+        dgp[t2] = pack_bf2(dgv[0], dgv[1]);
+        dup[t2] = pack_bf2(duv[0], duv[1]);
+      }
+      if (first) {
+        *reinterpret_cast<uint4*>(p.o0 + o) = make_uint4(dgp[0], dgp[1], dgp[2], dgp[3]);
+        *reinterpret_cast<uint4*>(p.o1 + o) = make_uint4(dup[0], dup[1], dup[2], dup[3]);
+      }
+      // rank partials with the stored bf16 dg, du
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float dq = __builtin_bit_cast(float, (dgp[t >> 1] >> (16 * (t & 1))) << 16);
+        const float uq = __builtin_bit_cast(float, (dup[t >> 1] >> (16 * (t & 1))) << 16);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          ag[j] += dq * Bst[(lc + t) * 8 + j];
+          au[j] += uq * Bst[(SKN_COLS + lc + t) * 8 + j];
+        }
+      }
+    }
+#pragma unroll
+    for (int o2 = 1; o2 < TPR; o2 <<= 1) {
+      dw += __shfl_xor(dw, o2, TPR);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        ag[j] += __shfl_xor(ag[j], o2, TPR);
+        au[j] += __shfl_xor(au[j], o2, TPR);
+      }
+    }
+    if (cq == 0 && row < RT && pr < r1) {
+      float* dst = p.f0 + ((int64_t)ntile * p.M + pr) * width;
+      if (first) dst[0] = dw;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (jb + j < r) {
+          dst[1 + jb + j] = ag[j];
+          dst[1 + r + jb + j] = au[j];
+        }
+      }
+    }
+  };
+  // Bg, Bu of the tile's columns in LDS, 8 ranks at a time: rank 16 takes a
+  // second pass over the rows for ranks 8..15 (dg, du recomputed, not stored)
+  for (int jb = 0; jb < r; jb += 8) {
+    if (jb) __syncthreads();  // the previous pass is done with Bst
+    for (int idx = tid; idx < 2 * SKN_COLS * 8; idx += NT) {
+      const int mat = idx / (SKN_COLS * 8), c = (idx >> 3) % SKN_COLS, j = idx & 7;
+      const int col = c0 + c;
+      Bst[idx] = (jb + j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + jb + j] : 0.f;
+    }
+    __syncthreads();  // (first pass: also Z)
+    if (r - jb <= 4)
+      rows(IntC<4>{}, jb);
+    else
+      rows(IntC<8>{}, jb);
+  }
+}
 
 template <int QT, int EPI, int RG>
 __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs p) {
-  static_assert(EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD, "NN epilogues");
+  static_assert(EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD || EPI == EPI_DOWN_BWD, "NN epilogues");
+  static_assert(SK_WAVES == 8, "four column groups x two reduction groups");
   constexpr int BS = QTraits<QT>::BS;
-  constexpr int SEGB = 8 * BS;             // bytes of a row's 8-block segment
-  constexpr int SEGQ = SEGB / 16;
-  constexpr int NCH = 64 * SEGQ;           // 16-byte chunks per step
+  constexpr int SEGB = 4 * BS;             // bytes of a row's 4-block segment (8-byte multiple)
+  constexpr int SEG8 = SEGB / 8;
+  constexpr int NCH = SKN_ROWS * SEG8;     // 8-byte chunks per step
   constexpr int NTHR = 64 * SK_WAVES;
   constexpr int CI = (NCH + NTHR - 1) / NTHR;
-  constexpr int RAWB = 64 * SEGB + 16;     // raw tile bytes (tail read slack)
+  constexpr int RAWB = SKN_ROWS * SEGB + 16;  // raw tile bytes (tail read slack)
   constexpr int DP = 40;                   // decoded row pitch (bf16): 32 + 8
   constexpr int NQ = RawBlock<QT>::NQ;
   constexpr int RT = 16 * RG;
+  static_assert(SEGB % 8 == 0, "8-byte chunks");
   __shared__ __attribute__((aligned(16))) uint8_t raw[2][RAWB];
   __shared__ __attribute__((aligned(16))) uint16_t dec[SK_WAVES][64 * DP];
+  // SwiGLU backward: Bg, Bu rows of the tile's 128 columns (8 ranks at a time)
+  __shared__ __attribute__((aligned(16))) float bst[EPI == EPI_DOWN_BWD ? 2 * SKN_COLS * 8 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int cg = wave & 3, kg = wave >> 2;  // column group, reduction group
   const int nl = lane & 15, q = lane >> 4;
 
   int bid;
@@ -454,9 +664,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
   }
   const int c0 = ntile * SKN_COLS;  // first output column (weight row element)
   const int Kr = p.K;               // reduction length (weight rows)
-  const int nsteps = (Kr + 63) / 64;
+  const int nsteps = (Kr + SKN_ROWS - 1) / SKN_ROWS;
 
-  // raw chunk loads: chunk t = row t / SEGQ of the step, bytes 16 (t % SEGQ)
+  // raw chunk loads: chunk t = row t / SEG8 of the step, bytes 8 (t % SEG8)
   // of the row's segment; rows past the reduction re-read row 0
   const uint8_t* wbase0 = p.w0 + (int64_t)e * p.w_estride + (int64_t)ntile * SEGB;
   const uint8_t* wbase1 = p.w1 ? p.w1 + (int64_t)e * p.w_estride + (int64_t)ntile * SEGB : wbase0;
@@ -467,29 +677,29 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
     const int t = i * NTHR + tid;
     cval[i] = t < NCH;
     const int tt = cval[i] ? t : 0;
-    crow[i] = tt / SEGQ;
-    coff[i] = (tt % SEGQ) * 16;
+    crow[i] = tt / SEG8;
+    coff[i] = (tt % SEG8) * 8;
   }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
-  u32x4 wr[CI];
-  auto load_w = [&](int st) {
+  typedef const __attribute__((address_space(1))) u32x2 g_u32x2;
+  auto load_w = [&](int st, u32x2 (&wr)[CI]) {
 #pragma unroll
     for (int i = 0; i < CI; ++i) {
-      int n = st * 64 + crow[i];
+      int n = st * SKN_ROWS + crow[i];
       if (n >= Kr) n = 0;
       const uint8_t* b = n >= p.wsplit ? wbase1 + (int64_t)(n - p.wsplit) * p.w_rowbytes
                                        : wbase0 + (int64_t)n * p.w_rowbytes;
-      wr[i] = *(g_u32x4*)(b + coff[i]);
+      wr[i] = *(g_u32x2*)(b + coff[i]);
     }
   };
-  auto store_w = [&](int buf) {
+  auto store_w = [&](int buf, const u32x2 (&wr)[CI]) {
 #pragma unroll
     for (int i = 0; i < CI; ++i)
-      if (cval[i]) *reinterpret_cast<u32x4*>(&raw[buf][crow[i] * SEGB + coff[i]]) = wr[i];
+      if (cval[i]) *reinterpret_cast<u32x2*>(&raw[buf][crow[i] * SEGB + coff[i]]) = wr[i];
   };
 
-  // A fragments: lane (m, q) holds A[row 16 rg + m][n0 + 32 ks + 8q .. +8]
+  // A fragments: lane (m, q) holds A[row 16 rg + m][step rows 64 kg + 32 ks + 8q .. +8]
   const uint16_t* arow[RG];
   bool aok[RG];
 #pragma unroll
@@ -503,13 +713,20 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
   const uint16_t* arow1[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) arow1[rg] = p.a1 ? arow[rg] - p.a0 + p.a1 : arow[rg];
-  auto load_a = [&](int st, int ks, int rg) -> bf16x8 {
-    const int n = st * 64 + ks * 32 + 8 * q;  // 8 reduction rows n .. n+7
-    const bool ok = aok[rg] && n < Kr;
-    const uint16_t* src = n >= p.asplit ? arow1[rg] + (n - p.asplit) : arow[rg] + n;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (ok) v = *reinterpret_cast<const uint4*>(src);
-    return __builtin_bit_cast(bf16x8, v);
+  auto arow_n = [&](int st, int ks) { return st * SKN_ROWS + kg * 64 + ks * 32 + 8 * q; };
+  auto load_a = [&](int st, bf16x8 (&af)[2][RG]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const int n = arow_n(st, ks);  // 8 reduction rows n .. n+7
+        const bool ok = aok[rg] && n < Kr;
+        const uint16_t* src = n >= p.asplit ? arow1[rg] + (n - p.asplit) : arow[rg] + n;
+        // unconditional load (from the row start when out of range), zeroed
+        // at its use: a conditional load, or a mask applied here, would make
+        // the loads wait right away or with the weight loads issued later
+        af[ks][rg] = *reinterpret_cast<const bf16x8*>(ok ? src : arow[rg]);
+      }
   };
 
   // transposed reads: lane 16g + 4t + m addresses decoded row 8g + t (+4),
@@ -527,20 +744,13 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[rg][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_w(0);
-  for (int st = 0; st < nsteps; ++st) {
+  // one step of 128 reduction rows whose raw segments sit in raw[st & 1]
+  auto compute_step = [&](int st, const bf16x8 (&af)[2][RG]) {
     const int buf = st & 1;
-    store_w(buf);
-    if (st + 1 < nsteps) load_w(st + 1);
-    bf16x8 af[2][RG];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) af[ks][rg] = load_a(st, ks, rg);
     __syncthreads();
-    // decode block `wave` of step row `lane` into the wave's region
+    // decode block cg of step row 64 kg + lane into the wave's region
     {
-      const int off = lane * SEGB + wave * BS;
+      const int off = (kg * 64 + lane) * SEGB + cg * BS;
       RawBlock<QT> rb;
       if constexpr (QT == QT_Q2_DM) {
         const uint32_t* d = reinterpret_cast<const uint32_t*>(&raw[buf][off]);
@@ -578,33 +788,85 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
         const v8i16 both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         const bf16x8 b = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-          acc[rg][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][rg], b, acc[rg][g], 0, 0, 0);
+        for (int rg = 0; rg < RG; ++rg) {
+          // rows past the tile or the reduction: zero A fragments
+          const uint32_t m = opaque_mask(aok[rg] && arow_n(st, ks) < Kr);
+          u32x4 av = __builtin_bit_cast(u32x4, af[ks][rg]);
+          av &= m;
+          acc[rg][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), b,
+                                                               acc[rg][g], 0, 0, 0);
+        }
       }
+  };
+
+  // Two-slot register ring: step s's weight chunks and A fragments sit in
+  // slot s & 1 and are loaded one step ahead.  Loads past the last step
+  // re-read it.
+  u32x2 wr[2][CI];
+  bf16x8 af[2][2][RG];
+  load_w(0, wr[0]);
+  load_a(0, af[0]);
+  int st = 0;
+  for (; st + 2 <= nsteps; st += 2) {
+    store_w(0, wr[0]);
+    load_w(min(st + 1, nsteps - 1), wr[1]);
+    load_a(min(st + 1, nsteps - 1), af[1]);
+    compute_step(st, af[0]);
+    store_w(1, wr[1]);
+    load_w(min(st + 2, nsteps - 1), wr[0]);
+    load_a(min(st + 2, nsteps - 1), af[0]);
+    compute_step(st + 1, af[1]);
+  }
+  if (st < nsteps) {
+    store_w(0, wr[0]);
+    compute_step(st, af[0]);
   }
 
-  // ---- epilogue: acc[rg][g][v] at row r0 + 16 rg + 4q + v, column
-  // c0 + 32 wave + 16 g + nl.  Adapter term in fp32:
+  // ---- the two reduction groups meet: group 1's sums through LDS, added
+  // to group 0's (fixed order)
+  __syncthreads();  // every wave is done with the raw and decode regions
+  float* red = reinterpret_cast<float*>(&dec[0][0]);  // [4][RG * 8][64]
+  if (kg == 1) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((cg * RG + rg) * 8 + g * 4 + v) * 64 + lane] = acc[rg][g][v];
+  }
+  __syncthreads();
+  if (kg == 0) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rg][g][v] += red[((cg * RG + rg) * 8 + g * 4 + v) * 64 + lane];
+  }
+
+  // ---- epilogue: group 0's acc[rg][g][v] at row r0 + 16 rg + 4q + v,
+  // column c0 + 32 cg + 16 g + nl.  Adapter term in fp32:
   //   + s * sum_j X(row, j) * A[j][col]   (GATEUP: both projections)
-  const int r = p.r;
-  const float s_ = p.s;
   const float* Y0 = p.lA0 + (int64_t)e * p.lA_estride;
   const float* Y1 = EPI == EPI_GATEUP_BWD ? p.lA1 + (int64_t)e * p.lA_estride : nullptr;
+  if constexpr (EPI == EPI_DOWN_BWD) {
+    __syncthreads();  // group 0 is done reading the partial sums
+    skinny_down_epilogue<RG>(p, acc, e, r0, r1, c0, ntile, reinterpret_cast<float*>(&dec[0][0]), bst);
+    return;
+  }
+  if (kg != 0) return;
+  float ad[RG][2][4];
+  nn_adapter<RG, EPI == EPI_GATEUP_BWD>(p, Y0, Y1, r0, r1, c0, ad);
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int col = c0 + 32 * wave + 16 * g + nl;
+    const int col = c0 + 32 * cg + 16 * g + nl;
     if (col >= p.N) continue;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
-#pragma unroll 1
+#pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t pr = r0 + rg * 16 + 4 * q + v;
-        if (pr >= r1) continue;
-        float t = 0.f;
-        for (int j = 0; j < r; ++j) t += p.rv0[pr * r + j] * Y0[(int64_t)j * p.N + col];
-        if constexpr (EPI == EPI_GATEUP_BWD)
-          for (int j = 0; j < r; ++j) t += p.rv1[pr * r + j] * Y1[(int64_t)j * p.N + col];
-        p.o0[pr * p.ldo + col] = f2bf(acc[rg][g][v] + s_ * t);
+        if (pr < r1) p.o0[pr * p.ldo + col] = f2bf(acc[rg][g][v] + ad[rg][g][v]);
       }
   }
 }

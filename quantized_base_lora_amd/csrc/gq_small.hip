@@ -607,38 +607,7 @@ __global__ void down_finish_kernel(const float* __restrict__ part, int32_t ntile
 }
 
 // --------------------------------------------------------- cross entropy
-__global__ void ce_prep_kernel(const int64_t* __restrict__ labels, int64_t T, int64_t V,
-                               int64_t ignore_index, int32_t* __restrict__ err,
-                               float* __restrict__ nvalid) {
-  __shared__ int32_t cnt[256];
-  __shared__ int32_t bad[256];
-  int c = 0, b = 0;
-  for (int64_t t = threadIdx.x; t < T; t += blockDim.x) {
-    const int64_t l = labels[t];
-    if (l == ignore_index) continue;
-    if (l >= 0 && l < V) ++c; else ++b;
-  }
-  cnt[threadIdx.x] = c;
-  bad[threadIdx.x] = b;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) {
-      cnt[threadIdx.x] += cnt[threadIdx.x + o];
-      bad[threadIdx.x] += bad[threadIdx.x + o];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    *nvalid = (float)cnt[0];
-    *err = bad[0] ? 1 : 0;
-  }
-}
-
-// per token: ordered online merge of the (max, sumexp) partials
-// Merge the per-tile (max, sum exp) partials [ntiles][T][2] of each token
-// into lse.  A block takes 8 tokens with 32 tile lanes each; lane g merges
-// tiles g, g+32, ... online and the 32 lane results are merged in lane order
-// through LDS (deterministic).
+// Online (max, sum exp) merge of log-sum-exp partials.
 __device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2) {
   if (m2 == -INFINITY) return;
   if (m2 > m) {
@@ -649,27 +618,46 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2
   }
 }
 
-__global__ __launch_bounds__(256) void ce_merge_kernel(const float* __restrict__ part,
-                                                       int32_t ntiles, int64_t T,
-                                                       const float* __restrict__ zlab,
-                                                       const int64_t* __restrict__ labels, int64_t V,
-                                                       int64_t ignore_index, float* __restrict__ lse,
-                                                       float* __restrict__ term) {
-  __shared__ float2 red[32][8];
-  const int ti = threadIdx.x & 7, g = threadIdx.x >> 3;
-  const int64_t t = (int64_t)blockIdx.x * 8 + ti;
+// Merge the per-tile (max, sum exp) partials [ntiles][T][2] of each token
+// into lse.  A block of NT threads takes NT/LPT tokens with LPT lanes each;
+// lane g merges tiles g, g+LPT, ... in order (eight loads in flight), and the
+// LPT lane results are merged by a fixed pairwise tree in LDS, so the result
+// does not depend on scheduling.  term[t] = lse - z[label] for a valid label.
+template <int NT, int LPT>
+__device__ __forceinline__ void ce_merge_tokens(const float* __restrict__ part, int32_t ntiles,
+                                                int64_t T, int64_t t0,
+                                                const float* __restrict__ zlab,
+                                                const int64_t* __restrict__ labels, int64_t V,
+                                                int64_t ignore_index, float* __restrict__ lse,
+                                                float* __restrict__ term, float2* red) {
+  constexpr int TPB = NT / LPT;
+  const int ti = threadIdx.x % TPB, seg = threadIdx.x / TPB;
+  const int64_t t = t0 + ti;
   float m = -INFINITY, l = 0.f;
   if (t < T) {
-#pragma unroll 4
-    for (int nt = g; nt < ntiles; nt += 32) {
-      const float2 v = *reinterpret_cast<const float2*>(part + ((int64_t)nt * T + t) * 2);
-      lse_merge(m, l, v.x, v.y);
+    for (int nb = seg; nb < ntiles; nb += 8 * LPT) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int nt = nb + u * LPT;
+        v[u] = nt < ntiles ? *reinterpret_cast<const float2*>(part + ((int64_t)nt * T + t) * 2)
+                           : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lse_merge(m, l, v[u].x, v[u].y);
     }
   }
-  red[g][ti] = make_float2(m, l);
-  __syncthreads();
-  if (g == 0 && t < T) {
-    for (int k = 1; k < 32; ++k) lse_merge(m, l, red[k][ti].x, red[k][ti].y);
+  red[threadIdx.x] = make_float2(m, l);
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) {
+    __syncthreads();
+    if (seg < o) {
+      const float2 q = red[(seg + o) * TPB + ti];
+      lse_merge(m, l, q.x, q.y);
+      red[threadIdx.x] = make_float2(m, l);
+    }
+  }
+  if (seg == 0 && t < T) {
     const float v = m + __logf(l);
     lse[t] = v;
     const int64_t lab = labels[t];
@@ -677,21 +665,80 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float* __restrict__
   }
 }
 
-__global__ void ce_loss_kernel(const float* __restrict__ term, int64_t T,
-                               const float* __restrict__ nvalid, float* __restrict__ loss) {
-  __shared__ float sh[1024];
+template <int LPT>
+__global__ __launch_bounds__(256) void ce_merge_kernel(const float* __restrict__ part,
+                                                       int32_t ntiles, int64_t T,
+                                                       const float* __restrict__ zlab,
+                                                       const int64_t* __restrict__ labels, int64_t V,
+                                                       int64_t ignore_index, float* __restrict__ lse,
+                                                       float* __restrict__ term) {
+  __shared__ float2 red[256];
+  ce_merge_tokens<256, LPT>(part, ntiles, T, (int64_t)blockIdx.x * (256 / LPT), zlab, labels, V,
+                            ignore_index, lse, term, red);
+}
+
+// Loss over the per-token terms, with the label checks: nvalid = number of
+// labels in [0, V); err = 1 if a label is neither valid nor ignore_index.
+// Fixed-order sums (one thread per strided subset, then a tree).
+template <int NT>
+__device__ __forceinline__ void ce_loss_block(const float* __restrict__ term,
+                                              const int64_t* __restrict__ labels, int64_t T,
+                                              int64_t V, int64_t ignore_index,
+                                              int32_t* __restrict__ err, float* __restrict__ nvalid,
+                                              float* __restrict__ loss, float* sh, int* shc) {
   float acc = 0.f;
-  for (int64_t t = threadIdx.x; t < T; t += blockDim.x) acc += term[t];
+  int c = 0, b = 0;
+  for (int64_t t = threadIdx.x; t < T; t += NT) {
+    acc += term[t];
+    const int64_t lab = labels[t];
+    if (lab == ignore_index) continue;
+    if (lab >= 0 && lab < V) ++c; else ++b;
+  }
   sh[threadIdx.x] = acc;
+  shc[threadIdx.x] = c;
+  shc[NT + threadIdx.x] = b;
   __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      sh[threadIdx.x] += sh[threadIdx.x + o];
+      shc[threadIdx.x] += shc[threadIdx.x + o];
+      shc[NT + threadIdx.x] += shc[NT + threadIdx.x + o];
+    }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const float nv = *nvalid;
+    const float nv = (float)shc[0];
+    *nvalid = nv;
+    *err = shc[NT] ? 1 : 0;
     *loss = nv > 0.f ? sh[0] / nv : 0.f;
   }
+}
+
+__global__ __launch_bounds__(1024) void ce_loss_kernel(const float* __restrict__ term,
+                                                       const int64_t* __restrict__ labels,
+                                                       int64_t T, int64_t V, int64_t ignore_index,
+                                                       int32_t* __restrict__ err,
+                                                       float* __restrict__ nvalid,
+                                                       float* __restrict__ loss) {
+  __shared__ float sh[1024];
+  __shared__ int shc[2048];
+  ce_loss_block<1024>(term, labels, T, V, ignore_index, err, nvalid, loss, sh, shc);
+}
+
+// Few tokens: merge, loss and label checks in one block of 1024 threads.
+template <int LPT>
+__global__ __launch_bounds__(1024) void ce_merge_loss_kernel(
+    const float* __restrict__ part, int32_t ntiles, int64_t T, const float* __restrict__ zlab,
+    const int64_t* __restrict__ labels, int64_t V, int64_t ignore_index, float* __restrict__ lse,
+    float* __restrict__ term, int32_t* __restrict__ err, float* __restrict__ nvalid,
+    float* __restrict__ loss) {
+  __shared__ float2 red[1024];
+  __shared__ int shc[2048];
+  ce_merge_tokens<1024, LPT>(part, ntiles, T, 0, zlab, labels, V, ignore_index, lse, term, red);
+  __threadfence_block();
+  __syncthreads();
+  ce_loss_block<1024>(term, labels, T, V, ignore_index, err, nvalid, loss,
+                      reinterpret_cast<float*>(red), shc);
 }
 
 __global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, const float* __restrict__ GB,
@@ -916,20 +963,45 @@ hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int3
   return hipGetLastError();
 }
 
-hipError_t launch_ce_prep(const int64_t* labels, int64_t T, int64_t V, int64_t ignore_index,
-                          int32_t* err, float* nvalid, hipStream_t st) {
-  hipLaunchKernelGGL(ce_prep_kernel, dim3(1), dim3(256), 0, st, labels, T, V, ignore_index, err,
-                     nvalid);
-  return hipGetLastError();
-}
-
 hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, const float* zlab,
-                           const int64_t* labels, int64_t V, int64_t ignore_index,
-                           const float* nvalid, float* lse, float* loss, float* term,
+                           const int64_t* labels, int64_t V, int64_t ignore_index, float* lse,
+                           float* term, int32_t* err, float* nvalid, float* loss,
                            hipStream_t st) {
-  hipLaunchKernelGGL(ce_merge_kernel, dim3(blocks_for(T, 8)), dim3(256), 0, st, part_ml, ntiles, T,
-                     zlab, labels, V, ignore_index, lse, term);
-  hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, term, T, nvalid, loss);
+  int lpt1 = 256;
+  while ((int64_t)lpt1 * T > 1024) lpt1 /= 2;
+  if (T <= 64 && (int64_t)lpt1 * 24 >= ntiles) {
+    // few tokens and partials: one block of 1024 threads, lpt1 lanes per token
+    const int lpt = lpt1;
+#define GQ_CE1(L) \
+  hipLaunchKernelGGL(ce_merge_loss_kernel<L>, dim3(1), dim3(1024), 0, st, part_ml, ntiles, T, zlab, \
+                     labels, V, ignore_index, lse, term, err, nvalid, loss)
+    switch (lpt) {
+      case 16: GQ_CE1(16); break;
+      case 32: GQ_CE1(32); break;
+      case 64: GQ_CE1(64); break;
+      case 128: GQ_CE1(128); break;
+      default: GQ_CE1(256); break;
+    }
+#undef GQ_CE1
+    return hipGetLastError();
+  }
+  // lanes per token: enough that each lane merges at most ~16 partials
+  int lpt = 16;
+  while (lpt < 256 && (int64_t)lpt * 16 < ntiles) lpt *= 2;
+  const dim3 g((unsigned)blocks_for(T, 256 / lpt)), b(256);
+#define GQ_CEM(L) \
+  hipLaunchKernelGGL(ce_merge_kernel<L>, g, b, 0, st, part_ml, ntiles, T, zlab, labels, V, \
+                     ignore_index, lse, term)
+  switch (lpt) {
+    case 16: GQ_CEM(16); break;
+    case 32: GQ_CEM(32); break;
+    case 64: GQ_CEM(64); break;
+    case 128: GQ_CEM(128); break;
+    default: GQ_CEM(256); break;
+  }
+#undef GQ_CEM
+  hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, term, labels, T, V, ignore_index,
+                     err, nvalid, loss);
   return hipGetLastError();
 }
 

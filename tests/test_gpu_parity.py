@@ -200,6 +200,11 @@ MOE_CASES = [
     # at most 8 rows per expert: the gate/up backward on the skinny NN MMQ
     (24, 256, 128, 8, 2, 2, 4, 1.0),
     (16, 512, 192, 16, 2, 0, 8, 0.0),
+    # ... and with I % 256 == 0 also the down backward (SwiGLU-backward
+    # epilogue; rank 16 reads the up/gate B rows from global memory)
+    (24, 256, 256, 8, 2, 1, 4, 1.0),
+    (20, 512, 512, 16, 2, 0, 8, 0.0),
+    (16, 256, 768, 8, 4, 2, 16, 1.0),
 ]
 
 
@@ -246,6 +251,8 @@ HEAD_CASES = [
     (16, 256, 1000, 1000, 0, 0.1),
     (30, 512, 3000, 1024, 1, 0.0),
     (7, 256, 712, 712, 2, 0.2),
+    # more than 64 tokens and 256 vocabulary tiles: the multi-block merge
+    (100, 256, 40000, 16384, 0, 0.1),
 ]
 
 
