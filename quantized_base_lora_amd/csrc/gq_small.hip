@@ -13,6 +13,7 @@
 //  * the online log-sum-exp merge of the chunked cross entropy
 #include <math.h>
 #include <string.h>
+#include <type_traits>
 
 #include "gq_dev.h"
 #include "gq_internal.h"
@@ -402,58 +403,153 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const ColFinJobs jb,
 // ----------------------------------------------------------------- routing
 constexpr int ROUTE_CHUNK = 256;
 
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// Selection key of logit v of expert ex: larger key = larger logit, ties to
+// the lower expert index (the low word holds the complement of the index).
+// -0 counts as +0; NaN ranks below every number.
+__device__ __forceinline__ uint64_t topk_key(float v, int ex) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  if (v != v) o = 0u;
+  return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)ex);
 }
 
-// one wave per token; up to 16 logits per lane (E <= 1024)
+// Maximum of a 64-bit value over the wave, returned to every lane: DPP
+// exchanges within each 16-lane row (xor 1, xor 2, half mirror, mirror),
+// then the four row maxima read as scalars.  No LDS traffic, so a round
+// costs a few dozen cycles instead of six LDS permute round trips.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto step = [&](auto ctrl_c) {
+    constexpr int CTRL = decltype(ctrl_c)::value;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  };
+  step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{});  // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    m = o > m ? o : m;
+  }
+  return m;
+}
+
+// One wave selects the top k of the E <= 64 NQ logits at row: k rounds of a
+// wave arg-max over 64-bit keys, no branches.  Lane j < k returns selection j
+// (expert and weight); every lane accumulates the softmax denominator in
+// selection order, so all lanes hold the same value.
+template <int NQ>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int32_t E, int32_t k,
+                                          int lane, int& my_ex, float& my_w) {
+  uint64_t key[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int ex = lane + 64 * q;
+    key[q] = ex < E ? topk_key(row[ex], ex) : 0ull;
+  }
+  float v0 = 0.f, sum = 0.f, my_v = 0.f;
+  my_ex = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) best = key[q] > best ? key[q] : best;
+    best = wave_max_u64(best);
+    const int ex = (int)(0xffffffffu - (uint32_t)best);
+    // the logit back from the key (NaN came in as key 0: reported as NaN)
+    const uint32_t o = (uint32_t)(best >> 32);
+    const float v = o == 0u ? __builtin_nanf("") : __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+    if (j == 0) v0 = v;
+    sum += __expf(v - v0);
+    if (lane == j) { my_ex = ex; my_v = v; }
+    // retire the winner (its owner lane clears the key)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) key[q] = key[q] == best ? 0ull : key[q];
+  }
+  my_w = __expf(my_v - v0) / sum;
+}
+
+template <class F>
+__device__ __forceinline__ void with_nq(int32_t E, F&& f) {
+  if (E <= 64) f(std::integral_constant<int, 1>{});
+  else if (E <= 128) f(std::integral_constant<int, 2>{});
+  else if (E <= 256) f(std::integral_constant<int, 4>{});
+  else if (E <= 512) f(std::integral_constant<int, 8>{});
+  else f(std::integral_constant<int, 16>{});
+}
+
+// one wave per token
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int32_t E, int32_t k, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float val[16];
-  const float* row = logits + t * E;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int ex = lane + 64 * q;
-    val[q] = ex < E ? row[ex] : -INFINITY;
+  int ex;
+  float wv;
+  with_nq(E, [&](auto nq) { wave_topk<decltype(nq)::value>(logits + t * E, E, k, lane, ex, wv); });
+  if (lane < k) {
+    ids[t * k + lane] = ex;
+    w[t * k + lane] = wv;
   }
-  uint32_t taken = 0;
-  float sel_v[16];
-  int sel_i[16];
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int ex = lane + 64 * q;
-      if (ex < E && !((taken >> q) & 1u) && (bi == 0x7fffffff || better(val[q], ex, bv, bi))) {
-        bv = val[q];
-        bi = ex;
-      }
+}
+
+// Few assignments (T k <= 256): the whole routing in one block of 1024
+// threads -- top-k per token (one wave per token), expert counts, offsets,
+// and the stable scatter (an assignment's rank among the earlier ones of its
+// expert, counted over the assignment list in LDS; linear in T k, which is
+// why larger counts take the chunked kernels).
+constexpr int ROUTE_SMALL = 256;
+__global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
+                                                           int64_t T, int32_t E, int32_t k,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ w,
+                                                           int32_t* __restrict__ sorted,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ pos) {
+  __shared__ int32_t sid[ROUTE_SMALL];
+  __shared__ int32_t cnt[1024];
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = (int)(T * k);
+  for (int e = tid; e < 1024; e += 1024) cnt[e] = 0;
+  for (int64_t t = wave; t < T; t += 16) {
+    int ex;
+    float wv;
+    with_nq(E, [&](auto nq) { wave_topk<decltype(nq)::value>(logits + t * E, E, k, lane, ex, wv); });
+    if (lane < k) {
+      ids[t * k + lane] = ex;
+      w[t * k + lane] = wv;
+      sid[t * k + lane] = ex;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    sel_v[j & 15] = bv;
-    sel_i[j & 15] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
   }
-  if (lane == 0) {
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += __expf(sel_v[j] - sel_v[0]);
-    for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = sel_i[j];
-      w[t * k + j] = __expf(sel_v[j] - sel_v[0]) / sum;
-    }
+  __syncthreads();
+  if (tid < n) atomicAdd(&cnt[sid[tid]], 1);  // integer counts: order-independent
+  __syncthreads();
+  // inclusive scan over the (up to 1024) experts
+  const int c = tid < E ? cnt[tid] : 0;
+  scan[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid] = scan[tid] - c;
+  if (tid == 0) offsets[E] = scan[1023];
+  if (tid < n) {
+    const int key = sid[tid];
+    int rank = 0;
+    for (int j = 0; j < tid; ++j) rank += sid[j] == key;
+    const int p = scan[key] - cnt[key] + rank;
+    sorted[p] = tid;
+    pos[tid] = p;
   }
 }
 
@@ -931,6 +1027,11 @@ hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, in
                         float* w, int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws,
                         hipStream_t st) {
   const int64_t n = T * k;
+  if (n <= ROUTE_SMALL) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, st, logits, T, E, k, ids, w,
+                       sorted, offsets, pos);
+    return hipGetLastError();
+  }
   const int nch = (int)((n + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
   int32_t* counts = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(topk_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, logits, T, E, k, ids, w);
