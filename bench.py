@@ -85,8 +85,8 @@ COPY_BYTES = 256 << 20
 # the two MMQ launches of the linear step: kernel name fragment, threads per
 # launch (tiles x workgroup size), key in mmq_traffic.json
 MMQ_LAUNCHES = (
-    ("gemm_kernel<1, 0, 128, 128, 1>", 768 * 256, "mmq_nt_lin_q4_0_cfg2"),
-    ("gemm_kernel<1, 4, 128, 128, 2>", 256 * 512, "mmq_nn_lin_bwd_q4_0_cfg2"),
+    ("gemm_kernel<1, 0, 128, 128, 1>", 768 * 256, "mmq_nt_lin_q4_0_t2048_2048x6144"),
+    ("gemm_kernel<1, 4, 128, 128, 2>", 256 * 512, "mmq_nn_lin_bwd_q4_0_t2048_2048x6144"),
 )
 
 
@@ -343,9 +343,9 @@ def main():
     # dominant kernel: the slower of the two MMQ launches of the step
     gemm_flops = 2 * cfg.T * cfg.N * cfg.K + 2 * cfg.T * cfg.N * cfg.rank
     if bwd_ms >= fwd_ms:
-        kname, kms, kkey = "mmq_nn_dx_q4_0_t2048_2048x6144", bwd_ms, "mmq_nn_lin_bwd_q4_0_cfg2"
+        kname, kms, kkey = "mmq_nn_dx_q4_0_t2048_2048x6144", bwd_ms, "mmq_nn_lin_bwd_q4_0_t2048_2048x6144"
     else:
-        kname, kms, kkey = "mmq_nt_fwd_q4_0_t2048_2048x6144", fwd_ms, "mmq_nt_lin_q4_0_cfg2"
+        kname, kms, kkey = "mmq_nt_fwd_q4_0_t2048_2048x6144", fwd_ms, "mmq_nt_lin_q4_0_t2048_2048x6144"
     achieved = gemm_flops / (kms * 1e-3) / 1e12
     roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
