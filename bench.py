@@ -265,7 +265,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def time_steps(fn, steps, warmup):
+    def time_steps(fn, steps, warmup, graph_too=True):
         """(eager ms, graph ms) per step: `steps` calls issued from Python, then
         the same step captured once in a HIP graph and replayed `steps` times
         (no host launch work between kernels; every kernel still runs)."""
@@ -279,7 +279,7 @@ def main():
         b.record()
         torch.cuda.synchronize()
         eager = a.elapsed_time(b) / steps
-        if args.eager:
+        if args.eager or not graph_too:
             return eager, eager
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -301,7 +301,7 @@ def main():
         return eager, replayed
 
     # ------------------------------------------------------------ linear step
-    cfg = synth.CFG2
+    cfg = synth.LINEAR_Q4_0_T2048
     t0 = time.time()
     inp = synth.make_linear(cfg)
     log(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s")
@@ -352,6 +352,26 @@ def main():
                 "traffic": load_traffic(kkey), "launch_us": round(kms * 1e3, 2),
                 "other_mmq_us": round((fwd_ms if kms == bwd_ms else bwd_ms) * 1e3, 2)}
 
+    # cold operands: the same step rotating over copies of W, x and dY that
+    # together exceed the 256 MB Infinity Cache, so every step streams its
+    # operands from HBM (the timed numbers above have them cache-resident)
+    set_bytes = inp["blocks"].nbytes + 2 * cfg.T * (cfg.K + cfg.N)
+    ncopy = max(2, -(-(512 << 20) // set_bytes))
+    copies = [(gq.Proj(cfg.qtype, cfg.N, cfg.K, p.blocks.clone(), p.A, p.B, float(inp["scale"])),
+               x.clone(), dy.clone()) for _ in range(ncopy)]
+    rot = [0]
+
+    def cold_step():
+        pc, xc, dyc = copies[rot[0] % ncopy]
+        rot[0] += 1
+        yc, xac = gq.linear_lora_fwd(pc, xc)
+        return gq.linear_lora_bwd(pc, xc, xac, dyc, ws=ws)
+
+    ms_cold = time_steps(cold_step, max(K, 2 * ncopy), ncopy, graph_too=False)[0]
+    del copies
+    log(f"[bench] linear step, cold operands ({ncopy} copies, {ncopy * set_bytes / 1e6:.0f} MB): "
+        f"{ms_cold:.3f} ms ({flops / (ms_cold * 1e-3) / 1e12:.1f} TFLOP/s)")
+
     result = {
         "metric": "fused dequant-GEMM+LoRA fwd+bwd TFLOP/s & MoE-layer train tokens/s, % roofline",
         "value": round(tflops, 3),
@@ -361,6 +381,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_hip_graph": round(ms_graph, 4),
+        "ms_per_step_cold_operands": round(ms_cold, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -374,7 +395,7 @@ def main():
 
     # --------------------------------------------------------------- MoE layer
     if not args.no_moe:
-        mc = synth.CFG3
+        mc = synth.MOE_Q4_0_T2048
         t0 = time.time()
         minp = synth.make_moe(mc)
         log(f"[bench] inputs {mc.name} generated in {time.time() - t0:.1f}s")
@@ -392,10 +413,16 @@ def main():
 
         mms, mms_graph = time_steps(mstep, K, max(2, args.warmup))
         mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
+        # rows routed to each expert (one routing call outside the timed steps)
+        counts = np.diff(gq.moe_route(mlg, mc.k)[3].cpu().numpy().astype(np.int64))
+        act = counts[counts > 0]
+        route_hist = {"active_experts": int(act.size), "max_rows": int(counts.max()),
+                      "median_rows": float(np.median(counts)), "min_active_rows": int(act.min())}
         result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
                                "ms_per_step": round(mms, 4), "ms_per_step_hip_graph": round(mms_graph, 4),
                                "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
-                               "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                               "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "route_rows_per_expert": route_hist}
         log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
 
     # ------------------------------------------------------- other workloads
@@ -405,7 +432,7 @@ def main():
         def timed(fn, steps):
             return time_steps(fn, steps, 2)[0]
 
-        c1 = synth.CFG1
+        c1 = synth.LINEAR_Q8_0_T128
         i1 = synth.make_linear(c1)
         p1 = gq.Proj(c1.qtype, c1.N, c1.K, u8(i1["blocks"]), f32(i1["A"]), f32(i1["B"]),
                      float(i1["scale"]))
@@ -420,7 +447,7 @@ def main():
         extra[c1.name] = {"ms_per_step": round(m1, 4), "tflops": round(f1 / (m1 * 1e-3) / 1e12, 2)}
         log(f"[bench] {c1.name}: {m1 * 1e3:.1f} us/step")
 
-        c4 = synth.CFG4
+        c4 = synth.MOE_Q2DM_T4096_ZIPF
         t0 = time.time()
         i4 = synth.make_moe(c4)
         log(f"[bench] inputs {c4.name} generated in {time.time() - t0:.1f}s")
@@ -438,12 +465,18 @@ def main():
 
         m4 = timed(st4, max(3, K // 4))
         f4 = moe_flops(c4.T, c4.H, c4.I, c4.k, c4.rank)
+        cnt4 = np.diff(gq.moe_route(lg4, c4.k)[3].cpu().numpy().astype(np.int64))
+        act4 = cnt4[cnt4 > 0]
         extra[c4.name] = {"ms_per_step": round(m4, 4), "tokens_per_s": round(c4.T / (m4 * 1e-3), 1),
-                          "tflops": round(f4 / (m4 * 1e-3) / 1e12, 2)}
+                          "tflops": round(f4 / (m4 * 1e-3) / 1e12, 2),
+                          "route_rows_per_expert": {"active_experts": int(act4.size),
+                                                    "max_rows": int(cnt4.max()),
+                                                    "median_rows": float(np.median(cnt4)),
+                                                    "min_active_rows": int(act4.min())}}
         log(f"[bench] {c4.name}: {m4:.3f} ms/step")
         del w4, x4, dy4, lg4
 
-        c5 = synth.CFG5
+        c5 = synth.LMHEAD_Q8_0_T2048
         t0 = time.time()
         i5 = synth.make_head(c5)
         log(f"[bench] inputs {c5.name} generated in {time.time() - t0:.1f}s")
@@ -468,7 +501,7 @@ def main():
     # ------------------------------------------------- small-token sweep
     if args.sweep or args.all:
         sweep = []
-        sc = synth.CFG3
+        sc = synth.MOE_Q4_0_T2048
         t0 = time.time()
         winp = synth.make_moe(sc)  # expert weights are per-expert streams: shared by every T
         log(f"[bench] sweep weights {sc.name} generated in {time.time() - t0:.1f}s")
@@ -501,7 +534,7 @@ def main():
             log(f"[bench] sweep {tc.name}: {tms:.3f} ms, {active} experts, {gbs:.0f} GB/s "
                 f"({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
         del swts
-        hc = synth.CFG5
+        hc = synth.LMHEAD_Q8_0_T2048
         for T in (16, 64, 128):
             cfgT = synth.HeadCfg(f"lmhead_fwd_q8_0_t{T}_h2048_v151936_r4", T=T, H=hc.H, V=hc.V,
                                  qtype=hc.qtype, rank=hc.rank, alpha=hc.alpha, chunk=hc.chunk,
@@ -536,11 +569,24 @@ def main():
         from oracle import linear as ol
 
         reps, spent = 0, 0.0
+        ref = None
         while spent < args.cpu_seconds and reps < 500:
             t0 = time.perf_counter()
-            ol.run(inp)
+            ref = ol.run(inp)
             spent += time.perf_counter() - t0
             reps += 1
+        # parity of the timed step against the oracle on the same inputs
+        # (relative Frobenius error per output)
+        yg, (dxg, dAg, dBg) = step()
+        torch.cuda.synchronize()
+
+        def rel(got, key):
+            g = got.float().cpu().numpy().astype(np.float64)
+            r = np.asarray(ref[key], np.float64)
+            return float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+
+        result["parity_rel_frobenius"] = {k: f"{rel(t, k):.2e}" for k, t in
+                                          (("y", yg), ("dx", dxg), ("dA", dAg), ("dB", dBg))}
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
         result["cpu_baseline"] = {"value": round(flops * reps / spent / 1e12, 5), "unit": "TFLOP/s",
                                   "cores": threads, "kind": "oracle",

@@ -191,15 +191,16 @@ class HeadCfg:
 
 
 # The five benchmark workloads.
-CFG1 = LinearCfg("linear_q8_0_t128_1024x1024_r4", T=128, K=1024, N=1024, qtype=Q8_0, rank=4, alpha=8)
-CFG2 = LinearCfg("linear_q4_0_t2048_2048x6144_r4", T=2048, K=2048, N=6144, qtype=Q4_0, rank=4, alpha=8)
-CFG3 = MoECfg("moe_q4_0_t2048_h2048_e128k8_i768_r4", T=2048, H=2048, I=768, E=128, k=8,
-              qtype=Q4_0, rank=4, alpha=8)
-CFG4 = MoECfg("moe_q2dm_t4096_h4096_e256k8_i1024_r8_zipf", T=4096, H=4096, I=1024, E=256, k=8,
-              qtype=Q2_DM, rank=8, alpha=16, zipf=1.0)
-CFG5 = HeadCfg("lmhead_q8_0_t2048_h2048_v151936_r4", T=2048, H=2048, V=151936, qtype=Q8_0,
-               rank=4, alpha=8, chunk=4096)
-CONFIGS = {c.name: c for c in (CFG1, CFG2, CFG3, CFG4, CFG5)}
+LINEAR_Q8_0_T128 = LinearCfg("linear_q8_0_t128_1024x1024_r4", T=128, K=1024, N=1024, qtype=Q8_0, rank=4, alpha=8)
+LINEAR_Q4_0_T2048 = LinearCfg("linear_q4_0_t2048_2048x6144_r4", T=2048, K=2048, N=6144, qtype=Q4_0, rank=4, alpha=8)
+MOE_Q4_0_T2048 = MoECfg("moe_q4_0_t2048_h2048_e128k8_i768_r4", T=2048, H=2048, I=768, E=128, k=8,
+                        qtype=Q4_0, rank=4, alpha=8)
+MOE_Q2DM_T4096_ZIPF = MoECfg("moe_q2dm_t4096_h4096_e256k8_i1024_r8_zipf", T=4096, H=4096, I=1024, E=256,
+                             k=8, qtype=Q2_DM, rank=8, alpha=16, zipf=1.0)
+LMHEAD_Q8_0_T2048 = HeadCfg("lmhead_q8_0_t2048_h2048_v151936_r4", T=2048, H=2048, V=151936, qtype=Q8_0,
+                            rank=4, alpha=8, chunk=4096)
+CONFIGS = {c.name: c for c in (LINEAR_Q8_0_T128, LINEAR_Q4_0_T2048, MOE_Q4_0_T2048, MOE_Q2DM_T4096_ZIPF,
+                               LMHEAD_Q8_0_T2048)}
 
 
 def _normal(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:

@@ -40,7 +40,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("cfg", [synth.CFG1, synth.CFG2], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.LINEAR_Q8_0_T128, synth.LINEAR_Q4_0_T2048], ids=lambda c: c.name)
 @pytest.mark.parametrize("large", [False, True])
 def test_linear_full(cfg, large):
     say("fullsize linear", cfg.name, "large" if large else "sigma")
@@ -65,7 +65,7 @@ def _moe_weights(inp):
 
 
 def test_moe_q4_0_full():
-    cfg = synth.CFG3
+    cfg = synth.MOE_Q4_0_T2048
     say("fullsize moe", cfg.name)
     inp = synth.make_moe(cfg)
     wts = _moe_weights(inp)
@@ -90,9 +90,9 @@ def test_moe_q4_0_full():
 # its smallest and largest token counts (skinny forward MMQ, 16- and 32-row
 # tiles)
 SAMPLED_MOE = [
-    synth.CFG4,
-    dataclasses.replace(synth.CFG3, name="moe_q4_0_t16_h2048_e128k8_i768_r4", T=16),
-    dataclasses.replace(synth.CFG3, name="moe_q4_0_t512_h2048_e128k8_i768_r4", T=512),
+    synth.MOE_Q2DM_T4096_ZIPF,
+    dataclasses.replace(synth.MOE_Q4_0_T2048, name="moe_q4_0_t16_h2048_e128k8_i768_r4", T=16),
+    dataclasses.replace(synth.MOE_Q4_0_T2048, name="moe_q4_0_t512_h2048_e128k8_i768_r4", T=512),
 ]
 
 
@@ -152,9 +152,9 @@ def test_moe_sampled(cfg):
 
 
 HEAD_FULL = [
-    synth.CFG5,
-    dataclasses.replace(synth.CFG5, name="lmhead_q8_0_t16_h2048_v151936_r4", T=16),
-    dataclasses.replace(synth.CFG5, name="lmhead_q8_0_t32_h2048_v151936_r4", T=32),
+    synth.LMHEAD_Q8_0_T2048,
+    dataclasses.replace(synth.LMHEAD_Q8_0_T2048, name="lmhead_q8_0_t16_h2048_v151936_r4", T=16),
+    dataclasses.replace(synth.LMHEAD_Q8_0_T2048, name="lmhead_q8_0_t32_h2048_v151936_r4", T=32),
 ]
 
 
