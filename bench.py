@@ -300,6 +300,29 @@ def main():
         del graph
         return eager, replayed
 
+    def batched_ms(fn, n, reps=5):
+        """ms per call of fn: n calls captured in one HIP graph, replayed."""
+        fn()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / (reps * n)
+
     # ------------------------------------------------------------ linear step
     cfg = synth.LINEAR_Q4_0_T2048
     t0 = time.time()
@@ -497,6 +520,47 @@ def main():
                           "tflops": round(f5 / (m5 * 1e-3) / 1e12, 2)}
         log(f"[bench] {c5.name}: {m5:.3f} ms/step")
         result["other_workloads"] = extra
+
+        # RMS normalisation ahead of the linear layers (hidden 2048 and 4096,
+        # 2048 tokens): HBM-bound, against the HBM roofline; the fp64 oracle
+        # on the same inputs beside it (host cores)
+        rng = np.random.default_rng(0)
+        norm = []
+        for Tn, Hn in ((2048, 2048), (2048, 4096)):
+            xnb = synth.f32_to_bf16_bits(rng.standard_normal((Tn, Hn)).astype(np.float32))
+            dynb = synth.f32_to_bf16_bits(rng.standard_normal((Tn, Hn)).astype(np.float32))
+            wn_h = rng.uniform(0.5, 1.5, Hn).astype(np.float32)
+            xn, dyn, wn = bf(xnb), bf(dynb), f32(wn_h)
+            # launches of a few us: 50 launches captured in one HIP graph and
+            # the graph replayed, so neither host launch work nor the graph
+            # launch hides the kernels
+            fms = batched_ms(lambda: gq.rmsnorm_fwd(xn, wn), 50)
+            _, rs = gq.rmsnorm_fwd(xn, wn)
+            bms = batched_ms(lambda: gq.rmsnorm_bwd(dyn, xn, wn, rs), 50)
+            fbytes = 2 * Tn * Hn * 2 + Hn * 4 + Tn * 4
+            bbytes = 3 * Tn * Hn * 2 + Hn * 4 + Tn * 4
+            ent = {"workload": f"rmsnorm_t{Tn}_h{Hn}", "fwd_us": round(fms * 1e3, 2),
+                   "bwd_us": round(bms * 1e3, 2),
+                   "fwd_GB_per_s": round(fbytes / (fms * 1e-3) / 1e9, 1),
+                   "bwd_GB_per_s": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                   "fwd_frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "bwd_frac_hbm": round(bbytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            if not args.no_cpu:
+                from oracle import rmsnorm as orms
+                xo = synth.bf16_bits_to_f32(xnb).astype(np.float64)
+                dyo = synth.bf16_bits_to_f32(dynb).astype(np.float64)
+                reps, spent = 0, 0.0
+                while spent < 1.0:
+                    t0 = time.perf_counter()
+                    orms.forward(xo, wn_h, 1e-6)
+                    orms.backward(xo, wn_h, dyo, 1e-6)
+                    spent += time.perf_counter() - t0
+                    reps += 1
+                ent["cpu_baseline_fwd_bwd_ms"] = round(1e3 * spent / reps, 2)
+            norm.append(ent)
+            log(f"[bench] rmsnorm T {Tn} H {Hn}: fwd {fms * 1e3:.1f} us ({ent['fwd_GB_per_s']:.0f} GB/s), "
+                f"bwd {bms * 1e3:.1f} us ({ent['bwd_GB_per_s']:.0f} GB/s)")
+        result["rmsnorm"] = norm
 
     # ------------------------------------------------- small-token sweep
     if args.sweep or args.all:

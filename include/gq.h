@@ -298,6 +298,24 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* head, const uint16_t* h, const in
                          float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
                          size_t ws_bytes, void* stream);
 
+/*
+ * RMS normalisation before a quantised linear layer, emitting the bf16
+ * activation the MMQ consumes (page 2 "Show HN: LoRA over GGUF", section
+ * "Things involved in the training": Liger Kernel's RMSNorm is on the
+ * training path; the pages give no formula, this is the usual definition):
+ *   rstd[t] = 1 / sqrt(mean_i x[t][i]^2 + eps)      fp32 [T] (saved for the backward)
+ *   y[t][i] = bf16(x[t][i] * rstd[t] * w[i])          bf16 [T][H]
+ * x bf16 [T][H], w fp32 [H] (the frozen base's norm weight).  The backward
+ * returns the input gradient only (w receives none):
+ *   dx[t][j] = rstd w_j dy[t][j] - (rstd^3 / H) x[t][j] sum_i dy[t][i] w_i x[t][i]
+ * H a positive multiple of 8; x, y, dy, dx and w 16-byte aligned; eps >= 0;
+ * T = 0 is a no-op.  No workspace.  Row sums have a fixed order.
+ */
+int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                   float* rstd, void* stream);
+int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const float* rstd,
+                   int64_t T, int64_t H, uint16_t* dx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

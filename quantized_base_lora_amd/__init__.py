@@ -33,6 +33,7 @@ EXPORTS = (
     "gq_grouped_mmq_lora_fwd_workspace_size", "gq_grouped_mmq_lora_fwd",
     "gq_grouped_mmq_lora_bwd_workspace_size", "gq_grouped_mmq_lora_bwd",
     "gq_lmhead_chunked_ce_workspace_size", "gq_lmhead_chunked_ce",
+    "gq_rmsnorm_fwd", "gq_rmsnorm_bwd",
 )
 
 
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH):
         "gq_lmhead_chunked_ce_workspace_size": (sz, [P(LoraLinear), i64, i64]),
         "gq_lmhead_chunked_ce": (C.c_int, [P(LoraLinear), vp, vp, i64, i64, i64, f32, vp, vp, vp,
                                            vp, vp, vp, sz, vp]),
+        "gq_rmsnorm_fwd": (C.c_int, [vp, vp, i64, i64, f32, vp, vp, vp]),
+        "gq_rmsnorm_bwd": (C.c_int, [vp, vp, vp, vp, i64, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -228,6 +231,23 @@ def moe_combine_bwd(dxrows, pos, T: int, k: int):
     H = dxrows.shape[1]
     dx = torch.empty((T, H), dtype=torch.bfloat16, device=dxrows.device)
     _check(lib().gq_moe_combine_bwd(_ptr(dxrows), _ptr(pos), T, k, H, _ptr(dx), _stream()))
+    return dx
+
+
+def rmsnorm_fwd(x, w, eps: float = 1e-6):
+    """y = x * rstd * w (bf16 [T, H]) and rstd (fp32 [T]); w fp32 [H]."""
+    T, H = x.shape
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    rstd = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _check(lib().gq_rmsnorm_fwd(_ptr(x), _ptr(w), T, H, float(eps), _ptr(y), _ptr(rstd), _stream()))
+    return y, rstd
+
+
+def rmsnorm_bwd(dy, x, w, rstd):
+    """Input gradient of rmsnorm_fwd (w is frozen)."""
+    T, H = x.shape
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib().gq_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), T, H, _ptr(dx), _stream()))
     return dx
 
 

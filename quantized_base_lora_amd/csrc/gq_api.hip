@@ -386,6 +386,33 @@ int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, in
   return GQ_OK;
 }
 
+int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                   float* rstd, void* stream) {
+  g_err.clear();
+  if (T < 0 || H < 8 || H % 8 || H > INT_MAX || (T + 3) / 4 > INT_MAX)
+    return fail(GQ_EINVAL, "gq_rmsnorm_fwd: bad T/H (H must be a positive multiple of 8)");
+  if (!(eps >= 0.f)) return fail(GQ_EINVAL, "gq_rmsnorm_fwd: eps must be >= 0");
+  if (T == 0) return GQ_OK;
+  if (!x || !w || !y || !rstd) return fail(GQ_EINVAL, "gq_rmsnorm_fwd: NULL pointer");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+    return fail(GQ_EINVAL, "gq_rmsnorm_fwd: x, w and y must be 16-byte aligned");
+  HIP_TRY(launch_rmsnorm_fwd(x, w, T, (int32_t)H, eps, y, rstd, S(stream)), "gq_rmsnorm_fwd");
+  return GQ_OK;
+}
+
+int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const float* rstd,
+                   int64_t T, int64_t H, uint16_t* dx, void* stream) {
+  g_err.clear();
+  if (T < 0 || H < 8 || H % 8 || H > INT_MAX || (T + 3) / 4 > INT_MAX)
+    return fail(GQ_EINVAL, "gq_rmsnorm_bwd: bad T/H (H must be a positive multiple of 8)");
+  if (T == 0) return GQ_OK;
+  if (!dy || !x || !w || !rstd || !dx) return fail(GQ_EINVAL, "gq_rmsnorm_bwd: NULL pointer");
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16))
+    return fail(GQ_EINVAL, "gq_rmsnorm_bwd: dy, x, w and dx must be 16-byte aligned");
+  HIP_TRY(launch_rmsnorm_bwd(dy, x, w, rstd, T, (int32_t)H, dx, S(stream)), "gq_rmsnorm_bwd");
+  return GQ_OK;
+}
+
 int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k, int64_t H,
                        uint16_t* dx, void* stream) {
   g_err.clear();

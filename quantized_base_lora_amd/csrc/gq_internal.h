@@ -245,6 +245,12 @@ hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, cons
                            const int64_t* labels, int64_t V, int64_t ignore_index, float* lse,
                            float* term, int32_t* err, float* nvalid, float* loss,
                            hipStream_t st);
+// RMS normalisation (y = x rstd w) and its input gradient; H % 8 == 0
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int32_t H, float eps,
+                              uint16_t* y, float* rstd, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w,
+                              const float* rstd, int64_t T, int32_t H, uint16_t* dx,
+                              hipStream_t st);
 hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
                               int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st);
 // out[p][j] = wflat[sorted[p]] * in[p][j]

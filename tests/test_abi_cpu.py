@@ -156,3 +156,16 @@ def test_workspace_never_reaches_a_full_precision_weight(gq):
     assert lib.gq_grouped_mmq_lora_bwd_workspace_size(P3, 2, 1, 16384) < experts_bf16
     H = proj(gq, qtype=0, n_out=151936, n_in=2048)
     assert lib.gq_lmhead_chunked_ce_workspace_size(C.byref(H), 2048, 4096) < 151936 * 2048 * 2
+
+
+def test_rmsnorm_validation(gq):
+    lib = gq.lib()
+    assert lib.gq_rmsnorm_fwd(FAKE, FAKE, 4, 12, 1e-6, FAKE, FAKE, None) == gq.GQ_EINVAL
+    assert "multiple of 8" in gq.last_error()
+    assert lib.gq_rmsnorm_fwd(FAKE, FAKE, 4, 64, -1.0, FAKE, FAKE, None) == gq.GQ_EINVAL
+    assert lib.gq_rmsnorm_fwd(FAKE + 2, FAKE, 4, 64, 1e-6, FAKE, FAKE, None) == gq.GQ_EINVAL
+    assert "aligned" in gq.last_error()
+    assert lib.gq_rmsnorm_fwd(None, FAKE, 4, 64, 1e-6, FAKE, FAKE, None) == gq.GQ_EINVAL
+    assert lib.gq_rmsnorm_fwd(FAKE, FAKE, 0, 64, 1e-6, FAKE, FAKE, None) == gq.GQ_OK  # T = 0: no-op
+    assert lib.gq_rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE, -1, 64, FAKE, None) == gq.GQ_EINVAL
+    assert lib.gq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, 4, 64, FAKE, None) == gq.GQ_EINVAL

@@ -14,6 +14,7 @@ from oracle import blocks as ob
 from oracle import linear as ol
 from oracle import lmhead as olm
 from oracle import moe as om
+from oracle import rmsnorm as orms
 from oracle import routing as orr
 
 pytestmark = pytest.mark.gpu
@@ -292,3 +293,42 @@ def test_lmhead_bad_label_flag():
     inp["labels"][3] = -100
     ref = olm.forward_backward(inp, chunk=128)
     assert abs(float(out["loss"]) - ref["loss"]) <= 1e-3 * ref["loss"]
+
+
+# ---------------------------------------------------------------- RMSNorm
+# H up to 4096 keeps a row in registers, longer rows read x twice
+NORM_CASES = [(1, 8, 1e-6), (5, 64, 1e-6), (37, 320, 1e-2), (256, 2048, 1e-6), (64, 4096, 1e-5),
+              (33, 4104, 1e-6), (3, 8192, 1e-6)]
+
+
+@pytest.mark.parametrize("T,H,eps", NORM_CASES)
+def test_rmsnorm(T, H, eps):
+    rng = np.random.default_rng(T * 7 + H)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x *= np.exp(rng.uniform(-4, 4, (T, 1))).astype(np.float32)  # rows of very different scale
+    if T > 2:
+        x[1] = 0.0  # zero row: rstd = 1/sqrt(eps), y = 0
+    xb = synth.f32_to_bf16_bits(x)
+    w = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    dyb = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    xr = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    dyr = synth.bf16_bits_to_f32(dyb).astype(np.float64)
+    say("rmsnorm", T, H, eps)
+    y, rstd = gq.rmsnorm_fwd(bf16_dev(xb), f32_dev(w), eps)
+    dx = gq.rmsnorm_bwd(bf16_dev(dyb), bf16_dev(xb), f32_dev(w), rstd)
+    torch.cuda.synchronize()
+    ref_y, ref_r = orms.forward(xr, w, eps)
+    ref_dx = orms.backward(xr, w, dyr, eps)
+    check("rstd", host(rstd), ref_r, 1e-5)
+    check("y", host(y), ref_y)
+    check("dx", host(dx), ref_dx)
+
+
+def test_rmsnorm_deterministic():
+    rng = np.random.default_rng(11)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((100, 2048)).astype(np.float32))
+    w = f32_dev(rng.uniform(0.5, 1.5, 2048))
+    x = bf16_dev(xb)
+    a = gq.rmsnorm_fwd(x, w)
+    b = gq.rmsnorm_fwd(x, w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
