@@ -21,9 +21,10 @@ Modules:
   moe      - grouped expert FFN forward/backward and a per-token brute force
   lmhead   - LM head with chunked online log-sum-exp cross entropy
   rmsnorm  - RMS normalisation with a frozen weight (the step before a linear)
+  adamw8bit - AdamW with 8-bit block-wise quantised states (the adapters' optimizer)
 
 Every function is pinned by tests under tests/ (marked "not gpu") to values
 fixed independently of the oracle: hand-built blocks, closed forms, brute
 force and finite differences.
 """
-from . import blocks, linear, routing, moe, lmhead, rmsnorm  # noqa: F401
+from . import blocks, linear, routing, moe, lmhead, rmsnorm, adamw8bit  # noqa: F401

@@ -1,0 +1,130 @@
+"""AdamW with 8-bit block-wise quantised states (oracle; test use only).
+
+Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
+the training", which names bitsandbytes' 8-bit AdamW as the optimizer of the
+adapters.  The pages give no formulas; the reading used here:
+
+* AdamW with decoupled weight decay.  Per element, in float32 and in this
+  order (the integer codes below are decided by these float32 values, so
+  the oracle takes them in the kernel's precision):
+      m  = b1 * m + (1 - b1) * g
+      v  = b2 * v + (1 - b2) * (g * g)
+      mh = m / c1,  vh = v / c2          (c = 1 - b^t, from the host)
+      p  = p - lr * (mh / (sqrt(vh) + eps) + wd * p)
+* Both states are stored block-wise: 256 consecutive elements share one
+  float32 scale (the block's largest |m|, or largest v, after the update),
+  and each element keeps an 8-bit code of its value divided by that scale.
+* The 8-bit code book is a "dynamic tree" layout: an optional sign bit,
+  then e zero bits, a one bit, and f fraction bits; the value is
+  10^-e * (0.1 + 0.9 * (i + 1) / 2^f) for fraction bits i (so every decade
+  below 1 gets its own group of codes), and the all-zero magnitude is 0.
+  Signed codes (for m): sign bit + 7 magnitude bits, e = 0..6, f = 6 - e.
+  Unsigned codes (for v): 8 magnitude bits, e = 0..7, f = 7 - e.
+* A value is stored as the code whose value is nearest (distances in
+  float32; on a tie the code of smaller magnitude).  A block whose scale is
+  0 stores code 0 everywhere.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 256
+F32 = np.float32
+
+
+# 10^-e as double literals (each the double nearest to the decimal value)
+_DECADE = (1.0, 0.1, 0.01, 0.001, 0.0001, 0.00001, 0.000001, 0.0000001)
+
+
+def _magnitudes(bits: int) -> np.ndarray:
+    """Values of the magnitude codes 0 .. 2^bits - 1: the rule evaluated in
+    double precision in the order written, then rounded to float32."""
+    out = np.zeros(1 << bits, np.float64)
+    for code in range(1, 1 << bits):
+        top = code.bit_length() - 1      # position of the indicator bit
+        e = bits - 1 - top                # leading zeros
+        f = top                           # fraction bits below the indicator
+        i = code - (1 << top)
+        out[code] = _DECADE[e] * (0.1 + 0.9 * ((i + 1) / (1 << f)))
+    return out
+
+
+def signed_table() -> np.ndarray:
+    """float32 [256]: code c = sign bit 7 | magnitude bits 0..6."""
+    mag = _magnitudes(7)
+    t = np.concatenate([mag, -mag])
+    return t.astype(F32)
+
+
+def unsigned_table() -> np.ndarray:
+    return _magnitudes(8).astype(F32)
+
+
+def quantize(xn: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Nearest code of each float32 value in xn (ties: smaller magnitude)."""
+    xn = np.asarray(xn, F32)
+    order = np.argsort(table, kind="stable")
+    vals = table[order]
+    # drop the duplicate -0 of the signed table: keep the first of equal values
+    keep = np.concatenate([[True], vals[1:] != vals[:-1]])
+    vals, order = vals[keep], order[keep]
+    hi = np.searchsorted(vals, xn, side="left")
+    hi = np.clip(hi, 0, vals.size - 1)
+    lo = np.clip(hi - 1, 0, vals.size - 1)
+    dlo = np.abs(xn - vals[lo]).astype(F32)
+    dhi = np.abs(vals[hi] - xn).astype(F32)
+    pick_hi = dhi < dlo
+    tie = dhi == dlo
+    # on a tie take the code of smaller magnitude
+    pick_hi = pick_hi | (tie & (np.abs(vals[hi]) < np.abs(vals[lo])))
+    idx = np.where(pick_hi, hi, lo)
+    return order[idx].astype(np.uint8)
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray, table: np.ndarray, n: int) -> np.ndarray:
+    """float32 [n] from codes [n] and block scales [ceil(n / 256)]."""
+    s = np.repeat(np.asarray(scale, F32), BLOCK)[:n]
+    return (table[np.asarray(codes, np.int64)] * s).astype(F32)
+
+
+def step(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
+    """One AdamW step on float32 p [n] with gradient g [n] and 8-bit states
+    (mq, vq uint8 [n]; sm, sv float32 [nblk]).  Returns new (p, mq, vq, sm, sv)."""
+    ts, tu = signed_table(), unsigned_table()
+    p = np.asarray(p, F32).copy()
+    g = np.asarray(g, F32)
+    n = p.size
+    m = dequantize(mq, sm, ts, n)
+    v = dequantize(vq, sv, tu, n)
+    b1f, b2f = F32(b1), F32(b2)
+    om1, om2 = F32(1.0 - b1), F32(1.0 - b2)
+    c1, c2 = F32(1.0 - b1 ** t), F32(1.0 - b2 ** t)
+    lrf, epsf, wdf = F32(lr), F32(eps), F32(wd)
+    m = (b1f * m + om1 * g).astype(F32)
+    v = (b2f * v + om2 * (g * g)).astype(F32)
+    mh = (m / c1).astype(F32)
+    vh = (v / c2).astype(F32)
+    upd = (mh / (np.sqrt(vh) + epsf)).astype(F32)
+    upd = (upd + wdf * p).astype(F32)
+    p = (p - lrf * upd).astype(F32)
+    nblk = (n + BLOCK - 1) // BLOCK
+    pad = nblk * BLOCK - n
+    am = np.pad(np.abs(m), (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
+    av = np.pad(v, (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
+    sm_r = np.repeat(am, BLOCK)[:n]
+    sv_r = np.repeat(av, BLOCK)[:n]
+    mn = np.where(sm_r > 0, m / np.where(sm_r > 0, sm_r, F32(1)), F32(0)).astype(F32)
+    vn = np.where(sv_r > 0, v / np.where(sv_r > 0, sv_r, F32(1)), F32(0)).astype(F32)
+    return p, quantize(mn, ts), quantize(vn, tu), am, av
+
+
+def step_fp64(p, g, m, v, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
+    """The same AdamW step in float64 with unquantised states (a pin)."""
+    p = np.asarray(p, np.float64)
+    g = np.asarray(g, np.float64)
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh = m / (1 - b1 ** t)
+    vh = v / (1 - b2 ** t)
+    p = p - lr * (mh / (np.sqrt(vh) + eps) + wd * p)
+    return p, m, v
