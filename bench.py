@@ -562,6 +562,33 @@ def main():
                 f"bwd {bms * 1e3:.1f} us ({ent['bwd_GB_per_s']:.0f} GB/s)")
         result["rmsnorm"] = norm
 
+        # 8-bit AdamW step over the adapters of the Q4_0 MoE layer (gate, up,
+        # down of 128 experts, rank 4: 4.3 M parameters), HBM-bound: p read
+        # and written, g read, both code arrays read and written, scales
+        mc = synth.MOE_Q4_0_T2048
+        na = mc.E * (2 * (mc.rank * mc.H + mc.I * mc.rank) + mc.rank * mc.I + mc.H * mc.rank)
+        pa = torch.from_numpy(rng.standard_normal(na).astype(np.float32)).to(dev)
+        ga = torch.from_numpy((1e-3 * rng.standard_normal(na)).astype(np.float32)).to(dev)
+        sta = gq.AdamW8bitState(na, pa.device)
+        for _ in range(3):
+            gq.adamw8bit_step(pa, ga, sta, 1e-4)
+        ams = batched_ms(lambda: gq.adamw8bit_step(pa, ga, sta, 1e-4), 20)
+        abytes = na * (4 + 4 + 4 + 1 + 1 + 1 + 1) + 4 * 4 * ((na + 255) // 256)
+        ent = {"workload": f"adamw8bit_moe_adapters_{na}", "params": na, "us": round(ams * 1e3, 2),
+               "GB_per_s": round(abytes / (ams * 1e-3) / 1e9, 1),
+               "frac_hbm": round(abytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if not args.no_cpu:
+            from oracle import adamw8bit as oa
+            ph = pa.cpu().numpy()
+            gh = ga.cpu().numpy()
+            z8 = np.zeros(na, np.uint8)
+            zs = np.zeros((na + 255) // 256, np.float32)
+            t0 = time.perf_counter()
+            oa.step(ph, gh, z8, z8, zs, zs, 1, 1e-4, 0.9, 0.999, 1e-8, 0.0)
+            ent["cpu_baseline_ms"] = round(1e3 * (time.perf_counter() - t0), 1)
+        result["adamw8bit"] = ent
+        log(f"[bench] adamw8bit {na} params: {ams * 1e3:.1f} us ({ent['GB_per_s']:.0f} GB/s)")
+
     # ------------------------------------------------- small-token sweep
     if args.sweep or args.all:
         sweep = []

@@ -5,8 +5,10 @@ the training", which names bitsandbytes' 8-bit AdamW as the optimizer of the
 adapters.  The pages give no formulas; the reading used here:
 
 * AdamW with decoupled weight decay.  Per element, in float32 and in this
-  order (the integer codes below are decided by these float32 values, so
-  the oracle takes them in the kernel's precision):
+  order, without fused multiply-adds (the integer codes below are decided
+  by these float32 values, so the oracle takes them in the kernel's
+  precision; b1, b2, lr, eps, wd are float32 values and 1 - b, 1 - b^t are
+  formed from them in double precision and rounded once):
       m  = b1 * m + (1 - b1) * g
       v  = b2 * v + (1 - b2) * (g * g)
       mh = m / c1,  vh = v / c2          (c = 1 - b^t, from the host)
@@ -90,6 +92,9 @@ def dequantize(codes: np.ndarray, scale: np.ndarray, table: np.ndarray, n: int) 
 def step(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
     """One AdamW step on float32 p [n] with gradient g [n] and 8-bit states
     (mq, vq uint8 [n]; sm, sv float32 [nblk]).  Returns new (p, mq, vq, sm, sv)."""
+    # hyper-parameters are float32 values (the kernel's argument type); the
+    # derived constants come from them in double precision, rounded once
+    b1, b2 = float(F32(b1)), float(F32(b2))
     ts, tu = signed_table(), unsigned_table()
     p = np.asarray(p, F32).copy()
     g = np.asarray(g, F32)

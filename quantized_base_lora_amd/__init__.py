@@ -33,7 +33,7 @@ EXPORTS = (
     "gq_grouped_mmq_lora_fwd_workspace_size", "gq_grouped_mmq_lora_fwd",
     "gq_grouped_mmq_lora_bwd_workspace_size", "gq_grouped_mmq_lora_bwd",
     "gq_lmhead_chunked_ce_workspace_size", "gq_lmhead_chunked_ce",
-    "gq_rmsnorm_fwd", "gq_rmsnorm_bwd",
+    "gq_rmsnorm_fwd", "gq_rmsnorm_bwd", "gq_adamw8bit_step",
 )
 
 
@@ -104,6 +104,7 @@ def load_library(path: str = LIB_PATH):
                                            vp, vp, vp, sz, vp]),
         "gq_rmsnorm_fwd": (C.c_int, [vp, vp, i64, i64, f32, vp, vp, vp]),
         "gq_rmsnorm_bwd": (C.c_int, [vp, vp, vp, vp, i64, i64, vp, vp]),
+        "gq_adamw8bit_step": (C.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,6 +250,31 @@ def rmsnorm_bwd(dy, x, w, rstd):
     dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(lib().gq_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), T, H, _ptr(dx), _stream()))
     return dx
+
+
+class AdamW8bitState:
+    """8-bit AdamW states of one fp32 parameter tensor of n elements: codes
+    uint8 [n] for m and v, one fp32 scale each per block of 256 (all zero =
+    the initial state)."""
+
+    def __init__(self, n: int, device):
+        nb = (n + 255) // 256
+        self.n = n
+        self.step = 0
+        self.m_codes = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.m_scale = torch.zeros(nb, dtype=torch.float32, device=device)
+        self.v_scale = torch.zeros(nb, dtype=torch.float32, device=device)
+
+
+def adamw8bit_step(p, g, st: AdamW8bitState, lr: float = 1e-4, betas=(0.9, 0.999), eps: float = 1e-8,
+                   weight_decay: float = 0.0):
+    """One in-place AdamW step of the fp32 tensor p (contiguous) with grad g."""
+    st.step += 1
+    _check(lib().gq_adamw8bit_step(_ptr(p), _ptr(g), _ptr(st.m_codes), _ptr(st.v_codes),
+                                   _ptr(st.m_scale), _ptr(st.v_scale), st.n, st.step, float(lr),
+                                   float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
+                                   _stream()))
 
 
 def _projs(ps):

@@ -1,0 +1,276 @@
+// AdamW step for the adapters with 8-bit block-wise quantised states (page 2
+// "Show HN: LoRA over GGUF", section "Things involved in the training":
+// bitsandbytes' 8-bit AdamW is the optimizer).  One wave per block of 256
+// elements (lane l holds elements l, l+64, l+128, l+192): dequantise m and v
+// (code book value x the block's scale), update in float32 (no fused
+// multiply-adds: the stored codes are decided by these values), write p, then
+// the block's new scales (largest |m|, largest v) and the nearest 8-bit codes.
+//
+// Code books ("dynamic tree" layout): an optional sign bit, e zero bits, a
+// one bit and f fraction bits i; value 10^-e (0.1 + 0.9 (i + 1) / 2^f), the
+// all-zero magnitude 0.  m uses the signed book (7 magnitude bits), v the
+// unsigned one (8 bits).  The books are built at compile time from that rule
+// in double precision and rounded to float.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "gq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gq {
+namespace adamw8 {
+
+constexpr int AB = 256;     // elements per quantisation block (one wave)
+constexpr int WAVES = 4;    // blocks per workgroup
+constexpr int PAD = 2;      // entries past the end of a staged book, +infinity
+
+constexpr double kDecade[8] = {1.0, 0.1, 0.01, 0.001, 0.0001, 0.00001, 0.000001, 0.0000001};
+
+struct CodeBook {
+  float v[256];
+};
+
+// magnitude code c of a `bits`-bit book
+constexpr float book_value(int bits, int c) {
+  if (c == 0) return 0.0f;
+  int top = 0;
+  while ((c >> (top + 1)) != 0) ++top;  // position of the leading one
+  const int e = bits - 1 - top, f = top, i = c - (1 << top);
+  return (float)(kDecade[e] * (0.1 + 0.9 * ((double)(i + 1) / (double)(1 << f))));
+}
+
+constexpr CodeBook make_book(int bits) {
+  CodeBook b{};
+  for (int c = 0; c < (1 << bits); ++c) b.v[c] = book_value(bits, c);
+  return b;
+}
+
+__constant__ CodeBook c_mag7 = make_book(7);  // |m| codes 0..127
+__constant__ CodeBook c_mag8 = make_book(8);  // v codes 0..255
+
+// Per decade, indexed by f + 1 for the leading-one position f (index 0: a
+// below the first non-zero code): the slope and offset of the fraction index
+// i as a linear function of the value inside that decade (the book is linear
+// in i there), the largest i, and the decade's first code.
+struct Decade {
+  float slope, off, top, base;
+};
+struct DecadeTable {
+  Decade d[9];
+};
+
+constexpr DecadeTable make_decades(int bits) {
+  DecadeTable t{};
+  t.d[0] = Decade{0.f, 0.f, 0.f, 1.f};  // window around code 1
+  for (int f = 0; f < bits; ++f) {
+    const double w = (double)(1 << f);
+    t.d[f + 1] = Decade{(float)(w / (0.9 * kDecade[bits - 1 - f])), (float)(-0.1 * w / 0.9 - 1.0),
+                        (float)(w - 1.0), (float)w};
+  }
+  return t;
+}
+
+// the decade edges (first non-zero code of each leading-one position)
+template <int BITS, int F>
+constexpr float kEdge = book_value(BITS, 1 << F);
+
+// Nearest magnitude code of a in [0, 1] in the increasing `BITS`-bit book
+// (ties to the smaller magnitude).  The decade comes from counting the decade
+// edges <= a, the fraction index from the linear estimate; the estimate is
+// within one code of the largest code <= a, so reading the book at k0-1 ..
+// k0+2 decides it exactly.  `book` holds 2^BITS values and PAD entries of
+// +infinity after them; `dec` is make_decades(BITS).  Host-callable so that
+// it can be checked on every float in [0, 1] against a plain bisection of
+// the same book.
+template <int BITS, int... F>
+__host__ __device__ __forceinline__ int nearest_code_impl(const float* book, const Decade* dec, float a,
+                                                          std::integer_sequence<int, F...>) {
+  const int nf = (0 + ... + (a >= kEdge<BITS, F> ? 1 : 0));  // f + 1
+  const Decade d = dec[nf];
+  float x = a * d.slope + d.off;
+  x = fminf(fmaxf(x, 0.f), d.top);  // also maps a NaN estimate to 0
+  const int k0 = (int)d.base + (int)floorf(x);
+  const float bm1 = book[k0 - 1], b0 = book[k0], b1 = book[k0 + 1], b2 = book[k0 + 2];
+  int lo = k0;
+  float blo = b0, bhi = b1;
+  if (!(b0 <= a)) {  // also a NaN: code 0, as a bisection gives
+    lo = k0 - 1;
+    blo = bm1;
+    bhi = b0;
+  } else if (b1 <= a) {
+    lo = k0 + 1;
+    blo = b1;
+    bhi = b2;
+  }
+  const float dlo = a - blo;
+  const float dhi = bhi - a;  // +infinity past the last code
+  return dhi < dlo ? lo + 1 : lo;
+}
+
+template <int BITS>
+__host__ __device__ __forceinline__ int nearest_code(const float* book, const Decade* dec, float a) {
+  return nearest_code_impl<BITS>(book, dec, a, std::make_integer_sequence<int, BITS>{});
+}
+
+__constant__ DecadeTable c_dec7 = make_decades(7);
+__constant__ DecadeTable c_dec8 = make_decades(8);
+
+#ifdef __HIP_DEVICE_COMPILE__
+__device__ __forceinline__ float wave_max_f32(float v) {
+  auto step = [&](auto ctrl_c) {
+    constexpr int CTRL = decltype(ctrl_c)::value;
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true)));
+  };
+  step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{});  // row_mirror
+  float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    s = fmaxf(s, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * r)));
+  return s;
+}
+#endif
+
+struct AdamArgs {
+  float lr, b1, b2, om1, om2, c1, c2, eps, wd;
+};
+
+// One block of 256 elements on one wave, in two phases around the workgroup
+// barrier that stages the books.  FULL: the block lies inside [0, n).
+// Out-of-range elements of the last block take code 0 and gradient 0, so
+// m = v = 0 there, which leaves the block maxima unchanged; they are not
+// stored.
+struct BlockRegs {
+  float g[4], p[4], sm, sv;
+  uint32_t cm[4], cv[4];
+};
+
+template <bool FULL>
+__device__ __forceinline__ void adam_load(BlockRegs& r, const float* __restrict__ p, const float* __restrict__ g,
+                                          const uint8_t* __restrict__ mq, const uint8_t* __restrict__ vq,
+                                          const float* __restrict__ sm, const float* __restrict__ sv, int64_t n,
+                                          int64_t blk, int lane) {
+  const int64_t i0 = blk * AB + lane;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + 64 * j;
+    if (FULL || i < n) {
+      r.g[j] = g[i];
+      r.p[j] = p[i];
+      r.cm[j] = mq[i];
+      r.cv[j] = vq[i];
+    }
+  }
+  r.sm = sm[blk];
+  r.sv = sv[blk];
+}
+
+template <bool FULL>
+__device__ __forceinline__ void adam_finish(BlockRegs& r, float* __restrict__ p, uint8_t* __restrict__ mq,
+                                            uint8_t* __restrict__ vq, float* __restrict__ sm,
+                                            float* __restrict__ sv, int64_t n, int64_t blk, int lane,
+                                            const AdamArgs& a, const float* book7, const float* book8,
+                                            const Decade* dec7, const Decade* dec8) {
+#ifdef __HIP_DEVICE_COMPILE__
+  const int64_t i0 = blk * AB + lane;
+  float m[4], v[4], am = 0.f, av = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = book7[r.cm[j] & 0x7f] * r.sm;
+    if (r.cm[j] & 0x80) m[j] = -m[j];
+    v[j] = book8[r.cv[j]] * r.sv;
+    m[j] = a.b1 * m[j] + a.om1 * r.g[j];
+    v[j] = a.b2 * v[j] + a.om2 * (r.g[j] * r.g[j]);
+    const float mh = m[j] / a.c1;
+    const float vh = v[j] / a.c2;
+    float upd = mh / (sqrtf(vh) + a.eps);
+    upd = upd + a.wd * r.p[j];
+    r.p[j] = r.p[j] - a.lr * upd;
+    am = fmaxf(am, fabsf(m[j]));
+    av = fmaxf(av, v[j]);
+  }
+  // block scales: largest |m| and largest v (max: order-independent)
+  am = wave_max_f32(am);
+  av = wave_max_f32(av);
+  if (lane == 0) {
+    sm[blk] = am;
+    sv[blk] = av;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float xm = am > 0.f ? m[j] / am : 0.f;
+    const float xv = av > 0.f ? v[j] / av : 0.f;
+    const int c = nearest_code<7>(book7, dec7, fabsf(xm));
+    const int cvj = nearest_code<8>(book8, dec8, xv);
+    const int64_t i = i0 + 64 * j;
+    if (FULL || i < n) {
+      p[i] = r.p[j];
+      mq[i] = (uint8_t)(xm < 0.f && c != 0 ? (0x80 | c) : c);
+      vq[i] = (uint8_t)cvj;
+    }
+  }
+#endif
+}
+
+__global__ __launch_bounds__(64 * WAVES) void adamw8bit_kernel(float* __restrict__ p, const float* __restrict__ g,
+                                                               uint8_t* __restrict__ mq, uint8_t* __restrict__ vq,
+                                                               float* __restrict__ sm, float* __restrict__ sv,
+                                                               int64_t n, int64_t nblk, const AdamArgs a) {
+#ifdef __HIP_DEVICE_COMPILE__
+  __shared__ float book7[128 + PAD], book8[256 + PAD];
+  __shared__ Decade dec7[8], dec8[9];
+  const int tid = threadIdx.x, lane = tid & 63;
+  book8[tid] = c_mag8.v[tid];
+  if (tid < 128) book7[tid] = c_mag7.v[tid];
+  if (tid < PAD) {
+    book7[128 + tid] = __builtin_inff();
+    book8[256 + tid] = __builtin_inff();
+  }
+  if (tid < 8) dec7[tid] = c_dec7.d[tid];
+  if (tid < 9) dec8[tid] = c_dec8.d[tid];
+  // the wave's block, kept in scalar registers so that the branches are uniform
+  const int64_t blk = (int64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool full = blk + 1 < nblk || (blk + 1 == nblk && n % AB == 0);
+  const bool live = blk < nblk;
+  BlockRegs r = {};  // zeros stand for the elements past n
+  if (full)
+    adam_load<true>(r, p, g, mq, vq, sm, sv, n, blk, lane);
+  else if (live)
+    adam_load<false>(r, p, g, mq, vq, sm, sv, n, blk, lane);
+  __syncthreads();  // books staged
+  if (full)
+    adam_finish<true>(r, p, mq, vq, sm, sv, n, blk, lane, a, book7, book8, dec7, dec8);
+  else if (live)
+    adam_finish<false>(r, p, mq, vq, sm, sv, n, blk, lane, a, book7, book8, dec7, dec8);
+#endif
+}
+
+}  // namespace adamw8
+
+hipError_t launch_adamw8bit(float* p, const float* g, uint8_t* mq, uint8_t* vq, float* sm, float* sv,
+                            int64_t n, int64_t t, float lr, float beta1, float beta2, float eps,
+                            float wd, hipStream_t st) {
+  using namespace adamw8;
+  AdamArgs a;
+  a.lr = lr;
+  a.b1 = beta1;
+  a.b2 = beta2;
+  a.om1 = (float)(1.0 - (double)beta1);
+  a.om2 = (float)(1.0 - (double)beta2);
+  a.c1 = (float)(1.0 - pow((double)beta1, (double)t));
+  a.c2 = (float)(1.0 - pow((double)beta2, (double)t));
+  a.eps = eps;
+  a.wd = wd;
+  const int64_t nblk = (n + AB - 1) / AB;
+  const int64_t nwg = (nblk + WAVES - 1) / WAVES;
+  hipLaunchKernelGGL(adamw8bit_kernel, dim3((unsigned)nwg), dim3(64 * WAVES), 0, st, p, g, mq, vq, sm, sv, n,
+                     nblk, a);
+  return hipGetLastError();
+}
+
+}  // namespace gq

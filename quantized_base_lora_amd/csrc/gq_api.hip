@@ -386,6 +386,24 @@ int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, in
   return GQ_OK;
 }
 
+int gq_adamw8bit_step(float* p, const float* g, uint8_t* m_codes, uint8_t* v_codes, float* m_scale,
+                      float* v_scale, int64_t n, int64_t step, float lr, float beta1, float beta2,
+                      float eps, float weight_decay, void* stream) {
+  g_err.clear();
+  if (n < 0 || (n + 255) / 256 > INT_MAX) return fail(GQ_EINVAL, "gq_adamw8bit_step: bad n");
+  if (step < 1) return fail(GQ_EINVAL, "gq_adamw8bit_step: step must be >= 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f) ||
+      !(lr >= 0.f) || !(weight_decay >= 0.f))
+    return fail(GQ_EINVAL, "gq_adamw8bit_step: need 0 <= beta < 1, eps > 0, lr >= 0, weight_decay >= 0");
+  if (n == 0) return GQ_OK;
+  if (!p || !g || !m_codes || !v_codes || !m_scale || !v_scale)
+    return fail(GQ_EINVAL, "gq_adamw8bit_step: NULL pointer");
+  HIP_TRY(launch_adamw8bit(p, g, m_codes, v_codes, m_scale, v_scale, n, step, lr, beta1, beta2, eps,
+                           weight_decay, S(stream)),
+          "gq_adamw8bit_step");
+  return GQ_OK;
+}
+
 int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
                    float* rstd, void* stream) {
   g_err.clear();

@@ -245,6 +245,10 @@ hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, cons
                            const int64_t* labels, int64_t V, int64_t ignore_index, float* lse,
                            float* term, int32_t* err, float* nvalid, float* loss,
                            hipStream_t st);
+// AdamW step with 8-bit block-wise states (blocks of 256 elements)
+hipError_t launch_adamw8bit(float* p, const float* g, uint8_t* mq, uint8_t* vq, float* sm, float* sv,
+                            int64_t n, int64_t t, float lr, float beta1, float beta2, float eps,
+                            float wd, hipStream_t st);
 // RMS normalisation (y = x rstd w) and its input gradient; H % 8 == 0
 hipError_t launch_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int32_t H, float eps,
                               uint16_t* y, float* rstd, hipStream_t st);

@@ -169,3 +169,16 @@ def test_rmsnorm_validation(gq):
     assert lib.gq_rmsnorm_fwd(FAKE, FAKE, 0, 64, 1e-6, FAKE, FAKE, None) == gq.GQ_OK  # T = 0: no-op
     assert lib.gq_rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE, -1, 64, FAKE, None) == gq.GQ_EINVAL
     assert lib.gq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, 4, 64, FAKE, None) == gq.GQ_EINVAL
+
+
+def test_adamw8bit_validation(gq):
+    lib = gq.lib()
+    st = lib.gq_adamw8bit_step
+    args = [FAKE] * 6
+    assert st(*args, 100, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL  # step 0
+    assert "step" in gq.last_error()
+    assert st(*args, 100, 1, 1e-3, 1.0, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL  # beta1 = 1
+    assert st(*args, 100, 1, 1e-3, 0.9, 0.999, 0.0, 0.0, None) == gq.GQ_EINVAL   # eps = 0
+    assert st(*args, -1, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL
+    assert st(None, *args[1:], 100, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL
+    assert st(*args, 0, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_OK  # n = 0: no-op

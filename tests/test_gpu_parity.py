@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import adamw8bit as oa
 from oracle import blocks as ob
 from oracle import linear as ol
 from oracle import lmhead as olm
@@ -332,3 +333,31 @@ def test_rmsnorm_deterministic():
     a = gq.rmsnorm_fwd(x, w)
     b = gq.rmsnorm_fwd(x, w)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------ 8-bit AdamW
+# codes, scales and parameters bit-exact against the oracle over several
+# steps (both sides take the same float32 operations in the same order)
+@pytest.mark.parametrize("n,steps,wd", [(1, 3, 0.0), (256, 4, 0.01), (700, 5, 0.0), (100003, 3, 0.1)])
+def test_adamw8bit_bit_exact(n, steps, wd):
+    rng = np.random.default_rng(n + steps)
+    p0 = rng.standard_normal(n).astype(np.float32)
+    p = torch.from_numpy(p0.copy()).cuda()
+    st = gq.AdamW8bitState(n, p.device)
+    ph, mq, vq = p0.copy(), np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    nb = (n + 255) // 256
+    sm, sv = np.zeros(nb, np.float32), np.zeros(nb, np.float32)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    say("adamw8bit", n, steps, wd)
+    for t in range(1, steps + 1):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+        if t == 2 and n > 300:
+            g[256:300] = 0.0  # a stretch of zero gradients
+        gq.adamw8bit_step(p, torch.from_numpy(g).cuda(), st, lr, (b1, b2), eps, wd)
+        ph, mq, vq, sm, sv = oa.step(ph, g, mq, vq, sm, sv, t, lr, b1, b2, eps, wd)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.m_codes.cpu().numpy(), mq)
+    assert np.array_equal(st.v_codes.cpu().numpy(), vq)
+    assert np.array_equal(st.m_scale.cpu().numpy().view(np.uint32), sm.view(np.uint32))
+    assert np.array_equal(st.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
+    assert np.array_equal(p.cpu().numpy().view(np.uint32), ph.view(np.uint32))
