@@ -7,15 +7,24 @@ adapters.  The pages give no formulas; the reading used here:
 * AdamW with decoupled weight decay.  Per element, in float32 and in this
   order, without fused multiply-adds (the integer codes below are decided
   by these float32 values, so the oracle takes them in the kernel's
-  precision; b1, b2, lr, eps, wd are float32 values and 1 - b, 1 - b^t are
-  formed from them in double precision and rounded once):
+  precision):
       m  = b1 * m + (1 - b1) * g
       v  = b2 * v + (1 - b2) * (g * g)
-      mh = m / c1,  vh = v / c2          (c = 1 - b^t, from the host)
-      p  = p - lr * (mh / (sqrt(vh) + eps) + wd * p)
+      d  = sqrt(v) * k2 + eps
+      p  = p * kd - s1 * (m / d)
+  with host constants k2 = 1 / sqrt(1 - b2^t), kd = 1 - lr * wd and
+  s1 = lr / (1 - b1^t), each formed in double precision from the float32
+  values of lr, b1, b2, wd and rounded once to float32; 1 - b1 and 1 - b2
+  likewise.  This is the textbook step p - lr (mh / (sqrt(vh) + eps) + wd p)
+  with mh = m / (1 - b1^t), vh = v / (1 - b2^t), the bias corrections moved
+  into constants (one division per element).
 * Both states are stored block-wise: 256 consecutive elements share one
   float32 scale (the block's largest |m|, or largest v, after the update),
-  and each element keeps an 8-bit code of its value divided by that scale.
+  and each element keeps an 8-bit code of its value normalised by that
+  scale: multiplied by the float32 reciprocal 1 / scale (one division per
+  block).  A scale below the smallest normal float32, 2^-126 (zero
+  included), normalises its block to 0, since its reciprocal would
+  overflow; states that small are far below eps and do not move p.
 * The 8-bit code book is a "dynamic tree" layout: an optional sign bit,
   then e zero bits, a one bit, and f fraction bits; the value is
   10^-e * (0.1 + 0.9 * (i + 1) / 2^f) for fraction bits i (so every decade
@@ -24,7 +33,7 @@ adapters.  The pages give no formulas; the reading used here:
   Unsigned codes (for v): 8 magnitude bits, e = 0..7, f = 7 - e.
 * A value is stored as the code whose value is nearest (distances in
   float32; on a tie the code of smaller magnitude).  A block whose scale is
-  0 stores code 0 everywhere.
+  below 2^-126 (0 included) stores code 0 everywhere.
 """
 from __future__ import annotations
 
@@ -94,7 +103,7 @@ def step(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: flo
     (mq, vq uint8 [n]; sm, sv float32 [nblk]).  Returns new (p, mq, vq, sm, sv)."""
     # hyper-parameters are float32 values (the kernel's argument type); the
     # derived constants come from them in double precision, rounded once
-    b1, b2 = float(F32(b1)), float(F32(b2))
+    lr, b1, b2, eps, wd = (float(F32(x)) for x in (lr, b1, b2, eps, wd))
     ts, tu = signed_table(), unsigned_table()
     p = np.asarray(p, F32).copy()
     g = np.asarray(g, F32)
@@ -103,23 +112,25 @@ def step(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: flo
     v = dequantize(vq, sv, tu, n)
     b1f, b2f = F32(b1), F32(b2)
     om1, om2 = F32(1.0 - b1), F32(1.0 - b2)
-    c1, c2 = F32(1.0 - b1 ** t), F32(1.0 - b2 ** t)
-    lrf, epsf, wdf = F32(lr), F32(eps), F32(wd)
+    k2 = F32(1.0 / np.sqrt(1.0 - b2 ** t))
+    kd = F32(1.0 - lr * wd)
+    s1 = F32(lr / (1.0 - b1 ** t))
+    epsf = F32(eps)
     m = (b1f * m + om1 * g).astype(F32)
     v = (b2f * v + om2 * (g * g)).astype(F32)
-    mh = (m / c1).astype(F32)
-    vh = (v / c2).astype(F32)
-    upd = (mh / (np.sqrt(vh) + epsf)).astype(F32)
-    upd = (upd + wdf * p).astype(F32)
-    p = (p - lrf * upd).astype(F32)
+    d = (np.sqrt(v) * k2 + epsf).astype(F32)
+    p = (p * kd - s1 * (m / d).astype(F32)).astype(F32)
     nblk = (n + BLOCK - 1) // BLOCK
     pad = nblk * BLOCK - n
     am = np.pad(np.abs(m), (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
     av = np.pad(v, (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
-    sm_r = np.repeat(am, BLOCK)[:n]
-    sv_r = np.repeat(av, BLOCK)[:n]
-    mn = np.where(sm_r > 0, m / np.where(sm_r > 0, sm_r, F32(1)), F32(0)).astype(F32)
-    vn = np.where(sv_r > 0, v / np.where(sv_r > 0, sv_r, F32(1)), F32(0)).astype(F32)
+    # per-block reciprocal scales; below the smallest normal float32 the
+    # block normalises to 0
+    tiny = F32(2.0 ** -126)
+    rm = np.where(am >= tiny, F32(1) / np.where(am >= tiny, am, F32(1)), F32(0)).astype(F32)
+    rv = np.where(av >= tiny, F32(1) / np.where(av >= tiny, av, F32(1)), F32(0)).astype(F32)
+    mn = (m * np.repeat(rm, BLOCK)[:n]).astype(F32)
+    vn = (v * np.repeat(rv, BLOCK)[:n]).astype(F32)
     return p, quantize(mn, ts), quantize(vn, tu), am, av
 
 

@@ -6,6 +6,8 @@
   the nearest by brute force over the whole book
 * the first step from zero states is plain sign descent up to eps:
   p - lr (g / (|g| + eps) + wd p), whatever the code books
+* a block whose scale is below the smallest normal float32 stores code 0
+  (its reciprocal would overflow) while a normal block beside it does not
 * several steps stay within the quantisation error of a float64 AdamW with
   unquantised states
 """
@@ -52,7 +54,9 @@ def test_first_step_is_sign_descent():
     lr, eps, wd = 1e-3, 1e-8, 0.01
     p1, mq, vq, sm, sv = oa.step(p, g, z8, z8, zs, zs, 1, lr, 0.9, 0.999, eps, wd)
     expect = p.astype(np.float64) - lr * (g / (np.abs(g.astype(np.float64)) + eps) + wd * p)
-    np.testing.assert_allclose(p1, expect, rtol=0, atol=2e-7)
+    # float32 p takes two roundings at its own scale (p * kd, then the
+    # subtraction), each within 2^-24 relative; the lr-sized term adds ~1e-9
+    np.testing.assert_allclose(p1, expect, rtol=2.5e-7, atol=1e-9)
     np.testing.assert_allclose(sm, [np.abs(0.1 * g[i:i + 256]).max() for i in (0, 256, 512)], rtol=1e-6)
 
 
@@ -73,3 +77,17 @@ def test_steps_track_float64_adamw():
     # each step moves p by at most lr / (1 - 0.9) in size; the 8-bit states
     # perturb the direction by a few per cent of that
     assert np.max(np.abs(p - p64)) < 0.1 * 5 * lr
+
+
+def test_subnormal_scale_block_stores_zero_codes():
+    rng = np.random.default_rng(3)
+    n = 512
+    g = rng.standard_normal(n).astype(np.float32)
+    g[256:] *= np.float32(1e-20)  # v = (1 - b2) g^2 ~ 1e-43: subnormal
+    z8 = np.zeros(n, np.uint8)
+    zs = np.zeros(2, np.float32)
+    p1, mq, vq, sm, sv = oa.step(np.zeros(n, np.float32), g, z8, z8, zs, zs, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert 0 < sv[1] < 2.0 ** -126 and sv[0] > 2.0 ** -126
+    assert np.all(vq[256:] == 0) and np.count_nonzero(vq[:256]) > 200
+    # m = 0.1 g ~ 1e-21 is normal: its block keeps non-zero codes
+    assert sm[1] > 2.0 ** -126 and np.count_nonzero(mq[256:]) > 200
