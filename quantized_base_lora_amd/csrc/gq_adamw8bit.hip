@@ -4,7 +4,11 @@
 // elements (lane l holds elements l, l+64, l+128, l+192): dequantise m and v
 // (code book value x the block's scale), update in float32 (no fused
 // multiply-adds: the stored codes are decided by these values), write p, then
-// the block's new scales (largest |m|, largest v) and the nearest 8-bit codes.
+// the block's new scales (largest |m|, largest v) and the nearest 8-bit codes
+// of the states times the reciprocal scales.  The update is the textbook AdamW
+// step with the bias corrections moved into host constants:
+//   d = sqrt(v) k2 + eps,  p = p kd - s1 (m / d),
+//   k2 = 1 / sqrt(1 - b2^t),  kd = 1 - lr wd,  s1 = lr / (1 - b1^t).
 //
 // Code books ("dynamic tree" layout): an optional sign bit, e zero bits, a
 // one bit and f fraction bits i; value 10^-e (0.1 + 0.9 (i + 1) / 2^f), the
@@ -54,9 +58,13 @@ __constant__ CodeBook c_mag8 = make_book(8);  // v codes 0..255
 // Per decade, indexed by f + 1 for the leading-one position f (index 0: a
 // below the first non-zero code): the slope and offset of the fraction index
 // i as a linear function of the value inside that decade (the book is linear
-// in i there), the largest i, and the decade's first code.
+// in i there), lowered by kBias so that the estimate never lies above the
+// answer; the largest i; and the decade's first code.
+constexpr double kBias = 1.0 / 32;
+
 struct Decade {
-  float slope, off, top, base;
+  float slope, off, top;
+  int base;
 };
 struct DecadeTable {
   Decade d[9];
@@ -64,59 +72,80 @@ struct DecadeTable {
 
 constexpr DecadeTable make_decades(int bits) {
   DecadeTable t{};
-  t.d[0] = Decade{0.f, 0.f, 0.f, 1.f};  // window around code 1
+  t.d[0] = Decade{0.f, 0.f, 0.f, 0};  // window at codes 0, 1
   for (int f = 0; f < bits; ++f) {
     const double w = (double)(1 << f);
-    t.d[f + 1] = Decade{(float)(w / (0.9 * kDecade[bits - 1 - f])), (float)(-0.1 * w / 0.9 - 1.0),
-                        (float)(w - 1.0), (float)w};
+    t.d[f + 1] = Decade{(float)(w / (0.9 * kDecade[bits - 1 - f])), (float)(-0.1 * w / 0.9 - 1.0 - kBias),
+                        (float)(w - 1.0), 1 << f};
   }
   return t;
 }
 
-// the decade edges (first non-zero code of each leading-one position)
-template <int BITS, int F>
-constexpr float kEdge = book_value(BITS, 1 << F);
+// Per binary octave [2^(E-127), 2^(E-126)) of a float with exponent field E
+// (E = 0: zero and the subnormals): the number of decade edges (first
+// non-zero code of each leading-one position) at or below the octave's lower
+// end, and the one edge inside the octave, if any (+infinity otherwise).
+// Consecutive edges are more than a factor 2 apart, so an octave holds at
+// most one; f + 1 of a value a is then cnt + (a >= edge).
+struct Octave {
+  float edge;
+  int cnt;
+};
+struct OctaveTable {
+  Octave o[128];
+};
 
-// Nearest magnitude code of a in [0, 1] in the increasing `BITS`-bit book
-// (ties to the smaller magnitude).  The decade comes from counting the decade
-// edges <= a, the fraction index from the linear estimate; the estimate is
-// within one code of the largest code <= a, so reading the book at k0-1 ..
-// k0+2 decides it exactly.  `book` holds 2^BITS values and PAD entries of
-// +infinity after them; `dec` is make_decades(BITS).  Host-callable so that
-// it can be checked on every float in [0, 1] against a plain bisection of
-// the same book.
-template <int BITS, int... F>
-__host__ __device__ __forceinline__ int nearest_code_impl(const float* book, const Decade* dec, float a,
-                                                          std::integer_sequence<int, F...>) {
-  const int nf = (0 + ... + (a >= kEdge<BITS, F> ? 1 : 0));  // f + 1
-  const Decade d = dec[nf];
-  float x = a * d.slope + d.off;
-  x = fminf(fmaxf(x, 0.f), d.top);  // also maps a NaN estimate to 0
-  const int k0 = (int)d.base + (int)floorf(x);
-  const float bm1 = book[k0 - 1], b0 = book[k0], b1 = book[k0 + 1], b2 = book[k0 + 2];
-  int lo = k0;
-  float blo = b0, bhi = b1;
-  if (!(b0 <= a)) {  // also a NaN: code 0, as a bisection gives
-    lo = k0 - 1;
-    blo = bm1;
-    bhi = b0;
-  } else if (b1 <= a) {
-    lo = k0 + 1;
-    blo = b1;
-    bhi = b2;
-  }
-  const float dlo = a - blo;
-  const float dhi = bhi - a;  // +infinity past the last code
-  return dhi < dlo ? lo + 1 : lo;
+constexpr double pow2(int k) {
+  double r = 1.0;
+  for (; k > 0; --k) r *= 2.0;
+  for (; k < 0; ++k) r *= 0.5;
+  return r;
 }
 
+constexpr OctaveTable make_octaves(int bits) {
+  OctaveTable t{};
+  for (int e = 0; e < 128; ++e) {
+    const double lo = e == 0 ? 0.0 : pow2(e - 127), hi = pow2(e - 126);
+    t.o[e] = Octave{__builtin_inff(), 0};
+    for (int f = 0; f < bits; ++f) {
+      const double edge = (double)book_value(bits, 1 << f);
+      if (edge <= lo) ++t.o[e].cnt;
+      else if (edge < hi) t.o[e].edge = (float)edge;
+    }
+  }
+  return t;
+}
+
+// Nearest magnitude code of a in [0, 1] (a little above 1 gives the top code)
+// in the increasing `BITS`-bit book, ties to the smaller magnitude.  The
+// decade comes from the octave table, the fraction index from the linear
+// estimate, which is the largest code <= a or the one below it; reading the
+// book at k0 .. k0+2 decides which, and the nearest of the two neighbours.
+// `book` holds 2^BITS values and PAD entries of +infinity after them, `oct`
+// is make_octaves(BITS) and `dec` make_decades(BITS).  Host-callable so that
+// it can be checked on every float in [0, 1] against a plain bisection of
+// the same book.  A NaN lands in the top octave and gets some code
+// (non-finite states are not meaningful).
 template <int BITS>
-__host__ __device__ __forceinline__ int nearest_code(const float* book, const Decade* dec, float a) {
-  return nearest_code_impl<BITS>(book, dec, a, std::make_integer_sequence<int, BITS>{});
+__host__ __device__ __forceinline__ int nearest_code(const float* book, const Octave* oct, const Decade* dec,
+                                                     float a) {
+  const uint32_t ex = (__builtin_bit_cast(uint32_t, a) >> 23) & 0x7f;  // a >= 0
+  const Octave o = oct[ex];
+  const Decade d = dec[o.cnt + (a >= o.edge ? 1 : 0)];
+  float x = a * d.slope + d.off;
+  x = fminf(fmaxf(x, 0.f), d.top);
+  const int k0 = d.base + (int)floorf(x);
+  const float b0 = book[k0], b1 = book[k0 + 1], b2 = book[k0 + 2];
+  const bool up = b1 <= a;  // the largest code <= a is k0 + 1
+  const float dlo = a - (up ? b1 : b0);
+  const float dhi = (up ? b2 : b1) - a;  // +infinity past the last code
+  return k0 + (up ? 1 : 0) + (dhi < dlo ? 1 : 0);
 }
 
 __constant__ DecadeTable c_dec7 = make_decades(7);
 __constant__ DecadeTable c_dec8 = make_decades(8);
+__constant__ OctaveTable c_oct7 = make_octaves(7);
+__constant__ OctaveTable c_oct8 = make_octaves(8);
 
 #ifdef __HIP_DEVICE_COMPILE__
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -137,7 +166,7 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 #endif
 
 struct AdamArgs {
-  float lr, b1, b2, om1, om2, c1, c2, eps, wd;
+  float b1, b2, om1, om2, k2, kd, s1, eps;
 };
 
 // One block of 256 elements on one wave, in two phases around the workgroup
@@ -174,23 +203,20 @@ template <bool FULL>
 __device__ __forceinline__ void adam_finish(BlockRegs& r, float* __restrict__ p, uint8_t* __restrict__ mq,
                                             uint8_t* __restrict__ vq, float* __restrict__ sm,
                                             float* __restrict__ sv, int64_t n, int64_t blk, int lane,
-                                            const AdamArgs& a, const float* book7, const float* book8,
-                                            const Decade* dec7, const Decade* dec8) {
+                                            const AdamArgs& a, const float* sbook, const float* book7,
+                                            const float* book8, const Octave* oct7, const Octave* oct8, const Decade* dec7,
+                                            const Decade* dec8) {
 #ifdef __HIP_DEVICE_COMPILE__
   const int64_t i0 = blk * AB + lane;
   float m[4], v[4], am = 0.f, av = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    m[j] = book7[r.cm[j] & 0x7f] * r.sm;
-    if (r.cm[j] & 0x80) m[j] = -m[j];
+    m[j] = sbook[r.cm[j]] * r.sm;
     v[j] = book8[r.cv[j]] * r.sv;
     m[j] = a.b1 * m[j] + a.om1 * r.g[j];
     v[j] = a.b2 * v[j] + a.om2 * (r.g[j] * r.g[j]);
-    const float mh = m[j] / a.c1;
-    const float vh = v[j] / a.c2;
-    float upd = mh / (sqrtf(vh) + a.eps);
-    upd = upd + a.wd * r.p[j];
-    r.p[j] = r.p[j] - a.lr * upd;
+    const float d = sqrtf(v[j]) * a.k2 + a.eps;
+    r.p[j] = r.p[j] * a.kd - a.s1 * (m[j] / d);
     am = fmaxf(am, fabsf(m[j]));
     av = fmaxf(av, v[j]);
   }
@@ -201,12 +227,16 @@ __device__ __forceinline__ void adam_finish(BlockRegs& r, float* __restrict__ p,
     sm[blk] = am;
     sv[blk] = av;
   }
+  // reciprocal scales; a scale below the smallest normal float (zero
+  // included) normalises the block to 0, as its reciprocal would overflow
+  const float rm = am >= 0x1p-126f ? 1.0f / am : 0.f;
+  const float rv = av >= 0x1p-126f ? 1.0f / av : 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float xm = am > 0.f ? m[j] / am : 0.f;
-    const float xv = av > 0.f ? v[j] / av : 0.f;
-    const int c = nearest_code<7>(book7, dec7, fabsf(xm));
-    const int cvj = nearest_code<8>(book8, dec8, xv);
+    const float xm = m[j] * rm;
+    const float xv = v[j] * rv;
+    const int c = nearest_code<7>(book7, oct7, dec7, fabsf(xm));
+    const int cvj = nearest_code<8>(book8, oct8, dec8, xv);
     const int64_t i = i0 + 64 * j;
     if (FULL || i < n) {
       p[i] = r.p[j];
@@ -222,11 +252,18 @@ __global__ __launch_bounds__(64 * WAVES) void adamw8bit_kernel(float* __restrict
                                                                float* __restrict__ sm, float* __restrict__ sv,
                                                                int64_t n, int64_t nblk, const AdamArgs a) {
 #ifdef __HIP_DEVICE_COMPILE__
+  __shared__ float sbook[256];  // signed m codes: magnitude, then negated
   __shared__ float book7[128 + PAD], book8[256 + PAD];
   __shared__ Decade dec7[8], dec8[9];
+  __shared__ Octave oct7[128], oct8[128];
   const int tid = threadIdx.x, lane = tid & 63;
   book8[tid] = c_mag8.v[tid];
-  if (tid < 128) book7[tid] = c_mag7.v[tid];
+  sbook[tid] = tid < 128 ? c_mag7.v[tid] : -c_mag7.v[tid - 128];
+  if (tid < 128) {
+    book7[tid] = c_mag7.v[tid];
+    oct7[tid] = c_oct7.o[tid];
+    oct8[tid] = c_oct8.o[tid];
+  }
   if (tid < PAD) {
     book7[128 + tid] = __builtin_inff();
     book8[256 + tid] = __builtin_inff();
@@ -244,9 +281,9 @@ __global__ __launch_bounds__(64 * WAVES) void adamw8bit_kernel(float* __restrict
     adam_load<false>(r, p, g, mq, vq, sm, sv, n, blk, lane);
   __syncthreads();  // books staged
   if (full)
-    adam_finish<true>(r, p, mq, vq, sm, sv, n, blk, lane, a, book7, book8, dec7, dec8);
+    adam_finish<true>(r, p, mq, vq, sm, sv, n, blk, lane, a, sbook, book7, book8, oct7, oct8, dec7, dec8);
   else if (live)
-    adam_finish<false>(r, p, mq, vq, sm, sv, n, blk, lane, a, book7, book8, dec7, dec8);
+    adam_finish<false>(r, p, mq, vq, sm, sv, n, blk, lane, a, sbook, book7, book8, oct7, oct8, dec7, dec8);
 #endif
 }
 
@@ -256,16 +293,17 @@ hipError_t launch_adamw8bit(float* p, const float* g, uint8_t* mq, uint8_t* vq, 
                             int64_t n, int64_t t, float lr, float beta1, float beta2, float eps,
                             float wd, hipStream_t st) {
   using namespace adamw8;
+  // derived constants from the float32 hyper-parameters, in double, rounded once
+  const double l = lr, b1d = beta1, b2d = beta2;
   AdamArgs a;
-  a.lr = lr;
   a.b1 = beta1;
   a.b2 = beta2;
-  a.om1 = (float)(1.0 - (double)beta1);
-  a.om2 = (float)(1.0 - (double)beta2);
-  a.c1 = (float)(1.0 - pow((double)beta1, (double)t));
-  a.c2 = (float)(1.0 - pow((double)beta2, (double)t));
+  a.om1 = (float)(1.0 - b1d);
+  a.om2 = (float)(1.0 - b2d);
+  a.k2 = (float)(1.0 / sqrt(1.0 - pow(b2d, (double)t)));
+  a.kd = (float)(1.0 - l * (double)wd);
+  a.s1 = (float)(l / (1.0 - pow(b1d, (double)t)));
   a.eps = eps;
-  a.wd = wd;
   const int64_t nblk = (n + AB - 1) / AB;
   const int64_t nwg = (nblk + WAVES - 1) / WAVES;
   hipLaunchKernelGGL(adamw8bit_kernel, dim3((unsigned)nwg), dim3(64 * WAVES), 0, st, p, g, mq, vq, sm, sv, n,
