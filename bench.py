@@ -563,8 +563,9 @@ def main():
         result["rmsnorm"] = norm
 
         # 8-bit AdamW step over the adapters of the Q4_0 MoE layer (gate, up,
-        # down of 128 experts, rank 4: 4.3 M parameters), HBM-bound: p read
-        # and written, g read, both code arrays read and written, scales
+        # down of 128 experts, rank 4: 4.3 M parameters), against HBM
+        # bandwidth: p read and written, g read, both code arrays read and
+        # written, scales
         mc = synth.MOE_Q4_0_T2048
         na = mc.E * (2 * (mc.rank * mc.H + mc.I * mc.rank) + mc.rank * mc.I + mc.H * mc.rank)
         pa = torch.from_numpy(rng.standard_normal(na).astype(np.float32)).to(dev)

@@ -304,15 +304,20 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* head, const uint16_t* h, const in
  * involved in the training": bitsandbytes' 8-bit AdamW; the pages give no
  * formulas, the definition here is this library's reading):
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2        (float32, no FMA)
- *   p -= lr (m / c1 / (sqrt(v / c2) + eps) + weight_decay p),  c = 1 - b^step
- * p fp32 [n] (updated in place), g fp32 [n].  The states are stored in
- * blocks of 256 elements: m_codes, v_codes uint8 [n] and m_scale, v_scale
- * fp32 [ceil(n / 256)]; an element's state = book[code] * its block's
- * scale, the scale being the block's largest |m| (largest v) after the
- * update and the code the nearest book entry (ties to the smaller
- * magnitude).  Books: "dynamic tree" codes -- optional sign bit, e zero
- * bits, a one bit, f fraction bits i -- value 10^-e (0.1 + 0.9 (i + 1) / 2^f),
- * all-zero magnitude 0; m signed (7 magnitude bits), v unsigned (8 bits).
+ *   d = sqrt(v) k2 + eps;   p = p kd - s1 (m / d)
+ * with k2 = 1 / sqrt(1 - b2^step), kd = 1 - lr weight_decay and
+ * s1 = lr / (1 - b1^step) formed in double from the float32 arguments and
+ * rounded once (the textbook AdamW step with the bias corrections moved into
+ * constants).  p fp32 [n] (updated in place), g fp32 [n].  The states are
+ * stored in blocks of 256 elements: m_codes, v_codes uint8 [n] and m_scale,
+ * v_scale fp32 [ceil(n / 256)]; an element's state = book[code] * its
+ * block's scale, the scale being the block's largest |m| (largest v) after
+ * the update and the code the book entry nearest to the state times the
+ * float32 reciprocal of the scale (ties to the smaller magnitude; a scale
+ * below 2^-126 stores code 0).  Books: "dynamic tree" codes -- optional sign
+ * bit, e zero bits, a one bit, f fraction bits i -- value
+ * 10^-e (0.1 + 0.9 (i + 1) / 2^f), all-zero magnitude 0; m signed (7
+ * magnitude bits), v unsigned (8 bits).
  * Zero-filled codes and scales are the initial (zero) state.  step >= 1;
  * 0 <= beta < 1, eps > 0, lr >= 0, weight_decay >= 0; n = 0 is a no-op.
  * No workspace; bitwise deterministic.
