@@ -226,23 +226,29 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- workgroup -> tile, XCD-contiguous runs of tiles
-  int bid;
-  {
-    const int nblk = gridDim.x, q = nblk >> 3, rem = nblk & 7;
-    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    bid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-  }
-  // Dense launches: each XCD's run of tiles covers GM m-tiles by a band of
-  // n-tiles (grouped ordering), so its L2 holds the activation rows of GM
-  // m-tiles and the weight columns of the band instead of every m-tile.
-  // Grouped launches keep m-slots fastest: their unused trailing slots are
-  // then spread evenly over the XCDs.
+  // ---- workgroup -> tile, XCD-contiguous runs of tiles.  Workgroup ids go
+  // round-robin over the 8 XCDs; renumbering them so that each XCD owns a
+  // contiguous run of tile ids keeps the tiles that share operands in one L2.
+  auto xcd_run = [](int id, int count) {
+    const int q = count >> 3, rem = count & 7, xcd = id & 7, loc = id >> 3;
+    return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+  };
+  // Grouped launches: the grid covers the largest possible number of m-slots;
+  // only the first tile_start[E] hold rows.  The runs are laid over those
+  // (the rest exit here), n-tiles fastest, so the n-tiles of one m-slot,
+  // which share its gathered activation rows, run together on one XCD.
+  // Dense launches: each XCD's run covers GM m-tiles by a band of n-tiles,
+  // so its L2 holds the activation rows of GM m-tiles and the weight columns
+  // of the band instead of every m-tile.
   int mslot, ntile;
   if (p.offsets) {
-    mslot = bid % p.mtiles;
-    ntile = bid / p.mtiles;
+    const int used = p.tile_start[p.E] * p.ntiles;
+    if ((int)blockIdx.x >= used) return;
+    const int bid = xcd_run(blockIdx.x, used);
+    mslot = bid / p.ntiles;
+    ntile = bid - mslot * p.ntiles;
   } else {
+    const int bid = xcd_run(blockIdx.x, gridDim.x);
     constexpr int GM = 4;
     const int gsize = GM * p.ntiles;
     const int g = bid / gsize;
