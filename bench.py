@@ -229,7 +229,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              "(the library has no multi-GPU path: each GPU would run these kernels on its share of the "
+              "tokens with the adapter gradients all-reduced, which is not built)",
               file=sys.stderr)
         sys.exit(2)
 
