@@ -195,6 +195,7 @@ MOE_CASES = [
     (100, 128, 128, 8, 2, 0, 4, 0.0),
     (257, 256, 192, 16, 4, 2, 8, 1.0),
     (64, 128, 64, 32, 8, 1, 4, 1.0),  # many idle experts
+    (200, 128, 64, 100, 4, 1, 4, 0.5),  # E not a multiple of 64: partly filled prefix lanes
     # few rows per expert, K % 256 == 0: the skinny forward MMQ (16-row tiles,
     # 32-row tiles in the last case); in the first only the down projection
     # (K = I = 256) runs skinny, on a ragged last column tile (H = 320)
