@@ -677,9 +677,8 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     rd.gdiv = a->gather_div; rd.offsets = a->offsets; rd.E = E; rd.tile16 = W.ts16;
     rd.W[0] = P[0].B; rd.w_estride = (int64_t)H * r; rd.w_jstride = 1; rd.w_cstride = r;
     rd.out[0] = W.dyB; rd.nout = 1; rd.out2 = W.wdyB; rd.wflat = a->w_flat; rd.sorted = a->sorted;
-    HIP_TRY(launch_rowdot(rd, st), "gq_grouped_mmq_lora_bwd: dY Bd");
-    HIP_TRY(launch_scale_rows(a->xa_d, a->w_flat, a->sorted, M, r, W.wxa, st),
-            "gq_grouped_mmq_lora_bwd: w xa_d");
+    rd.win = a->xa_d; rd.wout = W.wxa;  // the gate-weighted xa_d rows, in the same pass
+    HIP_TRY(launch_rowdot(rd, st), "gq_grouped_mmq_lora_bwd: dY Bd, w xa_d");
 
     GemmArgs g = gemm_defaults();
     g.M = M; g.N = I; g.K = H;
@@ -696,8 +695,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     g.rv0 = W.dyB; g.s0 = a->g; g.s1 = a->u; g.wflat = a->w_flat; g.sorted = a->sorted;
     g.o0 = a->dg; g.o1 = a->du; g.ldo = I; g.f0 = W.part_down;
     HIP_TRY(launch_gemm(P[0].qtype, EPI_DOWN_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: down MMQ");
-    HIP_TRY(launch_down_finish(W.part_down, g.ntiles, M, r, a->sorted, a->dw_flat, a->dgB, a->duB, st),
-            "gq_grouped_mmq_lora_bwd: dw, dgB, duB");
 
     // dA_d[e] = s sum_p (w dY Bd)^T h ;  dB_d[e] = s sum_p dY^T (w xa_d):
     // both reductions in one launch, both finishes in one launch
@@ -705,7 +702,10 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     cr.njobs = 2;
     cr.C_1 = H; cr.U_1 = a->dy; cr.ldu_1 = H; cr.gather_1 = a->gather; cr.gdiv_1 = a->gather_div;
     cr.Vv_1 = W.wxa; cr.part_1 = W.part[1];
-    HIP_TRY(launch_colred(cr, st), "dA_d, dB_d partials");
+    // dw, dgB, duB: the row sums of the down MMQ partials, as a side job
+    cr.dfin_part = W.part_down; cr.dfin_ntiles = g.ntiles; cr.dfin_sorted = a->sorted;
+    cr.dfin_dw = a->dw_flat; cr.dfin_dgB = a->dgB; cr.dfin_duB = a->duB;
+    HIP_TRY(launch_colred(cr, st), "dA_d, dB_d partials; dw, dgB, duB");
     ColFinJobs fj;
     memset(&fj, 0, sizeof fj);
     fj.n = 2;

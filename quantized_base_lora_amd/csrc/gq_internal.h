@@ -132,6 +132,7 @@ hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int32_t bm0, in
 // out[p][j] = sum_c act(p)[c] * W(e)[j][c]   (W [r][C] if w_jstride == C, or
 // [C][r] if w_jstride == 1, w_cstride == r); act rows via gather; e via offsets.
 // out2 (optional): out2[p][j] = wflat[sorted[p]] * out[p][j]
+// wout (optional): wout[p][j] = wflat[sorted[p]] * win[p][j] over the same rows
 struct RowDotArgs {
   int64_t M;
   int32_t C;
@@ -152,6 +153,8 @@ struct RowDotArgs {
   float* out2;  // weighted copy of out[0]
   const float* wflat;
   const int32_t* sorted;
+  const float* win;  // optional side job: wout[p][j] = wflat[sorted[p]] * win[p][j]
+  float* wout;       // over the same rows (needs wflat, sorted)
 };
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st);
 
@@ -188,6 +191,15 @@ struct ColRedArgs {
   int32_t gdiv_1;
   const float* Vv_1;
   float* part_1;
+  // optional side job over the same slots (workgroups of column block 0,
+  // job 0): the row sums of the grouped down MMQ's per-n-tile partials
+  // (dfin_part [ntiles][M][1 + 2r] -> dw_flat[sorted[p]], dgB[p], duB[p])
+  const float* dfin_part;
+  int32_t dfin_ntiles;
+  const int32_t* dfin_sorted;
+  float* dfin_dw;
+  float* dfin_dgB;
+  float* dfin_duB;
 };
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st);
 // columns covered by one launch_colred workgroup
@@ -233,9 +245,6 @@ hipError_t launch_combine(const uint16_t* rows, const float* w, const int32_t* p
 // MoE down-backward partial finish: from part [ntiles][M][1 + 2r]
 //   dw_flat[sorted[p]] = sum part[.][p][0]; dgB[p][j] = sum part[.][p][1+j];
 //   duB[p][j] = sum part[.][p][1+r+j]
-hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int32_t r,
-                              const int32_t* sorted, float* dw_flat, float* dgB, float* duB,
-                              hipStream_t st);
 
 // LM head helpers
 // term: [T] scratch for the per-token loss terms.  Also writes nvalid (the
@@ -257,9 +266,6 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float
                               hipStream_t st);
 hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
                               int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st);
-// out[p][j] = wflat[sorted[p]] * in[p][j]
-hipError_t launch_scale_rows(const float* in, const float* wflat, const int32_t* sorted, int64_t M,
-                             int32_t r, float* out, hipStream_t st);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st);
 

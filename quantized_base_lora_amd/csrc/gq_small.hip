@@ -211,10 +211,41 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
         if (p < p1) {
           a.out[o][p * r + j] = v[q];
           if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v[q];
+          if (o == 0 && a.wout) a.wout[p * r + j] = a.wflat[a.sorted[p]] * a.win[p * r + j];
         }
       }
     }
   }
+}
+
+// ------------------------------------------------ down-backward row sums
+// Row p of the grouped down MMQ's partials (one record of 1 + 2r floats per
+// n-tile: dw, dg.Bg, du.Bu over that tile's columns), summed over the
+// n-tiles in order.
+__device__ void down_finish_row(const float* __restrict__ part, int32_t ntiles, int64_t M, int32_t r,
+                                int64_t p, const int32_t* __restrict__ sorted, float* __restrict__ dw_flat,
+                                float* __restrict__ dgB, float* __restrict__ duB) {
+  const int width = 1 + 2 * r;
+  float dw = 0.f, g[16], u[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) g[j] = u[j] = 0.f;
+  for (int nt = 0; nt < ntiles; ++nt) {
+    const float* src = part + ((int64_t)nt * M + p) * width;
+    dw += src[0];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < r) {
+        g[j] += src[1 + j];
+        u[j] += src[1 + r + j];
+      }
+  }
+  dw_flat[sorted[p]] = dw;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < r) {
+      dgB[p * r + j] = g[j];
+      duB[p * r + j] = u[j];
+    }
 }
 
 // ---------------------------------------------------- column reductions
@@ -260,6 +291,13 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = a.r;
+  if (a.dfin_part && blockIdx.y == 0 && !z1) {
+    // side job: every row lies in exactly one slot, and every slot has a
+    // workgroup with column block 0 and job 0
+    for (int64_t p = r0 + tid; p < r1; p += 256)
+      down_finish_row(a.dfin_part, a.dfin_ntiles, a.M, r, p, a.dfin_sorted, a.dfin_dw, a.dfin_dgB,
+                      a.dfin_duB);
+  }
 
   // U tile loads: 32 rows x 256 columns = 1024 16-byte chunks, 4 per thread
   // (chunk t: row t / 32, columns 8 (t % 32) .. +8); zero past r1 or C
@@ -673,35 +711,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                  pack_bf2(acc[6], acc[7]));
 }
 
-__global__ void down_finish_kernel(const float* __restrict__ part, int32_t ntiles, int64_t M,
-                                   int32_t r, const int32_t* __restrict__ sorted,
-                                   float* __restrict__ dw_flat, float* __restrict__ dgB,
-                                   float* __restrict__ duB) {
-  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= M) return;
-  const int width = 1 + 2 * r;
-  float dw = 0.f, g[16], u[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) g[j] = u[j] = 0.f;
-  for (int nt = 0; nt < ntiles; ++nt) {
-    const float* src = part + ((int64_t)nt * M + p) * width;
-    dw += src[0];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) {
-        g[j] += src[1 + j];
-        u[j] += src[1 + r + j];
-      }
-  }
-  dw_flat[sorted[p]] = dw;
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < r) {
-      dgB[p * r + j] = g[j];
-      duB[p * r + j] = u[j];
-    }
-}
-
 // --------------------------------------------------------- cross entropy
 // Online (max, sum exp) merge of log-sum-exp partials.
 __device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2) {
@@ -849,14 +858,6 @@ __global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, const float
 }
 
 // out[p][j] = wflat[sorted[p]] * in[p][j]
-__global__ void scale_rows_kernel(const float* __restrict__ in, const float* __restrict__ wflat,
-                                  const int32_t* __restrict__ sorted, int64_t M, int32_t r,
-                                  float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M * r) return;
-  out[i] = wflat[sorted[i / r]] * in[i];
-}
-
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -1056,13 +1057,6 @@ hipError_t launch_combine(const uint16_t* rows, const float* w, const int32_t* p
   return hipGetLastError();
 }
 
-hipError_t launch_down_finish(const float* part, int32_t ntiles, int64_t M, int32_t r,
-                              const int32_t* sorted, float* dw_flat, float* dgB, float* duB,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(down_finish_kernel, dim3(blocks_for(M, 256)), dim3(256), 0, st, part, ntiles,
-                     M, r, sorted, dw_flat, dgB, duB);
-  return hipGetLastError();
-}
 
 hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, const float* zlab,
                            const int64_t* labels, int64_t V, int64_t ignore_index, float* lse,
@@ -1115,14 +1109,6 @@ hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_scale_rows(const float* in, const float* wflat, const int32_t* sorted, int64_t M,
-                             int32_t r, float* out, hipStream_t st) {
-  const int64_t n = M * r;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(scale_rows_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, in, wflat,
-                     sorted, M, r, out);
-  return hipGetLastError();
-}
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
   if (n == 0) return hipSuccess;
