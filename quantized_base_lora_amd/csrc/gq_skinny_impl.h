@@ -76,14 +76,26 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
   const int lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, q = lane >> 4;
 
-  int bid;
-  {
-    const int nblk = gridDim.x, qq = nblk >> 3, rem = nblk & 7;
-    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    bid = (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + loc;
+  // workgroup -> tile in XCD-contiguous runs (ids go round-robin over the 8
+  // XCDs).  Grouped launches lay the runs over the m-slots that hold rows
+  // (tile_start[E] of them; the rest exit), n-tiles fastest, so the n-tiles
+  // of one m-slot run together on one XCD; dense launches keep m fastest.
+  auto xcd_run = [](int id, int count) {
+    const int qq = count >> 3, rem = count & 7, xcd = id & 7, loc = id >> 3;
+    return (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + loc;
+  };
+  int mslot, ntile;
+  if (p.offsets) {
+    const int used = p.tile_start[p.E] * p.ntiles;
+    if ((int)blockIdx.x >= used) return;
+    const int bid = xcd_run(blockIdx.x, used);
+    mslot = bid / p.ntiles;
+    ntile = bid - mslot * p.ntiles;
+  } else {
+    const int bid = xcd_run(blockIdx.x, gridDim.x);
+    mslot = bid % p.mtiles;
+    ntile = bid / p.mtiles;
   }
-  const int mslot = bid % p.mtiles;
-  const int ntile = bid / p.mtiles;
   int e = 0;
   int64_t r0, r1;
   if (p.offsets) {
@@ -636,14 +648,26 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
   const int cg = wave & 3, kg = wave >> 2;  // column group, reduction group
   const int nl = lane & 15, q = lane >> 4;
 
-  int bid;
-  {
-    const int nblk = gridDim.x, qq = nblk >> 3, rem = nblk & 7;
-    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    bid = (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + loc;
+  // workgroup -> tile in XCD-contiguous runs (ids go round-robin over the 8
+  // XCDs).  Grouped launches lay the runs over the m-slots that hold rows
+  // (tile_start[E] of them; the rest exit), n-tiles fastest, so the n-tiles
+  // of one m-slot run together on one XCD; dense launches keep m fastest.
+  auto xcd_run = [](int id, int count) {
+    const int qq = count >> 3, rem = count & 7, xcd = id & 7, loc = id >> 3;
+    return (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + loc;
+  };
+  int mslot, ntile;
+  if (p.offsets) {
+    const int used = p.tile_start[p.E] * p.ntiles;
+    if ((int)blockIdx.x >= used) return;
+    const int bid = xcd_run(blockIdx.x, used);
+    mslot = bid / p.ntiles;
+    ntile = bid - mslot * p.ntiles;
+  } else {
+    const int bid = xcd_run(blockIdx.x, gridDim.x);
+    mslot = bid % p.mtiles;
+    ntile = bid / p.mtiles;
   }
-  const int mslot = bid % p.mtiles;
-  const int ntile = bid / p.mtiles;
   int e = 0;
   int64_t r0, r1;
   if (p.offsets) {
