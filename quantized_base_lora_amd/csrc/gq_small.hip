@@ -122,8 +122,13 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
   int64_t p0, p1;
   int e = 0;
   if (a.tile16) {
-    const int tile = blockIdx.x;
-    if (tile >= a.tile16[a.E]) return;
+    // XCD-contiguous runs over the used tiles (ids go round-robin over the
+    // 8 XCDs): the tiles of one expert, which read its rank vectors, share
+    // an L2
+    const int used = a.tile16[a.E];
+    if ((int)blockIdx.x >= used) return;
+    const int q8 = used >> 3, rem = used & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int tile = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + loc;
     e = find_expert(a.tile16, a.E, tile);
     p0 = (int64_t)a.offsets[e] + (int64_t)(tile - a.tile16[e]) * 16;
     p1 = min((int64_t)a.offsets[e + 1], p0 + 16);
