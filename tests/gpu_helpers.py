@@ -25,7 +25,7 @@ def i64_dev(a) -> torch.Tensor:
 
 
 def u8_dev(a) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+    return torch.from_numpy(np.array(a, dtype=np.uint8, order="C", copy=True)).to(DEV)
 
 
 def host(t: torch.Tensor) -> np.ndarray:
