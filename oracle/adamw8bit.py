@@ -2,145 +2,138 @@
 
 Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
 the training", which names bitsandbytes' 8-bit AdamW as the optimizer of the
-adapters.  The pages give no formulas; the reading used here:
+adapters.  The pages give no formulas; the reading used here is the
+textbook AdamW step with decoupled weight decay, taken on states that are
+stored as 8-bit codes with one scale per block, everything in float64:
 
-* AdamW with decoupled weight decay.  Per element, in float32 and in this
-  order, without fused multiply-adds (the integer codes below are decided
-  by these float32 values, so the oracle takes them in the kernel's
-  precision):
-      m  = b1 * m + (1 - b1) * g
-      v  = b2 * v + (1 - b2) * (g * g)
-      d  = sqrt(v) * k2 + eps
-      p  = p * kd - s1 * (m / d)
-  with host constants k2 = 1 / sqrt(1 - b2^t), kd = 1 - lr * wd and
-  s1 = lr / (1 - b1^t), each formed in double precision from the float32
-  values of lr, b1, b2, wd and rounded once to float32; 1 - b1 and 1 - b2
-  likewise.  This is the textbook step p - lr (mh / (sqrt(vh) + eps) + wd p)
-  with mh = m / (1 - b1^t), vh = v / (1 - b2^t), the bias corrections moved
-  into constants (one division per element).
-* Both states are stored block-wise: 256 consecutive elements share one
-  float32 scale (the block's largest |m|, or largest v, after the update),
-  and each element keeps an 8-bit code of its value normalised by that
-  scale: multiplied by the float32 reciprocal 1 / scale (one division per
-  block).  A scale below the smallest normal float32, 2^-126 (zero
-  included), normalises its block to 0, since its reciprocal would
-  overflow; states that small are far below eps and do not move p.
-* The 8-bit code book is a "dynamic tree" layout: an optional sign bit,
-  then e zero bits, a one bit, and f fraction bits; the value is
-  10^-e * (0.1 + 0.9 * (i + 1) / 2^f) for fraction bits i (so every decade
-  below 1 gets its own group of codes), and the all-zero magnitude is 0.
-  Signed codes (for m): sign bit + 7 magnitude bits, e = 0..6, f = 6 - e.
-  Unsigned codes (for v): 8 magnitude bits, e = 0..7, f = 7 - e.
-* A value is stored as the code whose value is nearest (distances in
-  float32; on a tie the code of smaller magnitude).  A block whose scale is
-  below 2^-126 (0 included) stores code 0 everywhere.
+* State storage.  256 consecutive elements form a block.  A block stores
+  one float32 scale per state (the block's largest |m|, or largest v) and
+  one 8-bit code per element; the element's state is book[code] * scale.
+* Code books ("dynamic tree" layout): an optional sign bit, then e zero
+  bits, a one bit and f fraction bits i; the value is
+  10^-e * (0.1 + 0.9 * (i + 1) / 2^f), and the all-zero magnitude is 0.
+  Signed book (for m): sign bit 7 + 7 magnitude bits, e = 0..6, f = 6 - e.
+  Unsigned book (for v): 8 magnitude bits, e = 0..7, f = 7 - e.
+  The books here are the real numbers of that rule (float64).
+* One step t >= 1 with gradient g, on the dequantised states m, v:
+      m' = b1 m + (1 - b1) g,   v' = b2 v + (1 - b2) g^2
+      p' = p - lr * ( m'/(1 - b1^t) / (sqrt(v'/(1 - b2^t)) + eps) + wd p )
+  The hyper-parameters are the float32 values the caller passes.
+* New storage: scale_m = max |m'| and scale_v = max v' over the block,
+  stored as float32 (round to nearest); each code is the book entry
+  nearest to m' / scale_m (v' / scale_v), ties to the smaller magnitude.
+  A block whose scale is below the smallest normal float32 (2^-126, zero
+  included) stores code 0 for every element (such states are far below any
+  eps and do not move p).  p' is stored as float32 (round to nearest).
+
+The GPU kernel takes these steps in float32; its results are compared with
+the float64 values here within float32 error bounds (see the tests).
 """
 from __future__ import annotations
 
 import numpy as np
 
 BLOCK = 256
-F32 = np.float32
-
-
-# 10^-e as double literals (each the double nearest to the decimal value)
-_DECADE = (1.0, 0.1, 0.01, 0.001, 0.0001, 0.00001, 0.000001, 0.0000001)
+TINY = 2.0 ** -126
 
 
 def _magnitudes(bits: int) -> np.ndarray:
-    """Values of the magnitude codes 0 .. 2^bits - 1: the rule evaluated in
-    double precision in the order written, then rounded to float32."""
+    """Values of the magnitude codes 0 .. 2^bits - 1 of a book (float64)."""
     out = np.zeros(1 << bits, np.float64)
     for code in range(1, 1 << bits):
         top = code.bit_length() - 1      # position of the indicator bit
-        e = bits - 1 - top                # leading zeros
-        f = top                           # fraction bits below the indicator
+        e = bits - 1 - top                # zero bits above it
+        f = top                           # fraction bits below it
         i = code - (1 << top)
-        out[code] = _DECADE[e] * (0.1 + 0.9 * ((i + 1) / (1 << f)))
+        out[code] = 10.0 ** (-e) * (0.1 + 0.9 * (i + 1) / 2.0 ** f)
     return out
 
 
 def signed_table() -> np.ndarray:
-    """float32 [256]: code c = sign bit 7 | magnitude bits 0..6."""
+    """float64 [256]: code c = sign bit 7 | magnitude bits 0..6."""
     mag = _magnitudes(7)
-    t = np.concatenate([mag, -mag])
-    return t.astype(F32)
+    return np.concatenate([mag, -mag])
 
 
 def unsigned_table() -> np.ndarray:
-    return _magnitudes(8).astype(F32)
+    return _magnitudes(8)
+
+
+def _sorted_book(table: np.ndarray):
+    order = np.argsort(table, kind="stable")
+    vals = table[order]
+    # the signed book holds 0 twice (+0 and -0): keep the first (code 0)
+    keep = np.concatenate([[True], vals[1:] != vals[:-1]])
+    return vals[keep], order[keep]
 
 
 def quantize(xn: np.ndarray, table: np.ndarray) -> np.ndarray:
-    """Nearest code of each float32 value in xn (ties: smaller magnitude)."""
-    xn = np.asarray(xn, F32)
-    order = np.argsort(table, kind="stable")
-    vals = table[order]
-    # drop the duplicate -0 of the signed table: keep the first of equal values
-    keep = np.concatenate([[True], vals[1:] != vals[:-1]])
-    vals, order = vals[keep], order[keep]
-    hi = np.searchsorted(vals, xn, side="left")
-    hi = np.clip(hi, 0, vals.size - 1)
+    """Nearest code of each value in xn (ties: smaller magnitude)."""
+    xn = np.asarray(xn, np.float64)
+    vals, order = _sorted_book(table)
+    hi = np.clip(np.searchsorted(vals, xn, side="left"), 0, vals.size - 1)
     lo = np.clip(hi - 1, 0, vals.size - 1)
-    dlo = np.abs(xn - vals[lo]).astype(F32)
-    dhi = np.abs(vals[hi] - xn).astype(F32)
-    pick_hi = dhi < dlo
-    tie = dhi == dlo
-    # on a tie take the code of smaller magnitude
-    pick_hi = pick_hi | (tie & (np.abs(vals[hi]) < np.abs(vals[lo])))
-    idx = np.where(pick_hi, hi, lo)
-    return order[idx].astype(np.uint8)
+    dlo = np.abs(xn - vals[lo])
+    dhi = np.abs(vals[hi] - xn)
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (np.abs(vals[hi]) < np.abs(vals[lo])))
+    return order[np.where(pick_hi, hi, lo)].astype(np.uint8)
+
+
+def neighbours(xn: np.ndarray, table: np.ndarray):
+    """For each value: the codes of the book entries just below and just
+    above it (equal when the value is a book entry or outside the book), and
+    the distance of the value from the midpoint between those two entries."""
+    xn = np.asarray(xn, np.float64)
+    vals, order = _sorted_book(table)
+    hi = np.clip(np.searchsorted(vals, xn, side="left"), 0, vals.size - 1)
+    lo = np.where(vals[hi] > xn, np.clip(hi - 1, 0, vals.size - 1), hi)
+    mid = 0.5 * (vals[lo] + vals[hi])
+    return order[lo].astype(np.uint8), order[hi].astype(np.uint8), np.abs(xn - mid)
 
 
 def dequantize(codes: np.ndarray, scale: np.ndarray, table: np.ndarray, n: int) -> np.ndarray:
-    """float32 [n] from codes [n] and block scales [ceil(n / 256)]."""
-    s = np.repeat(np.asarray(scale, F32), BLOCK)[:n]
-    return (table[np.asarray(codes, np.int64)] * s).astype(F32)
+    """float64 [n] states from codes [n] and block scales [ceil(n / 256)]."""
+    s = np.repeat(np.asarray(scale, np.float64), BLOCK)[:n]
+    return table[np.asarray(codes, np.int64)] * s
+
+
+def _block_max(a: np.ndarray) -> np.ndarray:
+    n = a.size
+    nblk = (n + BLOCK - 1) // BLOCK
+    return np.pad(a, (0, nblk * BLOCK - n)).reshape(nblk, BLOCK).max(axis=1)
+
+
+def step_exact(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
+    """One step in float64 from the stored state (p float32 [n], g float32
+    [n], codes uint8 [n], scales float32 [nblk]).  Returns a dict of float64
+    results before storage rounding: p, m, v (new states), scale_m, scale_v
+    (block maxima), mn, vn (states divided by their block's scale, 0 where
+    the scale is below 2^-126) and m_in, v_in (the dequantised old states)."""
+    lr, b1, b2, eps, wd = (float(np.float32(x)) for x in (lr, b1, b2, eps, wd))
+    p = np.asarray(p, np.float32).astype(np.float64)
+    g = np.asarray(g, np.float32).astype(np.float64)
+    n = p.size
+    m_in = dequantize(mq, sm, signed_table(), n)
+    v_in = dequantize(vq, sv, unsigned_table(), n)
+    m = b1 * m_in + (1.0 - b1) * g
+    v = b2 * v_in + (1.0 - b2) * g * g
+    mhat = m / (1.0 - b1 ** t)
+    vhat = v / (1.0 - b2 ** t)
+    p_new = p - lr * (mhat / (np.sqrt(vhat) + eps) + wd * p)
+    scale_m = _block_max(np.abs(m))
+    scale_v = _block_max(v)
+    rs_m = np.repeat(scale_m, BLOCK)[:n]
+    rs_v = np.repeat(scale_v, BLOCK)[:n]
+    mn = np.where(rs_m >= TINY, m / np.where(rs_m >= TINY, rs_m, 1.0), 0.0)
+    vn = np.where(rs_v >= TINY, v / np.where(rs_v >= TINY, rs_v, 1.0), 0.0)
+    return {"p": p_new, "p_in": p, "m": m, "v": v, "scale_m": scale_m, "scale_v": scale_v, "mn": mn, "vn": vn,
+            "m_in": m_in, "v_in": v_in, "g": g, "b1": b1, "b2": b2, "lr": lr, "eps": eps, "wd": wd, "t": t}
 
 
 def step(p, g, mq, vq, sm, sv, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
-    """One AdamW step on float32 p [n] with gradient g [n] and 8-bit states
-    (mq, vq uint8 [n]; sm, sv float32 [nblk]).  Returns new (p, mq, vq, sm, sv)."""
-    # hyper-parameters are float32 values (the kernel's argument type); the
-    # derived constants come from them in double precision, rounded once
-    lr, b1, b2, eps, wd = (float(F32(x)) for x in (lr, b1, b2, eps, wd))
-    ts, tu = signed_table(), unsigned_table()
-    p = np.asarray(p, F32).copy()
-    g = np.asarray(g, F32)
-    n = p.size
-    m = dequantize(mq, sm, ts, n)
-    v = dequantize(vq, sv, tu, n)
-    b1f, b2f = F32(b1), F32(b2)
-    om1, om2 = F32(1.0 - b1), F32(1.0 - b2)
-    k2 = F32(1.0 / np.sqrt(1.0 - b2 ** t))
-    kd = F32(1.0 - lr * wd)
-    s1 = F32(lr / (1.0 - b1 ** t))
-    epsf = F32(eps)
-    m = (b1f * m + om1 * g).astype(F32)
-    v = (b2f * v + om2 * (g * g)).astype(F32)
-    d = (np.sqrt(v) * k2 + epsf).astype(F32)
-    p = (p * kd - s1 * (m / d).astype(F32)).astype(F32)
-    nblk = (n + BLOCK - 1) // BLOCK
-    pad = nblk * BLOCK - n
-    am = np.pad(np.abs(m), (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
-    av = np.pad(v, (0, pad)).reshape(nblk, BLOCK).max(axis=1).astype(F32)
-    # per-block reciprocal scales; below the smallest normal float32 the
-    # block normalises to 0
-    tiny = F32(2.0 ** -126)
-    rm = np.where(am >= tiny, F32(1) / np.where(am >= tiny, am, F32(1)), F32(0)).astype(F32)
-    rv = np.where(av >= tiny, F32(1) / np.where(av >= tiny, av, F32(1)), F32(0)).astype(F32)
-    mn = (m * np.repeat(rm, BLOCK)[:n]).astype(F32)
-    vn = (v * np.repeat(rv, BLOCK)[:n]).astype(F32)
-    return p, quantize(mn, ts), quantize(vn, tu), am, av
-
-
-def step_fp64(p, g, m, v, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
-    """The same AdamW step in float64 with unquantised states (a pin)."""
-    p = np.asarray(p, np.float64)
-    g = np.asarray(g, np.float64)
-    m = b1 * m + (1 - b1) * g
-    v = b2 * v + (1 - b2) * g * g
-    mh = m / (1 - b1 ** t)
-    vh = v / (1 - b2 ** t)
-    p = p - lr * (mh / (np.sqrt(vh) + eps) + wd * p)
-    return p, m, v
+    """One step with the results stored: (p float32, m codes, v codes,
+    m scales float32, v scales float32)."""
+    r = step_exact(p, g, mq, vq, sm, sv, t, lr, b1, b2, eps, wd)
+    return (r["p"].astype(np.float32), quantize(r["mn"], signed_table()),
+            quantize(r["vn"], unsigned_table()), r["scale_m"].astype(np.float32),
+            r["scale_v"].astype(np.float32))
