@@ -29,7 +29,8 @@
  *  - No full-precision copy of a quantised weight is ever written: the
  *    blocks are decoded into registers / LDS inside the kernels.
  *  - Calls are reentrant; there is no global mutable state besides the
- *    thread-local error text.
+ *    thread-local error text and the fixed device scratch array of
+ *    gq_linear_lora_bwd_noalloc (see there).
  *
  * Block formats (32 weights per block, little-endian fields, the blocks of
  * one row contiguous, rows contiguous):
@@ -153,6 +154,32 @@ size_t gq_linear_lora_bwd_workspace_size(const gq_lora_linear* L, int64_t T);
 int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* xa,
                        const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the fast LoRA backward of
+ * gq_linear_lora_bwd with its scratch taken from a fixed device array inside
+ * the library instead of a caller workspace.  Same arguments, results and
+ * kernels as gq_linear_lora_bwd (bitwise equal outputs); it allocates
+ * nothing (no hipMalloc/hipFree, no allocating library call).
+ *  - The array holds GQ_NOALLOC_SCRATCH_BYTES bytes on each GPU the library
+ *    runs on, from the first call on that GPU until the process ends.  A
+ *    shape whose gq_linear_lora_bwd_workspace_size() exceeds it is rejected
+ *    with GQ_EWORKSPACE before any launch.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress) with that device current: the stream must belong
+ *    to the current device.
+ *  - Every call on one GPU shares that GPU's array and leaves its contents
+ *    behind; calls that overlap in time on one GPU (different streams or
+ *    threads without ordering) race on it and give undefined results.
+ *    Calls ordered on one stream are safe.
+ * gq_noalloc_scratch_bytes() returns the array's size.
+ */
+#define GQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t gq_noalloc_scratch_bytes(void);
+int gq_linear_lora_bwd_noalloc(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                               const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
+                               void* stream);
 
 /*
  * MoE routing, softmax top-k.  For each token t over logits [T][E] (fp32):

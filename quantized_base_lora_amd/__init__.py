@@ -28,6 +28,7 @@ EXPORTS = (
     "gq_version", "gq_last_error", "gq_block_bytes", "gq_profile_mmq_events", "gq_dequant",
     "gq_linear_lora_fwd_workspace_size", "gq_linear_lora_fwd",
     "gq_linear_lora_bwd_workspace_size", "gq_linear_lora_bwd",
+    "gq_noalloc_scratch_bytes", "gq_linear_lora_bwd_noalloc",
     "gq_moe_route_workspace_size", "gq_moe_route", "gq_moe_route_bwd",
     "gq_moe_combine_fwd", "gq_moe_combine_bwd",
     "gq_grouped_mmq_lora_fwd_workspace_size", "gq_grouped_mmq_lora_fwd",
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH):
         "gq_linear_lora_fwd": (C.c_int, [P(LoraLinear), vp, i64, vp, vp, vp, sz, vp]),
         "gq_linear_lora_bwd_workspace_size": (sz, [P(LoraLinear), i64]),
         "gq_linear_lora_bwd": (C.c_int, [P(LoraLinear), vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "gq_noalloc_scratch_bytes": (sz, []),
+        "gq_linear_lora_bwd_noalloc": (C.c_int, [P(LoraLinear), vp, vp, vp, i64, vp, vp, vp, vp]),
         "gq_moe_route_workspace_size": (sz, [i64, i32, i32]),
         "gq_moe_route": (C.c_int, [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "gq_moe_route_bwd": (C.c_int, [vp, vp, vp, i64, i32, i32, vp, vp]),
@@ -196,6 +199,23 @@ def linear_lora_bwd(p: Proj, x, xa, dy, need_dx: bool = True, ws: torch.Tensor |
         ws = _workspace(nbytes, x.device)
     _check(lib().gq_linear_lora_bwd(C.byref(L), _ptr(x), _ptr(xa), _ptr(dy), T, _ptr(dx), _ptr(dA),
                                     _ptr(dB), _ptr(ws), nbytes, _stream()))
+    return dx, dA, dB
+
+
+def linear_lora_bwd_noalloc(p: Proj, x, xa, dy, dx=None, dA=None, dB=None):
+    """gq_linear_lora_bwd_noalloc: the fast LoRA backward with the library's
+    fixed device scratch (no workspace).  Outputs may be passed in
+    (preallocated) so that the call itself allocates nothing."""
+    T = x.shape[0]
+    if dx is None:
+        dx = torch.empty((T, p.n_in), dtype=torch.bfloat16, device=x.device)
+    if dA is None:
+        dA = torch.empty((p.rank, p.n_in), dtype=torch.float32, device=x.device)
+    if dB is None:
+        dB = torch.empty((p.n_out, p.rank), dtype=torch.float32, device=x.device)
+    L = p.c()
+    _check(lib().gq_linear_lora_bwd_noalloc(C.byref(L), _ptr(x), _ptr(xa), _ptr(dy), T, _ptr(dx),
+                                            _ptr(dA), _ptr(dB), _stream()))
     return dx, dA, dB
 
 

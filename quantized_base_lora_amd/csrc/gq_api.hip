@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/gq.h"
@@ -331,6 +332,69 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
     g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
     g.o0 = dx; g.ldo = K;
     HIP_TRY(launch_gemm(L->qtype, EPI_LIN_BWD, tc, g, st), "gq_linear_lora_bwd: dX MMQ");
+  }
+  return GQ_OK;
+}
+
+// ------------------------------------------------ linear backward, no allocation
+}  // extern "C"
+
+namespace {
+// Scratch of gq_linear_lora_bwd_noalloc: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// never passes `scratch` itself to a kernel -- in host code that name is a
+// stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)GQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// device address of this device's scratch array (the current device must be
+// the one the stream belongs to)
+int scratch_for_current_device(void** out, const char* name) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, name);
+  if (dev < 0 || dev >= kMaxDevices) return fail(GQ_ENOTSUP, "%s: device %d beyond %d", name, dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], name);
+  *out = g_scratch_ptr[dev];
+  return GQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t gq_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int gq_linear_lora_bwd_noalloc(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                               const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
+                               void* stream) {
+  g_err.clear();
+  const char* name = "gq_linear_lora_bwd_noalloc";
+  int rc = check_proj(L, name, false);
+  if (rc) return rc;
+  if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "%s: bad T %lld", name, (long long)T);
+  const size_t need = T > 0 ? gq_linear_lora_bwd_workspace_size(L, T) : 0;
+  if (need > kScratchBytes)
+    return fail(GQ_EWORKSPACE, "%s: needs %zu bytes of scratch, the fixed maximum is %zu", name, need,
+                kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && (rc = scratch_for_current_device(&ws, name))) return rc;
+  // the same kernels as gq_linear_lora_bwd; every scratch word they read is
+  // written earlier in the same call, so nothing needs clearing
+  rc = gq_linear_lora_bwd(L, x, xa, dy, T, dx, dA, dB, ws, kScratchBytes, stream);
+  if (rc) {
+    std::string msg = g_err;
+    return fail(rc, "%s", msg.c_str());
   }
   return GQ_OK;
 }

@@ -182,3 +182,15 @@ def test_adamw8bit_validation(gq):
     assert st(*args, -1, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL
     assert st(None, *args[1:], 100, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_EINVAL
     assert st(*args, 0, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == gq.GQ_OK  # n = 0: no-op
+
+
+def test_noalloc_rejects_oversized_shapes_on_the_host(gq):
+    lib = gq.lib()
+    cap = lib.gq_noalloc_scratch_bytes()
+    L = proj(gq, qtype=1, rank=16, n_out=1 << 20, n_in=1 << 16)
+    T = 1 << 20
+    assert lib.gq_linear_lora_bwd_workspace_size(C.byref(L), T) > cap
+    rc = lib.gq_linear_lora_bwd_noalloc(C.byref(L), FAKE, FAKE, FAKE, T, FAKE, FAKE, FAKE, None)
+    assert rc == gq.GQ_EWORKSPACE and "scratch" in gq.last_error()
+    assert lib.gq_linear_lora_bwd_noalloc(C.byref(proj(gq, rank=17)), FAKE, FAKE, FAKE, 8, FAKE, FAKE,
+                                          FAKE, None) == gq.GQ_EINVAL
