@@ -18,6 +18,15 @@
  *    patterns.  The caller owns all memory; the library never allocates.
  *    Temporary storage comes from a caller-provided workspace sized by the
  *    matching *_workspace_size() query (bytes, 256-byte aligned pointer).
+ *  - Alignment (checked on the host; GQ_EINVAL names the argument): bf16
+ *    arrays read or written with 16-byte accesses must be 16-byte aligned --
+ *    x, dy of the linear layer, `in` of the grouped forward, dy, g, u, h, x,
+ *    dg, du of the grouped backward, o, y, dxrows, dx of the combines, h of
+ *    the LM head, every array of the RMS normalisation (w included), the
+ *    dequant output; the other bf16 outputs (y, dx of the linear layer,
+ *    out/save_g/save_u, dxrows of the grouped calls, dh) 2-byte aligned;
+ *    float32 and int32 arrays 4-byte; int64 labels 8-byte; w_blocks 4-byte
+ *    (2-byte for gq_dequant); A and B 16-byte; the workspace 256-byte.
  *  - `stream` is a hipStream_t (0 = the default stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises, nothing copies
  *    between host and device.  Results are stream-ordered.
@@ -115,11 +124,14 @@ int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int ou
  *   A         [E][rank][n_in]  float32
  *   B         [E][n_out][rank] float32
  *   scale     s = alpha / rank
- * Pointers: w_blocks 4-byte aligned, A and B 16-byte aligned.
- * Constraints: n_in % 64 == 0 (whole pairs of blocks per row, so every row
- * starts dword-aligned), n_out % 8 == 0 (16-byte activation rows in the
- * backward), 1 <= rank <= 16, 1 <= n_experts <= 1024.  Grouped backward also
- * needs the expert intermediate size (gate/up n_out) % 64 == 0.
+ * Pointers: w_blocks 4-byte aligned, A and B 16-byte aligned (rows of an
+ * odd number of Q8_0 / Q4_0 blocks start only 2-byte aligned: the kernels
+ * read blocks with 2-byte aligned loads).
+ * Constraints: n_in % 32 == 0 (whole blocks), n_out % 8 == 0 (the backward
+ * reads activation rows of n_out bf16 with 16-byte loads), 1 <= rank <= 16,
+ * 1 <= n_experts <= 1024.  The grouped GATEUP backward also needs the expert
+ * intermediate size (gate/up n_out) % 64 == 0: it reduces over [dg | du]
+ * in 64-deep steps and switches operands at a step boundary.
  */
 typedef struct gq_lora_linear {
     int32_t qtype;
@@ -312,6 +324,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
  * tokens):
  *   dh [T][H] bf16 = G deq(W) + s (G B) A;  dA [rank][H] = s (G B)^T h;
  *   dB [V][rank] = s G^T (h A^T)            (fp32, overwritten)
+ * V (n_out) may be any positive size (no multiple-of-8 constraint here).
  * labels [T] int64, each in [0, V) or == ignore_index.  With no valid label
  * the loss and gradients are zero.  A label outside [0, V) that is not
  * ignore_index is treated as ignored and sets the workspace's first 32-bit

@@ -128,7 +128,8 @@ def forward_bruteforce(inp: dict, ew: ExpertWeights | None = None, tokens=None):
 def backward(inp: dict, fwd: dict, ew: ExpertWeights | None = None):
     """Reverse mode of `forward` for upstream gradient dY = inp['dy'] (bf16).
 
-    Returns dx [T, H], dlogits [T, E], dw [T, k] and adapter gradients
+    Returns dx [T, H], dlogits [T, E], dw [T, k], the SwiGLU input gradients
+    dg, du [T*k, I] (rows in sorted order) and adapter gradients
     dAg, dAu [E, r, H]; dBg, dBu [E, I, r]; dAd [E, r, I]; dBd [E, H, r]."""
     ew = ew or ExpertWeights(inp)
     s = float(inp["scale"])
@@ -140,6 +141,8 @@ def backward(inp: dict, fwd: dict, ew: ExpertWeights | None = None):
     M = T * k
     dxrows = np.zeros((M, H))
     dw_flat = np.zeros(M)
+    dg_rows = np.zeros((M, I))
+    du_rows = np.zeros((M, I))
     g = dict(dAg=np.zeros((E, r, H)), dAu=np.zeros((E, r, H)), dBg=np.zeros((E, I, r)),
              dBu=np.zeros((E, I, r)), dAd=np.zeros((E, r, I)), dBd=np.zeros((E, H, r)))
     for e in range(E):
@@ -163,6 +166,8 @@ def backward(inp: dict, fwd: dict, ew: ExpertWeights | None = None):
         sg = _sigmoid(gg)
         dg = dh * uu * sg * (1.0 + gg * (1.0 - sg))
         du = dh * gg * sg
+        dg_rows[p0:p1] = dg
+        du_rows[p0:p1] = du
         dgB = dg @ Bg
         duB = du @ Bu
         dxrows[p0:p1] = dg @ Wg + du @ Wu + s * (dgB @ Ag + duB @ Au)
@@ -176,7 +181,7 @@ def backward(inp: dict, fwd: dict, ew: ExpertWeights | None = None):
         dx += dxrows[pos[a]]
     dw = dw_flat.reshape(T, k)
     dlogits = routing.backward(fwd["ids"], w, dw, E)
-    out = dict(dx=dx, dlogits=dlogits, dw=dw)
+    out = dict(dx=dx, dlogits=dlogits, dw=dw, dg=dg_rows, du=du_rows)
     out.update(g)
     return out
 
@@ -206,4 +211,5 @@ def expert_backward_rows(inp: dict, e: int, rows_a: np.ndarray, w_rows: np.ndarr
                 dBg=s * (dg.T @ f["xa_g"]), dBu=s * (du.T @ f["xa_u"]),
                 dAg=s * (dgB.T @ X), dAu=s * (duB.T @ X),
                 dxrows=dg @ Wg + du @ Wu + s * (dgB @ Ag + duB @ Au),
-                dw=(dy[t] * f["o"]).sum(axis=1), y_rows=f["o"])
+                dw=(dy[t] * f["o"]).sum(axis=1), y_rows=f["o"], dg=dg, du=du,
+                g=f["g"], u=f["u"], h=f["h"])

@@ -140,6 +140,36 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _expect(t, name: str, dtype, shape=None, min_rows=None, on_gpu=True):
+    """Argument check before any pointer reaches the library: a contiguous
+    GPU tensor of `dtype` with exactly `shape` (entries None: any size), or
+    at least `min_rows` rows.  The C layer only sees raw pointers, so a wrong
+    dtype, layout or size would otherwise be read as garbage or past the end
+    of the allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(s is None or int(a) == int(s) for a, s in zip(t.shape, shape))
+        if not ok:
+            want = tuple("*" if s is None else int(s) for s in shape)
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
+    if min_rows is not None and (t.dim() < 1 or t.shape[0] < min_rows):
+        raise ValueError(f"{name}: {t.shape[0] if t.dim() else 0} rows, at least {min_rows} needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (row-major)")
+    if on_gpu and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (device {t.device})")
+    return t
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor | None:
     if nbytes == 0:
         return None
@@ -163,6 +193,30 @@ class Proj:
     def rank(self) -> int:
         return self.A.shape[-2]
 
+    def check(self):
+        """Shapes, dtypes and sizes of the blocks and adapters against
+        (qtype, n_out, n_in, n_experts); raises before any library call."""
+        if self.qtype not in BLOCK_BYTES:
+            raise ValueError(f"unknown qtype {self.qtype}")
+        if self.n_in % 32:
+            raise ValueError(f"n_in {self.n_in} is not a multiple of 32")
+        E = self.n_experts
+        nbytes = E * self.n_out * (self.n_in // 32) * BLOCK_BYTES[self.qtype]
+        _expect(self.blocks, "blocks", torch.uint8, on_gpu=False)
+        if self.blocks.numel() != nbytes:
+            raise ValueError(f"blocks: {self.blocks.numel()} bytes, expected {nbytes} "
+                             f"({E} x {self.n_out} rows x {self.n_in // 32} blocks of {BLOCK_BYTES[self.qtype]} B)")
+        r = self.A.shape[-2] if self.A.dim() >= 2 else 0
+        if not 1 <= r <= 16:
+            raise ValueError(f"A {tuple(self.A.shape)}: rank {r} not in [1, 16]")
+        lead = (E,) if E > 1 or self.A.dim() == 3 else ()
+        _expect(self.A, "A", torch.float32, lead + (r, self.n_in), on_gpu=False)
+        _expect(self.B, "B", torch.float32, lead + (self.n_out, r), on_gpu=False)
+        for name, t in (("blocks", self.blocks), ("A", self.A), ("B", self.B)):
+            _expect(t, name, t.dtype)
+        _same_device(self.blocks, self.A, self.B)
+        return self
+
     def c(self) -> LoraLinear:
         return LoraLinear(self.qtype, self.rank, self.n_out, self.n_in, _ptr(self.blocks),
                           _ptr(self.A), _ptr(self.B), float(self.scale), self.n_experts)
@@ -170,6 +224,12 @@ class Proj:
 
 # ------------------------------------------------------------------ entry points
 def dequant(qtype: int, blocks: torch.Tensor, rows: int, cols: int, out_dtype=torch.float32):
+    if qtype not in BLOCK_BYTES or cols % 32:
+        raise ValueError(f"dequant: qtype {qtype} / cols {cols}")
+    _expect(blocks, "blocks", torch.uint8, on_gpu=False)
+    if blocks.numel() < rows * (cols // 32) * BLOCK_BYTES[qtype]:
+        raise ValueError(f"blocks: {blocks.numel()} bytes, {rows * (cols // 32) * BLOCK_BYTES[qtype]} needed")
+    _expect(blocks, "blocks", torch.uint8)
     out = torch.empty((rows, cols), dtype=out_dtype, device=blocks.device)
     code = F32 if out_dtype == torch.float32 else BF16
     _check(lib().gq_dequant(qtype, _ptr(blocks), rows, cols, code, _ptr(out), _stream()))
@@ -177,6 +237,9 @@ def dequant(qtype: int, blocks: torch.Tensor, rows: int, cols: int, out_dtype=to
 
 
 def linear_lora_fwd(p: Proj, x: torch.Tensor):
+    p.check()
+    _expect(x, "x", torch.bfloat16, (None, p.n_in))
+    _same_device(x, p.blocks)
     T = x.shape[0]
     y = torch.empty((T, p.n_out), dtype=torch.bfloat16, device=x.device)
     xa = torch.empty((T, p.rank), dtype=torch.float32, device=x.device)
@@ -188,8 +251,20 @@ def linear_lora_fwd(p: Proj, x: torch.Tensor):
     return y, xa
 
 
-def linear_lora_bwd(p: Proj, x, xa, dy, need_dx: bool = True, ws: torch.Tensor | None = None):
+def _check_lin_bwd(p: Proj, x, xa, dy):
+    p.check()
+    _expect(x, "x", torch.bfloat16, (None, p.n_in))
     T = x.shape[0]
+    _expect(xa, "xa", torch.float32, (T, p.rank))
+    _expect(dy, "dy", torch.bfloat16, (T, p.n_out))
+    _same_device(x, xa, dy, p.blocks)
+    return T
+
+
+def linear_lora_bwd(p: Proj, x, xa, dy, need_dx: bool = True, ws: torch.Tensor | None = None):
+    T = _check_lin_bwd(p, x, xa, dy)
+    if ws is not None:
+        _expect(ws, "ws", torch.uint8)
     dx = torch.empty((T, p.n_in), dtype=torch.bfloat16, device=x.device) if need_dx else None
     dA = torch.empty((p.rank, p.n_in), dtype=torch.float32, device=x.device)
     dB = torch.empty((p.n_out, p.rank), dtype=torch.float32, device=x.device)
@@ -206,13 +281,17 @@ def linear_lora_bwd_noalloc(p: Proj, x, xa, dy, dx=None, dA=None, dB=None):
     """gq_linear_lora_bwd_noalloc: the fast LoRA backward with the library's
     fixed device scratch (no workspace).  Outputs may be passed in
     (preallocated) so that the call itself allocates nothing."""
-    T = x.shape[0]
+    T = _check_lin_bwd(p, x, xa, dy)
     if dx is None:
         dx = torch.empty((T, p.n_in), dtype=torch.bfloat16, device=x.device)
     if dA is None:
         dA = torch.empty((p.rank, p.n_in), dtype=torch.float32, device=x.device)
     if dB is None:
         dB = torch.empty((p.n_out, p.rank), dtype=torch.float32, device=x.device)
+    _expect(dx, "dx", torch.bfloat16, (T, p.n_in))
+    _expect(dA, "dA", torch.float32, (p.rank, p.n_in))
+    _expect(dB, "dB", torch.float32, (p.n_out, p.rank))
+    _same_device(x, dx, dA, dB)
     L = p.c()
     _check(lib().gq_linear_lora_bwd_noalloc(C.byref(L), _ptr(x), _ptr(xa), _ptr(dy), T, _ptr(dx),
                                             _ptr(dA), _ptr(dB), _stream()))
@@ -220,6 +299,7 @@ def linear_lora_bwd_noalloc(p: Proj, x, xa, dy, dx=None, dA=None, dB=None):
 
 
 def moe_route(logits: torch.Tensor, k: int):
+    _expect(logits, "logits", torch.float32, (None, None))
     T, E = logits.shape
     dev = logits.device
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -235,13 +315,23 @@ def moe_route(logits: torch.Tensor, k: int):
 
 
 def moe_route_bwd(ids, w, dw, E: int):
+    _expect(ids, "ids", torch.int32, (None, None))
     T, k = ids.shape
+    _expect(w, "w", torch.float32, (T, k))
+    _expect(dw, "dw", torch.float32, (T, k))
+    _same_device(ids, w, dw)
     dl = torch.empty((T, E), dtype=torch.float32, device=ids.device)
     _check(lib().gq_moe_route_bwd(_ptr(ids), _ptr(w), _ptr(dw), T, E, k, _ptr(dl), _stream()))
     return dl
 
 
 def moe_combine_fwd(o, w, pos, T: int, k: int):
+    _expect(o, "o", torch.bfloat16, (T * k, None))
+    _expect(w, "w", torch.float32, None)
+    _expect(pos, "pos", torch.int32, None)
+    if w.numel() != T * k or pos.numel() != T * k:
+        raise ValueError(f"w / pos: {w.numel()} / {pos.numel()} elements, expected {T * k}")
+    _same_device(o, w, pos)
     H = o.shape[1]
     y = torch.empty((T, H), dtype=torch.bfloat16, device=o.device)
     _check(lib().gq_moe_combine_fwd(_ptr(o), _ptr(w), _ptr(pos), T, k, H, _ptr(y), _stream()))
@@ -249,6 +339,9 @@ def moe_combine_fwd(o, w, pos, T: int, k: int):
 
 
 def moe_combine_bwd(dxrows, pos, T: int, k: int):
+    _expect(dxrows, "dxrows", torch.bfloat16, (T * k, None))
+    _expect(pos, "pos", torch.int32, (T * k,))
+    _same_device(dxrows, pos)
     H = dxrows.shape[1]
     dx = torch.empty((T, H), dtype=torch.bfloat16, device=dxrows.device)
     _check(lib().gq_moe_combine_bwd(_ptr(dxrows), _ptr(pos), T, k, H, _ptr(dx), _stream()))
@@ -257,7 +350,10 @@ def moe_combine_bwd(dxrows, pos, T: int, k: int):
 
 def rmsnorm_fwd(x, w, eps: float = 1e-6):
     """y = x * rstd * w (bf16 [T, H]) and rstd (fp32 [T]); w fp32 [H]."""
+    _expect(x, "x", torch.bfloat16, (None, None))
     T, H = x.shape
+    _expect(w, "w", torch.float32, (H,))
+    _same_device(x, w)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     rstd = torch.empty((T,), dtype=torch.float32, device=x.device)
     _check(lib().gq_rmsnorm_fwd(_ptr(x), _ptr(w), T, H, float(eps), _ptr(y), _ptr(rstd), _stream()))
@@ -266,7 +362,12 @@ def rmsnorm_fwd(x, w, eps: float = 1e-6):
 
 def rmsnorm_bwd(dy, x, w, rstd):
     """Input gradient of rmsnorm_fwd (w is frozen)."""
+    _expect(x, "x", torch.bfloat16, (None, None))
     T, H = x.shape
+    _expect(dy, "dy", torch.bfloat16, (T, H))
+    _expect(w, "w", torch.float32, (H,))
+    _expect(rstd, "rstd", torch.float32, (T,))
+    _same_device(x, dy, w, rstd)
     dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(lib().gq_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), T, H, _ptr(dx), _stream()))
     return dx
@@ -290,6 +391,11 @@ class AdamW8bitState:
 def adamw8bit_step(p, g, st: AdamW8bitState, lr: float = 1e-4, betas=(0.9, 0.999), eps: float = 1e-8,
                    weight_decay: float = 0.0):
     """One in-place AdamW step of the fp32 tensor p (contiguous) with grad g."""
+    _expect(p, "p", torch.float32, None)
+    _expect(g, "g", torch.float32, None)
+    if p.numel() != st.n or g.numel() != st.n:
+        raise ValueError(f"p / g: {p.numel()} / {g.numel()} elements, the state holds {st.n}")
+    _same_device(p, g, st.m_codes)
     st.step += 1
     _check(lib().gq_adamw8bit_step(_ptr(p), _ptr(g), _ptr(st.m_codes), _ptr(st.v_codes),
                                    _ptr(st.m_scale), _ptr(st.v_scale), st.n, st.step, float(lr),
@@ -302,7 +408,19 @@ def _projs(ps):
     return arr
 
 
+def _check_group(projs, offsets, M: int, gather):
+    for p in projs:
+        p.check()
+    E = projs[0].n_experts
+    _expect(offsets, "offsets", torch.int32, (E + 1,))
+    if gather is not None:
+        _expect(gather, "gather", torch.int32, (M,))
+    _same_device(offsets, gather, *[p.blocks for p in projs])
+
+
 def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, offsets, M: int):
+    _check_group(projs, offsets, M, gather)
+    _expect(inp, "inp", torch.bfloat16, (None, projs[0].n_in), min_rows=None if gather is not None else M)
     dev = inp.device
     N = projs[0].n_out
     r = projs[0].rank
@@ -324,8 +442,33 @@ def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, off
 
 def grouped_mmq_lora_bwd(projs, mode: int, **t):
     """Thin wrapper: `t` maps gq_grouped_bwd_args field names to tensors/ints."""
-    arr = _projs(projs)
     M = int(t["M"])
+    _check_group(projs, t["offsets"], M, t.get("gather"))
+    H = projs[0].n_out if mode == BWD_DOWN_SWIGLU else projs[0].n_in
+    I = projs[0].n_in if mode == BWD_DOWN_SWIGLU else projs[0].n_out
+    E, r = projs[0].n_experts, projs[0].rank
+    gathered = t.get("gather") is not None
+    want = {"dy": (torch.bfloat16, (None, H)), "x": (torch.bfloat16, (None, H)),
+            "w_flat": (torch.float32, (M,)), "sorted": (torch.int32, (M,)),
+            "g": (torch.bfloat16, (M, I)), "u": (torch.bfloat16, (M, I)), "h": (torch.bfloat16, (M, I)),
+            "xa_d": (torch.float32, (M, r)), "dw_flat": (torch.float32, (M,)),
+            "dA_d": (torch.float32, (E, r, I)), "dB_d": (torch.float32, (E, H, r)),
+            "dg": (torch.bfloat16, (M, I)), "du": (torch.bfloat16, (M, I)),
+            "dgB": (torch.float32, (M, r)), "duB": (torch.float32, (M, r)),
+            "xa": (torch.float32, (2, M, r)), "dxrows": (torch.bfloat16, (M, H)),
+            "dA_g": (torch.float32, (E, r, H)), "dB_g": (torch.float32, (E, I, r)),
+            "dA_u": (torch.float32, (E, r, H)), "dB_u": (torch.float32, (E, I, r))}
+    for name, (dt, shape) in want.items():
+        v = t.get(name)
+        if v is None:
+            continue
+        if name in ("w_flat", "dw_flat", "sorted"):  # flat [M] views of [T, k] arrays
+            _expect(v, name, dt, None)
+            if v.numel() != M:
+                raise ValueError(f"{name}: {v.numel()} elements, expected {M}")
+        else:
+            _expect(v, name, dt, shape, min_rows=None if gathered or name not in ("dy", "x") else M)
+    arr = _projs(projs)
     dev = t["offsets"].device
     nbytes = lib().gq_grouped_mmq_lora_bwd_workspace_size(arr, len(projs), mode, M)
     ws = t.pop("ws", None)
@@ -345,7 +488,11 @@ def grouped_mmq_lora_bwd(projs, mode: int, **t):
 
 def lmhead_chunked_ce(head: Proj, h, labels, chunk_rows: int = 4096, ignore_index: int = -100,
                       grad_scale: float = 1.0, want_grad: bool = True, ws=None):
+    head.check()
+    _expect(h, "h", torch.bfloat16, (None, head.n_in))
     T = h.shape[0]
+    _expect(labels, "labels", torch.int64, (T,))
+    _same_device(h, labels, head.blocks)
     dev = h.device
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
@@ -417,4 +564,4 @@ def moe_ffn_bwd(wts: MoEWeights, x, dy, saved, k: int, E: int):
                          dB_g=grads["dB_g"], dA_u=grads["dA_u"], dB_u=grads["dB_u"])
     dx = moe_combine_bwd(dxrows, saved["pos"], T, k)
     dlogits = moe_route_bwd(saved["ids"], saved["w"], dw_flat.view(T, k), E)
-    return dict(dx=dx, dlogits=dlogits, dw=dw_flat.view(T, k), **grads)
+    return dict(dx=dx, dlogits=dlogits, dw=dw_flat.view(T, k), dg=dg, du=du, **grads)

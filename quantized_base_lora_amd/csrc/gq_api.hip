@@ -49,6 +49,13 @@ int64_t block_bytes(int qtype) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Alignment check of one (non-NULL) array argument, naming it in the error.
+#define REQ_ALIGN(ptr, a, fn)                                                             \
+  do {                                                                                    \
+    if ((ptr) && !aligned((ptr), (a)))                                                    \
+      return fail(GQ_EINVAL, "%s: %s must be %d-byte aligned", (fn), #ptr, (int)(a));     \
+  } while (0)
+
 // Bump allocator over the caller's workspace (256-byte aligned pieces).
 // With base == nullptr it only measures.
 struct Ws {
@@ -74,14 +81,17 @@ int check_ws(void* ws, size_t have, size_t need) {
   return GQ_OK;
 }
 
-int check_proj(const gq_lora_linear* L, const char* name, bool grouped) {
+// out8: the layer's backward reads activation rows of n_out bf16 with
+// 16-byte loads (not the LM head: its vocabulary rows are only walked by
+// masked tiles and a padded gradient chunk)
+int check_proj(const gq_lora_linear* L, const char* name, bool grouped, bool out8 = true) {
   if (!L) return fail(GQ_EINVAL, "%s: NULL projection", name);
   if (block_bytes(L->qtype) < 0) return fail(GQ_EINVAL, "%s: unknown qtype %d", name, L->qtype);
   if (L->rank < 1 || L->rank > 16) return fail(GQ_EINVAL, "%s: rank %d not in [1, 16]", name, L->rank);
-  if (L->n_in < 64 || L->n_in % 64)
-    return fail(GQ_ENOTSUP, "%s: n_in %lld must be a positive multiple of 64", name,
+  if (L->n_in < 32 || L->n_in % 32)
+    return fail(GQ_ENOTSUP, "%s: n_in %lld must be a positive multiple of 32", name,
                 (long long)L->n_in);
-  if (L->n_out < 8 || L->n_out % 8)
+  if (L->n_out < 1 || (out8 && (L->n_out < 8 || L->n_out % 8)))
     return fail(GQ_ENOTSUP, "%s: n_out %lld must be a positive multiple of 8", name,
                 (long long)L->n_out);
   if (L->n_in > INT_MAX / 2 || L->n_out > INT_MAX / 2)
@@ -91,8 +101,9 @@ int check_proj(const gq_lora_linear* L, const char* name, bool grouped) {
   if (L->n_experts < 1 || L->n_experts > 1024)
     return fail(GQ_EINVAL, "%s: n_experts %d not in [1, 1024]", name, L->n_experts);
   if (!L->w_blocks || !L->A || !L->B) return fail(GQ_EINVAL, "%s: NULL weight or adapter", name);
-  if (!aligned(L->w_blocks, 4) || !aligned(L->A, 16) || !aligned(L->B, 16))
-    return fail(GQ_EINVAL, "%s: w_blocks must be 4-byte and A, B 16-byte aligned", name);
+  REQ_ALIGN(L->w_blocks, 4, name);
+  REQ_ALIGN(L->A, 16, name);
+  REQ_ALIGN(L->B, 16, name);
   return GQ_OK;
 }
 
@@ -201,8 +212,8 @@ int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int ou
     return fail(GQ_EINVAL, "gq_dequant: unknown out_dtype %d", out_dtype);
   if (rows == 0) return GQ_OK;
   if (!blocks || !out) return fail(GQ_EINVAL, "gq_dequant: NULL pointer");
-  if (!aligned(blocks, 2) || !aligned(out, 16))
-    return fail(GQ_EINVAL, "gq_dequant: blocks must be 2-byte and out 16-byte aligned");
+  REQ_ALIGN(blocks, 2, "gq_dequant");
+  REQ_ALIGN(out, 16, "gq_dequant");
   HIP_TRY(launch_dequant(qtype, blocks, rows, cols, out_dtype == GQ_BF16, out, S(stream)),
           "gq_dequant");
   return GQ_OK;
@@ -221,8 +232,9 @@ int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, ui
   if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_linear_lora_fwd: bad T %lld", (long long)T);
   if (T == 0) return GQ_OK;
   if (!x || !y || !xa) return fail(GQ_EINVAL, "gq_linear_lora_fwd: NULL x, y or xa");
-  if (!aligned(x, 16) || !aligned(y, 2) || !aligned(xa, 4))
-    return fail(GQ_EINVAL, "gq_linear_lora_fwd: x must be 16-byte aligned");
+  REQ_ALIGN(x, 16, "gq_linear_lora_fwd");
+  REQ_ALIGN(y, 2, "gq_linear_lora_fwd");
+  REQ_ALIGN(xa, 4, "gq_linear_lora_fwd");
   const hipStream_t st = S(stream);
   const int r = L->rank, K = (int)L->n_in, N = (int)L->n_out;
 
@@ -282,14 +294,20 @@ int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* 
   if (!dA || !dB) return fail(GQ_EINVAL, "gq_linear_lora_bwd: NULL dA or dB");
   const hipStream_t st = S(stream);
   const int r = L->rank, K = (int)L->n_in, N = (int)L->n_out;
+  REQ_ALIGN(dA, 4, "gq_linear_lora_bwd");
+  REQ_ALIGN(dB, 4, "gq_linear_lora_bwd");
   if (T == 0) {
     HIP_TRY(launch_fill_f32(dA, (int64_t)r * K, 0.f, st), "gq_linear_lora_bwd: zero dA");
     HIP_TRY(launch_fill_f32(dB, (int64_t)N * r, 0.f, st), "gq_linear_lora_bwd: zero dB");
     return GQ_OK;
   }
   if (!x || !xa || !dy) return fail(GQ_EINVAL, "gq_linear_lora_bwd: NULL x, xa or dy");
-  if (!aligned(x, 16) || !aligned(dy, 16) || (dx && !aligned(dx, 2)))
-    return fail(GQ_EINVAL, "gq_linear_lora_bwd: x and dy must be 16-byte aligned");
+  REQ_ALIGN(x, 16, "gq_linear_lora_bwd");
+  REQ_ALIGN(dy, 16, "gq_linear_lora_bwd");
+  REQ_ALIGN(dx, 2, "gq_linear_lora_bwd");
+  REQ_ALIGN(xa, 4, "gq_linear_lora_bwd");
+  REQ_ALIGN(dA, 4, "gq_linear_lora_bwd");
+  REQ_ALIGN(dB, 4, "gq_linear_lora_bwd");
   Ws meas(nullptr);
   plan_lin_bwd(meas, L, T);
   if ((rc = check_ws(ws, ws_bytes, meas.size()))) return rc;
@@ -414,11 +432,18 @@ int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* 
   if (T < 0 || T * k > INT_MAX) return fail(GQ_EINVAL, "gq_moe_route: bad T %lld", (long long)T);
   if (!offsets) return fail(GQ_EINVAL, "gq_moe_route: NULL offsets");
   const hipStream_t st = S(stream);
+  REQ_ALIGN(offsets, 4, "gq_moe_route");
   if (T == 0) {
     HIP_TRY(launch_fill_f32(reinterpret_cast<float*>(offsets), E + 1, 0.f, st), "gq_moe_route");
     return GQ_OK;
   }
   if (!logits || !ids || !w || !sorted || !pos) return fail(GQ_EINVAL, "gq_moe_route: NULL pointer");
+  REQ_ALIGN(logits, 4, "gq_moe_route");
+  REQ_ALIGN(ids, 4, "gq_moe_route");
+  REQ_ALIGN(w, 4, "gq_moe_route");
+  REQ_ALIGN(sorted, 4, "gq_moe_route");
+  REQ_ALIGN(offsets, 4, "gq_moe_route");
+  REQ_ALIGN(pos, 4, "gq_moe_route");
   int rc = check_ws(ws, ws_bytes, gq_moe_route_workspace_size(T, E, k));
   if (rc) return rc;
   HIP_TRY(launch_route(logits, T, E, k, ids, w, sorted, offsets, pos, ws, st), "gq_moe_route");
@@ -433,6 +458,10 @@ int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_
   if (T < 0) return fail(GQ_EINVAL, "gq_moe_route_bwd: bad T");
   if (T == 0) return GQ_OK;
   if (!ids || !w || !dw || !dlogits) return fail(GQ_EINVAL, "gq_moe_route_bwd: NULL pointer");
+  REQ_ALIGN(ids, 4, "gq_moe_route_bwd");
+  REQ_ALIGN(w, 4, "gq_moe_route_bwd");
+  REQ_ALIGN(dw, 4, "gq_moe_route_bwd");
+  REQ_ALIGN(dlogits, 4, "gq_moe_route_bwd");
   HIP_TRY(launch_route_bwd(ids, w, dw, T, E, k, dlogits, S(stream)), "gq_moe_route_bwd");
   return GQ_OK;
 }
@@ -444,8 +473,10 @@ int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, in
     return fail(GQ_EINVAL, "gq_moe_combine_fwd: bad T/k/H (H must be a multiple of 8)");
   if (T == 0) return GQ_OK;
   if (!o || !w || !pos || !y) return fail(GQ_EINVAL, "gq_moe_combine_fwd: NULL pointer");
-  if (!aligned(o, 16) || !aligned(y, 16))
-    return fail(GQ_EINVAL, "gq_moe_combine_fwd: o and y must be 16-byte aligned");
+  REQ_ALIGN(o, 16, "gq_moe_combine_fwd");
+  REQ_ALIGN(y, 16, "gq_moe_combine_fwd");
+  REQ_ALIGN(w, 4, "gq_moe_combine_fwd");
+  REQ_ALIGN(pos, 4, "gq_moe_combine_fwd");
   HIP_TRY(launch_combine(o, w, pos, T, k, H, y, S(stream)), "gq_moe_combine_fwd");
   return GQ_OK;
 }
@@ -462,6 +493,10 @@ int gq_adamw8bit_step(float* p, const float* g, uint8_t* m_codes, uint8_t* v_cod
   if (n == 0) return GQ_OK;
   if (!p || !g || !m_codes || !v_codes || !m_scale || !v_scale)
     return fail(GQ_EINVAL, "gq_adamw8bit_step: NULL pointer");
+  REQ_ALIGN(p, 4, "gq_adamw8bit_step");
+  REQ_ALIGN(g, 4, "gq_adamw8bit_step");
+  REQ_ALIGN(m_scale, 4, "gq_adamw8bit_step");
+  REQ_ALIGN(v_scale, 4, "gq_adamw8bit_step");
   HIP_TRY(launch_adamw8bit(p, g, m_codes, v_codes, m_scale, v_scale, n, step, lr, beta1, beta2, eps,
                            weight_decay, S(stream)),
           "gq_adamw8bit_step");
@@ -476,8 +511,10 @@ int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, floa
   if (!(eps >= 0.f)) return fail(GQ_EINVAL, "gq_rmsnorm_fwd: eps must be >= 0");
   if (T == 0) return GQ_OK;
   if (!x || !w || !y || !rstd) return fail(GQ_EINVAL, "gq_rmsnorm_fwd: NULL pointer");
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
-    return fail(GQ_EINVAL, "gq_rmsnorm_fwd: x, w and y must be 16-byte aligned");
+  REQ_ALIGN(x, 16, "gq_rmsnorm_fwd");
+  REQ_ALIGN(w, 16, "gq_rmsnorm_fwd");
+  REQ_ALIGN(y, 16, "gq_rmsnorm_fwd");
+  REQ_ALIGN(rstd, 4, "gq_rmsnorm_fwd");
   HIP_TRY(launch_rmsnorm_fwd(x, w, T, (int32_t)H, eps, y, rstd, S(stream)), "gq_rmsnorm_fwd");
   return GQ_OK;
 }
@@ -489,8 +526,11 @@ int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const 
     return fail(GQ_EINVAL, "gq_rmsnorm_bwd: bad T/H (H must be a positive multiple of 8)");
   if (T == 0) return GQ_OK;
   if (!dy || !x || !w || !rstd || !dx) return fail(GQ_EINVAL, "gq_rmsnorm_bwd: NULL pointer");
-  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16))
-    return fail(GQ_EINVAL, "gq_rmsnorm_bwd: dy, x, w and dx must be 16-byte aligned");
+  REQ_ALIGN(dy, 16, "gq_rmsnorm_bwd");
+  REQ_ALIGN(x, 16, "gq_rmsnorm_bwd");
+  REQ_ALIGN(w, 16, "gq_rmsnorm_bwd");
+  REQ_ALIGN(dx, 16, "gq_rmsnorm_bwd");
+  REQ_ALIGN(rstd, 4, "gq_rmsnorm_bwd");
   HIP_TRY(launch_rmsnorm_bwd(dy, x, w, rstd, T, (int32_t)H, dx, S(stream)), "gq_rmsnorm_bwd");
   return GQ_OK;
 }
@@ -502,8 +542,9 @@ int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, in
     return fail(GQ_EINVAL, "gq_moe_combine_bwd: bad T/k/H (H must be a multiple of 8)");
   if (T == 0) return GQ_OK;
   if (!dxrows || !pos || !dx) return fail(GQ_EINVAL, "gq_moe_combine_bwd: NULL pointer");
-  if (!aligned(dxrows, 16) || !aligned(dx, 16))
-    return fail(GQ_EINVAL, "gq_moe_combine_bwd: dxrows and dx must be 16-byte aligned");
+  REQ_ALIGN(dxrows, 16, "gq_moe_combine_bwd");
+  REQ_ALIGN(dx, 16, "gq_moe_combine_bwd");
+  REQ_ALIGN(pos, 4, "gq_moe_combine_bwd");
   HIP_TRY(launch_combine(dxrows, nullptr, pos, T, k, H, dx, S(stream)), "gq_moe_combine_bwd");
   return GQ_OK;
 }
@@ -552,7 +593,16 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
   if (epilogue == GQ_EPI_SWIGLU && (!a->save_g || !a->save_u))
     return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: SWIGLU needs save_g and save_u");
   if (a->gather_div < 1) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: gather_div < 1");
-  if (!aligned(a->in, 16)) return fail(GQ_EINVAL, "gq_grouped_mmq_lora_fwd: in must be 16-byte aligned");
+  {
+    const char* fn = "gq_grouped_mmq_lora_fwd";
+    REQ_ALIGN(a->in, 16, fn);
+    REQ_ALIGN(a->out, 2, fn);
+    REQ_ALIGN(a->save_g, 2, fn);
+    REQ_ALIGN(a->save_u, 2, fn);
+    REQ_ALIGN(a->xa, 4, fn);
+    REQ_ALIGN(a->gather, 4, fn);
+    REQ_ALIGN(a->offsets, 4, fn);
+  }
   if ((rc = check_ws(ws, ws_bytes, gq_grouped_mmq_lora_fwd_workspace_size(P, nproj, M)))) return rc;
   const hipStream_t st = S(stream);
   const int E = P->n_experts, r = P->rank, K = (int)P->n_in, N = (int)P->n_out;
@@ -681,6 +731,15 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   }
   const int E = P->n_experts, r = P->rank;
   const float s = P->scale;
+  {
+    const char* fn = "gq_grouped_mmq_lora_bwd";
+    REQ_ALIGN(a->dA_d, 4, fn);
+    REQ_ALIGN(a->dB_d, 4, fn);
+    REQ_ALIGN(a->dA_g, 4, fn);
+    REQ_ALIGN(a->dB_g, 4, fn);
+    REQ_ALIGN(a->dA_u, 4, fn);
+    REQ_ALIGN(a->dB_u, 4, fn);
+  }
   if (M == 0) {
     // no rows: every adapter gradient is exactly zero
     if (mode == GQ_BWD_DOWN_SWIGLU) {
@@ -701,6 +760,51 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   }
   if ((rc = check_ws(ws, ws_bytes, gq_grouped_mmq_lora_bwd_workspace_size(P, nproj, mode, M))))
     return rc;
+  // every argument check before the first launch
+  if (mode == GQ_BWD_DOWN_SWIGLU) {
+    if (!a->dy || !a->w_flat || !a->sorted || !a->g || !a->u || !a->h || !a->xa_d || !a->dw_flat ||
+        !a->dA_d || !a->dB_d || !a->dg || !a->du || !a->dgB || !a->duB)
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for DOWN_SWIGLU");
+    const char* fn = "gq_grouped_mmq_lora_bwd";
+    REQ_ALIGN(a->dy, 16, fn);
+    REQ_ALIGN(a->g, 16, fn);
+    REQ_ALIGN(a->u, 16, fn);
+    REQ_ALIGN(a->h, 16, fn);
+    REQ_ALIGN(a->dg, 16, fn);
+    REQ_ALIGN(a->du, 16, fn);
+    REQ_ALIGN(a->w_flat, 4, fn);
+    REQ_ALIGN(a->sorted, 4, fn);
+    REQ_ALIGN(a->xa_d, 4, fn);
+    REQ_ALIGN(a->dw_flat, 4, fn);
+    REQ_ALIGN(a->dA_d, 4, fn);
+    REQ_ALIGN(a->dB_d, 4, fn);
+    REQ_ALIGN(a->dgB, 4, fn);
+    REQ_ALIGN(a->duB, 4, fn);
+    REQ_ALIGN(a->gather, 4, fn);
+    REQ_ALIGN(a->offsets, 4, fn);
+  } else {
+    if (!a->x || !a->xa || !a->dg || !a->du || !a->dgB || !a->duB || !a->dxrows || !a->dA_g ||
+        !a->dB_g || !a->dA_u || !a->dB_u)
+      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for GATEUP");
+    {
+      const char* fn = "gq_grouped_mmq_lora_bwd";
+      REQ_ALIGN(a->x, 16, fn);
+      REQ_ALIGN(a->dg, 16, fn);
+      REQ_ALIGN(a->du, 16, fn);
+      REQ_ALIGN(a->dxrows, 2, fn);
+      REQ_ALIGN(a->xa, 4, fn);
+      REQ_ALIGN(a->dgB, 4, fn);
+      REQ_ALIGN(a->duB, 4, fn);
+      REQ_ALIGN(a->dA_g, 4, fn);
+      REQ_ALIGN(a->dB_g, 4, fn);
+      REQ_ALIGN(a->dA_u, 4, fn);
+      REQ_ALIGN(a->dB_u, 4, fn);
+      REQ_ALIGN(a->gather, 4, fn);
+      REQ_ALIGN(a->offsets, 4, fn);
+    }
+    if (P[0].n_out % GEMM_BK)
+      return fail(GQ_ENOTSUP, "gq_grouped_mmq_lora_bwd: intermediate size must be a multiple of 64");
+  }
   Ws w(ws);
   const GrpBwdWs W = plan_grp_bwd(w, P, mode, M);
   const int rcg = grp_rc(P, M);
@@ -728,12 +832,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
 
   if (mode == GQ_BWD_DOWN_SWIGLU) {
     const int H = (int)P[0].n_out, I = (int)P[0].n_in;
-    if (!a->dy || !a->w_flat || !a->sorted || !a->g || !a->u || !a->h || !a->xa_d || !a->dw_flat ||
-        !a->dA_d || !a->dB_d || !a->dg || !a->du || !a->dgB || !a->duB)
-      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for DOWN_SWIGLU");
-    if (!aligned(a->dy, 16) || !aligned(a->h, 16) || !aligned(a->g, 16) || !aligned(a->u, 16) ||
-        !aligned(a->dg, 16) || !aligned(a->du, 16))
-      return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: dy, g, u, h, dg, du must be 16-byte aligned");
     // dY Bd (unweighted) and its gate-weighted copy
     RowDotArgs rd;
     memset(&rd, 0, sizeof rd);
@@ -781,11 +879,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
 
   // GATEUP
   const int H = (int)P[0].n_in, I = (int)P[0].n_out;
-  if (!a->x || !a->xa || !a->dg || !a->du || !a->dgB || !a->duB || !a->dxrows || !a->dA_g ||
-      !a->dB_g || !a->dA_u || !a->dB_u)
-    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: NULL pointer for GATEUP");
-  if (!aligned(a->x, 16) || !aligned(a->dg, 16) || !aligned(a->du, 16))
-    return fail(GQ_EINVAL, "gq_grouped_mmq_lora_bwd: x, dg, du must be 16-byte aligned");
   GemmArgs g = gemm_defaults();
   g.M = M; g.N = H; g.K = 2 * I;
   g.a0 = a->dg; g.a1 = a->du; g.lda = I; g.asplit = I;
@@ -800,8 +893,6 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
   g.lA0 = P[0].A; g.lA1 = P[1].A; g.lA_estride = (int64_t)r * H;
   g.rv0 = a->dgB; g.rv1 = a->duB;
   g.o0 = a->dxrows; g.ldo = H;
-  if (I % GEMM_BK)
-    return fail(GQ_ENOTSUP, "gq_grouped_mmq_lora_bwd: intermediate size must be a multiple of 64");
   HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: gate/up MMQ");
 
   // dA_g and dA_u in one pass over the gathered x rows
@@ -892,7 +983,7 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
                          float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
                          size_t ws_bytes, void* stream) {
   g_err.clear();
-  int rc = check_proj(L, "gq_lmhead_chunked_ce", false);
+  int rc = check_proj(L, "gq_lmhead_chunked_ce", false, false);
   if (rc) return rc;
   if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: bad T");
   if (chunk < 1) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: chunk_rows must be >= 1");
@@ -902,6 +993,9 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   const hipStream_t st = S(stream);
   const int64_t V = L->n_out;
   const int H = (int)L->n_in, r = L->rank;
+  REQ_ALIGN(loss, 4, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(dA, 4, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(dB, 4, "gq_lmhead_chunked_ce");
   if (T == 0) {
     HIP_TRY(launch_fill_f32(loss, 1, 0.f, st), "gq_lmhead_chunked_ce");
     if (grad) {
@@ -911,8 +1005,13 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
     return GQ_OK;
   }
   if (!h || !labels || !lse) return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: NULL h, labels or lse");
-  if (!aligned(h, 16) || (grad && !aligned(dh, 2)))
-    return fail(GQ_EINVAL, "gq_lmhead_chunked_ce: h must be 16-byte aligned");
+  REQ_ALIGN(h, 16, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(dh, 2, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(labels, 8, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(loss, 4, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(lse, 4, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(dA, 4, "gq_lmhead_chunked_ce");
+  REQ_ALIGN(dB, 4, "gq_lmhead_chunked_ce");
   if (chunk > V) chunk = V;
   if (chunk > INT_MAX / 2) return fail(GQ_ENOTSUP, "gq_lmhead_chunked_ce: chunk too large");
   Ws meas(nullptr);

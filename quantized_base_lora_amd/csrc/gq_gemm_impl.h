@@ -454,7 +454,9 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         } else {
           // unconditional load (block 0 of w0 when out of range), zeroed at
           // the store; branch-free address selection keeps the loop one block
-          const bool ok = wrow_ok[i] && (NN ? kt * BK + w_it_row[i] < p.K : kt < nk);
+          // NT: block 2kt + kb of the row must exist (a reduction of an odd
+          // number of blocks ends in a half k-step)
+          const bool ok = wrow_ok[i] && (NN ? kt * BK + w_it_row[i] < p.K : 2 * kt + w_it_kb[i] < p.w_nb);
           load_block<QT>(ok ? wptr[i] + koff : p.w0, wr[i]);
           wmsk[i] = opaque_mask(ok);
         }

@@ -70,7 +70,7 @@ def test_linear_validation(gq):
     L = proj(gq, rank=17)
     assert f(C.byref(L), FAKE, 8, FAKE, FAKE, None, 0, None) == gq.GQ_EINVAL
     assert "rank" in gq.last_error()
-    L = proj(gq, n_in=96)
+    L = proj(gq, n_in=80)
     assert f(C.byref(L), FAKE, 8, FAKE, FAKE, None, 0, None) == gq.GQ_ENOTSUP
     L = proj(gq, n_out=60)
     assert f(C.byref(L), FAKE, 8, FAKE, FAKE, None, 0, None) == gq.GQ_ENOTSUP
@@ -194,3 +194,108 @@ def test_noalloc_rejects_oversized_shapes_on_the_host(gq):
     assert rc == gq.GQ_EWORKSPACE and "scratch" in gq.last_error()
     assert lib.gq_linear_lora_bwd_noalloc(C.byref(proj(gq, rank=17)), FAKE, FAKE, FAKE, 8, FAKE, FAKE,
                                           FAKE, None) == gq.GQ_EINVAL
+
+
+def _bad(a):
+    """An address aligned to a/2 but not to a."""
+    return FAKE + a // 2
+
+
+def test_each_pointer_alignment_is_checked_and_named(gq):
+    """One misaligned argument at a time: GQ_EINVAL before any HIP call, with
+    the argument's name in the message."""
+    lib = gq.lib()
+    L = proj(gq)
+    big = 1 << 30
+
+    def expect(call, argname):
+        assert call() == gq.GQ_EINVAL, argname
+        assert argname in gq.last_error() and "aligned" in gq.last_error(), gq.last_error()
+
+    # dequant: blocks, out
+    for i, (nm, a) in enumerate((("blocks", 2), ("out", 16))):
+        args = [FAKE, FAKE]
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_dequant(0, args[0], 4, 64, 0, args[1], None), nm)
+    # linear forward: x, y, xa
+    for i, (nm, a) in enumerate((("x", 16), ("y", 2), ("xa", 4))):
+        args = [FAKE] * 3
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_linear_lora_fwd(C.byref(L), args[0], 8, args[1], args[2], None, 0, None), nm)
+    # linear backward: x, xa, dy, dx, dA, dB
+    for i, (nm, a) in enumerate((("x", 16), ("xa", 4), ("dy", 16), ("dx", 2), ("dA", 4), ("dB", 4))):
+        args = [FAKE] * 6
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_linear_lora_bwd(C.byref(L), args[0], args[1], args[2], 8, args[3], args[4],
+                                              args[5], FAKE, big, None), nm)
+    # projection pointers
+    for fld, a in (("w_blocks", 4), ("A", 16), ("B", 16)):
+        Lb = proj(gq, **{fld: _bad(a)})
+        expect(lambda: lib.gq_linear_lora_fwd(C.byref(Lb), FAKE, 8, FAKE, FAKE, None, 0, None), fld)
+    # routing
+    for i, nm in enumerate(("logits", "ids", "w", "sorted", "offsets", "pos")):
+        args = [FAKE] * 6
+        args[i] = _bad(4)
+        expect(lambda: lib.gq_moe_route(args[0], 16, 8, 2, args[1], args[2], args[3], args[4], args[5], FAKE,
+                                        big, None), nm)
+    for i, nm in enumerate(("ids", "w", "dw", "dlogits")):
+        args = [FAKE] * 4
+        args[i] = _bad(4)
+        expect(lambda: lib.gq_moe_route_bwd(args[0], args[1], args[2], 16, 8, 2, args[3], None), nm)
+    # combines
+    for i, (nm, a) in enumerate((("o", 16), ("w", 4), ("pos", 4), ("y", 16))):
+        args = [FAKE] * 4
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_moe_combine_fwd(args[0], args[1], args[2], 16, 2, 64, args[3], None), nm)
+    for i, (nm, a) in enumerate((("dxrows", 16), ("pos", 4), ("dx", 16))):
+        args = [FAKE] * 3
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_moe_combine_bwd(args[0], args[1], 16, 2, 64, args[2], None), nm)
+    # RMS normalisation
+    for i, (nm, a) in enumerate((("x", 16), ("w", 16), ("y", 16), ("rstd", 4))):
+        args = [FAKE] * 4
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_rmsnorm_fwd(args[0], args[1], 4, 64, 1e-6, args[2], args[3], None), nm)
+    for i, (nm, a) in enumerate((("dy", 16), ("x", 16), ("w", 16), ("rstd", 4), ("dx", 16))):
+        args = [FAKE] * 5
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_rmsnorm_bwd(args[0], args[1], args[2], args[3], 4, 64, args[4], None), nm)
+    # AdamW
+    for i, nm in ((0, "p"), (1, "g"), (4, "m_scale"), (5, "v_scale")):
+        args = [FAKE] * 6
+        args[i] = _bad(4)
+        expect(lambda: lib.gq_adamw8bit_step(*args, 100, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None), nm)
+    # LM head
+    for i, (nm, a) in enumerate((("h", 16), ("labels", 8), ("loss", 4), ("lse", 4), ("dh", 2), ("dA", 4),
+                                 ("dB", 4))):
+        args = [FAKE] * 7
+        args[i] = _bad(a)
+        expect(lambda: lib.gq_lmhead_chunked_ce(C.byref(proj(gq, n_out=1024)), args[0], args[1], 8, 256, -100,
+                                                1.0, args[2], args[3], args[4], args[5], args[6], FAKE, big,
+                                                None), nm)
+    # grouped forward
+    P2 = (gq.LoraLinear * 2)(proj(gq, n_experts=4), proj(gq, n_experts=4))
+    fields = (("in", "inp", 16), ("out", "out", 2), ("save_g", "save_g", 2), ("save_u", "save_u", 2),
+              ("xa", "xa", 4), ("gather", "gather", 4), ("offsets", "offsets", 4))
+    for nm, fld, a in fields:
+        ga = gq.GroupedFwdArgs(FAKE, FAKE, 2, FAKE, 64, FAKE, FAKE, FAKE, FAKE)
+        setattr(ga, fld, _bad(a))
+        expect(lambda: lib.gq_grouped_mmq_lora_fwd(P2, 2, 1, C.byref(ga), FAKE, big, None), nm)
+    # grouped backward, both modes
+    P3 = (gq.LoraLinear * 3)(proj(gq, n_experts=4, n_out=128, n_in=64),
+                             proj(gq, n_experts=4, n_out=64, n_in=128),
+                             proj(gq, n_experts=4, n_out=64, n_in=128))
+    down = (("dy", 16), ("g", 16), ("u", 16), ("h", 16), ("dg", 16), ("du", 16), ("w_flat", 4), ("sorted", 4),
+            ("xa_d", 4), ("dw_flat", 4), ("dA_d", 4), ("dB_d", 4), ("dgB", 4), ("duB", 4), ("gather", 4))
+    gu = (("x", 16), ("dg", 16), ("du", 16), ("dxrows", 2), ("xa", 4), ("dgB", 4), ("duB", 4), ("dA_g", 4),
+          ("dB_g", 4), ("dA_u", 4), ("dB_u", 4), ("gather", 4))
+    for mode, projs, n, table in ((0, P3, 3, down), (1, (gq.LoraLinear * 2)(P3[1], P3[2]), 2, gu)):
+        for nm, a in table:
+            b = gq.GroupedBwdArgs()
+            for f, _ in gq.GroupedBwdArgs._fields_:
+                if f not in ("M", "gather_div"):
+                    setattr(b, f, FAKE)
+            b.M = 64
+            b.gather_div = 1
+            setattr(b, nm, _bad(a))
+            expect(lambda: lib.gq_grouped_mmq_lora_bwd(projs, n, mode, C.byref(b), FAKE, big, None), nm)

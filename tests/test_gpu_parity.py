@@ -25,8 +25,8 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import quantized_base_lora_amd as gq  # noqa: E402
-from gpu_helpers import (bf16_dev, check, f32_dev, host, i32_dev, i64_dev, same_f32_bits,  # noqa: E402
-                         u8_dev)
+from gpu_helpers import (bf16_dev, check, check_per_expert, f32_dev, host, i32_dev, i64_dev,  # noqa: E402
+                         same_f32_bits, u8_dev)
 
 
 def say(*a):
@@ -76,6 +76,10 @@ LIN_CASES = [
     # T <= 64, K % 256 == 0: the skinny forward MMQ with 16-, 32- and 64-row
     # tiles, ragged last column tile
     (9, 256, 200, 0, 4), (20, 512, 264, 1, 8), (33, 256, 136, 2, 4), (64, 512, 128, 1, 16),
+    # an odd number of blocks per weight row (n_in % 64 == 32): the reduction
+    # ends in a half k-step, rows start 2-byte aligned
+    (19, 32, 40, 1, 4), (70, 96, 136, 0, 8), (130, 160, 64, 2, 4), (300, 160, 200, 1, 16),
+    (257, 96, 264, 0, 2),
 ]
 
 
@@ -128,6 +132,38 @@ def test_linear_one_hot_rows_bit_exact():
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
     for t, c in enumerate(cols):
         assert np.array_equal(got[t], synth.f32_to_bf16_bits(W[:, c]))
+
+
+@pytest.mark.parametrize("qtype", [0, 1, 2])
+def test_linear_nonfinite_scales(qtype):
+    """Blocks with an infinite or NaN scale: inside the MMQ the outputs they
+    feed are non-finite exactly where the oracle's are (the fused decode may
+    give NaN where d*q is +-inf, so only finiteness is compared there); every
+    other output meets the usual bar."""
+    cfg = synth.LinearCfg("nf", T=40, K=128, N=64, qtype=qtype, rank=4, alpha=8)
+    inp = synth.make_linear(cfg, large_adapter=True)
+    bs = synth.BLOCK_BYTES[qtype]
+    v = inp["blocks"].reshape(cfg.N, cfg.K // 32, bs)
+    v[5, 1, 0:2] = [0x00, 0x7C]   # +inf
+    v[20, 0, 0:2] = [0x00, 0xFC]  # -inf
+    v[33, 3, 0:2] = [0x00, 0x7E]  # NaN
+    say("linear non-finite scales", qtype)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = ol.run(inp)
+    p = lin_proj(inp)
+    x, dy = bf16_dev(inp["x"]), bf16_dev(inp["dy"])
+    y, xa = gq.linear_lora_fwd(p, x)
+    dx, dA, dB = gq.linear_lora_bwd(p, x, xa, dy)
+    torch.cuda.synchronize()
+    for n, got in (("y", y), ("dx", dx)):
+        g = host(got)
+        fin = np.isfinite(ref[n])
+        assert (~fin).any(), n
+        assert np.array_equal(np.isfinite(g), fin), f"{n}: non-finite pattern differs"
+        e = np.linalg.norm(g[fin] - ref[n][fin]) / np.linalg.norm(ref[n][fin])
+        assert e <= 1e-2, (n, e)
+    check("dA", host(dA), ref["dA"])
+    check("dB", host(dB), ref["dB"])
 
 
 def test_linear_deterministic():
@@ -211,6 +247,9 @@ MOE_CASES = [
     (24, 256, 256, 8, 2, 1, 4, 1.0),
     (20, 512, 512, 16, 2, 0, 8, 0.0),
     (16, 256, 768, 8, 4, 2, 16, 1.0),
+    # hidden size with an odd number of blocks (H % 64 == 32)
+    (60, 96, 64, 4, 2, 1, 4, 0.0),
+    (150, 160, 128, 8, 2, 0, 8, 1.0),
 ]
 
 
@@ -236,13 +275,16 @@ def test_moe_layer(T, H, I, E, k, qtype, r, zipf):
     check("o", host(saved["o"]), f["o"])
     check("y", host(y), f["y"])
     check("dw", host(g["dw"]), b["dw"])
+    check("dg", host(g["dg"]), b["dg"])
+    check("du", host(g["du"]), b["du"])
     check("dx", host(g["dx"]), b["dx"])
     check("dlogits", host(g["dlogits"]), b["dlogits"])
+    idle = np.diff(f["offsets"]) == 0
     for n in ("dA_d", "dB_d", "dA_g", "dB_g", "dA_u", "dB_u"):
         ref = b[n.replace("_", "")]
         got = host(g[n])
         check(n, got, ref)
-        idle = np.diff(f["offsets"]) == 0
+        check_per_expert(n, got, ref, np.diff(f["offsets"]))  # every active expert on its own, exact zeros for idle ones
         assert np.all(got[idle] == 0.0), f"{n}: idle experts must get exact zeros"
 
 
@@ -259,6 +301,11 @@ HEAD_CASES = [
     (7, 256, 712, 712, 2, 0.2),
     # more than 64 tokens and 256 vocabulary tiles: the multi-block merge
     (100, 256, 40000, 16384, 0, 0.1),
+    # hidden size with an odd number of blocks; vocabulary sizes that are not
+    # a multiple of 8 (tile and skinny logits passes)
+    (40, 96, 701, 256, 1, 0.1),
+    (150, 160, 2000, 512, 0, 0.0),
+    (16, 256, 1001, 333, 2, 0.1),
 ]
 
 
@@ -280,6 +327,28 @@ def test_lmhead(T, H, V, chunk, qtype, ign):
     check("dB", host(out["dB"]), ref["dB"])
     ign_rows = inp["labels"] == -100
     assert np.all(host(out["dh"])[ign_rows] == 0.0)
+    assert int(out["ws"][:4].view(torch.int32).item()) == 0
+    # every row of G sums to 0, so the columns of dB = s G^T xa sum to 0
+    # (the reference is 0 in exact arithmetic: compare against the size of dB)
+    dB = host(out["dB"]).astype(np.float64)
+    assert np.all(np.abs(dB.sum(axis=0)) <= 1e-3 * np.abs(dB).sum(axis=0) + 1e-30)
+
+
+def test_lmhead_all_labels_ignored():
+    """No valid label: loss 0 and every gradient exactly 0, lse still the
+    log-sum-exp of the logits."""
+    cfg = synth.HeadCfg("t", T=40, H=128, V=900, qtype=1, rank=4, alpha=8, chunk=256)
+    inp = synth.make_head(cfg, large_adapter=True)
+    inp["labels"][:] = -100
+    ref = olm.forward_backward(inp, chunk=256)
+    head = gq.Proj(1, 900, 128, u8_dev(inp["blocks"]), f32_dev(inp["A"]), f32_dev(inp["B"]),
+                   float(inp["scale"]))
+    out = gq.lmhead_chunked_ce(head, bf16_dev(inp["h"]), i64_dev(inp["labels"]), chunk_rows=256)
+    torch.cuda.synchronize()
+    assert float(out["loss"]) == 0.0 and ref["loss"] == 0.0
+    check("lse", host(out["lse"]), ref["lse"], 1e-4)
+    for n in ("dh", "dA", "dB"):
+        assert np.all(host(out[n]) == 0.0), n
     assert int(out["ws"][:4].view(torch.int32).item()) == 0
 
 
@@ -456,3 +525,27 @@ def test_adamw8bit_kernel_regression(n, steps, wd):
     assert np.array_equal(st.m_scale.cpu().numpy().view(np.uint32), sm.view(np.uint32))
     assert np.array_equal(st.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
     assert np.array_equal(p.cpu().numpy().view(np.uint32), ph.view(np.uint32))
+
+
+# ------------------------------------------------------------ binding checks
+def test_binding_rejects_mismatched_tensors_before_launch():
+    inp = synth.make_linear(synth.LinearCfg("chk", T=8, K=128, N=64, qtype=synth.Q4_0, rank=4, alpha=8))
+    p = lin_proj(inp)
+    x = bf16_dev(inp["x"])
+    with pytest.raises(TypeError, match="dtype"):
+        gq.linear_lora_fwd(p, x.float())
+    with pytest.raises(ValueError, match="shape"):
+        gq.linear_lora_fwd(p, x[:, :64].contiguous())
+    with pytest.raises(ValueError, match="contiguous"):
+        gq.linear_lora_fwd(p, torch.cat([x, x], 1)[:, ::2])
+    y, xa = gq.linear_lora_fwd(p, x)
+    dy = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="xa"):
+        gq.linear_lora_bwd(p, x, xa[:4].contiguous(), dy)
+    with pytest.raises(ValueError, match="dy"):
+        gq.linear_lora_bwd(p, x, xa, dy[:, :32].contiguous())
+    short = gq.Proj(p.qtype, p.n_out, p.n_in, p.blocks[:-18], p.A, p.B, p.scale)
+    with pytest.raises(ValueError, match="blocks"):
+        gq.linear_lora_fwd(short, x)
+    with pytest.raises(TypeError, match="labels"):
+        gq.lmhead_chunked_ce(p, x, torch.zeros(8, dtype=torch.int32, device="cuda"))
