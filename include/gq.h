@@ -68,7 +68,9 @@ extern "C" {
 #define GQ_ENOTSUP (-2)    /* valid but unsupported shape or type */
 #define GQ_EWORKSPACE (-3) /* workspace missing or smaller than required */
 #define GQ_EHIP (-4)       /* a HIP launch or runtime call failed */
-#define GQ_EDEVICE (-5)    /* reserved: device-detected data error */
+#define GQ_EDEVICE (-5)    /* device-detected data error: reported through the
+                              workspace's first 32-bit word (labels outside
+                              [0, V); inconsistent expert offsets) */
 
 /* quant types */
 #define GQ_Q8_0 0
@@ -210,7 +212,9 @@ int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* 
 
 /* Router backward (no load-balancing term): dlogits [T][E] fp32 (overwritten),
  * dlogits[t][ids[t][j]] = w[t][j] (dw[t][j] - sum_i w[t][i] dw[t][i]), else 0.
- * dw [T][k] fp32. */
+ * dw [T][k] fp32.  An id outside [0, E) matches no column: its term is
+ * dropped and nothing is written outside dlogits (there is no workspace to
+ * report it in; gq_moe_route never produces such ids). */
 int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
                      int32_t k, float* dlogits, void* stream);
 
@@ -236,6 +240,12 @@ int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, in
  *                 g, u as above; out[p] = silu(g) * u;
  *                 save_g[p] = g, save_u[p] = u (bf16); xa = [2][M][rank].
  * Only experts that own rows read their blocks.
+ * The offsets are checked on the device (offsets[0] == 0, non-decreasing,
+ * offsets[E] == M; expert ids outside [0, E) in the routing that produced
+ * them break this): invalid offsets set the workspace's first 32-bit word
+ * to nonzero (GQ_EDEVICE condition, readable after synchronising) and no
+ * row is processed, so the outputs are left unspecified but nothing is read
+ * or written out of bounds; valid offsets set it to 0.
  */
 typedef struct gq_grouped_fwd_args {
     const uint16_t* in;      /* activations [*][n_in] bf16 */
@@ -273,6 +283,9 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
  *   dA_g[e] = s sum_p dgB[p]^T x_p,  dB_g[e] = s sum_p dg[p]^T xa_g[p]; same for up.
  *   Inputs: x (activation rows via gather), dg, du, dgB, duB, xa (= [2][M][rank]).
  * Adapter gradients of experts without rows are written as exact zeros.
+ * Offsets are checked on the device as in the forward (the workspace's
+ * first 32-bit word: 0 valid, nonzero invalid; with invalid offsets the
+ * adapter gradients are zero and the row outputs unspecified).
  * All bf16 row arrays (dy, x, g, u, h, dg, du, dxrows) must be 16-byte
  * aligned (GQ_EINVAL otherwise).
  */

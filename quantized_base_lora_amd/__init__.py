@@ -418,7 +418,9 @@ def _check_group(projs, offsets, M: int, gather):
     _same_device(offsets, gather, *[p.blocks for p in projs])
 
 
-def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, offsets, M: int):
+def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, offsets, M: int, ws=None):
+    """Grouped forward; `ws` (uint8, optional) is the workspace to use, whose
+    first 32-bit word reports inconsistent offsets after synchronising."""
     _check_group(projs, offsets, M, gather)
     _expect(inp, "inp", torch.bfloat16, (None, projs[0].n_in), min_rows=None if gather is not None else M)
     dev = inp.device
@@ -432,7 +434,10 @@ def grouped_mmq_lora_fwd(projs, epilogue: int, inp, gather, gather_div: int, off
     xa = torch.empty((len(projs), M, r), dtype=torch.float32, device=dev)
     arr = _projs(projs)
     nbytes = lib().gq_grouped_mmq_lora_fwd_workspace_size(arr, len(projs), M)
-    ws = _workspace(nbytes, dev)
+    if ws is None or ws.numel() < nbytes:
+        ws = _workspace(nbytes, dev)
+    else:
+        _expect(ws, "ws", torch.uint8, None)
     a = GroupedFwdArgs(_ptr(inp), _ptr(gather), gather_div, _ptr(offsets), M, _ptr(out), _ptr(g),
                        _ptr(u), _ptr(xa))
     _check(lib().gq_grouped_mmq_lora_fwd(arr, len(projs), epilogue, C.byref(a), _ptr(ws), nbytes,

@@ -568,6 +568,7 @@ int64_t grouped_mtiles(int64_t M, int E, int bm) { return cdiv(M, bm) + E; }
 size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t, int64_t) {
   if (!P) return 0;
   Ws w(nullptr);
+  w.take<int32_t>(64);                // device error word (first 4 bytes)
   w.take<int32_t>(P->n_experts + 1);  // GEMM tiles
   w.take<int32_t>(P->n_experts + 1);  // 16-row tiles of the row dots
   return w.size();
@@ -607,13 +608,14 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
   const hipStream_t st = S(stream);
   const int E = P->n_experts, r = P->rank, K = (int)P->n_in, N = (int)P->n_out;
   Ws w(ws);
+  int32_t* err = w.take<int32_t>(64);
   int32_t* ts = w.take<int32_t>(E + 1);
   int32_t* ts16 = w.take<int32_t>(E + 1);
   const int ncols = epilogue == GQ_EPI_SWIGLU ? 2 * N : N;  // GEMM columns
   const bool w_al = aligned(P[0].w_blocks, 16) && (nproj < 2 || aligned(P[1].w_blocks, 16));
   const int tc = cdiv(M, E) <= 64 ? pick_fwd_tile(cdiv(M, E), M, cdiv(ncols, TILE_BN), K, w_al)
                                    : pick_grp_tile(M, E, cdiv(ncols, TILE_BN));
-  HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), ts, 16, ts16, 1, nullptr, st),
+  HIP_TRY(launch_tile_starts(a->offsets, E, M, err, tile_bm(tc), ts, 16, ts16, 1, nullptr, st),
           "gq_grouped_mmq_lora_fwd: tiles");
 
   RowDotArgs rd;
@@ -656,6 +658,7 @@ int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epil
 
 namespace {
 struct GrpBwdWs {
+  int32_t* err;
   int32_t* ts;
   int32_t* cs;
   int32_t* ts16;
@@ -673,6 +676,7 @@ GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
   GrpBwdWs p;
   memset(&p, 0, sizeof p);
   const int E = P->n_experts, r = P->rank;
+  p.err = w.take<int32_t>(64);  // device error word (first 4 bytes)
   p.ts = w.take<int32_t>(E + 1);
   p.cs = w.take<int32_t>(E + 1);
   p.ts16 = w.take<int32_t>(E + 1);
@@ -821,7 +825,7 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
     const int tn = pick_nn_tile(cdiv(M, E), M, ntiles_bwd, P[0].n_in, true, 0);
     if (tile_skinny(tn)) tc = tn;
   }
-  HIP_TRY(launch_tile_starts(a->offsets, E, tile_bm(tc), W.ts, rcg, W.cs, 16,
+  HIP_TRY(launch_tile_starts(a->offsets, E, M, W.err, tile_bm(tc), W.ts, rcg, W.cs, 16,
                              mode == GQ_BWD_DOWN_SWIGLU ? W.ts16 : nullptr, st),
           "gq_grouped_mmq_lora_bwd: tiles");
 

@@ -121,13 +121,13 @@ void set_profile_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols,
                           int out_bf16, void* out, hipStream_t st);
 
-// tile_start[e] = sum_{e' < e} ceil(cnt(e') / bm); E + 1 entries
-hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tile_start,
-                             hipStream_t st);
-// up to three prefixes in one launch (ts1 / ts2 nullable)
-hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int32_t bm0, int32_t* ts0,
-                              int32_t bm1, int32_t* ts1, int32_t bm2, int32_t* ts2,
-                              hipStream_t st);
+// Up to three tile prefixes in one launch (ts1 / ts2 nullable):
+// ts_q[e] = sum_{e' < e} ceil(cnt(e') / bm_q), E + 1 entries.  The offsets
+// are checked (offsets[0] == 0, non-decreasing, offsets[E] == M): invalid
+// ones set *err (nullable) to 1 and every prefix to zero, valid ones *err = 0.
+hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int64_t M, int32_t* err,
+                              int32_t bm0, int32_t* ts0, int32_t bm1, int32_t* ts1, int32_t bm2,
+                              int32_t* ts2, hipStream_t st);
 
 // out[p][j] = sum_c act(p)[c] * W(e)[j][c]   (W [r][C] if w_jstride == C, or
 // [C][r] if w_jstride == 1, w_cstride == r); act rows via gather; e via offsets.
@@ -161,7 +161,7 @@ hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st);
 // Partial outer-product reductions over row chunks:
 //   part[slot][c][j] = sum_{rows p of slot} U(p)[c] * Vv[p][j]
 // slots: chunks of `rc` rows within each expert (chunk_start from
-// launch_tile_start with bm = rc).  U rows via gather.
+// launch_tile_starts with bm = rc).  U rows via gather.
 struct ColRedArgs {
   int64_t M;
   int32_t C;

@@ -62,14 +62,25 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ blocks, int64_t nbloc
 // Exclusive prefix over experts of ceil(rows_e / bm[q]) for up to three tile
 // or chunk heights at once (one launch instead of one per height):
 // ts_q[e] = first tile of expert e, ts_q[E] = number of tiles.
+// The offsets are checked on the way: offsets[0] == 0, non-decreasing,
+// offsets[E] == M.  Invalid offsets (e.g. from expert ids outside [0, E))
+// set *err to 1 and make every prefix zero, so the launches that follow
+// process no rows (nothing is read or written out of bounds); valid ones
+// set *err to 0.
 __global__ __launch_bounds__(1024) void tile_start_kernel(const int32_t* __restrict__ offsets,
-                                                          int32_t E, int3 bm, int32_t* ts0,
-                                                          int32_t* ts1, int32_t* ts2) {
+                                                          int32_t E, int64_t M, int3 bm, int32_t* ts0,
+                                                          int32_t* ts1, int32_t* ts2,
+                                                          int32_t* __restrict__ err) {
   __shared__ int32_t sh[3][1024];
   const int t = threadIdx.x;
   const int bms[3] = {bm.x, bm.y, bm.z};
   int32_t* outs[3] = {ts0, ts1, ts2};
-  const int cnt = t < E ? offsets[t + 1] - offsets[t] : 0;
+  int cnt = t < E ? offsets[t + 1] - offsets[t] : 0;
+  bool bad_t = cnt < 0;
+  if (t == 0) bad_t = bad_t || offsets[0] != 0 || (int64_t)offsets[E] != M;
+  const bool bad = __syncthreads_or(bad_t) != 0;
+  if (bad) cnt = 0;
+  if (t == 0 && err) *err = bad ? 1 : 0;
 #pragma unroll
   for (int q = 0; q < 3; ++q) sh[q][t] = (t < E && outs[q]) ? (cnt + bms[q] - 1) / bms[q] : 0;
   __syncthreads();
@@ -892,16 +903,11 @@ hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t c
   return hipGetLastError();
 }
 
-hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t bm, int32_t* ts,
-                             hipStream_t st) {
-  return launch_tile_starts(offsets, E, bm, ts, 1, nullptr, 1, nullptr, st);
-}
-
-hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int32_t bm0, int32_t* ts0,
-                              int32_t bm1, int32_t* ts1, int32_t bm2, int32_t* ts2,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E,
-                     make_int3(bm0, bm1, bm2), ts0, ts1, ts2);
+hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int64_t M, int32_t* err,
+                              int32_t bm0, int32_t* ts0, int32_t bm1, int32_t* ts1, int32_t bm2,
+                              int32_t* ts2, hipStream_t st) {
+  hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E, M,
+                     make_int3(bm0, bm1, bm2), ts0, ts1, ts2, err);
   return hipGetLastError();
 }
 

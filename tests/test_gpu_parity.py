@@ -288,6 +288,27 @@ def test_moe_layer(T, H, I, E, k, qtype, r, zipf):
         assert np.all(got[idle] == 0.0), f"{n}: idle experts must get exact zeros"
 
 
+def test_grouped_offsets_checked_on_device():
+    """Inconsistent expert offsets (decreasing, not ending at M) set the
+    workspace's error word and no row is processed; consistent offsets on
+    the same workspace clear it."""
+    cfg = synth.MoECfg("t", T=32, H=128, I=64, E=4, k=2, qtype=1, rank=4, alpha=8)
+    inp = synth.make_moe(cfg)
+    wts = moe_weights(inp)
+    x = bf16_dev(inp["x"])
+    M = cfg.T * cfg.k
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    gather = torch.arange(M, dtype=torch.int32, device="cuda")
+    for offs, bad in (([0, 30, 20, 50, M], True), ([0, 10, 20, 30, M - 4], True), ([4, 10, 20, 30, M], True),
+                      ([0, 10, 20, 30, M], False)):
+        say("offsets", offs)
+        gq.grouped_mmq_lora_fwd([wts.gate, wts.up], gq.EPI_SWIGLU, x, gather, cfg.k,
+                                i32_dev(np.array(offs)), M, ws=ws)
+        torch.cuda.synchronize()
+        word = int(ws[:4].view(torch.int32).item())
+        assert (word != 0) == bad, (offs, word)
+
+
 # ----------------------------------------------------------------- LM head
 HEAD_CASES = [
     # T, H, V, chunk, qtype, ignore_frac
