@@ -10,7 +10,15 @@ intermediate 768, rank 4) train tokens/s, the roofline of the dominant MMQ
 kernel (timed with HIP events around each launch inside the timed region) and
 the fp64 oracle timed on the host cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+The default run also times every other workload on its own line entry:
+the Q8_0 linear layer (T 128), the 2-bit Zipf MoE layer (T 4096, 256
+experts), the LM head with chunked cross entropy (T 2048, V 151936), the
+small-token sweep (grouped layer T 16-512, LM-head forward T 16-128),
+RMSNorm and the 8-bit AdamW step, each against its roofline.  Every GPU
+time is the median of 5 repeats of K back-to-back steps (spread reported).
+--quick keeps only the headline linear step and the Q4_0 MoE layer.
 
 HBM traffic of the two MMQ launches: run the step under two rocprofv3
 counter passes with a plain device copy of known size in the same process,
@@ -201,6 +209,106 @@ def write_traffic(fetch_csv, write_csv, cmdline):
     log(json.dumps(out))
 
 
+def write_counters(sq_csv, fetch_csv, write_csv, out_md, title, cmdline):
+    """Per-kernel counter summary of one run of the bench under three
+    rocprofv3 --pmc passes (SQ counters + GRBM_GUI_ACTIVE, FETCH_SIZE,
+    WRITE_SIZE): MFMA busy (the MfmaUtil formula: MFMA-busy cycles of all
+    SIMDs over GUI-active cycles x SIMD count), VALU and LDS instructions per
+    MFMA, LDS bank-conflict cycles per CU cycle, HBM bytes (each counter
+    scaled by what it reads for the plain device copy of known size in the
+    same run).  Also merges the MMQ kernels into profiles/mmq_counters.json
+    under the current kernel source hash."""
+    import csv
+    import re
+    import statistics
+
+    def short(n):
+        n = n.replace("void ", "").replace("gq::(anonymous namespace)::", "").replace("gq::", "")
+        return re.sub(r"\(.*", "", n)
+
+    SIMDS, CUS, XCDS = 1024, 256, 8
+    rows = {}
+    for path in (sq_csv, fetch_csv, write_csv):
+        for r in csv.DictReader(open(path)):
+            key = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            ent = rows.setdefault(key, {})
+            ent.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                ent.setdefault("_dur", []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    scale = {}
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v for (n, g), e in rows.items() if "copy" in n.lower() for v in e.get(cn, [])
+                if v * 1024 > 0.5 * COPY_BYTES]
+        if not copy:
+            raise SystemExit(f"no reference copy of {COPY_BYTES} bytes for {cn}")
+        scale[cn] = statistics.median(copy) * 1024 / COPY_BYTES
+    med = lambda e, n: statistics.median(e[n]) if n in e else float("nan")
+    table = []
+    for (name, grid), e in rows.items():
+        if "GRBM_GUI_ACTIVE" not in e or "copy" in name.lower():
+            continue
+        gui = med(e, "GRBM_GUI_ACTIVE") / XCDS
+        mf = med(e, "SQ_INSTS_MFMA")
+        table.append({
+            "kernel": name, "grid": grid, "calls": len(e["GRBM_GUI_ACTIVE"]),
+            "us": statistics.median(e["_dur"]),
+            "mfma_busy": med(e, "SQ_VALU_MFMA_BUSY_CYCLES") / (gui * SIMDS),
+            "valu_per_mfma": med(e, "SQ_INSTS_VALU") / mf if mf else float("nan"),
+            "lds_per_mfma": med(e, "SQ_INSTS_LDS") / mf if mf else float("nan"),
+            "lds_conflict": med(e, "SQ_LDS_BANK_CONFLICT") / (gui * CUS),
+            "fetch_mb": med(e, "FETCH_SIZE") * 1024 / scale["FETCH_SIZE"] / 1e6,
+            "write_mb": med(e, "WRITE_SIZE") * 1024 / scale["WRITE_SIZE"] / 1e6,
+        })
+    table.sort(key=lambda t: -t["us"] * t["calls"])
+    with open(out_md, "w") as fh:
+        fh.write(f"# Hardware counters per kernel: {title}\n\n")
+        fh.write("Three counter passes over the same run (repo root on the GPU box, TMPDIR=/tmp, run from /tmp):\n\n")
+        fh.write("    rocprofv3 --pmc SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+                 "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE --output-format csv "
+                 f"-d <repo>/gpurun_out/pmc_sq -o run -- python3 <repo>/bench.py {title}\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch -o run -- "
+                 f"python3 <repo>/bench.py {title}\n")
+        fh.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write -o run -- "
+                 f"python3 <repo>/bench.py {title}\n\n")
+        fh.write(f"Summary written by: `{cmdline}`\n\n")
+        fh.write("MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs) (rocprofv3's MfmaUtil); "
+                 "LDS conflict = SQ_LDS_BANK_CONFLICT / (GUI-active cycles x 256 CUs); HBM MB = FETCH_SIZE / WRITE_SIZE "
+                 f"divided by the factor the same counter reads for a {COPY_BYTES >> 20} MiB device copy "
+                 f"(FETCH {scale['FETCH_SIZE']:.4f}, WRITE {scale['WRITE_SIZE']:.4f}).  Durations are under the "
+                 "profiler (kernels serialised).  Kernel template arguments: gemm_kernel<qtype, epilogue, BM, BN, "
+                 "k-groups> (qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, 1 SwiGLU, 2 CE logits, 3 CE gradient, "
+                 "4 linear backward (dX), 5 SwiGLU backward, 6 gate/up backward, 7 dh accumulate).\n\n")
+        fh.write("| kernel | threads | calls | us | MFMA busy | VALU/MFMA | LDS/MFMA | LDS conflict | HBM fetch MB | "
+                 "HBM write MB |\n|---|---|---|---|---|---|---|---|---|---|\n")
+        for t in table[:40]:
+            fh.write(f"| {t['kernel']} | {t['grid']} | {t['calls']} | {t['us']:.1f} | {t['mfma_busy']:.3f} | "
+                     f"{t['valu_per_mfma']:.2f} | {t['lds_per_mfma']:.2f} | {t['lds_conflict']:.3f} | "
+                     f"{t['fetch_mb']:.1f} | {t['write_mb']:.1f} |\n")
+    jpath = os.path.join(ROOT, "profiles", "mmq_counters.json")
+    js = json.load(open(jpath)) if os.path.exists(jpath) else {}
+    for t in table:
+        if "gemm_kernel" in t["kernel"] or "skinny" in t["kernel"]:
+            js[f"{t['kernel']}|{t['grid']}"] = dict(t, source_hash=gemm_source_hash())
+    with open(jpath, "w") as fh:
+        json.dump(js, fh, indent=1, sort_keys=True)
+    log(f"wrote {out_md} and {jpath}")
+
+
+def load_counters(kernel_name, grid):
+    """MFMA-busy fraction etc. of one MMQ launch from the committed counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "mmq_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        ent = json.load(open(p)).get(f"{kernel_name}|{grid}")
+    except Exception:
+        return None
+    if not ent or ent.get("source_hash") != gemm_source_hash():
+        return None
+    return ent
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -208,9 +316,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time the other workloads")
-    ap.add_argument("--sweep", action="store_true",
-                    help="small-token sweep (HBM-bound shapes); included in --all")
+    ap.add_argument("--all", action="store_true", help="(default) time every workload")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the headline linear step and the Q4_0 MoE layer")
+    ap.add_argument("--sweep", action="store_true", help="small-token sweep (part of the default run)")
+    ap.add_argument("--repeats", type=int, default=5, help="timing repeats (median reported)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="no HIP-graph replay (counter runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -218,11 +328,18 @@ def main():
     ap.add_argument("--kernel-summary", nargs=3, metavar=("CSV_DIR", "OUT_MD", "TITLE"),
                     help="write a kernel-time summary from a rocprofv3 --kernel-trace --stats "
                          "--output-format csv run (files run_kernel_stats.csv, run_kernel_trace.csv)")
+    ap.add_argument("--counters-from", nargs=5, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "OUT_MD", "TITLE"),
+                    help="write a per-kernel counter summary from three rocprofv3 --pmc runs and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/mmq_traffic.json from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if not args.quick:
+        args.all = True
     if args.traffic_from:
         write_traffic(*args.traffic_from, " ".join(sys.argv))
+        return
+    if args.counters_from:
+        write_counters(*args.counters_from, " ".join(sys.argv))
         return
     if args.kernel_summary:
         write_kernel_summary(*args.kernel_summary)
@@ -266,20 +383,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def time_steps(fn, steps, warmup, graph_too=True):
-        """(eager ms, graph ms) per step: `steps` calls issued from Python, then
-        the same step captured once in a HIP graph and replayed `steps` times
-        (no host launch work between kernels; every kernel still runs)."""
+    spreads = {}
+
+    def time_steps(fn, steps, warmup, graph_too=True, key=None):
+        """(eager ms, graph ms) per step: `steps` calls issued from Python
+        (the median of `--repeats` such runs; their spread is kept under
+        `key`), then the same step captured once in a HIP graph and replayed
+        `steps` times (no host launch work between kernels; every kernel
+        still runs)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         a, b = ev(), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        eager = a.elapsed_time(b) / steps
+        runs = []
+        for _ in range(max(1, args.repeats)):
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            runs.append(a.elapsed_time(b) / steps)
+        eager = float(np.median(runs))
+        if key:
+            spreads[key] = {"repeats": len(runs), "median_ms": round(eager, 4),
+                            "min_ms": round(min(runs), 4), "max_ms": round(max(runs), 4)}
         if args.eager or not graph_too:
             return eager, eager
         side = torch.cuda.Stream()
@@ -348,7 +475,7 @@ def main():
 
     K = args.steps
     # timed steps: nothing but the step itself on the stream
-    ms, ms_graph = time_steps(step, K, args.warmup)
+    ms, ms_graph = time_steps(step, K, args.warmup, key=cfg.name)
     # a second pass of K steps with events around the two MMQ launches (on
     # the stream they are launched on) gives the per-launch durations; the
     # event markers add queue latency, so they stay out of the timed steps
@@ -374,7 +501,12 @@ def main():
     roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic(kkey), "launch_us": round(kms * 1e3, 2),
-                "other_mmq_us": round((fwd_ms if kms == bwd_ms else bwd_ms) * 1e3, 2)}
+                "other_mmq_us": round((fwd_ms if kms == bwd_ms else bwd_ms) * 1e3, 2),
+                "algorithmic_flops_per_launch": gemm_flops}
+    # MFMA-busy fraction of the same launch from the committed counter summary
+    frag, grid = {k: (f, g) for f, g, k in MMQ_LAUNCHES}[kkey]
+    cnt = load_counters(frag, grid)
+    roofline["mfma_busy_counter"] = round(cnt["mfma_busy"], 4) if cnt else None
 
     # cold operands: the same step rotating over copies of W, x and dY that
     # together exceed the 256 MB Infinity Cache, so every step streams its
@@ -391,7 +523,7 @@ def main():
         yc, xac = gq.linear_lora_fwd(pc, xc)
         return gq.linear_lora_bwd(pc, xc, xac, dyc, ws=ws)
 
-    ms_cold = time_steps(cold_step, max(K, 2 * ncopy), ncopy, graph_too=False)[0]
+    ms_cold = time_steps(cold_step, max(K, 2 * ncopy), ncopy, graph_too=False, key=cfg.name + "_cold")[0]
     del copies
     log(f"[bench] linear step, cold operands ({ncopy} copies, {ncopy * set_bytes / 1e6:.0f} MB): "
         f"{ms_cold:.3f} ms ({flops / (ms_cold * 1e-3) / 1e12:.1f} TFLOP/s)")
@@ -435,7 +567,7 @@ def main():
             yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
             return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
 
-        mms, mms_graph = time_steps(mstep, K, max(2, args.warmup))
+        mms, mms_graph = time_steps(mstep, K, max(2, args.warmup), key=mc.name)
         mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
         # rows routed to each expert (one routing call outside the timed steps)
         counts = np.diff(gq.moe_route(mlg, mc.k)[3].cpu().numpy().astype(np.int64))
@@ -453,8 +585,8 @@ def main():
     if args.all:
         extra = {}
 
-        def timed(fn, steps):
-            return time_steps(fn, steps, 2)[0]
+        def timed(fn, steps, key):
+            return time_steps(fn, steps, 2, key=key)[0]
 
         c1 = synth.LINEAR_Q8_0_T128
         i1 = synth.make_linear(c1)
@@ -466,9 +598,18 @@ def main():
             yy, xa1 = gq.linear_lora_fwd(p1, x1)
             return gq.linear_lora_bwd(p1, x1, xa1, dy1)
 
-        m1 = timed(s1, K)
+        m1 = timed(s1, K, c1.name)
         f1 = linear_flops(c1.T, c1.K, c1.N, c1.rank)
-        extra[c1.name] = {"ms_per_step": round(m1, 4), "tflops": round(f1 / (m1 * 1e-3) / 1e12, 2)}
+        # algorithmic bytes: W blocks once per pass (fwd, bwd), x, dY read,
+        # y, dX written, adapters read, adapter gradients written
+        b1 = (2 * i1["blocks"].nbytes + 2 * 2 * c1.T * (c1.K + c1.N) +
+              2 * 4 * c1.rank * (c1.K + c1.N))
+        extra[c1.name] = {"ms_per_step": round(m1, 4), "tflops": round(f1 / (m1 * 1e-3) / 1e12, 2),
+                          "algorithmic_bytes": int(b1),
+                          "frac_hbm": round(b1 / (m1 * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                          "frac_bf16_peak": round(f1 / (m1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+                          "bound": "hbm; in practice launch latency (7 dependent launches)",
+                          "launches": 7}
         log(f"[bench] {c1.name}: {m1 * 1e3:.1f} us/step")
 
         c4 = synth.MOE_Q2DM_T4096_ZIPF
@@ -487,12 +628,13 @@ def main():
             yy, sv = gq.moe_ffn_fwd(w4, x4, lg4, c4.k)
             return gq.moe_ffn_bwd(w4, x4, dy4, sv, c4.k, c4.E)
 
-        m4 = timed(st4, max(3, K // 4))
+        m4 = timed(st4, max(3, K // 4), c4.name)
         f4 = moe_flops(c4.T, c4.H, c4.I, c4.k, c4.rank)
         cnt4 = np.diff(gq.moe_route(lg4, c4.k)[3].cpu().numpy().astype(np.int64))
         act4 = cnt4[cnt4 > 0]
         extra[c4.name] = {"ms_per_step": round(m4, 4), "tokens_per_s": round(c4.T / (m4 * 1e-3), 1),
                           "tflops": round(f4 / (m4 * 1e-3) / 1e12, 2),
+                          "frac_bf16_peak": round(f4 / (m4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "route_rows_per_expert": {"active_experts": int(act4.size),
                                                     "max_rows": int(cnt4.max()),
                                                     "median_rows": float(np.median(cnt4)),
@@ -515,10 +657,11 @@ def main():
             ws5[0] = out["ws"]
             return out
 
-        m5 = timed(st5, max(3, K // 4))
+        m5 = timed(st5, max(3, K // 4), c5.name)
         f5 = 6 * c5.T * c5.V * c5.H + 8 * c5.T * c5.V * c5.rank + 6 * c5.T * c5.rank * c5.H
         extra[c5.name] = {"ms_per_step": round(m5, 4), "tokens_per_s": round(c5.T / (m5 * 1e-3), 1),
-                          "tflops": round(f5 / (m5 * 1e-3) / 1e12, 2)}
+                          "tflops": round(f5 / (m5 * 1e-3) / 1e12, 2),
+                          "frac_bf16_peak": round(f5 / (m5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] {c5.name}: {m5:.3f} ms/step")
         result["other_workloads"] = extra
 
@@ -615,7 +758,7 @@ def main():
                 yy, sv = gq.moe_ffn_fwd(swts, tx, tlg, tc.k)
                 return gq.moe_ffn_bwd(swts, tx, tdy, sv, tc.k, tc.E)
 
-            tms = time_steps(tstep, max(10, K), 3)[0]
+            tms = time_steps(tstep, max(10, K), 3, key=tc.name)[0]
             _, sv = gq.moe_ffn_fwd(swts, tx, tlg, tc.k)
             active = int((sv["offsets"][1:] - sv["offsets"][:-1] > 0).sum().item())
             nbytes = moe_layer_bytes(T, sc.H, sc.I, sc.E, sc.k, sc.rank, bs, active)
@@ -645,7 +788,7 @@ def main():
                 hws[0] = out["ws"]
                 return out
 
-            hms = time_steps(hstep, max(10, K), 3)[0]
+            hms = time_steps(hstep, max(10, K), 3, key=cfgT.name)[0]
             nbytes = cfgT.V * (cfgT.H // 32) * 34 + T * cfgT.H * 2 + cfgT.V * cfgT.rank * 4 + cfgT.rank * cfgT.H * 4
             gbs = nbytes / (hms * 1e-3) / 1e9
             sweep.append({"workload": cfgT.name, "op": "LM head forward (loss, lse)", "ms": round(hms, 4),
@@ -657,17 +800,35 @@ def main():
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
         from oracle import linear as ol
 
+        # every host core this process may run on, set explicitly for the BLAS
+        ncpu = os.cpu_count() or 1
+        try:
+            n_affinity = len(os.sched_getaffinity(0))
+        except AttributeError:
+            n_affinity = ncpu
+        want = max(1, min(n_affinity, int(os.environ.get("OMP_NUM_THREADS", n_affinity))))
+        cpu_model = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         reps, spent = 0, 0.0
         ref = None
-        while spent < args.cpu_seconds and reps < 500:
-            t0 = time.perf_counter()
-            ref = ol.run(inp)
-            spent += time.perf_counter() - t0
-            reps += 1
+        with threadpool_limits(limits=want, user_api="blas"):
+            blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+            threads = max([i.get("num_threads", 1) for i in blas] or [1])
+            while spent < args.cpu_seconds and reps < 500:
+                t0 = time.perf_counter()
+                ref = ol.run(inp)
+                spent += time.perf_counter() - t0
+                reps += 1
         # parity of the timed step against the oracle on the same inputs
         # (relative Frobenius error per output)
         yg, (dxg, dAg, dBg) = step()
@@ -680,12 +841,21 @@ def main():
 
         result["parity_rel_frobenius"] = {k: f"{rel(t, k):.2e}" for k, t in
                                           (("y", yg), ("dx", dxg), ("dA", dAg), ("dB", dBg))}
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas_desc = ", ".join(f"{b.get('internal_api')} {b.get('version')} ({b.get('threading_layer')})"
+                              for b in blas) or "none found"
         result["cpu_baseline"] = {"value": round(flops * reps / spent / 1e12, 5), "unit": "TFLOP/s",
                                   "cores": threads, "kind": "oracle",
-                                  "sample": f"{reps} full fwd+bwd passes of {cfg.name} in fp64 "
-                                            f"numpy/OpenBLAS, {spent:.1f}s"}
-        log(f"[bench] cpu oracle {reps} reps in {spent:.1f}s on {threads} threads")
+                                  "sample": f"{reps} full fwd+bwd passes of {cfg.name} in fp64 numpy, "
+                                            f"{spent:.1f}s",
+                                  "os_cpu_count": ncpu, "affinity_cpus": n_affinity,
+                                  "cpu_model": cpu_model, "blas": blas_desc,
+                                  "blas_threads_set": want,
+                                  "tokens_per_s": round(cfg.T * reps / spent, 1),
+                                  "gflops_fp64": round(flops * reps / spent / 1e9, 1)}
+        log(f"[bench] cpu oracle {reps} reps in {spent:.1f}s on {threads} BLAS threads "
+            f"({cpu_model}, os.cpu_count {ncpu}, affinity {n_affinity}, {blas_desc})")
+
+    result["timing_spread"] = spreads
 
     print(json.dumps(result), flush=True)
 
