@@ -185,6 +185,17 @@ int nn_tile_bn(int tc) { (void)tc; return TILE_BN; }  // 128 for the tile and th
 
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
+// Dense forward launches with Q8_0 / Q4_0 weights and K % 64 == 0 run the
+// 256 x 192 wide tiles when those fill the chip: at least 192 tiles, and the
+// last round of one tile per CU at least three quarters full.
+bool wide_pays(int qtype, int64_t M, int64_t N, int64_t K) {
+  if (qtype == GQ_Q2_DM || K % GEMM_BK) return false;
+  const int64_t tiles = (int64_t)cdiv(M, WIDE_BM) * cdiv(N, WIDE_BN);
+  if (tiles < 192) return false;
+  const int64_t rounds = (tiles + 255) / 256;
+  return tiles * 4 >= rounds * 256 * 3;
+}
+
 hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
 
 }  // namespace
@@ -250,7 +261,11 @@ int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, ui
   g.w0 = static_cast<const uint8_t*>(L->w_blocks);
   g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
   g.ntiles = cdiv(N, TILE_BN);
-  const int tc = pick_fwd_tile(T, T, g.ntiles, K, aligned(L->w_blocks, 16), true);
+  int tc = pick_fwd_tile(T, T, g.ntiles, K, aligned(L->w_blocks, 16), true);
+  if (!tile_skinny(tc) && wide_pays(L->qtype, T, N, K)) {
+    tc = TILE_WIDE;
+    g.ntiles = cdiv(N, WIDE_BN);
+  }
   g.mtiles = cdiv(T, tile_bm(tc));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
   g.o0 = y; g.ldo = N;

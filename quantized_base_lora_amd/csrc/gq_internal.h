@@ -90,18 +90,23 @@ struct GemmArgs {
 // TILE_SKINNY{16,32,64}: the forward-only skinny MMQ for few rows per
 // weight (16, 32 or 64 rows per tile, 128 weight rows per workgroup;
 // K % 256 == 0).
+// TILE_WIDE: 256 x 192 tiles on 512 threads (gq_wide_impl.h), dense
+// forward launches with Q8_0 / Q4_0 weights and K % 64 == 0 only.
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,
   TILE_128x128_K2 = 2,
   TILE_SKINNY16 = 3,
   TILE_SKINNY32 = 4,
-  TILE_SKINNY64 = 5
+  TILE_SKINNY64 = 5,
+  TILE_WIDE = 6
 };
+constexpr int WIDE_BM = 256, WIDE_BN = 192;
 
-inline bool tile_skinny(int cfg) { return cfg >= TILE_SKINNY16; }
+inline bool tile_skinny(int cfg) { return cfg >= TILE_SKINNY16 && cfg <= TILE_SKINNY64; }
 inline int tile_bm(int cfg) {
   switch (cfg) {
+    case TILE_WIDE: return WIDE_BM;
     case TILE_64x128: return 64;
     case TILE_SKINNY16: return 16;
     case TILE_SKINNY32: return 32;

@@ -1,0 +1,310 @@
+// Wide-tile MMQ for large dense forward launches (the reduction runs along
+// the weight's block dimension): 256 x 192 output tiles on 512 threads.
+//
+// The tile GEMM in gq_gemm_impl.h decodes each 64-deep weight slice for 128
+// activation rows; here every decoded slice feeds 256 rows, which halves the
+// block-decode VALU per MFMA, and each wave's 64 x 96 share of the tile needs
+// 0.83 KB of LDS operand reads per 32x32x16 MFMA instead of 1 KB.  Eight
+// waves (two per SIMD) keep the decode of the next slice overlapped with the
+// matrix cores, and a 2048 x 6144 output is exactly one tile per CU.
+//
+//  * Activations: 256 rows x 64 bf16 per k-step, four coalesced 16-byte loads
+//    per thread into registers, stored into a padded LDS tile one step later.
+//  * Weights: the 192 rows x 2 blocks of a k-step as quarter-block items
+//    (three per thread): the fp16 scale plus one quarter of the payload,
+//    decoded to bf16 into the [n][k] LDS tile.
+//  * Double-buffered LDS, one barrier per k-step, loads two steps ahead.
+//  * Rows past M and weight rows past N are clamped to the last valid row
+//    (their results are never stored), so the pipeline has no masks; K must
+//    be a multiple of 64.
+//  * The rank-r adapter term is folded into the accumulators as extra k16
+//    MFMA slices (bf16 hi + lo parts), as in the tile GEMM.
+#pragma once
+#include "gq_dev.h"
+#include "gq_internal.h"
+
+namespace gq {
+namespace wide {
+
+constexpr int BM = 256, BN = 192, BK = 64, LDK = BK + 8, NTHR = 512;
+constexpr int TM = 2, TN = 3;      // 32x32 sub-tiles per wave (64 x 96)
+constexpr int WTM = 64, WTN = 96;  // wave tile
+constexpr int A_ST = BM * LDK, B_ST = BN * LDK;
+constexpr int SMEM_MAIN = (2 * A_ST + 2 * B_ST) * 2;
+constexpr int SP = WTN + 8;  // staged epilogue row pitch (bf16)
+constexpr int SMEM_EPI = 8 * WTM * SP * 2;
+constexpr int SMEM = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
+
+// A quarter of a block: its fp16 scale (low 16 bits of hdr) and payload
+// bytes [q*NB, q*NB + NB) with NB = 4 (Q4_0) or 8 (Q8_0).
+template <int QT> struct QuarterBytes;
+template <> struct QuarterBytes<QT_Q4_0> { static constexpr int NQ = 1; };
+template <> struct QuarterBytes<QT_Q8_0> { static constexpr int NQ = 2; };
+template <int QT> struct RawQuarter {
+  uint32_t hdr;
+  uint32_t q[QuarterBytes<QT>::NQ];
+};
+
+template <int QT>
+__device__ __forceinline__ void load_quarter(const uint8_t* blk, int qq, RawQuarter<QT>& r) {
+  typedef const __attribute__((address_space(1))) uint16_t g_u16;
+  typedef const __attribute__((address_space(1))) u32_a2 g_u32a2;
+  r.hdr = *(const g_u16*)blk;
+  const g_u32a2* q = (const g_u32a2*)(blk + 2 + 4 * QuarterBytes<QT>::NQ * qq);
+#pragma unroll
+  for (int i = 0; i < QuarterBytes<QT>::NQ; ++i) r.q[i] = q[i];
+}
+
+// Decode one quarter and store it into the [n][k] tile row `base` (the
+// block's first element).  Same arithmetic as decode_block_fast: every
+// product is exact, the bf16 value is d*q rounded once.
+//  Q4_0 quarter qq: bytes 4qq..4qq+3 -> elements 4qq.. (low nibbles) and
+//                   16+4qq.. (high nibbles)
+//  Q8_0 quarter qq: bytes 8qq..8qq+7 -> elements 8qq..8qq+7
+template <int QT>
+__device__ __forceinline__ void store_quarter(uint16_t* base, int qq, const RawQuarter<QT>& r) {
+  const float d = h2f(r.hdr & 0xffffu);
+  if constexpr (QT == QT_Q4_0) {
+    const float off = -8.f * d;
+    const uint32_t lo = r.q[0] & 0x0f0f0f0fu, hi = (r.q[0] >> 4) & 0x0f0f0f0fu;
+    float a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_fmaf(ubyte(lo, i), d, off);
+      b[i] = __builtin_fmaf(ubyte(hi, i), d, off);
+    }
+    *reinterpret_cast<uint2*>(base + 4 * qq) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+    *reinterpret_cast<uint2*>(base + 16 + 4 * qq) = make_uint2(pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3]));
+  } else {
+    const float off = -128.f * d;
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t u = r.q[h] ^ 0x80808080u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * h + i] = __builtin_fmaf(ubyte(u, i), d, off);
+    }
+    *reinterpret_cast<uint4*>(base + 8 * qq) =
+        make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+  }
+}
+
+// Dense forward: out[p][n] = sum_k a0[p][k] deq(W)[n][k] + s * rv0[p] . lB0[n]
+// (EPI_LIN).  Geometry from GemmArgs: M rows, N = w_rows output columns, K.
+template <int QT>
+__global__ __launch_bounds__(NTHR, 1) void wide_lin_kernel(const GemmArgs p) {
+  constexpr int BS = QTraits<QT>::BS;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Bs = As + 2 * A_ST;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+
+  // XCD-contiguous runs of tiles (ids go round-robin over the 8 XCDs), each
+  // run laid out as GM m-tiles by a band of n-tiles
+  const int count = gridDim.x;
+  const int q8 = count >> 3, rem = count & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int bid = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + loc;
+  constexpr int GM = 4;
+  const int g = bid / (GM * p.ntiles), m_first = g * GM, gm = min(p.mtiles - m_first, GM);
+  const int idx = bid - g * GM * p.ntiles;
+  const int mt = m_first + idx % gm, nt = idx / gm;
+  const int64_t r0 = (int64_t)mt * BM;
+  const int n0 = nt * BN;
+  if (r0 >= p.M || n0 >= p.w_rows) return;
+  const int nk = p.K / BK;
+
+  // activation rows of this thread's four 16-byte chunks (c = tid + 512 i:
+  // row c >> 3, chunk c & 7), clamped to the last row
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = min(r0 + (tid >> 3) + 64 * i, p.M - 1);
+    ap[i] = p.a0 + row * p.lda + (tid & 7) * 8;
+  }
+  // weight quarter items it = tid + 512 i: row it >> 3, block (it >> 2) & 1,
+  // quarter it & 3 (eight consecutive lanes cover a row's two blocks)
+  int w_row[3], w_blk[3], w_q[3];
+  const uint8_t* wp[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int it = tid + NTHR * i;
+    w_row[i] = it >> 3;
+    w_blk[i] = (it >> 2) & 1;
+    w_q[i] = it & 3;
+    const int nrow = min(n0 + w_row[i], p.w_rows - 1);
+    wp[i] = p.w0 + (int64_t)(p.w_row0 + nrow) * p.w_rowbytes + w_blk[i] * BS;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  uint4 a00, a01, a02, a03, a10, a11, a12, a13;
+  RawQuarter<QT> W0[3], W1[3];
+#define GQW_LOAD_A(KT, X0, X1, X2, X3)                           \
+  {                                                              \
+    const int k_ = min((KT), nk - 1) * BK;                       \
+    X0 = *reinterpret_cast<const uint4*>(ap[0] + k_);            \
+    X1 = *reinterpret_cast<const uint4*>(ap[1] + k_);            \
+    X2 = *reinterpret_cast<const uint4*>(ap[2] + k_);            \
+    X3 = *reinterpret_cast<const uint4*>(ap[3] + k_);            \
+  }
+#define GQW_STORE_A(ST, X0, X1, X2, X3)                                            \
+  {                                                                                \
+    uint16_t* d_ = As + (ST) * A_ST + (tid >> 3) * LDK + (tid & 7) * 8;            \
+    *reinterpret_cast<uint4*>(d_) = X0;                                            \
+    *reinterpret_cast<uint4*>(d_ + 64 * LDK) = X1;                                 \
+    *reinterpret_cast<uint4*>(d_ + 128 * LDK) = X2;                                \
+    *reinterpret_cast<uint4*>(d_ + 192 * LDK) = X3;                                \
+  }
+  auto load_w = [&](int kt, RawQuarter<QT> (&Wr)[3]) {
+    const int64_t koff = (int64_t)min(kt, nk - 1) * 2 * BS;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) load_quarter<QT>(wp[i] + koff, w_q[i], Wr[i]);
+  };
+  auto store_w = [&](int st, const RawQuarter<QT> (&Wr)[3]) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) store_quarter<QT>(Bs + st * B_ST + w_row[i] * LDK + w_blk[i] * 32, w_q[i], Wr[i]);
+  };
+  auto compute = [&](int st) {
+    const uint16_t* A = As + st * A_ST;
+    const uint16_t* B = Bs + st * B_ST + wn * WTN * LDK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(A + (wm * WTM + a * 32 + (lane & 31)) * LDK + kk * 16 +
+                                                 (lane >> 5) * 8);
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(B + (b * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // prologue: slices 0 and 1 in registers, slice 0 into stage 0
+  GQW_LOAD_A(0, a00, a01, a02, a03)
+  load_w(0, W0);
+  GQW_LOAD_A(1, a10, a11, a12, a13)
+  load_w(1, W1);
+  GQW_STORE_A(0, a00, a01, a02, a03)
+  store_w(0, W0);
+  __syncthreads();
+  // step kt (stage S = kt & 1): slice kt+2 is loaded into the register set
+  // slice kt was stored from, slice kt+1 (loaded a step earlier) goes into
+  // the other stage while the MFMAs of slice kt run
+#define GQW_STEP(KT, S, C0, C1, C2, C3, N0, N1, N2, N3, WC, WN) \
+  GQW_LOAD_A((KT) + 2, C0, C1, C2, C3)                          \
+  load_w((KT) + 2, WC);                                         \
+  __builtin_amdgcn_sched_barrier(0);                            \
+  compute(S);                                                   \
+  GQW_STORE_A(1 - (S), N0, N1, N2, N3)                          \
+  store_w(1 - (S), WN);                                         \
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    GQW_STEP(kt, 0, a00, a01, a02, a03, a10, a11, a12, a13, W0, W1)
+    GQW_STEP(kt + 1, 1, a10, a11, a12, a13, a00, a01, a02, a03, W1, W0)
+  }
+  if (kt < nk) {
+    GQW_STEP(kt, 0, a00, a01, a02, a03, a10, a11, a12, a13, W0, W1)
+  }
+#undef GQW_STEP
+#undef GQW_LOAD_A
+#undef GQW_STORE_A
+
+  // ---- rank-r adapter term on the MFMA: acc[row][col] += sum_j xa[row][j] *
+  // s * B[col][j], one k16 slice per 16 ranks, bf16 hi + lo parts (three
+  // products: hi*hi + hi*lo + lo*hi)
+  const int r = p.r;
+  const float s = p.s;
+  auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)v[i];
+      hi[i] = h;
+      lo[i] = (__bf16)(v[i] - (float)h);
+    }
+  };
+  for (int qr = 0; qr * 16 < r; ++qr) {
+    const int j0 = qr * 16 + (lane >> 5) * 8;
+    bf16x8 ah[TM], al[TM];
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int64_t row = r0 + wm * WTM + a * 32 + (lane & 31);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (row < p.M && j0 + i < r) ? p.rv0[row * r + j0 + i] : 0.f;
+      split8(v, ah[a], al[a]);
+    }
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int col = n0 + wn * WTN + b * 32 + (lane & 31);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = (col < p.w_rows && j0 + i < r) ? s * p.lB0[(int64_t)col * r + j0 + i] : 0.f;
+      bf16x8 bh, bl;
+      split8(v, bh, bl);
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bh, acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bl, acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a], bh, acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: the wave's 64 x 96 tile through its own LDS region (rows
+  // of 104 bf16), stored as 16-byte row pieces (12 lanes per row) when the
+  // output rows allow it, else one 2-byte store per value
+  __syncthreads();  // every wave is done reading the operand stages
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(smem) + wave * WTM * SP;
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        Ws[(a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * SP + b * 32 + (lane & 31)] = f2bf(acc[a][b][v]);
+  const int64_t rbase = r0 + wm * WTM;
+  const int cbase = n0 + wn * WTN;
+  const bool vec = ((uintptr_t)p.o0 % 16 == 0) && (p.ldo % 8 == 0) && (p.N % 8 == 0);
+  constexpr int CH = WTN / 8;
+  for (int i = lane; i < WTM * CH; i += 64) {
+    const int rr = i / CH, cc = (i % CH) * 8;
+    const int64_t pr = rbase + rr;
+    const int n = cbase + cc;
+    if (pr >= p.M || n >= p.N) continue;
+    const uint16_t* src = Ws + rr * SP + cc;
+    if (vec) {
+      *reinterpret_cast<uint4*>(p.o0 + pr * p.ldo + n) = *reinterpret_cast<const uint4*>(src);
+    } else {
+      for (int c = 0; c < 8 && n + c < p.N; ++c) p.o0[pr * p.ldo + n + c] = src[c];
+    }
+  }
+}
+
+}  // namespace wide
+
+namespace {
+// Launch of the wide-tile forward (EPI_LIN, dense, Q8_0 / Q4_0, K % 64 == 0);
+// declared beside launch_q in gq_gemm_impl.h.
+template <int QT>
+hipError_t launch_wide_lin(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
+  hipLaunchKernelGGL((wide::wide_lin_kernel<QT>), grid, dim3(wide::NTHR), 0, st, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+}  // namespace gq

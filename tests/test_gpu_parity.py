@@ -80,6 +80,9 @@ LIN_CASES = [
     # ends in a half k-step, rows start 2-byte aligned
     (19, 32, 40, 1, 4), (70, 96, 136, 0, 8), (130, 160, 64, 2, 4), (300, 160, 200, 1, 16),
     (257, 96, 264, 0, 2),
+    # enough 256 x 192 tiles for the wide forward MMQ, with a partial last
+    # row tile and a partial last column tile (T % 256, N % 192 != 0)
+    (2000, 1024, 6104, 0, 4), (1800, 512, 5760, 1, 8),
 ]
 
 
