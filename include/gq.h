@@ -4,13 +4,12 @@
  *
  * The method (page 2, "Show HN: LoRA over GGUF - Train Qwen3.8-Flash-Next in
  * 40G VRAM", section "Things involved in the training"): the base weights
- * stay in GGUF blocks and are multiplied without being expanded ("MMQ and
- * grouped MMQ like llama.cpp"); a LoRA adapter is folded into the same layer
- * and trained with the fast backward formula ("Fast LoRA bwd formula like
- * Unsloth for linear layer and MoE layer"); MoE routing is softmax top-k
- * ("MoE routing like OpenAI triton-kernels"); the LM head feeds a chunked
- * cross entropy ("Chunked cross entropy loss like Liger Kernel, which works
- * with MMQ"); no load-balancing loss.
+ * stay in GGUF blocks and are multiplied without being expanded, after
+ * llama.cpp's MMQ, dense and grouped by expert; a LoRA adapter is folded
+ * into the same layer and trained with Unsloth's fast backward formula for
+ * linear and MoE layers; MoE routing is softmax top-k after OpenAI's
+ * triton-kernels; the LM head feeds a chunked cross entropy after Liger
+ * Kernel's that consumes the MMQ output; no load-balancing loss.
  *
  * Conventions shared by every entry point
  *  - All array pointers are DEVICE pointers to contiguous row-major data

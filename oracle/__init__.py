@@ -7,10 +7,11 @@ its Python binding) may import, call or execute this package; only the tests,
 It is a plain, slow, obviously-correct restatement of what the method
 computes, written from the pages (page 2, "Show HN: LoRA over GGUF - Train
 Qwen3.8-Flash-Next in 40G VRAM", section "Things involved in the training":
-MMQ and grouped MMQ like llama.cpp; the fast LoRA backward formula like
-Unsloth for linear and MoE layers; MoE routing like OpenAI triton-kernels;
-chunked cross entropy like Liger Kernel, which works with MMQ; load-balancing
-loss disabled).  Everything is computed in float64 from the exact bytes and
+quantised matrix products over the GGUF blocks after llama.cpp's MMQ, dense
+and grouped by expert; Unsloth's fast LoRA backward for linear and MoE
+layers; top-k MoE routing after OpenAI's triton-kernels; a chunked cross
+entropy after Liger Kernel's that consumes the MMQ output; no
+load-balancing loss).  Everything is computed in float64 from the exact bytes and
 bf16 values the GPU receives.  It shares no code with the HIP path: the only
 module both sides import is ``synth`` (seeded inputs, no method arithmetic).
 

@@ -1,7 +1,7 @@
 """Block decode, written from the block definitions (oracle; test use only).
 
-The pages train over a GGUF base read by "MMQ ... like llama.cpp" (page 2,
-"Things involved in the training"), i.e. the weights stay as blocks of 32
+The pages train over a GGUF base read by quantised matrix products after
+llama.cpp's MMQ (page 2, "Things involved in the training"), i.e. the weights stay as blocks of 32
 small integers with fp16 scale(s).  Three formats are decoded:
 
 * Q8_0  (34 bytes): fp16 d, then 32 signed bytes q;            w_i = d*q_i

@@ -1,10 +1,10 @@
 """Fused quantised linear layer with a LoRA adapter (oracle; test use only).
 
 Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
-the training": the base product is an MMQ over the frozen block-quantised W
-("MMQ and grouped MMQ like llama.cpp") and the backward is the fast LoRA
-formula ("Fast LoRA bwd formula like Unsloth for linear layer"): the gradient
-never forms B.A and the frozen W receives no gradient.
+the training": the base product is a quantised matrix product over the
+frozen block-quantised W, after llama.cpp's MMQ, and the backward is
+Unsloth's fast LoRA formula for a linear layer: the gradient never forms
+B.A and the frozen W receives no gradient.
 
 With s the adapter scale (alpha / rank), A [r, K], B [N, r]:
     xa = x A^T

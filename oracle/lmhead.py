@@ -2,9 +2,9 @@
 cross entropy (oracle; test use only).
 
 Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
-the training": "Chunked cross entropy loss like Liger Kernel, which works with
-MMQ" -- the [tokens x vocab] logits are never held whole; the vocabulary is
-walked in row chunks with an online log-sum-exp.
+the training", which lists a chunked cross entropy after Liger Kernel's,
+computed over the MMQ output: the [tokens x vocab] logits are never held
+whole; the vocabulary is walked in row chunks with an online log-sum-exp.
 
     z      = h deq(W)^T + s (h A^T) B^T                 (per chunk of rows)
     m, l   : m' = max(m, max_v z),  l' = l e^(m - m') + sum_v e^(z - m')

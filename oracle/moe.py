@@ -2,10 +2,11 @@
 (oracle; test use only).
 
 Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
-the training": grouped MMQ over the GGUF experts ("MMQ and grouped MMQ like
-llama.cpp"), per-expert adapters ("AITER gmm/ptgmm ... for non-quantized MoE
-LoRA"), routing like triton-kernels, the fast LoRA backward "for linear layer
-and MoE layer", and no load-balancing loss.  The ai-manual.ru page describes
+the training": quantised products over the GGUF experts grouped by expert,
+after llama.cpp's grouped MMQ; per-expert adapters, which the pages run with
+AITER's grouped GEMMs since they are not quantised; top-k routing after
+triton-kernels; Unsloth's fast LoRA backward, which the pages apply to MoE
+layers as well as linear ones; and no load-balancing loss.  The ai-manual.ru page describes
 the fused MoE kernel as touching only active experts and combining the
 experts' outputs with a sparse reduce.
 

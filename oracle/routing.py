@@ -1,9 +1,9 @@
 """MoE routing (oracle; test use only).
 
 Follows page 2 ("Show HN: LoRA over GGUF ..."), section "Things involved in
-the training": "MoE routing like OpenAI triton-kernels", with the
-load-balancing loss disabled (same section), so the router gradient is that
-of the gate weights alone.
+the training", which names OpenAI's triton-kernels as the model for the
+MoE routing and turns the load-balancing loss off (same section), so the
+router gradient is that of the gate weights alone.
 
 Per token t over the E router logits l:
   1. the k experts with the largest logits, ties broken toward the lower

@@ -1,7 +1,7 @@
 // One MFMA GEMM template for every quantised contraction on the path.
 //
-// The pages' fused dequantize-and-multiply ("MMQ and grouped MMQ like
-// llama.cpp", page 2 "Show HN: LoRA over GGUF", section "Things involved in
+// The pages' fused dequantize-and-multiply (llama.cpp-style MMQ, dense and
+// grouped, page 2 "Show HN: LoRA over GGUF", section "Things involved in
 // the training"; the ai-manual.ru article describes the fused kernel as
 // decoding the compressed weights in registers and multiplying at once, with
 // no fp16 copy of W) is built here for CDNA4:

@@ -5,7 +5,7 @@
 //    shuffle reduction; column outer-product reductions (dA, dB) over fixed
 //    row chunks with partials summed in chunk order (deterministic, no float
 //    atomics)
-//  * MoE routing "like OpenAI triton-kernels" (page 2 "Show HN: LoRA over
+//  * MoE routing after OpenAI's triton-kernels (page 2 "Show HN: LoRA over
 //    GGUF", section "Things involved in the training"): wave-per-token top-k,
 //    a stable counting sort by expert (per-chunk histograms, a scan, and
 //    in-chunk ranks from an LDS key scan) -- positions never come from atomics
