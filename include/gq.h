@@ -37,8 +37,22 @@
  *  - No full-precision copy of a quantised weight is ever written: the
  *    blocks are decoded into registers / LDS inside the kernels.
  *  - Calls are reentrant; there is no global mutable state besides the
- *    thread-local error text and the fixed device scratch array of
- *    gq_linear_lora_bwd_noalloc (see there).
+ *    thread-local error text, the thread-local event pair that
+ *    gq_profile_mmq_events installs (see there), the two environment
+ *    switches below (read once per process) and the fixed device scratch
+ *    array of gq_linear_lora_bwd_noalloc (see there).
+ *  - Environment switches (both off when unset or 0):
+ *      GQ_TRACE=1  every entry point runs inside a roctx range named after
+ *                  it (rocprofv3 --marker-trace shows them; without the
+ *                  roctx library nothing is emitted); GQ_TRACE=2 also
+ *                  prints "[gq] <name> -> <status>[: <error text>]" to
+ *                  stderr for each call.
+ *      GQ_DEBUG=1  after queuing its work an entry point synchronises its
+ *                  stream, returns GQ_EHIP for an asynchronous HIP error
+ *                  and, for the calls that keep a device error word in the
+ *                  workspace, GQ_EDEVICE when that word is nonzero.  This
+ *                  breaks the "never synchronises" rule above on purpose:
+ *                  a debugging aid, not for timing or graph capture.
  *
  * Block formats (32 weights per block, little-endian fields, the blocks of
  * one row contiguous, rows contiguous):

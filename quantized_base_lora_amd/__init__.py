@@ -15,7 +15,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgq.so")
+# GQ_LIB names another build of the same library (e.g. the host-sanitized
+# libgq_san.so); the default is the in-tree libgq.so.
+LIB_PATH = os.environ.get("GQ_LIB") or os.path.join(_HERE, "libgq.so")
 
 GQ_OK, GQ_EINVAL, GQ_ENOTSUP, GQ_EWORKSPACE, GQ_EHIP, GQ_EDEVICE = 0, -1, -2, -3, -4, -5
 Q8_0, Q4_0, Q2_DM = 0, 1, 2

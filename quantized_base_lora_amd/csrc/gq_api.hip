@@ -1,8 +1,10 @@
 // C ABI of libgq: argument validation (before any HIP call), workspace
 // planning and launch sequencing.  Every step of the computation runs in the
 // HIP kernels of gq_gemm.hip / gq_small.hip on the caller's stream.
+#include <dlfcn.h>
 #include <limits.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -37,6 +39,87 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t _e = (expr);                  \
     if (_e != hipSuccess) return hip_fail(_e, what); \
   } while (0)
+
+// Environment switches, read once per process:
+//   GQ_TRACE=1  each entry point runs inside a roctx range named after it
+//               (visible to rocprofv3 --marker-trace); GQ_TRACE=2 also
+//               prints one line per call (name, status, error text) to
+//               stderr.
+//   GQ_DEBUG=1  after an entry point has queued its work, synchronise its
+//               stream and turn an asynchronous HIP error, or a nonzero
+//               device error word, into the call's own return code
+//               (GQ_EHIP / GQ_EDEVICE) instead of leaving it for the caller
+//               to find.  This serialises the caller with the GPU: a
+//               debugging aid, never for timing.
+struct Switches {
+  int trace = 0;
+  bool debug = false;
+};
+
+const Switches& switches() {
+  static const Switches s = [] {
+    Switches v;
+    if (const char* t = getenv("GQ_TRACE")) v.trace = atoi(t);
+    if (const char* d = getenv("GQ_DEBUG")) v.debug = atoi(d) != 0;
+    return v;
+  }();
+  return s;
+}
+
+// roctx is looked up at run time so that the library has no link-time
+// dependency on the tracer; without it the ranges are simply not emitted.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx v;
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so", "libroctx64.so.4",
+                            "libroctx64.so"}) {
+      void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (!h) continue;
+      v.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+      v.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+      if (v.push && v.pop) break;
+      v.push = nullptr;
+      v.pop = nullptr;
+    }
+    return v;
+  }();
+  return r;
+}
+
+int debug_check(const char* name, void* stream, const void* err_word) {
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQ_EHIP, "%s (GQ_DEBUG): %s", name, hipGetErrorString(e));
+  if (err_word) {
+    int32_t w = 0;
+    e = hipMemcpy(&w, err_word, sizeof w, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(GQ_EHIP, "%s (GQ_DEBUG): reading the error word: %s", name, hipGetErrorString(e));
+    if (w != 0) return fail(GQ_EDEVICE, "%s (GQ_DEBUG): device error word %d", name, (int)w);
+  }
+  return GQ_OK;
+}
+
+// Runs one entry point's body under the GQ_TRACE / GQ_DEBUG switches;
+// err_word is the workspace word the body's kernels report data errors in
+// (nullptr for entry points without one).
+template <class Body>
+int traced_call(const char* name, void* stream, const void* err_word, Body&& body) {
+  const Switches& sw = switches();
+  if (!sw.trace && !sw.debug) return body();
+  const Roctx& rx = roctx();
+  if (sw.trace && rx.push) rx.push(name);
+  int rc = body();
+  if (rc == GQ_OK && sw.debug) rc = debug_check(name, stream, err_word);
+  if (sw.trace && rx.pop) rx.pop();
+  if (sw.trace >= 2)
+    fprintf(stderr, "[gq] %s -> %d%s%s\n", name, rc, rc ? ": " : "", rc ? g_err.c_str() : "");
+  return rc;
+}
 
 int64_t block_bytes(int qtype) {
   switch (qtype) {
@@ -213,7 +296,7 @@ void gq_profile_mmq_events(void* start, void* stop) {
 }
 
 // ------------------------------------------------------------------ dequant
-int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype, void* out,
+static int dequant_impl(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype, void* out,
                void* stream) {
   g_err.clear();
   if (block_bytes(qtype) < 0) return fail(GQ_EINVAL, "gq_dequant: unknown qtype %d", qtype);
@@ -233,7 +316,7 @@ int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int ou
 // ------------------------------------------------------------------- linear
 size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear*, int64_t) { return 0; }
 
-int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
+static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
                        float* xa, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   (void)ws;
@@ -299,7 +382,7 @@ size_t gq_linear_lora_bwd_workspace_size(const gq_lora_linear* L, int64_t T) {
   return w.size();
 }
 
-int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+static int linear_lora_bwd_impl(const gq_lora_linear* L, const uint16_t* x, const float* xa,
                        const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB, void* ws,
                        size_t ws_bytes, void* stream) {
   g_err.clear();
@@ -408,7 +491,7 @@ extern "C" {
 
 size_t gq_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
-int gq_linear_lora_bwd_noalloc(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+static int linear_lora_bwd_noalloc_impl(const gq_lora_linear* L, const uint16_t* x, const float* xa,
                                const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
                                void* stream) {
   g_err.clear();
@@ -438,7 +521,7 @@ size_t gq_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
   return (route_ws_bytes(T, E, k) + 255) & ~(size_t)255;
 }
 
-int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+static int moe_route_impl(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
                  int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
                  void* stream) {
   g_err.clear();
@@ -465,7 +548,7 @@ int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* 
   return GQ_OK;
 }
 
-int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
+static int moe_route_bwd_impl(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
                      int32_t k, float* dlogits, void* stream) {
   g_err.clear();
   if (E < 1 || E > 1024 || k < 1 || k > 16 || k > E)
@@ -481,7 +564,7 @@ int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_
   return GQ_OK;
 }
 
-int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, int64_t T, int32_t k,
+static int moe_combine_fwd_impl(const uint16_t* o, const float* w, const int32_t* pos, int64_t T, int32_t k,
                        int64_t H, uint16_t* y, void* stream) {
   g_err.clear();
   if (T < 0 || k < 1 || k > 16 || H < 8 || H % 8 || T * ((H + 2047) / 2048) > INT_MAX)
@@ -496,7 +579,7 @@ int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, in
   return GQ_OK;
 }
 
-int gq_adamw8bit_step(float* p, const float* g, uint8_t* m_codes, uint8_t* v_codes, float* m_scale,
+static int adamw8bit_step_impl(float* p, const float* g, uint8_t* m_codes, uint8_t* v_codes, float* m_scale,
                       float* v_scale, int64_t n, int64_t step, float lr, float beta1, float beta2,
                       float eps, float weight_decay, void* stream) {
   g_err.clear();
@@ -518,7 +601,7 @@ int gq_adamw8bit_step(float* p, const float* g, uint8_t* m_codes, uint8_t* v_cod
   return GQ_OK;
 }
 
-int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+static int rmsnorm_fwd_impl(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
                    float* rstd, void* stream) {
   g_err.clear();
   if (T < 0 || H < 8 || H % 8 || H > INT_MAX || (T + 3) / 4 > INT_MAX)
@@ -534,7 +617,7 @@ int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, floa
   return GQ_OK;
 }
 
-int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const float* rstd,
+static int rmsnorm_bwd_impl(const uint16_t* dy, const uint16_t* x, const float* w, const float* rstd,
                    int64_t T, int64_t H, uint16_t* dx, void* stream) {
   g_err.clear();
   if (T < 0 || H < 8 || H % 8 || H > INT_MAX || (T + 3) / 4 > INT_MAX)
@@ -550,7 +633,7 @@ int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const 
   return GQ_OK;
 }
 
-int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k, int64_t H,
+static int moe_combine_bwd_impl(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k, int64_t H,
                        uint16_t* dx, void* stream) {
   g_err.clear();
   if (T < 0 || k < 1 || k > 16 || H < 8 || H % 8)
@@ -589,7 +672,7 @@ size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t, 
   return w.size();
 }
 
-int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epilogue,
+static int grouped_mmq_lora_fwd_impl(const gq_lora_linear* P, int32_t nproj, int32_t epilogue,
                             const gq_grouped_fwd_args* a, void* ws, size_t ws_bytes,
                             void* stream) {
   g_err.clear();
@@ -723,7 +806,7 @@ size_t gq_grouped_mmq_lora_bwd_workspace_size(const gq_lora_linear* P, int32_t n
   return w.size();
 }
 
-int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode,
+static int grouped_mmq_lora_bwd_impl(const gq_lora_linear* P, int32_t nproj, int32_t mode,
                             const gq_grouped_bwd_args* a, void* ws, size_t ws_bytes,
                             void* stream) {
   g_err.clear();
@@ -997,7 +1080,7 @@ size_t gq_lmhead_chunked_ce_workspace_size(const gq_lora_linear* L, int64_t T, i
   return w.size();
 }
 
-int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64_t* labels,
+static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, const int64_t* labels,
                          int64_t T, int64_t chunk, int64_t ignore_index, float grad_scale,
                          float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
                          size_t ws_bytes, void* stream) {
@@ -1097,6 +1180,104 @@ int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64
   HIP_TRY(launch_colred(cr, st), "ce: dA partials");
   HIP_TRY(launch_colred_finish(P.part, nullptr, 1, cr.slots, H, r, L->scale, 1, dA, st), "ce: dA");
   return GQ_OK;
+}
+
+}  // extern "C"
+
+// Exported entry points: each runs its implementation above inside
+// traced_call (GQ_TRACE ranges, GQ_DEBUG checks; both off by default).
+extern "C" {
+
+int gq_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols, int out_dtype, void* out,
+               void* stream) {
+  return traced_call("gq_dequant", stream, nullptr,
+                    [&] { return dequant_impl(qtype, blocks, rows, cols, out_dtype, out, stream); });
+}
+
+int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
+                       float* xa, void* ws, size_t ws_bytes, void* stream) {
+  return traced_call("gq_linear_lora_fwd", stream, nullptr,
+                    [&] { return linear_lora_fwd_impl(L, x, T, y, xa, ws, ws_bytes, stream); });
+}
+
+int gq_linear_lora_bwd(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                       const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return traced_call("gq_linear_lora_bwd", stream, nullptr,
+                    [&] { return linear_lora_bwd_impl(L, x, xa, dy, T, dx, dA, dB, ws, ws_bytes, stream); });
+}
+
+int gq_linear_lora_bwd_noalloc(const gq_lora_linear* L, const uint16_t* x, const float* xa,
+                               const uint16_t* dy, int64_t T, uint16_t* dx, float* dA, float* dB,
+                               void* stream) {
+  return traced_call("gq_linear_lora_bwd_noalloc", stream, nullptr,
+                    [&] { return linear_lora_bwd_noalloc_impl(L, x, xa, dy, T, dx, dA, dB, stream); });
+}
+
+int gq_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                 int32_t* sorted, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return traced_call("gq_moe_route", stream, nullptr,
+                    [&] { return moe_route_impl(logits, T, E, k, ids, w, sorted, offsets, pos, ws, ws_bytes, stream); });
+}
+
+int gq_moe_route_bwd(const int32_t* ids, const float* w, const float* dw, int64_t T, int32_t E,
+                     int32_t k, float* dlogits, void* stream) {
+  return traced_call("gq_moe_route_bwd", stream, nullptr,
+                    [&] { return moe_route_bwd_impl(ids, w, dw, T, E, k, dlogits, stream); });
+}
+
+int gq_moe_combine_fwd(const uint16_t* o, const float* w, const int32_t* pos, int64_t T, int32_t k,
+                       int64_t H, uint16_t* y, void* stream) {
+  return traced_call("gq_moe_combine_fwd", stream, nullptr,
+                    [&] { return moe_combine_fwd_impl(o, w, pos, T, k, H, y, stream); });
+}
+
+int gq_adamw8bit_step(float* p, const float* g, uint8_t* m_codes, uint8_t* v_codes, float* m_scale,
+                      float* v_scale, int64_t n, int64_t step, float lr, float beta1, float beta2,
+                      float eps, float weight_decay, void* stream) {
+  return traced_call("gq_adamw8bit_step", stream, nullptr,
+                    [&] { return adamw8bit_step_impl(p, g, m_codes, v_codes, m_scale, v_scale, n, step, lr, beta1, beta2, eps, weight_decay, stream); });
+}
+
+int gq_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                   float* rstd, void* stream) {
+  return traced_call("gq_rmsnorm_fwd", stream, nullptr,
+                    [&] { return rmsnorm_fwd_impl(x, w, T, H, eps, y, rstd, stream); });
+}
+
+int gq_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w, const float* rstd,
+                   int64_t T, int64_t H, uint16_t* dx, void* stream) {
+  return traced_call("gq_rmsnorm_bwd", stream, nullptr,
+                    [&] { return rmsnorm_bwd_impl(dy, x, w, rstd, T, H, dx, stream); });
+}
+
+int gq_moe_combine_bwd(const uint16_t* dxrows, const int32_t* pos, int64_t T, int32_t k, int64_t H,
+                       uint16_t* dx, void* stream) {
+  return traced_call("gq_moe_combine_bwd", stream, nullptr,
+                    [&] { return moe_combine_bwd_impl(dxrows, pos, T, k, H, dx, stream); });
+}
+
+int gq_grouped_mmq_lora_fwd(const gq_lora_linear* P, int32_t nproj, int32_t epilogue,
+                            const gq_grouped_fwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return traced_call("gq_grouped_mmq_lora_fwd", stream, a && a->M > 0 ? ws : nullptr,
+                    [&] { return grouped_mmq_lora_fwd_impl(P, nproj, epilogue, a, ws, ws_bytes, stream); });
+}
+
+int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode,
+                            const gq_grouped_bwd_args* a, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return traced_call("gq_grouped_mmq_lora_bwd", stream, a && a->M > 0 ? ws : nullptr,
+                    [&] { return grouped_mmq_lora_bwd_impl(P, nproj, mode, a, ws, ws_bytes, stream); });
+}
+
+int gq_lmhead_chunked_ce(const gq_lora_linear* L, const uint16_t* h, const int64_t* labels,
+                         int64_t T, int64_t chunk, int64_t ignore_index, float grad_scale,
+                         float* loss, float* lse, uint16_t* dh, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return traced_call("gq_lmhead_chunked_ce", stream, T > 0 ? ws : nullptr,
+                    [&] { return lmhead_chunked_ce_impl(L, h, labels, T, chunk, ignore_index, grad_scale, loss, lse, dh, dA, dB, ws, ws_bytes, stream); });
 }
 
 }  // extern "C"

@@ -39,3 +39,30 @@ def read_golden_blocks(path=os.path.join(GOLDEN, "dequant_handbuilt.txt")):
 @pytest.fixture(scope="session")
 def golden_blocks():
     return read_golden_blocks()
+
+
+@pytest.fixture(autouse=True)
+def output_guard_bands(request):
+    """Every output and workspace the binding allocates in a GPU test sits
+    between guard bands of a known byte pattern, checked after the test."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    try:
+        import torch
+    except ImportError:
+        yield
+        return
+    if not torch.cuda.is_available():
+        yield
+        return
+    import quantized_base_lora_amd as gq
+    from gpu_helpers import GuardedTorch
+    guarded = GuardedTorch(torch)
+    mp = pytest.MonkeyPatch()
+    mp.setattr(gq, "torch", guarded)
+    try:
+        yield
+    finally:
+        mp.undo()
+    guarded.check()

@@ -97,3 +97,86 @@ def check_per_expert(name, got, ref, rows, tol=TOL):
         assert err <= bar, f"{name}[{e}] ({rows[e]} rows): relative Frobenius error {err:.3e} > {bar:.3e}"
         worst = max(worst, err / bar)
     return worst
+
+
+class GuardedTorch:
+    """Stands in for the ``torch`` module inside the binding during a GPU
+    test: ``torch.empty`` / ``torch.zeros`` on the GPU return views into a
+    larger buffer whose margins (GUARD bytes before and after) hold a fixed
+    byte pattern.  ``check()`` synchronises and verifies that no margin byte
+    changed, i.e. no kernel wrote outside the output or workspace it was
+    given.  Everything else is the real torch.  Allocations made while a
+    stream is being captured into a graph are passed through unguarded (the
+    pattern fill would become part of the graph)."""
+
+    GUARD = 4096
+    PATTERN = 0xA5
+    HOLD_BYTES = 8 << 30  # check and release held buffers beyond this
+
+    def __init__(self, real, device_types=("cuda",)):
+        self._t = real
+        self._types = tuple(device_types)
+        self._held = []
+        self._held_bytes = 0
+        self.checked = 0
+
+    def __getattr__(self, name):
+        return getattr(self._t, name)
+
+    def _alloc(self, size, dtype, device, zero, kw):
+        t = self._t
+        if len(size) == 1 and isinstance(size[0], (tuple, list, t.Size)):
+            size = tuple(size[0])
+        size = tuple(int(s) for s in size)
+        dev = t.device(device) if device is not None else None
+        if (dev is None or dev.type not in self._types or kw
+                or (dev.type == "cuda" and t.cuda.is_current_stream_capturing())):
+            f = t.zeros if zero else t.empty
+            return f(size, dtype=dtype, device=device, **kw)
+        dtype = dtype or t.get_default_dtype()
+        esz = t.empty(0, dtype=dtype).element_size()
+        n = 1
+        for s in size:
+            n *= s
+        nbytes = n * esz
+        G = self.GUARD
+        raw = t.empty(nbytes + 2 * G, dtype=t.uint8, device=dev)
+        raw[:G].fill_(self.PATTERN)
+        raw[G + nbytes:].fill_(self.PATTERN)
+        mid = raw[G:G + nbytes]
+        if zero:
+            mid.zero_()
+        out = mid.view(dtype).view(size)
+        self._held.append((raw, nbytes))
+        self._held_bytes += raw.numel()
+        if self._held_bytes > self.HOLD_BYTES:
+            self.check()
+        return out
+
+    def empty(self, *size, dtype=None, device=None, **kw):
+        return self._alloc(size, dtype, device, False, kw)
+
+    def zeros(self, *size, dtype=None, device=None, **kw):
+        return self._alloc(size, dtype, device, True, kw)
+
+    def check(self):
+        """Raise AssertionError if any guard byte of a held buffer changed;
+        release the held buffers."""
+        if not self._held:
+            return
+        t = self._t
+        if any(raw.is_cuda for raw, _ in self._held):
+            t.cuda.synchronize()
+        G = self.GUARD
+        bad = []
+        for raw, nbytes in self._held:
+            lo = raw[:G]
+            hi = raw[G + nbytes:]
+            nlo = int((lo != self.PATTERN).sum().item())
+            nhi = int((hi != self.PATTERN).sum().item())
+            if nlo or nhi:
+                bad.append(f"buffer of {nbytes} bytes: {nlo} bytes changed before it, {nhi} after it")
+        self.checked += len(self._held)
+        self._held = []
+        self._held_bytes = 0
+        assert not bad, "writes outside an output or workspace: " + "; ".join(bad)

@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "quantized_base_lora_amd", "libgq.so")
+LIB = os.environ.get("GQ_LIB") or os.path.join(ROOT, "quantized_base_lora_amd", "libgq.so")
 HDR = os.path.join(ROOT, "include", "gq.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgq.so not built")
