@@ -309,6 +309,66 @@ def load_counters(kernel_name, grid):
     return ent
 
 
+EXPERT_FETCH_MD = "moe_expert_fetch_q4_0_t2048_h2048_e128k8_i768.md"
+EXPERT_FETCH_REPS = 3
+
+
+def write_expert_fetch(fetch_csv, cmdline):
+    """Summary of the --expert-fetch run under rocprofv3 --pmc FETCH_SIZE:
+    bytes fetched by the grouped gate/up (SwiGLU) and down launches when all
+    128 experts own rows and when only 8 do (same 16384 rows)."""
+    import csv
+    import statistics
+    rows = [r for r in csv.DictReader(open(fetch_csv)) if r["Counter_Name"] == "FETCH_SIZE"]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    copy = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()
+            and float(r["Counter_Value"]) * 1024 > 0.5 * COPY_BYTES]
+    if not copy:
+        raise SystemExit(f"no reference copy of {COPY_BYTES} bytes found in {fetch_csv}")
+    scale = statistics.median(copy) * 1024 / COPY_BYTES
+    mmq = [r for r in rows if "gemm_kernel" in r["Kernel_Name"] or "skinny" in r["Kernel_Name"]
+           or "wide" in r["Kernel_Name"]]
+    # dispatch order: per case, EXPERT_FETCH_REPS x (gate/up launch, down launch)
+    want = 2 * 2 * EXPERT_FETCH_REPS
+    if len(mmq) != want:
+        raise SystemExit(f"expected {want} MMQ dispatches, found {len(mmq)}")
+    res = {}
+    for ci, case in enumerate(("all 128 experts active", "8 experts active")):
+        part = mmq[ci * 2 * EXPERT_FETCH_REPS:(ci + 1) * 2 * EXPERT_FETCH_REPS]
+        for li, launch in enumerate(("gate/up + SwiGLU", "down")):
+            vals = [float(r["Counter_Value"]) * 1024 / scale for r in part[li::2]]
+            res[(case, launch)] = (statistics.median(vals), part[li]["Kernel_Name"])
+    bs = 18  # Q4_0 block bytes
+    wbytes = {"gate/up + SwiGLU": 2 * 768 * (2048 // 32) * bs, "down": 2048 * (768 // 32) * bs}
+    path = os.path.join(ROOT, "profiles", EXPERT_FETCH_MD)
+    with open(path, "w") as fh:
+        fh.write("# Idle experts' blocks are not fetched: grouped MMQ launches of the Q4_0 MoE layer\n\n")
+        fh.write("T 2048, H 2048, I 768, 128 experts, top-8: 16384 routed rows in both cases.  Case A: every "
+                 "expert owns 128 rows.  Case B: experts 0, 16, ..., 112 own 2048 rows each, the other 120 "
+                 "experts none.  The weights, activations and rows are the same; only the offsets differ.\n\n")
+        fh.write("Counter pass (repo root on the GPU box, TMPDIR=/tmp, run from /tmp):\n\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_experts -o run -- "
+                 "python3 <repo>/bench.py --expert-fetch\n\n")
+        fh.write(f"Summary written by: `{cmdline}`\n\n")
+        fh.write(f"FETCH_SIZE (KiB per dispatch) scaled by a {COPY_BYTES >> 20} MiB device copy in the same "
+                 f"process (factor {scale:.4f}); median of {EXPERT_FETCH_REPS} dispatches.\n\n")
+        fh.write("| case | launch | kernel | fetched MB | weight bytes of the active experts (MB) |\n"
+                 "|---|---|---|---|---|\n")
+        for (case, launch), (v, kname) in res.items():
+            nact = 128 if case.startswith("all") else 8
+            fh.write(f"| {case} | {launch} | `{kname}` | {v / 1e6:.1f} | {nact * wbytes[launch] / 1e6:.1f} |\n")
+        for launch in ("gate/up + SwiGLU", "down"):
+            a = res[("all 128 experts active", launch)][0]
+            b = res[("8 experts active", launch)][0]
+            fh.write(f"\n- {launch}: case B fetches {b / 1e6:.1f} MB in all, less than the "
+                     f"{128 * wbytes[launch] / 1e6:.1f} MB that the blocks of all 128 experts occupy, so the "
+                     f"blocks of its 120 idle experts ({120 * wbytes[launch] / 1e6:.1f} MB) are not fetched; "
+                     f"case A fetches {(a - b) / 1e6:.1f} MB more than case B (not exactly the idle weights: the "
+                     f"activation reads differ too, each expert of case B gathering every token).")
+        fh.write("\n")
+    log(open(path).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -330,6 +390,11 @@ def main():
                          "--output-format csv run (files run_kernel_stats.csv, run_kernel_trace.csv)")
     ap.add_argument("--counters-from", nargs=5, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "OUT_MD", "TITLE"),
                     help="write a per-kernel counter summary from three rocprofv3 --pmc runs and exit")
+    ap.add_argument("--expert-fetch", action="store_true",
+                    help="run the grouped Q4_0 MoE launches with all / 8 experts active and exit "
+                         "(for a rocprofv3 --pmc FETCH_SIZE pass)")
+    ap.add_argument("--expert-fetch-from", metavar="FETCH_CSV",
+                    help="write the idle-expert fetch summary from that counter pass and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/mmq_traffic.json from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
@@ -337,6 +402,9 @@ def main():
         args.all = True
     if args.traffic_from:
         write_traffic(*args.traffic_from, " ".join(sys.argv))
+        return
+    if args.expert_fetch_from:
+        write_expert_fetch(args.expert_fetch_from, " ".join(sys.argv))
         return
     if args.counters_from:
         write_counters(*args.counters_from, " ".join(sys.argv))
@@ -382,6 +450,31 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.expert_fetch:
+        if not args.copy_probe:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+            torch.empty_like(src).copy_(src)
+            del src
+        mc = synth.MOE_Q4_0_T2048
+        minp = synth.make_moe(mc)
+        E, H, I, s = mc.E, mc.H, mc.I, float(minp["scale"])
+        mk = lambda w, a, b, no, ni: gq.Proj(mc.qtype, no, ni, u8(w), f32(a), f32(b), s, E)
+        gate, up = mk(minp["wg"], minp["ag"], minp["bg"], I, H), mk(minp["wu"], minp["au"], minp["bu"], I, H)
+        down = mk(minp["wd"], minp["ad"], minp["bd"], H, I)
+        x = bf(minp["x"])
+        M = mc.T * mc.k
+        gather = torch.arange(M, dtype=torch.int32, device=dev) % mc.T * mc.k  # token t's rows, k-major
+        for case, counts in (("all", np.full(E, M // E)),
+                             ("eight", np.where(np.arange(E) % 16 == 0, M // 8, 0))):
+            offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+            log(f"[bench] expert fetch: case {case}, active experts {int((counts > 0).sum())}")
+            for _ in range(EXPERT_FETCH_REPS):
+                h, _, _, _ = gq.grouped_mmq_lora_fwd([gate, up], gq.EPI_SWIGLU, x, gather, mc.k, offs, M)
+                gq.grouped_mmq_lora_fwd([down], gq.EPI_NONE, h, None, 1, offs, M)
+            torch.cuda.synchronize()
+        log("[bench] expert fetch: done")
+        return
 
     spreads = {}
 

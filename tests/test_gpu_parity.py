@@ -291,6 +291,52 @@ def test_moe_layer(T, H, I, E, k, qtype, r, zipf):
         assert np.all(got[idle] == 0.0), f"{n}: idle experts must get exact zeros"
 
 
+@pytest.mark.parametrize("T,qtype", [(40, 1), (300, 0), (24, 2)])
+def test_idle_experts_blocks_unused(T, qtype):
+    """Only experts that own rows touch their blocks: every idle expert's
+    blocks get NaN scales, and the whole layer (forward and backward) must
+    give bitwise the same results as with clean blocks.  (The counter side,
+    that those blocks are not even fetched, is the grouped-launch FETCH_SIZE
+    profile.)"""
+    E, k, H, I, r = 16, 2, 128, 128, 4
+    cfg = synth.MoECfg("t", T=T, H=H, I=I, E=E, k=k, qtype=qtype, rank=r, alpha=8, seed=T)
+    inp = synth.make_moe(cfg, large_adapter=True)
+    active = [1, 6, 7, 12]
+    idle = [e for e in range(E) if e not in active]
+    inp["logits"][:, idle] = -1e4  # never among the top k
+    say("idle experts", T, qtype, "active", active)
+    runs = []
+    for poison in (False, True):
+        bl = {n: np.array(inp[n], copy=True) for n in ("wg", "wu", "wd")}
+        if poison:
+            for n in bl:
+                blocks = bl[n].reshape(E, -1, synth.BLOCK_BYTES[qtype])
+                blocks[idle, :, 0] = 0x00  # fp16 scale d = NaN (0x7E00)
+                blocks[idle, :, 1] = 0x7E
+                if qtype == 2:
+                    blocks[idle, :, 2] = 0x00  # and min m = NaN
+                    blocks[idle, :, 3] = 0x7E
+        s = float(inp["scale"])
+        wts = gq.MoEWeights(gq.Proj(qtype, I, H, u8_dev(bl["wg"]), f32_dev(inp["ag"]), f32_dev(inp["bg"]), s, E),
+                            gq.Proj(qtype, I, H, u8_dev(bl["wu"]), f32_dev(inp["au"]), f32_dev(inp["bu"]), s, E),
+                            gq.Proj(qtype, H, I, u8_dev(bl["wd"]), f32_dev(inp["ad"]), f32_dev(inp["bd"]), s, E))
+        x, dy, lg = bf16_dev(inp["x"]), bf16_dev(inp["dy"]), f32_dev(inp["logits"])
+        y, saved = gq.moe_ffn_fwd(wts, x, lg, k)
+        g = gq.moe_ffn_bwd(wts, x, dy, saved, k, E)
+        torch.cuda.synchronize()
+        offs = host(saved["offsets"])
+        assert set(np.flatnonzero(np.diff(offs))) == set(active)
+        out = {"y": y, "h": saved["h"], "o": saved["o"]}
+        out.update({n: g[n] for n in ("dx", "dlogits", "dw", "dg", "du", "dA_d", "dB_d", "dA_g", "dB_g",
+                                      "dA_u", "dB_u")})
+        runs.append({n: host(t) for n, t in out.items()})
+    clean, poisoned = runs
+    for n in clean:
+        assert np.isfinite(clean[n]).all(), n
+        say("bitwise equal:", n)
+        same_f32_bits(np.asarray(poisoned[n], np.float32), np.asarray(clean[n], np.float32))
+
+
 def test_grouped_offsets_checked_on_device():
     """Inconsistent expert offsets (decreasing, not ending at M) set the
     workspace's error word and no row is processed; consistent offsets on
