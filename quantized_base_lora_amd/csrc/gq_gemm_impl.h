@@ -51,8 +51,10 @@ struct Geom {
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int A_CHUNKS = BM * BK / 8 / NTHR;  // 16-byte chunks per thread
   // weight tile in LDS (bf16 elements): NT [BN][LDK] (k contiguous);
-  // NN [64][PN] row-major (columns contiguous), read with transposing loads
-  static constexpr int PN = BN + 16;
+  // NN [64][PN] row-major (columns contiguous), read with transposing loads;
+  // unpadded rows whose 16-byte chunks are XOR-swizzled by the row (see
+  // nn_chunk below)
+  static constexpr int PN = BN;
   static constexpr int B_TILE = NN ? BK * PN : BN * LDK;
   static constexpr int SMEM_MAIN = 2 * (BM * LDK + B_TILE) * 2;
   static constexpr int ZP = BN + 1;  // pitch (floats) of the staged epilogue tile
@@ -82,6 +84,16 @@ __device__ __forceinline__ uint32_t opaque_mask(bool keep) {
   asm volatile("" : "+v"(m));
   return m;
 }
+
+// NN weight tile: the 16-byte chunk c (8 columns) of reduction row `row` is
+// stored at chunk c ^ (5 * (row & 3)).  With 256-byte rows this makes both
+// LDS access patterns of the tile free of bank conflicts (64 banks of 4
+// bytes): a 16-lane pass of the decode's 16-byte writes covers rows R..R+3
+// (R % 4 == 0) x 4 blocks at one chunk position q, whose swizzled chunks
+// 4(kb ^ (row&3)) + (q ^ (row&3)) are all distinct; a 32-lane pass of the
+// transposing 8-byte reads covers rows t (mod 4) x chunks base+0..3, whose
+// swizzled chunks (base/4 ^ t, tc ^ t) are all distinct.
+__device__ __forceinline__ int nn_chunk(int row, int c) { return c ^ (5 * (row & 3)); }
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
 template <int I> struct IntC { static constexpr int value = I; };
@@ -299,6 +311,14 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   // L ends up with rows 8*(L/32) .. +8 of column L % 32 -- the MFMA B layout.
   const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // this lane's element offset of subtile b in the swizzled tile, at rows
+  // tr_row + 16kk (+4): the swizzle depends on row & 3 only, equal for all
+  int tr_off[TN];
+#pragma unroll
+  for (int b = 0; b < TN; ++b) {
+    const int col = wn * WTN + b * 32 + tr_col;
+    tr_off[b] = tr_row * PN + nn_chunk(tr_row, col >> 3) * 8 + (col & 7);
+  }
   // NA = the wave's 32-row sub-tiles that hold rows of the tile (a partly
   // filled MoE tile leaves whole sub-tiles empty: no MFMAs for them)
   auto compute = [&](int cur, auto na_c) {
@@ -318,7 +338,7 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         if constexpr (NN) {
           typedef short v4i16 __attribute__((ext_vector_type(4)));
           typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-          const uint16_t* base = B + (kk * 16 + tr_row) * PN + wn * WTN + b * 32 + tr_col;
+          const uint16_t* base = B + kk * 16 * PN + tr_off[b];
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16*)(__attribute__((address_space(3))) void*)(base));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -476,11 +496,14 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         decode_block_fast<QT>(wr, w);
         // NT: row w_it_row of the [n][k] tile, k = kb*32 .. +32
         // NN: reduction row w_it_row of the row-major tile, columns kb*32 .. +32
-        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * (NN ? PN : LDK) + w_it_kb[i] * 32);
+        uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * (NN ? PN : LDK));
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
-                              pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
+        for (int q = 0; q < 4; ++q) {
+          const int c = w_it_kb[i] * 4 + q;
+          dst[NN ? nn_chunk(w_it_row[i], c) : c] =
+              make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
+                         pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
+        }
       }
     };
 
