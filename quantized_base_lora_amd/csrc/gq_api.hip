@@ -1031,6 +1031,7 @@ struct CeWs {
   float* zlab;
   float* term;
   uint16_t* G;
+  uint16_t* G2;  // second gradient buffer when chunks are paired, else nullptr
   float* dh_acc;
   float* part_GB;
   float* part_dB;
@@ -1068,6 +1069,13 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     p.GB = w.take<float>(T * r);
     p.part = w.take<float>(colred_slots(T, pick_rc(T, H, (int)r, 1), 1) * H * r);
     p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), C, true);
+    // two or more chunks with 128-row tiles on both passes: chunk c's
+    // gradient tiles share a launch with chunk c-1's dh tiles, which needs a
+    // second gradient buffer
+    const int64_t nchunks = (V + chunk - 1) / chunk;
+    const int nce = cdiv(T, 128) * cdiv(C, TILE_BN);
+    if (nchunks >= 2 && p.tc_bwd == TILE_128x128 && tile_bm(p.tc_dh) == 128 && nce % 8 == 0)
+      p.G2 = w.take<uint16_t>(T * p.ldG);
   }
   return p;
 }
@@ -1144,9 +1152,19 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
           "ce: log-sum-exp merge, loss");
   if (!grad) return GQ_OK;
 
+  // Chunk after chunk: the gradient tiles write G for the chunk's vocabulary
+  // rows (plus the G.B and dB partials), the dh tiles accumulate G deq(W) of
+  // the chunk into dh_acc (chunk order fixed: deterministic).  With two
+  // gradient buffers, chunk c's gradient tiles and chunk c-1's dh tiles
+  // run in one launch.
+  const bool pair = P.G2 != nullptr;
+  GemmArgs dprev = gemm_defaults();
+  bool have_prev = false;
   int ntile_base = 0;
-  for (int64_t c0 = 0; c0 < V; c0 += chunk) {
+  int ci = 0;
+  for (int64_t c0 = 0; c0 < V; c0 += chunk, ++ci) {
     const int C = (int)((V - c0) < chunk ? V - c0 : chunk);
+    uint16_t* Gc = (pair && (ci & 1)) ? P.G2 : P.G;
     GemmArgs b = gemm_defaults();
     b.M = T; b.N = C; b.K = H;
     b.a0 = h; b.lda = H;
@@ -1154,22 +1172,35 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
     b.ntiles = cdiv(C, TILE_BN);
     b.mtiles = cdiv(T, tile_bm(P.tc_bwd));
     b.s = L->scale; b.r = r; b.lB0 = L->B; b.rv0 = P.xa;
-    b.o0 = P.G; b.ldo = P.ldG;
+    b.o0 = Gc; b.ldo = P.ldG;
     b.f1 = P.part_GB; b.f2 = P.part_dB;
     b.labels = labels; b.ignore_index = ignore_index; b.lse = lse; b.coef = grad_scale;
     b.nvalid = P.nvalid; b.V = (int)V; b.ntile_base = ntile_base;
-    HIP_TRY(launch_gemm(L->qtype, EPI_CE_BWD, P.tc_bwd, b, st), "ce: gradient tile pass");
     ntile_base += b.ntiles;
 
     GemmArgs d = gemm_defaults();
     d.M = T; d.N = H; d.K = C;
-    d.a0 = P.G; d.lda = P.ldG;
+    d.a0 = Gc; d.lda = P.ldG;
     d.w0 = wb; d.w_rowbytes = rowbytes(L); d.w_nb = H / 32; d.w_rows = C; d.w_row0 = (int)c0;
     d.ntiles = cdiv(H, TILE_BN);
     d.mtiles = cdiv(T, tile_bm(P.tc_dh));
     d.f0 = P.dh_acc; d.ldf = H; d.accum = c0 > 0;
-    HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, d, st), "ce: dh pass");
+    if (!pair) {
+      HIP_TRY(launch_gemm(L->qtype, EPI_CE_BWD, P.tc_bwd, b, st), "ce: gradient tile pass");
+      HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, d, st), "ce: dh pass");
+      continue;
+    }
+    if (have_prev) {
+      GemmArgs dk = dprev;
+      dk.mtiles = cdiv(T, 128);  // one group of four waves per 128 x 128 tile
+      HIP_TRY(launch_ce_bwd_dh(L->qtype, b, dk, st), "ce: gradient tiles + previous chunk's dh tiles");
+    } else {
+      HIP_TRY(launch_gemm(L->qtype, EPI_CE_BWD, P.tc_bwd, b, st), "ce: gradient tile pass");
+    }
+    dprev = d;
+    have_prev = true;
   }
+  if (pair && have_prev) HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, dprev, st), "ce: dh pass");
   HIP_TRY(launch_sum_parts(P.part_GB, P.ntiles_bwd, T, r, 1.f, P.GB, st), "ce: G B");
   HIP_TRY(launch_sum_parts(P.part_dB, P.mt, V, r, L->scale, dB, st), "ce: dB");
   HIP_TRY(launch_ce_final_dh(P.dh_acc, P.GB, L->A, T, H, r, L->scale, dh, st), "ce: dh");

@@ -11,6 +11,7 @@ hipError_t launch_gemm_q4_0_nt(int epi, int tilecfg, const GemmArgs& a, hipStrea
 hipError_t launch_gemm_q4_0_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_q2_dm_nt(int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_q2_dm_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
+hipError_t launch_ce_bwd_dh_q(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st);
 
 namespace {
 // optional timing events recorded around every MMQ launch of this thread
@@ -39,6 +40,16 @@ hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipSt
     if (e != hipSuccess) return e;
   }
   const hipError_t e = dispatch(qtype, epi, tilecfg, a, st);
+  if (e == hipSuccess && g_prof_stop) return hipEventRecord(g_prof_stop, st);
+  return e;
+}
+
+hipError_t launch_ce_bwd_dh(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st) {
+  if (g_prof_start) {
+    const hipError_t e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch_ce_bwd_dh_q(qtype, ce, dh, st);
   if (e == hipSuccess && g_prof_stop) return hipEventRecord(g_prof_stop, st);
   return e;
 }

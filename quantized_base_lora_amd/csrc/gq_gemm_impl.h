@@ -214,9 +214,12 @@ __device__ __forceinline__ void mfma_interleave() {
   }
 }
 
+// The tile GEMM of one workgroup: `block` of `nblocks` (the workgroup's
+// position in its launch, or in its part of a launch that runs two kinds of
+// tiles), `smem` the workgroup's LDS (at least Geom::SMEM bytes).
 template <int QT, int EPI, int BM, int BN, int KS>
-__global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
-    const GemmArgs p) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, const int block,
+                                          const int nblocks) {
   constexpr bool NN = EPI >= EPI_LIN_BWD;
   using G = Geom<BM, BN, epi_stages(EPI), NN, KS>;
   constexpr int BS = QTraits<QT>::BS;
@@ -228,7 +231,6 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
 
   // group `grp` of four waves takes k-steps grp, grp + KS, grp + 2KS, ...
   const int grp = KS > 1 ? (int)(threadIdx.x / NTHR) : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem + grp * G::SMEM_MAIN);
   uint16_t* Bs = As + 2 * BM * LDK;
   constexpr int B_TILE = G::B_TILE, PN = G::PN;
@@ -255,12 +257,12 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
   int mslot, ntile;
   if (p.offsets) {
     const int used = p.tile_start[p.E] * p.ntiles;
-    if ((int)blockIdx.x >= used) return;
-    const int bid = xcd_run(blockIdx.x, used);
+    if (block >= used) return;
+    const int bid = xcd_run(block, used);
     mslot = bid / p.ntiles;
     ntile = bid - mslot * p.ntiles;
   } else {
-    const int bid = xcd_run(blockIdx.x, gridDim.x);
+    const int bid = xcd_run(block, nblocks);
     constexpr int GM = 4;
     const int gsize = GM * p.ntiles;
     const int g = bid / gsize;
@@ -1066,6 +1068,33 @@ __global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2
         reductions(IntC<16>{});
     }
   }
+}
+
+template <int QT, int EPI, int BM, int BN, int KS>
+__global__ __launch_bounds__(NTHR * KS, (KS > 1 || BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
+    const GemmArgs p) {
+  using G = Geom<BM, BN, epi_stages(EPI), EPI >= EPI_LIN_BWD, KS>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
+  gemm_body<QT, EPI, BM, BN, KS>(p, smem, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// LM-head backward, two chunks in one launch: the first `nce` workgroups
+// are the gradient tiles of chunk c (EPI_CE_BWD, writing one G buffer), the
+// rest the dh tiles of chunk c-1 (EPI_DH_ACC, reading the other G buffer).
+// The two kinds share nothing, so the dh tiles fill the CUs while the
+// gradient tiles' epilogues run, instead of two single-round launches
+// back to back.
+template <int QT>
+__global__ __launch_bounds__(NTHR, 2) void ce_bwd_dh_kernel(const GemmArgs pce, const GemmArgs pdh,
+                                                            const int nce) {
+  using GC = Geom<128, 128, true, false, 1>;
+  using GD = Geom<128, 128, false, true, 1>;
+  constexpr int SM = GC::SMEM > GD::SMEM ? GC::SMEM : GD::SMEM;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SM];
+  if ((int)blockIdx.x < nce)
+    gemm_body<QT, EPI_CE_BWD, 128, 128, 1>(pce, smem, (int)blockIdx.x, nce);
+  else
+    gemm_body<QT, EPI_DH_ACC, 128, 128, 1>(pdh, smem, (int)blockIdx.x - nce, (int)gridDim.x - nce);
 }
 
 template <int QT, int EPI>
