@@ -269,10 +269,12 @@ int nn_tile_bn(int tc) { (void)tc; return TILE_BN; }  // 128 for the tile and th
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
 // Dense forward launches with Q8_0 / Q4_0 weights and K % 64 == 0 run the
-// 256 x 192 wide tiles when those fill the chip: at least 192 tiles, and the
-// last round of one tile per CU at least three quarters full.
+// 256 x 192 wide tiles when those fill the chip: their rows at least three
+// quarters used (clamped rows cost as much as real ones), at least 192
+// tiles, and the last round of one tile per CU at least three quarters full.
 bool wide_pays(int qtype, int64_t M, int64_t N, int64_t K) {
   if (qtype == GQ_Q2_DM || K % GEMM_BK) return false;
+  if (M * 4 < (int64_t)cdiv(M, WIDE_BM) * WIDE_BM * 3) return false;
   const int64_t tiles = (int64_t)cdiv(M, WIDE_BM) * cdiv(N, WIDE_BN);
   if (tiles < 192) return false;
   const int64_t rounds = (tiles + 255) / 256;
@@ -1051,6 +1053,9 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
   p.xa = w.take<float>(T * r);
   const int nt_v = cdiv(V, TILE_BN);
   p.tc_fwd = pick_fwd_tile(T, T, nt_v, H, aligned(L->w_blocks, 16));
+  // 256 x 192 tiles when they fill the chip (part_ml, sized for 128-column
+  // tiles, holds their fewer partials)
+  if (!tile_skinny(p.tc_fwd) && wide_pays(L->qtype, T, V, H)) p.tc_fwd = TILE_WIDE;
   p.part_ml = w.take<float>((int64_t)nt_v * T * 2);
   p.zlab = w.take<float>(T);
   p.term = w.take<float>(T);
@@ -1073,8 +1078,7 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     // gradient tiles share a launch with chunk c-1's dh tiles, which needs a
     // second gradient buffer
     const int64_t nchunks = (V + chunk - 1) / chunk;
-    const int nce = cdiv(T, 128) * cdiv(C, TILE_BN);
-    if (nchunks >= 2 && p.tc_bwd == TILE_128x128 && tile_bm(p.tc_dh) == 128 && nce % 8 == 0)
+    if (nchunks >= 2 && p.tc_bwd == TILE_128x128 && tile_bm(p.tc_dh) == 128)
       p.G2 = w.take<uint16_t>(T * p.ldG);
   }
   return p;
@@ -1141,7 +1145,7 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
   g.M = T; g.N = (int)V; g.K = H;
   g.a0 = h; g.lda = H;
   g.w0 = wb; g.w_rowbytes = rowbytes(L); g.w_nb = H / 32; g.w_rows = (int)V; g.w_row0 = 0;
-  g.ntiles = cdiv(V, tile_bn(P.tc_fwd));
+  g.ntiles = cdiv(V, P.tc_fwd == TILE_WIDE ? WIDE_BN : tile_bn(P.tc_fwd));
   g.mtiles = cdiv(T, tile_bm(P.tc_fwd));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = P.xa;
   g.f0 = P.part_ml; g.f1 = P.zlab; g.labels = labels; g.ignore_index = ignore_index;

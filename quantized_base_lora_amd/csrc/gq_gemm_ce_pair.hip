@@ -6,7 +6,7 @@
 namespace gq {
 hipError_t launch_ce_bwd_dh_q(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st) {
   const int nce = ce.mtiles * ce.ntiles, ndh = dh.mtiles * dh.ntiles;
-  if (nce <= 0 || ndh <= 0 || nce % 8) return hipErrorInvalidValue;
+  if (nce <= 0 || ndh <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(nce + ndh));
   switch (qtype) {
     case QT_Q8_0: hipLaunchKernelGGL(ce_bwd_dh_kernel<QT_Q8_0>, grid, dim3(NTHR), 0, st, ce, dh, nce); break;

@@ -1102,16 +1102,16 @@ hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st);
 template <int QT, int EPI>
 hipError_t launch_skinny_nn(int rg, const GemmArgs& a, hipStream_t st);
 
-template <int QT>
-hipError_t launch_wide_lin(const GemmArgs& a, hipStream_t st);
+template <int QT, int EPI>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t st);
 
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
   if (tilecfg == TILE_WIDE) {
-    if constexpr (EPI == EPI_LIN && QT != QT_Q2_DM) {
+    if constexpr ((EPI == EPI_LIN || EPI == EPI_CE_FWD) && QT != QT_Q2_DM) {
       if (a.offsets || a.gather || a.K % GEMM_BK) return hipErrorInvalidValue;
-      return launch_wide_lin<QT>(a, st);
+      return launch_wide<QT, EPI>(a, st);
     }
     return hipErrorInvalidValue;
   }

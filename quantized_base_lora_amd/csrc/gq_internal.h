@@ -120,8 +120,7 @@ constexpr int GEMM_BK = 64;
 
 hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st);
 // One launch of EPI_CE_BWD tiles (`ce`, 128 x 128, TILE_128x128) followed by
-// EPI_DH_ACC tiles (`dh`, 128 x 128, one group of four waves); the number of
-// gradient tiles must be a multiple of 8.
+// EPI_DH_ACC tiles (`dh`, 128 x 128, one group of four waves).
 hipError_t launch_ce_bwd_dh(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st);
 // thread-local timing events recorded around each launch_gemm (nullptr: off)
 void set_profile_events(hipEvent_t start, hipEvent_t stop);

@@ -1,5 +1,6 @@
 // Wide-tile MMQ for large dense forward launches (the reduction runs along
-// the weight's block dimension): 256 x 192 output tiles on 512 threads.
+// the weight's block dimension): 256 x 192 output tiles on 512 threads, for
+// the linear forward and the LM head's logits pass.
 //
 // The tile GEMM in gq_gemm_impl.h decodes each 64-deep weight slice for 128
 // activation rows; here every decoded slice feeds 256 rows, which halves the
@@ -34,6 +35,7 @@ constexpr int SMEM_MAIN = (2 * A_ST + 2 * B_ST) * 2;
 constexpr int SP = WTN + 8;  // staged epilogue row pitch (bf16)
 constexpr int SMEM_EPI = 8 * WTM * SP * 2;
 constexpr int SMEM = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
+static_assert(BM * 2 * 16 * 8 <= SMEM, "CE partial pairs fit the LDS");
 
 // A quarter of a block: its fp16 scale (low 16 bits of hdr) and payload
 // bytes [q*NB, q*NB + NB) with NB = 4 (Q4_0) or 8 (Q8_0).
@@ -89,10 +91,24 @@ __device__ __forceinline__ void store_quarter(uint16_t* base, int qq, const RawQ
   }
 }
 
-// Dense forward: out[p][n] = sum_k a0[p][k] deq(W)[n][k] + s * rv0[p] . lB0[n]
-// (EPI_LIN).  Geometry from GemmArgs: M rows, N = w_rows output columns, K.
-template <int QT>
-__global__ __launch_bounds__(NTHR, 1) void wide_lin_kernel(const GemmArgs p) {
+// Merge of two online (max, sum of exp) pairs into (m, l).
+__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  l = (m == -INFINITY ? 0.f : l * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : l2 * __expf(m2 - mn));
+  m = mn;
+}
+
+// Dense forward: z[p][n] = sum_k a0[p][k] deq(W)[n][k] + s * rv0[p] . lB0[n].
+// Geometry from GemmArgs: M rows, N = w_rows output columns, K.
+//   EPI_LIN:    z stored as bf16 (o0, ldo).
+//   EPI_CE_FWD: z never leaves the chip: per row and tile the online
+//               (max, sum exp) over the tile's columns below w_rows goes to
+//               f0[(tile column index) * M + row], and the row's label logit,
+//               when the label column is in this tile, to f1[row].
+template <int QT, int EPI>
+__global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
+  static_assert(EPI == EPI_LIN || EPI == EPI_CE_FWD, "wide epilogues");
   constexpr int BS = QTraits<QT>::BS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -264,6 +280,62 @@ __global__ __launch_bounds__(NTHR, 1) void wide_lin_kernel(const GemmArgs p) {
     }
   }
 
+  if constexpr (EPI == EPI_CE_FWD) {
+    // Each lane merges its three columns of a row, then the adjacent lane's
+    // (xor 1); the 16 pairs of each wave's half row go through LDS
+    // ([256 rows][2 wave columns][16] pairs, 64 KB), and two threads per
+    // row merge them in a fixed order.
+    __syncthreads();  // every wave is done reading the operand stages
+    float2* P = reinterpret_cast<float2*>(smem);
+    const int c0 = n0 + wn * WTN + (lane & 31);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int64_t pr = r0 + lr;
+        float m = -INFINITY, l = 0.f;
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          if (c0 + b * 32 < p.w_rows) m = fmaxf(m, acc[a][b][v]);
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            if (c0 + b * 32 < p.w_rows) l += __expf(acc[a][b][v] - m);
+        }
+        if (pr < p.M) {
+          const int64_t lab = p.labels[pr];
+          const int64_t lc = lab - c0;
+          if (lab != p.ignore_index && lab >= 0 && lab < p.V && lc >= 0 && lc % 32 == 0 && lc / 32 < TN) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+              if (lc == 32 * b) p.f1[pr] = acc[a][b][v];
+          }
+        }
+        const float m2 = __shfl_xor(m, 1), l2 = __shfl_xor(l, 1);
+        if ((lane & 1) == 0) {
+          ml_merge(m, l, m2, l2);
+          P[(lr * 2 + wn) * 16 + ((lane & 31) >> 1)] = make_float2(m, l);
+        }
+      }
+    __syncthreads();
+    const int row = tid >> 1, h = tid & 1;
+    float m = -INFINITY, l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float2 q = P[(row * 2 + h) * 16 + i];
+      ml_merge(m, l, q.x, q.y);
+    }
+    const float m2 = __shfl_xor(m, 1), l2 = __shfl_xor(l, 1);
+    if (h == 0 && r0 + row < p.M) {
+      ml_merge(m, l, m2, l2);  // wave column 0, then 1
+      float* dst = p.f0 + ((int64_t)(p.ntile_base + nt) * p.M + r0 + row) * 2;
+      dst[0] = m;
+      dst[1] = l;
+    }
+    return;
+  }
+
   // ---- epilogue: the wave's 64 x 96 tile through its own LDS region (rows
   // of 104 bf16), stored as 16-byte row pieces (12 lanes per row) when the
   // output rows allow it, else one 2-byte store per value
@@ -297,12 +369,12 @@ __global__ __launch_bounds__(NTHR, 1) void wide_lin_kernel(const GemmArgs p) {
 }  // namespace wide
 
 namespace {
-// Launch of the wide-tile forward (EPI_LIN, dense, Q8_0 / Q4_0, K % 64 == 0);
-// declared beside launch_q in gq_gemm_impl.h.
-template <int QT>
-hipError_t launch_wide_lin(const GemmArgs& a, hipStream_t st) {
+// Launch of the wide-tile forward (EPI_LIN or EPI_CE_FWD, dense, Q8_0 /
+// Q4_0, K % 64 == 0); declared beside launch_q in gq_gemm_impl.h.
+template <int QT, int EPI>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
-  hipLaunchKernelGGL((wide::wide_lin_kernel<QT>), grid, dim3(wide::NTHR), 0, st, a);
+  hipLaunchKernelGGL((wide::wide_kernel<QT, EPI>), grid, dim3(wide::NTHR), 0, st, a);
   return hipGetLastError();
 }
 }  // namespace

@@ -376,6 +376,10 @@ HEAD_CASES = [
     (40, 96, 701, 256, 1, 0.1),
     (150, 160, 2000, 512, 0, 0.0),
     (16, 256, 1001, 333, 2, 0.1),
+    # enough 256 x 192 tiles for the wide logits pass (ragged rows and
+    # vocabulary tile)
+    (600, 128, 30000, 8192, 1, 0.1),
+    (720, 64, 26000, 26000, 0, 0.0),
 ]
 
 
