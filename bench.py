@@ -64,7 +64,7 @@ def gemm_source_hash():
     """Hash of the MMQ kernel source with comments and blank lines dropped,
     so that counters stay attributed to the kernel until its code changes."""
     h = hashlib.sha256()
-    for f in ("gq_gemm_impl.h", "gq_dev.h"):
+    for f in ("gq_gemm_impl.h", "gq_wide_impl.h", "gq_skinny_impl.h", "gq_dev.h"):
         with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", f)) as fh:
             for line in fh:
                 code = line.split("//", 1)[0].strip()
@@ -93,9 +93,11 @@ COPY_BYTES = 256 << 20
 # the two MMQ launches of the linear step: kernel name fragment, threads per
 # launch (tiles x workgroup size), key in mmq_traffic.json
 MMQ_LAUNCHES = (
-    ("gemm_kernel<1, 0, 128, 128, 1>", 768 * 256, "mmq_nt_lin_q4_0_t2048_2048x6144"),
+    ("wide::wide_kernel<1, 0>", 256 * 512, "mmq_nt_lin_q4_0_t2048_2048x6144"),
     ("gemm_kernel<1, 4, 128, 128, 2>", 256 * 512, "mmq_nn_lin_bwd_q4_0_t2048_2048x6144"),
 )
+# kernels whose counters are kept in profiles/mmq_counters.json
+MMQ_KERNEL_TAGS = ("gemm_kernel", "skinny", "wide_kernel", "ce_bwd_dh_kernel")
 
 
 def moe_layer_bytes(T, H, I, E, k, r, qtype_bytes, active):
@@ -135,7 +137,9 @@ def write_kernel_summary(csv_dir, out_md, title):
                  f"python3 <repo>/bench.py {title}\n\n")
         fh.write("gemm_kernel<qtype, epilogue, BM, BN, k-groups>: qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, "
                  "1 SwiGLU, 2 CE logits, 3 CE gradient, 4 linear backward (dX), 5 SwiGLU backward, "
-                 "6 gate/up backward, 7 dh accumulate.\n\n")
+                 "6 gate/up backward, 7 dh accumulate; wide::wide_kernel<qtype, epilogue>: the 256 x 192 forward "
+                 "tile; ce_bwd_dh_kernel<qtype>: one vocabulary chunk's CE-gradient tiles with the previous "
+                 "chunk's dh tiles.\n\n")
         fh.write("## rocprofv3 --stats (run_kernel_stats.csv)\n\n| kernel | calls | avg us | min us | max us | % |\n"
                  "|---|---|---|---|---|---|\n")
         for r in stats[:30]:
@@ -277,7 +281,9 @@ def write_counters(sq_csv, fetch_csv, write_csv, out_md, title, cmdline):
                  f"(FETCH {scale['FETCH_SIZE']:.4f}, WRITE {scale['WRITE_SIZE']:.4f}).  Durations are under the "
                  "profiler (kernels serialised).  Kernel template arguments: gemm_kernel<qtype, epilogue, BM, BN, "
                  "k-groups> (qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, 1 SwiGLU, 2 CE logits, 3 CE gradient, "
-                 "4 linear backward (dX), 5 SwiGLU backward, 6 gate/up backward, 7 dh accumulate).\n\n")
+                 "4 linear backward (dX), 5 SwiGLU backward, 6 gate/up backward, 7 dh accumulate); "
+                 "wide::wide_kernel<qtype, epilogue> the 256 x 192 forward tile; ce_bwd_dh_kernel<qtype> one "
+                 "vocabulary chunk's CE-gradient tiles with the previous chunk's dh tiles.\n\n")
         fh.write("| kernel | threads | calls | us | MFMA busy | VALU/MFMA | LDS/MFMA | LDS conflict | HBM fetch MB | "
                  "HBM write MB |\n|---|---|---|---|---|---|---|---|---|---|\n")
         for t in table[:40]:
@@ -287,7 +293,7 @@ def write_counters(sq_csv, fetch_csv, write_csv, out_md, title, cmdline):
     jpath = os.path.join(ROOT, "profiles", "mmq_counters.json")
     js = json.load(open(jpath)) if os.path.exists(jpath) else {}
     for t in table:
-        if "gemm_kernel" in t["kernel"] or "skinny" in t["kernel"]:
+        if any(tag in t["kernel"] for tag in MMQ_KERNEL_TAGS):
             js[f"{t['kernel']}|{t['grid']}"] = dict(t, source_hash=gemm_source_hash())
     with open(jpath, "w") as fh:
         json.dump(js, fh, indent=1, sort_keys=True)
