@@ -355,7 +355,11 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
  * the loss and gradients are zero.  A label outside [0, V) that is not
  * ignore_index is treated as ignored and sets the workspace's first 32-bit
  * word to nonzero (GQ_EDEVICE condition, readable after synchronising).
- * chunk_rows >= 1.
+ * chunk_rows >= 1.  The workspace holds the gradient rows of one chunk
+ * (T x chunk_rows bf16), or of two when the backward runs one chunk's
+ * gradient tiles beside the previous chunk's dh tiles (two or more chunks
+ * with 128-row tiles), plus O(T x (H + r) + V x r) floats; it never holds
+ * T x V values.
  */
 size_t gq_lmhead_chunked_ce_workspace_size(const gq_lora_linear* head, int64_t T,
                                            int64_t chunk_rows);

@@ -380,6 +380,10 @@ HEAD_CASES = [
     # vocabulary tile)
     (600, 128, 30000, 8192, 1, 0.1),
     (720, 64, 26000, 26000, 0, 0.0),
+    # 128-row tiles over several chunks (gradient tiles of a chunk share a
+    # launch with the previous chunk's dh tiles), last chunk of 6 rows,
+    # hidden size with an odd number of blocks
+    (768, 96, 16390, 4096, 0, 0.2),
 ]
 
 
