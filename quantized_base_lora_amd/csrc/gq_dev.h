@@ -122,7 +122,8 @@ __device__ __forceinline__ void decode_block(const RawBlock<QT>& rb, float (&w)[
 //   Q4_0: u = nibble                        w = u*d - 8*d
 //   Q2:   u = bit pair                      w = u*d + m
 // Every product and sum is exact (fp16 d times an 8-bit integer), so the
-// result is bit-identical to d*q.  With an infinite scale the biased form
+// result is bit-identical to d*q, except that a zero weight comes out as +0
+// where d*0 is -0 for a negative d.  With an infinite scale the biased form
 // yields NaN where d*q would be +-inf.
 // byte b of x as float: one v_cvt_f32_ubyte{b} (register-only asm; the
 // optimiser would otherwise split it into a bit-field extract plus convert)
@@ -171,6 +172,42 @@ __device__ __forceinline__ void decode_block_fast(const RawBlock<QT>& rb, float 
         for (int b = 0; b < 4; ++b) w[8 * pp + 4 * h + b] = __builtin_fmaf(ubyte(u, b), d, m);
       }
     }
+  }
+}
+
+// Decode straight to packed bf16 pairs: o[i] = (bf16(w[2i]), bf16(w[2i+1]))
+// with w as decode_block_fast gives it (bit-identical).  For the 2-bit
+// scale/min block the four values d*u + m (u = 0..3) are rounded to bf16
+// once per block and kept as two byte planes (low bytes, high bytes); each
+// group of four bit pairs then takes a mask, two table permutes and two
+// byte interleaves, 1.5 VALU per weight instead of 3 (bit-field extract,
+// convert, FMA and half a pack).
+template <int QT>
+__device__ __forceinline__ void decode_block_bf16(const RawBlock<QT>& rb, uint32_t (&o)[16]) {
+  if constexpr (QT == QT_Q2_DM) {
+    const float d = h2f(rb.hdr & 0xffffu), m = h2f(rb.hdr >> 16);
+    const uint32_t p01 = pack_bf2(__builtin_fmaf(0.f, d, m), __builtin_fmaf(1.f, d, m));
+    const uint32_t p23 = pack_bf2(__builtin_fmaf(2.f, d, m), __builtin_fmaf(3.f, d, m));
+    // v_perm_b32 picks bytes of {src0 : src1} (src1 = bytes 0-3)
+    const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);  // low bytes of the 4 values
+    const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);  // high bytes
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // elements 8pp + 4h + b, b = 0..3: bit pair pp of byte b of q[h]
+        const uint32_t u = (rb.q[h] >> (2 * pp)) & 0x03030303u;
+        const uint32_t vl = __builtin_amdgcn_perm(0u, lo, u);
+        const uint32_t vh = __builtin_amdgcn_perm(0u, hi, u);
+        o[4 * pp + 2 * h] = __builtin_amdgcn_perm(vh, vl, 0x05010400u);
+        o[4 * pp + 2 * h + 1] = __builtin_amdgcn_perm(vh, vl, 0x07030602u);
+      }
+    }
+  } else {
+    float w[32];
+    decode_block_fast<QT>(rb, w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = pack_bf2(w[2 * i], w[2 * i + 1]);
   }
 }
 

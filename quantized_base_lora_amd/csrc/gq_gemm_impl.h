@@ -494,17 +494,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
 #pragma unroll
           for (int q = 0; q < RawBlock<QT>::NQ; ++q) wr.q[q] &= wmsk[i];
         }
-        float w[32];
-        decode_block_fast<QT>(wr, w);
+        uint32_t o[16];
+        decode_block_bf16<QT>(wr, o);
         // NT: row w_it_row of the [n][k] tile, k = kb*32 .. +32
         // NN: reduction row w_it_row of the row-major tile, columns kb*32 .. +32
         uint4* dst = reinterpret_cast<uint4*>(B + w_it_row[i] * (NN ? PN : LDK));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = w_it_kb[i] * 4 + q;
-          dst[NN ? nn_chunk(w_it_row[i], c) : c] =
-              make_uint4(pack_bf2(w[8 * q + 0], w[8 * q + 1]), pack_bf2(w[8 * q + 2], w[8 * q + 3]),
-                         pack_bf2(w[8 * q + 4], w[8 * q + 5]), pack_bf2(w[8 * q + 6], w[8 * q + 7]));
+          dst[NN ? nn_chunk(w_it_row[i], c) : c] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
         }
       }
     };

@@ -789,13 +789,11 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
 #pragma unroll
         for (int t = 0; t < NQ; ++t) rb.q[t] = __builtin_amdgcn_alignbyte(Dw[t + 1], Dw[t], sh);
       }
-      float w[32];
-      decode_block_fast<QT>(rb, w);
+      uint32_t o[16];
+      decode_block_bf16<QT>(rb, o);
       uint4* dst = reinterpret_cast<uint4*>(D + lane * DP);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        dst[q4] = make_uint4(pack_bf2(w[8 * q4 + 0], w[8 * q4 + 1]), pack_bf2(w[8 * q4 + 2], w[8 * q4 + 3]),
-                             pack_bf2(w[8 * q4 + 4], w[8 * q4 + 5]), pack_bf2(w[8 * q4 + 6], w[8 * q4 + 7]));
+      for (int q4 = 0; q4 < 4; ++q4) dst[q4] = make_uint4(o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]);
     }
     // (the wave's own region: the LDS writes above complete before the
     // reads below in this wave's program order)

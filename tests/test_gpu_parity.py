@@ -120,21 +120,43 @@ def test_linear_b_zero_is_base_and_da_zero():
     check("dB", host(dB), ref["dB"])
 
 
-def test_linear_one_hot_rows_bit_exact():
-    """x[t] = e_k and B = 0: y[t] = bf16(deq(W)[:, k]) exactly."""
-    cfg = synth.LinearCfg("t", T=8, K=128, N=64, qtype=0, rank=4, alpha=8)
+@pytest.mark.parametrize("qtype", [0, 1, 2])
+@pytest.mark.parametrize("T,K,N", [(8, 128, 64), (16, 256, 128), (300, 512, 384)])
+def test_linear_one_hot_rows_bit_exact(qtype, T, K, N):
+    """One-hot rows with B = 0 read single decoded weights back exactly:
+    x[t] = e_k gives y[t] = bf16(deq(W)[:, k]) (forward, the weight tile's
+    decode along its rows), dY[t] = e_n gives dX[t] = bf16(deq(W)[n, :])
+    (backward, the decode of whole weight rows)."""
+    cfg = synth.LinearCfg("t", T=T, K=K, N=N, qtype=qtype, rank=4, alpha=8, seed=T + qtype)
     inp = synth.make_linear(cfg)
-    cols = [0, 5, 31, 32, 63, 64, 100, 127]
-    X = np.zeros((8, 128), np.float32)
-    for t, c in enumerate(cols):
-        X[t, c] = 1.0
+    rng = np.random.default_rng(T + 7 * qtype)
+    cols = rng.integers(0, K, T)
+    rows = rng.integers(0, N, T)
+    cols[:4] = [0, 31, 32, K - 1]
+    rows[:4] = [0, 31, 32, N - 1]
+    X = np.zeros((T, K), np.float32)
+    X[np.arange(T), cols] = 1.0
+    DY = np.zeros((T, N), np.float32)
+    DY[np.arange(T), rows] = 1.0
     inp["x"] = synth.f32_to_bf16_bits(X)
+    inp["dy"] = synth.f32_to_bf16_bits(DY)
     inp["B"][:] = 0.0
-    W = ob.dequant_f32(0, inp["blocks"], 64, 128)
-    y, _ = gq.linear_lora_fwd(lin_proj(inp), bf16_dev(inp["x"]))
-    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
-    for t, c in enumerate(cols):
-        assert np.array_equal(got[t], synth.f32_to_bf16_bits(W[:, c]))
+    W = ob.dequant_f32(qtype, inp["blocks"], N, K)
+    say("one-hot", qtype, T, K, N)
+    p = lin_proj(inp)
+    x, dy = bf16_dev(inp["x"]), bf16_dev(inp["dy"])
+    y, xa = gq.linear_lora_fwd(p, x)
+    dx, _, _ = gq.linear_lora_bwd(p, x, xa, dy)
+    # bits compared with -0 read as +0: the fused decode forms d*(q - z) as
+    # d*q' + (-z*d), whose exact zero is +0 where d*0 is -0 for d < 0
+    def bits(a):
+        a = np.asarray(a, np.uint16).copy()
+        a[(a & 0x7FFF) == 0] = 0
+        return a
+    gy = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    gdx = dx.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits(gy), bits(synth.f32_to_bf16_bits(W[:, cols].T))), "forward"
+    assert np.array_equal(bits(gdx), bits(synth.f32_to_bf16_bits(W[rows, :]))), "backward"
 
 
 @pytest.mark.parametrize("qtype", [0, 1, 2])
