@@ -165,6 +165,9 @@ typedef struct gq_lora_linear {
  *   xa = x A^T                 [T][rank] float32 (saved for the backward)
  *   y  = x deq(W)^T + s xa B^T [T][n_out] bf16
  * x [T][n_in] bf16.  T == 0 is a no-op.
+ * Workspace: gq_linear_lora_fwd_workspace_size() bytes, zero except for
+ * launches too small to fill the GPU with output tiles, whose reduction is
+ * split over workgroups (their fp32 partial sums live there).
  */
 size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear* L, int64_t T);
 int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,

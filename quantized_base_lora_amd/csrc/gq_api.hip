@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -281,6 +282,19 @@ bool wide_pays(int qtype, int64_t M, int64_t N, int64_t K) {
   return tiles * 4 >= rounds * 256 * 3;
 }
 
+// Split-K for small dense launches: when even 64-row tiles leave most CUs
+// idle, each tile's reduction is cut into ksplit contiguous ranges (at least
+// two k-steps each), one workgroup per range writing fp32 sums that a fixup
+// pass adds up with the adapter term.  1 = no split.
+int small_split(int64_t M, int64_t N, int64_t K) {
+  if (K % GEMM_BK || N % 8) return 1;
+  const int64_t tiles = (int64_t)cdiv(M, 64) * cdiv(N, TILE_BN);
+  const int64_t nk = K / GEMM_BK;
+  if (tiles * 4 > 256 || nk < 4) return 1;
+  const int64_t ks = std::min<int64_t>(256 / tiles, nk / 2);
+  return ks > 1 ? (int)ks : 1;
+}
+
 hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
 
 }  // namespace
@@ -316,13 +330,18 @@ static int dequant_impl(int qtype, const void* blocks, int64_t rows, int64_t col
 }
 
 // ------------------------------------------------------------------- linear
-size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear*, int64_t) { return 0; }
+size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear* L, int64_t T) {
+  if (!L || T <= 0 || L->n_in <= 0 || L->n_out <= 0) return 0;
+  const int ks = small_split(T, L->n_out, L->n_in);
+  if (ks <= 1) return 0;
+  Ws w(nullptr);
+  w.take<float>((int64_t)ks * T * L->n_out);
+  return w.size();
+}
 
 static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,
                        float* xa, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_proj(L, "gq_linear_lora_fwd", false);
   if (rc) return rc;
   if (T < 0 || T > INT_MAX) return fail(GQ_EINVAL, "gq_linear_lora_fwd: bad T %lld", (long long)T);
@@ -333,12 +352,6 @@ static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int6
   REQ_ALIGN(xa, 4, "gq_linear_lora_fwd");
   const hipStream_t st = S(stream);
   const int r = L->rank, K = (int)L->n_in, N = (int)L->n_out;
-
-  RowDotArgs rd;
-  memset(&rd, 0, sizeof rd);
-  rd.M = T; rd.C = K; rd.r = r; rd.act = x; rd.lda = K; rd.gdiv = 1; rd.E = 1;
-  rd.W[0] = L->A; rd.w_jstride = K; rd.w_cstride = 1; rd.out[0] = xa; rd.nout = 1;
-  HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_fwd: x A^T");
 
   GemmArgs g = gemm_defaults();
   g.M = T; g.N = N; g.K = K;
@@ -351,10 +364,28 @@ static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int6
     tc = TILE_WIDE;
     g.ntiles = cdiv(N, WIDE_BN);
   }
+  // small launches: split the reduction (needs the workspace and 4-byte
+  // aligned y for the fixup's stores; else the unsplit tile)
+  const int ks = (tile_skinny(tc) || tc == TILE_WIDE || !aligned(y, 4)) ? 1 : small_split(T, N, K);
+  if (ks > 1) {
+    if ((rc = check_ws(ws, ws_bytes, gq_linear_lora_fwd_workspace_size(L, T)))) return rc;
+    tc = TILE_64x128;
+    g.ksplit = ks;
+    g.part = static_cast<float*>(ws);
+  }
   g.mtiles = cdiv(T, tile_bm(tc));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
   g.o0 = y; g.ldo = N;
+
+  RowDotArgs rd;
+  memset(&rd, 0, sizeof rd);
+  rd.M = T; rd.C = K; rd.r = r; rd.act = x; rd.lda = K; rd.gdiv = 1; rd.E = 1;
+  rd.W[0] = L->A; rd.w_jstride = K; rd.w_cstride = 1; rd.out[0] = xa; rd.nout = 1;
+  HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_fwd: x A^T");
   HIP_TRY(launch_gemm(L->qtype, EPI_LIN, tc, g, st), "gq_linear_lora_fwd: MMQ");
+  if (ks > 1)
+    HIP_TRY(launch_split_fixup(g.part, ks, T, N, xa, r, L->B, r, 1, L->scale, y, N, st),
+            "gq_linear_lora_fwd: split sums");
   return GQ_OK;
 }
 
@@ -363,6 +394,8 @@ struct LinBwdWs {
   float* dyB;
   float* part_dB;
   float* part_dA;
+  float* part_dx;  // split-K sums of a small dX launch (else nullptr)
+  int ks_dx;
 };
 int lin_rc(const gq_lora_linear* L, int64_t T) {
   return pick_rc(T, L->n_in > L->n_out ? L->n_in : L->n_out, L->rank, 1);
@@ -373,6 +406,8 @@ LinBwdWs plan_lin_bwd(Ws& w, const gq_lora_linear* L, int64_t T) {
   p.dyB = w.take<float>(T * L->rank);
   p.part_dB = w.take<float>(slots * L->n_out * L->rank);
   p.part_dA = w.take<float>(slots * L->n_in * L->rank);
+  p.ks_dx = small_split(T, L->n_in, L->n_out);
+  p.part_dx = p.ks_dx > 1 ? w.take<float>((int64_t)p.ks_dx * T * L->n_in) : nullptr;
   return p;
 }
 }  // namespace
@@ -444,12 +479,21 @@ static int linear_lora_bwd_impl(const gq_lora_linear* L, const uint16_t* x, cons
     g.a0 = dy; g.lda = N;
     g.w0 = static_cast<const uint8_t*>(L->w_blocks);
     g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
-    const int tc = pick_nn_tile(T, T, cdiv(K, TILE_BN), K, aligned(L->w_blocks, 16), N, true);
+    int tc = pick_nn_tile(T, T, cdiv(K, TILE_BN), K, aligned(L->w_blocks, 16), N, true);
+    const bool split = P.ks_dx > 1 && !tile_skinny(tc) && aligned(dx, 4);
+    if (split) {
+      tc = TILE_64x128;
+      g.ksplit = P.ks_dx;
+      g.part = P.part_dx;
+    }
     g.ntiles = cdiv(K, nn_tile_bn(tc));
     g.mtiles = cdiv(T, tile_bm(tc));
     g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
     g.o0 = dx; g.ldo = K;
     HIP_TRY(launch_gemm(L->qtype, EPI_LIN_BWD, tc, g, st), "gq_linear_lora_bwd: dX MMQ");
+    if (split)  // adapter term s (dY B) A: A is [r][n_in]
+      HIP_TRY(launch_split_fixup(P.part_dx, P.ks_dx, T, K, P.dyB, r, L->A, 1, K, L->scale, dx, K, st),
+              "gq_linear_lora_bwd: dX split sums");
   }
   return GQ_OK;
 }

@@ -255,6 +255,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
   // so its L2 holds the activation rows of GM m-tiles and the weight columns
   // of the band instead of every m-tile.
   int mslot, ntile;
+  int ksidx = 0;
   if (p.offsets) {
     const int used = p.tile_start[p.E] * p.ntiles;
     if (block >= used) return;
@@ -262,7 +263,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
     mslot = bid / p.ntiles;
     ntile = bid - mslot * p.ntiles;
   } else {
-    const int bid = xcd_run(block, nblocks);
+    int bid = xcd_run(block, nblocks);
+    if (p.ksplit > 1) {  // consecutive ids: the k-ranges of one tile
+      ksidx = bid % p.ksplit;
+      bid /= p.ksplit;
+    }
     constexpr int GM = 4;
     const int gsize = GM * p.ntiles;
     const int g = bid / gsize;
@@ -291,9 +296,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
     r1 = min(p.M, r0 + BM);
   }
   const int n0 = ntile * BN;
-  const int nk = (p.K + BK - 1) / BK;  // k-steps of the whole reduction
+  // k-steps of this workgroup: all of them, or split ksidx's contiguous range
+  const int nkall = (p.K + BK - 1) / BK;
+  const int kb0 = p.ksplit > 1 ? (int)((int64_t)ksidx * nkall / p.ksplit) : 0;
+  const int nk = p.ksplit > 1 ? (int)((int64_t)(ksidx + 1) * nkall / p.ksplit) - kb0 : nkall;
   const int nkl = (nk + KS - 1) / KS;   // k-steps of each group
-  auto KT = [&](int ls) { return ls * KS + grp; };
+  auto KT = [&](int ls) { return kb0 + ls * KS + grp; };
   auto LCb = [&](int b) { return wn * WTN + b * 32 + (lane & 31); };
 
   // ---- main loop
@@ -622,7 +630,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
   const float s = p.s;
   constexpr int NSET = EPI == EPI_SWIGLU ? 2 : 1;
   constexpr bool FOLD = EPI != EPI_DH_ACC;
-  if constexpr (FOLD) {
+  // (split-K parts get the adapter term in the fixup instead)
+  if constexpr (FOLD) if (p.ksplit <= 1) {
     const int rtot = EPI == EPI_GATEUP_BWD ? 2 * r : r;
     const float* Y0;
     const float* Y1 = nullptr;
@@ -716,6 +725,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
   auto LR = [&](int a, int v) { return wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); };
   auto LC = [&](int b) { return LCb(b); };
 
+  if constexpr (EPI == EPI_LIN || EPI == EPI_LIN_BWD) {
+    if (p.ksplit > 1) {
+      // this k-range's fp32 sums, summed with the others by the fixup
+      float* P = p.part + (int64_t)ksidx * p.M * p.N;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int n = n0 + LC(b);
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t pr = r0 + LR(a, v);
+            if (pr < r1) P[pr * p.N + n] = acc[a][b][v];
+          }
+      }
+      return;
+    }
+  }
   if constexpr (EPI == EPI_LIN || EPI == EPI_LIN_BWD || EPI == EPI_GATEUP_BWD) {
     // the wave's WTM x WTN output tile goes through a wave-private LDS
     // region (rows of WTN + 8 bf16) and leaves as 16-byte row stores (8
@@ -1105,7 +1133,13 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st);
 
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
+  const unsigned splits = a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
+  if (splits > 1) {  // dense EPI_LIN / EPI_LIN_BWD on one group of four waves, whole k-steps
+    if (a.offsets || a.K % GEMM_BK || tilecfg == TILE_128x128_K2 || tile_skinny(tilecfg) ||
+        tilecfg == TILE_WIDE || !(EPI == EPI_LIN || EPI == EPI_LIN_BWD) || !a.part)
+      return hipErrorInvalidValue;
+  }
+  const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles * splits);
   if (tilecfg == TILE_WIDE) {
     if constexpr ((EPI == EPI_LIN || EPI == EPI_CE_FWD) && QT != QT_Q2_DM) {
       if (a.offsets || a.gather || a.K % GEMM_BK) return hipErrorInvalidValue;

@@ -82,6 +82,12 @@ struct GemmArgs {
   int32_t ntile_base;  // global n-tile index of this launch's first n-tile
   int32_t accum;       // EPI_DH_ACC: add into f0
   const float* nvalid; // EPI_CE_BWD: device count of valid labels
+  // split-K (dense EPI_LIN / EPI_LIN_BWD, one group of waves, K % 64 == 0):
+  // ksplit > 1 workgroups per tile take contiguous k-step ranges and store
+  // their fp32 sums in part[split][M][N] (no adapter term, no bf16 output);
+  // launch_split_fixup then adds the parts, the adapter term, and rounds.
+  int32_t ksplit;
+  float* part;
 };
 
 // TILE_128x128_K2: 128x128 tiles computed by 512 threads, two groups of four
@@ -165,6 +171,12 @@ struct RowDotArgs {
   float* wout;       // over the same rows (needs wflat, sorted)
 };
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st);
+
+// out[t][n] = bf16( sum_{s < ksplit} part[s][t][n] + scale * sum_{j < r} X[t][j] * Y[n*ys_n + j*ys_j] )
+// for t < M, n < N (N even, out 4-byte aligned).
+hipError_t launch_split_fixup(const float* part, int ksplit, int64_t M, int32_t N, const float* X, int32_t r,
+                              const float* Y, int64_t ys_n, int64_t ys_j, float scale, uint16_t* out,
+                              int64_t ldo, hipStream_t st);
 
 // Partial outer-product reductions over row chunks:
 //   part[slot][c][j] = sum_{rows p of slot} U(p)[c] * Vv[p][j]

@@ -926,6 +926,42 @@ hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Split-K fixup: two output columns per thread (enough threads to hide the
+// latency of the few dependent loads), the parts summed in split order.
+__global__ __launch_bounds__(256) void split_fixup_kernel(const float* __restrict__ part, int ksplit, int64_t M,
+                                                          int32_t N, const float* __restrict__ X, int32_t r,
+                                                          const float* __restrict__ Y, int64_t ys_n, int64_t ys_j,
+                                                          float scale, uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nc = N / 2;
+  if (i >= M * nc) return;
+  const int64_t t = i / nc;
+  const int n = (int)(i % nc) * 2;
+  float v0 = 0.f, v1 = 0.f;
+  for (int k = 0; k < ksplit; ++k) {
+    const float2 a = *reinterpret_cast<const float2*>(part + ((int64_t)k * M + t) * N + n);
+    v0 += a.x;
+    v1 += a.y;
+  }
+  for (int j = 0; j < r; ++j) {
+    const float xj = scale * X[t * r + j];
+    v0 = __builtin_fmaf(xj, Y[(int64_t)n * ys_n + (int64_t)j * ys_j], v0);
+    v1 = __builtin_fmaf(xj, Y[(int64_t)(n + 1) * ys_n + (int64_t)j * ys_j], v1);
+  }
+  *reinterpret_cast<uint32_t*>(out + t * ldo + n) = pack_bf2(v0, v1);
+}
+
+hipError_t launch_split_fixup(const float* part, int ksplit, int64_t M, int32_t N, const float* X, int32_t r,
+                              const float* Y, int64_t ys_n, int64_t ys_j, float scale, uint16_t* out,
+                              int64_t ldo, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  if (N % 2 || ldo % 2 || (uintptr_t)out % 4 || (uintptr_t)part % 8) return hipErrorInvalidValue;
+  const int64_t n = M * (N / 2);
+  hipLaunchKernelGGL(split_fixup_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, part, ksplit, M, N, X, r,
+                     Y, ys_n, ys_j, scale, out, ldo);
+  return hipGetLastError();
+}
+
 int colred_cols_per_block(int) { return CR_COLS; }
 
 hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {

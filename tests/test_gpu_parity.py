@@ -83,6 +83,9 @@ LIN_CASES = [
     # enough 256 x 192 tiles for the wide forward MMQ, with a partial last
     # row tile and a partial last column tile (T % 256, N % 192 != 0)
     (2000, 1024, 6104, 0, 4), (1800, 512, 5760, 1, 8),
+    # few tiles: the reduction split over workgroups, summed by the fixup
+    # pass (forward and dX; ragged rows)
+    (100, 512, 512, 2, 8), (90, 256, 1024, 1, 4),
 ]
 
 
