@@ -1084,10 +1084,21 @@ struct CeWs {
   float* GB;
   float* part;
   int64_t ldG;
+  int64_t span;  // vocabulary rows per backward step (one or more chunks)
   int mt;
   int ntiles_bwd;
   int tc_fwd, tc_bwd, tc_dh;
 };
+// Chunks per backward step when the gradient tiles run on the 256 x 192
+// tile: the fewest (up to three) that give two full rounds of tiles, kept
+// only if the tiles fill the chip (wide_pays); 0 = 128 x 128 gradient tiles.
+int64_t ce_wide_chunks(int qtype, int64_t T, int64_t V, int64_t H, int r, int64_t C) {
+  if (r > 16) return 0;
+  const int64_t nchunks = (V + C - 1) / C;
+  int64_t g = 1;
+  while (g < 3 && g < nchunks && (int64_t)cdiv(T, WIDE_BM) * cdiv(std::min(g * C, V), WIDE_BN) < 512) ++g;
+  return wide_pays(qtype, T, std::min(g * C, V), H) ? g : 0;
+}
 CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad) {
   CeWs p;
   memset(&p, 0, sizeof p);
@@ -1105,24 +1116,29 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
   p.term = w.take<float>(T);
   if (grad) {
     const int64_t C = chunk < V ? chunk : V;
-    p.ldG = (C + 63) / 64 * 64;
+    // gradient tiles on the 256 x 192 tile, several chunks per step, when
+    // they fill the chip; else 128 x 128 tiles, one chunk per step
+    const int64_t gw = ce_wide_chunks(L->qtype, T, V, H, (int)r, C);
+    p.span = gw ? std::min(gw * C, V) : C;
+    const int bn = gw ? WIDE_BN : TILE_BN;
+    p.ldG = (p.span + 63) / 64 * 64;
     p.G = w.take<uint16_t>(T * p.ldG);
     p.dh_acc = w.take<float>(T * H);
     int64_t ntb = 0;
-    for (int64_t c0 = 0; c0 < V; c0 += chunk) ntb += cdiv((V - c0) < chunk ? V - c0 : chunk, TILE_BN);
+    for (int64_t c0 = 0; c0 < V; c0 += p.span) ntb += cdiv(std::min(p.span, V - c0), bn);
     p.ntiles_bwd = (int)ntb;
     p.part_GB = w.take<float>(ntb * T * r);
-    p.tc_bwd = pick_tile(T, cdiv(C, TILE_BN));
+    p.tc_bwd = gw ? TILE_WIDE : pick_tile(T, cdiv(C, TILE_BN));
     p.mt = cdiv(T, tile_bm(p.tc_bwd));
     p.part_dB = w.take<float>((int64_t)p.mt * V * r);
     p.GB = w.take<float>(T * r);
     p.part = w.take<float>(colred_slots(T, pick_rc(T, H, (int)r, 1), 1) * H * r);
-    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), C, true);
+    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), p.span, true);
     // two or more chunks with 128-row tiles on both passes: chunk c's
     // gradient tiles share a launch with chunk c-1's dh tiles, which needs a
     // second gradient buffer
-    const int64_t nchunks = (V + chunk - 1) / chunk;
-    if (nchunks >= 2 && p.tc_bwd == TILE_128x128 && tile_bm(p.tc_dh) == 128)
+    const int64_t nsteps = (V + p.span - 1) / p.span;
+    if (nsteps >= 2 && p.tc_bwd == TILE_128x128 && tile_bm(p.tc_dh) == 128)
       p.G2 = w.take<uint16_t>(T * p.ldG);
   }
   return p;
@@ -1200,24 +1216,25 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
           "ce: log-sum-exp merge, loss");
   if (!grad) return GQ_OK;
 
-  // Chunk after chunk: the gradient tiles write G for the chunk's vocabulary
-  // rows (plus the G.B and dB partials), the dh tiles accumulate G deq(W) of
-  // the chunk into dh_acc (chunk order fixed: deterministic).  With two
-  // gradient buffers, chunk c's gradient tiles and chunk c-1's dh tiles
-  // run in one launch.
+  // Step after step (one chunk, or up to three on the 256 x 192 gradient
+  // tile): the gradient tiles write G for the step's vocabulary rows (plus
+  // the G.B and dB partials), the dh tiles accumulate G deq(W) of the step
+  // into dh_acc (step order fixed: deterministic).  With two gradient
+  // buffers, step c's gradient tiles and step c-1's dh tiles run in one
+  // launch.
   const bool pair = P.G2 != nullptr;
   GemmArgs dprev = gemm_defaults();
   bool have_prev = false;
   int ntile_base = 0;
   int ci = 0;
-  for (int64_t c0 = 0; c0 < V; c0 += chunk, ++ci) {
-    const int C = (int)((V - c0) < chunk ? V - c0 : chunk);
+  for (int64_t c0 = 0; c0 < V; c0 += P.span, ++ci) {
+    const int C = (int)std::min(P.span, V - c0);
     uint16_t* Gc = (pair && (ci & 1)) ? P.G2 : P.G;
     GemmArgs b = gemm_defaults();
     b.M = T; b.N = C; b.K = H;
     b.a0 = h; b.lda = H;
     b.w0 = wb; b.w_rowbytes = rowbytes(L); b.w_nb = H / 32; b.w_rows = C; b.w_row0 = (int)c0;
-    b.ntiles = cdiv(C, TILE_BN);
+    b.ntiles = cdiv(C, P.tc_bwd == TILE_WIDE ? WIDE_BN : TILE_BN);
     b.mtiles = cdiv(T, tile_bm(P.tc_bwd));
     b.s = L->scale; b.r = r; b.lB0 = L->B; b.rv0 = P.xa;
     b.o0 = Gc; b.ldo = P.ldG;

@@ -97,7 +97,8 @@ struct GemmArgs {
 // weight (16, 32 or 64 rows per tile, 128 weight rows per workgroup;
 // K % 256 == 0).
 // TILE_WIDE: 256 x 192 tiles on 512 threads (gq_wide_impl.h), dense
-// forward launches with Q8_0 / Q4_0 weights and K % 64 == 0 only.
+// forward launches and the LM head's gradient tiles, with Q8_0 / Q4_0
+// weights and K % 64 == 0 only.
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,

@@ -20,6 +20,9 @@
 //    be a multiple of 64.
 //  * The rank-r adapter term is folded into the accumulators as extra k16
 //    MFMA slices (bf16 hi + lo parts), as in the tile GEMM.
+//  * The LM head's backward uses the same tile for its gradient tiles
+//    (EPI_CE_BWD): several vocabulary chunks per launch, so that the tiles
+//    fill whole rounds of the chip.
 #pragma once
 #include "gq_dev.h"
 #include "gq_internal.h"
@@ -36,6 +39,13 @@ constexpr int SP = WTN + 8;  // staged epilogue row pitch (bf16)
 constexpr int SMEM_EPI = 8 * WTM * SP * 2;
 constexpr int SMEM = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
 static_assert(BM * 2 * 16 * 8 <= SMEM, "CE partial pairs fit the LDS");
+// CE gradient epilogue: one wave column's half of the tile as fp32 [BM][HP],
+// then four ranks of the tile rows' xa (BM x 4) and of the half's B rows
+// (WTN x 4)
+constexpr int HP = WTN + 1;
+constexpr int CEB_Z = BM * HP * 4, CEB_X = BM * 4 * 4, CEB_B = WTN * 4 * 4;
+static_assert(CEB_Z + CEB_X + CEB_B <= SMEM, "CE gradient staging fits the LDS");
+static_assert(3 * WTN * 5 * 4 <= CEB_Z, "column partials fit the staged half");
 
 // A quarter of a block: its fp16 scale (low 16 bits of hdr) and payload
 // bytes [q*NB, q*NB + NB) with NB = 4 (Q4_0) or 8 (Q8_0).
@@ -99,6 +109,145 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
   m = mn;
 }
 
+// CE gradient epilogue of a 256 x 192 tile.  The accumulators hold the
+// logits z of the tile (adapter term included); they are turned into G in
+// place, then each wave column's 96-column half goes through LDS as fp32:
+// its bf16 rows go out as 16-byte stores, the row sums G . B accumulate
+// over both halves (two threads per row, 48 columns each, added at the
+// end), and the column sums G^T . xa of the half (four threads per column,
+// 64 rows each, added in a fixed order) are written.  Ranks are taken four
+// at a time (one pass for rank <= 4), which keeps the kernel within its
+// registers.
+__device__ __forceinline__ void ce_grad_epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN], uint8_t* smem,
+                                                 int64_t r0, int n0, int mt, int nt) {
+  constexpr int R = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int r = p.r;
+  const int64_t V = p.V, c0 = p.w_row0;
+  const float nv = *p.nvalid;
+  const float coef = nv > 0.f ? p.coef / nv : 0.f;
+  // z -> G in the accumulators (rows past M, ignored labels and columns past
+  // w_rows give 0)
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t pr = r0 + wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      int64_t lab = -1;
+      float lse = 0.f;
+      bool valid = false;
+      if (pr < p.M) {
+        lab = p.labels[pr];
+        valid = lab != p.ignore_index && lab >= 0 && lab < V;
+        lse = p.lse[pr];
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int n = n0 + wn * WTN + b * 32 + (lane & 31);
+        float gv = 0.f;
+        if (valid && n < p.w_rows) gv = coef * (__expf(acc[a][b][v] - lse) - (c0 + n == lab ? 1.f : 0.f));
+        acc[a][b][v] = gv;
+      }
+    }
+
+  float* Z = reinterpret_cast<float*>(smem);
+  float* Sx = reinterpret_cast<float*>(smem + CEB_Z);
+  float* Sb = reinterpret_cast<float*>(smem + CEB_Z + CEB_X);
+  const int row = tid >> 1, hh = tid & 1;        // row sums: 48 columns per thread
+  const int ccol = tid % WTN, cseg = tid / WTN;  // column sums: 64 rows per thread (tid < 384)
+  const bool vec = ((uintptr_t)p.o0 % 16 == 0) && (p.ldo % 8 == 0);
+  for (int jb = 0; jb < r; jb += R) {
+    __syncthreads();  // operand stages (first pass) or the previous pass's LDS reads are done
+    for (int i = tid; i < BM * R; i += NTHR) {
+      const int rr = i / R, j = jb + i % R;
+      Sx[i] = (j < r && r0 + rr < p.M) ? p.rv0[(r0 + rr) * r + j] : 0.f;
+    }
+    float racc[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) racc[j] = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int hc0 = n0 + h * WTN;  // first column of this half
+      if (h) __syncthreads();        // the previous half's column partials are summed
+      if (wn == h) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              Z[(wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * HP + b * 32 + (lane & 31)] =
+                  acc[a][b][v];
+      }
+      for (int i = tid; i < WTN * R; i += NTHR) {
+        const int c = i / R, j = jb + i % R;
+        Sb[i] = (j < r && hc0 + c < p.w_rows) ? p.lB0[(c0 + hc0 + c) * r + j] : 0.f;
+      }
+      __syncthreads();
+      if (jb == 0) {
+        // G rows as bf16: 12 pieces of 8 columns per row
+        for (int i = tid; i < BM * (WTN / 8); i += NTHR) {
+          const int rr = i / (WTN / 8), cc = (i % (WTN / 8)) * 8;
+          const int64_t pr = r0 + rr;
+          const int n = hc0 + cc;
+          if (pr >= p.M || n >= p.ldo) continue;
+          const float* z = Z + rr * HP + cc;
+          if (vec) {
+            *reinterpret_cast<uint4*>(p.o0 + pr * p.ldo + n) = make_uint4(
+                pack_bf2(z[0], z[1]), pack_bf2(z[2], z[3]), pack_bf2(z[4], z[5]), pack_bf2(z[6], z[7]));
+          } else {
+            for (int c = 0; c < 8 && n + c < p.ldo; ++c) p.o0[pr * p.ldo + n + c] = f2bf(z[c]);
+          }
+        }
+      }
+#pragma unroll 4
+      for (int c = hh * (WTN / 2); c < (hh + 1) * (WTN / 2); ++c) {
+        const float z = Z[row * HP + c];
+#pragma unroll
+        for (int j = 0; j < R; ++j) racc[j] += z * Sb[c * R + j];
+      }
+      float cacc[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) cacc[j] = 0.f;
+      if (cseg < 4) {
+#pragma unroll 4
+        for (int rr = cseg * 64; rr < cseg * 64 + 64; ++rr) {
+          const float z = Z[rr * HP + ccol];
+#pragma unroll
+          for (int j = 0; j < R; ++j) cacc[j] += z * Sx[rr * R + j];
+        }
+      }
+      __syncthreads();
+      float* Xs = Z;  // [3][WTN][R + 1] partials of segments 1..3
+      if (cseg >= 1 && cseg < 4) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) Xs[((cseg - 1) * WTN + ccol) * (R + 1) + j] = cacc[j];
+      }
+      __syncthreads();
+      if (cseg == 0) {
+#pragma unroll
+        for (int sg = 0; sg < 3; ++sg)
+#pragma unroll
+          for (int j = 0; j < R; ++j) cacc[j] += Xs[(sg * WTN + ccol) * (R + 1) + j];
+        const int n = hc0 + ccol;
+        if (n < p.w_rows) {
+          float* dst = p.f2 + ((int64_t)mt * V + c0 + n) * r + jb;
+#pragma unroll
+          for (int j = 0; j < R; ++j)
+            if (jb + j < r) dst[j] = cacc[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) racc[j] += __shfl_xor(racc[j], 1);
+    if (hh == 0 && r0 + row < p.M) {
+      float* dst = p.f1 + ((int64_t)(p.ntile_base + nt) * p.M + r0 + row) * r + jb;
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (jb + j < r) dst[j] = racc[j];
+    }
+  }
+}
+
 // Dense forward: z[p][n] = sum_k a0[p][k] deq(W)[n][k] + s * rv0[p] . lB0[n].
 // Geometry from GemmArgs: M rows, N = w_rows output columns, K.
 //   EPI_LIN:    z stored as bf16 (o0, ldo).
@@ -106,9 +255,15 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
 //               (max, sum exp) over the tile's columns below w_rows goes to
 //               f0[(tile column index) * M + row], and the row's label logit,
 //               when the label column is in this tile, to f1[row].
+//   EPI_CE_BWD: the columns are vocabulary rows w_row0 .. w_row0 + w_rows;
+//               G = coef/nvalid * (exp(z - lse[row]) - [col == label]) (zero
+//               for ignored labels and columns past w_rows) goes to o0 as
+//               bf16 (ldo, columns below ldo), the tile's G . B rows to
+//               f1[((ntile_base + tile column) * M + row) * r + j] and its
+//               G^T . xa columns to f2[(tile row * V + w_row0 + col) * r + j].
 template <int QT, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
-  static_assert(EPI == EPI_LIN || EPI == EPI_CE_FWD, "wide epilogues");
+  static_assert(EPI == EPI_LIN || EPI == EPI_CE_FWD || EPI == EPI_CE_BWD, "wide epilogues");
   constexpr int BS = QTraits<QT>::BS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -251,6 +406,7 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
       lo[i] = (__bf16)(v[i] - (float)h);
     }
   };
+  const float* Bw = p.lB0 + (int64_t)p.w_row0 * r;  // B rows of this launch's columns
   for (int qr = 0; qr * 16 < r; ++qr) {
     const int j0 = qr * 16 + (lane >> 5) * 8;
     bf16x8 ah[TM], al[TM];
@@ -268,7 +424,7 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        v[i] = (col < p.w_rows && j0 + i < r) ? s * p.lB0[(int64_t)col * r + j0 + i] : 0.f;
+        v[i] = (col < p.w_rows && j0 + i < r) ? s * Bw[(int64_t)col * r + j0 + i] : 0.f;
       bf16x8 bh, bl;
       split8(v, bh, bl);
 #pragma unroll
@@ -333,6 +489,11 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
       dst[0] = m;
       dst[1] = l;
     }
+    return;
+  }
+
+  if constexpr (EPI == EPI_CE_BWD) {
+    ce_grad_epilogue(p, acc, smem, r0, n0, mt, nt);
     return;
   }
 

@@ -412,12 +412,32 @@ HEAD_CASES = [
 ]
 
 
+# 256 x 192 gradient tiles over several chunks per launch, ranks taken four
+# at a time in their epilogue (rank 8, 6 and 12; ragged rows, ragged last
+# step, one k-step of hidden size)
+HEAD_WIDE_RANK_CASES = [
+    # T, H, V, chunk, qtype, ignore_frac, rank
+    (768, 128, 20000, 4096, 0, 0.1, 8),
+    (600, 64, 14000, 4096, 1, 0.0, 6),
+    (1024, 64, 10000, 4096, 1, 0.2, 12),
+]
+
+
 @pytest.mark.parametrize("T,H,V,chunk,qtype,ign", HEAD_CASES)
 def test_lmhead(T, H, V, chunk, qtype, ign):
-    cfg = synth.HeadCfg("t", T=T, H=H, V=V, qtype=qtype, rank=4, alpha=8, chunk=chunk,
+    _lmhead_case(T, H, V, chunk, qtype, ign, 4)
+
+
+@pytest.mark.parametrize("T,H,V,chunk,qtype,ign,rank", HEAD_WIDE_RANK_CASES)
+def test_lmhead_wide_ranks(T, H, V, chunk, qtype, ign, rank):
+    _lmhead_case(T, H, V, chunk, qtype, ign, rank)
+
+
+def _lmhead_case(T, H, V, chunk, qtype, ign, rank):
+    cfg = synth.HeadCfg("t", T=T, H=H, V=V, qtype=qtype, rank=rank, alpha=2 * rank, chunk=chunk,
                         ignore_frac=ign, seed=T + V)
     inp = synth.make_head(cfg, large_adapter=True, w_sigma=0.05)
-    say("lmhead", T, H, V, chunk, qtype)
+    say("lmhead", T, H, V, chunk, qtype, rank)
     ref = olm.forward_backward(inp, chunk=chunk)
     head = gq.Proj(qtype, V, H, u8_dev(inp["blocks"]), f32_dev(inp["A"]), f32_dev(inp["B"]),
                    float(inp["scale"]))
