@@ -137,8 +137,9 @@ def write_kernel_summary(csv_dir, out_md, title):
                  f"python3 <repo>/bench.py {title}\n\n")
         fh.write("gemm_kernel<qtype, epilogue, BM, BN, k-groups>: qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, "
                  "1 SwiGLU, 2 CE logits, 3 CE gradient, 4 linear backward (dX), 5 SwiGLU backward, "
-                 "6 gate/up backward, 7 dh accumulate; wide::wide_kernel<qtype, epilogue>: the 256 x 192 forward "
-                 "tile; ce_bwd_dh_kernel<qtype>: one vocabulary chunk's CE-gradient tiles with the previous "
+                 "6 gate/up backward, 7 dh accumulate; wide::wide_kernel<qtype, epilogue>: the 256 x 192 tile "
+                 "(epilogue 0 linear, 2 CE logits, 3 CE gradient over up to three vocabulary chunks); "
+                 "ce_bwd_dh_kernel<qtype>: one vocabulary chunk's CE-gradient tiles with the previous "
                  "chunk's dh tiles.\n\n")
         fh.write("## rocprofv3 --stats (run_kernel_stats.csv)\n\n| kernel | calls | avg us | min us | max us | % |\n"
                  "|---|---|---|---|---|---|\n")
@@ -282,7 +283,7 @@ def write_counters(sq_csv, fetch_csv, write_csv, out_md, title, cmdline):
                  "profiler (kernels serialised).  Kernel template arguments: gemm_kernel<qtype, epilogue, BM, BN, "
                  "k-groups> (qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, 1 SwiGLU, 2 CE logits, 3 CE gradient, "
                  "4 linear backward (dX), 5 SwiGLU backward, 6 gate/up backward, 7 dh accumulate); "
-                 "wide::wide_kernel<qtype, epilogue> the 256 x 192 forward tile; ce_bwd_dh_kernel<qtype> one "
+                 "wide::wide_kernel<qtype, epilogue> the 256 x 192 tile (epilogue 0, 2 or 3); ce_bwd_dh_kernel<qtype> one "
                  "vocabulary chunk's CE-gradient tiles with the previous chunk's dh tiles.\n\n")
         fh.write("| kernel | threads | calls | us | MFMA busy | VALU/MFMA | LDS/MFMA | LDS conflict | HBM fetch MB | "
                  "HBM write MB |\n|---|---|---|---|---|---|---|---|---|---|\n")
