@@ -273,8 +273,8 @@ int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E
 // 256 x 192 wide tiles when those fill the chip: their rows at least three
 // quarters used (clamped rows cost as much as real ones), at least 192
 // tiles, and the last round of one tile per CU at least three quarters full.
-bool wide_pays(int qtype, int64_t M, int64_t N, int64_t K) {
-  if (qtype == GQ_Q2_DM || K % GEMM_BK) return false;
+bool wide_pays(int qtype, int64_t M, int64_t N, int64_t K, int r) {
+  if (qtype == GQ_Q2_DM || K % GEMM_BK || r > WIDE_MAX_RANK) return false;
   if (M * 4 < (int64_t)cdiv(M, WIDE_BM) * WIDE_BM * 3) return false;
   const int64_t tiles = (int64_t)cdiv(M, WIDE_BM) * cdiv(N, WIDE_BN);
   if (tiles < 192) return false;
@@ -360,7 +360,7 @@ static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int6
   g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
   g.ntiles = cdiv(N, TILE_BN);
   int tc = pick_fwd_tile(T, T, g.ntiles, K, aligned(L->w_blocks, 16), true);
-  if (!tile_skinny(tc) && wide_pays(L->qtype, T, N, K)) {
+  if (!tile_skinny(tc) && wide_pays(L->qtype, T, N, K, L->rank)) {
     tc = TILE_WIDE;
     g.ntiles = cdiv(N, WIDE_BN);
   }
@@ -1093,11 +1093,10 @@ struct CeWs {
 // tile: the fewest (up to three) that give two full rounds of tiles, kept
 // only if the tiles fill the chip (wide_pays); 0 = 128 x 128 gradient tiles.
 int64_t ce_wide_chunks(int qtype, int64_t T, int64_t V, int64_t H, int r, int64_t C) {
-  if (r > 16) return 0;
   const int64_t nchunks = (V + C - 1) / C;
   int64_t g = 1;
   while (g < 3 && g < nchunks && (int64_t)cdiv(T, WIDE_BM) * cdiv(std::min(g * C, V), WIDE_BN) < 512) ++g;
-  return wide_pays(qtype, T, std::min(g * C, V), H) ? g : 0;
+  return wide_pays(qtype, T, std::min(g * C, V), H, r) ? g : 0;
 }
 CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad) {
   CeWs p;
@@ -1110,7 +1109,7 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
   p.tc_fwd = pick_fwd_tile(T, T, nt_v, H, aligned(L->w_blocks, 16));
   // 256 x 192 tiles when they fill the chip (part_ml, sized for 128-column
   // tiles, holds their fewer partials)
-  if (!tile_skinny(p.tc_fwd) && wide_pays(L->qtype, T, V, H)) p.tc_fwd = TILE_WIDE;
+  if (!tile_skinny(p.tc_fwd) && wide_pays(L->qtype, T, V, H, (int)r)) p.tc_fwd = TILE_WIDE;
   p.part_ml = w.take<float>((int64_t)nt_v * T * 2);
   p.zlab = w.take<float>(T);
   p.term = w.take<float>(T);

@@ -1142,7 +1142,7 @@ hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles * splits);
   if (tilecfg == TILE_WIDE) {
     if constexpr ((EPI == EPI_LIN || EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) && QT != QT_Q2_DM) {
-      if (a.offsets || a.gather || a.K % GEMM_BK) return hipErrorInvalidValue;
+      if (a.offsets || a.gather || a.K % GEMM_BK || a.r > WIDE_MAX_RANK) return hipErrorInvalidValue;
       return launch_wide<QT, EPI>(a, st);
     }
     return hipErrorInvalidValue;

@@ -98,7 +98,7 @@ struct GemmArgs {
 // K % 256 == 0).
 // TILE_WIDE: 256 x 192 tiles on 512 threads (gq_wide_impl.h), dense
 // forward launches and the LM head's gradient tiles, with Q8_0 / Q4_0
-// weights and K % 64 == 0 only.
+// weights, K % 64 == 0 and rank <= WIDE_MAX_RANK only.
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,
@@ -109,6 +109,7 @@ enum TileCfg {
   TILE_WIDE = 6
 };
 constexpr int WIDE_BM = 256, WIDE_BN = 192;
+constexpr int WIDE_MAX_RANK = 16;  // adapter rank the wide tile stages in LDS
 
 inline bool tile_skinny(int cfg) { return cfg >= TILE_SKINNY16 && cfg <= TILE_SKINNY64; }
 inline int tile_bm(int cfg) {

@@ -38,7 +38,7 @@ constexpr int SMEM_MAIN = (2 * A_ST + 2 * B_ST) * 2;
 constexpr int SP = WTN + 8;  // staged epilogue row pitch (bf16)
 constexpr int SMEM_EPI = 8 * WTM * SP * 2;
 constexpr int SMEM = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
-static_assert(BM * 2 * 16 * 8 <= SMEM, "CE partial pairs fit the LDS");
+static_assert(BM * 2 * 16 * 8 + (BM + 64) * 4 <= SMEM, "CE partial pairs and label logits fit the LDS");
 // CE gradient epilogue: one wave column's half of the tile as fp32 [BM][HP],
 // then four ranks of the tile rows' xa (BM x 4) and of the half's B rows
 // (WTN x 4)
@@ -46,6 +46,20 @@ constexpr int HP = WTN + 1;
 constexpr int CEB_Z = BM * HP * 4, CEB_X = BM * 4 * 4, CEB_B = WTN * 4 * 4;
 static_assert(CEB_Z + CEB_X + CEB_B <= SMEM, "CE gradient staging fits the LDS");
 static_assert(3 * WTN * 5 * 4 <= CEB_Z, "column partials fit the staged half");
+// Past the pipeline / epilogue area, written before the main loop and read
+// after it: the adapter-fold operands of the tile (xa rows and s*B rows as
+// bf16 hi + lo, 16 ranks, zero past the rank or the tile's valid rows /
+// columns), and per row the label's column relative to the tile (-1 or BN
+// when it lies in another tile, NO_LABEL when the label is ignored) and the
+// row's log-sum-exp.
+constexpr int FR = WIDE_MAX_RANK;
+constexpr int FOLD_OFF = SMEM;
+constexpr int FOLD_BYTES = (2 * BM * FR + 2 * BN * FR) * 2;
+constexpr int ROW_OFF = FOLD_OFF + FOLD_BYTES;
+constexpr int SMEM_ALL = ROW_OFF + BM * 8;
+static_assert(FR == 16, "one k16 slice of adapter ranks");
+constexpr int32_t NO_LABEL = -(1 << 20);
+static_assert(SMEM_ALL <= 160 * 1024, "fits the CU's LDS");
 
 // A quarter of a block: its fp16 scale (low 16 bits of hdr) and payload
 // bytes [q*NB, q*NB + NB) with NB = 4 (Q4_0) or 8 (Q8_0).
@@ -101,11 +115,12 @@ __device__ __forceinline__ void store_quarter(uint16_t* base, int qq, const RawQ
   }
 }
 
-// Merge of two online (max, sum of exp) pairs into (m, l).
-__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
+// Merge of two (max, sum of exp) pairs into (m, l) with one exp and no
+// branch; a pair with max -inf has sum 0.
+__device__ __forceinline__ void ml_merge1(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;
-  l = (m == -INFINITY ? 0.f : l * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : l2 * __expf(m2 - mn));
+  const float e = __expf(mn == -INFINITY ? 0.f : -fabsf(m - m2));
+  l = m >= m2 ? l + l2 * e : l * e + l2;
   m = mn;
 }
 
@@ -126,26 +141,23 @@ __device__ __forceinline__ void ce_grad_epilogue(const GemmArgs& p, f32x16 (&acc
   const int64_t V = p.V, c0 = p.w_row0;
   const float nv = *p.nvalid;
   const float coef = nv > 0.f ? p.coef / nv : 0.f;
+  const int32_t* LBL = reinterpret_cast<const int32_t*>(smem + ROW_OFF);
+  const float* LSE = reinterpret_cast<const float*>(smem + ROW_OFF + BM * 4);
   // z -> G in the accumulators (rows past M, ignored labels and columns past
-  // w_rows give 0)
+  // w_rows give 0); the rows' label column and lse come from LDS
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t pr = r0 + wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-      int64_t lab = -1;
-      float lse = 0.f;
-      bool valid = false;
-      if (pr < p.M) {
-        lab = p.labels[pr];
-        valid = lab != p.ignore_index && lab >= 0 && lab < V;
-        lse = p.lse[pr];
-      }
+      const int lr = wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int32_t rel = LBL[lr];
+      const float lse = LSE[lr];
+      const bool valid = rel != NO_LABEL;  // also false for rows past M
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
-        const int n = n0 + wn * WTN + b * 32 + (lane & 31);
+        const int lc = wn * WTN + b * 32 + (lane & 31);
         float gv = 0.f;
-        if (valid && n < p.w_rows) gv = coef * (__expf(acc[a][b][v] - lse) - (c0 + n == lab ? 1.f : 0.f));
+        if (valid && n0 + lc < p.w_rows) gv = coef * (__expf(acc[a][b][v] - lse) - (lc == rel ? 1.f : 0.f));
         acc[a][b][v] = gv;
       }
     }
@@ -265,7 +277,7 @@ template <int QT, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
   static_assert(EPI == EPI_LIN || EPI == EPI_CE_FWD || EPI == EPI_CE_BWD, "wide epilogues");
   constexpr int BS = QTraits<QT>::BS;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_ALL];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Bs = As + 2 * A_ST;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -362,11 +374,69 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
     }
   };
 
-  // prologue: slices 0 and 1 in registers, slice 0 into stage 0
-  GQW_LOAD_A(0, a00, a01, a02, a03)
-  load_w(0, W0);
-  GQW_LOAD_A(1, a10, a11, a12, a13)
-  load_w(1, W1);
+  // prologue: slices 0 and 1 in registers, slice 0 into stage 0; the fold
+  // operands and the per-row label / lse go to their LDS area meanwhile (so
+  // their latency hides behind the pipeline instead of after it)
+  const int r = p.r;
+  const float s = p.s;
+  auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)v[i];
+      hi[i] = h;
+      lo[i] = (__bf16)(v[i] - (float)h);
+    }
+  };
+  uint16_t* XH = reinterpret_cast<uint16_t*>(smem + FOLD_OFF);  // [BM][FR]
+  uint16_t* XL = XH + BM * FR;
+  uint16_t* YH = XL + BM * FR;                                   // [BN][FR]
+  uint16_t* YL = YH + BN * FR;
+  int32_t* LBL = reinterpret_cast<int32_t*>(smem + ROW_OFF);     // [BM]
+  float* LSE = reinterpret_cast<float*>(smem + ROW_OFF + BM * 4);  // [BM]
+  {
+    // thread t: xa row t >> 1 and (t < 2 BN) s*B row t >> 1, ranks 8 (t & 1) .. +8
+    const int j0 = (tid & 1) * 8;
+    const int64_t pr = r0 + (tid >> 1);
+    float xv[8], bv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = (pr < p.M && j0 + i < r) ? p.rv0[pr * r + j0 + i] : 0.f;
+    const int col = n0 + (tid >> 1);
+    const bool bt = tid < 2 * BN;
+    const float* Bw = p.lB0 + (int64_t)(p.w_row0 + col) * r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bv[i] = (bt && col < p.w_rows && j0 + i < r) ? s * Bw[j0 + i] : 0.f;
+    int32_t rel = NO_LABEL;
+    float ls = 0.f;
+    if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+      if (tid < BM && r0 + tid < p.M) {
+        const int64_t lab = p.labels[r0 + tid];
+        if (lab != p.ignore_index && lab >= 0 && lab < p.V) {
+          const int64_t rc = lab - p.w_row0 - n0;
+          rel = rc < 0 ? -1 : (rc >= BN ? BN : (int32_t)rc);
+        }
+        if constexpr (EPI == EPI_CE_BWD) ls = p.lse[r0 + tid];
+      }
+    }
+    GQW_LOAD_A(0, a00, a01, a02, a03)
+    load_w(0, W0);
+    GQW_LOAD_A(1, a10, a11, a12, a13)
+    load_w(1, W1);
+    bf16x8 h8, l8;
+    split8(xv, h8, l8);
+    *reinterpret_cast<bf16x8*>(XH + (tid >> 1) * FR + j0) = h8;
+    *reinterpret_cast<bf16x8*>(XL + (tid >> 1) * FR + j0) = l8;
+    if (bt) {
+      split8(bv, h8, l8);
+      *reinterpret_cast<bf16x8*>(YH + (tid >> 1) * FR + j0) = h8;
+      *reinterpret_cast<bf16x8*>(YL + (tid >> 1) * FR + j0) = l8;
+    }
+    if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+      if (tid < BM) {
+        LBL[tid] = rel;
+        LSE[tid] = ls;
+      }
+    }
+  }
   GQW_STORE_A(0, a00, a01, a02, a03)
   store_w(0, W0);
   __syncthreads();
@@ -394,39 +464,22 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
 #undef GQW_STORE_A
 
   // ---- rank-r adapter term on the MFMA: acc[row][col] += sum_j xa[row][j] *
-  // s * B[col][j], one k16 slice per 16 ranks, bf16 hi + lo parts (three
-  // products: hi*hi + hi*lo + lo*hi)
-  const int r = p.r;
-  const float s = p.s;
-  auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = (__bf16)v[i];
-      hi[i] = h;
-      lo[i] = (__bf16)(v[i] - (float)h);
-    }
-  };
-  const float* Bw = p.lB0 + (int64_t)p.w_row0 * r;  // B rows of this launch's columns
-  for (int qr = 0; qr * 16 < r; ++qr) {
-    const int j0 = qr * 16 + (lane >> 5) * 8;
+  // s * B[col][j], one k16 slice (rank <= 16) from the LDS copies, bf16 hi +
+  // lo parts (three products: hi*hi + hi*lo + lo*hi)
+  {
+    const int jo = (lane >> 5) * 8;
     bf16x8 ah[TM], al[TM];
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
-      const int64_t row = r0 + wm * WTM + a * 32 + (lane & 31);
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (row < p.M && j0 + i < r) ? p.rv0[row * r + j0 + i] : 0.f;
-      split8(v, ah[a], al[a]);
+      const int row = wm * WTM + a * 32 + (lane & 31);
+      ah[a] = *reinterpret_cast<const bf16x8*>(XH + row * FR + jo);
+      al[a] = *reinterpret_cast<const bf16x8*>(XL + row * FR + jo);
     }
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const int col = n0 + wn * WTN + b * 32 + (lane & 31);
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = (col < p.w_rows && j0 + i < r) ? s * Bw[(int64_t)col * r + j0 + i] : 0.f;
-      bf16x8 bh, bl;
-      split8(v, bh, bl);
+      const int col = wn * WTN + b * 32 + (lane & 31);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(YH + col * FR + jo);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(YL + col * FR + jo);
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bh, acc[a][b], 0, 0, 0);
@@ -437,58 +490,63 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
   }
 
   if constexpr (EPI == EPI_CE_FWD) {
-    // Each lane merges its three columns of a row, then the adjacent lane's
-    // (xor 1); the 16 pairs of each wave's half row go through LDS
-    // ([256 rows][2 wave columns][16] pairs, 64 KB), and two threads per
-    // row merge them in a fixed order.
+    // Branch-free per (row, lane pair): the pair's six columns give the max
+    // (one xor-1 exchange) and the sum of exp against it (three exps per
+    // lane, one exchange); the 16
+    // pairs of each wave's half row go through LDS ([256 rows][2 wave
+    // columns][16] pairs, 64 KB), and two threads per row combine them (max
+    // first, then the rescaled sum) and then the two halves.  A lane holding
+    // the row's label column writes that logit to an LDS slot of the row,
+    // every other lane to a slot of its own, so the loop has no branches.
     __syncthreads();  // every wave is done reading the operand stages
     float2* P = reinterpret_cast<float2*>(smem);
-    const int c0 = n0 + wn * WTN + (lane & 31);
+    float* ZL = reinterpret_cast<float*>(smem + BM * 2 * 16 * 8);  // [BM] label logits + [64] dump slots
+    const int lcol0 = wn * WTN + (lane & 31);  // this lane's first column in the tile
+    bool cok[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b) cok[b] = n0 + lcol0 + b * 32 < p.w_rows;
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int lr = wm * WTM + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int64_t pr = r0 + lr;
-        float m = -INFINITY, l = 0.f;
+        float z[TN];
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-          if (c0 + b * 32 < p.w_rows) m = fmaxf(m, acc[a][b][v]);
-        if (m != -INFINITY) {
+        for (int b = 0; b < TN; ++b) z[b] = cok[b] ? acc[a][b][v] : -INFINITY;
+        float m = z[0];
 #pragma unroll
-          for (int b = 0; b < TN; ++b)
-            if (c0 + b * 32 < p.w_rows) l += __expf(acc[a][b][v] - m);
-        }
-        if (pr < p.M) {
-          const int64_t lab = p.labels[pr];
-          const int64_t lc = lab - c0;
-          if (lab != p.ignore_index && lab >= 0 && lab < p.V && lc >= 0 && lc % 32 == 0 && lc / 32 < TN) {
+        for (int b = 1; b < TN; ++b) m = fmaxf(m, z[b]);
+        m = fmaxf(m, __shfl_xor(m, 1));  // the pair's max: the two sums share it
+        const float ms = m == -INFINITY ? 0.f : m;
+        float l = 0.f;
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
-              if (lc == 32 * b) p.f1[pr] = acc[a][b][v];
-          }
-        }
-        const float m2 = __shfl_xor(m, 1), l2 = __shfl_xor(l, 1);
-        if ((lane & 1) == 0) {
-          ml_merge(m, l, m2, l2);
-          P[(lr * 2 + wn) * 16 + ((lane & 31) >> 1)] = make_float2(m, l);
-        }
+        for (int b = 0; b < TN; ++b) l += __expf(z[b] - ms);
+        const int lc = LBL[lr] - lcol0;
+        const bool hit = lc >= 0 && lc < 32 * TN && (lc & 31) == 0;
+        ZL[hit ? lr : BM + lane] = lc == 0 ? acc[a][0][v] : (lc == 32 ? acc[a][1][v] : acc[a][2][v]);
+        l += __shfl_xor(l, 1);
+        P[(lr * 2 + wn) * 16 + ((lane & 31) >> 1)] = make_float2(m, l);  // both lanes: same pair
       }
     __syncthreads();
     const int row = tid >> 1, h = tid & 1;
-    float m = -INFINITY, l = 0.f;
+    float2 q[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float2 q = P[(row * 2 + h) * 16 + i];
-      ml_merge(m, l, q.x, q.y);
-    }
+    for (int i = 0; i < 16; ++i) q[i] = P[(row * 2 + h) * 16 + i];
+    float m = q[0].x;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, q[i].x);
+    const float ms = m == -INFINITY ? 0.f : m;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l += q[i].y * __expf(q[i].x - ms);  // q.y = 0 where q.x = -inf
     const float m2 = __shfl_xor(m, 1), l2 = __shfl_xor(l, 1);
     if (h == 0 && r0 + row < p.M) {
-      ml_merge(m, l, m2, l2);  // wave column 0, then 1
+      ml_merge1(m, l, m2, l2);  // wave column 0, then 1
       float* dst = p.f0 + ((int64_t)(p.ntile_base + nt) * p.M + r0 + row) * 2;
       dst[0] = m;
       dst[1] = l;
     }
+    if (tid < BM && LBL[tid] >= 0 && LBL[tid] < BN && r0 + tid < p.M) p.f1[r0 + tid] = ZL[tid];
     return;
   }
 
