@@ -436,6 +436,112 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
     full = full && (n0 + BN <= p.w_rows);
   }
 
+  // ---- rank-r adapter term, folded into the accumulators on the MFMA:
+  //   acc[row][col] += sum_j X(row, j) * s * Y(col, j)
+  // over one k16 slice per 16 adapter ranks.  X and s*Y are split into bf16
+  // hi + lo parts and accumulated as hi*hi + hi*lo + lo*hi (about 16
+  // significant bits, far inside the bf16 output precision).  Row / column
+  // operands follow the MFMA layout: lane l holds row (col) l%32 and ranks
+  // 8*(l/32) .. +8 of the slice.
+  const int r = p.r;
+  const float s = p.s;
+  constexpr int NSET = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr bool FOLD = EPI != EPI_DH_ACC;
+  // (split-K parts get the adapter term in the fixup instead).  It runs
+  // before the main loop, right after the first tiles' loads are issued,
+  // so the latency of its operand loads hides behind theirs; with two
+  // k-groups only the first group adds it.
+  auto fold_adapter = [&]() __attribute__((always_inline)) {
+  if constexpr (FOLD) if (p.ksplit <= 1 && grp == 0) {
+    const int rtot = EPI == EPI_GATEUP_BWD ? 2 * r : r;
+    const float* Y0;
+    const float* Y1 = nullptr;
+    if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD || EPI == EPI_GATEUP_BWD) {
+      Y0 = p.lA0 + (int64_t)e * p.lA_estride;  // A [r][N]: Y(c, j) = A[j*N + c]
+      if constexpr (EPI == EPI_GATEUP_BWD) Y1 = p.lA1 + (int64_t)e * p.lA_estride;
+    } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+      Y0 = p.lB0 + (int64_t)p.w_row0 * r;      // B [V][r], columns from w_row0
+    } else {
+      Y0 = p.lB0 + (int64_t)e * p.lB_estride;  // B [N][r]
+      if constexpr (EPI == EPI_SWIGLU) Y1 = p.lB1 + (int64_t)e * p.lB_estride;
+    }
+    auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)v[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(v[i] - (float)h);
+      }
+    };
+    for (int q = 0; q * 16 < rtot; ++q) {
+      const int j0 = q * 16 + (lane >> 5) * 8;
+      bf16x8 ah[TM][NSET], al[TM][NSET];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int64_t row = r0 + wm * WTM + a * 32 + (lane & 31);
+        const bool ok = row < r1;
+#pragma unroll
+        for (int st = 0; st < NSET; ++st) {
+          const float* X = st == 0 ? p.rv0 : p.rv1;
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i;
+            float x = 0.f;
+            if (ok && j < rtot) {
+              if constexpr (EPI == EPI_GATEUP_BWD)
+                x = j < r ? p.rv0[row * r + j] : p.rv1[row * r + j - r];
+              else
+                x = X[row * r + j];
+            }
+            v[i] = x;
+          }
+          split8(v, ah[a][st], al[a][st]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int st = EPI == EPI_SWIGLU ? (b & 1) : 0;
+        int col;
+        bool ok;
+        if constexpr (EPI == EPI_SWIGLU) {
+          col = (n0 >> 1) + (wn * (TN / 2) + (b >> 1)) * 32 + (lane & 31);
+          ok = col < p.w_rows;
+        } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
+          col = n0 + LCb(b);
+          ok = col < p.w_rows;
+        } else {
+          col = n0 + LCb(b);
+          ok = col < p.N;
+        }
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = j0 + i;
+          float y = 0.f;
+          if (ok && j < rtot) {
+            if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD)
+              y = Y0[(int64_t)j * p.N + col];
+            else if constexpr (EPI == EPI_GATEUP_BWD)
+              y = j < r ? Y0[(int64_t)j * p.N + col] : Y1[(int64_t)(j - r) * p.N + col];
+            else
+              y = (st == 0 ? Y0 : Y1)[(int64_t)col * r + j];
+          }
+          v[i] = s * y;
+        }
+        bf16x8 bh, bl;
+        split8(v, bh, bl);
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bh, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bl, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a][st], bh, acc[a][b], 0, 0, 0);
+        }
+      }
+    }
+  }
+  };
+
   auto pipeline = [&](auto full_c, auto na_c) {
     constexpr bool FULL = decltype(full_c)::value;
     constexpr int NA = decltype(na_c)::value;
@@ -524,6 +630,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
       load_a(KT(1), areg1, amsk1);
       load_w(KT(1), wr1, wmsk1);
     }
+    fold_adapter();
     store_a(0, areg0, amsk0);
     store_w(0, wr0, wmsk0);
     __syncthreads();
@@ -617,107 +724,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
           acc[a][b][4 * v4 + 2] += q.z;
           acc[a][b][4 * v4 + 3] += q.w;
         }
-  }
-
-  // ---- rank-r adapter term, folded into the accumulators on the MFMA:
-  //   acc[row][col] += sum_j X(row, j) * s * Y(col, j)
-  // over one k16 slice per 16 adapter ranks.  X and s*Y are split into bf16
-  // hi + lo parts and accumulated as hi*hi + hi*lo + lo*hi (about 16
-  // significant bits, far inside the bf16 output precision).  Row / column
-  // operands follow the MFMA layout: lane l holds row (col) l%32 and ranks
-  // 8*(l/32) .. +8 of the slice.
-  const int r = p.r;
-  const float s = p.s;
-  constexpr int NSET = EPI == EPI_SWIGLU ? 2 : 1;
-  constexpr bool FOLD = EPI != EPI_DH_ACC;
-  // (split-K parts get the adapter term in the fixup instead)
-  if constexpr (FOLD) if (p.ksplit <= 1) {
-    const int rtot = EPI == EPI_GATEUP_BWD ? 2 * r : r;
-    const float* Y0;
-    const float* Y1 = nullptr;
-    if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD || EPI == EPI_GATEUP_BWD) {
-      Y0 = p.lA0 + (int64_t)e * p.lA_estride;  // A [r][N]: Y(c, j) = A[j*N + c]
-      if constexpr (EPI == EPI_GATEUP_BWD) Y1 = p.lA1 + (int64_t)e * p.lA_estride;
-    } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
-      Y0 = p.lB0 + (int64_t)p.w_row0 * r;      // B [V][r], columns from w_row0
-    } else {
-      Y0 = p.lB0 + (int64_t)e * p.lB_estride;  // B [N][r]
-      if constexpr (EPI == EPI_SWIGLU) Y1 = p.lB1 + (int64_t)e * p.lB_estride;
-    }
-    auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)v[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(v[i] - (float)h);
-      }
-    };
-    for (int q = 0; q * 16 < rtot; ++q) {
-      const int j0 = q * 16 + (lane >> 5) * 8;
-      bf16x8 ah[TM][NSET], al[TM][NSET];
-#pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        const int64_t row = r0 + wm * WTM + a * 32 + (lane & 31);
-        const bool ok = row < r1;
-#pragma unroll
-        for (int st = 0; st < NSET; ++st) {
-          const float* X = st == 0 ? p.rv0 : p.rv1;
-          float v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int j = j0 + i;
-            float x = 0.f;
-            if (ok && j < rtot) {
-              if constexpr (EPI == EPI_GATEUP_BWD)
-                x = j < r ? p.rv0[row * r + j] : p.rv1[row * r + j - r];
-              else
-                x = X[row * r + j];
-            }
-            v[i] = x;
-          }
-          split8(v, ah[a][st], al[a][st]);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int st = EPI == EPI_SWIGLU ? (b & 1) : 0;
-        int col;
-        bool ok;
-        if constexpr (EPI == EPI_SWIGLU) {
-          col = (n0 >> 1) + (wn * (TN / 2) + (b >> 1)) * 32 + (lane & 31);
-          ok = col < p.w_rows;
-        } else if constexpr (EPI == EPI_CE_FWD || EPI == EPI_CE_BWD) {
-          col = n0 + LCb(b);
-          ok = col < p.w_rows;
-        } else {
-          col = n0 + LCb(b);
-          ok = col < p.N;
-        }
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int j = j0 + i;
-          float y = 0.f;
-          if (ok && j < rtot) {
-            if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_DOWN_BWD)
-              y = Y0[(int64_t)j * p.N + col];
-            else if constexpr (EPI == EPI_GATEUP_BWD)
-              y = j < r ? Y0[(int64_t)j * p.N + col] : Y1[(int64_t)(j - r) * p.N + col];
-            else
-              y = (st == 0 ? Y0 : Y1)[(int64_t)col * r + j];
-          }
-          v[i] = s * y;
-        }
-        bf16x8 bh, bl;
-        split8(v, bh, bl);
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bh, acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a][st], bl, acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a][st], bh, acc[a][b], 0, 0, 0);
-        }
-      }
-    }
   }
 
   // ---- epilogues.  acc[a][b][v] sits at local row
