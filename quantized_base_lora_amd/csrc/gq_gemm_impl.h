@@ -74,7 +74,9 @@ constexpr bool epi_stages(int epi) {
   return epi == EPI_CE_FWD || epi == EPI_CE_BWD || epi == EPI_DOWN_BWD;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// logistic function with the hardware reciprocal (about 1 ulp, no division
+// sequence)
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // all-ones / all-zeros mask the optimiser cannot see through (an empty
 // register-only asm), so a load whose result is masked is never turned back
@@ -849,18 +851,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
     const int width = 1 + 2 * r;
     const float* Bg = p.lB1 + (int64_t)e * p.lB_estride;
     const float* Bu = p.lB2 + (int64_t)e * p.lB_estride;
+    constexpr int BSTN = 2 * BN * 8 / NTHR;  // Bst values per thread
+    auto bst_value = [&](int idx, int jb) {
+      const int mat = idx / (BN * 8), c = (idx >> 3) % BN, j = idx & 7;
+      const int col = n0 + c;
+      return (jb + j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + jb + j] : 0.f;
+    };
+    // the first 8 ranks of Bg, Bu are loaded before the LDS staging (their
+    // latency overlaps it)
+    float bsv[BSTN];
+#pragma unroll
+    for (int i = 0; i < BSTN; ++i) bsv[i] = bst_value(tid + NTHR * i, 0);
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) Z[LR(a, v) * ZD + LC(b)] = acc[a][b][v];
-    // 4 threads per tile row, 4 chunks of 8 columns each (a wave's g, u
-    // loads and dg, du stores cover 16 rows x 64 contiguous bytes per
-    // chunk), 64 rows per pass; the row partials are summed over the row's
-    // 4 threads with xor shuffles (fixed order) and written by its first
-    // thread
-    constexpr int TPR = 4, RPP = NTHR / TPR, CPT = BN / TPR / 8;
+    // TPR threads per tile row (2 for 128-row tiles, one pass over the
+    // rows; 4 for 64-row tiles), CPT chunks of 8 columns each, RPP rows per
+    // pass; the row partials are summed over the row's threads with xor
+    // shuffles (fixed order) and written by its first thread
+    constexpr int TPR = BM >= 128 ? 2 : 4, RPP = NTHR / TPR, CPT = BN / TPR / 8;
+    static_assert(BM % RPP == 0, "whole row passes");
     const int cq = tid % TPR, rsub = tid / TPR;
     auto segment = [&](auto rc, const int jb) {
       constexpr int R = decltype(rc)::value;
@@ -945,12 +958,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
       }
     };
     for (int jb = 0; jb < r; jb += 8) {
-      if (jb) __syncthreads();  // the previous pass is done with Bst
-      for (int idx = tid; idx < 2 * BN * 8; idx += NTHR) {
-        const int mat = idx / (BN * 8), c = (idx >> 3) % BN, j = idx & 7;
-        const int col = n0 + c;
-        Bst[idx] = (jb + j < r && col < p.N) ? (mat ? Bu : Bg)[(int64_t)col * r + jb + j] : 0.f;
+      if (jb) {
+        __syncthreads();  // the previous pass is done with Bst
+#pragma unroll
+        for (int i = 0; i < BSTN; ++i) bsv[i] = bst_value(tid + NTHR * i, jb);
       }
+#pragma unroll
+      for (int i = 0; i < BSTN; ++i) Bst[tid + NTHR * i] = bsv[i];
       __syncthreads();
       if (r - jb <= 4)
         segment(IntC<4>{}, jb);
