@@ -798,26 +798,68 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // n-subtiles come in (gate, up) pairs over the same 32 intermediate rows
+    // n-subtiles come in (gate, up) pairs over the same 32 intermediate
+    // rows.  h, g, u of the wave's WTM x IW block go through a wave-private
+    // LDS region (three arrays, rows of IW + 8 bf16, past the split-K
+    // reduction buffer) and leave as 16-byte row stores when the rows allow
+    // it; else one 2-byte store per value.
+    constexpr int IW = TN / 2 * 32;  // intermediate columns of the wave
+    const int ibase = (n0 >> 1) + wn * IW;
+    const bool vec = ((uintptr_t)p.o0 % 16 == 0) && ((uintptr_t)p.o1 % 16 == 0) &&
+                     ((uintptr_t)p.o2 % 16 == 0) && (p.ldo % 8 == 0) && (p.w_rows % 8 == 0);
+    if (vec) {
+      constexpr int SPI = IW + 8;
+      uint16_t* Ws = reinterpret_cast<uint16_t*>(smem + (KS > 1 ? BM * BN * 4 : 0)) + wave * 3 * WTM * SPI;
+      static_assert((KS > 1 ? BM * BN * 4 : 0) + 4 * 3 * WTM * SPI * 2 <= G::SMEM, "staging fits");
 #pragma unroll
-    for (int b2 = 0; b2 < TN / 2; ++b2) {
-      const int i = (n0 >> 1) + (wn * (TN / 2) + b2) * 32 + (lane & 31);
-      if (i >= p.w_rows) continue;
+      for (int b2 = 0; b2 < TN / 2; ++b2)
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t pr = r0 + LR(a, v);
-          if (pr < r1) {
+          for (int v = 0; v < 16; ++v) {
+            const int lw = a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
             const float g = acc[a][2 * b2][v];
             const float u = acc[a][2 * b2 + 1][v];
             const float h = g * sigmoidf_(g) * u;
-            const int64_t o = pr * p.ldo + i;
-            p.o0[o] = f2bf(h);
-            p.o1[o] = f2bf(g);
-            p.o2[o] = f2bf(u);
+            const int c = b2 * 32 + (lane & 31);
+            Ws[lw * SPI + c] = f2bf(h);
+            Ws[(WTM + lw) * SPI + c] = f2bf(g);
+            Ws[(2 * WTM + lw) * SPI + c] = f2bf(u);
           }
+      // (the wave's own region: its LDS writes complete before these reads)
+      constexpr int CH = IW / 8;
+#pragma unroll
+      for (int i = lane; i < 3 * WTM * CH; i += 64) {
+        const int arr = i / (WTM * CH), q = i % (WTM * CH), rr = q / CH, cc = (q % CH) * 8;
+        const int64_t pr = r0 + wm * WTM + rr;
+        const int ic = ibase + cc;
+        if (pr < r1 && ic < p.w_rows) {
+          uint16_t* dst = arr == 0 ? p.o0 : (arr == 1 ? p.o1 : p.o2);
+          *reinterpret_cast<uint4*>(dst + pr * p.ldo + ic) =
+              *reinterpret_cast<const uint4*>(Ws + (arr * WTM + rr) * SPI + cc);
         }
+      }
+    } else {
+#pragma unroll
+      for (int b2 = 0; b2 < TN / 2; ++b2) {
+        const int i = ibase + b2 * 32 + (lane & 31);
+        if (i >= p.w_rows) continue;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t pr = r0 + LR(a, v);
+            if (pr < r1) {
+              const float g = acc[a][2 * b2][v];
+              const float u = acc[a][2 * b2 + 1][v];
+              const float h = g * sigmoidf_(g) * u;
+              const int64_t o = pr * p.ldo + i;
+              p.o0[o] = f2bf(h);
+              p.o1[o] = f2bf(g);
+              p.o2[o] = f2bf(u);
+            }
+          }
+      }
     }
   } else if constexpr (EPI == EPI_DH_ACC) {
 #pragma unroll
