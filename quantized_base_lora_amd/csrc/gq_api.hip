@@ -392,10 +392,12 @@ static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int6
 namespace {
 struct LinBwdWs {
   float* dyB;
+  float* dyB_part;  // column-range partials of dY B when the row-dot is cut (else nullptr)
   float* part_dB;
   float* part_dA;
   float* part_dx;  // split-K sums of a small dX launch (else nullptr)
   int ks_dx;
+  int cs_dyB;      // column ranges of the dY B row-dot (1 = one)
 };
 int lin_rc(const gq_lora_linear* L, int64_t T) {
   return pick_rc(T, L->n_in > L->n_out ? L->n_in : L->n_out, L->rank, 1);
@@ -404,6 +406,11 @@ LinBwdWs plan_lin_bwd(Ws& w, const gq_lora_linear* L, int64_t T) {
   LinBwdWs p;
   const int64_t slots = colred_slots(T, lin_rc(L, T), 1);
   p.dyB = w.take<float>(T * L->rank);
+  // dY B over column ranges when 16-row workgroups alone leave CUs idle;
+  // the dX MMQ's adapter fold (tile path, unsplit) or else the dB / dA
+  // reduction adds the partials and stores dY B for the other
+  p.cs_dyB = rowdot_csplit(T, L->n_out);
+  p.dyB_part = p.cs_dyB > 1 ? w.take<float>((int64_t)p.cs_dyB * T * L->rank) : nullptr;
   p.part_dB = w.take<float>(slots * L->n_out * L->rank);
   p.part_dA = w.take<float>(slots * L->n_in * L->rank);
   p.ks_dx = small_split(T, L->n_in, L->n_out);
@@ -454,33 +461,23 @@ static int linear_lora_bwd_impl(const gq_lora_linear* L, const uint16_t* x, cons
   RowDotArgs rd;
   memset(&rd, 0, sizeof rd);
   rd.M = T; rd.C = N; rd.r = r; rd.act = dy; rd.lda = N; rd.gdiv = 1; rd.E = 1;
-  rd.W[0] = L->B; rd.w_jstride = 1; rd.w_cstride = r; rd.out[0] = P.dyB; rd.nout = 1;
+  rd.W[0] = L->B; rd.w_jstride = 1; rd.w_cstride = r; rd.nout = 1;
+  rd.out[0] = P.cs_dyB > 1 ? P.dyB_part : P.dyB; rd.csplit = P.cs_dyB;
   HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_bwd: dY B");
 
-  // dB = s dY^T xa and dA = s (dY B)^T x: both reductions in one launch,
-  // both finishes in one launch
-  ColRedArgs cr;
-  memset(&cr, 0, sizeof cr);
-  cr.M = T; cr.C = N; cr.r = r; cr.U = dy; cr.ldu = N; cr.gdiv = 1; cr.Vv = xa;
-  cr.E = 1; cr.rc = rcl; cr.slots = slots; cr.part = P.part_dB;
-  cr.njobs = 2;
-  cr.C_1 = K; cr.U_1 = x; cr.ldu_1 = K; cr.gdiv_1 = 1; cr.Vv_1 = P.dyB; cr.part_1 = P.part_dA;
-  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB, dA partials");
-  ColFinJobs fj;
-  memset(&fj, 0, sizeof fj);
-  fj.n = 2;
-  fj.part[0] = P.part_dB; fj.out[0] = dB; fj.C[0] = N; fj.transpose[0] = 0;
-  fj.part[1] = P.part_dA; fj.out[1] = dA; fj.C[1] = K; fj.transpose[1] = 1;
-  HIP_TRY(launch_colred_finish_dense(fj, slots, r, L->scale, st), "gq_linear_lora_bwd: dB, dA");
-
-  if (dx) {
+  // dX MMQ.  With dY B as column-range partials, the tile path's adapter
+  // fold adds them and stores dY B, and runs before the dB / dA reductions;
+  // otherwise (split or skinny launches, or no dx) the reductions do.
+  const int tc0 = pick_nn_tile(T, T, cdiv(K, TILE_BN), K, aligned(L->w_blocks, 16), N, true);
+  const bool split = dx && P.ks_dx > 1 && !tile_skinny(tc0) && aligned(dx, 4);
+  const bool fold_sums = dx && P.cs_dyB > 1 && !split && !tile_skinny(tc0);
+  auto launch_dx = [&]() -> int {
     GemmArgs g = gemm_defaults();
     g.M = T; g.N = K; g.K = N;
     g.a0 = dy; g.lda = N;
     g.w0 = static_cast<const uint8_t*>(L->w_blocks);
     g.w_rowbytes = rowbytes(L); g.w_nb = K / 32; g.w_rows = N;
-    int tc = pick_nn_tile(T, T, cdiv(K, TILE_BN), K, aligned(L->w_blocks, 16), N, true);
-    const bool split = P.ks_dx > 1 && !tile_skinny(tc) && aligned(dx, 4);
+    int tc = tc0;
     if (split) {
       tc = TILE_64x128;
       g.ksplit = P.ks_dx;
@@ -489,12 +486,40 @@ static int linear_lora_bwd_impl(const gq_lora_linear* L, const uint16_t* x, cons
     g.ntiles = cdiv(K, nn_tile_bn(tc));
     g.mtiles = cdiv(T, tile_bm(tc));
     g.s = L->scale; g.r = r; g.lA0 = L->A; g.rv0 = P.dyB;
+    if (fold_sums) {
+      g.rv0 = P.dyB_part; g.rv_parts = P.cs_dyB; g.rv_out = P.dyB;
+    }
     g.o0 = dx; g.ldo = K;
     HIP_TRY(launch_gemm(L->qtype, EPI_LIN_BWD, tc, g, st), "gq_linear_lora_bwd: dX MMQ");
     if (split)  // adapter term s (dY B) A: A is [r][n_in]
       HIP_TRY(launch_split_fixup(P.part_dx, P.ks_dx, T, K, P.dyB, r, L->A, 1, K, L->scale, dx, K, st),
               "gq_linear_lora_bwd: dX split sums");
+    return GQ_OK;
+  };
+  if (fold_sums && (rc = launch_dx())) return rc;
+
+  // dB = s dY^T xa and dA = s (dY B)^T x: both reductions in one launch,
+  // both finishes in one launch
+  ColRedArgs cr;
+  memset(&cr, 0, sizeof cr);
+  cr.M = T; cr.C = N; cr.r = r; cr.U = dy; cr.ldu = N; cr.gdiv = 1; cr.Vv = xa;
+  cr.E = 1; cr.rc = rcl; cr.slots = slots; cr.part = P.part_dB;
+  cr.njobs = 2;
+  cr.C_1 = K; cr.U_1 = x; cr.ldu_1 = K; cr.gdiv_1 = 1; cr.part_1 = P.part_dA;
+  if (P.cs_dyB > 1 && !fold_sums) {  // the partials summed here, dY B stored for the dX MMQ
+    cr.Vv_1 = P.dyB_part; cr.vsplit_1 = P.cs_dyB; cr.vfinal_1 = P.dyB;
+  } else {
+    cr.Vv_1 = P.dyB;
   }
+  HIP_TRY(launch_colred(cr, st), "gq_linear_lora_bwd: dB, dA partials");
+  ColFinJobs fj;
+  memset(&fj, 0, sizeof fj);
+  fj.n = 2;
+  fj.part[0] = P.part_dB; fj.out[0] = dB; fj.C[0] = N; fj.transpose[0] = 0;
+  fj.part[1] = P.part_dA; fj.out[1] = dA; fj.C[1] = K; fj.transpose[1] = 1;
+  HIP_TRY(launch_colred_finish_dense(fj, slots, r, L->scale, st), "gq_linear_lora_bwd: dB, dA");
+
+  if (dx && !fold_sums && (rc = launch_dx())) return rc;
   return GQ_OK;
 }
 

@@ -491,10 +491,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
             const int j = j0 + i;
             float x = 0.f;
             if (ok && j < rtot) {
-              if constexpr (EPI == EPI_GATEUP_BWD)
+              if constexpr (EPI == EPI_GATEUP_BWD) {
                 x = j < r ? p.rv0[row * r + j] : p.rv1[row * r + j - r];
-              else
+              } else if constexpr (EPI == EPI_LIN_BWD) {
                 x = X[row * r + j];
+                for (int sp = 1; sp < p.rv_parts; ++sp) x += X[sp * p.M * r + row * r + j];
+                if (p.rv_out && ntile == 0 && wn == 0) p.rv_out[row * r + j] = x;
+              } else {
+                x = X[row * r + j];
+              }
             }
             v[i] = x;
           }

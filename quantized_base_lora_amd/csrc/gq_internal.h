@@ -62,6 +62,11 @@ struct GemmArgs {
   int64_t lB_estride;
   const float* rv0;    // per-row rank vectors [M][r]
   const float* rv1;
+  // EPI_LIN_BWD: rv0 as rv_parts partial arrays (rv0 + s * M * r) summed by
+  // the adapter fold; with rv_out, the workgroups of column tile 0 store
+  // that sum (rv_out[p][j]).  0 or 1: one array.
+  int32_t rv_parts;
+  float* rv_out;
   uint16_t* o0;
   uint16_t* o1;
   uint16_t* o2;
@@ -171,7 +176,14 @@ struct RowDotArgs {
   const int32_t* sorted;
   const float* win;  // optional side job: wout[p][j] = wflat[sorted[p]] * win[p][j]
   float* wout;       // over the same rows (needs wflat, sorted)
+  // dense only (no tile16, out2, wout): the columns are cut into csplit
+  // ranges, one workgroup each, and range s writes its partial sums to
+  // out[o] + s * M * r (the consumer adds the csplit partials); 0 or 1 = no cut
+  int32_t csplit;
 };
+// Column ranges for a dense row-dot: enough workgroups to give every CU one
+// (at most 4 ranges, each at least 768 columns).
+int rowdot_csplit(int64_t M, int64_t C);
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st);
 
 // out[t][n] = bf16( sum_{s < ksplit} part[s][t][n] + scale * sum_{j < r} X[t][j] * Y[n*ys_n + j*ys_j] )
@@ -213,6 +225,11 @@ struct ColRedArgs {
   int32_t gdiv_1;
   const float* Vv_1;
   float* part_1;
+  // job 1's rank vectors as vsplit_1 partial arrays (Vv_1 + s * M * r) that
+  // are summed on load (0 or 1: one array); with vfinal_1, workgroups of
+  // column block 0 also store that sum for their rows (vfinal_1[p][j])
+  int32_t vsplit_1;
+  float* vfinal_1;
   // optional side job over the same slots (workgroups of column block 0,
   // job 0): the row sums of the grouped down MMQ's per-n-tile partials
   // (dfin_part [ntiles][M][1 + 2r] -> dw_flat[sorted[p]], dgB[p], duB[p])

@@ -122,11 +122,13 @@ __device__ __forceinline__ int find_expert(const int32_t* offsets, int E, int64_
 // WT: W stored [C][r] (a LoRA B matrix) instead of [r][C] (an A matrix).
 constexpr int RD_WAVES = 8;
 
-template <int NOUT, bool WT>
+// CS: dense rows over a.csplit column ranges (one workgroup each).
+template <int NOUT, bool WT, bool CS>
 __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs a) {
   __shared__ f32x4 red[RD_WAVES - 1][NOUT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = a.r;
+  const int cs = CS ? a.csplit : 1;  // column ranges (dense only)
   // rows p0 .. p1-1 of one expert: grouped rows come in expert-aligned
   // 16-row tiles (prefix tile16), so every block makes one pass with one
   // expert's rank vectors
@@ -144,8 +146,16 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
     p0 = (int64_t)a.offsets[e] + (int64_t)(tile - a.tile16[e]) * 16;
     p1 = min((int64_t)a.offsets[e + 1], p0 + 16);
   } else {
-    p0 = (int64_t)blockIdx.x * 16;
+    p0 = (int64_t)(CS ? blockIdx.x / cs : blockIdx.x) * 16;
     p1 = min(a.M, p0 + 16);
+  }
+  // this workgroup's column range (whole 256-column groups)
+  int part = 0, c_lo = 0, c_hi = a.C;
+  if constexpr (CS) {
+    part = (int)blockIdx.x % cs;
+    const int ngrp = (a.C + 32 * RD_WAVES - 1) / (32 * RD_WAVES);
+    c_lo = part * ngrp / cs * 32 * RD_WAVES;
+    c_hi = min(a.C, (part + 1) * ngrp / cs * 32 * RD_WAVES);
   }
   // the activation row this lane feeds into the MFMA (row lane % 16)
   const int64_t pa = p0 + (lane & 15);
@@ -164,14 +174,14 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
     const float* Wb[NOUT];
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) Wb[o] = a.W[o] + (int64_t)e * a.w_estride + (int64_t)jc * a.w_jstride;
-    for (int cb = wave * 32; cb < a.C; cb += 32 * RD_WAVES * UNR) {
+    for (int cb = c_lo + wave * 32; cb < c_hi; cb += 32 * RD_WAVES * UNR) {
       uint4 raw[UNR];
       float w8[UNR][NOUT][8];
       bool aok[UNR], wok[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int c = cb + u * 32 * RD_WAVES + 8 * (lane >> 4);
-        const bool cok = c < a.C;  // C % 8 == 0: whole 8-column chunks
+        const bool cok = c < c_hi;  // C % 8 == 0: whole 8-column chunks
         const int cc = cok ? c : 0;
         aok[u] = rowok && cok;
         wok[u] = jok && cok;
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(64 * RD_WAVES) void rowdot_kernel(const RowDotArgs 
       for (int q = 0; q < 4; ++q) {
         const int64_t p = p0 + 4 * (lane >> 4) + q;
         if (p < p1) {
-          a.out[o][p * r + j] = v[q];
+          a.out[o][(CS ? (int64_t)part * a.M * r : 0) + p * r + j] = v[q];
           if (o == 0 && a.out2) a.out2[p * r + j] = a.wflat[a.sorted[p]] * v[q];
           if (o == 0 && a.wout) a.wout[p * r + j] = a.wflat[a.sorted[p]] * a.win[p * r + j];
         }
@@ -280,7 +290,8 @@ __device__ void down_finish_row(const float* __restrict__ part, int32_t ntiles, 
 constexpr int CR_COLS = 256;
 constexpr int CR_PITCH = CR_COLS + 8;  // bf16 elements per LDS tile row
 
-template <int NV>
+// VS: job 1's rank vectors come as a.vsplit_1 partial arrays, summed on load.
+template <int NV, bool VS>
 __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][32 * CR_PITCH];
   const bool z1 = blockIdx.z == 1;
@@ -290,6 +301,8 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   const int32_t* const gather = z1 ? a.gather_1 : a.gather;
   const int32_t gdiv = z1 ? a.gdiv_1 : a.gdiv;
   const float* const V0 = z1 ? a.Vv_1 : a.Vv;
+  const int vs = VS && z1 ? a.vsplit_1 : 1;  // partial arrays summed on load
+  const int64_t vstride = a.M * a.r;
   float* const part0 = z1 ? a.part_1 : a.part;
   const int slot = blockIdx.x;
   const int64_t c0 = (int64_t)blockIdx.y * CR_COLS;
@@ -307,6 +320,20 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = a.r;
+  if (VS && z1 && a.vfinal_1) {
+    // side job: the summed rank vectors of this slot's rows, spread over the
+    // slot's column blocks of this job (every row lies in one slot)
+    const int64_t nv = (r1 - r0) * r;
+    const int nb = (C + CR_COLS - 1) / CR_COLS;
+    const int64_t q0 = nv * blockIdx.y / nb, q1 = nv * (blockIdx.y + 1) / nb;
+    for (int64_t q = q0 + tid; q < q1; q += 256) {
+      const int64_t p = r0 + q / r;
+      const int j = (int)(q % r);
+      float v = V0[p * r + j];
+      for (int sp = 1; sp < vs; ++sp) v += V0[sp * vstride + p * r + j];
+      a.vfinal_1[p * r + j] = v;
+    }
+  }
   if (a.dfin_part && blockIdx.y == 0 && !z1) {
     // side job: every row lies in exactly one slot, and every slot has a
     // workgroup with column block 0 and job 0
@@ -354,7 +381,12 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t p = p0 + 8 * aq + i;
-      const float v = (p < r1 && aj < r) ? V[p * r + aj] : 0.f;
+      float v = 0.f;
+      if (p < r1 && aj < r) {
+        v = V[p * r + aj];
+        if constexpr (VS)
+          for (int sp = 1; sp < vs; ++sp) v += V[sp * vstride + p * r + aj];
+      }
       const __bf16 h = (__bf16)v;
       hi[i] = h;
       lo[i] = (__bf16)(v - (float)h);
@@ -911,17 +943,30 @@ hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int64_t M, int3
   return hipGetLastError();
 }
 
+int rowdot_csplit(int64_t M, int64_t C) {
+  const int64_t nwg = (M + 15) / 16;
+  int cs = 1;
+  while (cs < 4 && nwg * cs * 2 <= 256 && C / (cs * 2) >= 768) cs *= 2;
+  return cs;
+}
+
 hipError_t launch_rowdot(const RowDotArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  // grouped: at most M/16 + E expert-aligned tiles
-  const dim3 g(blocks_for(a.M, 16) + (a.tile16 ? (unsigned)a.E : 0u)), b(64 * RD_WAVES);
+  const unsigned cs = a.csplit > 1 ? (unsigned)a.csplit : 1u;
+  if (cs > 1 && (a.tile16 || a.out2 || a.wout)) return hipErrorInvalidValue;
+  // grouped: at most M/16 + E expert-aligned tiles; dense: cs per 16 rows
+  const dim3 g(blocks_for(a.M, 16) * cs + (a.tile16 ? (unsigned)a.E : 0u)), b(64 * RD_WAVES);
   const bool wt = a.w_jstride == 1;
-  if (a.nout == 2) {
-    if (wt) hipLaunchKernelGGL((rowdot_kernel<2, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((rowdot_kernel<2, false>), g, b, 0, st, a);
+  if (cs > 1) {
+    if (a.nout != 1) return hipErrorInvalidValue;
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<1, true, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<1, false, true>), g, b, 0, st, a);
+  } else if (a.nout == 2) {
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<2, true, false>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<2, false, false>), g, b, 0, st, a);
   } else {
-    if (wt) hipLaunchKernelGGL((rowdot_kernel<1, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((rowdot_kernel<1, false>), g, b, 0, st, a);
+    if (wt) hipLaunchKernelGGL((rowdot_kernel<1, true, false>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((rowdot_kernel<1, false, false>), g, b, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -970,11 +1015,14 @@ hipError_t launch_colred(const ColRedArgs& a, hipStream_t st) {
   const bool two = a.njobs == 2;
   const int32_t cmax = two && a.C_1 > a.C ? a.C_1 : a.C;
   const dim3 g((unsigned)a.slots, blocks_for(cmax, CR_COLS), two ? 2 : 1), b(256);
+  const bool vsum = two && a.vsplit_1 > 1;
   if (a.Vv2) {
     if (two) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(colred_kernel<2>, g, b, 0, st, a);
+    hipLaunchKernelGGL((colred_kernel<2, false>), g, b, 0, st, a);
+  } else if (vsum) {
+    hipLaunchKernelGGL((colred_kernel<1, true>), g, b, 0, st, a);
   } else {
-    hipLaunchKernelGGL(colred_kernel<1>, g, b, 0, st, a);
+    hipLaunchKernelGGL((colred_kernel<1, false>), g, b, 0, st, a);
   }
   return hipGetLastError();
 }

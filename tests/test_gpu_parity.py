@@ -86,6 +86,9 @@ LIN_CASES = [
     # few tiles: the reduction split over workgroups, summed by the fixup
     # pass (forward and dX; ragged rows)
     (100, 512, 512, 2, 8), (90, 256, 1024, 1, 4),
+    # dY B over four column ranges (unequal, ragged last) summed by the dB / dA
+    # reduction
+    (700, 256, 4000, 1, 4), (500, 128, 3200, 0, 16),
 ]
 
 
