@@ -167,7 +167,10 @@ typedef struct gq_lora_linear {
  * x [T][n_in] bf16.  T == 0 is a no-op.
  * Workspace: gq_linear_lora_fwd_workspace_size() bytes, zero except for
  * launches too small to fill the GPU with output tiles, whose reduction is
- * split over workgroups (their fp32 partial sums live there).
+ * split over workgroups (their fp32 partial sums live there), and for T
+ * whose x A^T row-dot runs over column ranges (its fp32 partials, summed by
+ * the MMQ).  Without that much workspace the row-dot runs uncut (same
+ * results up to rounding); the split launches need it.
  */
 size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear* L, int64_t T);
 int gq_linear_lora_fwd(const gq_lora_linear* L, const uint16_t* x, int64_t T, uint16_t* y,

@@ -333,9 +333,11 @@ static int dequant_impl(int qtype, const void* blocks, int64_t rows, int64_t col
 size_t gq_linear_lora_fwd_workspace_size(const gq_lora_linear* L, int64_t T) {
   if (!L || T <= 0 || L->n_in <= 0 || L->n_out <= 0) return 0;
   const int ks = small_split(T, L->n_out, L->n_in);
-  if (ks <= 1) return 0;
+  const int cs = rowdot_csplit(T, L->n_in);
+  if (ks <= 1 && cs <= 1) return 0;
   Ws w(nullptr);
-  w.take<float>((int64_t)ks * T * L->n_out);
+  if (ks > 1) w.take<float>((int64_t)ks * T * L->n_out);
+  if (cs > 1) w.take<float>((int64_t)cs * T * L->rank);
   return w.size();
 }
 
@@ -367,20 +369,36 @@ static int linear_lora_fwd_impl(const gq_lora_linear* L, const uint16_t* x, int6
   // small launches: split the reduction (needs the workspace and 4-byte
   // aligned y for the fixup's stores; else the unsplit tile)
   const int ks = (tile_skinny(tc) || tc == TILE_WIDE || !aligned(y, 4)) ? 1 : small_split(T, N, K);
+  Ws w(ws);
   if (ks > 1) {
     if ((rc = check_ws(ws, ws_bytes, gq_linear_lora_fwd_workspace_size(L, T)))) return rc;
     tc = TILE_64x128;
     g.ksplit = ks;
-    g.part = static_cast<float*>(ws);
+    g.part = w.take<float>((int64_t)ks * T * N);
   }
   g.mtiles = cdiv(T, tile_bm(tc));
   g.s = L->scale; g.r = r; g.lB0 = L->B; g.rv0 = xa;
   g.o0 = y; g.ldo = N;
+  // x A^T over column ranges when 16-row workgroups alone leave CUs idle
+  // (tile launches only, and only with the workspace for the partials): the
+  // MMQ's adapter fold adds them and stores xa
+  int cs = (tile_skinny(tc) || ks > 1) ? 1 : rowdot_csplit(T, K);
+  float* xa_part = nullptr;
+  if (cs > 1) {
+    const size_t need = gq_linear_lora_fwd_workspace_size(L, T);
+    if (ws && ws_bytes >= need) {
+      xa_part = w.take<float>((int64_t)cs * T * r);
+      g.rv0 = xa_part; g.rv_parts = cs; g.rv_out = xa;
+    } else {
+      cs = 1;
+    }
+  }
 
   RowDotArgs rd;
   memset(&rd, 0, sizeof rd);
   rd.M = T; rd.C = K; rd.r = r; rd.act = x; rd.lda = K; rd.gdiv = 1; rd.E = 1;
-  rd.W[0] = L->A; rd.w_jstride = K; rd.w_cstride = 1; rd.out[0] = xa; rd.nout = 1;
+  rd.W[0] = L->A; rd.w_jstride = K; rd.w_cstride = 1; rd.nout = 1;
+  rd.out[0] = cs > 1 ? xa_part : xa; rd.csplit = cs;
   HIP_TRY(launch_rowdot(rd, st), "gq_linear_lora_fwd: x A^T");
   HIP_TRY(launch_gemm(L->qtype, EPI_LIN, tc, g, st), "gq_linear_lora_fwd: MMQ");
   if (ks > 1)

@@ -493,7 +493,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p, uint8_t* smem, cons
             if (ok && j < rtot) {
               if constexpr (EPI == EPI_GATEUP_BWD) {
                 x = j < r ? p.rv0[row * r + j] : p.rv1[row * r + j - r];
-              } else if constexpr (EPI == EPI_LIN_BWD) {
+              } else if constexpr (EPI == EPI_LIN_BWD || EPI == EPI_LIN) {
                 x = X[row * r + j];
                 for (int sp = 1; sp < p.rv_parts; ++sp) x += X[sp * p.M * r + row * r + j];
                 if (p.rv_out && ntile == 0 && wn == 0) p.rv_out[row * r + j] = x;

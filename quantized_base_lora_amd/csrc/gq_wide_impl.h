@@ -399,7 +399,17 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(const GemmArgs p) {
     const int64_t pr = r0 + (tid >> 1);
     float xv[8], bv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = (pr < p.M && j0 + i < r) ? p.rv0[pr * r + j0 + i] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      float x = 0.f;
+      if (pr < p.M && j0 + i < r) {
+        x = p.rv0[pr * r + j0 + i];
+        // xa as rv_parts column-range partials: summed here; the tiles of
+        // column 0 store the sum
+        for (int sp = 1; sp < p.rv_parts; ++sp) x += p.rv0[sp * p.M * r + pr * r + j0 + i];
+        if (p.rv_out && nt == 0) p.rv_out[pr * r + j0 + i] = x;
+      }
+      xv[i] = x;
+    }
     const int col = n0 + (tid >> 1);
     const bool bt = tid < 2 * BN;
     const float* Bw = p.lB0 + (int64_t)(p.w_row0 + col) * r;
