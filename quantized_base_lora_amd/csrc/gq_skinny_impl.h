@@ -71,6 +71,11 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[SK_WAVES][WREG];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[2][XBUF];
   __shared__ float lds_s[2][RAW ? 8 * RT : 1];
+  // adapter-fold rows (xa, or xa_g / xa_u) of the tile, 16 ranks each, and
+  // the rows' label columns (the LM head): written before the main loop
+  constexpr int NXS = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ float lds_xa[NXS][RT * 16];
+  __shared__ int32_t lds_lab[EPI == EPI_CE_FWD ? RT : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -155,6 +160,42 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
     xsrc[i] = p.a0 + src * p.lda + piece * 8;
     xdst[i] = ((piece >> 2) * RT + rr) * XROW + (piece & 3) * 16;
     xsd[i] = (piece >> 2) * RT + rr;
+  }
+
+  // the adapter fold's operands and the label columns, loaded before the
+  // main loop (their latency hides behind it): rows into LDS, this lane's
+  // B row (its weight row, 16 ranks) into registers
+  const int r = p.r;
+  const float s_ = p.s;
+  for (int i = tid; i < NXS * RT * 16; i += NTHR) {
+    const int set = i / (RT * 16), rr = (i / 16) % RT, j = i % 16;
+    const float* X = set ? p.rv1 : p.rv0;
+    const int64_t pr = r0 + rr;
+    lds_xa[set][rr * 16 + j] = (j < r && pr < r1) ? X[pr * r + j] : 0.f;
+  }
+  if constexpr (EPI == EPI_CE_FWD) {
+    for (int i = tid; i < RT; i += NTHR) {
+      const int64_t pr = r0 + i;
+      int32_t rel = INT_MIN;  // ignored label (or no row)
+      if (pr < r1) {
+        const int64_t lab = p.labels[pr];
+        if (lab != p.ignore_index && lab >= 0 && lab < p.V) rel = (int32_t)(lab - p.w_row0);
+      }
+      lds_lab[i] = rel;
+    }
+  }
+  float bq[16];
+  {
+    const float* Bm;
+    if constexpr (EPI == EPI_SWIGLU)
+      Bm = (wave < 4 ? p.lB0 : p.lB1) + (int64_t)e * p.lB_estride;
+    else if constexpr (EPI == EPI_CE_FWD)
+      Bm = p.lB0 + (int64_t)p.w_row0 * r;
+    else
+      Bm = p.lB0 + (int64_t)e * p.lB_estride;
+    Bm += (int64_t)(wok ? wrow : 0) * r;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bq[j] = (wok && j < r) ? Bm[j] : 0.f;
   }
 
   const int nss = p.K / 256;
@@ -262,50 +303,20 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
   }
 
   // ---- epilogue.  acc[rg][v] sits at row r0 + rg*16 + 4q + v, weight row
-  // wrow.  Adapter term in fp32.
-  const int r = p.r;
-  const float s_ = p.s;
-  // four ranks at a time; every row's loads of a chunk are issued together
-  // (rows past the tile read the first row and add nothing)
+  // wrow.  Adapter term in fp32, from the rows staged in LDS and this lane's
+  // B row in registers (ranks past r are zero in both).
   if (wok) {
-    const float* Bm;
-    const float* X;
-    if constexpr (EPI == EPI_SWIGLU) {
-      Bm = (wave < 4 ? p.lB0 : p.lB1) + (int64_t)e * p.lB_estride;
-      X = wave < 4 ? p.rv0 : p.rv1;
-    } else if constexpr (EPI == EPI_CE_FWD) {
-      Bm = p.lB0 + (int64_t)p.w_row0 * r;
-      X = p.rv0;
-    } else {
-      Bm = p.lB0 + (int64_t)e * p.lB_estride;
-      X = p.rv0;
-    }
-    Bm += (int64_t)wrow * r;
-    float t[RG][4];
+    const float* X = lds_xa[EPI == EPI_SWIGLU && wave >= 4 ? 1 : 0];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) t[rg][v] = 0.f;
-#pragma unroll 1
-    for (int jc = 0; jc < r; jc += 4) {
-      float bv[4];
+      for (int v = 0; v < 4; ++v) {
+        const float* xr = X + (rg * 16 + 4 * q + v) * 16;
+        float t = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bv[jj] = jc + jj < r ? Bm[jc + jj] : 0.f;
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t pr = r0 + rg * 16 + 4 * q + v;
-          const float* xr = X + (pr < r1 ? pr : r0) * r + jc;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) t[rg][v] += (jc + jj < r ? xr[jj] : 0.f) * bv[jj];
-        }
-    }
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (r0 + rg * 16 + 4 * q + v < r1) acc[rg][v] += s_ * t[rg][v];
+        for (int j = 0; j < 16; ++j) t += xr[j] * bq[j];
+        if (r0 + rg * 16 + 4 * q + v < r1) acc[rg][v] += s_ * t;
+      }
   }
 
   if constexpr (EPI == EPI_LIN) {
@@ -350,8 +361,6 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
     // same rows (xor shuffles), then the 8 waves in order through LDS; the
     // label logit is written by its lane
     __shared__ float2 part[SK_WAVES][RT];
-    const int64_t V = p.V;
-    const int64_t c0 = p.w_row0;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -365,10 +374,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 16);
         if (nl == 0) part[wave][lr] = make_float2(m, l);
-        if (pr < r1 && wok) {
-          const int64_t lab = p.labels[pr];
-          if (lab != p.ignore_index && lab >= 0 && lab < V && c0 + wrow == lab) p.f1[pr] = acc[rg][v];
-        }
+        if (wok && lds_lab[lr] == wrow) p.f1[pr] = acc[rg][v];  // (no label / no row: INT_MIN)
       }
     __syncthreads();
     if (tid < RT) {
@@ -397,6 +403,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
 
 template <int QT, int EPI>
 hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st) {
+  if (a.r > 16) return hipErrorInvalidValue;  // the fold stages 16 ranks
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(64 * SK_WAVES);
   if (rg == 1)
     hipLaunchKernelGGL((skinny_kernel<QT, EPI, 1>), grid, block, 0, st, a);
