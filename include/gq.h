@@ -361,13 +361,14 @@ int gq_grouped_mmq_lora_bwd(const gq_lora_linear* P, int32_t nproj, int32_t mode
  * the loss and gradients are zero.  A label outside [0, V) that is not
  * ignore_index is treated as ignored and sets the workspace's first 32-bit
  * word to nonzero (GQ_EDEVICE condition, readable after synchronising).
- * chunk_rows >= 1.  The workspace holds the gradient rows of at most three
- * chunks (T x 3 chunk_rows bf16): of one chunk; of two when the backward
+ * chunk_rows >= 1.  The workspace holds the gradient rows of at most six
+ * chunks (T x 6 chunk_rows bf16): of one chunk; of two when the backward
  * runs one chunk's gradient tiles beside the previous chunk's dh tiles
- * (two or more chunks with 128-row tiles); of up to three when the gradient
+ * (two or more chunks with 128-row tiles); of up to six when the gradient
  * tiles run 256 x 192 and one launch covers the fewest chunks (at most
- * three) that give it two full rounds of tiles.  Plus O(T x (H + r) + V x r)
- * floats; it never holds T x V values.
+ * six) that give it four full rounds of tiles.  Plus O(T x (H + r) + V x r)
+ * floats (two T x H fp32 dh sums with the 256 x 192 gradient tiles); it
+ * never holds T x V values.
  */
 size_t gq_lmhead_chunked_ce_workspace_size(const gq_lora_linear* head, int64_t T,
                                            int64_t chunk_rows);

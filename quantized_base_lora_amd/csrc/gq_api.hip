@@ -1121,7 +1121,8 @@ struct CeWs {
   float* term;
   uint16_t* G;
   uint16_t* G2;  // second gradient buffer when chunks are paired, else nullptr
-  float* dh_acc;
+  float* dh_acc;  // dh_nacc fp32 [T][H] sums, added in order at the end
+  int dh_nacc;
   float* part_GB;
   float* part_dB;
   float* GB;
@@ -1133,12 +1134,14 @@ struct CeWs {
   int tc_fwd, tc_bwd, tc_dh;
 };
 // Chunks per backward step when the gradient tiles run on the 256 x 192
-// tile: the fewest (up to three) that give two full rounds of tiles, kept
+// tile: the fewest (up to six) that give four full rounds of tiles, kept
 // only if the tiles fill the chip (wide_pays); 0 = 128 x 128 gradient tiles.
+// Longer steps mean fewer dh launches, each of which reads and writes the
+// T x H fp32 sums once.
 int64_t ce_wide_chunks(int qtype, int64_t T, int64_t V, int64_t H, int r, int64_t C) {
   const int64_t nchunks = (V + C - 1) / C;
   int64_t g = 1;
-  while (g < 3 && g < nchunks && (int64_t)cdiv(T, WIDE_BM) * cdiv(std::min(g * C, V), WIDE_BN) < 512) ++g;
+  while (g < 6 && g < nchunks && (int64_t)cdiv(T, WIDE_BM) * cdiv(std::min(g * C, V), WIDE_BN) < 1024) ++g;
   return wide_pays(qtype, T, std::min(g * C, V), H, r) ? g : 0;
 }
 CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad) {
@@ -1165,7 +1168,16 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     const int bn = gw ? WIDE_BN : TILE_BN;
     p.ldG = (p.span + 63) / 64 * 64;
     p.G = w.take<uint16_t>(T * p.ldG);
-    p.dh_acc = w.take<float>(T * H);
+    // dh tiles: with the wide gradient tiles, 256 x 128 backward tiles whose
+    // two reduction ranges (halves of the step's vocabulary rows) sum into
+    // two accumulators; else the 128-row tiles and one accumulator
+    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), p.span, true);
+    p.dh_nacc = 1;
+    if (gw && L->qtype != GQ_Q2_DM) {
+      p.tc_dh = TILE_WIDE_NN;
+      p.dh_nacc = 2;
+    }
+    p.dh_acc = w.take<float>(p.dh_nacc * T * H);
     int64_t ntb = 0;
     for (int64_t c0 = 0; c0 < V; c0 += p.span) ntb += cdiv(std::min(p.span, V - c0), bn);
     p.ntiles_bwd = (int)ntb;
@@ -1175,7 +1187,6 @@ CeWs plan_ce(Ws& w, const gq_lora_linear* L, int64_t T, int64_t chunk, bool grad
     p.part_dB = w.take<float>((int64_t)p.mt * V * r);
     p.GB = w.take<float>(T * r);
     p.part = w.take<float>(colred_slots(T, pick_rc(T, H, (int)r, 1), 1) * H * r);
-    p.tc_dh = pick_tile(T, cdiv(H, TILE_BN), p.span, true);
     // two or more chunks with 128-row tiles on both passes: chunk c's
     // gradient tiles share a launch with chunk c-1's dh tiles, which needs a
     // second gradient buffer
@@ -1258,10 +1269,11 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
           "ce: log-sum-exp merge, loss");
   if (!grad) return GQ_OK;
 
-  // Step after step (one chunk, or up to three on the 256 x 192 gradient
+  // Step after step (one chunk, or up to six on the 256 x 192 gradient
   // tile): the gradient tiles write G for the step's vocabulary rows (plus
   // the G.B and dB partials), the dh tiles accumulate G deq(W) of the step
-  // into dh_acc (step order fixed: deterministic).  With two gradient
+  // into dh_acc (step order fixed: deterministic; with the 256 x 128 dh
+  // tiles the first and second half of the step's rows into two sums).  With two gradient
   // buffers, step c's gradient tiles and step c-1's dh tiles run in one
   // launch.
   const bool pair = P.G2 != nullptr;
@@ -1289,9 +1301,10 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
     d.M = T; d.N = H; d.K = C;
     d.a0 = Gc; d.lda = P.ldG;
     d.w0 = wb; d.w_rowbytes = rowbytes(L); d.w_nb = H / 32; d.w_rows = C; d.w_row0 = (int)c0;
-    d.ntiles = cdiv(H, TILE_BN);
+    d.ntiles = cdiv(H, P.tc_dh == TILE_WIDE_NN ? WIDE_NN_BN : TILE_BN);
     d.mtiles = cdiv(T, tile_bm(P.tc_dh));
     d.f0 = P.dh_acc; d.ldf = H; d.accum = c0 > 0;
+    d.ksplit = P.dh_nacc;
     if (!pair) {
       HIP_TRY(launch_gemm(L->qtype, EPI_CE_BWD, P.tc_bwd, b, st), "ce: gradient tile pass");
       HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, d, st), "ce: dh pass");
@@ -1310,7 +1323,7 @@ static int lmhead_chunked_ce_impl(const gq_lora_linear* L, const uint16_t* h, co
   if (pair && have_prev) HIP_TRY(launch_gemm(L->qtype, EPI_DH_ACC, P.tc_dh, dprev, st), "ce: dh pass");
   HIP_TRY(launch_sum_parts(P.part_GB, P.ntiles_bwd, T, r, 1.f, P.GB, st), "ce: G B");
   HIP_TRY(launch_sum_parts(P.part_dB, P.mt, V, r, L->scale, dB, st), "ce: dB");
-  HIP_TRY(launch_ce_final_dh(P.dh_acc, P.GB, L->A, T, H, r, L->scale, dh, st), "ce: dh");
+  HIP_TRY(launch_ce_final_dh(P.dh_acc, P.dh_nacc, P.GB, L->A, T, H, r, L->scale, dh, st), "ce: dh");
   ColRedArgs cr;
   memset(&cr, 0, sizeof cr);
   cr.M = T; cr.C = H; cr.r = r; cr.U = h; cr.ldu = H; cr.gdiv = 1; cr.Vv = P.GB; cr.E = 1;

@@ -1197,9 +1197,23 @@ hipError_t launch_skinny_nn(int rg, const GemmArgs& a, hipStream_t st);
 
 template <int QT, int EPI>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t st);
+template <int QT, int EPI>
+hipError_t launch_wide_nn(const GemmArgs& a, hipStream_t st);
 
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
+  if (tilecfg == TILE_WIDE_NN) {
+    if constexpr ((EPI == EPI_DH_ACC || EPI == EPI_LIN_BWD) && QT != QT_Q2_DM) {
+      // dense, one or two reduction ranges (a range without k-steps stores
+      // zero sums), activation rows holding K rounded up to 64 columns
+      const int64_t nkall = ((int64_t)a.K + GEMM_BK - 1) / GEMM_BK;
+      if (a.offsets || a.gather || a.K < 1 || a.ksplit > 2 || a.lda < nkall * GEMM_BK || a.asplit < a.K || a.wsplit < a.K || a.N > 32 * a.w_nb ||
+          (EPI == EPI_DH_ACC ? !a.f0 : !a.part))
+        return hipErrorInvalidValue;
+      return launch_wide_nn<QT, EPI>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   const unsigned splits = a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
   if (splits > 1) {  // dense EPI_LIN / EPI_LIN_BWD on one group of four waves, whole k-steps
     if (a.offsets || a.K % GEMM_BK || tilecfg == TILE_128x128_K2 || tile_skinny(tilecfg) ||

@@ -1,6 +1,7 @@
 // MFMA GEMM instantiations: Q8_0 blocks, backward (NN) epilogues.
 #include "gq_gemm_impl.h"
 #include "gq_skinny_impl.h"
+#include "gq_wide_nn_impl.h"
 
 namespace gq {
 hipError_t launch_gemm_q8_0_nn(int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {

@@ -104,6 +104,9 @@ struct GemmArgs {
 // TILE_WIDE: 256 x 192 tiles on 512 threads (gq_wide_impl.h), dense
 // forward launches and the LM head's gradient tiles, with Q8_0 / Q4_0
 // weights, K % 64 == 0 and rank <= WIDE_MAX_RANK only.
+// TILE_WIDE_NN: 256 x 128 backward (NN) tiles on 512 threads, the reduction
+// cut into ksplit (1 or 2) ranges of one workgroup each, fp32 sums per range
+// (gq_wide_nn_impl.h): the LM head's dh and dense dX, Q8_0 / Q4_0 weights.
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,
@@ -111,15 +114,18 @@ enum TileCfg {
   TILE_SKINNY16 = 3,
   TILE_SKINNY32 = 4,
   TILE_SKINNY64 = 5,
-  TILE_WIDE = 6
+  TILE_WIDE = 6,
+  TILE_WIDE_NN = 7
 };
 constexpr int WIDE_BM = 256, WIDE_BN = 192;
+constexpr int WIDE_NN_BM = 256, WIDE_NN_BN = 128;
 constexpr int WIDE_MAX_RANK = 16;  // adapter rank the wide tile stages in LDS
 
 inline bool tile_skinny(int cfg) { return cfg >= TILE_SKINNY16 && cfg <= TILE_SKINNY64; }
 inline int tile_bm(int cfg) {
   switch (cfg) {
     case TILE_WIDE: return WIDE_BM;
+    case TILE_WIDE_NN: return WIDE_NN_BM;
     case TILE_64x128: return 64;
     case TILE_SKINNY16: return 16;
     case TILE_SKINNY32: return 32;
@@ -303,7 +309,8 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const float* w, int64_t T, int3
 hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const float* w,
                               const float* rstd, int64_t T, int32_t H, uint16_t* dx,
                               hipStream_t st);
-hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
+// dh[t][c] = bf16( sum_{q < nacc} dh_acc[q][t][c] (in order) + s * sum_j GB[t][j] A[j][c] )
+hipError_t launch_ce_final_dh(const float* dh_acc, int32_t nacc, const float* GB, const float* A, int64_t T,
                               int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st);

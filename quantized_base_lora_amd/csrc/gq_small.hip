@@ -894,7 +894,7 @@ __global__ __launch_bounds__(1024) void ce_merge_loss_kernel(
                       reinterpret_cast<float*>(red), shc);
 }
 
-__global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, const float* __restrict__ GB,
+__global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, int32_t nacc, const float* __restrict__ GB,
                                    const float* __restrict__ A, int64_t T, int32_t H, int32_t r,
                                    float s, uint16_t* __restrict__ dh) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -902,7 +902,9 @@ __global__ void ce_final_dh_kernel(const float* __restrict__ dh_acc, const float
   const int64_t t = i / H, c = i % H;
   float v = 0.f;
   for (int j = 0; j < r; ++j) v += GB[t * r + j] * A[(int64_t)j * H + c];
-  dh[i] = f2bf(dh_acc[i] + s * v);
+  float acc = dh_acc[i];
+  for (int q = 1; q < nacc; ++q) acc += dh_acc[q * T * H + i];
+  dh[i] = f2bf(acc + s * v);
 }
 
 // out[p][j] = wflat[sorted[p]] * in[p][j]
@@ -1195,11 +1197,11 @@ hipError_t launch_ce_merge(const float* part_ml, int32_t ntiles, int64_t T, cons
   return hipGetLastError();
 }
 
-hipError_t launch_ce_final_dh(const float* dh_acc, const float* GB, const float* A, int64_t T,
+hipError_t launch_ce_final_dh(const float* dh_acc, int32_t nacc, const float* GB, const float* A, int64_t T,
                               int32_t H, int32_t r, float s, uint16_t* dh, hipStream_t st) {
   const int64_t n = T * H;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_final_dh_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, dh_acc, GB, A,
+  hipLaunchKernelGGL(ce_final_dh_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, dh_acc, nacc, GB, A,
                      T, H, r, s, dh);
   return hipGetLastError();
 }

@@ -417,12 +417,14 @@ HEAD_CASES = [
 
 # 256 x 192 gradient tiles over several chunks per launch, ranks taken four
 # at a time in their epilogue (rank 8, 6 and 12; ragged rows, ragged last
-# step, one k-step of hidden size)
+# step, one k-step of hidden size); the dh sums on 256 x 128 tiles over two
+# steps (ragged rows and reduction, a half-used column tile) or one
 HEAD_WIDE_RANK_CASES = [
     # T, H, V, chunk, qtype, ignore_frac, rank
-    (768, 128, 20000, 4096, 0, 0.1, 8),
-    (600, 64, 14000, 4096, 1, 0.0, 6),
+    (768, 128, 20000, 2048, 0, 0.1, 8),
+    (600, 64, 14000, 2048, 1, 0.0, 6),
     (1024, 64, 10000, 4096, 1, 0.2, 12),
+    (600, 192, 14000, 2048, 0, 0.1, 4),
 ]
 
 
