@@ -1203,13 +1203,15 @@ hipError_t launch_wide_nn(const GemmArgs& a, hipStream_t st);
 template <int QT, int EPI>
 hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   if (tilecfg == TILE_WIDE_NN) {
-    if constexpr ((EPI == EPI_DH_ACC || EPI == EPI_LIN_BWD) && QT != QT_Q2_DM) {
+    if constexpr (EPI == EPI_DH_ACC && QT != QT_Q2_DM) {
       // dense, one or two reduction ranges (a range without k-steps stores
       // zero sums), activation rows holding K rounded up to 64 columns
       const int64_t nkall = ((int64_t)a.K + GEMM_BK - 1) / GEMM_BK;
-      if (a.offsets || a.gather || a.K < 1 || a.ksplit > 2 || a.lda < nkall * GEMM_BK || a.asplit < a.K || a.wsplit < a.K || a.N > 32 * a.w_nb ||
-          (EPI == EPI_DH_ACC ? !a.f0 : !a.part))
+      if (a.offsets || a.gather || a.K < 1 || a.ksplit > 2 || a.lda < nkall * GEMM_BK || a.asplit < a.K ||
+          a.wsplit < a.K || a.N > 32 * a.w_nb || a.N % 4)
         return hipErrorInvalidValue;
+      // the range sums leave as 16-byte row pieces
+      if (!a.f0 || (uintptr_t)a.f0 % 16 || a.ldf % 4) return hipErrorInvalidValue;
       return launch_wide_nn<QT, EPI>(a, st);
     }
     return hipErrorInvalidValue;

@@ -106,7 +106,7 @@ struct GemmArgs {
 // weights, K % 64 == 0 and rank <= WIDE_MAX_RANK only.
 // TILE_WIDE_NN: 256 x 128 backward (NN) tiles on 512 threads, the reduction
 // cut into ksplit (1 or 2) ranges of one workgroup each, fp32 sums per range
-// (gq_wide_nn_impl.h): the LM head's dh and dense dX, Q8_0 / Q4_0 weights.
+// (gq_wide_nn_impl.h): the LM head's dh, Q8_0 / Q4_0 weights.
 enum TileCfg {
   TILE_128x128 = 0,
   TILE_64x128 = 1,

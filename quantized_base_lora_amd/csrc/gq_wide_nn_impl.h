@@ -1,16 +1,19 @@
-// Wide-tile MMQ in the backward (NN) direction, dX = dY deq(W) and the LM
-// head's dh = G deq(W): the reduction runs along the weight rows and the
+// Wide-tile MMQ in the backward (NN) direction for the LM head's dh =
+// G deq(W): the reduction runs along the weight (vocabulary) rows and the
 // output columns along the blocks of a row.  256 x 128 output tiles on 512
 // threads, the reduction of every tile cut into `ksplit` (1 or 2) contiguous
-// ranges, one workgroup each.
+// ranges, one workgroup each, each range summing into its own fp32 array.
 //
-// The 128 x 128 tile of gq_gemm_impl.h gives a 2048 x 2048 output (dX of a
-// 2048 -> 6144 layer, the LM head's dh) one round of workgroups by running
-// two groups of four waves on alternate k-steps of the same tile, so each
-// decoded weight slice feeds 128 rows.  Here the same number of workgroups
-// comes from two reduction ranges of a 256-row tile: every decoded slice
-// feeds 256 rows (half the decode VALU per MFMA) at the same LDS operand
-// reads per MFMA (each wave owns a 64 x 64 share of the tile).
+// The 128 x 128 tile of gq_gemm_impl.h gives a 2048 x 2048 output one round
+// of workgroups by running two groups of four waves on alternate k-steps of
+// the same tile, so each decoded weight slice feeds 128 rows.  Here the same
+// number of workgroups comes from two reduction ranges of a 256-row tile:
+// every decoded slice feeds 256 rows (half the decode VALU per MFMA) at the
+// same LDS operand reads per MFMA (each wave owns a 64 x 64 share of the
+// tile).  The dh sums are read and written once per launch anyway, so the
+// two ranges cost a second array, not an extra pass.  (For dX the range
+// sums would need a fixup pass over 2 x T x n_in floats, which costs more
+// than the tile saves.)
 //
 //  * Activations: 256 rows x 64 bf16 per k-step, four coalesced 16-byte
 //    loads per thread, stored into a padded LDS tile one step later.
@@ -20,16 +23,14 @@
 //    transposing LDS reads (ds_read_b64_tr_b16).
 //  * Double-buffered LDS, one barrier per k-step, loads two steps ahead.
 //  * Rows past M and blocks past the row are clamped to the last valid one
-//    (never stored); reduction rows past K decode to zero (scale 0) and the
-//    activation columns past K are zeroed, so K needs no alignment (the
-//    activation rows must hold K rounded up to 64 columns).
-//  * Each range stores fp32 sums, no adapter term:
-//      EPI_DH_ACC:  f0 + s * M * ldf  (+)=  sums of range s
-//      EPI_LIN_BWD: part + s * M * N   =   sums of range s (the split-K
-//                   fixup adds the ranges in order, the adapter term, and
-//                   rounds to bf16)
-//    Ranges are never added on the device between workgroups, so the result
-//    does not depend on their timing.
+//    (never stored).  With K % 64 != 0 (the RAGGED instance) reduction rows
+//    past K decode to zero (scale 0) and the activation columns past K are
+//    zeroed (the activation rows must hold K rounded up to 64 columns); the
+//    other instance has no masks in its loop.
+//  * Range s accumulates its fp32 sums into f0 + s * M * ldf (or sets them
+//    when accum == 0), no adapter term; the consumer adds the ranges in
+//    order.  Ranges are never added between workgroups, so the result does
+//    not depend on their timing.
 #pragma once
 #include "gq_dev.h"
 #include "gq_internal.h"
@@ -44,7 +45,9 @@ constexpr int WTM = 64, WTN = 64;  // wave tile
 constexpr int PN = BN;             // [k][n] weight tile pitch: 16 chunks of 8, swizzled
 constexpr int A_ST = BM * LDK, B_ST = BK * PN;
 constexpr int SMEM = (2 * A_ST + 2 * B_ST) * 2;
+constexpr int ZP = 40;  // epilogue staging pitch (fp32)
 static_assert(BN == 128 && PN / 8 == 16, "one 16-chunk swizzle group per weight row");
+static_assert(8 * WTM * ZP * 4 <= SMEM, "epilogue staging fits the operand stages");
 static_assert(SMEM <= 160 * 1024, "fits the CU's LDS");
 
 using wide::RawQuarter;
@@ -97,9 +100,9 @@ __device__ __forceinline__ void store_quarter_nn(uint16_t* tile, int row, int co
 // w_nb), K reduction rows; activations a0 (lda >= K rounded up to 64),
 // weights w0 from reduction row w_row0, w_rowbytes per row.  Grid: mtiles *
 // ntiles * ksplit workgroups.
-template <int QT, int EPI>
+template <int QT, int EPI, bool RAGGED>
 __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
-  static_assert(EPI == EPI_DH_ACC || EPI == EPI_LIN_BWD, "fp32 range sums");
+  static_assert(EPI == EPI_DH_ACC, "fp32 range sums");
   constexpr int BS = QTraits<QT>::BS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -121,7 +124,6 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
   const int nkall = (p.K + BK - 1) / BK;
   const int kb0 = (int)((int64_t)ks * nkall / KS);
   const int nk = (int)((int64_t)(ks + 1) * nkall / KS) - kb0;
-  const bool ragged = (p.K % BK) != 0;
 
   // activation rows of this thread's four 16-byte chunks (c = tid + 512 i:
   // row c >> 3, chunk c & 7), clamped to the last row
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
   // k-step, block (it % 16) / 4 of the tile's four, quarter it % 4
   int w_row[2], w_blk[2], w_q[2];
   const uint8_t* wp[2];
-  const uint8_t* wlast[2];  // the same block in reduction row K - 1
+  const uint8_t* wlast[2];  // RAGGED: the same block in reduction row K - 1
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int it = tid + NTHR * i;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
       x1 = *reinterpret_cast<const uint4*>(ap[1] + k_);
       x2 = *reinterpret_cast<const uint4*>(ap[2] + k_);
       x3 = *reinterpret_cast<const uint4*>(ap[3] + k_);
-      if (ragged && kb0 + kk == nkall - 1) {
+      if (RAGGED && kb0 + kk == nkall - 1) {
         const int valid = p.K - (kb0 + kk) * BK - (tid & 7) * 8;  // columns of the chunk below K
         auto cut = [&](uint4& x) {
           uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -197,9 +199,13 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
       const int64_t koff = (int64_t)kk * BK * p.w_rowbytes;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const bool ok = (kb0 + kk) * BK + w_row[i] < p.K;
-        load_quarter<QT>(ok ? wp[i] + koff : wlast[i], w_q[i], Wr[i]);
-        if (!ok) Wr[i].hdr = 0u;  // scale 0: the row decodes to zeros
+        if constexpr (RAGGED) {
+          const bool ok = (kb0 + kk) * BK + w_row[i] < p.K;
+          load_quarter<QT>(ok ? wp[i] + koff : wlast[i], w_q[i], Wr[i]);
+          if (!ok) Wr[i].hdr = 0u;  // scale 0: the row decodes to zeros
+        } else {
+          load_quarter<QT>(wp[i] + koff, w_q[i], Wr[i]);
+        }
       }
     };
     auto store_w = [&](int st, const RawQuarter<QT> (&Wr)[2]) __attribute__((always_inline)) {
@@ -276,51 +282,41 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
 
   // ---- fp32 sums of this range.  acc[a][b][v] sits at tile row
   // wm*64 + a*32 + (v>>2)*8 + (lane>>5)*4 + (v&3), column wn*64 + b*32 + (lane&31)
-  float* dst;
-  int64_t ld;
-  bool add;
-  if constexpr (EPI == EPI_DH_ACC) {
-    dst = p.f0 + (int64_t)ks * p.M * p.ldf;
-    ld = p.ldf;
-    add = p.accum != 0;
-  } else {
-    dst = p.part + (int64_t)ks * p.M * p.N;
-    ld = p.N;
-    add = false;
-  }
-  // per 32 x 32 sub-tile: the 16 old values are loaded together, then the
-  // 16 sums stored (one memory round trip per sub-tile, not per value);
-  // tiles with every row take the path without per-value conditions
-  const bool all_rows = r0 + BM <= p.M;
+  float* dst = p.f0 + (int64_t)ks * p.M * p.ldf;
+  const int64_t ld = p.ldf;
+  const bool add = p.accum != 0;
+  // The wave's 64 x 64 share goes out through its own LDS region, one
+  // 32-column half at a time ([64][ZP] fp32; ZP = 40 puts rows four apart
+  // 32 banks apart), as 16-byte row pieces (8 lanes per 128-byte row piece);
+  // the accumulating form reads the old sums the same way.
+  __syncthreads();  // every wave is done reading the operand stages
+  float* Z = reinterpret_cast<float*>(smem) + wave * WTM * ZP;
+  const int64_t rbase = r0 + wm * WTM;
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
-    const int c = n0 + wn * WTN + b * 32 + (lane & 31);
-    if (c >= p.N) continue;
 #pragma unroll
-    for (int a = 0; a < TM; ++a) {
-      const int64_t pr0 = r0 + wm * WTM + a * 32 + (lane >> 5) * 4;
-      float* base = dst + pr0 * ld + c;
-      if (all_rows) {
-        if (add) {
-          float old[16];
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) old[v] = base[((v >> 2) * 8 + (v & 3)) * ld];
+      for (int v = 0; v < 16; ++v)
+        Z[(a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * ZP + (lane & 31)] = acc[a][b][v];
+    // (the wave's own region: its LDS writes complete before these reads)
+    const int cb = n0 + wn * WTN + b * 32;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) base[((v >> 2) * 8 + (v & 3)) * ld] = old[v] + acc[a][b][v];
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) base[((v >> 2) * 8 + (v & 3)) * ld] = acc[a][b][v];
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t pr = pr0 + (v >> 2) * 8 + (v & 3);
-          if (pr < p.M) {
-            float* d = base + ((v >> 2) * 8 + (v & 3)) * ld;
-            *d = add ? *d + acc[a][b][v] : acc[a][b][v];
-          }
-        }
+    for (int i = lane; i < WTM * 8; i += 64) {
+      const int rr = i >> 3, c4 = (i & 7) * 4;
+      const int64_t pr = rbase + rr;
+      const int n = cb + c4;
+      if (pr >= p.M || n >= p.N) continue;
+      float4 val = *reinterpret_cast<const float4*>(Z + rr * ZP + c4);
+      float4* d = reinterpret_cast<float4*>(dst + pr * ld + n);
+      if (add) {
+        const float4 o = *d;
+        val.x = o.x + val.x;
+        val.y = o.y + val.y;
+        val.z = o.z + val.z;
+        val.w = o.w + val.w;
       }
+      *d = val;
     }
   }
 }
@@ -328,13 +324,16 @@ __global__ __launch_bounds__(NTHR, 1) void wide_nn_kernel(const GemmArgs p) {
 }  // namespace wnn
 
 namespace {
-// Launch of the wide NN tile (EPI_DH_ACC or EPI_LIN_BWD, dense, Q8_0 /
-// Q4_0); declared beside launch_q in gq_gemm_impl.h.
+// Launch of the wide NN tile (EPI_DH_ACC, dense, Q8_0 / Q4_0); declared
+// beside launch_q in gq_gemm_impl.h.
 template <int QT, int EPI>
 hipError_t launch_wide_nn(const GemmArgs& a, hipStream_t st) {
   const unsigned ks = a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles * ks);
-  hipLaunchKernelGGL((wnn::wide_nn_kernel<QT, EPI>), grid, dim3(wnn::NTHR), 0, st, a);
+  if (a.K % wnn::BK)
+    hipLaunchKernelGGL((wnn::wide_nn_kernel<QT, EPI, true>), grid, dim3(wnn::NTHR), 0, st, a);
+  else
+    hipLaunchKernelGGL((wnn::wide_nn_kernel<QT, EPI, false>), grid, dim3(wnn::NTHR), 0, st, a);
   return hipGetLastError();
 }
 }  // namespace
