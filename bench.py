@@ -64,7 +64,7 @@ def gemm_source_hash():
     """Hash of the MMQ kernel source with comments and blank lines dropped,
     so that counters stay attributed to the kernel until its code changes."""
     h = hashlib.sha256()
-    for f in ("gq_gemm_impl.h", "gq_wide_impl.h", "gq_skinny_impl.h", "gq_dev.h"):
+    for f in ("gq_gemm_impl.h", "gq_wide_impl.h", "gq_wide_nn_impl.h", "gq_skinny_impl.h", "gq_dev.h"):
         with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", f)) as fh:
             for line in fh:
                 code = line.split("//", 1)[0].strip()
@@ -97,7 +97,7 @@ MMQ_LAUNCHES = (
     ("gemm_kernel<1, 4, 128, 128, 2>", 256 * 512, "mmq_nn_lin_bwd_q4_0_t2048_2048x6144"),
 )
 # kernels whose counters are kept in profiles/mmq_counters.json
-MMQ_KERNEL_TAGS = ("gemm_kernel", "skinny", "wide_kernel", "ce_bwd_dh_kernel")
+MMQ_KERNEL_TAGS = ("gemm_kernel", "skinny", "wide_kernel", "wide_nn_kernel", "ce_bwd_dh_kernel")
 
 
 def moe_layer_bytes(T, H, I, E, k, r, qtype_bytes, active):
@@ -138,9 +138,10 @@ def write_kernel_summary(csv_dir, out_md, title):
         fh.write("gemm_kernel<qtype, epilogue, BM, BN, k-groups>: qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, "
                  "1 SwiGLU, 2 CE logits, 3 CE gradient, 4 linear backward (dX), 5 SwiGLU backward, "
                  "6 gate/up backward, 7 dh accumulate; wide::wide_kernel<qtype, epilogue>: the 256 x 192 tile "
-                 "(epilogue 0 linear, 2 CE logits, 3 CE gradient over up to three vocabulary chunks); "
-                 "ce_bwd_dh_kernel<qtype>: one vocabulary chunk's CE-gradient tiles with the previous "
-                 "chunk's dh tiles.\n\n")
+                 "(epilogue 0 linear, 2 CE logits, 3 CE gradient over up to six vocabulary chunks); "
+                 "wnn::wide_nn_kernel<qtype, 7, ragged>: the LM head's dh on 256 x 128 tiles, two reduction "
+                 "ranges per tile; ce_bwd_dh_kernel<qtype>: one vocabulary chunk's CE-gradient tiles with the "
+                 "previous chunk's dh tiles.\n\n")
         fh.write("## rocprofv3 --stats (run_kernel_stats.csv)\n\n| kernel | calls | avg us | min us | max us | % |\n"
                  "|---|---|---|---|---|---|\n")
         for r in stats[:30]:
@@ -283,7 +284,8 @@ def write_counters(sq_csv, fetch_csv, write_csv, out_md, title, cmdline):
                  "profiler (kernels serialised).  Kernel template arguments: gemm_kernel<qtype, epilogue, BM, BN, "
                  "k-groups> (qtype 0 Q8_0, 1 Q4_0, 2 2-bit; epilogue 0 linear, 1 SwiGLU, 2 CE logits, 3 CE gradient, "
                  "4 linear backward (dX), 5 SwiGLU backward, 6 gate/up backward, 7 dh accumulate); "
-                 "wide::wide_kernel<qtype, epilogue> the 256 x 192 tile (epilogue 0, 2 or 3); ce_bwd_dh_kernel<qtype> one "
+                 "wide::wide_kernel<qtype, epilogue> the 256 x 192 tile (epilogue 0, 2 or 3); "
+                 "wnn::wide_nn_kernel<qtype, 7, ragged> the LM head's dh on 256 x 128 tiles; ce_bwd_dh_kernel<qtype> one "
                  "vocabulary chunk's CE-gradient tiles with the previous chunk's dh tiles.\n\n")
         fh.write("| kernel | threads | calls | us | MFMA busy | VALU/MFMA | LDS/MFMA | LDS conflict | HBM fetch MB | "
                  "HBM write MB |\n|---|---|---|---|---|---|---|---|---|---|\n")
