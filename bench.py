@@ -24,12 +24,13 @@ HBM traffic of the two MMQ launches: run the step under two rocprofv3
 counter passes with a plain device copy of known size in the same process,
 
     rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- \\
-        python3 bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1
+        python3 bench.py --eager --copy-probe --no-cpu --steps 2 --warmup 1 --repeats 1
     rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- (same)
 
 then `python bench.py --traffic-from F/run_counter_collection.csv
-W/run_counter_collection.csv` (no GPU needed) scales each counter by what it
-reads for the copy and writes profiles/mmq_traffic.json and its summary.
+W/run_counter_collection.csv "<the bench arguments of those runs>"` (no GPU
+needed) scales each counter by what it reads for the copy and writes
+profiles/mmq_traffic.json and its summary.
 """
 from __future__ import annotations
 
@@ -37,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import shlex
 import sys
 import time
 
@@ -155,7 +157,7 @@ def write_kernel_summary(csv_dir, out_md, title):
     log(f"wrote {out_md}")
 
 
-def write_traffic(fetch_csv, write_csv, cmdline):
+def write_traffic(fetch_csv, write_csv, run_args, cmdline):
     """Bytes per launch of the MMQ kernels from FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), each scaled so that the reference copy reads and writes
     exactly its size."""
@@ -201,9 +203,9 @@ def write_traffic(fetch_csv, write_csv, cmdline):
                  "(T 2048, 2048 -> 6144, rank 4)\n\n")
         fh.write("Counter passes (repo root on the GPU box, TMPDIR=/tmp, run from /tmp):\n\n")
         fh.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch -o run -- "
-                 "python3 <repo>/bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1\n")
+                 f"python3 <repo>/bench.py {run_args}\n")
         fh.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write -o run -- "
-                 "python3 <repo>/bench.py --eager --copy-probe --no-moe --no-cpu --steps 3 --warmup 1\n\n")
+                 f"python3 <repo>/bench.py {run_args}\n\n")
         fh.write(f"Summary written by: `{cmdline}`\n\n")
         fh.write("Each counter (KiB per dispatch, median over dispatches) is divided by what the same "
                  "counter reads for a plain device copy of known size in the same process.\n\n")
@@ -404,19 +406,19 @@ def main():
                          "(for a rocprofv3 --pmc FETCH_SIZE pass)")
     ap.add_argument("--expert-fetch-from", metavar="FETCH_CSV",
                     help="write the idle-expert fetch summary from that counter pass and exit")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "RUN_ARGS"),
                     help="write profiles/mmq_traffic.json from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
     if not args.quick:
         args.all = True
     if args.traffic_from:
-        write_traffic(*args.traffic_from, " ".join(sys.argv))
+        write_traffic(*args.traffic_from, shlex.join(sys.argv))
         return
     if args.expert_fetch_from:
-        write_expert_fetch(args.expert_fetch_from, " ".join(sys.argv))
+        write_expert_fetch(args.expert_fetch_from, shlex.join(sys.argv))
         return
     if args.counters_from:
-        write_counters(*args.counters_from, " ".join(sys.argv))
+        write_counters(*args.counters_from, shlex.join(sys.argv))
         return
     if args.kernel_summary:
         write_kernel_summary(*args.kernel_summary)
