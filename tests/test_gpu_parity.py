@@ -425,6 +425,9 @@ HEAD_WIDE_RANK_CASES = [
     (600, 64, 14000, 2048, 1, 0.0, 6),
     (1024, 64, 10000, 4096, 1, 0.2, 12),
     (600, 192, 14000, 2048, 0, 0.1, 4),
+    # last step of 12 vocabulary rows: one ragged k-step, the first dh range
+    # of that step empty
+    (768, 128, 12300, 2048, 1, 0.1, 4),
 ]
 
 
