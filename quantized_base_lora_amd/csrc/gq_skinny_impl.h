@@ -714,10 +714,24 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef const __attribute__((address_space(1))) u32x2 g_u32x2;
+  // a step whose rows all lie below Kr and on one side of wsplit (the
+  // common case, uniform across the workgroup) adds one scalar row offset to
+  // a per-thread chunk offset; other steps take each chunk's row apart
+  int64_t woff[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) woff[i] = (int64_t)crow[i] * p.w_rowbytes + coff[i];
   auto load_w = [&](int st, u32x2 (&wr)[CI]) {
+    const int n0s = st * SKN_ROWS;
+    if (n0s + SKN_ROWS <= Kr && (n0s + SKN_ROWS <= p.wsplit || n0s >= p.wsplit)) {
+      const uint8_t* sb = n0s >= p.wsplit ? wbase1 + (int64_t)(n0s - p.wsplit) * p.w_rowbytes
+                                          : wbase0 + (int64_t)n0s * p.w_rowbytes;
+#pragma unroll
+      for (int i = 0; i < CI; ++i) wr[i] = *(g_u32x2*)(sb + woff[i]);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CI; ++i) {
-      int n = st * SKN_ROWS + crow[i];
+      int n = n0s + crow[i];
       if (n >= Kr) n = 0;
       const uint8_t* b = n >= p.wsplit ? wbase1 + (int64_t)(n - p.wsplit) * p.w_rowbytes
                                        : wbase0 + (int64_t)n * p.w_rowbytes;
@@ -742,10 +756,28 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
     arow[rg] = p.a0 + src * p.lda;
   }
   const uint16_t* arow1[RG];
+  uint32_t amask[RG];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) arow1[rg] = p.a1 ? arow[rg] - p.a0 + p.a1 : arow[rg];
+  for (int rg = 0; rg < RG; ++rg) {
+    arow1[rg] = p.a1 ? arow[rg] - p.a0 + p.a1 : arow[rg];
+    amask[rg] = opaque_mask(aok[rg]);
+  }
   auto arow_n = [&](int st, int ks) { return st * SKN_ROWS + kg * 64 + ks * 32 + 8 * q; };
   auto load_a = [&](int st, bf16x8 (&af)[2][RG]) {
+    const int n0s = st * SKN_ROWS;
+    if (n0s + SKN_ROWS <= Kr && (n0s + SKN_ROWS <= p.asplit || n0s >= p.asplit)) {
+      // whole step below Kr, one side of asplit: every lane reads its own
+      // rows (rows past the tile read row r0's columns and are zeroed at use)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          const int n = n0s + kg * 64 + ks * 32 + 8 * q;
+          const uint16_t* src = n0s >= p.asplit ? arow1[rg] + (n - p.asplit) : arow[rg] + n;
+          af[ks][rg] = *reinterpret_cast<const bf16x8*>(src);
+        }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -818,8 +850,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
         const bf16x8 b = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          // rows past the tile or the reduction: zero A fragments
-          const uint32_t m = opaque_mask(aok[rg] && arow_n(st, ks) < Kr);
+          // rows past the tile or the reduction: zero A fragments (the
+          // reduction test only matters in the last step)
+          const uint32_t m = st * SKN_ROWS + SKN_ROWS <= Kr ? amask[rg] : opaque_mask(aok[rg] && arow_n(st, ks) < Kr);
           u32x4 av = __builtin_bit_cast(u32x4, af[ks][rg]);
           av &= m;
           acc[rg][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), b,
