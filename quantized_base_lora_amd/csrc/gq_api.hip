@@ -267,6 +267,24 @@ int pick_nn_tile(int64_t rows_per_w, int64_t rows_est, int64_t ntiles128, int64_
 }
 int nn_tile_bn(int tc) { (void)tc; return TILE_BN; }  // 128 for the tile and the skinny NN MMQ
 
+// Grouped tile launches: an expert's last few rows past its full tiles (a
+// nearly empty tile that still decodes the expert's whole weight slice) run
+// on a second, skinny launch, which streams each such slice once.  Forward:
+// remainders of up to 32 rows.  Backward (NN): only experts of at most 8 rows
+// in all, and only beside 128-row tiles -- the skinny NN MMQ is VALU-bound on
+// its decode and gets few workgroups from a handful of remainders (measured
+// slower than the tiles it saves), and beside 64-row tiles (few rows per
+// expert) spilling measured slower too.  Needs the
+// skinny layout: reduction a multiple of 256 (forward) / output row a
+// multiple of 128 (backward), 16-byte aligned weights.  Returns the spill
+// threshold in rows, 0 = no spill launch.
+int spill_rows(int tc, int E, bool nn, int64_t kdim_or_nout, bool w_aligned) {
+  if (tile_skinny(tc) || E < 2 || !w_aligned) return 0;
+  if (nn) return kdim_or_nout % 128 == 0 && tile_bm(tc) == 128 ? 8 : 0;
+  return kdim_or_nout % 256 == 0 ? 32 : 0;
+}
+int spill_tile(int rows) { return rows <= 16 ? TILE_SKINNY16 : TILE_SKINNY32; }
+
 int64_t colred_slots(int64_t M, int rc, int E) { return cdiv(M, rc) + (E > 1 ? E : 0); }
 
 // Dense forward launches with Q8_0 / Q4_0 weights and K % 64 == 0 run the
@@ -758,6 +776,7 @@ size_t gq_grouped_mmq_lora_fwd_workspace_size(const gq_lora_linear* P, int32_t, 
   w.take<int32_t>(64);                // device error word (first 4 bytes)
   w.take<int32_t>(P->n_experts + 1);  // GEMM tiles
   w.take<int32_t>(P->n_experts + 1);  // 16-row tiles of the row dots
+  w.take<int32_t>(P->n_experts + 1);  // skinny tiles of the spill rows
   return w.size();
 }
 
@@ -798,11 +817,14 @@ static int grouped_mmq_lora_fwd_impl(const gq_lora_linear* P, int32_t nproj, int
   int32_t* err = w.take<int32_t>(64);
   int32_t* ts = w.take<int32_t>(E + 1);
   int32_t* ts16 = w.take<int32_t>(E + 1);
+  int32_t* tsp = w.take<int32_t>(E + 1);
   const int ncols = epilogue == GQ_EPI_SWIGLU ? 2 * N : N;  // GEMM columns
   const bool w_al = aligned(P[0].w_blocks, 16) && (nproj < 2 || aligned(P[1].w_blocks, 16));
   const int tc = cdiv(M, E) <= 64 ? pick_fwd_tile(cdiv(M, E), M, cdiv(ncols, TILE_BN), K, w_al)
                                    : pick_grp_tile(M, E, cdiv(ncols, TILE_BN));
-  HIP_TRY(launch_tile_starts(a->offsets, E, M, err, tile_bm(tc), ts, 16, ts16, 1, nullptr, st),
+  const int spill = spill_rows(tc, E, false, K, w_al);
+  HIP_TRY(launch_tile_starts(a->offsets, E, M, err, tile_bm(tc), ts, 16, ts16, 1, nullptr, st,
+                             spill, spill ? tsp : nullptr),
           "gq_grouped_mmq_lora_fwd: tiles");
 
   RowDotArgs rd;
@@ -840,6 +862,12 @@ static int grouped_mmq_lora_fwd_impl(const gq_lora_linear* P, int32_t nproj, int
   }
   g.mtiles = (int)grouped_mtiles(M, E, tile_bm(tc));
   HIP_TRY(launch_gemm(P->qtype, epi, tc, g, st), "gq_grouped_mmq_lora_fwd: grouped MMQ");
+  if (spill) {  // at most one spill tile per expert
+    g.tile_start = tsp;
+    g.mtiles = E;
+    g.spill_bm = tile_bm(tc);
+    HIP_TRY(launch_gemm(P->qtype, epi, spill_tile(spill), g, st), "gq_grouped_mmq_lora_fwd: spill rows");
+  }
   return GQ_OK;
 }
 
@@ -849,6 +877,7 @@ struct GrpBwdWs {
   int32_t* ts;
   int32_t* cs;
   int32_t* ts16;
+  int32_t* tsp;  // skinny tiles of the spill rows
   float* dyB;
   float* wdyB;
   float* wxa;
@@ -867,6 +896,7 @@ GrpBwdWs plan_grp_bwd(Ws& w, const gq_lora_linear* P, int mode, int64_t M) {
   p.ts = w.take<int32_t>(E + 1);
   p.cs = w.take<int32_t>(E + 1);
   p.ts16 = w.take<int32_t>(E + 1);
+  p.tsp = w.take<int32_t>(E + 1);
   const int64_t slots = colred_slots(M, grp_rc(P, M), E);
   if (mode == GQ_BWD_DOWN_SWIGLU) {
     const int64_t H = P[0].n_out, I = P[0].n_in;
@@ -1012,8 +1042,11 @@ static int grouped_mmq_lora_bwd_impl(const gq_lora_linear* P, int32_t nproj, int
     const int tn = pick_nn_tile(cdiv(M, E), M, ntiles_bwd, P[0].n_in, true, 0);
     if (tile_skinny(tn)) tc = tn;
   }
+  // output row of both backward MMQs: I (down) or H (gate/up) = P[0].n_in
+  const int spill = spill_rows(tc, E, true, P[0].n_in, w_al);
   HIP_TRY(launch_tile_starts(a->offsets, E, M, W.err, tile_bm(tc), W.ts, rcg, W.cs, 16,
-                             mode == GQ_BWD_DOWN_SWIGLU ? W.ts16 : nullptr, st),
+                             mode == GQ_BWD_DOWN_SWIGLU ? W.ts16 : nullptr, st,
+                             spill, spill ? W.tsp : nullptr, true),
           "gq_grouped_mmq_lora_bwd: tiles");
 
   ColRedArgs cr;
@@ -1048,6 +1081,14 @@ static int grouped_mmq_lora_bwd_impl(const gq_lora_linear* P, int32_t nproj, int
     g.rv0 = W.dyB; g.s0 = a->g; g.s1 = a->u; g.wflat = a->w_flat; g.sorted = a->sorted;
     g.o0 = a->dg; g.o1 = a->du; g.ldo = I; g.f0 = W.part_down;
     HIP_TRY(launch_gemm(P[0].qtype, EPI_DOWN_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: down MMQ");
+    if (spill) {
+      GemmArgs gs = g;
+      gs.tile_start = W.tsp;
+      gs.mtiles = E;
+      gs.spill_bm = tile_bm(tc);
+      HIP_TRY(launch_gemm(P[0].qtype, EPI_DOWN_BWD, spill_tile(spill), gs, st),
+              "gq_grouped_mmq_lora_bwd: down spill rows");
+    }
 
     // dA_d[e] = s sum_p (w dY Bd)^T h ;  dB_d[e] = s sum_p dY^T (w xa_d):
     // both reductions in one launch, both finishes in one launch
@@ -1085,6 +1126,13 @@ static int grouped_mmq_lora_bwd_impl(const gq_lora_linear* P, int32_t nproj, int
   g.rv0 = a->dgB; g.rv1 = a->duB;
   g.o0 = a->dxrows; g.ldo = H;
   HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, tc, g, st), "gq_grouped_mmq_lora_bwd: gate/up MMQ");
+  if (spill) {
+    g.tile_start = W.tsp;
+    g.mtiles = E;
+    g.spill_bm = tile_bm(tc);
+    HIP_TRY(launch_gemm(P[0].qtype, EPI_GATEUP_BWD, spill_tile(spill), g, st),
+            "gq_grouped_mmq_lora_bwd: gate/up spill rows");
+  }
 
   // dA_g and dA_u in one pass over the gathered x rows
   cr.C = H; cr.U = a->x; cr.ldu = H; cr.gather = a->gather; cr.gdiv = a->gather_div;

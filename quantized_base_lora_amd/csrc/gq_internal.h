@@ -93,6 +93,9 @@ struct GemmArgs {
   // launch_split_fixup then adds the parts, the adapter term, and rounds.
   int32_t ksplit;
   float* part;
+  // grouped skinny launch over spill rows: each expert's rows start after its
+  // full spill_bm-row tiles (those run on the tile MMQ); 0 = all its rows
+  int32_t spill_bm;
 };
 
 // TILE_128x128_K2: 128x128 tiles computed by 512 threads, two groups of four
@@ -152,9 +155,14 @@ hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t c
 // ts_q[e] = sum_{e' < e} ceil(cnt(e') / bm_q), E + 1 entries.  The offsets
 // are checked (offsets[0] == 0, non-decreasing, offsets[E] == M): invalid
 // ones set *err (nullable) to 1 and every prefix to zero, valid ones *err = 0.
+// With spill > 0 and ts_sp non-null, an expert whose rows leave a remainder
+// rem = cnt mod bm0 of 1..spill rows (spill_whole: an expert of 1..spill rows
+// in all) counts only its full bm0-row tiles in ts0 and ceil(rem / spill)
+// tiles of `spill` rows in ts_sp (others: 0).
 hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int64_t M, int32_t* err,
                               int32_t bm0, int32_t* ts0, int32_t bm1, int32_t* ts1, int32_t bm2,
-                              int32_t* ts2, hipStream_t st);
+                              int32_t* ts2, hipStream_t st, int32_t spill = 0,
+                              int32_t* ts_sp = nullptr, bool spill_whole = false);
 
 // out[p][j] = sum_c act(p)[c] * W(e)[j][c]   (W [r][C] if w_jstride == C, or
 // [C][r] if w_jstride == 1, w_cstride == r); act rows via gather; e via offsets.

@@ -113,6 +113,10 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(const GemmArgs p)
     }
     e = lo;
     r0 = (int64_t)p.offsets[e] + (int64_t)(mslot - ts[e]) * RT;
+    if (p.spill_bm > 0) {  // past the expert's full tiles (run by the tile MMQ)
+      const int cnt = p.offsets[e + 1] - p.offsets[e];
+      r0 += cnt - cnt % p.spill_bm;
+    }
     r1 = min((int64_t)p.offsets[e + 1], r0 + RT);
   } else {
     r0 = (int64_t)mslot * RT;
@@ -687,6 +691,10 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_nn_kernel(const GemmArgs
     }
     e = lo;
     r0 = (int64_t)p.offsets[e] + (int64_t)(mslot - ts[e]) * RT;
+    if (p.spill_bm > 0) {  // past the expert's full tiles (run by the tile MMQ)
+      const int cnt = p.offsets[e + 1] - p.offsets[e];
+      r0 += cnt - cnt % p.spill_bm;
+    }
     r1 = min((int64_t)p.offsets[e + 1], r0 + RT);
   } else {
     r0 = (int64_t)mslot * RT;

@@ -70,11 +70,12 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ blocks, int64_t nbloc
 __global__ __launch_bounds__(1024) void tile_start_kernel(const int32_t* __restrict__ offsets,
                                                           int32_t E, int64_t M, int3 bm, int32_t* ts0,
                                                           int32_t* ts1, int32_t* ts2,
-                                                          int32_t* __restrict__ err) {
-  __shared__ int32_t sh[3][1024];
+                                                          int32_t* __restrict__ err, int32_t spill,
+                                                          int32_t spill_whole, int32_t* ts3) {
+  __shared__ int32_t sh[4][1024];
   const int t = threadIdx.x;
   const int bms[3] = {bm.x, bm.y, bm.z};
-  int32_t* outs[3] = {ts0, ts1, ts2};
+  int32_t* outs[4] = {ts0, ts1, ts2, ts3};
   int cnt = t < E ? offsets[t + 1] - offsets[t] : 0;
   bool bad_t = cnt < 0;
   if (t == 0) bad_t = bad_t || offsets[0] != 0 || (int64_t)offsets[E] != M;
@@ -83,18 +84,25 @@ __global__ __launch_bounds__(1024) void tile_start_kernel(const int32_t* __restr
   if (t == 0 && err) *err = bad ? 1 : 0;
 #pragma unroll
   for (int q = 0; q < 3; ++q) sh[q][t] = (t < E && outs[q]) ? (cnt + bms[q] - 1) / bms[q] : 0;
+  // spill rows: a remainder of 1..spill rows past the full bm0-row tiles
+  // (spill_whole: only an expert's whole 1..spill rows) leaves the tile MMQ
+  // for ceil(rem / spill) skinny tiles
+  const int rem = cnt % bms[0];
+  const bool sp = ts3 && spill > 0 && rem > 0 && rem <= spill && (!spill_whole || cnt <= spill);
+  if (sp) sh[0][t] -= 1;
+  sh[3][t] = sp ? (rem + spill - 1) / spill : 0;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    int add[3];
+    int add[4];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) add[q] = t >= o ? sh[q][t - o] : 0;
+    for (int q = 0; q < 4; ++q) add[q] = t >= o ? sh[q][t - o] : 0;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 3; ++q) sh[q][t] += add[q];
+    for (int q = 0; q < 4; ++q) sh[q][t] += add[q];
     __syncthreads();
   }
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < 4; ++q) {
     if (!outs[q]) continue;
     if (t < E) outs[q][t + 1] = sh[q][t];
     if (t == 0) outs[q][0] = 0;
@@ -939,9 +947,11 @@ hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t c
 
 hipError_t launch_tile_starts(const int32_t* offsets, int32_t E, int64_t M, int32_t* err,
                               int32_t bm0, int32_t* ts0, int32_t bm1, int32_t* ts1, int32_t bm2,
-                              int32_t* ts2, hipStream_t st) {
+                              int32_t* ts2, hipStream_t st, int32_t spill, int32_t* ts_sp,
+                              bool spill_whole) {
+  if (ts_sp && (spill < 1 || spill > bm0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(tile_start_kernel, dim3(1), dim3(1024), 0, st, offsets, E, M,
-                     make_int3(bm0, bm1, bm2), ts0, ts1, ts2, err);
+                     make_int3(bm0, bm1, bm2), ts0, ts1, ts2, err, spill, spill_whole ? 1 : 0, ts_sp);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import synth
+from moe_cases import SPILL_CASES
 from oracle import adamw8bit as oa
 from oracle import blocks as ob
 from oracle import linear as ol
@@ -281,7 +282,7 @@ MOE_CASES = [
     # hidden size with an odd number of blocks (H % 64 == 32)
     (60, 96, 64, 4, 2, 1, 4, 0.0),
     (150, 160, 128, 8, 2, 0, 8, 1.0),
-]
+] + SPILL_CASES
 
 
 @pytest.mark.parametrize("T,H,I,E,k,qtype,r,zipf", MOE_CASES)

@@ -129,3 +129,27 @@ def test_zipf_bias_skews_load():
     heavy = np.argmin(-bias)  # rank 1
     assert counts[heavy] == counts.max()
     assert counts.max() > 4 * np.median(counts)
+
+
+def test_spill_cases_have_spill_experts():
+    """The GPU cases meant for the spill launches route at least one expert a
+    remainder of 1..32 rows past its full 64-row tiles and at least one expert
+    a full tile; one of them does the same for 128-row tiles, and one routes
+    experts of 1..8 rows in all beside experts with full 128-row tiles (the
+    backward spill; host-side routing check)."""
+    from moe_cases import SPILL_CASES
+
+    seen128 = seen_nn = False
+    for T, H, I, E, k, qtype, r, zipf in SPILL_CASES:
+        cfg = synth.MoECfg("t", T=T, H=H, I=I, E=E, k=k, qtype=qtype, rank=r, alpha=2.0 * r, zipf=zipf,
+                           seed=T + E)
+        rng = np.random.default_rng([cfg.seed, 0])
+        logits = synth._normal(rng, (T, E), 1.0)
+        if zipf:
+            logits = (logits + synth.zipf_bias(E, zipf, rng)[None, :]).astype(np.float32)
+        cnt = np.diff(orr.route(logits, k)[3])
+        rem = cnt % 64
+        assert np.any((rem >= 1) & (rem <= 32)) and np.any(cnt >= 64), (T, E)
+        seen128 = seen128 or (np.any((cnt % 128 >= 1) & (cnt % 128 <= 32)) and np.any(cnt >= 128))
+        seen_nn = seen_nn or (np.any((cnt >= 1) & (cnt <= 8)) and np.any(cnt >= 128))
+    assert seen128 and seen_nn
