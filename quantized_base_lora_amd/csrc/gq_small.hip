@@ -365,14 +365,24 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
     uoff[i] = c0 + (ucok[i] ? ucol[i] : 0);
   }
   uint4 ur[UCH];
+  // source rows of the next load_u: gathered row indices are read one step
+  // before the rows themselves, so the index load's latency is not paid in
+  // series with the row load's
+  int64_t srow[UCH];
+  auto rows_for = [&](int64_t p0) {
+#pragma unroll
+    for (int i = 0; i < UCH; ++i) {
+      const int64_t p = p0 + urow[i];
+      const int64_t pc = p < r1 ? p : r0;
+      srow[i] = gather ? (int64_t)(gather[pc] / gdiv) : pc;
+    }
+  };
   auto load_u = [&](int64_t p0) {
 #pragma unroll
     for (int i = 0; i < UCH; ++i) {
       const int64_t p = p0 + urow[i];
       const bool ok = p < r1 && ucok[i];
-      const int64_t pc = p < r1 ? p : r0;
-      const int64_t src = gather ? (int64_t)(gather[pc] / gdiv) : pc;
-      ur[i] = *reinterpret_cast<const uint4*>(U + src * ldu + uoff[i]);
+      ur[i] = *reinterpret_cast<const uint4*>(U + srow[i] * ldu + uoff[i]);
       if (!ok) ur[i] = make_uint4(0, 0, 0, 0);
     }
   };
@@ -416,10 +426,15 @@ __global__ __launch_bounds__(256) void colred_kernel(const ColRedArgs a) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   int buf = 0;
+  rows_for(r0);
   load_u(r0);
+  rows_for(r0 + 32);
   for (int64_t p0 = r0; p0 < r1; p0 += 32) {
     store_u(buf);
-    if (p0 + 32 < r1) load_u(p0 + 32);
+    if (p0 + 32 < r1) {
+      load_u(p0 + 32);
+      rows_for(p0 + 64);
+    }
     bf16x8 ahi[NV], alo[NV];
     load_a(V0, p0, ahi[0], alo[0]);
     if constexpr (NV == 2) load_a(a.Vv2, p0, ahi[1], alo[1]);
