@@ -7,8 +7,9 @@ gq_linear_lora_fwd + gq_linear_lora_bwd on inputs already resident in HBM.
 `value` is its algorithmic TFLOP/s.  The same JSON line also carries the
 routed MoE layer (Q4_0, 2048 tokens, hidden 2048, 128 experts top-8,
 intermediate 768, rank 4) train tokens/s, the roofline of the dominant MMQ
-kernel (timed with HIP events around each launch inside the timed region) and
-the fp64 oracle timed on the host cores.
+kernel (timed with HIP events that the kernel dispatch itself stamps, in a
+pass of the same steps beside the timed one) and the fp64 oracle timed on the
+host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 
@@ -580,9 +581,9 @@ def main():
     K = args.steps
     # timed steps: nothing but the step itself on the stream
     ms, ms_graph = time_steps(step, K, args.warmup, key=cfg.name)
-    # a second pass of K steps with events around the two MMQ launches (on
-    # the stream they are launched on) gives the per-launch durations; the
-    # event markers add queue latency, so they stay out of the timed steps
+    # a second pass of K steps with events on the two MMQ launches (stamped
+    # by the kernel dispatch itself on the stream they are launched on)
+    # gives the per-launch durations, outside the timed steps
     prof = [[ev() for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):

@@ -113,11 +113,13 @@ int64_t gq_block_bytes(int qtype);
 
 /*
  * Timing hook for profilers and benchmarks (not part of the method): while
- * `start` / `stop` are non-NULL hipEvent_t handles, every fused MMQ kernel
- * this thread launches records `start` on its stream just before the kernel
- * and `stop` just after it, so hipEventElapsedTime(start, stop) is that
- * kernel's duration.  Pass NULL, NULL to switch it off.  The events belong
- * to the caller; they are recorded again by each later MMQ launch.
+ * `start` / `stop` are non-NULL hipEvent_t handles (created with timing
+ * enabled), every fused MMQ kernel this thread launches is dispatched with
+ * them through hipExtLaunchKernel, which stamps `start` when the kernel
+ * begins executing and `stop` when it ends, so hipEventElapsedTime(start,
+ * stop) is that kernel's duration without the queue time around it.  Pass
+ * NULL, NULL to switch it off.  The events belong to the caller; they are
+ * stamped again by each later MMQ launch.
  */
 void gq_profile_mmq_events(void* start, void* stop);
 

@@ -14,7 +14,7 @@ hipError_t launch_gemm_q2_dm_nn(int epi, int tilecfg, const GemmArgs& a, hipStre
 hipError_t launch_ce_bwd_dh_q(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st);
 
 namespace {
-// optional timing events recorded around every MMQ launch of this thread
+// optional timing events of every MMQ launch of this thread (mmq_launch)
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 hipError_t dispatch(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {
@@ -33,24 +33,14 @@ void set_profile_events(hipEvent_t start, hipEvent_t stop) {
   g_prof_stop = stop;
 }
 
+hipEvent_t profile_event(int stop) { return stop ? g_prof_stop : g_prof_start; }
+
 hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipStream_t st) {
   if ((int64_t)a.mtiles * a.ntiles == 0) return hipSuccess;
-  if (g_prof_start) {
-    const hipError_t e = hipEventRecord(g_prof_start, st);
-    if (e != hipSuccess) return e;
-  }
-  const hipError_t e = dispatch(qtype, epi, tilecfg, a, st);
-  if (e == hipSuccess && g_prof_stop) return hipEventRecord(g_prof_stop, st);
-  return e;
+  return dispatch(qtype, epi, tilecfg, a, st);
 }
 
 hipError_t launch_ce_bwd_dh(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st) {
-  if (g_prof_start) {
-    const hipError_t e = hipEventRecord(g_prof_start, st);
-    if (e != hipSuccess) return e;
-  }
-  const hipError_t e = launch_ce_bwd_dh_q(qtype, ce, dh, st);
-  if (e == hipSuccess && g_prof_stop) return hipEventRecord(g_prof_stop, st);
-  return e;
+  return launch_ce_bwd_dh_q(qtype, ce, dh, st);
 }
 }  // namespace gq

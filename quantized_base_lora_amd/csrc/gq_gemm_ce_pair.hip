@@ -9,9 +9,9 @@ hipError_t launch_ce_bwd_dh_q(int qtype, const GemmArgs& ce, const GemmArgs& dh,
   if (nce <= 0 || ndh <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(nce + ndh));
   switch (qtype) {
-    case QT_Q8_0: hipLaunchKernelGGL(ce_bwd_dh_kernel<QT_Q8_0>, grid, dim3(NTHR), 0, st, ce, dh, nce); break;
-    case QT_Q4_0: hipLaunchKernelGGL(ce_bwd_dh_kernel<QT_Q4_0>, grid, dim3(NTHR), 0, st, ce, dh, nce); break;
-    case QT_Q2_DM: hipLaunchKernelGGL(ce_bwd_dh_kernel<QT_Q2_DM>, grid, dim3(NTHR), 0, st, ce, dh, nce); break;
+    case QT_Q8_0: mmq_launch(ce_bwd_dh_kernel<QT_Q8_0>, grid, dim3(NTHR), st, ce, dh, nce); break;
+    case QT_Q4_0: mmq_launch(ce_bwd_dh_kernel<QT_Q4_0>, grid, dim3(NTHR), st, ce, dh, nce); break;
+    case QT_Q2_DM: mmq_launch(ce_bwd_dh_kernel<QT_Q2_DM>, grid, dim3(NTHR), st, ce, dh, nce); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

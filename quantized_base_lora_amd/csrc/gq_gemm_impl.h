@@ -1241,14 +1241,14 @@ hipError_t launch_q(int tilecfg, const GemmArgs& a, hipStream_t st) {
   }
   if constexpr (!epi_stages(EPI)) {
     if (tilecfg == TILE_128x128_K2) {
-      hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128, 2>), grid, dim3(2 * NTHR), 0, st, a);
+      mmq_launch((gemm_kernel<QT, EPI, 128, 128, 2>), grid, dim3(2 * NTHR), st, a);
       return hipGetLastError();
     }
   }
   if (tilecfg == TILE_128x128)
-    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 128, 128, 1>), grid, dim3(NTHR), 0, st, a);
+    mmq_launch((gemm_kernel<QT, EPI, 128, 128, 1>), grid, dim3(NTHR), st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<QT, EPI, 64, 128, 1>), grid, dim3(NTHR), 0, st, a);
+    mmq_launch((gemm_kernel<QT, EPI, 64, 128, 1>), grid, dim3(NTHR), st, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (gq_api.hip) and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -144,8 +145,22 @@ hipError_t launch_gemm(int qtype, int epi, int tilecfg, const GemmArgs& a, hipSt
 // One launch of EPI_CE_BWD tiles (`ce`, 128 x 128, TILE_128x128) followed by
 // EPI_DH_ACC tiles (`dh`, 128 x 128, one group of four waves).
 hipError_t launch_ce_bwd_dh(int qtype, const GemmArgs& ce, const GemmArgs& dh, hipStream_t st);
-// thread-local timing events recorded around each launch_gemm (nullptr: off)
+// thread-local timing events of the MMQ launches (nullptr: off)
 void set_profile_events(hipEvent_t start, hipEvent_t stop);
+hipEvent_t profile_event(int stop);
+
+// Every MMQ kernel is launched through this: with the thread's timing events
+// set, through hipExtLaunchKernelGGL, whose dispatch itself stamps `start`
+// when the kernel begins and `stop` when it ends (no queue time between an
+// event and the kernel); a plain launch otherwise.
+template <typename F, typename... Args>
+inline void mmq_launch(F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  const hipEvent_t a = profile_event(0), b = profile_event(1);
+  if (a && b)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // ---- small kernels (gq_small.hip) ----
 hipError_t launch_dequant(int qtype, const void* blocks, int64_t rows, int64_t cols,

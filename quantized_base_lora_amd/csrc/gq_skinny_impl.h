@@ -410,11 +410,11 @@ hipError_t launch_skinny(int rg, const GemmArgs& a, hipStream_t st) {
   if (a.r > 16) return hipErrorInvalidValue;  // the fold stages 16 ranks
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(64 * SK_WAVES);
   if (rg == 1)
-    hipLaunchKernelGGL((skinny_kernel<QT, EPI, 1>), grid, block, 0, st, a);
+    mmq_launch((skinny_kernel<QT, EPI, 1>), grid, block, st, a);
   else if (rg == 2)
-    hipLaunchKernelGGL((skinny_kernel<QT, EPI, 2>), grid, block, 0, st, a);
+    mmq_launch((skinny_kernel<QT, EPI, 2>), grid, block, st, a);
   else
-    hipLaunchKernelGGL((skinny_kernel<QT, EPI, 4>), grid, block, 0, st, a);
+    mmq_launch((skinny_kernel<QT, EPI, 4>), grid, block, st, a);
   return hipGetLastError();
 }
 
@@ -945,9 +945,9 @@ template <int QT, int EPI>
 hipError_t launch_skinny_nn(int rg, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles), block(64 * SK_WAVES);
   if (rg == 1)
-    hipLaunchKernelGGL((skinny_nn_kernel<QT, EPI, 1>), grid, block, 0, st, a);
+    mmq_launch((skinny_nn_kernel<QT, EPI, 1>), grid, block, st, a);
   else
-    hipLaunchKernelGGL((skinny_nn_kernel<QT, EPI, 2>), grid, block, 0, st, a);
+    mmq_launch((skinny_nn_kernel<QT, EPI, 2>), grid, block, st, a);
   return hipGetLastError();
 }
 

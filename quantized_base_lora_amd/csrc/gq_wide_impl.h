@@ -603,7 +603,7 @@ namespace {
 template <int QT, int EPI>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles);
-  hipLaunchKernelGGL((wide::wide_kernel<QT, EPI>), grid, dim3(wide::NTHR), 0, st, a);
+  mmq_launch((wide::wide_kernel<QT, EPI>), grid, dim3(wide::NTHR), st, a);
   return hipGetLastError();
 }
 }  // namespace

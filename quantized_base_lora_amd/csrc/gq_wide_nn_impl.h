@@ -331,9 +331,9 @@ hipError_t launch_wide_nn(const GemmArgs& a, hipStream_t st) {
   const unsigned ks = a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
   const dim3 grid((unsigned)a.mtiles * (unsigned)a.ntiles * ks);
   if (a.K % wnn::BK)
-    hipLaunchKernelGGL((wnn::wide_nn_kernel<QT, EPI, true>), grid, dim3(wnn::NTHR), 0, st, a);
+    mmq_launch((wnn::wide_nn_kernel<QT, EPI, true>), grid, dim3(wnn::NTHR), st, a);
   else
-    hipLaunchKernelGGL((wnn::wide_nn_kernel<QT, EPI, false>), grid, dim3(wnn::NTHR), 0, st, a);
+    mmq_launch((wnn::wide_nn_kernel<QT, EPI, false>), grid, dim3(wnn::NTHR), st, a);
   return hipGetLastError();
 }
 }  // namespace
