@@ -217,7 +217,8 @@ def test_linear_deterministic():
 @pytest.mark.parametrize("T,E,k,zipf", [(37, 8, 2, 0.0), (1000, 128, 8, 0.0), (4096, 256, 8, 1.0),
                                         (5, 1, 1, 0.0), (64, 16, 16, 0.0), (300, 1024, 16, 0.0),
                                         (16, 1024, 16, 1.0), (32, 128, 8, 0.0), (33, 128, 8, 0.0),
-                                        (16, 60, 8, 0.0), (100, 200, 8, 1.0), (50, 600, 4, 0.0)])
+                                        (16, 60, 8, 0.0), (100, 200, 8, 1.0), (50, 600, 4, 0.0),
+                                        (128, 128, 8, 1.0), (205, 64, 5, 0.0), (128, 3, 3, 0.0)])
 def test_route_bit_exact(T, E, k, zipf):
     rng = np.random.default_rng(T + E)
     logits = rng.standard_normal((T, E), dtype=np.float32)
