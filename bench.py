@@ -556,11 +556,12 @@ def main():
         del g
         return a.elapsed_time(b) / (reps * n)
 
-    # The headline linear step is timed after the other workloads: their timed
-    # work brings the GPU to its sustained clocks (a kernel trace of this run
+    # The Q4_0 MoE layer and then the headline linear step are timed after the
+    # other workloads, with their inputs made up front: the timed work before
+    # them brings the GPU to its sustained clocks (a kernel trace of this run
     # shows the dX MMQ going from 82 to 69.5 us per launch over the first
-    # ~30 ms of sustained work), so the headline's W warm-up steps and K timed
-    # steps run at the clocks a training loop runs at, not at the ramp.  Every
+    # ~30 ms of sustained work), so their W warm-up steps and K timed steps
+    # run at the clocks a training loop runs at, not at the ramp.  Every
     # workload keeps its own W untimed warm-up steps.
     K = args.steps
     result = {}
@@ -578,7 +579,8 @@ def main():
     ws = torch.empty(lib.gq_linear_lora_bwd_workspace_size(gq.C.byref(p.c()), cfg.T),
                      dtype=torch.uint8, device=dev)
 
-    # --------------------------------------------------------------- MoE layer
+    # inputs of the Q4_0 MoE layer, resident from here on (timed below, after
+    # the other workloads, like the headline step)
     if not args.no_moe:
         mc = synth.MOE_Q4_0_T2048
         t0 = time.time()
@@ -591,24 +593,6 @@ def main():
                             mk(minp["wd"], minp["ad"], minp["bd"], H, I))
         mx, mdy, mlg = bf(minp["x"]), bf(minp["dy"]), f32(minp["logits"])
         del minp
-
-        def mstep():
-            yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
-            return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
-
-        mms, mms_graph = time_steps(mstep, K, max(2, args.warmup), key=mc.name)
-        mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
-        # rows routed to each expert (one routing call outside the timed steps)
-        counts = np.diff(gq.moe_route(mlg, mc.k)[3].cpu().numpy().astype(np.int64))
-        act = counts[counts > 0]
-        route_hist = {"active_experts": int(act.size), "max_rows": int(counts.max()),
-                      "median_rows": float(np.median(counts)), "min_active_rows": int(act.min())}
-        result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
-                               "ms_per_step": round(mms, 4), "ms_per_step_hip_graph": round(mms_graph, 4),
-                               "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
-                               "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                               "route_rows_per_expert": route_hist}
-        log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
 
     # ------------------------------------------------------- other workloads
     if args.all:
@@ -834,6 +818,26 @@ def main():
                 f"({100 * gbs / PEAK_HBM_GBS:.1f}% HBM)")
             del hd
         result["small_token_sweep"] = sweep
+
+    # --------------------------------------------------------------- MoE layer
+    if not args.no_moe:
+        def mstep():
+            yy, saved = gq.moe_ffn_fwd(wts, mx, mlg, mc.k)
+            return gq.moe_ffn_bwd(wts, mx, mdy, saved, mc.k, E)
+
+        mms, mms_graph = time_steps(mstep, K, max(2, args.warmup), key=mc.name)
+        mfl = moe_flops(mc.T, H, I, mc.k, mc.rank)
+        # rows routed to each expert (one routing call outside the timed steps)
+        counts = np.diff(gq.moe_route(mlg, mc.k)[3].cpu().numpy().astype(np.int64))
+        act = counts[counts > 0]
+        route_hist = {"active_experts": int(act.size), "max_rows": int(counts.max()),
+                      "median_rows": float(np.median(counts)), "min_active_rows": int(act.min())}
+        result["moe_layer"] = {"workload": mc.name, "tokens_per_s": round(mc.T / (mms * 1e-3), 1),
+                               "ms_per_step": round(mms, 4), "ms_per_step_hip_graph": round(mms_graph, 4),
+                               "tflops": round(mfl / (mms * 1e-3) / 1e12, 2),
+                               "frac_bf16_peak": round(mfl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "route_rows_per_expert": route_hist}
+        log(f"[bench] moe layer {mms:.3f} ms/step, {mc.T / (mms * 1e-3):.0f} tok/s")
 
     # ------------------------------------------------------------ linear step (timed below)
     def step(prof=None):
